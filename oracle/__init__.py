@@ -1,0 +1,149 @@
+"""LAPLEX CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The GPU library never calls it and shares no
+code with it.
+
+Two parts, both float64:
+
+* ``dense_*``: the plain definition of the operator of "LAPLEX: The FFT of
+  Learnable Laplace Kernels" (technical summary, section 2.1 "The Operator"),
+  ``y_i = sum_j exp(-|a_i - b_j|) [cos(phi_i - psi_j)] x_j``, written out with
+  NumPy in row chunks and no sort.  O(n k m); for small sizes and spot rows.
+* ``sym_apply`` / ``general_apply`` / ``phased_apply`` / ``stable_argsort``:
+  the sequential scan algebra of section 2.2 ("Exact Scan Algebra") in plain C
+  (``laplex_oracle.c``), O(n log n).
+
+Pins (the test-suite checks these against facts other than the oracle
+itself): the closed-form Kac-Murdock-Szego inverse for equispaced anchors, the
+tridiagonal inverse of the exponential (Markov) covariance for arbitrary
+distinct anchors, the Toeplitz/FFT reduction on a uniform grid, geometric-series
+row sums, symmetry and adjointness, K e_j = column j, the zero-temperature
+permutation limit, and brute force on tiny inputs.  No function here is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "laplex_oracle.c")
+_SO = os.path.join(_HERE, "liblaplex_oracle.so")
+_lock = threading.Lock()
+_lib_handle = None
+
+
+def build(force: bool = False, out: Optional[str] = None, src: Optional[str] = None) -> str:
+    """Compile the C oracle with gcc (plain -O2, IEEE arithmetic)."""
+    out = out or _SO
+    src = src or _SRC
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-std=gnu11", "-fPIC", "-shared", "-o", tmp, src, "-lm"], check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def load(path: Optional[str] = None):
+    """Load (building if needed) the C oracle library and declare its signatures."""
+    global _lib_handle
+    with _lock:
+        if path is None and _lib_handle is not None:
+            return _lib_handle
+        lib = ctypes.CDLL(path or build())
+        f32p = ctypes.POINTER(ctypes.c_float)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        u32p = ctypes.POINTER(ctypes.c_uint32)
+        i64 = ctypes.c_int64
+        lib.lo_stable_argsort.argtypes = [f32p, i64, u32p]
+        lib.lo_sym_apply.argtypes = [f32p, i64, i64, f32p, f64p]
+        lib.lo_general_apply.argtypes = [f32p, i64, f32p, i64, i64, f32p, f64p]
+        lib.lo_phased_apply.argtypes = [f32p, f32p, i64, f32p, f32p, i64, i64, f32p, f64p]
+        for fn in (lib.lo_stable_argsort, lib.lo_sym_apply, lib.lo_general_apply, lib.lo_phased_apply):
+            fn.restype = ctypes.c_int
+        if path is None:
+            _lib_handle = lib
+        return lib
+
+
+def _f32(v):
+    return np.ascontiguousarray(v, dtype=np.float32)
+
+
+def _ptr(arr, ct):
+    return arr.ctypes.data_as(ctypes.POINTER(ct))
+
+
+def _check(rc):
+    if rc == -1:
+        raise ValueError("non-finite anchor")
+    if rc != 0:
+        raise MemoryError("oracle allocation failed (rc=%d)" % rc)
+
+
+def _as2d(x, rows):
+    x = _f32(x)
+    if x.ndim == 1:
+        x = x.reshape(rows, 1)
+    return x
+
+
+def stable_argsort(a, lib=None) -> np.ndarray:
+    """Ascending stable argsort (ties by input index, -0.0 == +0.0), uint32."""
+    lib = lib or load()
+    a = _f32(a).ravel()
+    perm = np.empty(a.size, np.uint32)
+    _check(lib.lo_stable_argsort(_ptr(a, ctypes.c_float), a.size, _ptr(perm, ctypes.c_uint32)))
+    return perm
+
+
+def sym_apply(a, x, lib=None) -> np.ndarray:
+    """K(a, a) x by the sorted prefix/suffix recurrences (float64, n x m)."""
+    lib = lib or load()
+    a = _f32(a).ravel()
+    x2 = _as2d(x, a.size)
+    y = np.empty(x2.shape, np.float64)
+    _check(lib.lo_sym_apply(_ptr(a, ctypes.c_float), a.size, x2.shape[1], _ptr(x2, ctypes.c_float), _ptr(y, ctypes.c_double)))
+    return y
+
+
+def general_apply(a, b, x, lib=None) -> np.ndarray:
+    """K(a, b) x by interval aggregation into u, v and two scans (float64, n x m)."""
+    lib = lib or load()
+    a = _f32(a).ravel()
+    b = _f32(b).ravel()
+    x2 = _as2d(x, b.size)
+    y = np.empty((a.size, x2.shape[1]), np.float64)
+    _check(lib.lo_general_apply(_ptr(a, ctypes.c_float), a.size, _ptr(b, ctypes.c_float), b.size, x2.shape[1],
+                                _ptr(x2, ctypes.c_float), _ptr(y, ctypes.c_double)))
+    return y
+
+
+def phased_apply(a, phi, x, b=None, psi=None, lib=None) -> np.ndarray:
+    """Phased operator by complex scans.  ``b is None`` selects b = a, psi = phi."""
+    lib = lib or load()
+    a = _f32(a).ravel()
+    phi = _f32(phi).ravel()
+    if b is None:
+        x2 = _as2d(x, a.size)
+        y = np.empty(x2.shape, np.float64)
+        _check(lib.lo_phased_apply(_ptr(a, ctypes.c_float), _ptr(phi, ctypes.c_float), a.size, None, None, 0,
+                                   x2.shape[1], _ptr(x2, ctypes.c_float), _ptr(y, ctypes.c_double)))
+        return y
+    b = _f32(b).ravel()
+    psi = _f32(psi).ravel()
+    x2 = _as2d(x, b.size)
+    y = np.empty((a.size, x2.shape[1]), np.float64)
+    _check(lib.lo_phased_apply(_ptr(a, ctypes.c_float), _ptr(phi, ctypes.c_float), a.size, _ptr(b, ctypes.c_float),
+                               _ptr(psi, ctypes.c_float), b.size, x2.shape[1], _ptr(x2, ctypes.c_float),
+                               _ptr(y, ctypes.c_double)))
+    return y
+
+
+from .dense import dense_apply, dense_envelope, dense_rows, normwise_error  # noqa: E402,F401

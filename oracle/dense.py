@@ -1,0 +1,101 @@
+"""Dense float64 brute force of the LAPLEX operator -- TEST INFRASTRUCTURE ONLY.
+
+The plain definition of "LAPLEX: The FFT of Learnable Laplace Kernels"
+(technical summary, section 2.1 "The Operator"):
+
+    LAPLEX(a, b)_ij              = exp(-|a_i - b_j|)
+    LAPLEX(a, phi; b, psi)_ij    = exp(-|a_i - b_j|) * cos(phi_i - psi_j)
+
+applied to x with no sort and no scan, rows processed in chunks so memory
+stays bounded.  Inputs are widened to float64 exactly (float32 arrays, as
+the GPU receives them, convert without rounding).  Row index i runs over the
+output anchors a, column index j over the input anchors b (the pages relabel
+the indices between the two formulas; the first index is always the output).
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+
+
+def _chunk_rows(k: int, budget: int = 1 << 24) -> int:
+    return max(1, budget // max(1, k))
+
+
+def _weights(ai, b, phi_i=None, psi=None):
+    w = np.exp(-np.abs(ai[:, None] - b[None, :]))
+    if phi_i is not None:
+        w *= np.cos(phi_i[:, None] - psi[None, :])
+    return w
+
+
+def dense_apply(a, x, b=None, phi=None, psi=None) -> np.ndarray:
+    """y = LAPLEX(a[, phi]; b[, psi]) x in float64; b None -> b = a (and psi = phi)."""
+    a = np.asarray(a, np.float64).ravel()
+    b = a if b is None else np.asarray(b, np.float64).ravel()
+    if phi is not None:
+        phi = np.asarray(phi, np.float64).ravel()
+        psi = phi if psi is None else np.asarray(psi, np.float64).ravel()
+    x = np.asarray(x, np.float64)
+    x2 = x.reshape(b.size, -1)
+    y = np.zeros((a.size, x2.shape[1]), np.float64)
+    step = _chunk_rows(b.size)
+    for lo in range(0, a.size, step):
+        hi = min(a.size, lo + step)
+        w = _weights(a[lo:hi], b, None if phi is None else phi[lo:hi], psi)
+        y[lo:hi] = w @ x2
+    return y
+
+
+def dense_envelope(a, x, b=None) -> np.ndarray:
+    """K0 |x| with the unphased kernel: the scale of the normwise error measure."""
+    return dense_apply(a, np.abs(np.asarray(x, np.float64)), b=b)
+
+
+def dense_rows(rows: Sequence[int], a, x, b=None, phi=None, psi=None, col_chunk: int = 1 << 22):
+    """Selected rows of y and of K0|x| by the plain definition, for inputs too large
+    for a full dense product.  Returns (y_rows, env_rows), each len(rows) x m."""
+    rows = np.asarray(rows, np.int64)
+    a = np.asarray(a).ravel()
+    b = a if b is None else np.asarray(b).ravel()
+    ai = a[rows].astype(np.float64)
+    phi_i = None
+    if phi is not None:
+        phi = np.asarray(phi).ravel()
+        psi = phi if psi is None else np.asarray(psi).ravel()
+        phi_i = phi[rows].astype(np.float64)
+    x2 = np.asarray(x).reshape(b.size, -1)
+    m = x2.shape[1]
+    y = np.zeros((rows.size, m), np.float64)
+    env = np.zeros((rows.size, m), np.float64)
+    for lo in range(0, b.size, col_chunk):
+        hi = min(b.size, lo + col_chunk)
+        bj = b[lo:hi].astype(np.float64)
+        xc = x2[lo:hi].astype(np.float64)
+        env += _weights(ai, bj) @ np.abs(xc)
+        if phi_i is None:
+            y += _weights(ai, bj) @ xc
+        else:
+            y += _weights(ai, bj, phi_i, psi[lo:hi].astype(np.float64)) @ xc
+    return y, env
+
+
+def normwise_error(y, y_ref, env, env_scale: Optional[np.ndarray] = None) -> float:
+    """max over columns c of ||y_c - y_ref_c||_inf / ||(K0|x|)_c||_inf.
+
+    ``env_scale`` may supply the per-column denominators directly (e.g. the
+    maximum over sampled rows, which is a lower bound and so a stricter test)."""
+    y = np.asarray(y, np.float64).reshape(np.shape(y_ref))
+    y_ref = np.asarray(y_ref, np.float64)
+    if y_ref.ndim == 1:
+        y_ref = y_ref[:, None]
+        y = y.reshape(y_ref.shape)
+    num = np.max(np.abs(y - y_ref), axis=0)
+    if env_scale is None:
+        env = np.asarray(env, np.float64).reshape(y_ref.shape)
+        den = np.max(np.abs(env), axis=0)
+    else:
+        den = np.asarray(env_scale, np.float64).ravel()
+    den = np.where(den > 0, den, 1.0)
+    return float(np.max(num / den)) if num.size else 0.0

@@ -1,0 +1,95 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in a temporary copy of the C oracle (or patches
+the dense brute force's weight function), rebuilds it on the CPU, and checks
+that at least one pin of oracle_pins.py then fails.  The oracle itself is not
+modified.
+"""
+import os
+import shutil
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import dense as odense
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "laplex_oracle.c")
+
+# (name, original text, replacement, which occurrence)
+C_MUTANTS = [
+    ("merge_unstable", "if (src[q].v < src[p].v)", "if (src[q].v <= src[p].v)", 0),
+    ("insertion_unstable", "while (j >= lo && buf0[j].v > t.v)", "while (j >= lo && buf0[j].v >= t.v)", 0),
+    ("nonfinite_accepted", "if (!isfinite(a[i])) return -1;", "if (0) return -1;", 0),
+    ("sym_prefix_decay_sign", "double d = exp(as[i - 1] - as[i]);", "double d = exp(as[i] - as[i - 1]);", 0),
+    ("sym_suffix_decay_sign", "exp(as[i] - as[i + 1]);", "exp(as[i + 1] - as[i]);", 0),
+    ("sym_diagonal_twice", "yr[c] = ls[i * m + c] + u[c] - (double)xr[c];", "yr[c] = ls[i * m + c] + u[c];", 0),
+    ("sym_no_scatter", "double* yr = y + (size_t)perm[i] * m;", "double* yr = y + (size_t)i * m;", 0),
+    ("sym_suffix_dropped", "u[c] = (double)xr[c] + d * u[c];", "u[c] = (double)xr[c];", 0),
+    ("general_u_weight_sign", "double w = exp(bj - as[p]);", "double w = exp(as[p] - bj);", 0),
+    ("general_v_weight_sign", "double w = exp(as[p - 1] - bj);", "double w = exp(bj - as[p - 1]);", 0),
+    ("general_v_dropped", "vv[(p - 1) * m + c] += w * (double)xr[c];", "vv[(p - 1) * m + c] += 0.0 * w * (double)xr[c];", 0),
+    ("general_x_unsorted", "const float* xr = x + (size_t)pb[j] * m;", "const float* xr = x + (size_t)j * m;", 0),
+    ("general_prefix_decay_sign", "double d = exp(as[i - 1] - as[i]);", "double d = exp(as[i] - as[i - 1]);", 1),
+    ("general_suffix_decay_sign", "exp(as[i] - as[i + 1]);", "exp(as[i + 1] - as[i]);", 1),
+    ("general_y_unpermuted", "double* yr = y + (size_t)pa[i] * m;", "double* yr = y + (size_t)i * m;", 0),
+    ("phased_input_phase_sign", "double complex e = cexp(-I * ph);", "double complex e = cexp(I * ph);", 0),
+    ("phased_output_phase_sign", "double complex eo = cexp(I * (double)phi[pa[i]]);", "double complex eo = cexp(-I * (double)phi[pa[i]]);", 0),
+    ("phased_imag_part", "yr[c] = creal(eo * w);", "yr[c] = cimag(eo * w);", 0),
+    ("phased_diagonal_twice", "if (sym) w -= cexp(", "if (0) w -= cexp(", 0),
+    ("phased_general_psi_unsorted", "cexp(-I * (double)psi[pb[j]]);", "cexp(-I * (double)psi[j]);", 0),
+    ("phased_general_u_weight", "double w = exp(bj - as[p]);", "double w = exp(as[p] - bj);", 1),
+]
+
+
+def _replace_nth(text, old, new, nth):
+    start = -1
+    for _ in range(nth + 1):
+        start = text.find(old, start + 1)
+        assert start >= 0, "mutation anchor not found: %r (occurrence %d)" % (old, nth)
+    return text[:start] + new + text[start + len(old):]
+
+
+def _any_pin_fails(lib):
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(lib)
+        except Exception as e:  # AssertionError, ValueError, ...
+            failed.append((pin.__name__, type(e).__name__))
+    return failed
+
+
+@pytest.mark.parametrize("mut", C_MUTANTS, ids=[m[0] for m in C_MUTANTS])
+def test_c_mutant_is_caught(mut, tmp_path):
+    name, old, new, nth = mut
+    text = open(SRC).read()
+    src = tmp_path / ("mut_%s.c" % name)
+    src.write_text(_replace_nth(text, old, new, nth))
+    so = oracle.build(force=True, out=str(tmp_path / ("libmut_%s.so" % name)), src=str(src))
+    lib = oracle.load(so)
+    failed = _any_pin_fails(lib)
+    assert failed, "planted mistake %s passed every pin" % name
+
+
+DENSE_MUTANTS = {
+    "no_abs": lambda ai, b, phi_i=None, psi=None: np.exp(-(ai[:, None] - b[None, :])) * (
+        1.0 if phi_i is None else np.cos(phi_i[:, None] - psi[None, :])),
+    "half_rate": lambda ai, b, phi_i=None, psi=None: np.exp(-0.5 * np.abs(ai[:, None] - b[None, :])) * (
+        1.0 if phi_i is None else np.cos(phi_i[:, None] - psi[None, :])),
+    "phase_sum": lambda ai, b, phi_i=None, psi=None: np.exp(-np.abs(ai[:, None] - b[None, :])) * (
+        1.0 if phi_i is None else np.cos(phi_i[:, None] + psi[None, :])),
+    "phase_sine": lambda ai, b, phi_i=None, psi=None: np.exp(-np.abs(ai[:, None] - b[None, :])) * (
+        1.0 if phi_i is None else np.sin(phi_i[:, None] - psi[None, :])),
+    "squared_distance": lambda ai, b, phi_i=None, psi=None: np.exp(-np.square(ai[:, None] - b[None, :])) * (
+        1.0 if phi_i is None else np.cos(phi_i[:, None] - psi[None, :])),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DENSE_MUTANTS))
+def test_dense_mutant_is_caught(name, monkeypatch, oracle_lib):
+    monkeypatch.setattr(odense, "_weights", DENSE_MUTANTS[name])
+    failed = _any_pin_fails(oracle_lib)
+    assert failed, "planted mistake %s in the dense oracle passed every pin" % name

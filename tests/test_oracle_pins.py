@@ -1,0 +1,9 @@
+"""The CPU oracle against its pins (closed forms, invariants, brute force)."""
+import pytest
+
+from oracle_pins import ALL_PINS
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_oracle_pin(pin, oracle_lib):
+    pin(oracle_lib)
