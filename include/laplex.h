@@ -1,0 +1,126 @@
+/*
+ * laplex.h -- C interface of the LAPLEX operator library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operator ("LAPLEX: The FFT of Learnable Laplace Kernels", technical
+ * summary, section 2.1 "The Operator"):
+ *
+ *     LAPLEX(a, b)_ij           = exp(-|a_i - b_j|)                  a in R^n, b in R^k
+ *     LAPLEX(a, phi; b, psi)_ij = exp(-|a_i - b_j|) cos(phi_i - psi_j)
+ *
+ * applied to a block of m right-hand sides, y = LAPLEX x, in O((n + k) log)
+ * work through the sort and prefix/suffix scan algebra of section 2.2
+ * ("Exact Scan Algebra"); the dense matrix is never formed.  Row index i is
+ * the output (anchors a), column index j the input (anchors b).
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller (for example
+ *    the data of torch tensors).  float arrays are IEEE binary32; permutations
+ *    are uint32.  All must be 4-byte aligned.
+ *  - x is row-major (rows x m): row r holds the m columns of input r
+ *    contiguously; y likewise (n x m).  x, y, phi and psi are in the ORIGINAL
+ *    (unsorted) order of their anchors.
+ *  - Work is enqueued on `stream` and is asynchronous: argument errors are
+ *    returned synchronously, nothing is waited on.  The library allocates no
+ *    memory and keeps no global state; each call needs its own workspace of
+ *    at least laplex_workspace_bytes(...) bytes (256-byte aligned), and calls
+ *    whose workspaces differ may run concurrently on different streams.
+ *  - Outputs must not overlap inputs or the workspace.
+ *  - n, k < 2^32 (permutations are uint32).  n == 0 or m == 0 is a no-op.
+ */
+#ifndef LAPLEX_H
+#define LAPLEX_H
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LAPLEX_OK = 0,
+  LAPLEX_ERR_NULL = 1,       /* a required pointer is NULL */
+  LAPLEX_ERR_SIZE = 2,       /* n or k >= 2^32, or m too large */
+  LAPLEX_ERR_ALIGN = 3,      /* a pointer is not 4-byte aligned (workspace: 256-byte) */
+  LAPLEX_ERR_WORKSPACE = 4,  /* ws_bytes smaller than laplex_workspace_bytes(...) */
+  LAPLEX_ERR_NONFINITE = 5,  /* an anchor was NaN or +-Inf (reported by laplex_status_poll) */
+  LAPLEX_ERR_HIP = 6,        /* a HIP launch or runtime call failed */
+  LAPLEX_ERR_OVERLAP = 7,    /* an output overlaps an input or the workspace */
+  LAPLEX_ERR_STALLED = 8,    /* a look-back wait hit its spin limit (reported by laplex_status_poll) */
+  LAPLEX_ERR_ARG = 9         /* any other invalid argument */
+} laplex_status;
+
+/* Operations, for laplex_workspace_bytes. */
+enum {
+  LAPLEX_OP_SORT = 0,
+  LAPLEX_OP_SYM = 1,
+  LAPLEX_OP_GENERAL = 2,
+  LAPLEX_OP_PHASED = 3,         /* symmetric phased operator (b = a, psi = phi) */
+  LAPLEX_OP_PHASED_GENERAL = 4  /* phased operator with a != b */
+};
+
+/* Bytes of workspace one call of `op` needs for n output anchors, k input
+ * anchors (ignored by the symmetric operations) and m columns.  Returns 0 when
+ * the sizes are out of range. */
+size_t laplex_workspace_bytes(int op, uint64_t n, uint64_t k, uint32_t m);
+
+/* Sort of the anchors ("after sorting the anchors", section 2.2, symmetric
+ * case): perm[r] is the input index of the r-th smallest anchor and
+ * a_sorted[r] = a[perm[r]] bit for bit.  The order is ascending and stable
+ * (equal anchors keep their input order; -0.0 and +0.0 count as equal).
+ * The pair (a_sorted, perm) is the sort handle every apply takes, so one sort
+ * serves any number of applies.  NaN/Inf anchors leave the outputs undefined
+ * and raise LAPLEX_ERR_NONFINITE in laplex_status_poll(ws).
+ * a: n floats (input); a_sorted: n floats (output); perm: n uint32 (output);
+ * ws: workspace of laplex_workspace_bytes(LAPLEX_OP_SORT, n, 0, 1) bytes. */
+laplex_status laplex_sort_anchors(const float* a, uint64_t n, float* a_sorted, uint32_t* perm, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/* Waits for `stream`, then returns the sticky device-side status of the last
+ * sort that used `ws` (LAPLEX_OK, LAPLEX_ERR_NONFINITE or LAPLEX_ERR_STALLED). */
+laplex_status laplex_status_poll(const void* ws, hipStream_t stream);
+
+/* Symmetric operator y = LAPLEX(a, a) x (section 2.2, symmetric case: lower
+ * part by a prefix scan y_i = x_i + exp(a_{i-1} - a_i) y_{i-1}, upper part by
+ * the mirrored suffix scan, combined as lower + upper - diagonal).
+ * a_sorted, perm: the sort handle of a (n each); x: n x m (input, original
+ * order); y: n x m (output, original order);
+ * ws: laplex_workspace_bytes(LAPLEX_OP_SYM, n, 0, m) bytes. */
+laplex_status laplex_matvec_sym(const float* a_sorted, const uint32_t* perm, uint64_t n, uint32_t m, const float* x, float* y,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* General operator y = LAPLEX(a, b) x with a != b (section 2.2, general case:
+ * the input anchors b are placed into the intervals of the sorted output
+ * anchors a and propagated with the same scan primitive; here the two sorted
+ * sequences are merged, b before a on equal anchors, and scanned once in
+ * each direction).  A b anchor equal to an a anchor couples with weight 1.
+ * a_sorted, perm_a: sort handle of a (n); b_sorted, perm_b: sort handle of b
+ * (k); x: k x m (input); y: n x m (output);
+ * ws: laplex_workspace_bytes(LAPLEX_OP_GENERAL, n, k, m) bytes.
+ * k == 0 sets y to zero. */
+laplex_status laplex_matvec_general(const float* a_sorted, const uint32_t* perm_a, uint64_t n, const float* b_sorted,
+                                    const uint32_t* perm_b, uint64_t k, uint32_t m, const float* x, float* y, void* ws,
+                                    size_t ws_bytes, hipStream_t stream);
+
+/* Phased operator y = LAPLEX(a, phi; b, psi) x (section 2.1, phased
+ * extension), computed as two real scans of the columns cos(psi) x and
+ * sin(psi) x, recombined with cos(phi) and sin(phi)
+ * (cos(phi_i - psi_j) = cos phi_i cos psi_j + sin phi_i sin psi_j).
+ * b_sorted == NULL selects the symmetric operator b = a, psi = phi (perm_b,
+ * psi and k are then ignored and x is n x m).  phi: n floats, psi: k floats,
+ * both in original order.
+ * ws: laplex_workspace_bytes(LAPLEX_OP_PHASED or LAPLEX_OP_PHASED_GENERAL, n, k, m). */
+laplex_status laplex_matvec_phased(const float* a_sorted, const uint32_t* perm_a, const float* phi, uint64_t n,
+                                   const float* b_sorted, const uint32_t* perm_b, const float* psi, uint64_t k, uint32_t m,
+                                   const float* x, float* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Short English description of a status code (static storage). */
+const char* laplex_status_string(laplex_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAPLEX_H */

@@ -1,0 +1,29 @@
+"""LAPLEX operator on AMD Instinct MI355X (gfx950).
+
+Python binding of liblaplex.so (include/laplex.h).  Argument marshalling
+only: every step of the computation runs in the HIP kernels of the library;
+PyTorch provides device memory and the current stream.  If the library has
+not been built the calls raise -- there is no fallback.
+
+    a_sorted, perm = laplex_sort_anchors(a)          # sort handle of a
+    y = laplex_matvec_sym(a_sorted, perm, x)         # y_i = sum_j exp(-|a_i - a_j|) x_j
+    y = laplex_matvec_general(a_sorted, perm, b_sorted, perm_b, xb)
+    y = laplex_matvec_phased(a_sorted, perm, phi, x)  # extra cos(phi_i - phi_j)
+"""
+from ._binding import (  # noqa: F401
+    LAPLEX_OP_GENERAL,
+    LAPLEX_OP_PHASED,
+    LAPLEX_OP_PHASED_GENERAL,
+    LAPLEX_OP_SORT,
+    LAPLEX_OP_SYM,
+    LaplexError,
+    lib,
+    lib_path,
+    laplex_matvec_general,
+    laplex_matvec_phased,
+    laplex_matvec_sym,
+    laplex_sort_anchors,
+    laplex_status_poll,
+    laplex_workspace_bytes,
+    workspace,
+)

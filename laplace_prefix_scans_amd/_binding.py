@@ -1,0 +1,198 @@
+"""ctypes binding of liblaplex.so (declarations in include/laplex.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblaplex.so")
+
+LAPLEX_OP_SORT, LAPLEX_OP_SYM, LAPLEX_OP_GENERAL, LAPLEX_OP_PHASED, LAPLEX_OP_PHASED_GENERAL = 0, 1, 2, 3, 4
+
+_STATUS = {
+    0: "LAPLEX_OK", 1: "LAPLEX_ERR_NULL", 2: "LAPLEX_ERR_SIZE", 3: "LAPLEX_ERR_ALIGN", 4: "LAPLEX_ERR_WORKSPACE",
+    5: "LAPLEX_ERR_NONFINITE", 6: "LAPLEX_ERR_HIP", 7: "LAPLEX_ERR_OVERLAP", 8: "LAPLEX_ERR_STALLED", 9: "LAPLEX_ERR_ARG",
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class LaplexError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s: %s (%s)" % (where, _STATUS.get(code, "?"), _lib.laplex_status_string(code).decode()
+                                          if _lib is not None else ""))
+
+
+def lib_path() -> str:
+    return LIB_PATH
+
+
+def lib():
+    """Load liblaplex.so once; raise if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("liblaplex.so is not built (python -m laplace_prefix_scans_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, u64, u32, sz, i32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_int
+        L.laplex_workspace_bytes.argtypes = [i32, u64, u64, u32]
+        L.laplex_workspace_bytes.restype = sz
+        L.laplex_sort_anchors.argtypes = [vp, u64, vp, vp, vp, sz, vp]
+        L.laplex_status_poll.argtypes = [vp, vp]
+        L.laplex_matvec_sym.argtypes = [vp, vp, u64, u32, vp, vp, vp, sz, vp]
+        L.laplex_matvec_general.argtypes = [vp, vp, u64, vp, vp, u64, u32, vp, vp, vp, sz, vp]
+        L.laplex_matvec_phased.argtypes = [vp, vp, vp, u64, vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
+        for f in (L.laplex_sort_anchors, L.laplex_status_poll, L.laplex_matvec_sym, L.laplex_matvec_general,
+                  L.laplex_matvec_phased):
+            f.restype = i32
+        L.laplex_status_string.argtypes = [i32]
+        L.laplex_status_string.restype = ctypes.c_char_p
+        _lib = L
+        return L
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise LaplexError(code, where)
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _vec(t: torch.Tensor, name: str, dtype=torch.float32) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _cols(x: torch.Tensor, rows: int, name: str = "x") -> int:
+    _vec(x, name)
+    if x.dim() == 1:
+        if x.shape[0] != rows:
+            raise ValueError("%s has %d rows, expected %d" % (name, x.shape[0], rows))
+        return 1
+    if x.dim() != 2 or x.shape[0] != rows:
+        raise ValueError("%s must be (%d,) or (%d, m), got %s" % (name, rows, rows, tuple(x.shape)))
+    return x.shape[1]
+
+
+def laplex_workspace_bytes(op: int, n: int, k: int = 0, m: int = 1) -> int:
+    return int(lib().laplex_workspace_bytes(op, n, k, m))
+
+
+def workspace(op: int, n: int, k: int = 0, m: int = 1, device=None) -> torch.Tensor:
+    """A byte tensor big enough for one call of ``op``."""
+    nbytes = max(256, laplex_workspace_bytes(op, n, k, m))
+    return torch.empty(nbytes, dtype=torch.uint8, device=device or torch.device("cuda"))
+
+
+def _ws(ws: Optional[torch.Tensor], op, n, k, m, dev) -> torch.Tensor:
+    if ws is None:
+        return workspace(op, n, k, m, dev)
+    if ws.device != dev or ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
+    return ws
+
+
+def laplex_sort_anchors(a: torch.Tensor, a_sorted: Optional[torch.Tensor] = None, perm: Optional[torch.Tensor] = None,
+                        ws: Optional[torch.Tensor] = None, check: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Stable ascending sort of the anchors: returns (a_sorted, perm) with
+    a_sorted = a[perm] and perm a uint32 tensor.  ``check=True`` waits for the
+    stream and raises LaplexError if an anchor was NaN/Inf."""
+    _vec(a, "a")
+    if a.dim() != 1:
+        raise ValueError("a must be 1-D")
+    n, dev = a.shape[0], a.device
+    a_sorted = torch.empty_like(a) if a_sorted is None else _vec(a_sorted, "a_sorted")
+    perm = torch.empty(n, dtype=torch.uint32, device=dev) if perm is None else _vec(perm, "perm", torch.uint32)
+    ws = _ws(ws, LAPLEX_OP_SORT, n, 0, 1, dev)
+    L = lib()
+    _check(L.laplex_sort_anchors(_ptr(a), n, _ptr(a_sorted), _ptr(perm), _ptr(ws), ws.numel(), _stream(dev)),
+           "laplex_sort_anchors")
+    if check:
+        _check(L.laplex_status_poll(_ptr(ws), _stream(dev)), "laplex_sort_anchors")
+    return a_sorted, perm
+
+
+def laplex_status_poll(ws: torch.Tensor) -> int:
+    """Wait for the current stream and return the sort workspace's sticky status code."""
+    return int(lib().laplex_status_poll(_ptr(ws), _stream(ws.device)))
+
+
+def laplex_matvec_sym(a_sorted: torch.Tensor, perm: torch.Tensor, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                      ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = LAPLEX(a, a) x for the sort handle (a_sorted, perm); x is (n,) or (n, m)."""
+    _vec(a_sorted, "a_sorted")
+    _vec(perm, "perm", torch.uint32)
+    n, dev = a_sorted.shape[0], a_sorted.device
+    m = _cols(x, n)
+    y = torch.empty_like(x) if y is None else y
+    _cols(y, n, "y")
+    ws = _ws(ws, LAPLEX_OP_SYM, n, 0, m, dev)
+    _check(lib().laplex_matvec_sym(_ptr(a_sorted), _ptr(perm), n, m, _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(dev)),
+           "laplex_matvec_sym")
+    return y
+
+
+def laplex_matvec_general(a_sorted: torch.Tensor, perm_a: torch.Tensor, b_sorted: torch.Tensor, perm_b: torch.Tensor,
+                          x: torch.Tensor, y: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = LAPLEX(a, b) x; x is (k,) or (k, m), y is (n,) or (n, m)."""
+    _vec(a_sorted, "a_sorted")
+    _vec(perm_a, "perm_a", torch.uint32)
+    _vec(b_sorted, "b_sorted")
+    _vec(perm_b, "perm_b", torch.uint32)
+    n, k, dev = a_sorted.shape[0], b_sorted.shape[0], a_sorted.device
+    m = _cols(x, k)
+    if y is None:
+        y = torch.empty((n,) if x.dim() == 1 else (n, m), dtype=torch.float32, device=dev)
+    _cols(y, n, "y")
+    ws = _ws(ws, LAPLEX_OP_GENERAL, n, k, m, dev)
+    _check(lib().laplex_matvec_general(_ptr(a_sorted), _ptr(perm_a), n, _ptr(b_sorted), _ptr(perm_b), k, m, _ptr(x), _ptr(y),
+                                       _ptr(ws), ws.numel(), _stream(dev)), "laplex_matvec_general")
+    return y
+
+
+def laplex_matvec_phased(a_sorted: torch.Tensor, perm_a: torch.Tensor, phi: torch.Tensor, x: torch.Tensor,
+                         b_sorted: Optional[torch.Tensor] = None, perm_b: Optional[torch.Tensor] = None,
+                         psi: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                         ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = LAPLEX(a, phi; b, psi) x.  Without b: the symmetric phased operator (b = a, psi = phi)."""
+    _vec(a_sorted, "a_sorted")
+    _vec(perm_a, "perm_a", torch.uint32)
+    _vec(phi, "phi")
+    n, dev = a_sorted.shape[0], a_sorted.device
+    if b_sorted is None:
+        k, op = 0, LAPLEX_OP_PHASED
+        m = _cols(x, n)
+    else:
+        _vec(b_sorted, "b_sorted")
+        _vec(perm_b, "perm_b", torch.uint32)
+        _vec(psi, "psi")
+        k, op = b_sorted.shape[0], LAPLEX_OP_PHASED_GENERAL
+        m = _cols(x, k)
+    if y is None:
+        y = torch.empty((n,) if x.dim() == 1 else (n, m), dtype=torch.float32, device=dev)
+    _cols(y, n, "y")
+    ws = _ws(ws, op, n, k, m, dev)
+    _check(lib().laplex_matvec_phased(_ptr(a_sorted), _ptr(perm_a), _ptr(phi), n, _ptr(b_sorted), _ptr(perm_b), _ptr(psi), k, m,
+                                      _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(dev)), "laplex_matvec_phased")
+    return y

@@ -1,0 +1,228 @@
+// C-ABI entry points: argument checks, workspace layout, launches.
+#include <hip/hip_runtime.h>
+
+#include "../../include/laplex.h"
+#include "laplex_kernels.hpp"
+
+namespace laplex {
+hipError_t fill_zero_u32(void* p, uint64_t words, hipStream_t s);
+}
+
+namespace {
+
+using namespace laplex;
+
+constexpr uint64_t kMaxLen = 0xFFFFFFFFull;  // uint32 permutations
+constexpr uint32_t kMaxCols = 1u << 16;
+
+// Carves 256-byte aligned regions out of a workspace (base 0: sizing only).
+struct Carver {
+  uintptr_t base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(reinterpret_cast<uintptr_t>(b)) {}
+  template <typename T>
+  T* take(size_t bytes) {
+    off = (off + 255) & ~size_t(255);
+    T* p = reinterpret_cast<T*>(base + off);
+    off += bytes;
+    return p;
+  }
+};
+
+SortWorkspace carve_sort(void* ws, uint64_t n) {
+  Carver c(ws);
+  SortWorkspace w;
+  w.header = c.take<uint32_t>(kSortHeaderBytes);
+  w.hist = w.header + kSortHistOffset / 4;
+  w.offsets = w.header + kSortOffsOffset / 4;
+  w.status = c.take<void>(sort_status_bytes(n));  // directly after the header
+  for (int i = 0; i < 2; ++i) w.keys[i] = c.take<uint32_t>(n * 4);
+  for (int i = 0; i < 2; ++i) w.vals[i] = c.take<uint32_t>(n * 4);
+  (void)c.take<char>(0);
+  return w;
+}
+size_t sort_bytes(uint64_t n) {
+  Carver c(nullptr);
+  c.take<uint32_t>(kSortHeaderBytes);
+  c.take<void>(sort_status_bytes(n));
+  for (int i = 0; i < 4; ++i) c.take<uint32_t>(n * 4);
+  return (c.off + 255) & ~size_t(255);
+}
+
+// rows: length of the gathered input (n symmetric, k general); len: scanned length
+ApplyWorkspace carve_apply(void* ws, uint64_t rows, uint64_t len, uint32_t m, Variant var, bool general, size_t* total) {
+  Carver c(ws);
+  ApplyWorkspace w{};
+  const uint64_t T = apply_tiles(len, m, var);
+  const uint64_t M = (var == Variant::Phased) ? 2ull * m : m;
+  w.xs = c.take<float>(rows * m * 4);
+  w.phs = (var == Variant::Phased) ? c.take<float>(rows * 4) : nullptr;
+  w.bf = c.take<float>(T * M * 4);
+  w.bb = c.take<float>(T * M * 4);
+  w.cf = c.take<float>(T * M * 4);
+  w.cb = c.take<float>(T * M * 4);
+  w.tanch = c.take<float2>(T * 8);
+  w.tsplit = general ? c.take<uint2>((T + 1) * 8) : nullptr;
+  if (total) *total = (c.off + 255) & ~size_t(255);
+  return w;
+}
+
+bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+bool overlaps(const void* p, size_t pb, const void* q, size_t qb) {
+  if (!p || !q || pb == 0 || qb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + pb;
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(q), b1 = b0 + qb;
+  return a0 < b1 && b0 < a1;
+}
+
+laplex_status from_hip(hipError_t e) { return e == hipSuccess ? LAPLEX_OK : LAPLEX_ERR_HIP; }
+
+}  // namespace
+
+extern "C" size_t laplex_workspace_bytes(int op, uint64_t n, uint64_t k, uint32_t m) {
+  if (n > kMaxLen || k > kMaxLen || m > kMaxCols) return 0;
+  if (m == 0) m = 1;
+  size_t total = 0;
+  switch (op) {
+    case LAPLEX_OP_SORT: return sort_bytes(n);
+    case LAPLEX_OP_SYM: carve_apply(nullptr, n, n, m, Variant::Sym, false, &total); return total;
+    case LAPLEX_OP_PHASED: carve_apply(nullptr, n, n, m, Variant::Phased, false, &total); return total;
+    case LAPLEX_OP_GENERAL: carve_apply(nullptr, k, n + k, m, Variant::Sym, true, &total); return total;
+    case LAPLEX_OP_PHASED_GENERAL: carve_apply(nullptr, k, n + k, m, Variant::Phased, true, &total); return total;
+    default: return 0;
+  }
+}
+
+extern "C" laplex_status laplex_sort_anchors(const float* a, uint64_t n, float* a_sorted, uint32_t* perm, void* ws,
+                                             size_t ws_bytes, hipStream_t stream) {
+  if (n == 0) return LAPLEX_OK;
+  if (n > kMaxLen) return LAPLEX_ERR_SIZE;
+  if (!a || !a_sorted || !perm || !ws) return LAPLEX_ERR_NULL;
+  if (misaligned(a, 4) || misaligned(a_sorted, 4) || misaligned(perm, 4) || misaligned(ws, 256)) return LAPLEX_ERR_ALIGN;
+  if (ws_bytes < sort_bytes(n)) return LAPLEX_ERR_WORKSPACE;
+  const size_t vb = n * 4;
+  if (overlaps(a_sorted, vb, a, vb) || overlaps(perm, vb, a, vb) || overlaps(a_sorted, vb, perm, vb) ||
+      overlaps(a_sorted, vb, ws, ws_bytes) || overlaps(perm, vb, ws, ws_bytes))
+    return LAPLEX_ERR_OVERLAP;
+  const SortWorkspace w = carve_sort(ws, n);
+  return from_hip(sort_anchors(w, a, n, a_sorted, perm, stream));
+}
+
+extern "C" laplex_status laplex_status_poll(const void* ws, hipStream_t stream) {
+  if (!ws) return LAPLEX_ERR_NULL;
+  if (hipStreamSynchronize(stream) != hipSuccess) return LAPLEX_ERR_HIP;
+  uint32_t flags = 0;
+  if (hipMemcpy(&flags, static_cast<const uint32_t*>(ws) + kHdrFlags, 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return LAPLEX_ERR_HIP;
+  if (flags & kFlagNonFinite) return LAPLEX_ERR_NONFINITE;
+  if (flags & kFlagWatchdog) return LAPLEX_ERR_STALLED;
+  return LAPLEX_OK;
+}
+
+static laplex_status check_apply_common(const float* a_sorted, const uint32_t* perm, uint64_t n, uint32_t m, const float* x,
+                                        float* y, void* ws) {
+  if (n > kMaxLen) return LAPLEX_ERR_SIZE;
+  if (m > kMaxCols) return LAPLEX_ERR_SIZE;
+  if (!a_sorted || !perm || !x || !y || !ws) return LAPLEX_ERR_NULL;
+  if (misaligned(a_sorted, 4) || misaligned(perm, 4) || misaligned(x, 4) || misaligned(y, 4) || misaligned(ws, 256))
+    return LAPLEX_ERR_ALIGN;
+  return LAPLEX_OK;
+}
+
+extern "C" laplex_status laplex_matvec_sym(const float* a_sorted, const uint32_t* perm, uint64_t n, uint32_t m, const float* x,
+                                           float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (n == 0 || m == 0) return LAPLEX_OK;
+  laplex_status st = check_apply_common(a_sorted, perm, n, m, x, y, ws);
+  if (st != LAPLEX_OK) return st;
+  size_t need = 0;
+  carve_apply(nullptr, n, n, m, Variant::Sym, false, &need);
+  if (ws_bytes < need) return LAPLEX_ERR_WORKSPACE;
+  const size_t yb = n * (size_t)m * 4, vb = n * 4;
+  if (overlaps(y, yb, x, yb) || overlaps(y, yb, a_sorted, vb) || overlaps(y, yb, perm, vb) || overlaps(y, yb, ws, ws_bytes))
+    return LAPLEX_ERR_OVERLAP;
+  const ApplyWorkspace w = carve_apply(ws, n, n, m, Variant::Sym, false, nullptr);
+  return from_hip(apply_sym(w, Variant::Sym, a_sorted, perm, nullptr, n, m, x, y, stream));
+}
+
+extern "C" laplex_status laplex_matvec_general(const float* a_sorted, const uint32_t* perm_a, uint64_t n, const float* b_sorted,
+                                               const uint32_t* perm_b, uint64_t k, uint32_t m, const float* x, float* y, void* ws,
+                                               size_t ws_bytes, hipStream_t stream) {
+  if (n == 0 || m == 0) return LAPLEX_OK;
+  laplex_status st = check_apply_common(a_sorted, perm_a, n, m, x ? x : (const float*)y, y, ws);
+  if (st != LAPLEX_OK) return st;
+  if (k > kMaxLen) return LAPLEX_ERR_SIZE;
+  const size_t yb = n * (size_t)m * 4;
+  if (k == 0) {
+    if (overlaps(y, yb, a_sorted, n * 4) || overlaps(y, yb, perm_a, n * 4)) return LAPLEX_ERR_OVERLAP;
+    return from_hip(fill_zero_u32(y, n * (uint64_t)m, stream));
+  }
+  if (!b_sorted || !perm_b || !x) return LAPLEX_ERR_NULL;
+  if (misaligned(b_sorted, 4) || misaligned(perm_b, 4)) return LAPLEX_ERR_ALIGN;
+  size_t need = 0;
+  carve_apply(nullptr, k, n + k, m, Variant::Sym, true, &need);
+  if (ws_bytes < need) return LAPLEX_ERR_WORKSPACE;
+  const size_t xb = k * (size_t)m * 4;
+  if (overlaps(y, yb, x, xb) || overlaps(y, yb, a_sorted, n * 4) || overlaps(y, yb, perm_a, n * 4) ||
+      overlaps(y, yb, b_sorted, k * 4) || overlaps(y, yb, perm_b, k * 4) || overlaps(y, yb, ws, ws_bytes))
+    return LAPLEX_ERR_OVERLAP;
+  const ApplyWorkspace w = carve_apply(ws, k, n + k, m, Variant::Sym, true, nullptr);
+  return from_hip(apply_general(w, Variant::Sym, a_sorted, perm_a, nullptr, n, b_sorted, perm_b, nullptr, k, m, x, y, stream));
+}
+
+extern "C" laplex_status laplex_matvec_phased(const float* a_sorted, const uint32_t* perm_a, const float* phi, uint64_t n,
+                                              const float* b_sorted, const uint32_t* perm_b, const float* psi, uint64_t k,
+                                              uint32_t m, const float* x, float* y, void* ws, size_t ws_bytes,
+                                              hipStream_t stream) {
+  if (n == 0 || m == 0) return LAPLEX_OK;
+  laplex_status st = check_apply_common(a_sorted, perm_a, n, m, x ? x : (const float*)y, y, ws);
+  if (st != LAPLEX_OK) return st;
+  if (!phi) return LAPLEX_ERR_NULL;
+  if (misaligned(phi, 4)) return LAPLEX_ERR_ALIGN;
+  const size_t yb = n * (size_t)m * 4;
+  if (b_sorted == nullptr) {
+    if (!x) return LAPLEX_ERR_NULL;
+    size_t need = 0;
+    carve_apply(nullptr, n, n, m, Variant::Phased, false, &need);
+    if (ws_bytes < need) return LAPLEX_ERR_WORKSPACE;
+    if (overlaps(y, yb, x, yb) || overlaps(y, yb, a_sorted, n * 4) || overlaps(y, yb, perm_a, n * 4) ||
+        overlaps(y, yb, phi, n * 4) || overlaps(y, yb, ws, ws_bytes))
+      return LAPLEX_ERR_OVERLAP;
+    const ApplyWorkspace w = carve_apply(ws, n, n, m, Variant::Phased, false, nullptr);
+    return from_hip(apply_sym(w, Variant::Phased, a_sorted, perm_a, phi, n, m, x, y, stream));
+  }
+  if (k > kMaxLen) return LAPLEX_ERR_SIZE;
+  if (k == 0) {
+    if (overlaps(y, yb, a_sorted, n * 4) || overlaps(y, yb, perm_a, n * 4) || overlaps(y, yb, phi, n * 4))
+      return LAPLEX_ERR_OVERLAP;
+    return from_hip(fill_zero_u32(y, n * (uint64_t)m, stream));
+  }
+  if (!perm_b || !psi || !x) return LAPLEX_ERR_NULL;
+  if (misaligned(b_sorted, 4) || misaligned(perm_b, 4) || misaligned(psi, 4)) return LAPLEX_ERR_ALIGN;
+  size_t need = 0;
+  carve_apply(nullptr, k, n + k, m, Variant::Phased, true, &need);
+  if (ws_bytes < need) return LAPLEX_ERR_WORKSPACE;
+  const size_t xb = k * (size_t)m * 4;
+  if (overlaps(y, yb, x, xb) || overlaps(y, yb, a_sorted, n * 4) || overlaps(y, yb, perm_a, n * 4) ||
+      overlaps(y, yb, phi, n * 4) || overlaps(y, yb, b_sorted, k * 4) || overlaps(y, yb, perm_b, k * 4) ||
+      overlaps(y, yb, psi, k * 4) || overlaps(y, yb, ws, ws_bytes))
+    return LAPLEX_ERR_OVERLAP;
+  const ApplyWorkspace w = carve_apply(ws, k, n + k, m, Variant::Phased, true, nullptr);
+  return from_hip(apply_general(w, Variant::Phased, a_sorted, perm_a, phi, n, b_sorted, perm_b, psi, k, m, x, y, stream));
+}
+
+extern "C" const char* laplex_status_string(laplex_status s) {
+  switch (s) {
+    case LAPLEX_OK: return "ok";
+    case LAPLEX_ERR_NULL: return "a required pointer is NULL";
+    case LAPLEX_ERR_SIZE: return "size out of range (n, k < 2^32; m <= 65536)";
+    case LAPLEX_ERR_ALIGN: return "misaligned pointer (arrays 4 bytes, workspace 256 bytes)";
+    case LAPLEX_ERR_WORKSPACE: return "workspace too small";
+    case LAPLEX_ERR_NONFINITE: return "an anchor is NaN or infinite";
+    case LAPLEX_ERR_HIP: return "HIP runtime error";
+    case LAPLEX_ERR_OVERLAP: return "an output overlaps an input or the workspace";
+    case LAPLEX_ERR_STALLED: return "a look-back wait hit its spin limit";
+    case LAPLEX_ERR_ARG: return "invalid argument";
+  }
+  return "unknown status";
+}

@@ -1,0 +1,309 @@
+// Stable LSD radix sort of float anchors with their permutation ("after
+// sorting the anchors": LAPLEX technical summary, section 2.2, symmetric case).
+//
+// Keys are the order-preserving unsigned image of the float bits (-0.0 made
+// equal to +0.0).  One read of the anchors builds all four 8-bit digit
+// histograms; then four single-pass ("onesweep") scatter passes, each tile
+// ranking its keys stably in LDS, publishing per-digit counts and looking back
+// over earlier tiles (decoupled look-back) to find its global offsets.  Pass
+// 1 generates the identity permutation itself; pass 4 writes the sorted
+// anchors and the permutation.
+#include "laplex_kernels.hpp"
+
+namespace laplex {
+
+// ------------------------------------------------------------------ status words
+template <typename ST>
+struct Status;
+template <>
+struct Status<uint32_t> {  // n <= 2^30: 2-bit flag, 30-bit count
+  static __device__ __forceinline__ uint32_t pack(uint32_t flag, uint32_t v) { return (flag << 30) | (v & 0x3FFFFFFFu); }
+  static __device__ __forceinline__ uint32_t flag(uint32_t w) { return w >> 30; }
+  static __device__ __forceinline__ uint32_t value(uint32_t w) { return w & 0x3FFFFFFFu; }
+};
+template <>
+struct Status<uint64_t> {  // n < 2^32: flag in the high word, count in the low word
+  static __device__ __forceinline__ uint64_t pack(uint32_t flag, uint32_t v) { return ((uint64_t)flag << 32) | v; }
+  static __device__ __forceinline__ uint32_t flag(uint64_t w) { return (uint32_t)(w >> 32); }
+  static __device__ __forceinline__ uint32_t value(uint64_t w) { return (uint32_t)w; }
+};
+constexpr uint32_t kFlagAggregate = 1, kFlagInclusive = 2;
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, uint64_t count, uint32_t value) {
+  uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (; i < count; i += stride) p[i] = value;
+}
+
+// ------------------------------------------------------------------ histograms
+// All four digit histograms in one read.  Sub-histograms are replicated
+// kHistRep times in LDS (lane % kHistRep picks one) so that keys sharing a
+// digit (e.g. the top byte of anchors in a narrow range) do not all hit one
+// LDS word.  Integer atomics: the result does not depend on ordering.
+constexpr int kHistRep = 8;
+constexpr int kHistBlock = 256;
+constexpr int kHistItems = 16;
+
+__global__ __launch_bounds__(kHistBlock) void k_sort_hist(const uint32_t* __restrict__ a_bits, uint64_t n,
+                                                          uint32_t* __restrict__ hist, uint32_t* __restrict__ header) {
+  __shared__ uint32_t sh[4][256][kHistRep];
+  for (int i = threadIdx.x; i < 4 * 256 * kHistRep; i += kHistBlock) (&sh[0][0][0])[i] = 0;
+  __syncthreads();
+  const int rep = lane_id() % kHistRep;
+  uint32_t bad = 0;
+  const uint64_t chunk = (uint64_t)kHistBlock * kHistItems;
+  const uint64_t nchunks = (n + chunk - 1) / chunk;
+  for (uint64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    const uint64_t base = c * chunk;
+#pragma unroll
+    for (int it = 0; it < kHistItems; ++it) {
+      const uint64_t i = base + (uint64_t)it * kHistBlock + threadIdx.x;
+      if (i < n) {
+        const uint32_t u = a_bits[i];
+        bad |= bits_nonfinite(u) ? 1u : 0u;
+        const uint32_t k = float_to_key(u);
+        atomicAdd(&sh[0][k & 255u][rep], 1u);
+        atomicAdd(&sh[1][(k >> 8) & 255u][rep], 1u);
+        atomicAdd(&sh[2][(k >> 16) & 255u][rep], 1u);
+        atomicAdd(&sh[3][k >> 24][rep], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 4 * 256; i += kHistBlock) {
+    uint32_t s = 0;
+#pragma unroll
+    for (int r = 0; r < kHistRep; ++r) s += sh[i >> 8][i & 255][r];
+    if (s) atomicAdd(&hist[i], s);
+  }
+  if (__ballot(bad) != 0ull && lane_id() == 0) atomicOr(&header[kHdrFlags], kFlagNonFinite);
+}
+
+// Exclusive prefix of each digit histogram -> global start of each bucket.
+// One block of 256 threads; thread d handles digit value d of every pass.
+__global__ __launch_bounds__(256) void k_sort_offsets(const uint32_t* __restrict__ hist, uint32_t* __restrict__ offs) {
+  __shared__ uint32_t wsum[4];
+  const int d = threadIdx.x, lane = lane_id(), w = d / kWave;
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t v = hist[p * 256 + d];
+    uint32_t x = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t t = __shfl_up(x, off);
+      if (lane >= off) x += t;
+    }
+    if (lane == kWave - 1) wsum[w] = x;
+    __syncthreads();
+    uint32_t pre = 0;
+    for (int i = 0; i < w; ++i) pre += wsum[i];
+    offs[p * 256 + d] = pre + x - v;
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ onesweep pass
+// MODE 0: input is the anchors' float bits (keys computed here, values are the
+//         input indices); MODE 1: key/value buffers to key/value buffers;
+// MODE 2: writes float bits of the sorted anchors and the permutation.
+template <int MODE, typename ST>
+__global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin,
+                                                         uint32_t* __restrict__ kout, uint32_t* __restrict__ vout,
+                                                         const uint32_t* __restrict__ a_bits, ST* __restrict__ status,
+                                                         uint32_t* __restrict__ header, int pass,
+                                                         const uint32_t* __restrict__ digit_start, uint64_t n) {
+  static_assert(kSortBlock == 256, "one thread per digit value");
+  constexpr int E = kSortItems;
+  constexpr int TILE = kSortTile;
+  constexpr int NW = kSortBlock / kWave;
+  __shared__ uint32_t s_keys[TILE];
+  __shared__ uint32_t s_vals[TILE];
+  __shared__ uint32_t s_whist[NW][256];
+  __shared__ uint32_t s_dstart[256];
+  __shared__ uint32_t s_gbase[256];
+  __shared__ uint32_t s_wsum[NW];
+  __shared__ uint32_t s_tile;
+
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  const uint32_t shift = 8u * (uint32_t)pass;
+  if (tid == 0) s_tile = atomicAdd(&header[kHdrTicket0 + pass], 1u);
+  for (int i = tid; i < NW * 256; i += kSortBlock) (&s_whist[0][0])[i] = 0;
+  __syncthreads();
+  const uint32_t tile = s_tile;
+  const uint64_t base = (uint64_t)tile * TILE;
+
+  // load: wave w owns the contiguous run [w*64*E, (w+1)*64*E) of the tile;
+  // iteration e reads 64 consecutive keys, so (e, lane) is input order
+  uint32_t k[E], v[E], rk[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint64_t idx = base + (uint64_t)wid * (kWave * E) + (uint64_t)e * kWave + lane;
+    const bool valid = idx < n;
+    if (MODE == 0) {
+      k[e] = valid ? float_to_key(kin[idx]) : 0xFFFFFFFFu;
+      v[e] = (uint32_t)idx;
+    } else {
+      k[e] = valid ? kin[idx] : 0xFFFFFFFFu;
+      v[e] = valid ? vin[idx] : 0u;
+    }
+  }
+  // stable rank within the wave's run: earlier iterations first, then lower lanes
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint64_t idx = base + (uint64_t)wid * (kWave * E) + (uint64_t)e * kWave + lane;
+    const bool valid = idx < n;
+    const uint64_t vmask = __ballot(valid);
+    const uint32_t d = (k[e] >> shift) & 255u;
+    const uint64_t peers = match_digit8(d, vmask);
+    const uint32_t before = s_whist[wid][d];
+    const uint32_t r = lanes_below(peers);
+    rk[e] = before + r;
+    if (valid && r == 0) s_whist[wid][d] = before + (uint32_t)__popcll(peers);
+  }
+  __syncthreads();
+
+  // per digit: offsets of each wave inside the tile's digit run, tile count
+  const int d = tid;
+  uint32_t cnt = 0;
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t c = s_whist[w][d];
+    s_whist[w][d] = cnt;
+    cnt += c;
+  }
+  // exclusive scan of the counts over digit values -> local start of each digit
+  uint32_t x = cnt;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t t = __shfl_up(x, off);
+    if (lane >= off) x += t;
+  }
+  if (lane == kWave - 1) s_wsum[wid] = x;
+  // publish this tile's count, then look back for the exclusive prefix
+  ST* my = status + (uint64_t)tile * 256 + d;
+  if (tile == 0)
+    store_agent(my, Status<ST>::pack(kFlagInclusive, cnt));
+  else
+    store_agent(my, Status<ST>::pack(kFlagAggregate, cnt));
+  uint32_t excl = 0;
+  if (tile > 0) {
+    uint64_t t = tile - 1;
+    uint32_t spins = 0;
+    while (true) {
+      const ST w = load_agent(status + t * 256 + d);
+      const uint32_t f = Status<ST>::flag(w);
+      if (f == 0) {
+        if (++spins > kSpinLimit) {
+          atomicOr(&header[kHdrFlags], kFlagWatchdog);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        continue;
+      }
+      excl += Status<ST>::value(w);
+      if (f == kFlagInclusive || t == 0) break;
+      --t;
+    }
+    store_agent(my, Status<ST>::pack(kFlagInclusive, excl + cnt));
+  }
+  __syncthreads();
+  uint32_t pre = 0;
+  for (int i = 0; i < wid; ++i) pre += s_wsum[i];
+  const uint32_t dstart = pre + x - cnt;
+  s_dstart[d] = dstart;
+  s_gbase[d] = digit_start[d] + excl - dstart;  // modular: gbase + local index >= 0
+  __syncthreads();
+
+  // place the keys in LDS in digit order (stable)
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint64_t idx = base + (uint64_t)wid * (kWave * E) + (uint64_t)e * kWave + lane;
+    if (idx < n) {
+      const uint32_t dd = (k[e] >> shift) & 255u;
+      const uint32_t pos = s_dstart[dd] + s_whist[wid][dd] + rk[e];
+      s_keys[pos] = k[e];
+      s_vals[pos] = v[e];
+    }
+  }
+  __syncthreads();
+
+  // write out: consecutive threads write consecutive slots of a digit's run
+  const uint64_t rem = n - base;
+  const uint32_t count = rem < (uint64_t)TILE ? (uint32_t)rem : (uint32_t)TILE;
+  for (uint32_t i = tid; i < count; i += kSortBlock) {
+    const uint32_t key = s_keys[i];
+    const uint32_t val = s_vals[i];
+    const uint32_t o = s_gbase[(key >> shift) & 255u] + i;
+    if ((uint64_t)o >= n) continue;  // cannot happen for consistent counts; never write out of range
+    if (MODE == 2) {
+      kout[o] = (key == kKeyPlusZero && (uint64_t)val < n) ? a_bits[val] : key_to_float_bits(key);
+      vout[o] = val;
+    } else {
+      kout[o] = key;
+      vout[o] = val;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host side
+template <typename ST>
+static hipError_t launch_sort_passes(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,
+                                     hipStream_t s) {
+  const uint32_t* a_bits = reinterpret_cast<const uint32_t*>(a);
+  const uint64_t tiles = (n + kSortTile - 1) / kSortTile;
+  ST* st = reinterpret_cast<ST*>(w.status);
+  const uint32_t* src_k = nullptr;
+  const uint32_t* src_v = nullptr;
+  for (int p = 0; p < 4; ++p) {
+    ST* stp = st + (uint64_t)p * tiles * 256;
+    uint32_t* dk = (p == 3) ? reinterpret_cast<uint32_t*>(a_sorted) : w.keys[p & 1];
+    uint32_t* dv = (p == 3) ? perm : w.vals[p & 1];
+    if (p == 0)
+      k_onesweep<0, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(a_bits, nullptr, dk, dv, a_bits, stp, w.header, p,
+                                                                        w.offsets + p * 256, n);
+    else if (p == 3)
+      k_onesweep<2, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(src_k, src_v, dk, dv, a_bits, stp, w.header, p,
+                                                                        w.offsets + p * 256, n);
+    else
+      k_onesweep<1, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(src_k, src_v, dk, dv, a_bits, stp, w.header, p,
+                                                                        w.offsets + p * 256, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    src_k = dk;
+    src_v = dv;
+  }
+  return hipSuccess;
+}
+
+size_t sort_status_bytes(uint64_t n) {
+  const uint64_t tiles = (n + kSortTile - 1) / kSortTile;
+  const size_t word = (n <= (1ull << 30)) ? 4 : 8;
+  return (size_t)(4 * tiles * 256) * word;
+}
+
+hipError_t sort_anchors(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm, hipStream_t s) {
+  // clear the header, histograms and look-back status with a fill kernel
+  const uint64_t clear_words = (uint64_t)(kSortHeaderBytes / 4) + sort_status_bytes(n) / 4;
+  const unsigned fill_blocks = (unsigned)std::min<uint64_t>((clear_words + 255) / 256, 4096);
+  k_fill_u32<<<fill_blocks, 256, 0, s>>>(w.header, clear_words, 0u);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint64_t chunk = (uint64_t)kHistBlock * kHistItems;
+  const unsigned hist_blocks = (unsigned)std::min<uint64_t>((n + chunk - 1) / chunk, 2048);
+  k_sort_hist<<<hist_blocks, kHistBlock, 0, s>>>(reinterpret_cast<const uint32_t*>(a), n, w.hist, w.header);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  k_sort_offsets<<<1, 256, 0, s>>>(w.hist, w.offsets);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (n <= (1ull << 30)) return launch_sort_passes<uint32_t>(w, a, n, a_sorted, perm, s);
+  return launch_sort_passes<uint64_t>(w, a, n, a_sorted, perm, s);
+}
+
+}  // namespace laplex
+
+namespace laplex {
+hipError_t fill_zero_u32(void* p, uint64_t words, hipStream_t s) {
+  if (words == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<uint64_t>((words + 255) / 256, 4096);
+  k_fill_u32<<<blocks, 256, 0, s>>>(static_cast<uint32_t*>(p), words, 0u);
+  return hipGetLastError();
+}
+}  // namespace laplex

@@ -65,7 +65,9 @@ def load(path: Optional[str] = None):
         lib.lo_sym_apply.argtypes = [f32p, i64, i64, f32p, f64p]
         lib.lo_general_apply.argtypes = [f32p, i64, f32p, i64, i64, f32p, f64p]
         lib.lo_phased_apply.argtypes = [f32p, f32p, i64, f32p, f32p, i64, i64, f32p, f64p]
-        for fn in (lib.lo_stable_argsort, lib.lo_sym_apply, lib.lo_general_apply, lib.lo_phased_apply):
+        lib.lo_dense_rows.argtypes = [f32p, f32p, ctypes.POINTER(ctypes.c_int64), i64, f32p, f32p, i64, i64, f32p, f64p,
+                                      f64p]
+        for fn in (lib.lo_stable_argsort, lib.lo_sym_apply, lib.lo_general_apply, lib.lo_phased_apply, lib.lo_dense_rows):
             fn.restype = ctypes.c_int
         if path is None:
             _lib_handle = lib
@@ -144,6 +146,27 @@ def phased_apply(a, phi, x, b=None, psi=None, lib=None) -> np.ndarray:
                                _ptr(psi, ctypes.c_float), b.size, x2.shape[1], _ptr(x2, ctypes.c_float),
                                _ptr(y, ctypes.c_double)))
     return y
+
+
+def dense_rows_c(rows, a, x, b=None, phi=None, psi=None, lib=None):
+    """Rows ``rows`` of y and of K0|x| by the plain definition, in C (one pass
+    over the input anchors; for spot checks at sizes too large for NumPy
+    temporaries).  Returns (y_rows, env_rows), float64, len(rows) x m."""
+    lib = lib or load()
+    a = _f32(a).ravel()
+    bb = a if b is None else _f32(b).ravel()
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    x2 = _as2d(x, bb.size)
+    m = x2.shape[1]
+    y = np.empty((rows.size, m), np.float64)
+    env = np.empty((rows.size, m), np.float64)
+    ph = None if phi is None else _f32(phi).ravel()
+    ps = None if phi is None else (ph if psi is None else _f32(psi).ravel())
+    _check(lib.lo_dense_rows(_ptr(a, ctypes.c_float), None if ph is None else _ptr(ph, ctypes.c_float),
+                             rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), rows.size, _ptr(bb, ctypes.c_float),
+                             None if ps is None else _ptr(ps, ctypes.c_float), bb.size, m, _ptr(x2, ctypes.c_float),
+                             _ptr(y, ctypes.c_double), _ptr(env, ctypes.c_double)))
+    return y, env
 
 
 from .dense import dense_apply, dense_envelope, dense_rows, normwise_error  # noqa: E402,F401

@@ -295,3 +295,45 @@ int lo_phased_apply(const float* a, const float* phi, int64_t n, const float* b,
   free(z);
   return rc;
 }
+
+/* Selected rows of the operator by its plain definition (section 2.1), for
+ * spot checks of inputs too large for a full dense product:
+ *   y[r][c]   = sum_j exp(-|a[rows[r]] - b_j|) cos(phi - psi) x[j][c]
+ *   env[r][c] = sum_j exp(-|a[rows[r]] - b_j|) |x[j][c]|
+ * (phi/psi NULL: unphased).  Terms with |a - b| >= 746 are skipped: their
+ * weight exp(-|a - b|) underflows to exactly 0 in float64, so the sums are
+ * unchanged.  One pass over b for all rows. */
+int lo_dense_rows(const float* a, const float* phi, const int64_t* rows, int64_t nrows, const float* b, const float* psi,
+                  int64_t k, int64_t m, const float* x, double* y, double* env) {
+  if (nrows <= 0 || m <= 0) return 0;
+  double* ai = (double*)malloc(sizeof(double) * (size_t)nrows);
+  double* pi = (double*)malloc(sizeof(double) * (size_t)nrows);
+  if (!ai || !pi) {
+    free(ai);
+    free(pi);
+    return -2;
+  }
+  for (int64_t r = 0; r < nrows; ++r) {
+    ai[r] = (double)a[rows[r]];
+    pi[r] = phi ? (double)phi[rows[r]] : 0.0;
+  }
+  memset(y, 0, sizeof(double) * (size_t)(nrows * m));
+  memset(env, 0, sizeof(double) * (size_t)(nrows * m));
+  for (int64_t j = 0; j < k; ++j) {
+    const double bj = (double)b[j];
+    const float* xr = x + (size_t)j * m;
+    for (int64_t r = 0; r < nrows; ++r) {
+      const double d = fabs(ai[r] - bj);
+      if (d >= 746.0) continue;
+      const double w = exp(-d);
+      const double wc = phi ? w * cos(pi[r] - (double)psi[j]) : w;
+      for (int64_t c = 0; c < m; ++c) {
+        y[r * m + c] += wc * (double)xr[c];
+        env[r * m + c] += w * fabs((double)xr[c]);
+      }
+    }
+  }
+  free(ai);
+  free(pi);
+  return 0;
+}

@@ -394,6 +394,32 @@ def pin_brute_force_tiny(lib):
                                              odense.dense_apply(a, xb, b=b, phi=phi, psi=psi), envb) < 1e-13, "phased general"
 
 
+def pin_dense_rows_c(lib):
+    """C spot rows (plain definition, one pass) against the NumPy dense
+    oracle and the scan oracle, on anchors spread wider than the 746 cut-off."""
+    r = _rng(12)
+    n, k, m = 3000, 2500, 2
+    a = r.uniform(-2000, 2000, n).astype(np.float32)
+    a[:50] = a[50]
+    b = r.uniform(-2100, 2100, k).astype(np.float32)
+    b[:20] = a[60]
+    x = r.standard_normal((n, m)).astype(np.float32)
+    xb = r.standard_normal((k, m)).astype(np.float32)
+    phi = r.uniform(0, 6.3, n).astype(np.float32)
+    psi = r.uniform(0, 6.3, k).astype(np.float32)
+    rows = np.array([0, 1, 50, 60, 1234, n - 1])
+    y, env = oracle.dense_rows_c(rows, a, x, lib=lib)
+    _close(y, oracle.sym_apply(a, x, lib=lib)[rows], 1e-12, "C rows vs sym scan")
+    _close(env, odense.dense_envelope(a, x)[rows], 1e-12, "C rows envelope")
+    y, env = oracle.dense_rows_c(rows, a, xb, b=b, lib=lib)
+    _close(y, oracle.general_apply(a, b, xb, lib=lib)[rows], 1e-12, "C rows vs general scan")
+    _close(y, odense.dense_apply(a, xb, b=b)[rows], 1e-12, "C rows vs dense general")
+    y, env = oracle.dense_rows_c(rows, a, xb, b=b, phi=phi, psi=psi, lib=lib)
+    _close(y, odense.dense_apply(a, xb, b=b, phi=phi, psi=psi)[rows], 1e-12, "C rows phased general")
+    y, env = oracle.dense_rows_c(rows, a, x, phi=phi, lib=lib)
+    _close(y, oracle.phased_apply(a, phi, x, lib=lib)[rows], 1e-12, "C rows phased sym")
+
+
 ALL_PINS = [
     pin_sort_definition,
     pin_sort_rejects_nonfinite,
@@ -409,4 +435,5 @@ ALL_PINS = [
     pin_general_reductions,
     pin_phased,
     pin_brute_force_tiny,
+    pin_dense_rows_c,
 ]

@@ -1,0 +1,92 @@
+"""The C-ABI library: it loads, exports every symbol include/laplex.h declares,
+and rejects bad arguments on the host (no GPU work is started by any call
+here: each one fails an argument check before a launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "laplex.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(laplex_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import laplace_prefix_scans_amd as lp
+    if not os.path.exists(lp.lib_path()):
+        pytest.skip("liblaplex.so not built")
+    return lp.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for required in ("laplex_sort_anchors", "laplex_matvec_sym", "laplex_matvec_general", "laplex_matvec_phased",
+                     "laplex_workspace_bytes", "laplex_status_poll", "laplex_status_string"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_workspace_sizes(L):
+    import laplace_prefix_scans_amd as lp
+    assert lp.laplex_workspace_bytes(lp.LAPLEX_OP_SORT, 1 << 20) >= 16 * (1 << 20)
+    assert lp.laplex_workspace_bytes(lp.LAPLEX_OP_SYM, 1 << 20, 0, 16) >= 4 * 16 * (1 << 20)
+    assert lp.laplex_workspace_bytes(lp.LAPLEX_OP_PHASED, 1000, 0, 3) > lp.laplex_workspace_bytes(lp.LAPLEX_OP_SYM, 1000, 0, 3)
+    assert lp.laplex_workspace_bytes(lp.LAPLEX_OP_GENERAL, 1 << 24, 1 << 16, 1) > 0
+    assert lp.laplex_workspace_bytes(lp.LAPLEX_OP_SORT, 1 << 32) == 0  # n out of range
+    assert lp.laplex_workspace_bytes(99, 10) == 0
+    for op in range(5):
+        a = lp.laplex_workspace_bytes(op, 4096, 100, 1)
+        b = lp.laplex_workspace_bytes(op, 1 << 22, 1 << 20, 1)
+        assert a % 256 == 0 and b % 256 == 0 and b >= a
+
+
+def test_host_argument_errors(L):
+    vp = ctypes.c_void_p
+    A = vp(0x100000)      # never dereferenced: every call below fails a check first
+    B = vp(0x200000)
+    W = vp(0x400000)
+    OK, NULL, SIZE, ALIGN, WS, OVERLAP = 0, 1, 2, 3, 4, 7
+    # n == 0 / m == 0 are no-ops
+    assert L.laplex_sort_anchors(None, 0, None, None, None, 0, None) == OK
+    assert L.laplex_matvec_sym(None, None, 0, 1, None, None, None, 0, None) == OK
+    assert L.laplex_matvec_sym(A, B, 10, 0, A, B, W, 0, None) == OK
+    # NULL
+    assert L.laplex_sort_anchors(None, 10, B, A, W, 1 << 30, None) == NULL
+    assert L.laplex_matvec_sym(A, B, 10, 1, None, B, W, 1 << 30, None) == NULL
+    assert L.laplex_status_poll(None, None) == NULL
+    # size
+    assert L.laplex_sort_anchors(A, 1 << 32, B, A, W, 1 << 40, None) == SIZE
+    assert L.laplex_matvec_sym(A, B, 1 << 32, 1, A, B, W, 1 << 40, None) == SIZE
+    # alignment
+    assert L.laplex_sort_anchors(vp(0x100002), 10, B, vp(0x300000), W, 1 << 30, None) == ALIGN
+    assert L.laplex_sort_anchors(A, 10, B, vp(0x300000), vp(0x400010), 1 << 30, None) == ALIGN
+    # workspace too small
+    assert L.laplex_sort_anchors(A, 1000, B, vp(0x300000), W, 64, None) == WS
+    assert L.laplex_matvec_sym(A, vp(0x300000), 1000, 4, vp(0x500000), vp(0x600000), W, 64, None) == WS
+    # overlap: y on top of x
+    need = L.laplex_workspace_bytes(1, 1000, 0, 1)
+    assert L.laplex_matvec_sym(A, vp(0x300000), 1000, 1, vp(0x500000), vp(0x500100), vp(0x10000000), need, None) == OVERLAP
+    assert L.laplex_sort_anchors(A, 1000, vp(0x100100), vp(0x300000), vp(0x10000000), 1 << 30, None) == OVERLAP
+    # general without b
+    need = L.laplex_workspace_bytes(2, 100, 50, 1)
+    assert L.laplex_matvec_general(A, vp(0x300000), 100, None, None, 50, 1, vp(0x500000), vp(0x600000), W, need, None) == NULL
+    assert L.laplex_matvec_phased(A, vp(0x300000), None, 100, None, None, None, 0, 1, vp(0x500000), vp(0x600000), W, need,
+                                  None) == NULL
+    assert L.laplex_status_string(4) == b"workspace too small"
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    import laplace_prefix_scans_amd as lp
+    with pytest.raises((ValueError, RuntimeError)):
+        lp.laplex_sort_anchors(torch.zeros(8))

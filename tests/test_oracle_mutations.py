@@ -40,6 +40,9 @@ C_MUTANTS = [
     ("phased_diagonal_twice", "if (sym) w -= cexp(", "if (0) w -= cexp(", 0),
     ("phased_general_psi_unsorted", "cexp(-I * (double)psi[pb[j]]);", "cexp(-I * (double)psi[j]);", 0),
     ("phased_general_u_weight", "double w = exp(bj - as[p]);", "double w = exp(as[p] - bj);", 1),
+    ("rows_cutoff_too_small", "if (d >= 746.0) continue;", "if (d >= 7.0) continue;", 0),
+    ("rows_phase_sign", "cos(pi[r] - (double)psi[j])", "cos(pi[r] + (double)psi[j])", 0),
+    ("rows_envelope_signed", "env[r * m + c] += w * fabs((double)xr[c]);", "env[r * m + c] += w * (double)xr[c];", 0),
 ]
 
 
