@@ -22,9 +22,10 @@
  *    (unsorted) order of their anchors.
  *  - Work is enqueued on `stream` and is asynchronous: argument errors are
  *    returned synchronously, nothing is waited on.  The library allocates no
- *    memory and keeps no global state; each call needs its own workspace of
- *    at least laplex_workspace_bytes(...) bytes (256-byte aligned), and calls
- *    whose workspaces differ may run concurrently on different streams.
+ *    device memory and keeps no global state (apart from the opt-in launch
+ *    profiler at the end of this header); each call needs its own workspace
+ *    of at least laplex_workspace_bytes(...) bytes (256-byte aligned), and
+ *    calls whose workspaces differ may run concurrently on different streams.
  *  - Outputs must not overlap inputs or the workspace.
  *  - n, k < 2^32 (permutations are uint32).  n == 0 or m == 0 is a no-op.
  */
@@ -118,6 +119,19 @@ laplex_status laplex_matvec_phased(const float* a_sorted, const uint32_t* perm_a
 
 /* Short English description of a status code (static storage). */
 const char* laplex_status_string(laplex_status s);
+
+/* Opt-in launch profiler (diagnostics; not for use under stream capture).
+ * laplex_profile_begin enables it for up to `capacity` kernel launches: each
+ * kernel the library launches from then on is bracketed by two hipEvents
+ * recorded on the stream it is launched on (events are created on the host
+ * here, once).  laplex_profile_end disables it and returns the number of
+ * launches recorded.  laplex_profile_get waits for record i and returns the
+ * kernel's name (static storage) and its duration in milliseconds.  The
+ * profiler is process-wide state guarded by a mutex; while disabled it costs
+ * one relaxed atomic load per launch. */
+laplex_status laplex_profile_begin(uint32_t capacity);
+uint32_t laplex_profile_end(void);
+laplex_status laplex_profile_get(uint32_t i, const char** name, float* ms);
 
 #ifdef __cplusplus
 }

@@ -25,5 +25,6 @@ from ._binding import (  # noqa: F401
     laplex_sort_anchors,
     laplex_status_poll,
     laplex_workspace_bytes,
+    profile_launches,
     workspace,
 )

@@ -55,6 +55,12 @@ def lib():
             f.restype = i32
         L.laplex_status_string.argtypes = [i32]
         L.laplex_status_string.restype = ctypes.c_char_p
+        L.laplex_profile_begin.argtypes = [u32]
+        L.laplex_profile_begin.restype = i32
+        L.laplex_profile_end.argtypes = []
+        L.laplex_profile_end.restype = u32
+        L.laplex_profile_get.argtypes = [u32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float)]
+        L.laplex_profile_get.restype = i32
         _lib = L
         return L
 
@@ -196,3 +202,31 @@ def laplex_matvec_phased(a_sorted: torch.Tensor, perm_a: torch.Tensor, phi: torc
     _check(lib().laplex_matvec_phased(_ptr(a_sorted), _ptr(perm_a), _ptr(phi), n, _ptr(b_sorted), _ptr(perm_b), _ptr(psi), k, m,
                                       _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(dev)), "laplex_matvec_phased")
     return y
+
+
+class profile_launches:
+    """Context manager recording the duration of every kernel the library
+    launches inside it (HIP events on each launch's stream).
+
+        with profile_launches() as prof:
+            ...
+        prof.records  # [(kernel name, ms), ...] in launch order
+    """
+
+    def __init__(self, capacity: int = 65536):
+        self.capacity = capacity
+        self.records = []
+
+    def __enter__(self):
+        _check(lib().laplex_profile_begin(self.capacity), "laplex_profile_begin")
+        return self
+
+    def __exit__(self, *exc):
+        L = lib()
+        cnt = L.laplex_profile_end()
+        name, ms = ctypes.c_char_p(), ctypes.c_float()
+        self.records = []
+        for i in range(cnt):
+            _check(L.laplex_profile_get(i, ctypes.byref(name), ctypes.byref(ms)), "laplex_profile_get")
+            self.records.append((name.value.decode(), float(ms.value)))
+        return False

@@ -226,3 +226,64 @@ extern "C" const char* laplex_status_string(laplex_status s) {
   }
   return "unknown status";
 }
+
+// ------------------------------------------------------------------ opt-in launch profiler
+#include <atomic>
+#include <mutex>
+#include <vector>
+
+namespace {
+std::mutex g_prof_mu;
+std::atomic<bool> g_prof_on{false};
+std::vector<hipEvent_t> g_prof_ev;       // 2 per record: before, after
+std::vector<const char*> g_prof_names;
+uint32_t g_prof_cap = 0, g_prof_cnt = 0;
+}  // namespace
+
+namespace laplex {
+int prof_begin(hipStream_t s) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return -1;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (g_prof_cnt >= g_prof_cap) return -1;
+  const int slot = (int)g_prof_cnt++;
+  if (hipEventRecord(g_prof_ev[2 * slot], s) != hipSuccess) return -1;
+  return slot;
+}
+void prof_end(int slot, const char* name, hipStream_t s) {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_names[slot] = name;
+  (void)hipEventRecord(g_prof_ev[2 * slot + 1], s);
+}
+}  // namespace laplex
+
+extern "C" laplex_status laplex_profile_begin(uint32_t capacity) {
+  if (capacity == 0 || capacity > (1u << 20)) return LAPLEX_ERR_ARG;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  while (g_prof_ev.size() < 2 * (size_t)capacity) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return LAPLEX_ERR_HIP;
+    g_prof_ev.push_back(e);
+  }
+  g_prof_names.assign(capacity, nullptr);
+  g_prof_cap = capacity;
+  g_prof_cnt = 0;
+  g_prof_on.store(true);
+  return LAPLEX_OK;
+}
+
+extern "C" uint32_t laplex_profile_end(void) {
+  g_prof_on.store(false);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  return g_prof_cnt;
+}
+
+extern "C" laplex_status laplex_profile_get(uint32_t i, const char** name, float* ms) {
+  if (!name || !ms) return LAPLEX_ERR_NULL;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (i >= g_prof_cnt) return LAPLEX_ERR_ARG;
+  if (hipEventSynchronize(g_prof_ev[2 * i + 1]) != hipSuccess) return LAPLEX_ERR_HIP;
+  if (hipEventElapsedTime(ms, g_prof_ev[2 * i], g_prof_ev[2 * i + 1]) != hipSuccess) return LAPLEX_ERR_HIP;
+  *name = g_prof_names[i];
+  return LAPLEX_OK;
+}

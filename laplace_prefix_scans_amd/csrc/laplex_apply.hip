@@ -432,13 +432,16 @@ static hipError_t run_sym(const ApplyWorkspace& w, const float* a_s, const uint3
   constexpr int P = apply_tile(CC);
   const uint64_t T = (n + P - 1) / P;
   const uint32_t M = PH ? 2 * m : m;
-  k_sym_gather_reduce<C, PH><<<dim3((unsigned)T), dim3(kApplyBlock), 0, s>>>(a_s, perm, phi, x, n, m, w.xs, w.phs, w.bf, w.bb,
-                                                                              w.tanch);
+  LAPLEX_LAUNCH(PH ? "k_phased_gather_reduce" : "k_sym_gather_reduce", s,
+                k_sym_gather_reduce<C, PH><<<dim3((unsigned)T), dim3(kApplyBlock), 0, s>>>(a_s, perm, phi, x, n, m, w.xs, w.phs,
+                                                                                            w.bf, w.bb, w.tanch));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_tile_carry<<<1, kCarryBlock, 0, s>>>(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb);
+  LAPLEX_LAUNCH("k_tile_carry", s, k_tile_carry<<<1, kCarryBlock, 0, s>>>(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  k_sym_apply<C, PH><<<dim3((unsigned)T), dim3(kApplyBlock), 0, s>>>(a_s, perm, w.xs, w.phs, w.cf, w.cb, w.tanch, n, m, T, y);
+  LAPLEX_LAUNCH(PH ? "k_phased_apply" : "k_sym_apply", s,
+                k_sym_apply<C, PH><<<dim3((unsigned)T), dim3(kApplyBlock), 0, s>>>(a_s, perm, w.xs, w.phs, w.cf, w.cb, w.tanch, n,
+                                                                                    m, T, y));
   return hipGetLastError();
 }
 
@@ -672,16 +675,18 @@ static hipError_t run_general(const ApplyWorkspace& w, const float* a_s, const u
   const uint64_t T = (n + k + P - 1) / P;
   const uint32_t M = PH ? 2 * m : m;
   const unsigned gblocks = (unsigned)std::min<uint64_t>((k + 255) / 256, 8192);
-  k_gather_rows<<<gblocks, 256, 0, s>>>(x, perm_b, PH ? psi : nullptr, k, m, w.xs, w.phs);
+  LAPLEX_LAUNCH("k_gather_rows", s, k_gather_rows<<<gblocks, 256, 0, s>>>(x, perm_b, PH ? psi : nullptr, k, m, w.xs, w.phs));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_gen_reduce<C, PH><<<dim3((unsigned)T), dim3(kApplyBlock), 0, s>>>(a_s, n, b_s, k, w.xs, w.phs, m, T, w.bf, w.bb, w.tanch,
-                                                                       w.tsplit);
+  LAPLEX_LAUNCH(PH ? "k_phased_gen_reduce" : "k_gen_reduce", s,
+                k_gen_reduce<C, PH><<<dim3((unsigned)T), dim3(kApplyBlock), 0, s>>>(a_s, n, b_s, k, w.xs, w.phs, m, T, w.bf, w.bb,
+                                                                                     w.tanch, w.tsplit));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  k_tile_carry<<<1, kCarryBlock, 0, s>>>(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb);
+  LAPLEX_LAUNCH("k_tile_carry", s, k_tile_carry<<<1, kCarryBlock, 0, s>>>(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  k_gen_apply<C, PH><<<dim3((unsigned)T), dim3(kApplyBlock), 0, s>>>(a_s, perm_a, phi, n, b_s, k, w.xs, w.phs, m, T, w.cf, w.cb,
-                                                                      w.tanch, w.tsplit, y);
+  LAPLEX_LAUNCH(PH ? "k_phased_gen_apply" : "k_gen_apply", s,
+                k_gen_apply<C, PH><<<dim3((unsigned)T), dim3(kApplyBlock), 0, s>>>(a_s, perm_a, phi, n, b_s, k, w.xs, w.phs, m, T,
+                                                                                    w.cf, w.cb, w.tanch, w.tsplit, y));
   return hipGetLastError();
 }
 

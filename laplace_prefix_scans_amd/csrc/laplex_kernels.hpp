@@ -9,6 +9,18 @@
 
 namespace laplex {
 
+// ------------------------------------------------------------------ opt-in launch profiler
+// When enabled through laplex_profile_begin, each kernel launch is bracketed
+// by two hipEvents recorded on its stream; otherwise these are no-ops.
+int prof_begin(hipStream_t s);
+void prof_end(int slot, const char* name, hipStream_t s);
+#define LAPLEX_LAUNCH(NAME, STREAM, ...)                \
+  do {                                                  \
+    const int prof_slot_ = ::laplex::prof_begin(STREAM); \
+    __VA_ARGS__;                                        \
+    ::laplex::prof_end(prof_slot_, (NAME), (STREAM));   \
+  } while (0)
+
 // ------------------------------------------------------------------ sort
 constexpr int kSortBlock = 256;
 constexpr int kSortItems = 16;

@@ -258,14 +258,17 @@ static hipError_t launch_sort_passes(const SortWorkspace& w, const float* a, uin
     uint32_t* dk = (p == 3) ? reinterpret_cast<uint32_t*>(a_sorted) : w.keys[p & 1];
     uint32_t* dv = (p == 3) ? perm : w.vals[p & 1];
     if (p == 0)
-      k_onesweep<0, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(a_bits, nullptr, dk, dv, a_bits, stp, w.header, p,
-                                                                        w.offsets + p * 256, n);
+      LAPLEX_LAUNCH("k_onesweep_first", s,
+                    k_onesweep<0, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(
+                        a_bits, nullptr, dk, dv, a_bits, stp, w.header, p, w.offsets + p * 256, n));
     else if (p == 3)
-      k_onesweep<2, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(src_k, src_v, dk, dv, a_bits, stp, w.header, p,
-                                                                        w.offsets + p * 256, n);
+      LAPLEX_LAUNCH("k_onesweep_last", s,
+                    k_onesweep<2, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(
+                        src_k, src_v, dk, dv, a_bits, stp, w.header, p, w.offsets + p * 256, n));
     else
-      k_onesweep<1, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(src_k, src_v, dk, dv, a_bits, stp, w.header, p,
-                                                                        w.offsets + p * 256, n);
+      LAPLEX_LAUNCH("k_onesweep_mid", s,
+                    k_onesweep<1, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(
+                        src_k, src_v, dk, dv, a_bits, stp, w.header, p, w.offsets + p * 256, n));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     src_k = dk;
@@ -284,14 +287,15 @@ hipError_t sort_anchors(const SortWorkspace& w, const float* a, uint64_t n, floa
   // clear the header, histograms and look-back status with a fill kernel
   const uint64_t clear_words = (uint64_t)(kSortHeaderBytes / 4) + sort_status_bytes(n) / 4;
   const unsigned fill_blocks = (unsigned)std::min<uint64_t>((clear_words + 255) / 256, 4096);
-  k_fill_u32<<<fill_blocks, 256, 0, s>>>(w.header, clear_words, 0u);
+  LAPLEX_LAUNCH("k_fill_u32", s, k_fill_u32<<<fill_blocks, 256, 0, s>>>(w.header, clear_words, 0u));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint64_t chunk = (uint64_t)kHistBlock * kHistItems;
   const unsigned hist_blocks = (unsigned)std::min<uint64_t>((n + chunk - 1) / chunk, 2048);
-  k_sort_hist<<<hist_blocks, kHistBlock, 0, s>>>(reinterpret_cast<const uint32_t*>(a), n, w.hist, w.header);
+  LAPLEX_LAUNCH("k_sort_hist", s,
+                k_sort_hist<<<hist_blocks, kHistBlock, 0, s>>>(reinterpret_cast<const uint32_t*>(a), n, w.hist, w.header));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  k_sort_offsets<<<1, 256, 0, s>>>(w.hist, w.offsets);
+  LAPLEX_LAUNCH("k_sort_offsets", s, k_sort_offsets<<<1, 256, 0, s>>>(w.hist, w.offsets));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (n <= (1ull << 30)) return launch_sort_passes<uint32_t>(w, a, n, a_sorted, perm, s);
   return launch_sort_passes<uint64_t>(w, a, n, a_sorted, perm, s);
@@ -303,7 +307,7 @@ namespace laplex {
 hipError_t fill_zero_u32(void* p, uint64_t words, hipStream_t s) {
   if (words == 0) return hipSuccess;
   const unsigned blocks = (unsigned)std::min<uint64_t>((words + 255) / 256, 4096);
-  k_fill_u32<<<blocks, 256, 0, s>>>(static_cast<uint32_t*>(p), words, 0u);
+  LAPLEX_LAUNCH("k_fill_u32", s, k_fill_u32<<<blocks, 256, 0, s>>>(static_cast<uint32_t*>(p), words, 0u));
   return hipGetLastError();
 }
 }  // namespace laplex

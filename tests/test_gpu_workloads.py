@@ -1,0 +1,104 @@
+"""GPU parity at the five workload sizes, in the launch configuration the
+benchmark times (sort + apply through the C-ABI).
+
+Up to n = 3*2^20 the whole output is compared with the float64 oracle and the
+permutation bit for bit with the oracle's stable argsort.  At n = 2^30 the
+permutation is checked through the properties that determine the stable
+argsort uniquely, and y on rows the oracle computes one by one by the plain
+definition (including the extreme anchors and rows on tile boundaries of the
+sorted order), plus the symmetry <u, K v> = <K u, v>.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import TOL, assert_perm_is_stable_argsort, dev, have_gpu, host
+from synth import make_workload
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+
+def _run(w):
+    import laplace_prefix_scans_amd as lp
+    a_d = dev(w.a)
+    a_s, pa = lp.laplex_sort_anchors(a_d, check=True)
+    out = {"a_s": a_s, "pa": pa}
+    if w.kind == "general":
+        b_s, pb = lp.laplex_sort_anchors(dev(w.b), check=True)
+        out.update(b_s=b_s, pb=pb)
+        out["y"] = lp.laplex_matvec_general(a_s, pa, b_s, pb, dev(w.x))
+    elif w.kind == "phased":
+        out["y"] = lp.laplex_matvec_phased(a_s, pa, dev(w.phi), dev(w.x))
+    else:
+        out["y"] = lp.laplex_matvec_sym(a_s, pa, dev(w.x))
+    return out
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", ["sym4096", "sym2p20m16", "gen2p24k2p16", "phased3x1024x1024m8"])
+def test_workload_full_parity(name):
+    w = make_workload(name)
+    print("workload", name, "n", w.n, "m", w.m, "k", w.k, flush=True)
+    out = _run(w)
+    pa = host(out["pa"])
+    assert np.array_equal(pa, oracle.stable_argsort(w.a)), "perm(a) differs"
+    assert np.array_equal(host(out["a_s"]).view(np.uint32), w.a[pa].view(np.uint32))
+    y = host(out["y"])
+    if w.kind == "general":
+        assert np.array_equal(host(out["pb"]), oracle.stable_argsort(w.b)), "perm(b) differs"
+        ref = oracle.general_apply(w.a, w.b, w.x)
+        env = oracle.general_apply(w.a, w.b, np.abs(w.x))
+    elif w.kind == "phased":
+        ref = oracle.phased_apply(w.a, w.phi, w.x)
+        env = oracle.sym_apply(w.a, np.abs(w.x))
+    elif w.n <= 4096:
+        ref = oracle.dense_apply(w.a, w.x)
+        env = oracle.dense_envelope(w.a, w.x)
+    else:
+        ref = oracle.sym_apply(w.a, w.x)
+        env = oracle.sym_apply(w.a, np.abs(w.x))
+    err = oracle.normwise_error(y, ref, env)
+    print("normwise error %.3e" % err, flush=True)
+    assert err <= TOL
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_workload_sym2p30_sampled():
+    import torch
+    import laplace_prefix_scans_amd as lp
+    w = make_workload("sym2p30")
+    print("generated n=%d" % w.n, flush=True)
+    a_d = dev(w.a)
+    x_d = dev(w.x)
+    a_s, pa = lp.laplex_sort_anchors(a_d, check=True)
+    y_d = lp.laplex_matvec_sym(a_s, pa, x_d)
+    torch.cuda.synchronize()
+    print("gpu done", flush=True)
+    perm = host(pa)
+    assert_perm_is_stable_argsort(w.a, perm, host(a_s))
+    print("perm properties ok", flush=True)
+    y = host(y_d)
+    r = np.random.default_rng(2024)
+    P = 4096
+    rows = np.unique(np.concatenate([
+        perm[[0, 1, P - 1, P, 2 * P - 1, w.n // 2, w.n - P, w.n - 1]].astype(np.int64),
+        r.integers(0, w.n, 8),
+    ]))
+    y_ref, env = oracle.dense_rows_c(rows, w.a, w.x)
+    # sampled rows give a lower bound on ||K0|x|||_inf: a stricter denominator
+    err = oracle.normwise_error(y[rows], y_ref, env, env_scale=np.max(env, axis=0))
+    print("sampled normwise error %.3e over %d rows" % (err, rows.size), flush=True)
+    assert err <= TOL
+    # symmetry of the operator at full size
+    del y, y_d
+    u = torch.randn(w.n, device="cuda", generator=torch.Generator(device="cuda").manual_seed(5))
+    v = torch.randn(w.n, device="cuda", generator=torch.Generator(device="cuda").manual_seed(6))
+    ku = lp.laplex_matvec_sym(a_s, pa, u)
+    kv = lp.laplex_matvec_sym(a_s, pa, v)
+    kabs = lp.laplex_matvec_sym(a_s, pa, v.abs())
+    lhs = float(torch.dot(u.double(), kv.double()))
+    rhs = float(torch.dot(ku.double(), v.double()))
+    scale = float(torch.dot(u.abs().double(), kabs.double()))
+    print("symmetry |lhs-rhs|/scale = %.3e" % (abs(lhs - rhs) / scale), flush=True)
+    assert abs(lhs - rhs) <= TOL * scale
