@@ -44,30 +44,41 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_bytes(name: str, units: int, m: int, k_units: int = 0) -> float:
+def kernel_bytes(name: str, units: int, m: int, k: int = 0) -> float:
     """Algorithmic bytes of one launch: every array the kernel must touch, once,
-    at its useful size (random row accesses count their 4m useful bytes).
-    ``units`` = elements the launch processes (n, or k for b-side kernels)."""
-    if name == "k_sort_hist":
-        return 4.0 * units
-    if name == "k_onesweep_first":
-        return 12.0 * units          # read anchors; write keys and indices
-    if name in ("k_onesweep_mid", "k_onesweep_last"):
-        return 16.0 * units          # read and write key + value
-    if name == "k_sym_gather_reduce":
-        return (8.0 + 8.0 * m) * units   # perm, sorted anchors, x rows in, sorted rows out
-    if name == "k_sym_apply":
-        return (8.0 + 8.0 * m) * units   # sorted anchors, perm, sorted rows in, y rows out
-    if name == "k_phased_gather_reduce":
-        return (16.0 + 8.0 * m) * units  # + phase gathered and stored
-    if name == "k_phased_apply":
-        return (12.0 + 8.0 * m) * units  # + sorted phase
-    if name == "k_gather_rows":
-        return (4.0 + 8.0 * m) * units
-    if name == "k_gen_reduce":
-        return (4.0 + 4.0 * m) * units
+    at its useful size (a random row access counts its 4m useful bytes).
+    ``units`` = elements (rows) the launch processes; ``k`` = input anchors of
+    the general operator."""
+    route = 2.0 + 1536.0 / 4096.0   # u16 position per element + 1.5 KiB of digit tables per 4096-element tile
+    table = {
+        "k_sort_hist": 4.0,                      # read anchors
+        "k_onesweep_first": 12.0,                # read anchors; write keys and indices
+        "k_onesweep_mid": 16.0,                  # read and write key + value
+        "k_onesweep_last": 16.0,
+        "k_onesweep_first_routed": 12.0 + route,
+        "k_onesweep_mid_routed": 16.0 + route,
+        "k_onesweep_last_routed": 16.0 + route,
+        "k_sym_gather_reduce": 8.0 + 8.0 * m,    # perm, sorted anchors, x rows in (random), sorted rows out
+        "k_sym_apply": 8.0 + 8.0 * m,            # sorted anchors, perm, sorted rows in, y rows out (random)
+        "k_sym_reduce": 4.0 + 4.0 * m,           # sorted anchors, sorted rows
+        "k_sym_apply_sorted": 4.0 + 8.0 * m,     # sorted anchors, sorted rows in, sorted rows out
+        "k_phased_gather_reduce": 16.0 + 8.0 * m,
+        "k_phased_apply": 12.0 + 8.0 * m,
+        "k_phased_reduce": 8.0 + 4.0 * m,
+        "k_phased_apply_sorted": 8.0 + 8.0 * m,
+        "k_gather_rows": 4.0 + 8.0 * m,
+        "k_gen_reduce": 4.0 + 4.0 * m,
+        "k_phased_gen_reduce": 8.0 + 4.0 * m,
+    }
+    for w in (1, 2, 3, 4):
+        table["k_route_fwd_w%d" % w] = route + 8.0 * w   # position, row in, row out
+        table["k_route_inv_w%d" % w] = route + 8.0 * w
+    if name in table:
+        return table[name] * units
     if name in ("k_gen_apply", "k_phased_gen_apply"):
-        return (8.0 + 4.0 * m) * units + (4.0 + 4.0 * m) * k_units
+        return (8.0 + 4.0 * m) * units + (4.0 + 4.0 * m) * k
+    if name in ("k_gen_apply_sorted", "k_phased_gen_apply_sorted"):
+        return (4.0 + 4.0 * m) * units + (4.0 + 4.0 * m) * k
     return 0.0
 
 
@@ -138,6 +149,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="sym2p30")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-route", action="store_true", help="move x and y by index instead of along the sort route")
     ap.add_argument("--cpu-sample-log2", type=int, default=25)
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (counter calibration)")
@@ -158,8 +170,10 @@ def main():
     w = make_workload(args.workload)
     t_gen = time.perf_counter() - t_gen
     n, m, k = w.n, w.m, w.k
+    use_route = m <= 4 and not args.no_route
     a = torch.from_numpy(w.a).to(dev)
     x = torch.from_numpy(w.x).to(dev)
+    ra = lp.route_buffer(n, device=dev) if use_route else None
     a_s = torch.empty_like(a)
     pa = torch.empty(n, dtype=torch.uint32, device=dev)
     ws_sort_a = lp.workspace(lp.LAPLEX_OP_SORT, n, device=dev)
@@ -168,6 +182,7 @@ def main():
         b = torch.from_numpy(w.b).to(dev)
         b_s = torch.empty_like(b)
         pb = torch.empty(k, dtype=torch.uint32, device=dev)
+        rb = lp.route_buffer(k, device=dev) if use_route else None
         ws_sort_b = lp.workspace(lp.LAPLEX_OP_SORT, k, device=dev)
         ws_apply = lp.workspace(lp.LAPLEX_OP_GENERAL, n, k, m, device=dev)
     elif w.kind == "phased":
@@ -178,14 +193,14 @@ def main():
     del w.a, w.x
 
     def step():
-        lp.laplex_sort_anchors(a, a_s, pa, ws=ws_sort_a)
+        lp.laplex_sort_anchors(a, a_s, pa, route=ra, ws=ws_sort_a)
         if w.kind == "general":
-            lp.laplex_sort_anchors(b, b_s, pb, ws=ws_sort_b)
-            lp.laplex_matvec_general(a_s, pa, b_s, pb, x, y=y, ws=ws_apply)
+            lp.laplex_sort_anchors(b, b_s, pb, route=rb, ws=ws_sort_b)
+            lp.laplex_matvec_general(a_s, pa, b_s, pb, x, y=y, ws=ws_apply, route_a=ra, route_b=rb)
         elif w.kind == "phased":
-            lp.laplex_matvec_phased(a_s, pa, phi, x, y=y, ws=ws_apply)
+            lp.laplex_matvec_phased(a_s, pa, phi, x, y=y, ws=ws_apply, route_a=ra)
         else:
-            lp.laplex_matvec_sym(a_s, pa, x, y=y, ws=ws_apply)
+            lp.laplex_matvec_sym(a_s, pa, x, y=y, ws=ws_apply, route=ra)
 
     for _ in range(args.warmup):
         step()
@@ -202,23 +217,13 @@ def main():
         torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    # per-kernel statistics from the launch events, attributing sizes by call
-    per_step = len(prof.records) // max(1, args.steps)
-    seq = prof.records[:per_step]
-    sort_launches = 7
+    # per-kernel statistics from the launch events (each records its element count)
     stats = {}
-    for i, (name, _) in enumerate(prof.records):
-        j = i % per_step
-        if w.kind == "general" and sort_launches <= j < 2 * sort_launches:
-            units, ku = k, 0
-        else:
-            units, ku = n, k
-        if name in ("k_gather_rows", "k_gen_reduce", "k_phased_gen_reduce"):
-            units = k
-        s = stats.setdefault(name, {"ms": 0.0, "launches": 0, "bytes": 0.0})
-        s["ms"] += prof.records[i][1]
-        s["launches"] += 1
-        s["bytes"] += kernel_bytes(name, units, m, ku)
+    for name, ms, units in prof.records:
+        s_ = stats.setdefault(name, {"ms": 0.0, "launches": 0, "bytes": 0.0})
+        s_["ms"] += ms
+        s_["launches"] += 1
+        s_["bytes"] += kernel_bytes(name, units, m, k)
     kernels = {}
     for name, s in stats.items():
         avg = s["ms"] / s["launches"]
@@ -261,7 +266,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "kind": w.kind, "n": n, "m": m, "k": k if w.kind == "general" else None,
-                   "step": "sort + apply", "recipe": w.recipe},
+                   "step": "sort + apply", "route": use_route, "recipe": w.recipe},
         "roofline": roofline,
         "step_alg_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "kernels": kernels,

@@ -67,17 +67,26 @@ enum {
  * the sizes are out of range. */
 size_t laplex_workspace_bytes(int op, uint64_t n, uint64_t k, uint32_t m);
 
+/* Bytes of the optional sort route for n anchors (see laplex_sort_anchors);
+ * 0 when n is out of range. */
+size_t laplex_route_bytes(uint64_t n);
+
 /* Sort of the anchors ("after sorting the anchors", section 2.2, symmetric
  * case): perm[r] is the input index of the r-th smallest anchor and
  * a_sorted[r] = a[perm[r]] bit for bit.  The order is ascending and stable
  * (equal anchors keep their input order; -0.0 and +0.0 count as equal).
- * The pair (a_sorted, perm) is the sort handle every apply takes, so one sort
- * serves any number of applies.  NaN/Inf anchors leave the outputs undefined
- * and raise LAPLEX_ERR_NONFINITE in laplex_status_poll(ws).
+ * The triple (a_sorted, perm, route) is the sort handle every apply takes, so
+ * one sort serves any number of applies.  NaN/Inf anchors leave the outputs
+ * undefined and raise LAPLEX_ERR_NONFINITE in laplex_status_poll(ws).
  * a: n floats (input); a_sorted: n floats (output); perm: n uint32 (output);
+ * route: NULL, or a device buffer of laplex_route_bytes(n) bytes (256-byte
+ * aligned, output) that records, for each of the four radix passes, where
+ * every element went; an apply given the route moves x into sorted order and
+ * y back along it with coalesced passes instead of per-element gathers and
+ * scatters through perm (used when m <= 4; the results are bitwise the same);
  * ws: workspace of laplex_workspace_bytes(LAPLEX_OP_SORT, n, 0, 1) bytes. */
-laplex_status laplex_sort_anchors(const float* a, uint64_t n, float* a_sorted, uint32_t* perm, void* ws, size_t ws_bytes,
-                                  hipStream_t stream);
+laplex_status laplex_sort_anchors(const float* a, uint64_t n, float* a_sorted, uint32_t* perm, void* route, size_t route_bytes,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Waits for `stream`, then returns the sticky device-side status of the last
  * sort that used `ws` (LAPLEX_OK, LAPLEX_ERR_NONFINITE or LAPLEX_ERR_STALLED). */
@@ -86,36 +95,37 @@ laplex_status laplex_status_poll(const void* ws, hipStream_t stream);
 /* Symmetric operator y = LAPLEX(a, a) x (section 2.2, symmetric case: lower
  * part by a prefix scan y_i = x_i + exp(a_{i-1} - a_i) y_{i-1}, upper part by
  * the mirrored suffix scan, combined as lower + upper - diagonal).
- * a_sorted, perm: the sort handle of a (n each); x: n x m (input, original
- * order); y: n x m (output, original order);
+ * a_sorted, perm, route: the sort handle of a (n each; route may be NULL);
+ * x: n x m (input, original order); y: n x m (output, original order);
  * ws: laplex_workspace_bytes(LAPLEX_OP_SYM, n, 0, m) bytes. */
-laplex_status laplex_matvec_sym(const float* a_sorted, const uint32_t* perm, uint64_t n, uint32_t m, const float* x, float* y,
-                                void* ws, size_t ws_bytes, hipStream_t stream);
+laplex_status laplex_matvec_sym(const float* a_sorted, const uint32_t* perm, const void* route, uint64_t n, uint32_t m,
+                                const float* x, float* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* General operator y = LAPLEX(a, b) x with a != b (section 2.2, general case:
  * the input anchors b are placed into the intervals of the sorted output
  * anchors a and propagated with the same scan primitive; here the two sorted
  * sequences are merged, b before a on equal anchors, and scanned once in
  * each direction).  A b anchor equal to an a anchor couples with weight 1.
- * a_sorted, perm_a: sort handle of a (n); b_sorted, perm_b: sort handle of b
- * (k); x: k x m (input); y: n x m (output);
- * ws: laplex_workspace_bytes(LAPLEX_OP_GENERAL, n, k, m) bytes.
- * k == 0 sets y to zero. */
-laplex_status laplex_matvec_general(const float* a_sorted, const uint32_t* perm_a, uint64_t n, const float* b_sorted,
-                                    const uint32_t* perm_b, uint64_t k, uint32_t m, const float* x, float* y, void* ws,
-                                    size_t ws_bytes, hipStream_t stream);
+ * a_sorted, perm_a, route_a: sort handle of a (n); b_sorted, perm_b, route_b:
+ * sort handle of b (k); either route may be NULL; x: k x m (input);
+ * y: n x m (output); ws: laplex_workspace_bytes(LAPLEX_OP_GENERAL, n, k, m)
+ * bytes.  k == 0 sets y to zero. */
+laplex_status laplex_matvec_general(const float* a_sorted, const uint32_t* perm_a, const void* route_a, uint64_t n,
+                                    const float* b_sorted, const uint32_t* perm_b, const void* route_b, uint64_t k, uint32_t m,
+                                    const float* x, float* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Phased operator y = LAPLEX(a, phi; b, psi) x (section 2.1, phased
  * extension), computed as two real scans of the columns cos(psi) x and
  * sin(psi) x, recombined with cos(phi) and sin(phi)
  * (cos(phi_i - psi_j) = cos phi_i cos psi_j + sin phi_i sin psi_j).
  * b_sorted == NULL selects the symmetric operator b = a, psi = phi (perm_b,
- * psi and k are then ignored and x is n x m).  phi: n floats, psi: k floats,
- * both in original order.
+ * route_b, psi and k are then ignored and x is n x m).  phi: n floats, psi:
+ * k floats, both in original order; routes may be NULL.
  * ws: laplex_workspace_bytes(LAPLEX_OP_PHASED or LAPLEX_OP_PHASED_GENERAL, n, k, m). */
-laplex_status laplex_matvec_phased(const float* a_sorted, const uint32_t* perm_a, const float* phi, uint64_t n,
-                                   const float* b_sorted, const uint32_t* perm_b, const float* psi, uint64_t k, uint32_t m,
-                                   const float* x, float* y, void* ws, size_t ws_bytes, hipStream_t stream);
+laplex_status laplex_matvec_phased(const float* a_sorted, const uint32_t* perm_a, const void* route_a, const float* phi,
+                                   uint64_t n, const float* b_sorted, const uint32_t* perm_b, const void* route_b,
+                                   const float* psi, uint64_t k, uint32_t m, const float* x, float* y, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
 
 /* Short English description of a status code (static storage). */
 const char* laplex_status_string(laplex_status s);
@@ -126,12 +136,13 @@ const char* laplex_status_string(laplex_status s);
  * recorded on the stream it is launched on (events are created on the host
  * here, once).  laplex_profile_end disables it and returns the number of
  * launches recorded.  laplex_profile_get waits for record i and returns the
- * kernel's name (static storage) and its duration in milliseconds.  The
+ * kernel's name (static storage), its duration in milliseconds and the number
+ * of elements (rows) the launch processed.  The
  * profiler is process-wide state guarded by a mutex; while disabled it costs
  * one relaxed atomic load per launch. */
 laplex_status laplex_profile_begin(uint32_t capacity);
 uint32_t laplex_profile_end(void);
-laplex_status laplex_profile_get(uint32_t i, const char** name, float* ms);
+laplex_status laplex_profile_get(uint32_t i, const char** name, float* ms, uint64_t* units);
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,9 @@ from ._binding import (  # noqa: F401
     laplex_matvec_sym,
     laplex_sort_anchors,
     laplex_status_poll,
+    laplex_route_bytes,
     laplex_workspace_bytes,
     profile_launches,
+    route_buffer,
     workspace,
 )

@@ -45,11 +45,13 @@ def lib():
         vp, u64, u32, sz, i32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_int
         L.laplex_workspace_bytes.argtypes = [i32, u64, u64, u32]
         L.laplex_workspace_bytes.restype = sz
-        L.laplex_sort_anchors.argtypes = [vp, u64, vp, vp, vp, sz, vp]
+        L.laplex_route_bytes.argtypes = [u64]
+        L.laplex_route_bytes.restype = sz
+        L.laplex_sort_anchors.argtypes = [vp, u64, vp, vp, vp, sz, vp, sz, vp]
         L.laplex_status_poll.argtypes = [vp, vp]
-        L.laplex_matvec_sym.argtypes = [vp, vp, u64, u32, vp, vp, vp, sz, vp]
-        L.laplex_matvec_general.argtypes = [vp, vp, u64, vp, vp, u64, u32, vp, vp, vp, sz, vp]
-        L.laplex_matvec_phased.argtypes = [vp, vp, vp, u64, vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
+        L.laplex_matvec_sym.argtypes = [vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
+        L.laplex_matvec_general.argtypes = [vp, vp, vp, u64, vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
+        L.laplex_matvec_phased.argtypes = [vp, vp, vp, vp, u64, vp, vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
         for f in (L.laplex_sort_anchors, L.laplex_status_poll, L.laplex_matvec_sym, L.laplex_matvec_general,
                   L.laplex_matvec_phased):
             f.restype = i32
@@ -59,7 +61,8 @@ def lib():
         L.laplex_profile_begin.restype = i32
         L.laplex_profile_end.argtypes = []
         L.laplex_profile_end.restype = u32
-        L.laplex_profile_get.argtypes = [u32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float)]
+        L.laplex_profile_get.argtypes = [u32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
+                                         ctypes.POINTER(ctypes.c_uint64)]
         L.laplex_profile_get.restype = i32
         _lib = L
         return L
@@ -119,21 +122,35 @@ def _ws(ws: Optional[torch.Tensor], op, n, k, m, dev) -> torch.Tensor:
     return ws
 
 
+def laplex_route_bytes(n: int) -> int:
+    return int(lib().laplex_route_bytes(n))
+
+
+def route_buffer(n: int, device=None) -> torch.Tensor:
+    """A byte tensor that can receive the route of a sort of n anchors."""
+    return torch.empty(max(256, laplex_route_bytes(n)), dtype=torch.uint8, device=device or torch.device("cuda"))
+
+
 def laplex_sort_anchors(a: torch.Tensor, a_sorted: Optional[torch.Tensor] = None, perm: Optional[torch.Tensor] = None,
-                        ws: Optional[torch.Tensor] = None, check: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+                        route: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                        check: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """Stable ascending sort of the anchors: returns (a_sorted, perm) with
-    a_sorted = a[perm] and perm a uint32 tensor.  ``check=True`` waits for the
-    stream and raises LaplexError if an anchor was NaN/Inf."""
+    a_sorted = a[perm] and perm a uint32 tensor.  ``route``: optional byte
+    tensor (route_buffer(n)) that receives the sort's route for the applies.
+    ``check=True`` waits for the stream and raises LaplexError if an anchor
+    was NaN/Inf."""
     _vec(a, "a")
     if a.dim() != 1:
         raise ValueError("a must be 1-D")
     n, dev = a.shape[0], a.device
     a_sorted = torch.empty_like(a) if a_sorted is None else _vec(a_sorted, "a_sorted")
     perm = torch.empty(n, dtype=torch.uint32, device=dev) if perm is None else _vec(perm, "perm", torch.uint32)
+    if route is not None:
+        _vec(route, "route", torch.uint8)
     ws = _ws(ws, LAPLEX_OP_SORT, n, 0, 1, dev)
     L = lib()
-    _check(L.laplex_sort_anchors(_ptr(a), n, _ptr(a_sorted), _ptr(perm), _ptr(ws), ws.numel(), _stream(dev)),
-           "laplex_sort_anchors")
+    _check(L.laplex_sort_anchors(_ptr(a), n, _ptr(a_sorted), _ptr(perm), _ptr(route), 0 if route is None else route.numel(),
+                                 _ptr(ws), ws.numel(), _stream(dev)), "laplex_sort_anchors")
     if check:
         _check(L.laplex_status_poll(_ptr(ws), _stream(dev)), "laplex_sort_anchors")
     return a_sorted, perm
@@ -145,7 +162,7 @@ def laplex_status_poll(ws: torch.Tensor) -> int:
 
 
 def laplex_matvec_sym(a_sorted: torch.Tensor, perm: torch.Tensor, x: torch.Tensor, y: Optional[torch.Tensor] = None,
-                      ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+                      ws: Optional[torch.Tensor] = None, route: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y = LAPLEX(a, a) x for the sort handle (a_sorted, perm); x is (n,) or (n, m)."""
     _vec(a_sorted, "a_sorted")
     _vec(perm, "perm", torch.uint32)
@@ -154,13 +171,14 @@ def laplex_matvec_sym(a_sorted: torch.Tensor, perm: torch.Tensor, x: torch.Tenso
     y = torch.empty_like(x) if y is None else y
     _cols(y, n, "y")
     ws = _ws(ws, LAPLEX_OP_SYM, n, 0, m, dev)
-    _check(lib().laplex_matvec_sym(_ptr(a_sorted), _ptr(perm), n, m, _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(dev)),
-           "laplex_matvec_sym")
+    _check(lib().laplex_matvec_sym(_ptr(a_sorted), _ptr(perm), _ptr(route), n, m, _ptr(x), _ptr(y), _ptr(ws), ws.numel(),
+                                   _stream(dev)), "laplex_matvec_sym")
     return y
 
 
 def laplex_matvec_general(a_sorted: torch.Tensor, perm_a: torch.Tensor, b_sorted: torch.Tensor, perm_b: torch.Tensor,
-                          x: torch.Tensor, y: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+                          x: torch.Tensor, y: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                          route_a: Optional[torch.Tensor] = None, route_b: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y = LAPLEX(a, b) x; x is (k,) or (k, m), y is (n,) or (n, m)."""
     _vec(a_sorted, "a_sorted")
     _vec(perm_a, "perm_a", torch.uint32)
@@ -172,15 +190,17 @@ def laplex_matvec_general(a_sorted: torch.Tensor, perm_a: torch.Tensor, b_sorted
         y = torch.empty((n,) if x.dim() == 1 else (n, m), dtype=torch.float32, device=dev)
     _cols(y, n, "y")
     ws = _ws(ws, LAPLEX_OP_GENERAL, n, k, m, dev)
-    _check(lib().laplex_matvec_general(_ptr(a_sorted), _ptr(perm_a), n, _ptr(b_sorted), _ptr(perm_b), k, m, _ptr(x), _ptr(y),
-                                       _ptr(ws), ws.numel(), _stream(dev)), "laplex_matvec_general")
+    _check(lib().laplex_matvec_general(_ptr(a_sorted), _ptr(perm_a), _ptr(route_a), n, _ptr(b_sorted), _ptr(perm_b),
+                                       _ptr(route_b), k, m, _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(dev)),
+           "laplex_matvec_general")
     return y
 
 
 def laplex_matvec_phased(a_sorted: torch.Tensor, perm_a: torch.Tensor, phi: torch.Tensor, x: torch.Tensor,
                          b_sorted: Optional[torch.Tensor] = None, perm_b: Optional[torch.Tensor] = None,
                          psi: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
-                         ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+                         ws: Optional[torch.Tensor] = None, route_a: Optional[torch.Tensor] = None,
+                         route_b: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y = LAPLEX(a, phi; b, psi) x.  Without b: the symmetric phased operator (b = a, psi = phi)."""
     _vec(a_sorted, "a_sorted")
     _vec(perm_a, "perm_a", torch.uint32)
@@ -199,8 +219,9 @@ def laplex_matvec_phased(a_sorted: torch.Tensor, perm_a: torch.Tensor, phi: torc
         y = torch.empty((n,) if x.dim() == 1 else (n, m), dtype=torch.float32, device=dev)
     _cols(y, n, "y")
     ws = _ws(ws, op, n, k, m, dev)
-    _check(lib().laplex_matvec_phased(_ptr(a_sorted), _ptr(perm_a), _ptr(phi), n, _ptr(b_sorted), _ptr(perm_b), _ptr(psi), k, m,
-                                      _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(dev)), "laplex_matvec_phased")
+    _check(lib().laplex_matvec_phased(_ptr(a_sorted), _ptr(perm_a), _ptr(route_a), _ptr(phi), n, _ptr(b_sorted), _ptr(perm_b),
+                                      _ptr(route_b), _ptr(psi), k, m, _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(dev)),
+           "laplex_matvec_phased")
     return y
 
 
@@ -210,7 +231,7 @@ class profile_launches:
 
         with profile_launches() as prof:
             ...
-        prof.records  # [(kernel name, ms), ...] in launch order
+        prof.records  # [(kernel name, ms, elements), ...] in launch order
     """
 
     def __init__(self, capacity: int = 65536):
@@ -224,9 +245,9 @@ class profile_launches:
     def __exit__(self, *exc):
         L = lib()
         cnt = L.laplex_profile_end()
-        name, ms = ctypes.c_char_p(), ctypes.c_float()
+        name, ms, units = ctypes.c_char_p(), ctypes.c_float(), ctypes.c_uint64()
         self.records = []
         for i in range(cnt):
-            _check(L.laplex_profile_get(i, ctypes.byref(name), ctypes.byref(ms)), "laplex_profile_get")
-            self.records.append((name.value.decode(), float(ms.value)))
+            _check(L.laplex_profile_get(i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(units)), "laplex_profile_get")
+            self.records.append((name.value.decode(), float(ms.value), int(units.value)))
         return False

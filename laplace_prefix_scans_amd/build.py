@@ -13,13 +13,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblaplex.so")
-SOURCES = ["laplex_sort.hip", "laplex_apply.hip", "laplex_api.hip"]
+SOURCES = ["laplex_sort.hip", "laplex_route.hip", "laplex_apply.hip", "laplex_api.hip"]
 ARCH = "gfx950"
 FLAGS = [
     "-O3",
     "-std=c++17",
     "--offload-arch=" + ARCH,
     "-fPIC",
+    # no implicit multiply-add contraction: every fused multiply-add is an
+    # explicit fmaf, so results do not depend on code generation
+    "-ffp-contract=off",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

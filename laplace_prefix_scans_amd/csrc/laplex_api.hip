@@ -49,20 +49,31 @@ size_t sort_bytes(uint64_t n) {
   return (c.off + 255) & ~size_t(255);
 }
 
-// rows: length of the gathered input (n symmetric, k general); len: scanned length
-ApplyWorkspace carve_apply(void* ws, uint64_t rows, uint64_t len, uint32_t m, Variant var, bool general, size_t* total) {
+// rows_in: length of the gathered input (n symmetric, k general); rows_out:
+// outputs (n); len: scanned length.  Buffers for moving x and y along a sort
+// route (zs, t0, t1, phas) are laid out when m is small enough for routes.
+ApplyWorkspace carve_apply(void* ws, uint64_t rows_in, uint64_t rows_out, uint64_t len, uint32_t m, Variant var, bool general,
+                           size_t* total) {
   Carver c(ws);
   ApplyWorkspace w{};
   const uint64_t T = apply_tiles(len, m, var);
   const uint64_t M = (var == Variant::Phased) ? 2ull * m : m;
-  w.xs = c.take<float>(rows * m * 4);
-  w.phs = (var == Variant::Phased) ? c.take<float>(rows * 4) : nullptr;
+  const bool ph = var == Variant::Phased;
+  w.xs = c.take<float>(rows_in * m * 4);
+  w.phs = ph ? c.take<float>(rows_in * 4) : nullptr;
   w.bf = c.take<float>(T * M * 4);
   w.bb = c.take<float>(T * M * 4);
   w.cf = c.take<float>(T * M * 4);
   w.cb = c.take<float>(T * M * 4);
   w.tanch = c.take<float2>(T * 8);
   w.tsplit = general ? c.take<uint2>((T + 1) * 8) : nullptr;
+  if (m <= kRouteMaxCols) {
+    const uint64_t rmax = std::max(rows_in, rows_out);
+    w.zs = c.take<float>(rows_out * m * 4);
+    w.phas = (ph && general) ? c.take<float>(rows_out * 4) : nullptr;
+    w.t0 = c.take<float>(rmax * m * 4);
+    w.t1 = c.take<float>(rmax * m * 4);
+  }
   if (total) *total = (c.off + 255) & ~size_t(255);
   return w;
 }
@@ -86,27 +97,40 @@ extern "C" size_t laplex_workspace_bytes(int op, uint64_t n, uint64_t k, uint32_
   size_t total = 0;
   switch (op) {
     case LAPLEX_OP_SORT: return sort_bytes(n);
-    case LAPLEX_OP_SYM: carve_apply(nullptr, n, n, m, Variant::Sym, false, &total); return total;
-    case LAPLEX_OP_PHASED: carve_apply(nullptr, n, n, m, Variant::Phased, false, &total); return total;
-    case LAPLEX_OP_GENERAL: carve_apply(nullptr, k, n + k, m, Variant::Sym, true, &total); return total;
-    case LAPLEX_OP_PHASED_GENERAL: carve_apply(nullptr, k, n + k, m, Variant::Phased, true, &total); return total;
+    case LAPLEX_OP_SYM: carve_apply(nullptr, n, n, n, m, Variant::Sym, false, &total); return total;
+    case LAPLEX_OP_PHASED: carve_apply(nullptr, n, n, n, m, Variant::Phased, false, &total); return total;
+    case LAPLEX_OP_GENERAL: carve_apply(nullptr, k, n, n + k, m, Variant::Sym, true, &total); return total;
+    case LAPLEX_OP_PHASED_GENERAL: carve_apply(nullptr, k, n, n + k, m, Variant::Phased, true, &total); return total;
     default: return 0;
   }
 }
 
-extern "C" laplex_status laplex_sort_anchors(const float* a, uint64_t n, float* a_sorted, uint32_t* perm, void* ws,
-                                             size_t ws_bytes, hipStream_t stream) {
+extern "C" size_t laplex_route_bytes(uint64_t n) {
+  if (n > kMaxLen) return 0;
+  return route_bytes(n);
+}
+
+extern "C" laplex_status laplex_sort_anchors(const float* a, uint64_t n, float* a_sorted, uint32_t* perm, void* route,
+                                             size_t route_bytes_, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (n == 0) return LAPLEX_OK;
   if (n > kMaxLen) return LAPLEX_ERR_SIZE;
   if (!a || !a_sorted || !perm || !ws) return LAPLEX_ERR_NULL;
-  if (misaligned(a, 4) || misaligned(a_sorted, 4) || misaligned(perm, 4) || misaligned(ws, 256)) return LAPLEX_ERR_ALIGN;
+  if (misaligned(a, 4) || misaligned(a_sorted, 4) || misaligned(perm, 4) || misaligned(ws, 256) ||
+      (route && misaligned(route, 256)))
+    return LAPLEX_ERR_ALIGN;
   if (ws_bytes < sort_bytes(n)) return LAPLEX_ERR_WORKSPACE;
+  if (route && route_bytes_ < route_bytes(n)) return LAPLEX_ERR_WORKSPACE;
   const size_t vb = n * 4;
   if (overlaps(a_sorted, vb, a, vb) || overlaps(perm, vb, a, vb) || overlaps(a_sorted, vb, perm, vb) ||
       overlaps(a_sorted, vb, ws, ws_bytes) || overlaps(perm, vb, ws, ws_bytes))
     return LAPLEX_ERR_OVERLAP;
+  if (route && (overlaps(route, route_bytes_, a, vb) || overlaps(route, route_bytes_, a_sorted, vb) ||
+                overlaps(route, route_bytes_, perm, vb) || overlaps(route, route_bytes_, ws, ws_bytes)))
+    return LAPLEX_ERR_OVERLAP;
   const SortWorkspace w = carve_sort(ws, n);
-  return from_hip(sort_anchors(w, a, n, a_sorted, perm, stream));
+  SortRoute r{};
+  if (route) r = carve_route(route, n);
+  return from_hip(sort_anchors(w, a, n, a_sorted, perm, route ? &r : nullptr, stream));
 }
 
 extern "C" laplex_status laplex_status_poll(const void* ws, hipStream_t stream) {
@@ -130,28 +154,34 @@ static laplex_status check_apply_common(const float* a_sorted, const uint32_t* p
   return LAPLEX_OK;
 }
 
-extern "C" laplex_status laplex_matvec_sym(const float* a_sorted, const uint32_t* perm, uint64_t n, uint32_t m, const float* x,
-                                           float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+extern "C" laplex_status laplex_matvec_sym(const float* a_sorted, const uint32_t* perm, const void* route, uint64_t n, uint32_t m,
+                                           const float* x, float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (n == 0 || m == 0) return LAPLEX_OK;
   laplex_status st = check_apply_common(a_sorted, perm, n, m, x, y, ws);
   if (st != LAPLEX_OK) return st;
+  if (route && misaligned(route, 256)) return LAPLEX_ERR_ALIGN;
   size_t need = 0;
-  carve_apply(nullptr, n, n, m, Variant::Sym, false, &need);
+  carve_apply(nullptr, n, n, n, m, Variant::Sym, false, &need);
   if (ws_bytes < need) return LAPLEX_ERR_WORKSPACE;
   const size_t yb = n * (size_t)m * 4, vb = n * 4;
-  if (overlaps(y, yb, x, yb) || overlaps(y, yb, a_sorted, vb) || overlaps(y, yb, perm, vb) || overlaps(y, yb, ws, ws_bytes))
+  if (overlaps(y, yb, x, yb) || overlaps(y, yb, a_sorted, vb) || overlaps(y, yb, perm, vb) || overlaps(y, yb, ws, ws_bytes) ||
+      overlaps(y, yb, route, route ? route_bytes(n) : 0))
     return LAPLEX_ERR_OVERLAP;
-  const ApplyWorkspace w = carve_apply(ws, n, n, m, Variant::Sym, false, nullptr);
-  return from_hip(apply_sym(w, Variant::Sym, a_sorted, perm, nullptr, n, m, x, y, stream));
+  const ApplyWorkspace w = carve_apply(ws, n, n, n, m, Variant::Sym, false, nullptr);
+  SortRoute r{};
+  if (route) r = carve_route(route, n);
+  return from_hip(apply_sym(w, Variant::Sym, a_sorted, perm, route ? &r : nullptr, nullptr, n, m, x, y, stream));
 }
 
-extern "C" laplex_status laplex_matvec_general(const float* a_sorted, const uint32_t* perm_a, uint64_t n, const float* b_sorted,
-                                               const uint32_t* perm_b, uint64_t k, uint32_t m, const float* x, float* y, void* ws,
-                                               size_t ws_bytes, hipStream_t stream) {
+extern "C" laplex_status laplex_matvec_general(const float* a_sorted, const uint32_t* perm_a, const void* route_a, uint64_t n,
+                                               const float* b_sorted, const uint32_t* perm_b, const void* route_b, uint64_t k,
+                                               uint32_t m, const float* x, float* y, void* ws, size_t ws_bytes,
+                                               hipStream_t stream) {
   if (n == 0 || m == 0) return LAPLEX_OK;
   laplex_status st = check_apply_common(a_sorted, perm_a, n, m, x ? x : (const float*)y, y, ws);
   if (st != LAPLEX_OK) return st;
   if (k > kMaxLen) return LAPLEX_ERR_SIZE;
+  if ((route_a && misaligned(route_a, 256)) || (route_b && misaligned(route_b, 256))) return LAPLEX_ERR_ALIGN;
   const size_t yb = n * (size_t)m * 4;
   if (k == 0) {
     if (overlaps(y, yb, a_sorted, n * 4) || overlaps(y, yb, perm_a, n * 4)) return LAPLEX_ERR_OVERLAP;
@@ -160,36 +190,44 @@ extern "C" laplex_status laplex_matvec_general(const float* a_sorted, const uint
   if (!b_sorted || !perm_b || !x) return LAPLEX_ERR_NULL;
   if (misaligned(b_sorted, 4) || misaligned(perm_b, 4)) return LAPLEX_ERR_ALIGN;
   size_t need = 0;
-  carve_apply(nullptr, k, n + k, m, Variant::Sym, true, &need);
+  carve_apply(nullptr, k, n, n + k, m, Variant::Sym, true, &need);
   if (ws_bytes < need) return LAPLEX_ERR_WORKSPACE;
   const size_t xb = k * (size_t)m * 4;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, a_sorted, n * 4) || overlaps(y, yb, perm_a, n * 4) ||
-      overlaps(y, yb, b_sorted, k * 4) || overlaps(y, yb, perm_b, k * 4) || overlaps(y, yb, ws, ws_bytes))
+      overlaps(y, yb, b_sorted, k * 4) || overlaps(y, yb, perm_b, k * 4) || overlaps(y, yb, ws, ws_bytes) ||
+      overlaps(y, yb, route_a, route_a ? route_bytes(n) : 0) || overlaps(y, yb, route_b, route_b ? route_bytes(k) : 0))
     return LAPLEX_ERR_OVERLAP;
-  const ApplyWorkspace w = carve_apply(ws, k, n + k, m, Variant::Sym, true, nullptr);
-  return from_hip(apply_general(w, Variant::Sym, a_sorted, perm_a, nullptr, n, b_sorted, perm_b, nullptr, k, m, x, y, stream));
+  const ApplyWorkspace w = carve_apply(ws, k, n, n + k, m, Variant::Sym, true, nullptr);
+  SortRoute ra{}, rb{};
+  if (route_a) ra = carve_route(route_a, n);
+  if (route_b) rb = carve_route(route_b, k);
+  return from_hip(apply_general(w, Variant::Sym, a_sorted, perm_a, route_a ? &ra : nullptr, nullptr, n, b_sorted, perm_b,
+                                route_b ? &rb : nullptr, nullptr, k, m, x, y, stream));
 }
 
-extern "C" laplex_status laplex_matvec_phased(const float* a_sorted, const uint32_t* perm_a, const float* phi, uint64_t n,
-                                              const float* b_sorted, const uint32_t* perm_b, const float* psi, uint64_t k,
-                                              uint32_t m, const float* x, float* y, void* ws, size_t ws_bytes,
-                                              hipStream_t stream) {
+extern "C" laplex_status laplex_matvec_phased(const float* a_sorted, const uint32_t* perm_a, const void* route_a, const float* phi,
+                                              uint64_t n, const float* b_sorted, const uint32_t* perm_b, const void* route_b,
+                                              const float* psi, uint64_t k, uint32_t m, const float* x, float* y, void* ws,
+                                              size_t ws_bytes, hipStream_t stream) {
   if (n == 0 || m == 0) return LAPLEX_OK;
   laplex_status st = check_apply_common(a_sorted, perm_a, n, m, x ? x : (const float*)y, y, ws);
   if (st != LAPLEX_OK) return st;
   if (!phi) return LAPLEX_ERR_NULL;
   if (misaligned(phi, 4)) return LAPLEX_ERR_ALIGN;
+  if ((route_a && misaligned(route_a, 256)) || (route_b && misaligned(route_b, 256))) return LAPLEX_ERR_ALIGN;
   const size_t yb = n * (size_t)m * 4;
+  SortRoute ra{}, rb{};
+  if (route_a) ra = carve_route(route_a, n);
   if (b_sorted == nullptr) {
     if (!x) return LAPLEX_ERR_NULL;
     size_t need = 0;
-    carve_apply(nullptr, n, n, m, Variant::Phased, false, &need);
+    carve_apply(nullptr, n, n, n, m, Variant::Phased, false, &need);
     if (ws_bytes < need) return LAPLEX_ERR_WORKSPACE;
     if (overlaps(y, yb, x, yb) || overlaps(y, yb, a_sorted, n * 4) || overlaps(y, yb, perm_a, n * 4) ||
-        overlaps(y, yb, phi, n * 4) || overlaps(y, yb, ws, ws_bytes))
+        overlaps(y, yb, phi, n * 4) || overlaps(y, yb, ws, ws_bytes) || overlaps(y, yb, route_a, route_a ? route_bytes(n) : 0))
       return LAPLEX_ERR_OVERLAP;
-    const ApplyWorkspace w = carve_apply(ws, n, n, m, Variant::Phased, false, nullptr);
-    return from_hip(apply_sym(w, Variant::Phased, a_sorted, perm_a, phi, n, m, x, y, stream));
+    const ApplyWorkspace w = carve_apply(ws, n, n, n, m, Variant::Phased, false, nullptr);
+    return from_hip(apply_sym(w, Variant::Phased, a_sorted, perm_a, route_a ? &ra : nullptr, phi, n, m, x, y, stream));
   }
   if (k > kMaxLen) return LAPLEX_ERR_SIZE;
   if (k == 0) {
@@ -200,15 +238,18 @@ extern "C" laplex_status laplex_matvec_phased(const float* a_sorted, const uint3
   if (!perm_b || !psi || !x) return LAPLEX_ERR_NULL;
   if (misaligned(b_sorted, 4) || misaligned(perm_b, 4) || misaligned(psi, 4)) return LAPLEX_ERR_ALIGN;
   size_t need = 0;
-  carve_apply(nullptr, k, n + k, m, Variant::Phased, true, &need);
+  carve_apply(nullptr, k, n, n + k, m, Variant::Phased, true, &need);
   if (ws_bytes < need) return LAPLEX_ERR_WORKSPACE;
   const size_t xb = k * (size_t)m * 4;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, a_sorted, n * 4) || overlaps(y, yb, perm_a, n * 4) ||
       overlaps(y, yb, phi, n * 4) || overlaps(y, yb, b_sorted, k * 4) || overlaps(y, yb, perm_b, k * 4) ||
-      overlaps(y, yb, psi, k * 4) || overlaps(y, yb, ws, ws_bytes))
+      overlaps(y, yb, psi, k * 4) || overlaps(y, yb, ws, ws_bytes) || overlaps(y, yb, route_a, route_a ? route_bytes(n) : 0) ||
+      overlaps(y, yb, route_b, route_b ? route_bytes(k) : 0))
     return LAPLEX_ERR_OVERLAP;
-  const ApplyWorkspace w = carve_apply(ws, k, n + k, m, Variant::Phased, true, nullptr);
-  return from_hip(apply_general(w, Variant::Phased, a_sorted, perm_a, phi, n, b_sorted, perm_b, psi, k, m, x, y, stream));
+  if (route_b) rb = carve_route(route_b, k);
+  const ApplyWorkspace w = carve_apply(ws, k, n, n + k, m, Variant::Phased, true, nullptr);
+  return from_hip(apply_general(w, Variant::Phased, a_sorted, perm_a, route_a ? &ra : nullptr, phi, n, b_sorted, perm_b,
+                                route_b ? &rb : nullptr, psi, k, m, x, y, stream));
 }
 
 extern "C" const char* laplex_status_string(laplex_status s) {
@@ -237,6 +278,7 @@ std::mutex g_prof_mu;
 std::atomic<bool> g_prof_on{false};
 std::vector<hipEvent_t> g_prof_ev;       // 2 per record: before, after
 std::vector<const char*> g_prof_names;
+std::vector<uint64_t> g_prof_units;
 uint32_t g_prof_cap = 0, g_prof_cnt = 0;
 }  // namespace
 
@@ -249,10 +291,11 @@ int prof_begin(hipStream_t s) {
   if (hipEventRecord(g_prof_ev[2 * slot], s) != hipSuccess) return -1;
   return slot;
 }
-void prof_end(int slot, const char* name, hipStream_t s) {
+void prof_end(int slot, const char* name, uint64_t units, hipStream_t s) {
   if (slot < 0) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_names[slot] = name;
+  g_prof_units[slot] = units;
   (void)hipEventRecord(g_prof_ev[2 * slot + 1], s);
 }
 }  // namespace laplex
@@ -266,6 +309,7 @@ extern "C" laplex_status laplex_profile_begin(uint32_t capacity) {
     g_prof_ev.push_back(e);
   }
   g_prof_names.assign(capacity, nullptr);
+  g_prof_units.assign(capacity, 0);
   g_prof_cap = capacity;
   g_prof_cnt = 0;
   g_prof_on.store(true);
@@ -278,12 +322,13 @@ extern "C" uint32_t laplex_profile_end(void) {
   return g_prof_cnt;
 }
 
-extern "C" laplex_status laplex_profile_get(uint32_t i, const char** name, float* ms) {
-  if (!name || !ms) return LAPLEX_ERR_NULL;
+extern "C" laplex_status laplex_profile_get(uint32_t i, const char** name, float* ms, uint64_t* units) {
+  if (!name || !ms || !units) return LAPLEX_ERR_NULL;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (i >= g_prof_cnt) return LAPLEX_ERR_ARG;
   if (hipEventSynchronize(g_prof_ev[2 * i + 1]) != hipSuccess) return LAPLEX_ERR_HIP;
   if (hipEventElapsedTime(ms, g_prof_ev[2 * i], g_prof_ev[2 * i + 1]) != hipSuccess) return LAPLEX_ERR_HIP;
   *name = g_prof_names[i];
+  *units = g_prof_units[i];
   return LAPLEX_OK;
 }

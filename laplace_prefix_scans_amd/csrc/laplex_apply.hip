@@ -25,8 +25,6 @@
 
 namespace laplex {
 
-constexpr int kApplyWaves = kApplyBlock / kWave;
-
 // summary/carry column of injected column j of chunk cc (phased: cos part at
 // [0, m), sin part at [m, 2m))
 template <int C, bool PH>
@@ -36,7 +34,7 @@ __device__ __forceinline__ uint32_t sumcol(uint32_t m, uint32_t cc, int j) {
 }
 
 // Sum CC values over the block; totals land in out0[col(j)], out1[col(j)].
-template <int CC>
+template <int CC, int NW>
 __device__ __forceinline__ void block_sum2(float (&a)[CC], float (&b)[CC], float* s_red /* [2][NW][CC] */, int& jcol_valid) {
   const int lane = lane_id(), wid = threadIdx.x / kWave;
   wave_sum<CC>(a);
@@ -44,8 +42,8 @@ __device__ __forceinline__ void block_sum2(float (&a)[CC], float (&b)[CC], float
   if (lane == 0) {
 #pragma unroll
     for (int j = 0; j < CC; ++j) {
-      s_red[(0 * kApplyWaves + wid) * CC + j] = a[j];
-      s_red[(1 * kApplyWaves + wid) * CC + j] = b[j];
+      s_red[(0 * NW + wid) * CC + j] = a[j];
+      s_red[(1 * NW + wid) * CC + j] = b[j];
     }
   }
   __syncthreads();
@@ -57,7 +55,7 @@ __device__ __forceinline__ void block_sum2(float (&a)[CC], float (&b)[CC], float
 // ae[], nondecreasing across the whole tile); carries into the tile from the
 // left (cf, anchored at sf) and right (cb, anchored at sb).
 // Out: v[e][j] = strict forward value + inclusive backward value.
-template <int E, int CC>
+template <int E, int CC, int NW>
 __device__ __forceinline__ void tile_scan(const float (&ae)[E], float (&v)[E][CC], const float (&cf)[CC], float sf,
                                           const float (&cb)[CC], float sb, float* s_wf, float* s_wfs, float* s_wb,
                                           float* s_wbs) {
@@ -129,7 +127,7 @@ __device__ __forceinline__ void tile_scan(const float (&ae)[E], float (&v)[E][CC
   float sz2 = sb;
 #pragma unroll
   for (int j = 0; j < CC; ++j) cz[j] = cb[j];
-  for (int w = kApplyWaves - 1; w > wid; --w) {
+  for (int w = NW - 1; w > wid; --w) {
     const float s2 = s_wbs[w];
     const float g = decay(s2 - sz2);
 #pragma unroll
@@ -170,124 +168,248 @@ __device__ __forceinline__ void tile_scan(const float (&ae)[E], float (&v)[E][CC
 
 // ---------------------------------------------------------------- carries
 constexpr int kCarryBlock = 1024;
+constexpr int kCarryBatch = 8;
 
 // Scan of the tile aggregates into the carry entering each tile from the left
 // (cf: value at the previous tile's last element) and from the right (cb:
-// value at the next tile's first element).  One workgroup: each thread folds
-// a contiguous run of tiles, wave 0 scans the 1024 run aggregates in 16
-// rounds, then each thread walks its run again writing carries.
+// value at the next tile's first element).  One workgroup per column: each
+// thread owns a contiguous run of tiles, folds it as a direct weighted sum
+// (every weight exp(s - s_end) <= 1), wave 0 scans the 1024 run aggregates in
+// 16 rounds, then each thread walks its run again writing carries, with the
+// loads of each batch of tiles issued before its dependent chain.
 __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restrict__ bf, const float* __restrict__ bb,
                                                             const float2* __restrict__ tanch, uint64_t T, uint32_t M,
                                                             float* __restrict__ cf, float* __restrict__ cb) {
   __shared__ float sB[kCarryBlock], sS[kCarryBlock];
+  const uint32_t c = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
   const uint64_t q = (T + kCarryBlock - 1) / kCarryBlock;
   const uint64_t t0 = std::min<uint64_t>(T, (uint64_t)tid * q), t1 = std::min<uint64_t>(T, t0 + q);
   const float s_min = tanch[0].y, s_maxf = tanch[T - 1].x, s_maxl = tanch[T - 1].y;
-  for (uint32_t c = 0; c < M; ++c) {
-    // ---- forward
-    float B = 0.f, s = s_maxl;
-    if (t0 < t1) {
-      B = bf[t0 * M + c];
-      s = tanch[t0].y;
-      for (uint64_t t = t0 + 1; t < t1; ++t) {
-        const float s2 = tanch[t].y;
-        B = fmaf(decay(s - s2), B, bf[t * M + c]);
-        s = s2;
+
+  // ---- forward: fold, scan, walk
+  float B = 0.f, s = s_maxl;
+  if (t0 < t1) {
+    s = tanch[t1 - 1].y;
+#pragma unroll 8
+    for (uint64_t t = t0; t < t1; ++t) B = fmaf(decay(tanch[t].y - s), bf[t * M + c], B);
+  }
+  sB[tid] = B;
+  sS[tid] = s;
+  __syncthreads();
+  if (wid == 0) {
+    float cB = 0.f, cS = s_min;
+    for (int r = 0; r < kCarryBlock / kWave; ++r) {
+      const int i = r * kWave + lane;
+      float b1[1] = {sB[i]};
+      const float s1 = sS[i];
+      wave_scan_fwd<1>(b1, s1);
+      const float inc = fmaf(decay(cS - s1), cB, b1[0]);
+      float ex = __shfl_up(inc, 1), es = __shfl_up(s1, 1);
+      if (lane == 0) {
+        ex = cB;
+        es = cS;
       }
+      sB[i] = ex;
+      sS[i] = es;
+      cB = __shfl(inc, kWave - 1);
+      cS = __shfl(s1, kWave - 1);
     }
-    sB[tid] = B;
-    sS[tid] = s;
-    __syncthreads();
-    if (wid == 0) {
-      float cB = 0.f, cS = s_min;
-      for (int r = 0; r < kCarryBlock / kWave; ++r) {
-        const int i = r * kWave + lane;
-        float b1[1] = {sB[i]};
-        const float s1 = sS[i];
-        wave_scan_fwd<1>(b1, s1);
-        const float inc = fmaf(decay(cS - s1), cB, b1[0]);
-        float ex = __shfl_up(inc, 1), es = __shfl_up(s1, 1);
-        if (lane == 0) {
-          ex = cB;
-          es = cS;
+  }
+  __syncthreads();
+  if (t0 < t1) {
+    float C = sB[tid], sc = sS[tid];
+    for (uint64_t tb = t0; tb < t1; tb += kCarryBatch) {
+      float sl[kCarryBatch], bv[kCarryBatch];
+#pragma unroll
+      for (int u = 0; u < kCarryBatch; ++u) {
+        const uint64_t t = std::min<uint64_t>(tb + u, t1 - 1);
+        sl[u] = tanch[t].y;
+        bv[u] = bf[t * M + c];
+      }
+#pragma unroll
+      for (int u = 0; u < kCarryBatch; ++u) {
+        if (tb + u < t1) {
+          cf[(tb + u) * M + c] = C;
+          C = fmaf(decay(sc - sl[u]), C, bv[u]);
+          sc = sl[u];
         }
-        sB[i] = ex;
-        sS[i] = es;
-        cB = __shfl(inc, kWave - 1);
-        cS = __shfl(s1, kWave - 1);
       }
     }
-    __syncthreads();
-    if (t0 < t1) {
-      float C = sB[tid], sc = sS[tid];
-      for (uint64_t t = t0; t < t1; ++t) {
-        cf[t * M + c] = C;
-        const float s2 = tanch[t].y;
-        C = fmaf(decay(sc - s2), C, bf[t * M + c]);
-        sc = s2;
+  }
+  __syncthreads();
+
+  // ---- backward
+  B = 0.f;
+  s = s_maxf;
+  if (t0 < t1) {
+    s = tanch[t0].x;
+#pragma unroll 8
+    for (uint64_t t = t0; t < t1; ++t) B = fmaf(decay(s - tanch[t].x), bb[t * M + c], B);
+  }
+  sB[tid] = B;
+  sS[tid] = s;
+  __syncthreads();
+  if (wid == 0) {
+    float cB = 0.f, cS = s_maxf;
+    for (int r = kCarryBlock / kWave - 1; r >= 0; --r) {
+      const int i = r * kWave + lane;
+      float b1[1] = {sB[i]};
+      const float s1 = sS[i];
+      wave_scan_bwd<1>(b1, s1);
+      const float inc = fmaf(decay(s1 - cS), cB, b1[0]);
+      float ex = __shfl_down(inc, 1), es = __shfl_down(s1, 1);
+      if (lane == kWave - 1) {
+        ex = cB;
+        es = cS;
       }
+      sB[i] = ex;
+      sS[i] = es;
+      cB = __shfl(inc, 0);
+      cS = __shfl(s1, 0);
     }
-    __syncthreads();
-    // ---- backward
-    B = 0.f;
-    s = s_maxf;
-    if (t0 < t1) {
-      B = bb[(t1 - 1) * M + c];
-      s = tanch[t1 - 1].x;
-      for (uint64_t t = t1 - 1; t-- > t0;) {
-        const float s2 = tanch[t].x;
-        B = fmaf(decay(s2 - s), B, bb[t * M + c]);
-        s = s2;
+  }
+  __syncthreads();
+  if (t0 < t1) {
+    float C = sB[tid], sc = sS[tid];
+    for (uint64_t te = t1; te > t0;) {
+      const uint64_t tb = te > t0 + kCarryBatch ? te - kCarryBatch : t0;
+      float sf[kCarryBatch], bv[kCarryBatch];
+#pragma unroll
+      for (int u = 0; u < kCarryBatch; ++u) {
+        const uint64_t t = std::min<uint64_t>(tb + u, te - 1);
+        sf[u] = tanch[t].x;
+        bv[u] = bb[t * M + c];
       }
-    }
-    sB[tid] = B;
-    sS[tid] = s;
-    __syncthreads();
-    if (wid == 0) {
-      float cB = 0.f, cS = s_maxf;
-      for (int r = kCarryBlock / kWave - 1; r >= 0; --r) {
-        const int i = r * kWave + lane;
-        float b1[1] = {sB[i]};
-        const float s1 = sS[i];
-        wave_scan_bwd<1>(b1, s1);
-        const float inc = fmaf(decay(s1 - cS), cB, b1[0]);
-        float ex = __shfl_down(inc, 1), es = __shfl_down(s1, 1);
-        if (lane == kWave - 1) {
-          ex = cB;
-          es = cS;
+#pragma unroll
+      for (int u = kCarryBatch - 1; u >= 0; --u) {
+        if (tb + u < te) {
+          cb[(tb + u) * M + c] = C;
+          C = fmaf(decay(sf[u] - sc), C, bv[u]);
+          sc = sf[u];
         }
-        sB[i] = ex;
-        sS[i] = es;
-        cB = __shfl(inc, 0);
-        cS = __shfl(s1, 0);
       }
+      te = tb;
     }
-    __syncthreads();
-    if (t0 < t1) {
-      float C = sB[tid], sc = sS[tid];
-      for (uint64_t t = t1; t-- > t0;) {
-        cb[t * M + c] = C;
-        const float s2 = tanch[t].x;
-        C = fmaf(decay(s2 - sc), C, bb[t * M + c]);
-        sc = s2;
-      }
-    }
-    __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------- symmetric
-template <int C, bool PH>
-__global__ __launch_bounds__(kApplyBlock) void k_sym_gather_reduce(const float* __restrict__ a_s, const uint32_t* __restrict__ perm,
-                                                                   const float* __restrict__ phi, const float* __restrict__ x,
-                                                                   uint64_t n, uint32_t m, float* __restrict__ xs,
-                                                                   float* __restrict__ phs, float* __restrict__ bf,
-                                                                   float* __restrict__ bb, float2* __restrict__ tanch) {
+// Contiguous loads and stores of N floats; vector instructions when the
+// caller knows the address is 16-byte (N % 4 == 0) or 8-byte (N % 2 == 0)
+// aligned.
+template <int N>
+__device__ __forceinline__ void ld_contig(const float* __restrict__ p, float (&v)[N], bool vec) {
+  if constexpr (N % 4 == 0) {
+    if (vec) {
+#pragma unroll
+      for (int i = 0; i < N / 4; ++i) {
+        const float4 q = reinterpret_cast<const float4*>(p)[i];
+        v[4 * i] = q.x;
+        v[4 * i + 1] = q.y;
+        v[4 * i + 2] = q.z;
+        v[4 * i + 3] = q.w;
+      }
+      return;
+    }
+  } else if constexpr (N % 2 == 0) {
+    if (vec) {
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) {
+        const float2 q = reinterpret_cast<const float2*>(p)[i];
+        v[2 * i] = q.x;
+        v[2 * i + 1] = q.y;
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = p[i];
+}
+template <int N>
+__device__ __forceinline__ void st_contig(float* __restrict__ p, const float (&v)[N], bool vec) {
+  if constexpr (N % 4 == 0) {
+    if (vec) {
+#pragma unroll
+      for (int i = 0; i < N / 4; ++i) reinterpret_cast<float4*>(p)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+      return;
+    }
+  } else if constexpr (N % 2 == 0) {
+    if (vec) {
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) reinterpret_cast<float2*>(p)[i] = make_float2(v[2 * i], v[2 * i + 1]);
+      return;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) p[i] = v[i];
+}
+
+// Anchors of this thread's E consecutive sorted positions (pad: `pad`).
+template <int E>
+__device__ __forceinline__ void load_anchors(const float* __restrict__ a_s, uint64_t p0, uint64_t n, float pad, bool vec,
+                                             float (&ae)[E]) {
+  if (p0 + E <= n) {
+    ld_contig<E>(a_s + p0, ae, vec && (E % 4 == 0 || E % 2 == 0));
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) ae[e] = (p0 + e < n) ? a_s[p0 + e] : pad;
+  }
+}
+
+// Rows p0 .. p0+E-1, columns [cc*C, cc*C + C) of a row-major n x m array;
+// rows past n read as zero.  When m == C the thread's E*C floats are
+// contiguous and are loaded as one block.
+template <int E, int C>
+__device__ __forceinline__ void load_rows(const float* __restrict__ x, uint64_t p0, uint64_t n, uint32_t m, uint32_t cc, bool vec,
+                                          float (&xv)[E][C]) {
+  if (m == C && p0 + E <= n) {
+    float flat[E * C];
+    ld_contig<E * C>(x + p0 * C, flat, vec);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int j = 0; j < C; ++j) xv[e][j] = flat[e * C + j];
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+#pragma unroll
+    for (int j = 0; j < C; ++j) xv[e][j] = (p0 + e < n) ? x[(p0 + e) * m + cc * C + j] : 0.f;
+}
+template <int E, int C>
+__device__ __forceinline__ void store_rows(float* __restrict__ y, uint64_t p0, uint64_t n, uint32_t m, uint32_t cc, bool vec,
+                                           const float (&yv)[E][C]) {
+  if (m == C && p0 + E <= n) {
+    float flat[E * C];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int j = 0; j < C; ++j) flat[e * C + j] = yv[e][j];
+    st_contig<E * C>(y + p0 * C, flat, vec);
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (p0 + e < n)
+#pragma unroll
+      for (int j = 0; j < C; ++j) y[(p0 + e) * m + cc * C + j] = yv[e][j];
+}
+
+// GATHER: inputs in original order, gathered through perm and stored to xs
+// (and phs); otherwise xs (and phs) already hold them in sorted order.
+// vec: a_s is 16-byte aligned (workspace buffers always are).
+template <int C, bool PH, bool GATHER>
+__global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_sym_gather_reduce(
+    const float* __restrict__ a_s, const uint32_t* __restrict__ perm, const float* __restrict__ phi, const float* __restrict__ x,
+    uint64_t n, uint32_t m, float* __restrict__ xs, float* __restrict__ phs, float* __restrict__ bf, float* __restrict__ bb,
+    float2* __restrict__ tanch, bool vec) {
   constexpr int CC = PH ? 2 * C : C;
   constexpr int E = apply_items(CC);
-  constexpr int P = kApplyBlock * E;
-  __shared__ float s_red[2 * kApplyWaves * CC];
+  constexpr int BLOCK = apply_block(CC);
+  constexpr int NW = BLOCK / kWave;
+  constexpr int P = BLOCK * E;
+  __shared__ float s_red[2 * NW * CC];
   const uint32_t M = PH ? 2 * m : m;
   const int tid = threadIdx.x;
   const uint64_t tile = blockIdx.x;
@@ -296,59 +418,72 @@ __global__ __launch_bounds__(kApplyBlock) void k_sym_gather_reduce(const float* 
   const float s_first = a_s[lo], s_last = a_s[hi - 1];
   if (tid == 0) tanch[tile] = make_float2(s_first, s_last);
   const uint64_t p0 = lo + (uint64_t)tid * E;
-  float wf[E], wb[E], cs[E], sn[E];
+  float ae[E], wf[E], wb[E], cs[E], sn[E];
   uint32_t src[E];
+  load_anchors<E>(a_s, p0, n, s_last, vec, ae);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint64_t p = p0 + e;
     const bool valid = p < n;
-    const float ae = valid ? a_s[p] : s_last;
-    src[e] = valid ? perm[p] : 0u;
+    src[e] = (GATHER && valid) ? perm[p] : 0u;
     if ((uint64_t)src[e] >= n) src[e] = 0;  // a handle from the sort is always in range
-    wf[e] = valid ? decay(ae - s_last) : 0.f;
-    wb[e] = valid ? decay(s_first - ae) : 0.f;
+    wf[e] = valid ? decay(ae[e] - s_last) : 0.f;
+    wb[e] = valid ? decay(s_first - ae[e]) : 0.f;
     cs[e] = 1.f;
     sn[e] = 0.f;
-    if (PH) {
-      const float ph = valid ? phi[src[e]] : 0.f;
-      if (valid) phs[p] = ph;
-      sincosf(ph, &sn[e], &cs[e]);
+  }
+  if (PH) {
+    float ph[E];
+    if (GATHER) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        ph[e] = (p0 + e < n) ? phi[src[e]] : 0.f;
+        if (p0 + e < n) phs[p0 + e] = ph[e];
+      }
+    } else {
+      load_anchors<E>(phs, p0, n, 0.f, true, ph);
     }
+#pragma unroll
+    for (int e = 0; e < E; ++e) sincosf(ph[e], &sn[e], &cs[e]);
   }
   for (uint32_t cc = 0; cc < m / C; ++cc) {
+    float xv[E][C];
+    if (GATHER) {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int j = 0; j < C; ++j) xv[e][j] = (p0 + e < n) ? x[(uint64_t)src[e] * m + cc * C + j] : 0.f;
+      store_rows<E, C>(xs, p0, n, m, cc, true, xv);
+    } else {
+      load_rows<E, C>(xs, p0, n, m, cc, true, xv);
+    }
     float sf[CC], sb[CC];
 #pragma unroll
     for (int j = 0; j < CC; ++j) sf[j] = sb[j] = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const uint64_t p = p0 + e;
-      if (p < n) {
-        const float* xr = x + (uint64_t)src[e] * m + cc * C;
-        float* xo = xs + p * m + cc * C;
 #pragma unroll
-        for (int j = 0; j < C; ++j) {
-          const float xv = xr[j];
-          xo[j] = xv;
-          if (PH) {
-            const float vc = cs[e] * xv, vs = sn[e] * xv;
-            sf[j] = fmaf(wf[e], vc, sf[j]);
-            sf[C + j] = fmaf(wf[e], vs, sf[C + j]);
-            sb[j] = fmaf(wb[e], vc, sb[j]);
-            sb[C + j] = fmaf(wb[e], vs, sb[C + j]);
-          } else {
-            sf[j] = fmaf(wf[e], xv, sf[j]);
-            sb[j] = fmaf(wb[e], xv, sb[j]);
-          }
+      for (int j = 0; j < C; ++j) {
+        const float v = xv[e][j];
+        if (PH) {
+          const float vc = cs[e] * v, vs = sn[e] * v;
+          sf[j] = fmaf(wf[e], vc, sf[j]);
+          sf[C + j] = fmaf(wf[e], vs, sf[C + j]);
+          sb[j] = fmaf(wb[e], vc, sb[j]);
+          sb[C + j] = fmaf(wb[e], vs, sb[C + j]);
+        } else {
+          sf[j] = fmaf(wf[e], v, sf[j]);
+          sb[j] = fmaf(wb[e], v, sb[j]);
         }
       }
     }
     int writer = 0;
-    block_sum2<CC>(sf, sb, s_red, writer);
+    block_sum2<CC, NW>(sf, sb, s_red, writer);
     if (writer) {
       float tf = 0.f, tb = 0.f;
-      for (int w = 0; w < kApplyWaves; ++w) {
-        tf += s_red[(0 * kApplyWaves + w) * CC + tid];
-        tb += s_red[(1 * kApplyWaves + w) * CC + tid];
+      for (int w = 0; w < NW; ++w) {
+        tf += s_red[(0 * NW + w) * CC + tid];
+        tb += s_red[(1 * NW + w) * CC + tid];
       }
       const uint32_t col = sumcol<C, PH>(m, cc, tid);
       bf[tile * M + col] = tf;
@@ -358,16 +493,19 @@ __global__ __launch_bounds__(kApplyBlock) void k_sym_gather_reduce(const float* 
   }
 }
 
-template <int C, bool PH>
-__global__ __launch_bounds__(kApplyBlock) void k_sym_apply(const float* __restrict__ a_s, const uint32_t* __restrict__ perm,
-                                                           const float* __restrict__ xs, const float* __restrict__ phs,
-                                                           const float* __restrict__ cfw, const float* __restrict__ cbw,
-                                                           const float2* __restrict__ tanch, uint64_t n, uint32_t m, uint64_t T,
-                                                           float* __restrict__ y) {
+// SCATTER: y rows written to original order through perm; otherwise to
+// sorted order (row p of y).
+template <int C, bool PH, bool SCATTER>
+__global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_sym_apply(
+    const float* __restrict__ a_s, const uint32_t* __restrict__ perm, const float* __restrict__ xs,
+    const float* __restrict__ phs, const float* __restrict__ cfw, const float* __restrict__ cbw,
+    const float2* __restrict__ tanch, uint64_t n, uint32_t m, uint64_t T, float* __restrict__ y, bool vec) {
   constexpr int CC = PH ? 2 * C : C;
   constexpr int E = apply_items(CC);
-  constexpr int P = kApplyBlock * E;
-  __shared__ float s_wf[kApplyWaves * CC], s_wb[kApplyWaves * CC], s_wfs[kApplyWaves], s_wbs[kApplyWaves];
+  constexpr int BLOCK = apply_block(CC);
+  constexpr int NW = BLOCK / kWave;
+  constexpr int P = BLOCK * E;
+  __shared__ float s_wf[NW * CC], s_wb[NW * CC], s_wfs[NW], s_wbs[NW];
   const uint32_t M = PH ? 2 * m : m;
   const int tid = threadIdx.x;
   const uint64_t tile = blockIdx.x;
@@ -375,33 +513,41 @@ __global__ __launch_bounds__(kApplyBlock) void k_sym_apply(const float* __restri
   const float a_max = a_s[n - 1];
   float ae[E], cs[E], sn[E];
   uint32_t dst[E];
+  load_anchors<E>(a_s, p0, n, a_max, vec, ae);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint64_t p = p0 + e;
     const bool valid = p < n;
-    ae[e] = valid ? a_s[p] : a_max;
-    dst[e] = valid ? perm[p] : 0u;
-    if ((uint64_t)dst[e] >= n) dst[e] = 0;
+    dst[e] = 0u;
+    if (SCATTER) {
+      dst[e] = valid ? perm[p] : 0u;
+      if ((uint64_t)dst[e] >= n) dst[e] = 0;
+    }
     cs[e] = 1.f;
     sn[e] = 0.f;
-    if (PH) sincosf(valid ? phs[p] : 0.f, &sn[e], &cs[e]);
+  }
+  if (PH) {
+    float ph[E];
+    load_anchors<E>(phs, p0, n, 0.f, true, ph);
+#pragma unroll
+    for (int e = 0; e < E; ++e) sincosf(ph[e], &sn[e], &cs[e]);
   }
   const float2 ta = tanch[tile];
   const float sf = tile > 0 ? tanch[tile - 1].y : ta.x;
   const float sb = tile + 1 < T ? tanch[tile + 1].x : ta.y;
   for (uint32_t cc = 0; cc < m / C; ++cc) {
+    float xv[E][C];
+    load_rows<E, C>(xs, p0, n, m, cc, true, xv);
     float v[E][CC];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const uint64_t p = p0 + e;
 #pragma unroll
       for (int j = 0; j < C; ++j) {
-        const float xv = (p < n) ? xs[p * m + cc * C + j] : 0.f;
         if (PH) {
-          v[e][j] = cs[e] * xv;
-          v[e][C + j] = sn[e] * xv;
+          v[e][j] = cs[e] * xv[e][j];
+          v[e][C + j] = sn[e] * xv[e][j];
         } else {
-          v[e][j] = xv;
+          v[e][j] = xv[e][j];
         }
       }
     }
@@ -412,48 +558,77 @@ __global__ __launch_bounds__(kApplyBlock) void k_sym_apply(const float* __restri
       cin_f[j] = cfw[tile * M + col];
       cin_b[j] = cbw[tile * M + col];
     }
-    tile_scan<E, CC>(ae, v, cin_f, sf, cin_b, sb, s_wf, s_wfs, s_wb, s_wbs);
+    tile_scan<E, CC, NW>(ae, v, cin_f, sf, cin_b, sb, s_wf, s_wfs, s_wb, s_wbs);
+    float yv[E][C];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if (p0 + e < n) {
-        float* yr = y + (uint64_t)dst[e] * m + cc * C;
+    for (int e = 0; e < E; ++e)
 #pragma unroll
-        for (int j = 0; j < C; ++j) yr[j] = PH ? fmaf(cs[e], v[e][j], sn[e] * v[e][C + j]) : v[e][j];
+      for (int j = 0; j < C; ++j) yv[e][j] = PH ? fmaf(cs[e], v[e][j], sn[e] * v[e][C + j]) : v[e][j];
+    if (SCATTER) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (p0 + e < n) {
+          float* yr = y + (uint64_t)dst[e] * m + cc * C;
+#pragma unroll
+          for (int j = 0; j < C; ++j) yr[j] = yv[e][j];
+        }
       }
+    } else {
+      store_rows<E, C>(y, p0, n, m, cc, true, yv);
     }
     __syncthreads();
   }
 }
 
 template <int C, bool PH>
-static hipError_t run_sym(const ApplyWorkspace& w, const float* a_s, const uint32_t* perm, const float* phi, uint64_t n,
-                          uint32_t m, const float* x, float* y, hipStream_t s) {
+static hipError_t run_sym(const ApplyWorkspace& w, const float* a_s, const uint32_t* perm, const SortRoute* route,
+                          const float* phi, uint64_t n, uint32_t m, const float* x, float* y, hipStream_t s) {
   constexpr int CC = PH ? 2 * C : C;
   constexpr int P = apply_tile(CC);
   const uint64_t T = (n + P - 1) / P;
   const uint32_t M = PH ? 2 * m : m;
-  LAPLEX_LAUNCH(PH ? "k_phased_gather_reduce" : "k_sym_gather_reduce", s,
-                k_sym_gather_reduce<C, PH><<<dim3((unsigned)T), dim3(kApplyBlock), 0, s>>>(a_s, perm, phi, x, n, m, w.xs, w.phs,
-                                                                                            w.bf, w.bb, w.tanch));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  LAPLEX_LAUNCH("k_tile_carry", s, k_tile_carry<<<1, kCarryBlock, 0, s>>>(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb));
+  const dim3 grid((unsigned)T), block(apply_block(CC));
+  const bool routed = route != nullptr && m <= kRouteMaxCols;
+  const bool vec = (reinterpret_cast<uintptr_t>(a_s) & 15) == 0;
+  hipError_t e;
+  if (routed) {
+    if ((e = route_forward(*route, n, m, x, w.xs, w.t0, w.t1, s)) != hipSuccess) return e;
+    if (PH && (e = route_forward(*route, n, 1, phi, w.phs, w.t0, w.t1, s)) != hipSuccess) return e;
+    LAPLEX_LAUNCH(PH ? "k_phased_reduce" : "k_sym_reduce", n, s,
+                  k_sym_gather_reduce<C, PH, false><<<grid, block, 0, s>>>(a_s, perm, phi, x, n, m, w.xs, w.phs, w.bf, w.bb,
+                                                                           w.tanch, vec));
+  } else {
+    LAPLEX_LAUNCH(PH ? "k_phased_gather_reduce" : "k_sym_gather_reduce", n, s,
+                  k_sym_gather_reduce<C, PH, true><<<grid, block, 0, s>>>(a_s, perm, phi, x, n, m, w.xs, w.phs, w.bf, w.bb,
+                                                                          w.tanch, vec));
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  LAPLEX_LAUNCH(PH ? "k_phased_apply" : "k_sym_apply", s,
-                k_sym_apply<C, PH><<<dim3((unsigned)T), dim3(kApplyBlock), 0, s>>>(a_s, perm, w.xs, w.phs, w.cf, w.cb, w.tanch, n,
-                                                                                    m, T, y));
+  LAPLEX_LAUNCH("k_tile_carry", T, s, k_tile_carry<<<M, kCarryBlock, 0, s>>>(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (routed) {
+    LAPLEX_LAUNCH(PH ? "k_phased_apply_sorted" : "k_sym_apply_sorted", n, s,
+                  k_sym_apply<C, PH, false><<<grid, block, 0, s>>>(a_s, perm, w.xs, w.phs, w.cf, w.cb, w.tanch, n, m, T, w.zs, vec));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return route_inverse(*route, n, m, w.zs, y, w.t0, w.t1, s);
+  }
+  LAPLEX_LAUNCH(PH ? "k_phased_apply" : "k_sym_apply", n, s,
+                k_sym_apply<C, PH, true><<<grid, block, 0, s>>>(a_s, perm, w.xs, w.phs, w.cf, w.cb, w.tanch, n, m, T, y, vec));
   return hipGetLastError();
 }
 
-hipError_t apply_sym(const ApplyWorkspace& w, Variant var, const float* a_s, const uint32_t* perm, const float* phi, uint64_t n,
-                     uint32_t m, const float* x, float* y, hipStream_t s) {
+hipError_t apply_sym(const ApplyWorkspace& w, Variant var, const float* a_s, const uint32_t* perm, const SortRoute* route,
+                     const float* phi, uint64_t n, uint32_t m, const float* x, float* y, hipStream_t s) {
   const bool ph = var == Variant::Phased;
+#define LAPLEX_SYM(CW)                                                               \
+  return ph ? run_sym<CW, true>(w, a_s, perm, route, phi, n, m, x, y, s)          \
+            : run_sym<CW, false>(w, a_s, perm, route, phi, n, m, x, y, s)
   switch (column_chunk(m)) {
-    case 8: return ph ? run_sym<8, true>(w, a_s, perm, phi, n, m, x, y, s) : run_sym<8, false>(w, a_s, perm, phi, n, m, x, y, s);
-    case 4: return ph ? run_sym<4, true>(w, a_s, perm, phi, n, m, x, y, s) : run_sym<4, false>(w, a_s, perm, phi, n, m, x, y, s);
-    case 2: return ph ? run_sym<2, true>(w, a_s, perm, phi, n, m, x, y, s) : run_sym<2, false>(w, a_s, perm, phi, n, m, x, y, s);
-    default: return ph ? run_sym<1, true>(w, a_s, perm, phi, n, m, x, y, s) : run_sym<1, false>(w, a_s, perm, phi, n, m, x, y, s);
+    case 8: LAPLEX_SYM(8);
+    case 4: LAPLEX_SYM(4);
+    case 2: LAPLEX_SYM(2);
+    default: LAPLEX_SYM(1);
   }
+#undef LAPLEX_SYM
 }
 
 // ---------------------------------------------------------------- general (merged a and b)
@@ -484,14 +659,16 @@ __global__ void k_gather_rows(const float* __restrict__ x, const uint32_t* __res
 }
 
 template <int C, bool PH>
-__global__ __launch_bounds__(kApplyBlock) void k_gen_reduce(const float* __restrict__ a_s, uint64_t n, const float* __restrict__ b_s,
+__global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_gen_reduce(const float* __restrict__ a_s, uint64_t n, const float* __restrict__ b_s,
                                                             uint64_t k, const float* __restrict__ xbs, const float* __restrict__ psis,
                                                             uint32_t m, uint64_t T, float* __restrict__ bf, float* __restrict__ bb,
                                                             float2* __restrict__ tanch, uint2* __restrict__ tsplit) {
   constexpr int CC = PH ? 2 * C : C;
   constexpr int E = apply_items(CC);
-  constexpr int P = kApplyBlock * E;
-  __shared__ float s_red[2 * kApplyWaves * CC];
+  constexpr int BLOCK = apply_block(CC);
+  constexpr int NW = BLOCK / kWave;
+  constexpr int P = BLOCK * E;
+  __shared__ float s_red[2 * NW * CC];
   __shared__ uint64_t s_split[4];
   const uint32_t M = PH ? 2 * m : m;
   const int tid = threadIdx.x;
@@ -525,7 +702,7 @@ __global__ __launch_bounds__(kApplyBlock) void k_gen_reduce(const float* __restr
     float sf[CC], sb[CC];
 #pragma unroll
     for (int j = 0; j < CC; ++j) sf[j] = sb[j] = 0.f;
-    for (uint64_t jb = j0 + tid; jb < j1; jb += kApplyBlock) {
+    for (uint64_t jb = j0 + tid; jb < j1; jb += BLOCK) {
       const float bj = b_s[jb];
       const float wf = decay(bj - s_last), wb = decay(s_first - bj);
       float cs = 1.f, sn = 0.f;
@@ -547,12 +724,12 @@ __global__ __launch_bounds__(kApplyBlock) void k_gen_reduce(const float* __restr
       }
     }
     int writer = 0;
-    block_sum2<CC>(sf, sb, s_red, writer);
+    block_sum2<CC, NW>(sf, sb, s_red, writer);
     if (writer) {
       float tf = 0.f, tb = 0.f;
-      for (int w = 0; w < kApplyWaves; ++w) {
-        tf += s_red[(0 * kApplyWaves + w) * CC + tid];
-        tb += s_red[(1 * kApplyWaves + w) * CC + tid];
+      for (int w = 0; w < NW; ++w) {
+        tf += s_red[(0 * NW + w) * CC + tid];
+        tb += s_red[(1 * NW + w) * CC + tid];
       }
       const uint32_t col = sumcol<C, PH>(m, cc, tid);
       bf[tile * M + col] = tf;
@@ -562,8 +739,11 @@ __global__ __launch_bounds__(kApplyBlock) void k_gen_reduce(const float* __restr
   }
 }
 
-template <int C, bool PH>
-__global__ __launch_bounds__(kApplyBlock) void k_gen_apply(const float* __restrict__ a_s, const uint32_t* __restrict__ perm_a,
+// SCATTER: a-side outputs go to y in original order (through perm_a, phases
+// phi in original order); otherwise to y in sorted-a order, with phi already
+// in sorted-a order.
+template <int C, bool PH, bool SCATTER>
+__global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_gen_apply(const float* __restrict__ a_s, const uint32_t* __restrict__ perm_a,
                                                            const float* __restrict__ phi, uint64_t n, const float* __restrict__ b_s,
                                                            uint64_t k, const float* __restrict__ xbs, const float* __restrict__ psis,
                                                            uint32_t m, uint64_t T, const float* __restrict__ cfw,
@@ -571,16 +751,18 @@ __global__ __launch_bounds__(kApplyBlock) void k_gen_apply(const float* __restri
                                                            const uint2* __restrict__ tsplit, float* __restrict__ y) {
   constexpr int CC = PH ? 2 * C : C;
   constexpr int E = apply_items(CC);
-  constexpr int P = kApplyBlock * E;
+  constexpr int BLOCK = apply_block(CC);
+  constexpr int NW = BLOCK / kWave;
+  constexpr int P = BLOCK * E;
   __shared__ float s_a[P], s_b[P];
-  __shared__ float s_wf[kApplyWaves * CC], s_wb[kApplyWaves * CC], s_wfs[kApplyWaves], s_wbs[kApplyWaves];
+  __shared__ float s_wf[NW * CC], s_wb[NW * CC], s_wfs[NW], s_wbs[NW];
   const uint32_t M = PH ? 2 * m : m;
   const int tid = threadIdx.x;
   const uint64_t tile = blockIdx.x;
   const uint2 sp0 = tsplit[tile], sp1 = tsplit[tile + 1];
   const uint32_t na = std::min<uint32_t>(sp1.x - sp0.x, P), nb = std::min<uint32_t>(sp1.y - sp0.y, P - na);
-  for (uint32_t i = tid; i < na; i += kApplyBlock) s_a[i] = a_s[(uint64_t)sp0.x + i];
-  for (uint32_t i = tid; i < nb; i += kApplyBlock) s_b[i] = b_s[(uint64_t)sp0.y + i];
+  for (uint32_t i = tid; i < na; i += BLOCK) s_a[i] = a_s[(uint64_t)sp0.x + i];
+  for (uint32_t i = tid; i < nb; i += BLOCK) s_b[i] = b_s[(uint64_t)sp0.y + i];
   __syncthreads();
   const float s_max = fmaxf(a_s[n - 1], b_s[k - 1]);
   // this thread's E merged elements
@@ -621,7 +803,7 @@ __global__ __launch_bounds__(kApplyBlock) void k_gen_apply(const float* __restri
     sn[e] = 0.f;
     dst[e] = 0;
     if (kind[e] == 1) {
-      dst[e] = perm_a[idx[e]];
+      dst[e] = SCATTER ? perm_a[idx[e]] : idx[e];
       if ((uint64_t)dst[e] >= n) dst[e] = 0;
       if (PH) sincosf(phi[dst[e]], &sn[e], &cs[e]);
     } else if (kind[e] == 2 && PH) {
@@ -653,7 +835,7 @@ __global__ __launch_bounds__(kApplyBlock) void k_gen_apply(const float* __restri
       cin_f[j] = cfw[tile * M + col];
       cin_b[j] = cbw[tile * M + col];
     }
-    tile_scan<E, CC>(ae, v, cin_f, sf, cin_b, sb, s_wf, s_wfs, s_wb, s_wbs);
+    tile_scan<E, CC, NW>(ae, v, cin_f, sf, cin_b, sb, s_wf, s_wfs, s_wb, s_wbs);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       if (kind[e] == 1) {
@@ -667,36 +849,55 @@ __global__ __launch_bounds__(kApplyBlock) void k_gen_apply(const float* __restri
 }
 
 template <int C, bool PH>
-static hipError_t run_general(const ApplyWorkspace& w, const float* a_s, const uint32_t* perm_a, const float* phi, uint64_t n,
-                              const float* b_s, const uint32_t* perm_b, const float* psi, uint64_t k, uint32_t m, const float* x,
-                              float* y, hipStream_t s) {
+static hipError_t run_general(const ApplyWorkspace& w, const float* a_s, const uint32_t* perm_a, const SortRoute* route_a,
+                              const float* phi, uint64_t n, const float* b_s, const uint32_t* perm_b, const SortRoute* route_b,
+                              const float* psi, uint64_t k, uint32_t m, const float* x, float* y, hipStream_t s) {
   constexpr int CC = PH ? 2 * C : C;
   constexpr int P = apply_tile(CC);
   const uint64_t T = (n + k + P - 1) / P;
   const uint32_t M = PH ? 2 * m : m;
-  const unsigned gblocks = (unsigned)std::min<uint64_t>((k + 255) / 256, 8192);
-  LAPLEX_LAUNCH("k_gather_rows", s, k_gather_rows<<<gblocks, 256, 0, s>>>(x, perm_b, PH ? psi : nullptr, k, m, w.xs, w.phs));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  LAPLEX_LAUNCH(PH ? "k_phased_gen_reduce" : "k_gen_reduce", s,
-                k_gen_reduce<C, PH><<<dim3((unsigned)T), dim3(kApplyBlock), 0, s>>>(a_s, n, b_s, k, w.xs, w.phs, m, T, w.bf, w.bb,
-                                                                                     w.tanch, w.tsplit));
+  const dim3 grid((unsigned)T), block(apply_block(CC));
+  hipError_t e;
+  // inputs into sorted-b order
+  if (route_b != nullptr && m <= kRouteMaxCols) {
+    if ((e = route_forward(*route_b, k, m, x, w.xs, w.t0, w.t1, s)) != hipSuccess) return e;
+    if (PH && (e = route_forward(*route_b, k, 1, psi, w.phs, w.t0, w.t1, s)) != hipSuccess) return e;
+  } else {
+    const unsigned gblocks = (unsigned)std::min<uint64_t>((k + 255) / 256, 8192);
+    LAPLEX_LAUNCH("k_gather_rows", k, s,
+                  k_gather_rows<<<gblocks, 256, 0, s>>>(x, perm_b, PH ? psi : nullptr, k, m, w.xs, w.phs));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  LAPLEX_LAUNCH(PH ? "k_phased_gen_reduce" : "k_gen_reduce", k, s,
+                k_gen_reduce<C, PH><<<grid, block, 0, s>>>(a_s, n, b_s, k, w.xs, w.phs, m, T, w.bf, w.bb, w.tanch, w.tsplit));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  LAPLEX_LAUNCH("k_tile_carry", s, k_tile_carry<<<1, kCarryBlock, 0, s>>>(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb));
+  LAPLEX_LAUNCH("k_tile_carry", T, s, k_tile_carry<<<M, kCarryBlock, 0, s>>>(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  LAPLEX_LAUNCH(PH ? "k_phased_gen_apply" : "k_gen_apply", s,
-                k_gen_apply<C, PH><<<dim3((unsigned)T), dim3(kApplyBlock), 0, s>>>(a_s, perm_a, phi, n, b_s, k, w.xs, w.phs, m, T,
-                                                                                    w.cf, w.cb, w.tanch, w.tsplit, y));
+  if (route_a != nullptr && m <= kRouteMaxCols) {
+    const float* phas = nullptr;
+    if (PH) {
+      if ((e = route_forward(*route_a, n, 1, phi, w.phas, w.t0, w.t1, s)) != hipSuccess) return e;
+      phas = w.phas;
+    }
+    LAPLEX_LAUNCH(PH ? "k_phased_gen_apply_sorted" : "k_gen_apply_sorted", n, s,
+                  k_gen_apply<C, PH, false><<<grid, block, 0, s>>>(a_s, perm_a, phas, n, b_s, k, w.xs, w.phs, m, T, w.cf, w.cb,
+                                                                   w.tanch, w.tsplit, w.zs));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return route_inverse(*route_a, n, m, w.zs, y, w.t0, w.t1, s);
+  }
+  LAPLEX_LAUNCH(PH ? "k_phased_gen_apply" : "k_gen_apply", n, s,
+                k_gen_apply<C, PH, true><<<grid, block, 0, s>>>(a_s, perm_a, phi, n, b_s, k, w.xs, w.phs, m, T, w.cf, w.cb,
+                                                                w.tanch, w.tsplit, y));
   return hipGetLastError();
 }
 
-hipError_t apply_general(const ApplyWorkspace& w, Variant var, const float* a_s, const uint32_t* perm_a, const float* phi,
-                         uint64_t n, const float* b_s, const uint32_t* perm_b, const float* psi, uint64_t k, uint32_t m,
-                         const float* x, float* y, hipStream_t s) {
+hipError_t apply_general(const ApplyWorkspace& w, Variant var, const float* a_s, const uint32_t* perm_a, const SortRoute* route_a,
+                         const float* phi, uint64_t n, const float* b_s, const uint32_t* perm_b, const SortRoute* route_b,
+                         const float* psi, uint64_t k, uint32_t m, const float* x, float* y, hipStream_t s) {
   const bool ph = var == Variant::Phased;
-#define LAPLEX_GEN(CW)                                                                                  \
-  return ph ? run_general<CW, true>(w, a_s, perm_a, phi, n, b_s, perm_b, psi, k, m, x, y, s)          \
-            : run_general<CW, false>(w, a_s, perm_a, phi, n, b_s, perm_b, psi, k, m, x, y, s)
+#define LAPLEX_GEN(CW)                                                                                                   \
+  return ph ? run_general<CW, true>(w, a_s, perm_a, route_a, phi, n, b_s, perm_b, route_b, psi, k, m, x, y, s)          \
+            : run_general<CW, false>(w, a_s, perm_a, route_a, phi, n, b_s, perm_b, route_b, psi, k, m, x, y, s)
   switch (column_chunk(m)) {
     case 8: LAPLEX_GEN(8);
     case 4: LAPLEX_GEN(4);

@@ -12,13 +12,14 @@ namespace laplex {
 // ------------------------------------------------------------------ opt-in launch profiler
 // When enabled through laplex_profile_begin, each kernel launch is bracketed
 // by two hipEvents recorded on its stream; otherwise these are no-ops.
+// UNITS is the number of elements (rows) the launch processes.
 int prof_begin(hipStream_t s);
-void prof_end(int slot, const char* name, hipStream_t s);
-#define LAPLEX_LAUNCH(NAME, STREAM, ...)                \
-  do {                                                  \
-    const int prof_slot_ = ::laplex::prof_begin(STREAM); \
-    __VA_ARGS__;                                        \
-    ::laplex::prof_end(prof_slot_, (NAME), (STREAM));   \
+void prof_end(int slot, const char* name, uint64_t units, hipStream_t s);
+#define LAPLEX_LAUNCH(NAME, UNITS, STREAM, ...)                  \
+  do {                                                           \
+    const int prof_slot_ = ::laplex::prof_begin(STREAM);         \
+    __VA_ARGS__;                                                 \
+    ::laplex::prof_end(prof_slot_, (NAME), (UNITS), (STREAM));   \
   } while (0)
 
 // ------------------------------------------------------------------ sort
@@ -43,14 +44,37 @@ struct SortWorkspace {
   uint32_t* vals[2];  // ping-pong value buffers, n each
 };
 
+// Route of a sort: for every radix pass, the tile-local sorted position of
+// each element of the pass's input, and per tile the start of each digit's
+// run in that order and its global position.  With it a payload can be moved
+// between original and sorted order by the same run-coalesced passes the
+// sort made (forward: scatter in runs; inverse: gather in runs).
+struct SortRoute {
+  uint16_t* lpos[4];    // [n]
+  uint16_t* dstart[4];  // [tiles][256]
+  uint32_t* gbase[4];   // [tiles][256] run position minus local start (mod 2^32)
+};
+size_t route_bytes(uint64_t n);
+SortRoute carve_route(const void* base, uint64_t n);
+
 size_t sort_status_bytes(uint64_t n);
-hipError_t sort_anchors(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm, hipStream_t s);
+hipError_t sort_anchors(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,
+                        const SortRoute* route, hipStream_t s);
+
+// Move rows of W floats through the sort's passes: forward (original ->
+// sorted order) or inverse (sorted -> original).  t0, t1: scratch, n rows each.
+hipError_t route_forward(const SortRoute& r, uint64_t n, uint32_t W, const float* in, float* out, float* t0, float* t1,
+                         hipStream_t s);
+hipError_t route_inverse(const SortRoute& r, uint64_t n, uint32_t W, const float* in, float* out, float* t0, float* t1,
+                         hipStream_t s);
+constexpr uint32_t kRouteMaxCols = 4;
 
 // ------------------------------------------------------------------ apply
-constexpr int kApplyBlock = 256;
-// values per thread: E items x CC columns = 16
-constexpr int apply_items(int cc) { return cc >= 16 ? 1 : 16 / cc; }
-constexpr int apply_tile(int cc) { return kApplyBlock * apply_items(cc); }
+// Tile shape for CC injected columns: E consecutive items per thread (the
+// single-column cases load them as one float4/float2), threads per block.
+constexpr int apply_items(int cc) { return cc == 1 ? 4 : cc == 2 ? 2 : cc >= 16 ? 1 : 16 / cc; }
+constexpr int apply_block(int cc) { return cc <= 2 ? 1024 : 256; }
+constexpr int apply_tile(int cc) { return apply_block(cc) * apply_items(cc); }
 
 // column chunk: the largest of 8, 4, 2, 1 that divides m
 inline uint32_t column_chunk(uint32_t m) { return (m % 8 == 0) ? 8 : (m % 4 == 0) ? 4 : (m % 2 == 0) ? 2 : 1; }
@@ -58,6 +82,10 @@ inline uint32_t column_chunk(uint32_t m) { return (m % 8 == 0) ? 8 : (m % 4 == 0
 struct ApplyWorkspace {
   float* xs;       // gathered inputs in sorted order (rows x m)
   float* phs;      // gathered input phases in sorted order (phased)
+  float* zs;       // outputs in sorted order before the inverse route (rows_out x m)
+  float* phas;     // output phases in sorted order (phased general with a route)
+  float* t0;       // route scratch (max rows x m)
+  float* t1;       // route scratch (max rows x m)
   float* bf;       // [tiles][M] forward tile aggregates
   float* bb;       // [tiles][M] backward tile aggregates
   float* cf;       // [tiles][M] forward carry into each tile
@@ -68,11 +96,12 @@ struct ApplyWorkspace {
 
 enum class Variant { Sym, Phased };
 
-hipError_t apply_sym(const ApplyWorkspace& w, Variant var, const float* a_s, const uint32_t* perm, const float* phi, uint64_t n,
-                     uint32_t m, const float* x, float* y, hipStream_t s);
-hipError_t apply_general(const ApplyWorkspace& w, Variant var, const float* a_s, const uint32_t* perm_a, const float* phi,
-                         uint64_t n, const float* b_s, const uint32_t* perm_b, const float* psi, uint64_t k, uint32_t m,
-                         const float* x, float* y, hipStream_t s);
+// route / route_a / route_b may be null (then x and y move by index).
+hipError_t apply_sym(const ApplyWorkspace& w, Variant var, const float* a_s, const uint32_t* perm, const SortRoute* route,
+                     const float* phi, uint64_t n, uint32_t m, const float* x, float* y, hipStream_t s);
+hipError_t apply_general(const ApplyWorkspace& w, Variant var, const float* a_s, const uint32_t* perm_a, const SortRoute* route_a,
+                         const float* phi, uint64_t n, const float* b_s, const uint32_t* perm_b, const SortRoute* route_b,
+                         const float* psi, uint64_t k, uint32_t m, const float* x, float* y, hipStream_t s);
 
 // tile count and summary width of an apply
 inline uint64_t apply_tiles(uint64_t len, uint32_t m, Variant var) {

@@ -111,7 +111,9 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
                                                          uint32_t* __restrict__ kout, uint32_t* __restrict__ vout,
                                                          const uint32_t* __restrict__ a_bits, ST* __restrict__ status,
                                                          uint32_t* __restrict__ header, int pass,
-                                                         const uint32_t* __restrict__ digit_start, uint64_t n) {
+                                                         const uint32_t* __restrict__ digit_start, uint64_t n,
+                                                         uint16_t* __restrict__ r_lpos, uint16_t* __restrict__ r_dstart,
+                                                         uint32_t* __restrict__ r_gbase) {
   static_assert(kSortBlock == 256, "one thread per digit value");
   constexpr int E = kSortItems;
   constexpr int TILE = kSortTile;
@@ -211,6 +213,10 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
   const uint32_t dstart = pre + x - cnt;
   s_dstart[d] = dstart;
   s_gbase[d] = digit_start[d] + excl - dstart;  // modular: gbase + local index >= 0
+  if (r_dstart != nullptr) {
+    r_dstart[(uint64_t)tile * 256 + d] = (uint16_t)dstart;
+    r_gbase[(uint64_t)tile * 256 + d] = digit_start[d] + excl - dstart;
+  }
   __syncthreads();
 
   // place the keys in LDS in digit order (stable)
@@ -222,6 +228,7 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
       const uint32_t pos = s_dstart[dd] + s_whist[wid][dd] + rk[e];
       s_keys[pos] = k[e];
       s_vals[pos] = v[e];
+      if (r_lpos != nullptr) r_lpos[idx] = (uint16_t)pos;
     }
   }
   __syncthreads();
@@ -247,7 +254,7 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
 // ------------------------------------------------------------------ host side
 template <typename ST>
 static hipError_t launch_sort_passes(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,
-                                     hipStream_t s) {
+                                     const SortRoute* route, hipStream_t s) {
   const uint32_t* a_bits = reinterpret_cast<const uint32_t*>(a);
   const uint64_t tiles = (n + kSortTile - 1) / kSortTile;
   ST* st = reinterpret_cast<ST*>(w.status);
@@ -257,18 +264,21 @@ static hipError_t launch_sort_passes(const SortWorkspace& w, const float* a, uin
     ST* stp = st + (uint64_t)p * tiles * 256;
     uint32_t* dk = (p == 3) ? reinterpret_cast<uint32_t*>(a_sorted) : w.keys[p & 1];
     uint32_t* dv = (p == 3) ? perm : w.vals[p & 1];
+    uint16_t* rl = route ? route->lpos[p] : nullptr;
+    uint16_t* rd = route ? route->dstart[p] : nullptr;
+    uint32_t* rg = route ? route->gbase[p] : nullptr;
     if (p == 0)
-      LAPLEX_LAUNCH("k_onesweep_first", s,
+      LAPLEX_LAUNCH(route ? "k_onesweep_first_routed" : "k_onesweep_first", n, s,
                     k_onesweep<0, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(
-                        a_bits, nullptr, dk, dv, a_bits, stp, w.header, p, w.offsets + p * 256, n));
+                        a_bits, nullptr, dk, dv, a_bits, stp, w.header, p, w.offsets + p * 256, n, rl, rd, rg));
     else if (p == 3)
-      LAPLEX_LAUNCH("k_onesweep_last", s,
+      LAPLEX_LAUNCH(route ? "k_onesweep_last_routed" : "k_onesweep_last", n, s,
                     k_onesweep<2, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(
-                        src_k, src_v, dk, dv, a_bits, stp, w.header, p, w.offsets + p * 256, n));
+                        src_k, src_v, dk, dv, a_bits, stp, w.header, p, w.offsets + p * 256, n, rl, rd, rg));
     else
-      LAPLEX_LAUNCH("k_onesweep_mid", s,
+      LAPLEX_LAUNCH(route ? "k_onesweep_mid_routed" : "k_onesweep_mid", n, s,
                     k_onesweep<1, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(
-                        src_k, src_v, dk, dv, a_bits, stp, w.header, p, w.offsets + p * 256, n));
+                        src_k, src_v, dk, dv, a_bits, stp, w.header, p, w.offsets + p * 256, n, rl, rd, rg));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     src_k = dk;
@@ -283,22 +293,23 @@ size_t sort_status_bytes(uint64_t n) {
   return (size_t)(4 * tiles * 256) * word;
 }
 
-hipError_t sort_anchors(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm, hipStream_t s) {
+hipError_t sort_anchors(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,
+                        const SortRoute* route, hipStream_t s) {
   // clear the header, histograms and look-back status with a fill kernel
   const uint64_t clear_words = (uint64_t)(kSortHeaderBytes / 4) + sort_status_bytes(n) / 4;
   const unsigned fill_blocks = (unsigned)std::min<uint64_t>((clear_words + 255) / 256, 4096);
-  LAPLEX_LAUNCH("k_fill_u32", s, k_fill_u32<<<fill_blocks, 256, 0, s>>>(w.header, clear_words, 0u));
+  LAPLEX_LAUNCH("k_fill_u32", clear_words, s, k_fill_u32<<<fill_blocks, 256, 0, s>>>(w.header, clear_words, 0u));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint64_t chunk = (uint64_t)kHistBlock * kHistItems;
   const unsigned hist_blocks = (unsigned)std::min<uint64_t>((n + chunk - 1) / chunk, 2048);
-  LAPLEX_LAUNCH("k_sort_hist", s,
+  LAPLEX_LAUNCH("k_sort_hist", n, s,
                 k_sort_hist<<<hist_blocks, kHistBlock, 0, s>>>(reinterpret_cast<const uint32_t*>(a), n, w.hist, w.header));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  LAPLEX_LAUNCH("k_sort_offsets", s, k_sort_offsets<<<1, 256, 0, s>>>(w.hist, w.offsets));
+  LAPLEX_LAUNCH("k_sort_offsets", 1024, s, k_sort_offsets<<<1, 256, 0, s>>>(w.hist, w.offsets));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (n <= (1ull << 30)) return launch_sort_passes<uint32_t>(w, a, n, a_sorted, perm, s);
-  return launch_sort_passes<uint64_t>(w, a, n, a_sorted, perm, s);
+  if (n <= (1ull << 30)) return launch_sort_passes<uint32_t>(w, a, n, a_sorted, perm, route, s);
+  return launch_sort_passes<uint64_t>(w, a, n, a_sorted, perm, route, s);
 }
 
 }  // namespace laplex
@@ -307,7 +318,7 @@ namespace laplex {
 hipError_t fill_zero_u32(void* p, uint64_t words, hipStream_t s) {
   if (words == 0) return hipSuccess;
   const unsigned blocks = (unsigned)std::min<uint64_t>((words + 255) / 256, 4096);
-  LAPLEX_LAUNCH("k_fill_u32", s, k_fill_u32<<<blocks, 256, 0, s>>>(static_cast<uint32_t*>(p), words, 0u));
+  LAPLEX_LAUNCH("k_fill_u32", words, s, k_fill_u32<<<blocks, 256, 0, s>>>(static_cast<uint32_t*>(p), words, 0u));
   return hipGetLastError();
 }
 }  // namespace laplex

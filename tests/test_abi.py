@@ -57,31 +57,37 @@ def test_host_argument_errors(L):
     W = vp(0x400000)
     OK, NULL, SIZE, ALIGN, WS, OVERLAP = 0, 1, 2, 3, 4, 7
     # n == 0 / m == 0 are no-ops
-    assert L.laplex_sort_anchors(None, 0, None, None, None, 0, None) == OK
-    assert L.laplex_matvec_sym(None, None, 0, 1, None, None, None, 0, None) == OK
-    assert L.laplex_matvec_sym(A, B, 10, 0, A, B, W, 0, None) == OK
+    assert L.laplex_sort_anchors(None, 0, None, None, None, 0, None, 0, None) == OK
+    assert L.laplex_matvec_sym(None, None, None, 0, 1, None, None, None, 0, None) == OK
+    assert L.laplex_matvec_sym(A, B, None, 10, 0, A, B, W, 0, None) == OK
     # NULL
-    assert L.laplex_sort_anchors(None, 10, B, A, W, 1 << 30, None) == NULL
-    assert L.laplex_matvec_sym(A, B, 10, 1, None, B, W, 1 << 30, None) == NULL
+    assert L.laplex_sort_anchors(None, 10, B, A, None, 0, W, 1 << 30, None) == NULL
+    assert L.laplex_matvec_sym(A, B, None, 10, 1, None, B, W, 1 << 30, None) == NULL
     assert L.laplex_status_poll(None, None) == NULL
     # size
-    assert L.laplex_sort_anchors(A, 1 << 32, B, A, W, 1 << 40, None) == SIZE
-    assert L.laplex_matvec_sym(A, B, 1 << 32, 1, A, B, W, 1 << 40, None) == SIZE
+    assert L.laplex_sort_anchors(A, 1 << 32, B, A, None, 0, W, 1 << 40, None) == SIZE
+    assert L.laplex_matvec_sym(A, B, None, 1 << 32, 1, A, B, W, 1 << 40, None) == SIZE
     # alignment
-    assert L.laplex_sort_anchors(vp(0x100002), 10, B, vp(0x300000), W, 1 << 30, None) == ALIGN
-    assert L.laplex_sort_anchors(A, 10, B, vp(0x300000), vp(0x400010), 1 << 30, None) == ALIGN
+    assert L.laplex_sort_anchors(vp(0x100002), 10, B, vp(0x300000), None, 0, W, 1 << 30, None) == ALIGN
+    assert L.laplex_sort_anchors(A, 10, B, vp(0x300000), None, 0, vp(0x400010), 1 << 30, None) == ALIGN
     # workspace too small
-    assert L.laplex_sort_anchors(A, 1000, B, vp(0x300000), W, 64, None) == WS
-    assert L.laplex_matvec_sym(A, vp(0x300000), 1000, 4, vp(0x500000), vp(0x600000), W, 64, None) == WS
+    assert L.laplex_sort_anchors(A, 1000, B, vp(0x300000), None, 0, W, 64, None) == WS
+    assert L.laplex_matvec_sym(A, vp(0x300000), None, 1000, 4, vp(0x500000), vp(0x600000), W, 64, None) == WS
     # overlap: y on top of x
     need = L.laplex_workspace_bytes(1, 1000, 0, 1)
-    assert L.laplex_matvec_sym(A, vp(0x300000), 1000, 1, vp(0x500000), vp(0x500100), vp(0x10000000), need, None) == OVERLAP
-    assert L.laplex_sort_anchors(A, 1000, vp(0x100100), vp(0x300000), vp(0x10000000), 1 << 30, None) == OVERLAP
+    assert L.laplex_matvec_sym(A, vp(0x300000), None, 1000, 1, vp(0x500000), vp(0x500100), vp(0x10000000), need, None) == OVERLAP
+    assert L.laplex_sort_anchors(A, 1000, vp(0x100100), vp(0x300000), None, 0, vp(0x10000000), 1 << 30, None) == OVERLAP
     # general without b
     need = L.laplex_workspace_bytes(2, 100, 50, 1)
-    assert L.laplex_matvec_general(A, vp(0x300000), 100, None, None, 50, 1, vp(0x500000), vp(0x600000), W, need, None) == NULL
-    assert L.laplex_matvec_phased(A, vp(0x300000), None, 100, None, None, None, 0, 1, vp(0x500000), vp(0x600000), W, need,
-                                  None) == NULL
+    assert L.laplex_matvec_general(A, vp(0x300000), None, 100, None, None, None, 50, 1, vp(0x500000), vp(0x600000), W, need, None) == NULL
+    assert L.laplex_matvec_phased(A, vp(0x300000), None, None, 100, None, None, None, None, 0, 1, vp(0x500000),
+                                  vp(0x600000), W, need, None) == NULL
+    # route: too small, misaligned, overlapping
+    assert L.laplex_sort_anchors(A, 1000, B, vp(0x300000), vp(0x20000000), 16, vp(0x10000000), 1 << 30, None) == WS
+    assert L.laplex_sort_anchors(A, 1000, B, vp(0x300000), vp(0x20000010), 1 << 20, vp(0x10000000), 1 << 30, None) == ALIGN
+    assert L.laplex_sort_anchors(A, 1000, B, vp(0x300000), vp(0x100000), 1 << 20, vp(0x10000000), 1 << 30, None) == OVERLAP
+    assert L.laplex_route_bytes(1 << 20) >= 4 * 2 * (1 << 20)
+    assert L.laplex_route_bytes(1 << 32) == 0
     assert L.laplex_status_string(4) == b"workspace too small"
 
 
