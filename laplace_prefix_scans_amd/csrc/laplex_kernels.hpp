@@ -23,7 +23,7 @@ void prof_end(int slot, const char* name, uint64_t units, hipStream_t s);
   } while (0)
 
 // ------------------------------------------------------------------ sort
-constexpr int kSortBlock = 256;
+constexpr int kSortBlock = 512;
 constexpr int kSortItems = 16;
 constexpr int kSortTile = kSortBlock * kSortItems;
 

@@ -20,12 +20,59 @@ __device__ __forceinline__ void paint_digits(const uint16_t* s_start, uint8_t* s
   }
 }
 
+// The side of a route pass that runs in input order is read or written in
+// groups of kGroup consecutive elements per thread (one 8-byte load of their
+// positions, W vector loads of their rows when `vec`); the side that runs in
+// digit runs moves one element per thread and step, all steps unrolled.
+constexpr int kGroup = 4;
+
+template <int W>
+__device__ __forceinline__ void ld_group(const float* __restrict__ p, float (&v)[kGroup * W], bool vec) {
+  if (vec) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const float4 q = reinterpret_cast<const float4*>(p)[i];
+      v[4 * i] = q.x;
+      v[4 * i + 1] = q.y;
+      v[4 * i + 2] = q.z;
+      v[4 * i + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kGroup * W; ++i) v[i] = p[i];
+  }
+}
+template <int W>
+__device__ __forceinline__ void st_group(float* __restrict__ p, const float (&v)[kGroup * W], bool vec) {
+  if (vec) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) reinterpret_cast<float4*>(p)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kGroup * W; ++i) p[i] = v[i];
+  }
+}
+
+// Tile tables into LDS: run starts (clamped to the tile) and run positions.
+__device__ __forceinline__ void load_tables(const uint16_t* __restrict__ dstart, const uint32_t* __restrict__ gbase, uint64_t tile,
+                                            uint32_t count, uint16_t* s_start, uint32_t* s_gb) {
+  const int tid = threadIdx.x;
+  if (tid < 256) {
+    s_start[tid] = std::min<uint16_t>(dstart[tile * 256 + tid], (uint16_t)count);
+    s_gb[tid] = gbase[tile * 256 + tid];
+  }
+  if (tid == 0) s_start[256] = (uint16_t)count;
+}
+
+// vec: `in` (fwd) or `out` (inv), the input-order side, is 16-byte aligned.
 template <int W>
 __global__ __launch_bounds__(kSortBlock) void k_route_fwd(const float* __restrict__ in, float* __restrict__ out,
                                                           const uint16_t* __restrict__ lpos, const uint16_t* __restrict__ dstart,
-                                                          const uint32_t* __restrict__ gbase, uint64_t n) {
+                                                          const uint32_t* __restrict__ gbase, uint64_t n, bool vec) {
   constexpr int TILE = kSortTile;
   constexpr int NW = kSortBlock / kWave;
+  constexpr int STEPS = TILE / kSortBlock;
+  constexpr int GSTEPS = TILE / (kSortBlock * kGroup);
   __shared__ float s_val[TILE * W];
   __shared__ uint8_t s_dig[TILE];
   __shared__ uint16_t s_start[257];
@@ -33,25 +80,45 @@ __global__ __launch_bounds__(kSortBlock) void k_route_fwd(const float* __restric
   const int tid = threadIdx.x;
   const uint64_t tile = blockIdx.x, base = tile * TILE;
   const uint32_t count = (uint32_t)std::min<uint64_t>(TILE, n - base);
-  s_start[tid] = std::min<uint16_t>(dstart[tile * 256 + tid], (uint16_t)count);
-  s_gb[tid] = gbase[tile * 256 + tid];
-  if (tid == 0) s_start[256] = (uint16_t)count;
-  __syncthreads();
-  paint_digits<NW>(s_start, s_dig);
-  for (uint32_t i = tid; i < count; i += kSortBlock) {
-    const uint64_t j = base + i;
-    const uint32_t lp = lpos[j];
-    if (lp < count) {
+  load_tables(dstart, gbase, tile, count, s_start, s_gb);
+  // input order side: rows to their tile-local sorted position
 #pragma unroll
-      for (int c = 0; c < W; ++c) s_val[lp * W + c] = in[j * W + c];
+  for (int r = 0; r < GSTEPS; ++r) {
+    const uint32_t i0 = (uint32_t)(r * kSortBlock + tid) * kGroup;
+    if (i0 + kGroup <= count) {
+      const uint2 lp2 = *reinterpret_cast<const uint2*>(lpos + base + i0);
+      const uint32_t lp[kGroup] = {lp2.x & 0xFFFFu, lp2.x >> 16, lp2.y & 0xFFFFu, lp2.y >> 16};
+      float v[kGroup * W];
+      ld_group<W>(in + (base + i0) * W, v, vec);
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g)
+        if (lp[g] < count) {
+#pragma unroll
+          for (int c = 0; c < W; ++c) s_val[lp[g] * W + c] = v[g * W + c];
+        }
+    } else {
+      for (uint32_t i = i0; i < count && i < i0 + kGroup; ++i) {
+        const uint32_t lp = lpos[base + i];
+        if (lp < count) {
+#pragma unroll
+          for (int c = 0; c < W; ++c) s_val[lp * W + c] = in[(base + i) * W + c];
+        }
+      }
     }
   }
   __syncthreads();
-  for (uint32_t i = tid; i < count; i += kSortBlock) {
-    const uint32_t o = s_gb[s_dig[i]] + i;
-    if ((uint64_t)o < n) {
+  paint_digits<NW>(s_start, s_dig);
+  __syncthreads();
+  // digit-run side: each run written contiguously
 #pragma unroll
-      for (int c = 0; c < W; ++c) out[(uint64_t)o * W + c] = s_val[i * W + c];
+  for (int r = 0; r < STEPS; ++r) {
+    const uint32_t i = (uint32_t)(r * kSortBlock + tid);
+    if (i < count) {
+      const uint32_t o = s_gb[s_dig[i]] + i;
+      if ((uint64_t)o < n) {
+#pragma unroll
+        for (int c = 0; c < W; ++c) out[(uint64_t)o * W + c] = s_val[i * W + c];
+      }
     }
   }
 }
@@ -59,9 +126,11 @@ __global__ __launch_bounds__(kSortBlock) void k_route_fwd(const float* __restric
 template <int W>
 __global__ __launch_bounds__(kSortBlock) void k_route_inv(const float* __restrict__ in, float* __restrict__ out,
                                                           const uint16_t* __restrict__ lpos, const uint16_t* __restrict__ dstart,
-                                                          const uint32_t* __restrict__ gbase, uint64_t n) {
+                                                          const uint32_t* __restrict__ gbase, uint64_t n, bool vec) {
   constexpr int TILE = kSortTile;
   constexpr int NW = kSortBlock / kWave;
+  constexpr int STEPS = TILE / kSortBlock;
+  constexpr int GSTEPS = TILE / (kSortBlock * kGroup);
   __shared__ float s_val[TILE * W];
   __shared__ uint8_t s_dig[TILE];
   __shared__ uint16_t s_start[257];
@@ -69,24 +138,44 @@ __global__ __launch_bounds__(kSortBlock) void k_route_inv(const float* __restric
   const int tid = threadIdx.x;
   const uint64_t tile = blockIdx.x, base = tile * TILE;
   const uint32_t count = (uint32_t)std::min<uint64_t>(TILE, n - base);
-  s_start[tid] = std::min<uint16_t>(dstart[tile * 256 + tid], (uint16_t)count);
-  s_gb[tid] = gbase[tile * 256 + tid];
-  if (tid == 0) s_start[256] = (uint16_t)count;
+  load_tables(dstart, gbase, tile, count, s_start, s_gb);
   __syncthreads();
   paint_digits<NW>(s_start, s_dig);
   __syncthreads();
-  for (uint32_t i = tid; i < count; i += kSortBlock) {
-    const uint32_t src = s_gb[s_dig[i]] + i;
-    const bool ok = (uint64_t)src < n;
+  // digit-run side: each run read contiguously
 #pragma unroll
-    for (int c = 0; c < W; ++c) s_val[i * W + c] = ok ? in[(uint64_t)src * W + c] : 0.f;
+  for (int r = 0; r < STEPS; ++r) {
+    const uint32_t i = (uint32_t)(r * kSortBlock + tid);
+    if (i < count) {
+      const uint32_t src = s_gb[s_dig[i]] + i;
+      const bool ok = (uint64_t)src < n;
+#pragma unroll
+      for (int c = 0; c < W; ++c) s_val[i * W + c] = ok ? in[(uint64_t)src * W + c] : 0.f;
+    }
   }
   __syncthreads();
-  for (uint32_t i = tid; i < count; i += kSortBlock) {
-    const uint64_t j = base + i;
-    const uint32_t lp = std::min<uint32_t>(lpos[j], count - 1);
+  // input order side
 #pragma unroll
-    for (int c = 0; c < W; ++c) out[j * W + c] = s_val[lp * W + c];
+  for (int r = 0; r < GSTEPS; ++r) {
+    const uint32_t i0 = (uint32_t)(r * kSortBlock + tid) * kGroup;
+    if (i0 + kGroup <= count) {
+      const uint2 lp2 = *reinterpret_cast<const uint2*>(lpos + base + i0);
+      const uint32_t lp[kGroup] = {lp2.x & 0xFFFFu, lp2.x >> 16, lp2.y & 0xFFFFu, lp2.y >> 16};
+      float v[kGroup * W];
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) {
+        const uint32_t q = std::min<uint32_t>(lp[g], count - 1);
+#pragma unroll
+        for (int c = 0; c < W; ++c) v[g * W + c] = s_val[q * W + c];
+      }
+      st_group<W>(out + (base + i0) * W, v, vec);
+    } else {
+      for (uint32_t i = i0; i < count && i < i0 + kGroup; ++i) {
+        const uint32_t q = std::min<uint32_t>(lpos[base + i], count - 1);
+#pragma unroll
+        for (int c = 0; c < W; ++c) out[(base + i) * W + c] = s_val[q * W + c];
+      }
+    }
   }
 }
 
@@ -115,15 +204,19 @@ SortRoute carve_route(const void* base, uint64_t n) {
 
 template <int W>
 static hipError_t route_pass(bool fwd, const SortRoute& r, int k, uint64_t n, const float* in, float* out, hipStream_t s) {
+  // the input-order side: `in` going forward, `out` going back
+  const bool vec = (reinterpret_cast<uintptr_t>(fwd ? in : out) & 15) == 0;
   static const char* const kFwd[5] = {"", "k_route_fwd_w1", "k_route_fwd_w2", "k_route_fwd_w3", "k_route_fwd_w4"};
   static const char* const kInv[5] = {"", "k_route_inv_w1", "k_route_inv_w2", "k_route_inv_w3", "k_route_inv_w4"};
   const uint64_t tiles = (n + kSortTile - 1) / kSortTile;
   if (fwd)
     LAPLEX_LAUNCH(kFwd[W], n, s,
-                  k_route_fwd<W><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(in, out, r.lpos[k], r.dstart[k], r.gbase[k], n));
+                  k_route_fwd<W><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(in, out, r.lpos[k], r.dstart[k], r.gbase[k], n,
+                                                                                    vec));
   else
     LAPLEX_LAUNCH(kInv[W], n, s,
-                  k_route_inv<W><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(in, out, r.lpos[k], r.dstart[k], r.gbase[k], n));
+                  k_route_inv<W><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(in, out, r.lpos[k], r.dstart[k], r.gbase[k], n,
+                                                                                    vec));
   return hipGetLastError();
 }
 

@@ -106,6 +106,9 @@ __global__ __launch_bounds__(256) void k_sort_offsets(const uint32_t* __restrict
 // MODE 0: input is the anchors' float bits (keys computed here, values are the
 //         input indices); MODE 1: key/value buffers to key/value buffers;
 // MODE 2: writes float bits of the sorted anchors and the permutation.
+// Threads 0..255 also own one digit value each for the per-digit steps.
+constexpr int kLookback = 8;  // predecessor status words read per round trip
+
 template <int MODE, typename ST>
 __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin,
                                                          uint32_t* __restrict__ kout, uint32_t* __restrict__ vout,
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
                                                          const uint32_t* __restrict__ digit_start, uint64_t n,
                                                          uint16_t* __restrict__ r_lpos, uint16_t* __restrict__ r_dstart,
                                                          uint32_t* __restrict__ r_gbase) {
-  static_assert(kSortBlock == 256, "one thread per digit value");
+  static_assert(kSortBlock % 256 == 0, "at least one thread per digit value");
   constexpr int E = kSortItems;
   constexpr int TILE = kSortTile;
   constexpr int NW = kSortBlock / kWave;
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
   __shared__ uint32_t s_whist[NW][256];
   __shared__ uint32_t s_dstart[256];
   __shared__ uint32_t s_gbase[256];
-  __shared__ uint32_t s_wsum[NW];
+  __shared__ uint32_t s_wsum[4];
   __shared__ uint32_t s_tile;
 
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
@@ -164,58 +167,76 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
   }
   __syncthreads();
 
-  // per digit: offsets of each wave inside the tile's digit run, tile count
-  const int d = tid;
-  uint32_t cnt = 0;
-  for (int w = 0; w < NW; ++w) {
-    const uint32_t c = s_whist[w][d];
-    s_whist[w][d] = cnt;
-    cnt += c;
-  }
-  // exclusive scan of the counts over digit values -> local start of each digit
-  uint32_t x = cnt;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint32_t t = __shfl_up(x, off);
-    if (lane >= off) x += t;
-  }
-  if (lane == kWave - 1) s_wsum[wid] = x;
-  // publish this tile's count, then look back for the exclusive prefix
-  ST* my = status + (uint64_t)tile * 256 + d;
-  if (tile == 0)
-    store_agent(my, Status<ST>::pack(kFlagInclusive, cnt));
-  else
-    store_agent(my, Status<ST>::pack(kFlagAggregate, cnt));
-  uint32_t excl = 0;
-  if (tile > 0) {
-    uint64_t t = tile - 1;
-    uint32_t spins = 0;
-    while (true) {
-      const ST w = load_agent(status + t * 256 + d);
-      const uint32_t f = Status<ST>::flag(w);
-      if (f == 0) {
-        if (++spins > kSpinLimit) {
-          atomicOr(&header[kHdrFlags], kFlagWatchdog);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        continue;
-      }
-      excl += Status<ST>::value(w);
-      if (f == kFlagInclusive || t == 0) break;
-      --t;
+  // per digit (threads 0..255): offsets of each wave inside the tile's digit
+  // run, the tile's count, and the inclusive scan of counts over digit values
+  const int d = tid & 255;
+  const bool digit_owner = tid < 256;
+  uint32_t cnt = 0, x = 0;
+  if (digit_owner) {
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t c = s_whist[w][d];
+      s_whist[w][d] = cnt;
+      cnt += c;
     }
-    store_agent(my, Status<ST>::pack(kFlagInclusive, excl + cnt));
+    x = cnt;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t t = __shfl_up(x, off);
+      if (lane >= off) x += t;
+    }
+    if (lane == kWave - 1) s_wsum[wid] = x;
+  }
+  // publish this tile's count, then look back for the exclusive prefix:
+  // each round reads up to kLookback predecessors at once and consumes them
+  // newest first until an inclusive prefix (or a not-yet-published tile)
+  uint32_t excl = 0;
+  if (digit_owner) {
+    ST* my = status + (uint64_t)tile * 256 + d;
+    store_agent(my, Status<ST>::pack(tile == 0 ? kFlagInclusive : kFlagAggregate, cnt));
+    if (tile > 0) {
+      int64_t t = (int64_t)tile - 1;
+      uint32_t spins = 0;
+      bool done = false;
+      while (!done) {
+        ST w[kLookback];
+#pragma unroll
+        for (int i = 0; i < kLookback; ++i)
+          w[i] = (t - i >= 0) ? load_agent(status + (uint64_t)(t - i) * 256 + d) : Status<ST>::pack(kFlagInclusive, 0);
+        int used = 0;
+#pragma unroll
+        for (int i = 0; i < kLookback; ++i) {
+          if (done || used < i) continue;  // stopped earlier in this window
+          const uint32_t f = Status<ST>::flag(w[i]);
+          if (f == 0) continue;            // not published yet: re-read from here
+          excl += Status<ST>::value(w[i]);
+          used = i + 1;
+          if (f == kFlagInclusive) done = true;
+        }
+        if (!done) {
+          t -= used;
+          if (used == 0) {
+            if (++spins > kSpinLimit) {
+              atomicOr(&header[kHdrFlags], kFlagWatchdog);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+      }
+      store_agent(my, Status<ST>::pack(kFlagInclusive, excl + cnt));
+    }
   }
   __syncthreads();
-  uint32_t pre = 0;
-  for (int i = 0; i < wid; ++i) pre += s_wsum[i];
-  const uint32_t dstart = pre + x - cnt;
-  s_dstart[d] = dstart;
-  s_gbase[d] = digit_start[d] + excl - dstart;  // modular: gbase + local index >= 0
-  if (r_dstart != nullptr) {
-    r_dstart[(uint64_t)tile * 256 + d] = (uint16_t)dstart;
-    r_gbase[(uint64_t)tile * 256 + d] = digit_start[d] + excl - dstart;
+  if (digit_owner) {
+    uint32_t pre = 0;
+    for (int i = 0; i < wid; ++i) pre += s_wsum[i];
+    const uint32_t dstart = pre + x - cnt;
+    s_dstart[d] = dstart;
+    s_gbase[d] = digit_start[d] + excl - dstart;  // modular: gbase + local index >= 0
+    if (r_dstart != nullptr) {
+      r_dstart[(uint64_t)tile * 256 + d] = (uint16_t)dstart;
+      r_gbase[(uint64_t)tile * 256 + d] = digit_start[d] + excl - dstart;
+    }
   }
   __syncthreads();
 
@@ -236,7 +257,10 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
   // write out: consecutive threads write consecutive slots of a digit's run
   const uint64_t rem = n - base;
   const uint32_t count = rem < (uint64_t)TILE ? (uint32_t)rem : (uint32_t)TILE;
-  for (uint32_t i = tid; i < count; i += kSortBlock) {
+#pragma unroll
+  for (int r = 0; r < TILE / kSortBlock; ++r) {
+    const uint32_t i = (uint32_t)(r * kSortBlock + tid);
+    if (i >= count) continue;
     const uint32_t key = s_keys[i];
     const uint32_t val = s_vals[i];
     const uint32_t o = s_gbase[(key >> shift) & 255u] + i;
