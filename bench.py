@@ -82,6 +82,40 @@ def kernel_bytes(name: str, units: int, m: int, k: int = 0) -> float:
     return 0.0
 
 
+# rocprofv3 kernel names (template arguments stripped) -> launch labels
+ROCPROF_LABELS = {
+    "k_sort_hist": "k_sort_hist",
+    "k_sort_offsets": "k_sort_offsets",
+    "k_fill_u32": "k_fill_u32",
+    "k_tile_carry": "k_tile_carry",
+    "k_gather_rows": "k_gather_rows",
+}
+
+
+def rocprof_label(name: str, pass_index: int = 0, routed: bool = True) -> str:
+    import re
+    base = re.sub(r"\(.*$", "", name).replace("void ", "").replace("laplex::", "").strip()
+    m = re.match(r"(k_\w+)<(.*)>$", base)
+    kern, targs = (m.group(1), [t.strip() for t in m.group(2).split(",")]) if m else (base, [])
+    if kern == "k_onesweep":
+        label = {"0": "k_onesweep_first", "1": "k_onesweep_mid", "2": "k_onesweep_last"}[targs[0]]
+        return label + ("_routed" if routed else "")
+    if kern in ("k_route_fwd", "k_route_inv"):
+        return "%s_w%s" % (kern, targs[0])
+    if kern == "k_sym_gather_reduce":
+        ph, gather = targs[1] == "true", targs[2] == "true"
+        return ("k_phased" if ph else "k_sym") + ("_gather_reduce" if gather else "_reduce")
+    if kern == "k_sym_apply":
+        ph, scatter = targs[1] == "true", targs[2] == "true"
+        return ("k_phased_apply" if ph else "k_sym_apply") + ("" if scatter else "_sorted")
+    if kern == "k_gen_reduce":
+        return "k_phased_gen_reduce" if targs[1] == "true" else "k_gen_reduce"
+    if kern == "k_gen_apply":
+        ph, scatter = targs[1] == "true", targs[2] == "true"
+        return ("k_phased_gen_apply" if ph else "k_gen_apply") + ("" if scatter else "_sorted")
+    return ROCPROF_LABELS.get(kern, kern)
+
+
 def load_traffic(workload: str, kernel: str, src_hash: str):
     """HBM bytes per launch of ``kernel`` from a committed counter summary, or None."""
     path = os.path.join(ROOT, "profiles", "counters_%s.txt" % workload)
@@ -100,9 +134,72 @@ def load_traffic(workload: str, kernel: str, src_hash: str):
                     rows[parts[0]] = (float(parts[1]), float(parts[2]))
     if meta.get("source_hash") != src_hash or kernel not in rows:
         return None, path
-    factor = float(meta.get("copy_factor", "1.0"))
     fetch_kib, write_kib = rows[kernel]
-    return (fetch_kib + write_kib) * 1024.0 * factor, path
+    fetch_factor = float(meta.get("fetch_factor", "1.0"))
+    write_factor = float(meta.get("write_factor", "1.0"))
+    return (fetch_kib * fetch_factor + write_kib * write_factor) * 1024.0, path
+
+
+def rocprof_summary(stats_csv: str, fetch_csv: str, write_csv: str, workload: str, command: str) -> str:
+    """Text summaries of a rocprofv3 kernel-trace --stats run and of two --pmc runs
+    (FETCH_SIZE, WRITE_SIZE).  The counters are scaled by what they read for the
+    plain 1 GiB device copy the benchmark runs with --calib-copy."""
+    import csv
+    out = []
+    out.append("# rocprofv3 kernel statistics, workload %s" % workload)
+    out.append("# command: rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- %s" % command)
+    out.append("# source_hash = %s" % source_hash())
+    out.append("# %-26s %6s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us"))
+    agg = {}
+    for r in csv.DictReader(open(stats_csv)):
+        lab = rocprof_label(r["Name"])
+        a = agg.setdefault(lab, [0, 0.0, float("inf"), 0.0])
+        calls = int(r["Calls"])
+        a[0] += calls
+        a[1] += float(r["TotalDurationNs"])
+        a[2] = min(a[2], float(r["MinNs"]))
+        a[3] = max(a[3], float(r["MaxNs"]))
+    for lab, (c, tot, mn, mx) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        out.append("%-28s %6d %12.1f %12.1f %12.1f" % (lab, c, tot / c / 1e3, mn / 1e3, mx / 1e3))
+    kernels_txt = "\n".join(out) + "\n"
+
+    def per_dispatch(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = per_dispatch(write_csv, "WRITE_SIZE")
+    gib_kib = float(1 << 20)  # 1 GiB in KiB
+    copy_f = [v for k, vs in fetch.items() if "copyBuffer" in k for v in vs]
+    copy_w = [v for k, vs in write.items() if "copyBuffer" in k for v in vs]
+    fetch_factor = gib_kib / max(copy_f) if copy_f else 1.0
+    write_factor = gib_kib / max(copy_w) if copy_w else 1.0
+    c = []
+    c.append("# rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch, mean over dispatches), workload %s" % workload)
+    c.append("# commands: rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- %s" % command)
+    c.append("#           rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- %s" % command)
+    c.append("# calibration: a plain device copy of 1 GiB (bench.py --calib-copy) reads FETCH_SIZE %.0f KiB and"
+             " WRITE_SIZE %.0f KiB" % (max(copy_f) if copy_f else 0, max(copy_w) if copy_w else 0))
+    c.append("# fetch_factor = %.4f" % fetch_factor)
+    c.append("# write_factor = %.4f" % write_factor)
+    c.append("# source_hash = %s" % source_hash())
+    c.append("# %-26s %14s %14s   (raw counter values; bytes = KiB * 1024 * factor)" % ("kernel", "FETCH_KiB", "WRITE_KiB"))
+    lab_f, lab_w = {}, {}
+    for k, vs in fetch.items():
+        lab_f.setdefault(rocprof_label(k), []).extend(vs)
+    for k, vs in write.items():
+        lab_w.setdefault(rocprof_label(k), []).extend(vs)
+    for lab in sorted(lab_f, key=lambda q: -sum(lab_f[q]) / len(lab_f[q])):
+        if "copyBuffer" in lab:
+            continue
+        fv = sum(lab_f[lab]) / len(lab_f[lab])
+        wv = sum(lab_w.get(lab, [0.0])) / max(1, len(lab_w.get(lab, [0.0])))
+        c.append("%-28s %14.1f %14.1f" % (lab, fv, wv))
+    return kernels_txt, "\n".join(c) + "\n"
 
 
 def cpu_baseline(workload: str, log2_sample: int):
@@ -153,7 +250,19 @@ def main():
     ap.add_argument("--cpu-sample-log2", type=int, default=25)
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--rocprof-summary", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/kernels_<workload>.txt and profiles/counters_<workload>.txt from rocprofv3 output")
+    ap.add_argument("--rocprof-command", default="", help="the program command line the rocprofv3 runs profiled")
     args = ap.parse_args()
+    if args.rocprof_summary:
+        ktxt, ctxt = rocprof_summary(*args.rocprof_summary, workload=args.workload, command=args.rocprof_command)
+        os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+        with open(os.path.join(ROOT, "profiles", "kernels_%s.txt" % args.workload), "w") as f:
+            f.write(ktxt)
+        with open(os.path.join(ROOT, "profiles", "counters_%s.txt" % args.workload), "w") as f:
+            f.write(ctxt)
+        print(ktxt + ctxt)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
               file=sys.stderr)
