@@ -66,6 +66,12 @@ ApplyWorkspace carve_apply(void* ws, uint64_t rows_in, uint64_t rows_out, uint64
   w.cf = c.take<float>(T * M * 4);
   w.cb = c.take<float>(T * M * 4);
   w.tanch = c.take<float2>(T * 8);
+  const uint64_t G = (T + 1023) / 1024;
+  w.gbf = c.take<float>(G * M * 4);
+  w.gbb = c.take<float>(G * M * 4);
+  w.gcf = c.take<float>(G * M * 4);
+  w.gcb = c.take<float>(G * M * 4);
+  w.ganch = c.take<float2>(G * 8);
   w.tsplit = general ? c.take<uint2>((T + 1) * 8) : nullptr;
   if (m <= kRouteMaxCols) {
     const uint64_t rmax = std::max(rows_in, rows_out);

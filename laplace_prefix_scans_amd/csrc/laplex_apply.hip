@@ -294,6 +294,129 @@ __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restr
   }
 }
 
+// Large tile counts: the tiles are grouped by 1024.  k_carry_up folds each
+// group into one aggregate per direction (direct weighted sums), k_tile_carry
+// scans the group aggregates, and k_carry_down turns each group's carry into
+// the carries of its tiles with a block-wide scan (wave shuffles, then the
+// waves' totals in order).  All three run one block per (group, column).
+constexpr int kCarryGroup = 1024;
+
+__global__ __launch_bounds__(kCarryGroup) void k_carry_up(const float* __restrict__ bf, const float* __restrict__ bb,
+                                                          const float2* __restrict__ tanch, uint64_t T, uint32_t M,
+                                                          float* __restrict__ gbf, float* __restrict__ gbb,
+                                                          float2* __restrict__ ganch) {
+  constexpr int NW = kCarryGroup / kWave;
+  __shared__ float s_red[2 * NW];
+  const uint64_t g = blockIdx.x;
+  const uint32_t c = blockIdx.y;
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  const uint64_t t0 = g * kCarryGroup, t1 = std::min<uint64_t>(T, t0 + kCarryGroup);
+  const uint64_t t = t0 + tid;
+  const float s_first = tanch[t0].x, s_last = tanch[t1 - 1].y;
+  float vf[1] = {0.f}, vb[1] = {0.f};
+  if (t < t1) {
+    const float2 ta = tanch[t];
+    vf[0] = decay(ta.y - s_last) * bf[t * M + c];
+    vb[0] = decay(s_first - ta.x) * bb[t * M + c];
+  }
+  wave_sum<1>(vf);
+  wave_sum<1>(vb);
+  if (lane == 0) {
+    s_red[wid] = vf[0];
+    s_red[NW + wid] = vb[0];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float f = 0.f, b = 0.f;
+    for (int w = 0; w < NW; ++w) {
+      f += s_red[w];
+      b += s_red[NW + w];
+    }
+    gbf[g * M + c] = f;
+    gbb[g * M + c] = b;
+    if (c == 0) ganch[g] = make_float2(s_first, s_last);
+  }
+}
+
+__global__ __launch_bounds__(kCarryGroup) void k_carry_down(const float* __restrict__ bf, const float* __restrict__ bb,
+                                                            const float2* __restrict__ tanch, uint64_t T, uint32_t M,
+                                                            const float* __restrict__ gcf, const float* __restrict__ gcb,
+                                                            const float2* __restrict__ ganch, uint64_t G,
+                                                            float* __restrict__ cf, float* __restrict__ cb) {
+  constexpr int NW = kCarryGroup / kWave;
+  __shared__ float s_f[NW], s_fs[NW], s_b[NW], s_bs[NW];
+  const uint64_t g = blockIdx.x;
+  const uint32_t c = blockIdx.y;
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  const uint64_t t0 = g * kCarryGroup, t1 = std::min<uint64_t>(T, t0 + kCarryGroup);
+  const uint64_t t = t0 + tid;
+  const bool valid = t < t1;
+  const float2 last_tile = tanch[t1 - 1];
+  const float2 ta = valid ? tanch[t] : last_tile;
+  float B[1] = {valid ? bf[t * M + c] : 0.f};
+  float D[1] = {valid ? bb[t * M + c] : 0.f};
+  // inclusive scans within the wave (forward by last anchors, backward by first)
+  wave_scan_fwd<1>(B, ta.y);
+  wave_scan_bwd<1>(D, ta.x);
+  if (lane == kWave - 1) {
+    s_f[wid] = B[0];
+    s_fs[wid] = ta.y;
+  }
+  if (lane == 0) {
+    s_b[wid] = D[0];
+    s_bs[wid] = ta.x;
+  }
+  const float X = __shfl_up(B[0], 1), sx = __shfl_up(ta.y, 1);
+  const float Z = __shfl_down(D[0], 1), sz = __shfl_down(ta.x, 1);
+  __syncthreads();
+  // forward: group carry, earlier waves, then earlier lanes of this wave
+  float C = gcf[g * M + c];
+  float sc = g > 0 ? ganch[g - 1].y : ganch[0].x;
+  for (int w = 0; w < wid; ++w) {
+    C = fmaf(decay(sc - s_fs[w]), C, s_f[w]);
+    sc = s_fs[w];
+  }
+  if (lane > 0) {
+    C = fmaf(decay(sc - sx), C, X);
+    sc = sx;
+  }
+  // backward: group carry, later waves, then later lanes of this wave
+  float Cb = gcb[g * M + c];
+  float sb = g + 1 < G ? ganch[g + 1].x : ganch[G - 1].y;
+  for (int w = NW - 1; w > wid; --w) {
+    Cb = fmaf(decay(s_bs[w] - sb), Cb, s_b[w]);
+    sb = s_bs[w];
+  }
+  if (lane < kWave - 1) {
+    Cb = fmaf(decay(sz - sb), Cb, Z);
+    sb = sz;
+  }
+  if (valid) {
+    cf[t * M + c] = C;
+    cb[t * M + c] = Cb;
+  }
+}
+
+// Carries for T tiles: one level when T is small, three levels otherwise.
+// g_* hold the group aggregates and carries (ceil(T / 1024) x M each).
+static hipError_t tile_carries(const float* bf, const float* bb, const float2* tanch, uint64_t T, uint32_t M, float* cf,
+                               float* cb, float* gbf, float* gbb, float* gcf, float* gcb, float2* ganch, hipStream_t s) {
+  if (T <= (uint64_t)kCarryGroup * 4) {
+    LAPLEX_LAUNCH("k_tile_carry", T, s, k_tile_carry<<<M, kCarryBlock, 0, s>>>(bf, bb, tanch, T, M, cf, cb));
+    return hipGetLastError();
+  }
+  const uint64_t G = (T + kCarryGroup - 1) / kCarryGroup;
+  const dim3 grid((unsigned)G, M);
+  LAPLEX_LAUNCH("k_carry_up", T, s, k_carry_up<<<grid, kCarryGroup, 0, s>>>(bf, bb, tanch, T, M, gbf, gbb, ganch));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  LAPLEX_LAUNCH("k_tile_carry", G, s, k_tile_carry<<<M, kCarryBlock, 0, s>>>(gbf, gbb, ganch, G, M, gcf, gcb));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  LAPLEX_LAUNCH("k_carry_down", T, s,
+                k_carry_down<<<grid, kCarryGroup, 0, s>>>(bf, bb, tanch, T, M, gcf, gcb, ganch, G, cf, cb));
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- symmetric
 // Contiguous loads and stores of N floats; vector instructions when the
 // caller knows the address is 16-byte (N % 4 == 0) or 8-byte (N % 2 == 0)
@@ -603,8 +726,7 @@ static hipError_t run_sym(const ApplyWorkspace& w, const float* a_s, const uint3
                                                                           w.tanch, vec));
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  LAPLEX_LAUNCH("k_tile_carry", T, s, k_tile_carry<<<M, kCarryBlock, 0, s>>>(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb));
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = tile_carries(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb, w.gbf, w.gbb, w.gcf, w.gcb, w.ganch, s)) != hipSuccess) return e;
   if (routed) {
     LAPLEX_LAUNCH(PH ? "k_phased_apply_sorted" : "k_sym_apply_sorted", n, s,
                   k_sym_apply<C, PH, false><<<grid, block, 0, s>>>(a_s, perm, w.xs, w.phs, w.cf, w.cb, w.tanch, n, m, T, w.zs, vec));
@@ -871,8 +993,7 @@ static hipError_t run_general(const ApplyWorkspace& w, const float* a_s, const u
   LAPLEX_LAUNCH(PH ? "k_phased_gen_reduce" : "k_gen_reduce", k, s,
                 k_gen_reduce<C, PH><<<grid, block, 0, s>>>(a_s, n, b_s, k, w.xs, w.phs, m, T, w.bf, w.bb, w.tanch, w.tsplit));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  LAPLEX_LAUNCH("k_tile_carry", T, s, k_tile_carry<<<M, kCarryBlock, 0, s>>>(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb));
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = tile_carries(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb, w.gbf, w.gbb, w.gcf, w.gcb, w.ganch, s)) != hipSuccess) return e;
   if (route_a != nullptr && m <= kRouteMaxCols) {
     const float* phas = nullptr;
     if (PH) {

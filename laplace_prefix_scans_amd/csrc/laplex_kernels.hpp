@@ -91,6 +91,11 @@ struct ApplyWorkspace {
   float* cf;       // [tiles][M] forward carry into each tile
   float* cb;       // [tiles][M] backward carry into each tile
   float2* tanch;   // [tiles] (first, last) anchor of each tile
+  float* gbf;      // [groups][M] group aggregates and carries (groups = tiles / 1024, rounded up)
+  float* gbb;
+  float* gcf;
+  float* gcb;
+  float2* ganch;   // [groups]
   uint2* tsplit;   // [tiles+1] merge-path split (a index, b index) at each tile start (general)
 };
 

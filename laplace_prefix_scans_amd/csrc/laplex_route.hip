@@ -64,6 +64,17 @@ __device__ __forceinline__ void load_tables(const uint16_t* __restrict__ dstart,
   if (tid == 0) s_start[256] = (uint16_t)count;
 }
 
+// Tile of this block.  Workgroups are dispatched to the 8 XCDs round-robin, so
+// block b runs on XCD b % 8; giving each XCD a contiguous range of tiles puts
+// neighbouring tiles -- whose digit runs share cache lines at their ends --
+// behind the same L2.  Returns false for the few padding blocks.
+constexpr unsigned kXcds = 8;
+__device__ __forceinline__ bool xcd_tile(uint64_t tiles, uint64_t& tile) {
+  const uint64_t per = (tiles + kXcds - 1) / kXcds;
+  tile = (uint64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  return tile < tiles;
+}
+
 // vec: `in` (fwd) or `out` (inv), the input-order side, is 16-byte aligned.
 template <int W>
 __global__ __launch_bounds__(kSortBlock) void k_route_fwd(const float* __restrict__ in, float* __restrict__ out,
@@ -78,7 +89,9 @@ __global__ __launch_bounds__(kSortBlock) void k_route_fwd(const float* __restric
   __shared__ uint16_t s_start[257];
   __shared__ uint32_t s_gb[256];
   const int tid = threadIdx.x;
-  const uint64_t tile = blockIdx.x, base = tile * TILE;
+  uint64_t tile;
+  if (!xcd_tile((n + TILE - 1) / TILE, tile)) return;
+  const uint64_t base = tile * TILE;
   const uint32_t count = (uint32_t)std::min<uint64_t>(TILE, n - base);
   load_tables(dstart, gbase, tile, count, s_start, s_gb);
   // input order side: rows to their tile-local sorted position
@@ -136,7 +149,9 @@ __global__ __launch_bounds__(kSortBlock) void k_route_inv(const float* __restric
   __shared__ uint16_t s_start[257];
   __shared__ uint32_t s_gb[256];
   const int tid = threadIdx.x;
-  const uint64_t tile = blockIdx.x, base = tile * TILE;
+  uint64_t tile;
+  if (!xcd_tile((n + TILE - 1) / TILE, tile)) return;
+  const uint64_t base = tile * TILE;
   const uint32_t count = (uint32_t)std::min<uint64_t>(TILE, n - base);
   load_tables(dstart, gbase, tile, count, s_start, s_gb);
   __syncthreads();
@@ -209,13 +224,14 @@ static hipError_t route_pass(bool fwd, const SortRoute& r, int k, uint64_t n, co
   static const char* const kFwd[5] = {"", "k_route_fwd_w1", "k_route_fwd_w2", "k_route_fwd_w3", "k_route_fwd_w4"};
   static const char* const kInv[5] = {"", "k_route_inv_w1", "k_route_inv_w2", "k_route_inv_w3", "k_route_inv_w4"};
   const uint64_t tiles = (n + kSortTile - 1) / kSortTile;
+  const uint64_t blocks = ((tiles + kXcds - 1) / kXcds) * kXcds;
   if (fwd)
     LAPLEX_LAUNCH(kFwd[W], n, s,
-                  k_route_fwd<W><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(in, out, r.lpos[k], r.dstart[k], r.gbase[k], n,
+                  k_route_fwd<W><<<dim3((unsigned)blocks), dim3(kSortBlock), 0, s>>>(in, out, r.lpos[k], r.dstart[k], r.gbase[k], n,
                                                                                     vec));
   else
     LAPLEX_LAUNCH(kInv[W], n, s,
-                  k_route_inv<W><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(in, out, r.lpos[k], r.dstart[k], r.gbase[k], n,
+                  k_route_inv<W><<<dim3((unsigned)blocks), dim3(kSortBlock), 0, s>>>(in, out, r.lpos[k], r.dstart[k], r.gbase[k], n,
                                                                                     vec));
   return hipGetLastError();
 }
