@@ -93,16 +93,25 @@ __global__ __launch_bounds__(kSortBlock) void k_route_fwd(const float* __restric
   if (!xcd_tile((n + TILE - 1) / TILE, tile)) return;
   const uint64_t base = tile * TILE;
   const uint32_t count = (uint32_t)std::min<uint64_t>(TILE, n - base);
-  load_tables(dstart, gbase, tile, count, s_start, s_gb);
-  // input order side: rows to their tile-local sorted position
+  // input order side: rows to their tile-local sorted position; every load
+  // of the thread is issued before the first LDS write
+  uint2 lp2[GSTEPS];
+  float vv[GSTEPS][kGroup * W];
 #pragma unroll
   for (int r = 0; r < GSTEPS; ++r) {
     const uint32_t i0 = (uint32_t)(r * kSortBlock + tid) * kGroup;
     if (i0 + kGroup <= count) {
-      const uint2 lp2 = *reinterpret_cast<const uint2*>(lpos + base + i0);
-      const uint32_t lp[kGroup] = {lp2.x & 0xFFFFu, lp2.x >> 16, lp2.y & 0xFFFFu, lp2.y >> 16};
-      float v[kGroup * W];
-      ld_group<W>(in + (base + i0) * W, v, vec);
+      lp2[r] = *reinterpret_cast<const uint2*>(lpos + base + i0);
+      ld_group<W>(in + (base + i0) * W, vv[r], vec);
+    }
+  }
+  load_tables(dstart, gbase, tile, count, s_start, s_gb);
+#pragma unroll
+  for (int r = 0; r < GSTEPS; ++r) {
+    const uint32_t i0 = (uint32_t)(r * kSortBlock + tid) * kGroup;
+    if (i0 + kGroup <= count) {
+      const uint32_t lp[kGroup] = {lp2[r].x & 0xFFFFu, lp2[r].x >> 16, lp2[r].y & 0xFFFFu, lp2[r].y >> 16};
+      const float(&v)[kGroup * W] = vv[r];
 #pragma unroll
       for (int g = 0; g < kGroup; ++g)
         if (lp[g] < count) {
@@ -153,6 +162,14 @@ __global__ __launch_bounds__(kSortBlock) void k_route_inv(const float* __restric
   if (!xcd_tile((n + TILE - 1) / TILE, tile)) return;
   const uint64_t base = tile * TILE;
   const uint32_t count = (uint32_t)std::min<uint64_t>(TILE, n - base);
+  // the input-order side's positions are loaded first, so that their latency
+  // overlaps the tables and the run-side reads
+  uint2 lp2[GSTEPS];
+#pragma unroll
+  for (int r = 0; r < GSTEPS; ++r) {
+    const uint32_t i0 = (uint32_t)(r * kSortBlock + tid) * kGroup;
+    lp2[r] = i0 + kGroup <= count ? *reinterpret_cast<const uint2*>(lpos + base + i0) : make_uint2(0u, 0u);
+  }
   load_tables(dstart, gbase, tile, count, s_start, s_gb);
   __syncthreads();
   paint_digits<NW>(s_start, s_dig);
@@ -174,8 +191,149 @@ __global__ __launch_bounds__(kSortBlock) void k_route_inv(const float* __restric
   for (int r = 0; r < GSTEPS; ++r) {
     const uint32_t i0 = (uint32_t)(r * kSortBlock + tid) * kGroup;
     if (i0 + kGroup <= count) {
-      const uint2 lp2 = *reinterpret_cast<const uint2*>(lpos + base + i0);
-      const uint32_t lp[kGroup] = {lp2.x & 0xFFFFu, lp2.x >> 16, lp2.y & 0xFFFFu, lp2.y >> 16};
+      const uint32_t lp[kGroup] = {lp2[r].x & 0xFFFFu, lp2[r].x >> 16, lp2[r].y & 0xFFFFu, lp2[r].y >> 16};
+      float v[kGroup * W];
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) {
+        const uint32_t q = std::min<uint32_t>(lp[g], count - 1);
+#pragma unroll
+        for (int c = 0; c < W; ++c) v[g * W + c] = s_val[q * W + c];
+      }
+      st_group<W>(out + (base + i0) * W, v, vec);
+    } else {
+      for (uint32_t i = i0; i < count && i < i0 + kGroup; ++i) {
+        const uint32_t q = std::min<uint32_t>(lpos[base + i], count - 1);
+#pragma unroll
+        for (int c = 0; c < W; ++c) out[(base + i) * W + c] = s_val[q * W + c];
+      }
+    }
+  }
+}
+
+// Inverse pass whose digit-run side reads 16-byte aligned chunks (W = 1, 2,
+// 4 floats per row; `in` 16-byte aligned).  Each run [G, G + L) of global rows
+// is covered by the aligned 4-float chunks that overlap it; a thread loads one
+// chunk and keeps the floats of the run, so a wave's loads touch whole cache
+// lines instead of one dword per lane.  The floats of a boundary chunk that
+// lie outside the run belong to neighbouring runs and are discarded; a chunk
+// reaching past the end of the array is read float by float.  vec: `out` is
+// 16-byte aligned.
+template <int W>
+__global__ __launch_bounds__(kSortBlock) void k_route_inv_chunked(const float* __restrict__ in, float* __restrict__ out,
+                                                                  const uint16_t* __restrict__ lpos,
+                                                                  const uint16_t* __restrict__ dstart,
+                                                                  const uint32_t* __restrict__ gbase, uint64_t n, bool vec) {
+  static_assert(W == 1 || W == 2 || W == 4, "rows must tile a 16-byte chunk");
+  constexpr int TILE = kSortTile;
+  constexpr int NW = kSortBlock / kWave;
+  constexpr int GSTEPS = TILE / (kSortBlock * kGroup);
+  constexpr int MAXCH = TILE * W / 4 + 512;  // sum over runs of (L W + 6) / 4
+  constexpr int CSTEPS = (MAXCH + kSortBlock - 1) / kSortBlock;
+  constexpr int RPC = 4 / W;  // rows per chunk
+  __shared__ float s_val[TILE * W];
+  __shared__ uint8_t s_cdig[MAXCH];
+  __shared__ uint16_t s_start[257];
+  __shared__ uint32_t s_gb[256];
+  __shared__ uint32_t s_cs[257];  // first block-local chunk of each run
+  __shared__ uint32_t s_c0[256];  // global chunk index of each run's first chunk
+  __shared__ uint32_t s_len[256];
+  __shared__ uint32_t s_wsum[4];
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  uint64_t tile;
+  if (!xcd_tile((n + TILE - 1) / TILE, tile)) return;
+  const uint64_t base = tile * TILE;
+  const uint32_t count = (uint32_t)std::min<uint64_t>(TILE, n - base);
+  uint2 lp2[GSTEPS];
+#pragma unroll
+  for (int r = 0; r < GSTEPS; ++r) {
+    const uint32_t i0 = (uint32_t)(r * kSortBlock + tid) * kGroup;
+    lp2[r] = i0 + kGroup <= count ? *reinterpret_cast<const uint2*>(lpos + base + i0) : make_uint2(0u, 0u);
+  }
+  load_tables(dstart, gbase, tile, count, s_start, s_gb);
+  __syncthreads();
+  // per run: global first row G, length L (clipped to the array), chunk range
+  uint32_t nch = 0, x = 0;
+  if (tid < 256) {
+    const uint32_t lo = s_start[tid], hi = s_start[tid + 1];
+    const uint64_t G = (uint64_t)(uint32_t)(s_gb[tid] + lo);
+    uint64_t L = hi > lo ? hi - lo : 0;
+    if (G >= n) L = 0;
+    else if (G + L > n) L = n - G;
+    const uint64_t c0 = G * W / 4, c1 = ((G + L) * W + 3) / 4;
+    nch = L ? (uint32_t)(c1 - c0) : 0u;
+    s_c0[tid] = (uint32_t)c0;
+    s_len[tid] = (uint32_t)L;
+    x = nch;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t t = __shfl_up(x, off);
+      if (lane >= off) x += t;
+    }
+    if (lane == kWave - 1) s_wsum[wid] = x;
+  }
+  __syncthreads();
+  if (tid < 256) {
+    uint32_t pre = 0;
+    for (int i = 0; i < wid; ++i) pre += s_wsum[i];
+    s_cs[tid] = pre + x - nch;
+    if (tid == 255) s_cs[256] = pre + x;
+  }
+  __syncthreads();
+  for (int d = wid; d < 256; d += NW) {
+    const uint32_t lo = s_cs[d], hi = s_cs[d + 1];
+    for (uint32_t c = lo + lane; c < hi; c += kWave) s_cdig[c] = (uint8_t)d;
+  }
+  __syncthreads();
+  const uint32_t total = s_cs[256];
+  const uint64_t nfl = n * W;  // >= 4 (the host launches this kernel only then)
+  // all chunk loads are issued before any is consumed; a chunk that is not
+  // loaded whole (past `total`, or reaching past the array) loads chunk 0
+  uint32_t dg[CSTEPS];
+  uint64_t gg[CSTEPS];
+  float4 q[CSTEPS];
+#pragma unroll
+  for (int r = 0; r < CSTEPS; ++r) {
+    const uint32_t c = std::min<uint32_t>((uint32_t)(r * kSortBlock + tid), MAXCH - 1);
+    dg[r] = s_cdig[c];
+  }
+#pragma unroll
+  for (int r = 0; r < CSTEPS; ++r) {
+    const uint32_t c = (uint32_t)(r * kSortBlock + tid);
+    gg[r] = (uint64_t)s_c0[dg[r]] + (c - s_cs[dg[r]]);
+    const bool whole = c < total && 4 * gg[r] + 4 <= nfl;
+    q[r] = reinterpret_cast<const float4*>(in)[whole ? gg[r] : 0];
+  }
+#pragma unroll
+  for (int r = 0; r < CSTEPS; ++r) {
+    const uint32_t c = (uint32_t)(r * kSortBlock + tid);
+    if (c < total) {
+      const uint32_t d = dg[r];
+      const uint64_t g = gg[r];
+      const uint32_t gb = s_gb[d];
+      const uint64_t G = (uint64_t)(uint32_t)(gb + s_start[d]);
+      const uint64_t Gend = G + s_len[d];
+      float v[4] = {q[r].x, q[r].y, q[r].z, q[r].w};
+      if (4 * g + 4 > nfl) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = (4 * g + k < nfl) ? in[4 * g + k] : 0.f;
+      }
+#pragma unroll
+      for (int rr = 0; rr < RPC; ++rr) {
+        const uint64_t row = g * RPC + rr;
+        if (row >= G && row < Gend) {
+          const uint32_t i = (uint32_t)row - gb;  // tile-local sorted position
+#pragma unroll
+          for (int cc = 0; cc < W; ++cc) s_val[i * W + cc] = v[rr * W + cc];
+        }
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < GSTEPS; ++r) {
+    const uint32_t i0 = (uint32_t)(r * kSortBlock + tid) * kGroup;
+    if (i0 + kGroup <= count) {
+      const uint32_t lp[kGroup] = {lp2[r].x & 0xFFFFu, lp2[r].x >> 16, lp2[r].y & 0xFFFFu, lp2[r].y >> 16};
       float v[kGroup * W];
 #pragma unroll
       for (int g = 0; g < kGroup; ++g) {
@@ -229,6 +387,10 @@ static hipError_t route_pass(bool fwd, const SortRoute& r, int k, uint64_t n, co
     LAPLEX_LAUNCH(kFwd[W], n, s,
                   k_route_fwd<W><<<dim3((unsigned)blocks), dim3(kSortBlock), 0, s>>>(in, out, r.lpos[k], r.dstart[k], r.gbase[k], n,
                                                                                     vec));
+  else if (W != 3 && (reinterpret_cast<uintptr_t>(in) & 15) == 0 && n * W >= 4)
+    LAPLEX_LAUNCH(kInv[W], n, s,
+                  k_route_inv_chunked<W == 3 ? 1 : W><<<dim3((unsigned)blocks), dim3(kSortBlock), 0, s>>>(
+                      in, out, r.lpos[k], r.dstart[k], r.gbase[k], n, vec));
   else
     LAPLEX_LAUNCH(kInv[W], n, s,
                   k_route_inv<W><<<dim3((unsigned)blocks), dim3(kSortBlock), 0, s>>>(in, out, r.lpos[k], r.dstart[k], r.gbase[k], n,

@@ -121,18 +121,22 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
   constexpr int E = kSortItems;
   constexpr int TILE = kSortTile;
   constexpr int NW = kSortBlock / kWave;
-  __shared__ uint32_t s_keys[TILE];
+  __shared__ __align__(16) uint32_t s_keys[TILE];
   __shared__ uint32_t s_vals[TILE];
   __shared__ uint32_t s_whist[NW][256];
-  __shared__ uint32_t s_dstart[256];
   __shared__ uint32_t s_gbase[256];
   __shared__ uint32_t s_wsum[4];
   __shared__ uint32_t s_tile;
 
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
   const uint32_t shift = 8u * (uint32_t)pass;
+  // Ranking scratch, on top of s_keys (unused until the scatter): per wave and
+  // digit value, {mask of the lanes holding that digit in the current
+  // iteration (64 bits), the wave's running count of that digit, unused}.
+  static_assert(NW * 256 * sizeof(uint4) <= sizeof(s_keys), "ranking scratch fits in the key buffer");
+  uint4* s_match = reinterpret_cast<uint4*>(s_keys);
   if (tid == 0) s_tile = atomicAdd(&header[kHdrTicket0 + pass], 1u);
-  for (int i = tid; i < NW * 256; i += kSortBlock) (&s_whist[0][0])[i] = 0;
+  for (int i = tid; i < NW * 256; i += kSortBlock) s_match[i] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
   const uint32_t tile = s_tile;
   const uint64_t base = (uint64_t)tile * TILE;
@@ -152,18 +156,28 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
       v[e] = valid ? vin[idx] : 0u;
     }
   }
-  // stable rank within the wave's run: earlier iterations first, then lower lanes
+  // stable rank within the wave's run: earlier iterations first, then lower
+  // lanes.  The lanes sharing a digit are found by each lane OR-ing its bit
+  // into the digit's mask and reading the mask back (LDS instructions of one
+  // wave complete in order, so the read sees every lane's OR of this
+  // iteration); the lowest such lane then clears the mask and advances the
+  // count.
+  uint4* my = s_match + wid * 256;
+  const unsigned long long lanebit = 1ull << lane;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint64_t idx = base + (uint64_t)wid * (kWave * E) + (uint64_t)e * kWave + lane;
     const bool valid = idx < n;
-    const uint64_t vmask = __ballot(valid);
     const uint32_t d = (k[e] >> shift) & 255u;
-    const uint64_t peers = match_digit8(d, vmask);
-    const uint32_t before = s_whist[wid][d];
+    if (valid)
+      __hip_atomic_fetch_or(reinterpret_cast<unsigned long long*>(&my[d]), lanebit, __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint4 ent = my[d];
+    const uint64_t peers = ((uint64_t)ent.y << 32) | ent.x;
     const uint32_t r = lanes_below(peers);
-    rk[e] = before + r;
-    if (valid && r == 0) s_whist[wid][d] = before + (uint32_t)__popcll(peers);
+    const uint32_t next = ent.z + (uint32_t)__popcll(peers);
+    rk[e] = ent.z + r;
+    if (valid && r == 0) my[d] = make_uint4(0u, 0u, next, 0u);
   }
   __syncthreads();
 
@@ -174,7 +188,7 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
   uint32_t cnt = 0, x = 0;
   if (digit_owner) {
     for (int w = 0; w < NW; ++w) {
-      const uint32_t c = s_whist[w][d];
+      const uint32_t c = s_match[w * 256 + d].z;
       s_whist[w][d] = cnt;
       cnt += c;
     }
@@ -231,7 +245,8 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
     uint32_t pre = 0;
     for (int i = 0; i < wid; ++i) pre += s_wsum[i];
     const uint32_t dstart = pre + x - cnt;
-    s_dstart[d] = dstart;
+    // s_whist[w][d] becomes the tile-local start of wave w's keys of digit d
+    for (int w = 0; w < NW; ++w) s_whist[w][d] += dstart;
     s_gbase[d] = digit_start[d] + excl - dstart;  // modular: gbase + local index >= 0
     if (r_dstart != nullptr) {
       r_dstart[(uint64_t)tile * 256 + d] = (uint16_t)dstart;
@@ -240,37 +255,57 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
   }
   __syncthreads();
 
-  // place the keys in LDS in digit order (stable)
+  // place the keys in LDS in digit order (stable).  All table reads are
+  // issued before the LDS writes, and the route's global stores come last so
+  // that no LDS write waits on them.
+  const uint64_t rem = n - base;
+  const uint32_t count = rem < (uint64_t)TILE ? (uint32_t)rem : (uint32_t)TILE;
+  const uint32_t first = (uint32_t)(wid * (kWave * E) + lane);  // tile-local index at e = 0
+  uint32_t pos[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) pos[e] = s_whist[wid][(k[e] >> shift) & 255u] + rk[e];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const uint64_t idx = base + (uint64_t)wid * (kWave * E) + (uint64_t)e * kWave + lane;
-    if (idx < n) {
-      const uint32_t dd = (k[e] >> shift) & 255u;
-      const uint32_t pos = s_dstart[dd] + s_whist[wid][dd] + rk[e];
-      s_keys[pos] = k[e];
-      s_vals[pos] = v[e];
-      if (r_lpos != nullptr) r_lpos[idx] = (uint16_t)pos;
+    if (first + (uint32_t)(e * kWave) < count) {
+      s_keys[pos[e]] = k[e];
+      s_vals[pos[e]] = v[e];
     }
+  }
+  if (r_lpos != nullptr) {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (first + (uint32_t)(e * kWave) < count) r_lpos[base + first + (uint32_t)(e * kWave)] = (uint16_t)pos[e];
   }
   __syncthreads();
 
-  // write out: consecutive threads write consecutive slots of a digit's run
-  const uint64_t rem = n - base;
-  const uint32_t count = rem < (uint64_t)TILE ? (uint32_t)rem : (uint32_t)TILE;
+  // write out: consecutive threads write consecutive slots of a digit's run;
+  // in batches whose LDS reads are all issued before the stores
+  constexpr int kOutBatch = 8;
+  static_assert((TILE / kSortBlock) % kOutBatch == 0, "write-out batches");
 #pragma unroll
-  for (int r = 0; r < TILE / kSortBlock; ++r) {
-    const uint32_t i = (uint32_t)(r * kSortBlock + tid);
-    if (i >= count) continue;
-    const uint32_t key = s_keys[i];
-    const uint32_t val = s_vals[i];
-    const uint32_t o = s_gbase[(key >> shift) & 255u] + i;
-    if ((uint64_t)o >= n) continue;  // cannot happen for consistent counts; never write out of range
-    if (MODE == 2) {
-      kout[o] = (key == kKeyPlusZero && (uint64_t)val < n) ? a_bits[val] : key_to_float_bits(key);
-      vout[o] = val;
-    } else {
-      kout[o] = key;
-      vout[o] = val;
+  for (int r0 = 0; r0 < TILE / kSortBlock; r0 += kOutBatch) {
+    uint32_t key[kOutBatch], val[kOutBatch], o[kOutBatch];
+#pragma unroll
+    for (int j = 0; j < kOutBatch; ++j) {
+      const uint32_t i = (uint32_t)((r0 + j) * kSortBlock + tid);  // < TILE: slots past count hold stale words
+      key[j] = s_keys[i];
+      val[j] = s_vals[i];
+    }
+#pragma unroll
+    for (int j = 0; j < kOutBatch; ++j) o[j] = s_gbase[(key[j] >> shift) & 255u] + (uint32_t)((r0 + j) * kSortBlock + tid);
+#pragma unroll
+    for (int j = 0; j < kOutBatch; ++j) {
+      const uint32_t i = (uint32_t)((r0 + j) * kSortBlock + tid);
+      // o < n holds for consistent counts; it is checked so nothing is ever written out of range
+      if (i < count && (uint64_t)o[j] < n) {
+        if (MODE == 2) {
+          kout[o[j]] = (key[j] == kKeyPlusZero && (uint64_t)val[j] < n) ? a_bits[val[j]] : key_to_float_bits(key[j]);
+          vout[o[j]] = val[j];
+        } else {
+          kout[o[j]] = key[j];
+          vout[o[j]] = val[j];
+        }
+      }
     }
   }
 }
