@@ -36,8 +36,7 @@ SortWorkspace carve_sort(void* ws, uint64_t n) {
   w.hist = w.header + kSortHistOffset / 4;
   w.offsets = w.header + kSortOffsOffset / 4;
   w.status = c.take<void>(sort_status_bytes(n));  // directly after the header
-  for (int i = 0; i < 2; ++i) w.keys[i] = c.take<uint32_t>(n * 4);
-  for (int i = 0; i < 2; ++i) w.vals[i] = c.take<uint32_t>(n * 4);
+  for (int i = 0; i < 2; ++i) w.kv[i] = c.take<uint2>(n * 8);
   (void)c.take<char>(0);
   return w;
 }
@@ -45,7 +44,7 @@ size_t sort_bytes(uint64_t n) {
   Carver c(nullptr);
   c.take<uint32_t>(kSortHeaderBytes);
   c.take<void>(sort_status_bytes(n));
-  for (int i = 0; i < 4; ++i) c.take<uint32_t>(n * 4);
+  for (int i = 0; i < 2; ++i) c.take<uint2>(n * 8);
   return (c.off + 255) & ~size_t(255);
 }
 

@@ -40,8 +40,7 @@ struct SortWorkspace {
   uint32_t* hist;     // [4][256]
   uint32_t* offsets;  // [4][256]
   void* status;       // [4][tiles][256] u32 (n <= 2^30) or u64
-  uint32_t* keys[2];  // ping-pong key buffers, n each
-  uint32_t* vals[2];  // ping-pong value buffers, n each
+  uint2* kv[2];       // ping-pong buffers of (key, value) pairs, n each
 };
 
 // Route of a sort: for every radix pass, the tile-local sorted position of

@@ -104,13 +104,15 @@ __global__ __launch_bounds__(256) void k_sort_offsets(const uint32_t* __restrict
 
 // ------------------------------------------------------------------ onesweep pass
 // MODE 0: input is the anchors' float bits (keys computed here, values are the
-//         input indices); MODE 1: key/value buffers to key/value buffers;
-// MODE 2: writes float bits of the sorted anchors and the permutation.
+//         input indices); MODE 1: (key, value) pairs to pairs;
+// MODE 2: pairs in; writes float bits of the sorted anchors and the permutation.
+// Keys and values travel as interleaved pairs so that each digit run is one
+// contiguous stretch of 8-byte elements.
 // Threads 0..255 also own one digit value each for the per-digit steps.
 constexpr int kLookback = 8;  // predecessor status words read per round trip
 
 template <int MODE, typename ST>
-__global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin,
+__global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint2* __restrict__ kvin, uint2* __restrict__ kvout,
                                                          uint32_t* __restrict__ kout, uint32_t* __restrict__ vout,
                                                          const uint32_t* __restrict__ a_bits, ST* __restrict__ status,
                                                          uint32_t* __restrict__ header, int pass,
@@ -121,8 +123,7 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
   constexpr int E = kSortItems;
   constexpr int TILE = kSortTile;
   constexpr int NW = kSortBlock / kWave;
-  __shared__ __align__(16) uint32_t s_keys[TILE];
-  __shared__ uint32_t s_vals[TILE];
+  __shared__ __align__(16) uint2 s_kv[TILE];
   __shared__ uint32_t s_whist[NW][256];
   __shared__ uint32_t s_gbase[256];
   __shared__ uint32_t s_wsum[4];
@@ -130,11 +131,11 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
 
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
   const uint32_t shift = 8u * (uint32_t)pass;
-  // Ranking scratch, on top of s_keys (unused until the scatter): per wave and
+  // Ranking scratch, on top of s_kv (unused until the scatter): per wave and
   // digit value, {mask of the lanes holding that digit in the current
   // iteration (64 bits), the wave's running count of that digit, unused}.
-  static_assert(NW * 256 * sizeof(uint4) <= sizeof(s_keys), "ranking scratch fits in the key buffer");
-  uint4* s_match = reinterpret_cast<uint4*>(s_keys);
+  static_assert(NW * 256 * sizeof(uint4) <= sizeof(s_kv), "ranking scratch fits in the staging buffer");
+  uint4* s_match = reinterpret_cast<uint4*>(s_kv);
   if (tid == 0) s_tile = atomicAdd(&header[kHdrTicket0 + pass], 1u);
   for (int i = tid; i < NW * 256; i += kSortBlock) s_match[i] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
@@ -149,11 +150,12 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
     const uint64_t idx = base + (uint64_t)wid * (kWave * E) + (uint64_t)e * kWave + lane;
     const bool valid = idx < n;
     if (MODE == 0) {
-      k[e] = valid ? float_to_key(kin[idx]) : 0xFFFFFFFFu;
+      k[e] = valid ? float_to_key(a_bits[idx]) : 0xFFFFFFFFu;
       v[e] = (uint32_t)idx;
     } else {
-      k[e] = valid ? kin[idx] : 0xFFFFFFFFu;
-      v[e] = valid ? vin[idx] : 0u;
+      const uint2 kv = valid ? kvin[idx] : make_uint2(0xFFFFFFFFu, 0u);
+      k[e] = kv.x;
+      v[e] = kv.y;
     }
   }
   // stable rank within the wave's run: earlier iterations first, then lower
@@ -266,10 +268,7 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
   for (int e = 0; e < E; ++e) pos[e] = s_whist[wid][(k[e] >> shift) & 255u] + rk[e];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    if (first + (uint32_t)(e * kWave) < count) {
-      s_keys[pos[e]] = k[e];
-      s_vals[pos[e]] = v[e];
-    }
+    if (first + (uint32_t)(e * kWave) < count) s_kv[pos[e]] = make_uint2(k[e], v[e]);
   }
   if (r_lpos != nullptr) {
 #pragma unroll
@@ -284,26 +283,23 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint32_t* __restr
   static_assert((TILE / kSortBlock) % kOutBatch == 0, "write-out batches");
 #pragma unroll
   for (int r0 = 0; r0 < TILE / kSortBlock; r0 += kOutBatch) {
-    uint32_t key[kOutBatch], val[kOutBatch], o[kOutBatch];
+    uint2 kv[kOutBatch];
+    uint32_t o[kOutBatch];
 #pragma unroll
-    for (int j = 0; j < kOutBatch; ++j) {
-      const uint32_t i = (uint32_t)((r0 + j) * kSortBlock + tid);  // < TILE: slots past count hold stale words
-      key[j] = s_keys[i];
-      val[j] = s_vals[i];
-    }
+    for (int j = 0; j < kOutBatch; ++j) kv[j] = s_kv[(r0 + j) * kSortBlock + tid];  // slots past count: stale
 #pragma unroll
-    for (int j = 0; j < kOutBatch; ++j) o[j] = s_gbase[(key[j] >> shift) & 255u] + (uint32_t)((r0 + j) * kSortBlock + tid);
+    for (int j = 0; j < kOutBatch; ++j) o[j] = s_gbase[(kv[j].x >> shift) & 255u] + (uint32_t)((r0 + j) * kSortBlock + tid);
 #pragma unroll
     for (int j = 0; j < kOutBatch; ++j) {
       const uint32_t i = (uint32_t)((r0 + j) * kSortBlock + tid);
       // o < n holds for consistent counts; it is checked so nothing is ever written out of range
       if (i < count && (uint64_t)o[j] < n) {
         if (MODE == 2) {
-          kout[o[j]] = (key[j] == kKeyPlusZero && (uint64_t)val[j] < n) ? a_bits[val[j]] : key_to_float_bits(key[j]);
-          vout[o[j]] = val[j];
+          const uint32_t key = kv[j].x, val = kv[j].y;
+          kout[o[j]] = (key == kKeyPlusZero && (uint64_t)val < n) ? a_bits[val] : key_to_float_bits(key);
+          vout[o[j]] = val;
         } else {
-          kout[o[j]] = key[j];
-          vout[o[j]] = val[j];
+          kvout[o[j]] = kv[j];
         }
       }
     }
@@ -317,31 +313,30 @@ static hipError_t launch_sort_passes(const SortWorkspace& w, const float* a, uin
   const uint32_t* a_bits = reinterpret_cast<const uint32_t*>(a);
   const uint64_t tiles = (n + kSortTile - 1) / kSortTile;
   ST* st = reinterpret_cast<ST*>(w.status);
-  const uint32_t* src_k = nullptr;
-  const uint32_t* src_v = nullptr;
+  const uint2* src = nullptr;
   for (int p = 0; p < 4; ++p) {
     ST* stp = st + (uint64_t)p * tiles * 256;
-    uint32_t* dk = (p == 3) ? reinterpret_cast<uint32_t*>(a_sorted) : w.keys[p & 1];
-    uint32_t* dv = (p == 3) ? perm : w.vals[p & 1];
+    uint2* dst = (p == 3) ? nullptr : w.kv[p & 1];
+    uint32_t* fk = (p == 3) ? reinterpret_cast<uint32_t*>(a_sorted) : nullptr;
+    uint32_t* fv = (p == 3) ? perm : nullptr;
     uint16_t* rl = route ? route->lpos[p] : nullptr;
     uint16_t* rd = route ? route->dstart[p] : nullptr;
     uint32_t* rg = route ? route->gbase[p] : nullptr;
     if (p == 0)
       LAPLEX_LAUNCH(route ? "k_onesweep_first_routed" : "k_onesweep_first", n, s,
                     k_onesweep<0, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(
-                        a_bits, nullptr, dk, dv, a_bits, stp, w.header, p, w.offsets + p * 256, n, rl, rd, rg));
+                        nullptr, dst, fk, fv, a_bits, stp, w.header, p, w.offsets + p * 256, n, rl, rd, rg));
     else if (p == 3)
       LAPLEX_LAUNCH(route ? "k_onesweep_last_routed" : "k_onesweep_last", n, s,
                     k_onesweep<2, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(
-                        src_k, src_v, dk, dv, a_bits, stp, w.header, p, w.offsets + p * 256, n, rl, rd, rg));
+                        src, dst, fk, fv, a_bits, stp, w.header, p, w.offsets + p * 256, n, rl, rd, rg));
     else
       LAPLEX_LAUNCH(route ? "k_onesweep_mid_routed" : "k_onesweep_mid", n, s,
                     k_onesweep<1, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(
-                        src_k, src_v, dk, dv, a_bits, stp, w.header, p, w.offsets + p * 256, n, rl, rd, rg));
+                        src, dst, fk, fv, a_bits, stp, w.header, p, w.offsets + p * 256, n, rl, rd, rg));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    src_k = dk;
-    src_v = dv;
+    src = dst;
   }
   return hipSuccess;
 }
