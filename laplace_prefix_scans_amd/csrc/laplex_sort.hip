@@ -144,18 +144,26 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint2* __restrict
 
   // load: wave w owns the contiguous run [w*64*E, (w+1)*64*E) of the tile;
   // iteration e reads 64 consecutive keys, so (e, lane) is input order
+  // (all loads are issued before any loaded value is used)
   uint32_t k[E], v[E], rk[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint64_t idx = base + (uint64_t)wid * (kWave * E) + (uint64_t)e * kWave + lane;
     const bool valid = idx < n;
     if (MODE == 0) {
-      k[e] = valid ? float_to_key(a_bits[idx]) : 0xFFFFFFFFu;
+      k[e] = valid ? a_bits[idx] : 0u;
       v[e] = (uint32_t)idx;
     } else {
       const uint2 kv = valid ? kvin[idx] : make_uint2(0xFFFFFFFFu, 0u);
       k[e] = kv.x;
       v[e] = kv.y;
+    }
+  }
+  if (MODE == 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint64_t idx = base + (uint64_t)wid * (kWave * E) + (uint64_t)e * kWave + lane;
+      k[e] = idx < n ? float_to_key(k[e]) : 0xFFFFFFFFu;
     }
   }
   // stable rank within the wave's run: earlier iterations first, then lower
