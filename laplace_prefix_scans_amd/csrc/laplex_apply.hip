@@ -104,45 +104,45 @@ __device__ __forceinline__ void tile_scan(const float (&ae)[E], float (&v)[E][CC
   const float sz = __shfl_down(ae[0], 1);
   __syncthreads();
 
-  // forward carry into the wave: tile carry, then earlier waves
-  float cw[CC];
-  float sw = sf;
+  // Carries into the wave, as direct weighted sums (every weight <= 1):
+  // forward, at the last anchor s_ref of the previous wave (the tile carry's
+  // anchor for wave 0): lane l < wid holds wave l's aggregate weighted by
+  // exp(s_end(l) - s_ref), lane kWave-1 the tile carry weighted by
+  // exp(sf - s_ref); backward, mirrored.  Lane sums are butterflies, so every
+  // lane gets the same bits.
+  static_assert(NW < kWave, "one lane per wave aggregate plus one for the tile carry");
+  const float sw = wid > 0 ? s_wfs[wid - 1] : sf;
+  const float sz2 = wid < NW - 1 ? s_wbs[wid + 1] : sb;
+  float cw[CC], cz[CC];
+  {
+    const bool fw = lane < wid, bw = lane > wid && lane < NW;
+    const int lf = fw ? lane : 0, lb = bw ? lane : 0;
+    const float gf = fw ? decay(s_wfs[lf] - sw) : (lane == kWave - 1 ? decay(sf - sw) : 0.f);
+    const float gb = bw ? decay(sz2 - s_wbs[lb]) : (lane == kWave - 1 ? decay(sz2 - sb) : 0.f);
 #pragma unroll
-  for (int j = 0; j < CC; ++j) cw[j] = cf[j];
-  for (int w = 0; w < wid; ++w) {
-    const float s2 = s_wfs[w];
-    const float g = decay(sw - s2);
-#pragma unroll
-    for (int j = 0; j < CC; ++j) cw[j] = fmaf(g, cw[j], s_wf[w * CC + j]);
-    sw = s2;
+    for (int j = 0; j < CC; ++j) {
+      cw[j] = fw ? gf * s_wf[lf * CC + j] : (lane == kWave - 1 ? gf * cf[j] : 0.f);
+      cz[j] = bw ? gb * s_wb[lb * CC + j] : (lane == kWave - 1 ? gb * cb[j] : 0.f);
+    }
+    wave_sum<CC>(cw);
+    wave_sum<CC>(cz);
   }
+  float swl = sw, szl = sz2;
   if (lane > 0) {
-    const float g = decay(sw - sx);
+    const float g = decay(swl - sx);
 #pragma unroll
     for (int j = 0; j < CC; ++j) cw[j] = fmaf(g, cw[j], X[j]);
-    sw = sx;
-  }
-  // backward carry into the wave: tile carry, then later waves
-  float cz[CC];
-  float sz2 = sb;
-#pragma unroll
-  for (int j = 0; j < CC; ++j) cz[j] = cb[j];
-  for (int w = NW - 1; w > wid; --w) {
-    const float s2 = s_wbs[w];
-    const float g = decay(s2 - sz2);
-#pragma unroll
-    for (int j = 0; j < CC; ++j) cz[j] = fmaf(g, cz[j], s_wb[w * CC + j]);
-    sz2 = s2;
+    swl = sx;
   }
   if (lane < kWave - 1) {
-    const float g = decay(sz - sz2);
+    const float g = decay(sz - szl);
 #pragma unroll
     for (int j = 0; j < CC; ++j) cz[j] = fmaf(g, cz[j], Z[j]);
-    sz2 = sz;
+    szl = sz;
   }
 
   // full forward pass: strict lower part of each element
-  const float d0 = decay(sw - ae[0]);
+  const float d0 = decay(swl - ae[0]);
   float F[E][CC];
 #pragma unroll
   for (int j = 0; j < CC; ++j) {
@@ -154,7 +154,7 @@ __device__ __forceinline__ void tile_scan(const float (&ae)[E], float (&v)[E][CC
     }
   }
   // full backward pass, combined
-  const float dl = decay(ae[E - 1] - sz2);
+  const float dl = decay(ae[E - 1] - szl);
 #pragma unroll
   for (int j = 0; j < CC; ++j) {
     float U = cz[j];
@@ -616,31 +616,76 @@ __global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_sym_gather_redu
   }
 }
 
+// Row loads and stores of a thread's E consecutive rows.  FAST: the block's
+// rows are all in range, m == C, and the arrays are aligned for vector access.
+template <int E, int C, bool FAST>
+__device__ __forceinline__ void load_rows_t(const float* __restrict__ x, uint64_t p0, uint64_t n, uint32_t m, uint32_t cc,
+                                            float (&xv)[E][C]) {
+  if constexpr (FAST) {
+    float flat[E * C];
+    ld_contig<E * C>(x + p0 * C, flat, true);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int j = 0; j < C; ++j) xv[e][j] = flat[e * C + j];
+  } else {
+    load_rows<E, C>(x, p0, n, m, cc, true, xv);
+  }
+}
+template <int E, int C, bool FAST>
+__device__ __forceinline__ void store_rows_t(float* __restrict__ y, uint64_t p0, uint64_t n, uint32_t m, uint32_t cc,
+                                             const float (&yv)[E][C]) {
+  if constexpr (FAST) {
+    float flat[E * C];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int j = 0; j < C; ++j) flat[e * C + j] = yv[e][j];
+    st_contig<E * C>(y + p0 * C, flat, true);
+  } else {
+    store_rows<E, C>(y, p0, n, m, cc, true, yv);
+  }
+}
+
 // SCATTER: y rows written to original order through perm; otherwise to
 // sorted order (row p of y).
-template <int C, bool PH, bool SCATTER>
-__global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_sym_apply(
-    const float* __restrict__ a_s, const uint32_t* __restrict__ perm, const float* __restrict__ xs,
-    const float* __restrict__ phs, const float* __restrict__ cfw, const float* __restrict__ cbw,
-    const float2* __restrict__ tanch, uint64_t n, uint32_t m, uint64_t T, float* __restrict__ y, bool vec) {
+template <int C, bool PH, bool SCATTER, bool FAST>
+__device__ __forceinline__ void sym_apply_tile(const float* __restrict__ a_s, const uint32_t* __restrict__ perm,
+                                               const float* __restrict__ xs, const float* __restrict__ phs,
+                                               const float* __restrict__ cfw, const float* __restrict__ cbw,
+                                               const float2* __restrict__ tanch, uint64_t n, uint32_t m, uint64_t T,
+                                               float* __restrict__ y, bool vec, float* s_wf, float* s_wb, float* s_wfs,
+                                               float* s_wbs) {
   constexpr int CC = PH ? 2 * C : C;
   constexpr int E = apply_items(CC);
   constexpr int BLOCK = apply_block(CC);
   constexpr int NW = BLOCK / kWave;
   constexpr int P = BLOCK * E;
-  __shared__ float s_wf[NW * CC], s_wb[NW * CC], s_wfs[NW], s_wbs[NW];
   const uint32_t M = PH ? 2 * m : m;
   const int tid = threadIdx.x;
   const uint64_t tile = blockIdx.x;
   const uint64_t p0 = tile * P + (uint64_t)tid * E;
-  const float a_max = a_s[n - 1];
+  // the first column chunk's rows and carries are requested before anything
+  // else, so that all of the thread's loads are in flight together
+  float xv_n[E][C], cinf_n[CC], cinb_n[CC];
+  load_rows_t<E, C, FAST>(xs, p0, n, m, 0, xv_n);
+#pragma unroll
+  for (int j = 0; j < CC; ++j) {
+    const uint32_t col = sumcol<C, PH>(m, 0, j);
+    cinf_n[j] = cfw[tile * M + col];
+    cinb_n[j] = cbw[tile * M + col];
+  }
   float ae[E], cs[E], sn[E];
   uint32_t dst[E];
-  load_anchors<E>(a_s, p0, n, a_max, vec, ae);
+  if constexpr (FAST) {
+    ld_contig<E>(a_s + p0, ae, true);
+  } else {
+    load_anchors<E>(a_s, p0, n, a_s[n - 1], vec, ae);
+  }
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint64_t p = p0 + e;
-    const bool valid = p < n;
+    const bool valid = FAST || p < n;
     dst[e] = 0u;
     if (SCATTER) {
       dst[e] = valid ? perm[p] : 0u;
@@ -651,7 +696,11 @@ __global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_sym_apply(
   }
   if (PH) {
     float ph[E];
-    load_anchors<E>(phs, p0, n, 0.f, true, ph);
+    if constexpr (FAST) {
+      ld_contig<E>(phs + p0, ph, true);
+    } else {
+      load_anchors<E>(phs, p0, n, 0.f, true, ph);
+    }
 #pragma unroll
     for (int e = 0; e < E; ++e) sincosf(ph[e], &sn[e], &cs[e]);
   }
@@ -659,8 +708,25 @@ __global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_sym_apply(
   const float sf = tile > 0 ? tanch[tile - 1].y : ta.x;
   const float sb = tile + 1 < T ? tanch[tile + 1].x : ta.y;
   for (uint32_t cc = 0; cc < m / C; ++cc) {
-    float xv[E][C];
-    load_rows<E, C>(xs, p0, n, m, cc, true, xv);
+    float xv[E][C], cin_f[CC], cin_b[CC];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int j = 0; j < C; ++j) xv[e][j] = xv_n[e][j];
+#pragma unroll
+    for (int j = 0; j < CC; ++j) {
+      cin_f[j] = cinf_n[j];
+      cin_b[j] = cinb_n[j];
+    }
+    if (cc + 1 < m / C) {  // next chunk's loads overlap this chunk's scan
+      load_rows_t<E, C, FAST>(xs, p0, n, m, cc + 1, xv_n);
+#pragma unroll
+      for (int j = 0; j < CC; ++j) {
+        const uint32_t col = sumcol<C, PH>(m, cc + 1, j);
+        cinf_n[j] = cfw[tile * M + col];
+        cinb_n[j] = cbw[tile * M + col];
+      }
+    }
     float v[E][CC];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -674,13 +740,6 @@ __global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_sym_apply(
         }
       }
     }
-    float cin_f[CC], cin_b[CC];
-#pragma unroll
-    for (int j = 0; j < CC; ++j) {
-      const uint32_t col = sumcol<C, PH>(m, cc, j);
-      cin_f[j] = cfw[tile * M + col];
-      cin_b[j] = cbw[tile * M + col];
-    }
     tile_scan<E, CC, NW>(ae, v, cin_f, sf, cin_b, sb, s_wf, s_wfs, s_wb, s_wbs);
     float yv[E][C];
 #pragma unroll
@@ -690,17 +749,32 @@ __global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_sym_apply(
     if (SCATTER) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        if (p0 + e < n) {
+        if (FAST || p0 + e < n) {
           float* yr = y + (uint64_t)dst[e] * m + cc * C;
 #pragma unroll
           for (int j = 0; j < C; ++j) yr[j] = yv[e][j];
         }
       }
     } else {
-      store_rows<E, C>(y, p0, n, m, cc, true, yv);
+      store_rows_t<E, C, FAST>(y, p0, n, m, cc, yv);
     }
     __syncthreads();
   }
+}
+
+template <int C, bool PH, bool SCATTER>
+__global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_sym_apply(
+    const float* __restrict__ a_s, const uint32_t* __restrict__ perm, const float* __restrict__ xs,
+    const float* __restrict__ phs, const float* __restrict__ cfw, const float* __restrict__ cbw,
+    const float2* __restrict__ tanch, uint64_t n, uint32_t m, uint64_t T, float* __restrict__ y, bool vec) {
+  constexpr int CC = PH ? 2 * C : C;
+  constexpr int NW = apply_block(CC) / kWave;
+  constexpr int P = apply_tile(CC);
+  __shared__ float s_wf[NW * CC], s_wb[NW * CC], s_wfs[NW], s_wbs[NW];
+  if (vec && m == C && ((uint64_t)blockIdx.x + 1) * P <= n)
+    sym_apply_tile<C, PH, SCATTER, true>(a_s, perm, xs, phs, cfw, cbw, tanch, n, m, T, y, vec, s_wf, s_wb, s_wfs, s_wbs);
+  else
+    sym_apply_tile<C, PH, SCATTER, false>(a_s, perm, xs, phs, cfw, cbw, tanch, n, m, T, y, vec, s_wf, s_wb, s_wfs, s_wbs);
 }
 
 template <int C, bool PH>
