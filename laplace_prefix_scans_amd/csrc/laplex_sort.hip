@@ -41,8 +41,11 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, uint64_t count, uint32_t va
 // kHistRep times in LDS (lane % kHistRep picks one) so that keys sharing a
 // digit (e.g. the top byte of anchors in a narrow range) do not all hit one
 // LDS word.  Integer atomics: the result does not depend on ordering.
-constexpr int kHistRep = 8;
-constexpr int kHistBlock = 256;
+// One replica of every histogram per lane position (lane mod 32), so the 32
+// lanes an LDS cycle serves always hit 32 different banks; 1024 threads keep
+// enough loads in flight with one block per CU.
+constexpr int kHistRep = 32;
+constexpr int kHistBlock = 1024;
 constexpr int kHistItems = 16;
 
 __global__ __launch_bounds__(kHistBlock) void k_sort_hist(const uint32_t* __restrict__ a_bits, uint64_t n,
@@ -56,13 +59,18 @@ __global__ __launch_bounds__(kHistBlock) void k_sort_hist(const uint32_t* __rest
   const uint64_t nchunks = (n + chunk - 1) / chunk;
   for (uint64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
     const uint64_t base = c * chunk;
+    uint32_t u[kHistItems];
+#pragma unroll
+    for (int it = 0; it < kHistItems; ++it) {
+      const uint64_t i = base + (uint64_t)it * kHistBlock + threadIdx.x;
+      u[it] = i < n ? a_bits[i] : 0u;
+    }
 #pragma unroll
     for (int it = 0; it < kHistItems; ++it) {
       const uint64_t i = base + (uint64_t)it * kHistBlock + threadIdx.x;
       if (i < n) {
-        const uint32_t u = a_bits[i];
-        bad |= bits_nonfinite(u) ? 1u : 0u;
-        const uint32_t k = float_to_key(u);
+        bad |= bits_nonfinite(u[it]) ? 1u : 0u;
+        const uint32_t k = float_to_key(u[it]);
         atomicAdd(&sh[0][k & 255u][rep], 1u);
         atomicAdd(&sh[1][(k >> 8) & 255u][rep], 1u);
         atomicAdd(&sh[2][(k >> 16) & 255u][rep], 1u);
@@ -74,7 +82,7 @@ __global__ __launch_bounds__(kHistBlock) void k_sort_hist(const uint32_t* __rest
   for (int i = threadIdx.x; i < 4 * 256; i += kHistBlock) {
     uint32_t s = 0;
 #pragma unroll
-    for (int r = 0; r < kHistRep; ++r) s += sh[i >> 8][i & 255][r];
+    for (int r = 0; r < kHistRep; ++r) s += sh[i >> 8][i & 255][(r + i) % kHistRep];
     if (s) atomicAdd(&hist[i], s);
   }
   if (__ballot(bad) != 0ull && lane_id() == 0) atomicOr(&header[kHdrFlags], kFlagNonFinite);
@@ -364,7 +372,7 @@ hipError_t sort_anchors(const SortWorkspace& w, const float* a, uint64_t n, floa
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint64_t chunk = (uint64_t)kHistBlock * kHistItems;
-  const unsigned hist_blocks = (unsigned)std::min<uint64_t>((n + chunk - 1) / chunk, 2048);
+  const unsigned hist_blocks = (unsigned)std::min<uint64_t>((n + chunk - 1) / chunk, 256);
   LAPLEX_LAUNCH("k_sort_hist", n, s,
                 k_sort_hist<<<hist_blocks, kHistBlock, 0, s>>>(reinterpret_cast<const uint32_t*>(a), n, w.hist, w.header));
   if ((e = hipGetLastError()) != hipSuccess) return e;
