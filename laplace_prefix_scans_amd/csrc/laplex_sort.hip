@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void k_sort_offsets(const uint32_t* __restrict
 constexpr int kLookback = 8;  // predecessor status words read per round trip
 
 template <int MODE, typename ST>
-__global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint2* __restrict__ kvin, uint2* __restrict__ kvout,
+__global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6))) void k_onesweep(const uint2* __restrict__ kvin, uint2* __restrict__ kvout,
                                                          uint32_t* __restrict__ kout, uint32_t* __restrict__ vout,
                                                          const uint32_t* __restrict__ a_bits, ST* __restrict__ status,
                                                          uint32_t* __restrict__ header, int pass,
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint2* __restrict
   constexpr int E = kSortItems;
   constexpr int TILE = kSortTile;
   constexpr int NW = kSortBlock / kWave;
-  __shared__ __align__(16) uint2 s_kv[TILE];
+  __shared__ __align__(16) uint2 s_kv[TILE / 2];
   __shared__ uint32_t s_whist[NW][256];
   __shared__ uint32_t s_gbase[256];
   __shared__ uint32_t s_wsum[4];
@@ -152,19 +152,21 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint2* __restrict
 
   // load: wave w owns the contiguous run [w*64*E, (w+1)*64*E) of the tile;
   // iteration e reads 64 consecutive keys, so (e, lane) is input order
-  // (all loads are issued before any loaded value is used)
-  uint32_t k[E], v[E], rk[E];
+  // (all loads are issued before any loaded value is used).  Ranks and
+  // positions (< 2^13) are kept two per register, and the first pass
+  // recomputes its values (the input indices) instead of holding them.
+  static_assert(E % 2 == 0 && TILE <= 65536, "16-bit packed ranks");
+  uint32_t k[E], v[MODE == 0 ? 1 : E], rkp[E / 2];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint64_t idx = base + (uint64_t)wid * (kWave * E) + (uint64_t)e * kWave + lane;
     const bool valid = idx < n;
     if (MODE == 0) {
       k[e] = valid ? a_bits[idx] : 0u;
-      v[e] = (uint32_t)idx;
     } else {
       const uint2 kv = valid ? kvin[idx] : make_uint2(0xFFFFFFFFu, 0u);
       k[e] = kv.x;
-      v[e] = kv.y;
+      v[MODE == 0 ? 0 : e] = kv.y;
     }
   }
   if (MODE == 0) {
@@ -186,6 +188,8 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint2* __restrict
   for (int e = 0; e < E; ++e) {
     const uint64_t idx = base + (uint64_t)wid * (kWave * E) + (uint64_t)e * kWave + lane;
     const bool valid = idx < n;
+    // (keeps the compiler from computing every iteration's digit up front)
+    asm volatile("" : "+v"(k[e])::"memory");
     const uint32_t d = (k[e] >> shift) & 255u;
     if (valid)
       __hip_atomic_fetch_or(reinterpret_cast<unsigned long long*>(&my[d]), lanebit, __ATOMIC_RELAXED,
@@ -194,8 +198,15 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint2* __restrict
     const uint64_t peers = ((uint64_t)ent.y << 32) | ent.x;
     const uint32_t r = lanes_below(peers);
     const uint32_t next = ent.z + (uint32_t)__popcll(peers);
-    rk[e] = ent.z + r;
-    if (valid && r == 0) my[d] = make_uint4(0u, 0u, next, 0u);
+    if (e % 2 == 0)
+      rkp[e / 2] = ent.z + r;
+    else
+      rkp[e / 2] |= (ent.z + r) << 16;
+    asm volatile("" : "+v"(rkp[e / 2]));  // packed now, not at its distant use
+    if (valid && r == 0) {
+      reinterpret_cast<uint64_t*>(&my[d])[0] = 0ull;
+      reinterpret_cast<uint32_t*>(&my[d])[2] = next;
+    }
   }
   __syncthreads();
 
@@ -273,52 +284,74 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(const uint2* __restrict
   }
   __syncthreads();
 
-  // place the keys in LDS in digit order (stable).  All table reads are
-  // issued before the LDS writes, and the route's global stores come last so
-  // that no LDS write waits on them.
+  // place the keys in LDS in digit order (stable) and write them out, one
+  // half of the tile's sorted order at a time (the staging buffer holds half a
+  // tile, which keeps three blocks resident per CU).  All table reads are
+  // issued before the LDS writes, and the route's global stores come after
+  // them so that no LDS write waits on a store.
   const uint64_t rem = n - base;
   const uint32_t count = rem < (uint64_t)TILE ? (uint32_t)rem : (uint32_t)TILE;
   const uint32_t first = (uint32_t)(wid * (kWave * E) + lane);  // tile-local index at e = 0
-  uint32_t pos[E];
+  // (the empty asm makes the keys opaque here, so that the digits computed
+  // during the ranking are recomputed rather than held in registers across
+  // the look-back)
 #pragma unroll
-  for (int e = 0; e < E; ++e) pos[e] = s_whist[wid][(k[e] >> shift) & 255u] + rk[e];
+  for (int e = 0; e < E; ++e) asm volatile("" : "+v"(k[e]));
+  uint32_t posp[E / 2];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    if (first + (uint32_t)(e * kWave) < count) s_kv[pos[e]] = make_uint2(k[e], v[e]);
+  for (int e = 0; e < E; e += 2) {
+    const uint32_t p0 = s_whist[wid][(k[e] >> shift) & 255u] + (rkp[e / 2] & 0xFFFFu);
+    const uint32_t p1 = s_whist[wid][(k[e + 1] >> shift) & 255u] + (rkp[e / 2] >> 16);
+    posp[e / 2] = p0 | (p1 << 16);
   }
-  if (r_lpos != nullptr) {
+  auto pos_of = [&](int e) -> uint32_t { return (e % 2 == 0) ? (posp[e / 2] & 0xFFFFu) : (posp[e / 2] >> 16); };
+  auto val_of = [&](int e) -> uint32_t {
+    return MODE == 0 ? (uint32_t)(base + first + (uint32_t)(e * kWave)) : v[MODE == 0 ? 0 : e];
+  };
+  constexpr uint32_t HALF = TILE / 2;
+  constexpr int kOutSteps = HALF / kSortBlock;  // slots per thread and half
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (first + (uint32_t)(e * kWave) < count) r_lpos[base + first + (uint32_t)(e * kWave)] = (uint16_t)pos[e];
-  }
-  __syncthreads();
-
-  // write out: consecutive threads write consecutive slots of a digit's run;
-  // in batches whose LDS reads are all issued before the stores
-  constexpr int kOutBatch = 8;
-  static_assert((TILE / kSortBlock) % kOutBatch == 0, "write-out batches");
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t lo = (uint32_t)h * HALF;
 #pragma unroll
-  for (int r0 = 0; r0 < TILE / kSortBlock; r0 += kOutBatch) {
-    uint2 kv[kOutBatch];
-    uint32_t o[kOutBatch];
+    for (int e = 0; e < E; ++e) {
+      if (first + (uint32_t)(e * kWave) < count && pos_of(e) - lo < HALF) s_kv[pos_of(e) - lo] = make_uint2(k[e], val_of(e));
+    }
+    if (h == 0 && r_lpos != nullptr) {
 #pragma unroll
-    for (int j = 0; j < kOutBatch; ++j) kv[j] = s_kv[(r0 + j) * kSortBlock + tid];  // slots past count: stale
+      for (int e = 0; e < E; ++e)
+        if (first + (uint32_t)(e * kWave) < count) r_lpos[base + first + (uint32_t)(e * kWave)] = (uint16_t)pos_of(e);
+    }
+    __syncthreads();
+    // consecutive threads write consecutive slots of a digit's run, in
+    // batches whose LDS reads are all issued before their stores
+    constexpr int kOutBatch = 4;
+    static_assert(kOutSteps % kOutBatch == 0, "write-out batches");
 #pragma unroll
-    for (int j = 0; j < kOutBatch; ++j) o[j] = s_gbase[(kv[j].x >> shift) & 255u] + (uint32_t)((r0 + j) * kSortBlock + tid);
+    for (int j0 = 0; j0 < kOutSteps; j0 += kOutBatch) {
+      uint2 kv[kOutBatch];
+      uint32_t o[kOutBatch];
 #pragma unroll
-    for (int j = 0; j < kOutBatch; ++j) {
-      const uint32_t i = (uint32_t)((r0 + j) * kSortBlock + tid);
-      // o < n holds for consistent counts; it is checked so nothing is ever written out of range
-      if (i < count && (uint64_t)o[j] < n) {
-        if (MODE == 2) {
-          const uint32_t key = kv[j].x, val = kv[j].y;
-          kout[o[j]] = (key == kKeyPlusZero && (uint64_t)val < n) ? a_bits[val] : key_to_float_bits(key);
-          vout[o[j]] = val;
-        } else {
-          kvout[o[j]] = kv[j];
+      for (int j = 0; j < kOutBatch; ++j) kv[j] = s_kv[(j0 + j) * kSortBlock + tid];  // slots past count: stale
+#pragma unroll
+      for (int j = 0; j < kOutBatch; ++j)
+        o[j] = s_gbase[(kv[j].x >> shift) & 255u] + lo + (uint32_t)((j0 + j) * kSortBlock + tid);
+#pragma unroll
+      for (int j = 0; j < kOutBatch; ++j) {
+        const uint32_t i = lo + (uint32_t)((j0 + j) * kSortBlock + tid);
+        // o < n holds for consistent counts; it is checked so nothing is ever written out of range
+        if (i < count && (uint64_t)o[j] < n) {
+          if (MODE == 2) {
+            const uint32_t key = kv[j].x, val = kv[j].y;
+            kout[o[j]] = (key == kKeyPlusZero && (uint64_t)val < n) ? a_bits[val] : key_to_float_bits(key);
+            vout[o[j]] = val;
+          } else {
+            kvout[o[j]] = kv[j];
+          }
         }
       }
     }
+    if (h == 0) __syncthreads();  // the second half reuses the staging buffer
   }
 }
 
