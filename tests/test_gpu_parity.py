@@ -76,7 +76,11 @@ def test_sym_parity(n, m):
     for ties in (False, True):
         a, x = _sym_case(n, m, n / 8.0 + 1.0, 10 + n + m, ties)
         _, a_s, perm = gpu_sort(a)
+        pa = host(perm)
+        bad = np.nonzero(pa != oracle.stable_argsort(a))[0]
+        assert bad.size == 0, "sym n=%d m=%d ties=%s: perm differs at %d positions, first %d" % (n, m, ties, bad.size, bad[0])
         y = host(lp.laplex_matvec_sym(a_s, perm, dev(x)))
+        assert np.isfinite(y).all(), "sym n=%d m=%d ties=%s: non-finite output" % (n, m, ties)
         ref = oracle.sym_apply(a, x)
         env = oracle.sym_apply(a, np.abs(x))
         err = oracle.normwise_error(y, ref, env)
