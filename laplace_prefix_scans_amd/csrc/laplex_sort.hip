@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void k_sort_offsets(const uint32_t* __restrict
 // Keys and values travel as interleaved pairs so that each digit run is one
 // contiguous stretch of 8-byte elements.
 // Threads 0..255 also own one digit value each for the per-digit steps.
-constexpr int kLookback = 8;  // predecessor status words read per round trip
+constexpr int kLookback = 4;  // predecessor status words read per round trip (more costs more status traffic than it saves)
 
 template <int MODE, typename ST>
 __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6))) void k_onesweep(const uint2* __restrict__ kvin, uint2* __restrict__ kvout,
