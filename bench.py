@@ -100,8 +100,8 @@ def rocprof_label(name: str, pass_index: int = 0, routed: bool = True) -> str:
     if kern == "k_onesweep":
         label = {"0": "k_onesweep_first", "1": "k_onesweep_mid", "2": "k_onesweep_last"}[targs[0]]
         return label + ("_routed" if routed else "")
-    if kern in ("k_route_fwd", "k_route_inv"):
-        return "%s_w%s" % (kern, targs[0])
+    if kern in ("k_route_fwd", "k_route_inv", "k_route_inv_chunked"):
+        return "%s_w%s" % (kern.replace("_chunked", ""), targs[0])
     if kern == "k_sym_gather_reduce":
         ph, gather = targs[1] == "true", targs[2] == "true"
         return ("k_phased" if ph else "k_sym") + ("_gather_reduce" if gather else "_reduce")
