@@ -763,7 +763,8 @@ __device__ __forceinline__ void sym_apply_tile(const float* __restrict__ a_s, co
 }
 
 template <int C, bool PH, bool SCATTER>
-__global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_sym_apply(
+__global__ __launch_bounds__(apply_block(PH ? 2 * C : C))
+__attribute__((amdgpu_waves_per_eu(!PH && C == 1 ? 8 : 1))) void k_sym_apply(
     const float* __restrict__ a_s, const uint32_t* __restrict__ perm, const float* __restrict__ xs,
     const float* __restrict__ phs, const float* __restrict__ cfw, const float* __restrict__ cbw,
     const float2* __restrict__ tanch, uint64_t n, uint32_t m, uint64_t T, float* __restrict__ y, bool vec) {

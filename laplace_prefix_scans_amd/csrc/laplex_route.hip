@@ -243,6 +243,8 @@ __global__ __launch_bounds__(kSortBlock) void k_route_inv_chunked(const float* _
   if (!xcd_tile((n + TILE - 1) / TILE, tile)) return;
   const uint64_t base = tile * TILE;
   const uint32_t count = (uint32_t)std::min<uint64_t>(TILE, n - base);
+  // the input-order side's positions are requested first, so that their
+  // latency overlaps the tables and the run-side reads
   uint2 lp2[GSTEPS];
 #pragma unroll
   for (int r = 0; r < GSTEPS; ++r) {
@@ -288,8 +290,7 @@ __global__ __launch_bounds__(kSortBlock) void k_route_inv_chunked(const float* _
   const uint64_t nfl = n * W;  // >= 4 (the host launches this kernel only then)
   // all chunk loads are issued before any is consumed; a chunk that is not
   // loaded whole (past `total`, or reaching past the array) loads chunk 0
-  uint32_t dg[CSTEPS];
-  uint64_t gg[CSTEPS];
+  uint32_t dg[CSTEPS], gg[CSTEPS];  // run and global chunk index (< n W / 4 + 1 <= 2^32)
   float4 q[CSTEPS];
 #pragma unroll
   for (int r = 0; r < CSTEPS; ++r) {
@@ -299,8 +300,8 @@ __global__ __launch_bounds__(kSortBlock) void k_route_inv_chunked(const float* _
 #pragma unroll
   for (int r = 0; r < CSTEPS; ++r) {
     const uint32_t c = (uint32_t)(r * kSortBlock + tid);
-    gg[r] = (uint64_t)s_c0[dg[r]] + (c - s_cs[dg[r]]);
-    const bool whole = c < total && 4 * gg[r] + 4 <= nfl;
+    gg[r] = s_c0[dg[r]] + (c - s_cs[dg[r]]);
+    const bool whole = c < total && 4 * (uint64_t)gg[r] + 4 <= nfl;
     q[r] = reinterpret_cast<const float4*>(in)[whole ? gg[r] : 0];
   }
 #pragma unroll
