@@ -210,6 +210,61 @@ __global__ __launch_bounds__(kSortBlock) void k_route_inv(const float* __restric
   }
 }
 
+// Chunk cover of a tile's digit runs, for rows of W floats (W = 1, 2, 4):
+// run d covers global rows [G, G + L); the aligned 4-float chunks that overlap
+// it are numbered block-locally from cs[d], the first being global chunk
+// c0[d]; cdig[c] is the run of block-local chunk c.  L is clipped to the
+// array, so no chunk lies wholly past it.
+template <int W>
+struct RunChunks {
+  static constexpr int kMax = kSortTile * W / 4 + 512;  // sum over runs of (L W + 6) / 4
+  uint8_t cdig[kMax];
+  uint32_t cs[257];
+  uint32_t c0[256];
+  uint32_t len[256];
+  uint32_t wsum[4];
+};
+
+// Called by every thread of the block after s_start / s_gb are written (and
+// not yet synchronised); ends with a barrier.
+template <int W, int NW>
+__device__ __forceinline__ void build_chunks(RunChunks<W>& rc, const uint16_t* s_start, const uint32_t* s_gb, uint64_t n) {
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  __syncthreads();
+  uint32_t nch = 0, x = 0;
+  if (tid < 256) {
+    const uint32_t lo = s_start[tid], hi = s_start[tid + 1];
+    const uint64_t G = (uint64_t)(uint32_t)(s_gb[tid] + lo);
+    uint64_t L = hi > lo ? hi - lo : 0;
+    if (G >= n) L = 0;
+    else if (G + L > n) L = n - G;
+    const uint64_t c0 = G * W / 4, c1 = ((G + L) * W + 3) / 4;
+    nch = L ? (uint32_t)(c1 - c0) : 0u;
+    rc.c0[tid] = (uint32_t)c0;
+    rc.len[tid] = (uint32_t)L;
+    x = nch;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t t = __shfl_up(x, off);
+      if (lane >= off) x += t;
+    }
+    if (lane == kWave - 1) rc.wsum[wid] = x;
+  }
+  __syncthreads();
+  if (tid < 256) {
+    uint32_t pre = 0;
+    for (int i = 0; i < wid; ++i) pre += rc.wsum[i];
+    rc.cs[tid] = pre + x - nch;
+    if (tid == 255) rc.cs[256] = pre + x;
+  }
+  __syncthreads();
+  for (int d = wid; d < 256; d += NW) {
+    const uint32_t lo = rc.cs[d], hi = rc.cs[d + 1];
+    for (uint32_t c = lo + lane; c < hi; c += kWave) rc.cdig[c] = (uint8_t)d;
+  }
+  __syncthreads();
+}
+
 // Inverse pass whose digit-run side reads 16-byte aligned chunks (W = 1, 2,
 // 4 floats per row; `in` 16-byte aligned).  Each run [G, G + L) of global rows
 // is covered by the aligned 4-float chunks that overlap it; a thread loads one
@@ -219,7 +274,7 @@ __global__ __launch_bounds__(kSortBlock) void k_route_inv(const float* __restric
 // reaching past the end of the array is read float by float.  vec: `out` is
 // 16-byte aligned.
 template <int W>
-__global__ __launch_bounds__(kSortBlock) void k_route_inv_chunked(const float* __restrict__ in, float* __restrict__ out,
+__global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(W == 1 ? 8 : 1))) void k_route_inv_chunked(const float* __restrict__ in, float* __restrict__ out,
                                                                   const uint16_t* __restrict__ lpos,
                                                                   const uint16_t* __restrict__ dstart,
                                                                   const uint32_t* __restrict__ gbase, uint64_t n, bool vec) {
@@ -227,18 +282,14 @@ __global__ __launch_bounds__(kSortBlock) void k_route_inv_chunked(const float* _
   constexpr int TILE = kSortTile;
   constexpr int NW = kSortBlock / kWave;
   constexpr int GSTEPS = TILE / (kSortBlock * kGroup);
-  constexpr int MAXCH = TILE * W / 4 + 512;  // sum over runs of (L W + 6) / 4
+  constexpr int MAXCH = RunChunks<W>::kMax;
   constexpr int CSTEPS = (MAXCH + kSortBlock - 1) / kSortBlock;
   constexpr int RPC = 4 / W;  // rows per chunk
   __shared__ float s_val[TILE * W];
-  __shared__ uint8_t s_cdig[MAXCH];
   __shared__ uint16_t s_start[257];
   __shared__ uint32_t s_gb[256];
-  __shared__ uint32_t s_cs[257];  // first block-local chunk of each run
-  __shared__ uint32_t s_c0[256];  // global chunk index of each run's first chunk
-  __shared__ uint32_t s_len[256];
-  __shared__ uint32_t s_wsum[4];
-  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  __shared__ RunChunks<W> rc;
+  const int tid = threadIdx.x;
   uint64_t tile;
   if (!xcd_tile((n + TILE - 1) / TILE, tile)) return;
   const uint64_t base = tile * TILE;
@@ -252,67 +303,31 @@ __global__ __launch_bounds__(kSortBlock) void k_route_inv_chunked(const float* _
     lp2[r] = i0 + kGroup <= count ? *reinterpret_cast<const uint2*>(lpos + base + i0) : make_uint2(0u, 0u);
   }
   load_tables(dstart, gbase, tile, count, s_start, s_gb);
-  __syncthreads();
-  // per run: global first row G, length L (clipped to the array), chunk range
-  uint32_t nch = 0, x = 0;
-  if (tid < 256) {
-    const uint32_t lo = s_start[tid], hi = s_start[tid + 1];
-    const uint64_t G = (uint64_t)(uint32_t)(s_gb[tid] + lo);
-    uint64_t L = hi > lo ? hi - lo : 0;
-    if (G >= n) L = 0;
-    else if (G + L > n) L = n - G;
-    const uint64_t c0 = G * W / 4, c1 = ((G + L) * W + 3) / 4;
-    nch = L ? (uint32_t)(c1 - c0) : 0u;
-    s_c0[tid] = (uint32_t)c0;
-    s_len[tid] = (uint32_t)L;
-    x = nch;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const uint32_t t = __shfl_up(x, off);
-      if (lane >= off) x += t;
-    }
-    if (lane == kWave - 1) s_wsum[wid] = x;
-  }
-  __syncthreads();
-  if (tid < 256) {
-    uint32_t pre = 0;
-    for (int i = 0; i < wid; ++i) pre += s_wsum[i];
-    s_cs[tid] = pre + x - nch;
-    if (tid == 255) s_cs[256] = pre + x;
-  }
-  __syncthreads();
-  for (int d = wid; d < 256; d += NW) {
-    const uint32_t lo = s_cs[d], hi = s_cs[d + 1];
-    for (uint32_t c = lo + lane; c < hi; c += kWave) s_cdig[c] = (uint8_t)d;
-  }
-  __syncthreads();
-  const uint32_t total = s_cs[256];
+  build_chunks<W, NW>(rc, s_start, s_gb, n);
+  const uint32_t total = rc.cs[256];
   const uint64_t nfl = n * W;  // >= 4 (the host launches this kernel only then)
   // all chunk loads are issued before any is consumed; a chunk that is not
-  // loaded whole (past `total`, or reaching past the array) loads chunk 0
-  uint32_t dg[CSTEPS], gg[CSTEPS];  // run and global chunk index (< n W / 4 + 1 <= 2^32)
+  // loaded whole (past `total`, or reaching past the array) loads chunk 0.
+  // The run and global index of each chunk are looked up again afterwards
+  // rather than held in registers across the loads.
   float4 q[CSTEPS];
 #pragma unroll
   for (int r = 0; r < CSTEPS; ++r) {
-    const uint32_t c = std::min<uint32_t>((uint32_t)(r * kSortBlock + tid), MAXCH - 1);
-    dg[r] = s_cdig[c];
-  }
-#pragma unroll
-  for (int r = 0; r < CSTEPS; ++r) {
     const uint32_t c = (uint32_t)(r * kSortBlock + tid);
-    gg[r] = s_c0[dg[r]] + (c - s_cs[dg[r]]);
-    const bool whole = c < total && 4 * (uint64_t)gg[r] + 4 <= nfl;
-    q[r] = reinterpret_cast<const float4*>(in)[whole ? gg[r] : 0];
+    const uint32_t d = rc.cdig[std::min<uint32_t>(c, MAXCH - 1)];
+    const uint32_t g = rc.c0[d] + (c - rc.cs[d]);  // global chunk index (< n W / 4 + 1 <= 2^32)
+    const bool whole = c < total && 4 * (uint64_t)g + 4 <= nfl;
+    q[r] = reinterpret_cast<const float4*>(in)[whole ? g : 0u];
   }
 #pragma unroll
   for (int r = 0; r < CSTEPS; ++r) {
     const uint32_t c = (uint32_t)(r * kSortBlock + tid);
     if (c < total) {
-      const uint32_t d = dg[r];
-      const uint64_t g = gg[r];
+      const uint32_t d = rc.cdig[c];
+      const uint64_t g = rc.c0[d] + (c - rc.cs[d]);
       const uint32_t gb = s_gb[d];
       const uint64_t G = (uint64_t)(uint32_t)(gb + s_start[d]);
-      const uint64_t Gend = G + s_len[d];
+      const uint64_t Gend = G + rc.len[d];
       float v[4] = {q[r].x, q[r].y, q[r].z, q[r].w};
       if (4 * g + 4 > nfl) {
 #pragma unroll
