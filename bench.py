@@ -361,6 +361,18 @@ def main():
         "avg_launch_ms": dk["avg_launch_ms"],
     }
     step_bytes = sum(s["bytes"] for s in stats.values()) / args.steps
+
+    # the step split into its sort (row a1) and its apply (rows a2-a7, given
+    # the sort handle): kernel time and algorithmic bytes of each part
+    def part(names):
+        ms = sum(stats[q]["ms"] for q in names) / args.steps
+        by = sum(stats[q]["bytes"] for q in names) / args.steps
+        gbps = by / (ms * 1e-3) / 1e9 if ms > 0 else None
+        return {"kernel_ms": round(ms, 4), "alg_GB": round(by / 1e9, 3), "alg_GBps": round(gbps, 1) if gbps else None,
+                "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4) if gbps else None,
+                "Gelem_per_s": round(n * m / (ms * 1e-3) / 1e9, 4) if ms > 0 else None}
+    sort_names = [q for q in stats if q.startswith(("k_sort", "k_onesweep", "k_fill"))]
+    apply_names = [q for q in stats if q not in sort_names]
     line = {
         "metric": METRIC,
         "value": round(n * m / (ms_per_step * 1e-3) / 1e9, 4),
@@ -378,6 +390,8 @@ def main():
                    "step": "sort + apply", "route": use_route, "recipe": w.recipe},
         "roofline": roofline,
         "step_alg_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "sort_part": part(sort_names),
+        "apply_part": part(apply_names),
         "kernels": kernels,
         "source_hash": src,
         "host_gen_s": round(t_gen, 1),

@@ -421,7 +421,7 @@ namespace laplex {
 hipError_t fill_zero_u32(void* p, uint64_t words, hipStream_t s) {
   if (words == 0) return hipSuccess;
   const unsigned blocks = (unsigned)std::min<uint64_t>((words + 255) / 256, 4096);
-  LAPLEX_LAUNCH("k_fill_u32", words, s, k_fill_u32<<<blocks, 256, 0, s>>>(static_cast<uint32_t*>(p), words, 0u));
+  LAPLEX_LAUNCH("k_zero_rows", words, s, k_fill_u32<<<blocks, 256, 0, s>>>(static_cast<uint32_t*>(p), words, 0u));
   return hipGetLastError();
 }
 }  // namespace laplex
