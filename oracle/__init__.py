@@ -67,7 +67,10 @@ def load(path: Optional[str] = None):
         lib.lo_phased_apply.argtypes = [f32p, f32p, i64, f32p, f32p, i64, i64, f32p, f64p]
         lib.lo_dense_rows.argtypes = [f32p, f32p, ctypes.POINTER(ctypes.c_int64), i64, f32p, f32p, i64, i64, f32p, f64p,
                                       f64p]
-        for fn in (lib.lo_stable_argsort, lib.lo_sym_apply, lib.lo_general_apply, lib.lo_phased_apply, lib.lo_dense_rows):
+        lib.lo_sym_backward.argtypes = [f32p, i64, i64, f32p, f32p, f64p, f64p]
+        lib.lo_general_backward.argtypes = [f32p, i64, f32p, i64, i64, f32p, f32p, f64p, f64p, f64p]
+        for fn in (lib.lo_stable_argsort, lib.lo_sym_apply, lib.lo_general_apply, lib.lo_phased_apply, lib.lo_dense_rows,
+                   lib.lo_sym_backward, lib.lo_general_backward):
             fn.restype = ctypes.c_int
         if path is None:
             _lib_handle = lib
@@ -113,6 +116,35 @@ def sym_apply(a, x, lib=None) -> np.ndarray:
     y = np.empty(x2.shape, np.float64)
     _check(lib.lo_sym_apply(_ptr(a, ctypes.c_float), a.size, x2.shape[1], _ptr(x2, ctypes.c_float), _ptr(y, ctypes.c_double)))
     return y
+
+
+def sym_backward(a, x, g, lib=None):
+    """Backward of y = K(a, a) x for an upstream gradient g = dL/dy (float64):
+    returns (dx = K g, n x m; da, n) with sign(0) = 0 at tied anchors."""
+    lib = lib or load()
+    a = _f32(a).ravel()
+    x2, g2 = _as2d(x, a.size), _as2d(g, a.size)
+    dx = np.empty(g2.shape, np.float64)
+    da = np.empty(a.size, np.float64)
+    _check(lib.lo_sym_backward(_ptr(a, ctypes.c_float), a.size, x2.shape[1], _ptr(x2, ctypes.c_float),
+                               _ptr(g2, ctypes.c_float), _ptr(dx, ctypes.c_double), _ptr(da, ctypes.c_double)))
+    return dx, da
+
+
+def general_backward(a, b, x, g, lib=None):
+    """Backward of y = K(a, b) x (n x k operator) for g = dL/dy (float64):
+    returns (dx = K^T g, k x m; da, n; db, k)."""
+    lib = lib or load()
+    a, b = _f32(a).ravel(), _f32(b).ravel()
+    x2, g2 = _as2d(x, b.size), _as2d(g, a.size)
+    m = x2.shape[1]
+    dx = np.zeros((b.size, m), np.float64)
+    da = np.empty(a.size, np.float64)
+    db = np.empty(b.size, np.float64)
+    _check(lib.lo_general_backward(_ptr(a, ctypes.c_float), a.size, _ptr(b, ctypes.c_float), b.size, m,
+                                   _ptr(x2, ctypes.c_float), _ptr(g2, ctypes.c_float), _ptr(dx, ctypes.c_double),
+                                   _ptr(da, ctypes.c_double), _ptr(db, ctypes.c_double)))
+    return dx, da, db
 
 
 def general_apply(a, b, x, lib=None) -> np.ndarray:
@@ -169,4 +201,4 @@ def dense_rows_c(rows, a, x, b=None, phi=None, psi=None, lib=None):
     return y, env
 
 
-from .dense import dense_apply, dense_envelope, dense_rows, normwise_error  # noqa: E402,F401
+from .dense import dense_apply, dense_backward, dense_envelope, dense_rows, normwise_error  # noqa: E402,F401

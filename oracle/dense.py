@@ -99,3 +99,27 @@ def normwise_error(y, y_ref, env, env_scale: Optional[np.ndarray] = None) -> flo
         den = np.asarray(env_scale, np.float64).ravel()
     den = np.where(den > 0, den, 1.0)
     return float(np.max(num / den)) if num.size else 0.0
+
+
+def dense_backward(a, x, g, b=None):
+    """Backward of y = LAPLEX(a, b) x by the plain definition (float64), for an
+    upstream gradient g = dL/dy.  With K_ij = exp(-|a_i - b_j|) and
+    dK_ij/da_i = -sign(a_i - b_j) K_ij = -dK_ij/db_j (sign(0) = 0):
+        dx = K^T g,   da_i = -sum_jc sign(a_i - b_j) K_ij g_ic x_jc,
+        db_j = +sum_ic sign(a_i - b_j) K_ij g_ic x_jc.
+    Symmetric (b None): one anchor set receives both terms; returns (dx, da).
+    General: returns (dx, da, db)."""
+    a = np.asarray(a, np.float64).ravel()
+    sym = b is None
+    b = a if sym else np.asarray(b, np.float64).ravel()
+    x2 = np.asarray(x, np.float64).reshape(b.size, -1)
+    g2 = np.asarray(g, np.float64).reshape(a.size, -1)
+    D = a[:, None] - b[None, :]
+    K = np.exp(-np.abs(D))
+    SK = np.sign(D) * K
+    dx = K.T @ g2
+    da = -np.einsum("ij,ic,jc->i", SK, g2, x2)
+    db = np.einsum("ij,ic,jc->j", SK, g2, x2)
+    if sym:
+        return dx, da + db
+    return dx, da, db

@@ -337,3 +337,134 @@ int lo_dense_rows(const float* a, const float* phi, const int64_t* rows, int64_t
   free(pi);
   return 0;
 }
+
+/* ------------------------------------------------------------------ backward
+ * The operator is differentiable in its anchors (technical summary, section
+ * 2.3, expressivity and limits: the relation to the FFT keeps exactness and
+ * differentiability with respect to the anchors).  With y = K x and an upstream gradient g = dL/dy, the chain rule
+ * on K_ij = exp(-|a_i - b_j|) gives
+ *     dL/dx   = K^T g
+ *     dL/da_i = - sum_c g_ic  S_{b,x_c}(a_i),   S_{s,v}(t) = sum_j sign(t - s_j) exp(-|t - s_j|) v_j
+ *     dL/db_j = - sum_c x_jc  S_{a,g_c}(b_j)
+ * and in the symmetric case (b = a, one anchor set) both terms land on a:
+ *     dL/da_i = - sum_c [ g_ic S_{a,x_c}(a_i) + x_ic S_{a,g_c}(a_i) ].
+ * sign(0) = 0: equal anchors contribute nothing, the value a central
+ * difference gives at a tie (|t| has a kink there).
+ *
+ * S is evaluated from the sorted sources: with the stable prefix and suffix
+ * scans  P_t = sum_{j<=t} exp(s_j - s_t) v_j  and  Q_t = sum_{j>=t} exp(s_t - s_j) v_j,
+ *     S(t) = exp(s_{p-1} - t) P_{p-1} - exp(t - s_q) Q_q,
+ * p = #{s_j < t} (lower bound), q = #{s_j <= t} (upper bound); every factor
+ * is a single exp of a non-positive difference. */
+
+/* number of sorted anchors <= v */
+static int64_t upper_bound_d(const double* as, int64_t n, double v) {
+  int64_t lo = 0, hi = n;
+  while (lo < hi) {
+    int64_t mid = lo + (hi - lo) / 2;
+    if (as[mid] <= v)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+/* out[e*m + c] = S_{s, v_c}(t_e) for sources s (ns, unsorted) with values v
+ * (ns x m, row-major) and evaluation points t (ne). */
+static int signed_sums(const float* s, int64_t ns, const float* v, int64_t m, const float* t, int64_t ne, double* out) {
+  if (ne <= 0 || m <= 0) return 0;
+  if (ns <= 0) {
+    memset(out, 0, sizeof(double) * (size_t)ne * (size_t)m);
+    return 0;
+  }
+  uint32_t* ps = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)ns);
+  double* ss = (double*)malloc(sizeof(double) * (size_t)ns);
+  double* P = (double*)malloc(sizeof(double) * (size_t)ns * (size_t)m);
+  double* Q = (double*)malloc(sizeof(double) * (size_t)ns * (size_t)m);
+  int rc = (ps && ss && P && Q) ? 0 : -2;
+  if (rc == 0) rc = lo_stable_argsort(s, ns, ps);
+  if (rc == 0) {
+    for (int64_t j = 0; j < ns; ++j) ss[j] = (double)s[ps[j]];
+    for (int64_t c = 0; c < m; ++c) P[c] = (double)v[(size_t)ps[0] * m + c];
+    for (int64_t j = 1; j < ns; ++j) {
+      const double d = exp(ss[j - 1] - ss[j]);
+      for (int64_t c = 0; c < m; ++c) P[j * m + c] = (double)v[(size_t)ps[j] * m + c] + d * P[(j - 1) * m + c];
+    }
+    for (int64_t c = 0; c < m; ++c) Q[(ns - 1) * m + c] = (double)v[(size_t)ps[ns - 1] * m + c];
+    for (int64_t j = ns - 2; j >= 0; --j) {
+      const double d = exp(ss[j] - ss[j + 1]);
+      for (int64_t c = 0; c < m; ++c) Q[j * m + c] = (double)v[(size_t)ps[j] * m + c] + d * Q[(j + 1) * m + c];
+    }
+    for (int64_t e = 0; e < ne; ++e) {
+      const double te = (double)t[e];
+      const int64_t p = lower_bound_d(ss, ns, te), q = upper_bound_d(ss, ns, te);
+      const double wl = p >= 1 ? exp(ss[p - 1] - te) : 0.0;
+      const double wu = q < ns ? exp(te - ss[q]) : 0.0;
+      for (int64_t c = 0; c < m; ++c) {
+        const double lo = p >= 1 ? wl * P[(p - 1) * m + c] : 0.0;
+        const double hi = q < ns ? wu * Q[q * m + c] : 0.0;
+        out[e * m + c] = lo - hi;
+      }
+    }
+  }
+  free(ps);
+  free(ss);
+  free(P);
+  free(Q);
+  return rc;
+}
+
+/* Symmetric backward: dx = K g (n x m), da (n). */
+int lo_sym_backward(const float* a, int64_t n, int64_t m, const float* x, const float* g, double* dx, double* da) {
+  if (n <= 0 || m <= 0) return 0;
+  int rc = lo_sym_apply(a, n, m, g, dx);
+  if (rc != 0) return rc;
+  double* sx = (double*)malloc(sizeof(double) * (size_t)n * (size_t)m);
+  double* sg = (double*)malloc(sizeof(double) * (size_t)n * (size_t)m);
+  rc = (sx && sg) ? 0 : -2;
+  if (rc == 0) rc = signed_sums(a, n, x, m, a, n, sx);
+  if (rc == 0) rc = signed_sums(a, n, g, m, a, n, sg);
+  if (rc == 0) {
+    for (int64_t i = 0; i < n; ++i) {
+      double acc = 0.0;
+      for (int64_t c = 0; c < m; ++c)
+        acc += (double)g[i * m + c] * sx[i * m + c] + (double)x[i * m + c] * sg[i * m + c];
+      da[i] = -acc;
+    }
+  }
+  free(sx);
+  free(sg);
+  return rc;
+}
+
+/* General backward (K is n x k, rows a, columns b): dx = K^T g (k x m),
+ * da (n), db (k). */
+int lo_general_backward(const float* a, int64_t n, const float* b, int64_t k, int64_t m, const float* x, const float* g,
+                        double* dx, double* da, double* db) {
+  if (m <= 0) return 0;
+  if (k > 0) {
+    int rc0 = lo_general_apply(b, k, a, n, m, g, dx);
+    if (rc0 != 0) return rc0;
+  }
+  double* sa = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * (size_t)m);
+  double* sb = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1) * (size_t)m);
+  int rc = (sa && sb) ? 0 : -2;
+  if (rc == 0) rc = signed_sums(b, k, x, m, a, n, sa);
+  if (rc == 0) rc = signed_sums(a, n, g, m, b, k, sb);
+  if (rc == 0) {
+    for (int64_t i = 0; i < n; ++i) {
+      double acc = 0.0;
+      for (int64_t c = 0; c < m; ++c) acc += (double)g[i * m + c] * sa[i * m + c];
+      da[i] = -acc;
+    }
+    for (int64_t j = 0; j < k; ++j) {
+      double acc = 0.0;
+      for (int64_t c = 0; c < m; ++c) acc += (double)x[j * m + c] * sb[j * m + c];
+      db[j] = -acc;
+    }
+  }
+  free(sa);
+  free(sb);
+  return rc;
+}

@@ -420,6 +420,92 @@ def pin_dense_rows_c(lib):
     _close(y, oracle.phased_apply(a, phi, x, lib=lib)[rows], 1e-12, "C rows phased sym")
 
 
+# ----------------------------------------------------------------------------- backward
+# The operator is differentiable in its anchors (section 2.3); the backward
+# formulas are the chain rule on the plain definition.  Pinned by central
+# differences of the dense forward product (itself pinned above): f(a, x) =
+# sum(g * K(a) x) has df/dx = K^T g exactly (f is linear in x) and df/da by
+# central differences, which at a tie (|t| has a kink) give the sign(0) = 0
+# value the oracle uses.
+
+def _fd_anchor_grad(f, a, h):
+    a = np.asarray(a, np.float64)
+    out = np.empty(a.size)
+    for k in range(a.size):
+        ap, am = a.copy(), a.copy()
+        ap[k] += h
+        am[k] -= h
+        out[k] = (f(ap) - f(am)) / (2.0 * h)
+    return out
+
+
+def _spread_anchors(r, n, gap):
+    """Distinct anchors at least `gap` apart (in random order)."""
+    return r.permutation(np.cumsum(r.uniform(gap, 4.0 * gap, n))).astype(np.float32)
+
+
+def pin_backward_finite_differences(lib):
+    r = _rng(61)
+    h = 1e-5
+    for ties in (False, True):
+        n, m = 26, 2
+        a = (r.integers(0, 9, n).astype(np.float32) if ties else _spread_anchors(r, n, 0.05))
+        x = r.standard_normal((n, m)).astype(np.float32)
+        g = r.standard_normal((n, m)).astype(np.float32)
+        x64, g64 = x.astype(np.float64), g.astype(np.float64)
+        fd_da = _fd_anchor_grad(lambda aa: float(np.sum(g64 * odense.dense_apply(aa, x64))), a, h)
+        dx, da = oracle.sym_backward(a, x, g, lib=lib)
+        _close(da, fd_da, 1e-7, "sym da vs central differences (ties=%s)" % ties)
+        _close(dx, odense.dense_apply(a, g64).reshape(n, m), 1e-12, "sym dx vs K g (ties=%s)" % ties)
+        dxd, dad = odense.dense_backward(a, x, g)
+        _close(dad, fd_da, 1e-7, "dense sym da vs central differences")
+        # df/dx_j = (K^T g)_j: the product is linear in x, so one difference each is exact up to rounding
+        j, c = 3, 1
+        xp, xm = x64.copy(), x64.copy()
+        xp[j, c] += 0.5
+        xm[j, c] -= 0.5
+        fdx = float(np.sum(g64 * odense.dense_apply(a, xp))) - float(np.sum(g64 * odense.dense_apply(a, xm)))
+        _close([dx[j, c]], [fdx], 1e-10, "sym dx vs difference in x")
+        # general: K is n x k over rows a and columns b (shared grid: a/b ties)
+        k = 19
+        b = (r.integers(0, 9, k).astype(np.float32) if ties else _spread_anchors(r, k, 0.05) + np.float32(0.013))
+        xb = r.standard_normal((k, m)).astype(np.float32)
+        xb64 = xb.astype(np.float64)
+        fd_da = _fd_anchor_grad(lambda aa: float(np.sum(g64 * odense.dense_apply(aa, xb64, b=b))), a, h)
+        fd_db = _fd_anchor_grad(lambda bb: float(np.sum(g64 * odense.dense_apply(a, xb64, b=bb))), b, h)
+        dxg, dag, dbg = oracle.general_backward(a, b, xb, g, lib=lib)
+        _close(dag, fd_da, 1e-7, "general da vs central differences (ties=%s)" % ties)
+        _close(dbg, fd_db, 1e-7, "general db vs central differences (ties=%s)" % ties)
+        _close(dxg, odense.dense_apply(b, g64, b=a).reshape(k, m), 1e-12, "general dx vs K^T g")
+        _, dad2, dbd2 = odense.dense_backward(a, xb, g, b=b)
+        _close(dad2, fd_da, 1e-7, "dense general da vs central differences")
+        _close(dbd2, fd_db, 1e-7, "dense general db vs central differences")
+
+
+def pin_backward_brute_force(lib):
+    """The scan-and-search backward against the dense definition at sizes the
+    difference pin does not reach (several hundred anchors, ties, m = 3)."""
+    r = _rng(62)
+    for ties in (False, True):
+        n, k, m = 700, 450, 3
+        a = r.uniform(0, 90, n).astype(np.float32)
+        b = r.uniform(0, 90, k).astype(np.float32)
+        if ties:
+            a, b = np.round(a), np.round(b)
+        x = r.standard_normal((n, m)).astype(np.float32)
+        xb = r.standard_normal((k, m)).astype(np.float32)
+        g = r.standard_normal((n, m)).astype(np.float32)
+        dx, da = oracle.sym_backward(a, x, g, lib=lib)
+        dxd, dad = odense.dense_backward(a, x, g)
+        _close(dx, dxd, 1e-12, "sym dx brute force")
+        _close(da, dad, 1e-12, "sym da brute force")
+        dx, da, db = oracle.general_backward(a, b, xb, g, lib=lib)
+        dxd, dad, dbd = odense.dense_backward(a, xb, g, b=b)
+        _close(dx, dxd, 1e-12, "general dx brute force")
+        _close(da, dad, 1e-12, "general da brute force")
+        _close(db, dbd, 1e-12, "general db brute force")
+
+
 ALL_PINS = [
     pin_sort_definition,
     pin_sort_rejects_nonfinite,
@@ -436,4 +522,6 @@ ALL_PINS = [
     pin_phased,
     pin_brute_force_tiny,
     pin_dense_rows_c,
+    pin_backward_finite_differences,
+    pin_backward_brute_force,
 ]

@@ -43,6 +43,16 @@ C_MUTANTS = [
     ("rows_cutoff_too_small", "if (d >= 746.0) continue;", "if (d >= 7.0) continue;", 0),
     ("rows_phase_sign", "cos(pi[r] - (double)psi[j])", "cos(pi[r] + (double)psi[j])", 0),
     ("rows_envelope_signed", "env[r * m + c] += w * fabs((double)xr[c]);", "env[r * m + c] += w * (double)xr[c];", 0),
+    ("bwd_signed_sum_sign", "out[e * m + c] = lo - hi;", "out[e * m + c] = hi - lo;", 0),
+    ("bwd_ties_counted_above", "q = upper_bound_d(ss, ns, te);", "q = lower_bound_d(ss, ns, te);", 0),
+    ("bwd_ties_counted_below", "const int64_t p = lower_bound_d(ss, ns, te)", "const int64_t p = upper_bound_d(ss, ns, te)", 0),
+    ("bwd_prefix_decay_sign", "const double d = exp(ss[j - 1] - ss[j]);", "const double d = exp(ss[j] - ss[j - 1]);", 0),
+    ("bwd_left_weight_sign", "const double wl = p >= 1 ? exp(ss[p - 1] - te) : 0.0;", "const double wl = p >= 1 ? exp(te - ss[p - 1]) : 0.0;", 0),
+    ("bwd_sym_da_sign", "da[i] = -acc;", "da[i] = acc;", 0),
+    ("bwd_sym_second_term_dropped", "acc += (double)g[i * m + c] * sx[i * m + c] + (double)x[i * m + c] * sg[i * m + c];",
+     "acc += (double)g[i * m + c] * sx[i * m + c];", 0),
+    ("bwd_general_db_sign", "db[j] = -acc;", "db[j] = acc;", 0),
+    ("bwd_general_da_unweighted", "acc += (double)g[i * m + c] * sa[i * m + c];", "acc += sa[i * m + c];", 0),
 ]
 
 
