@@ -69,8 +69,9 @@ def load(path: Optional[str] = None):
                                       f64p]
         lib.lo_sym_backward.argtypes = [f32p, i64, i64, f32p, f32p, f64p, f64p]
         lib.lo_general_backward.argtypes = [f32p, i64, f32p, i64, i64, f32p, f32p, f64p, f64p, f64p]
+        lib.lo_backward_rows.argtypes = [f32p, i64, i64, f32p, f32p, ctypes.POINTER(ctypes.c_int64), i64, f64p, f64p]
         for fn in (lib.lo_stable_argsort, lib.lo_sym_apply, lib.lo_general_apply, lib.lo_phased_apply, lib.lo_dense_rows,
-                   lib.lo_sym_backward, lib.lo_general_backward):
+                   lib.lo_sym_backward, lib.lo_general_backward, lib.lo_backward_rows):
             fn.restype = ctypes.c_int
         if path is None:
             _lib_handle = lib
@@ -129,6 +130,24 @@ def sym_backward(a, x, g, lib=None):
     _check(lib.lo_sym_backward(_ptr(a, ctypes.c_float), a.size, x2.shape[1], _ptr(x2, ctypes.c_float),
                                _ptr(g2, ctypes.c_float), _ptr(dx, ctypes.c_double), _ptr(da, ctypes.c_double)))
     return dx, da
+
+
+def backward_rows(rows, a, x, g, lib=None):
+    """Symmetric anchor gradient da and its envelope at selected rows, by the
+    plain definition (O(n) per row)."""
+    lib = lib or load()
+    a = _f32(a).ravel()
+    x2, g2 = _as2d(x, a.size), _as2d(g, a.size)
+    rows = np.ascontiguousarray(rows, np.int64)
+    da = np.empty(rows.size, np.float64)
+    env = np.empty(rows.size, np.float64)
+    rc = lib.lo_backward_rows(_ptr(a, ctypes.c_float), a.size, x2.shape[1], _ptr(x2, ctypes.c_float), _ptr(g2, ctypes.c_float),
+                              rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), rows.size, _ptr(da, ctypes.c_double),
+                              _ptr(env, ctypes.c_double))
+    if rc == -3:
+        raise IndexError("row out of range")
+    _check(rc)
+    return da, env
 
 
 def general_backward(a, b, x, g, lib=None):

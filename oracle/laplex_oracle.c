@@ -468,3 +468,34 @@ int lo_general_backward(const float* a, int64_t n, const float* b, int64_t k, in
   free(sb);
   return rc;
 }
+
+/* Anchor gradient of the symmetric backward at selected rows, by the plain
+ * definition (no sort), and its envelope
+ *     env_r = sum_c sum_j exp(-|a_i - a_j|) (|g_ic| |x_jc| + |x_ic| |g_jc|),   i = rows[r],
+ * for sizes where only spot rows can be checked.  Terms with |a_i - a_j| >= 746
+ * are skipped (exp underflows to 0 in float64). */
+int lo_backward_rows(const float* a, int64_t n, int64_t m, const float* x, const float* g, const int64_t* rows, int64_t nrows,
+                     double* da, double* env) {
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t i = rows[r];
+    if (i < 0 || i >= n) return -3;
+    const double ai = (double)a[i];
+    double acc = 0.0, e = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+      const double d = ai - (double)a[j];
+      const double ad = fabs(d);
+      if (ad >= 746.0) continue;
+      const double w = exp(-ad);
+      const double sg = d > 0.0 ? 1.0 : (d < 0.0 ? -1.0 : 0.0);
+      for (int64_t c = 0; c < m; ++c) {
+        const double gi = (double)g[i * m + c], xi = (double)x[i * m + c];
+        const double xj = (double)x[j * m + c], gj = (double)g[j * m + c];
+        acc += sg * w * (gi * xj + xi * gj);
+        e += w * (fabs(gi) * fabs(xj) + fabs(xi) * fabs(gj));
+      }
+    }
+    da[r] = -acc;
+    env[r] = e;
+  }
+  return 0;
+}

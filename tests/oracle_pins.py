@@ -499,6 +499,11 @@ def pin_backward_brute_force(lib):
         dxd, dad = odense.dense_backward(a, x, g)
         _close(dx, dxd, 1e-12, "sym dx brute force")
         _close(da, dad, 1e-12, "sym da brute force")
+        rows = np.array([0, 1, 77, n // 2, n - 1], np.int64)
+        dar, envr = oracle.backward_rows(rows, a, x, g, lib=lib)
+        _close(dar, dad[rows], 1e-12, "sym da at rows vs brute force")
+        envd = (np.abs(g) * odense.dense_apply(a, np.abs(x)) + np.abs(x) * odense.dense_apply(a, np.abs(g))).sum(1)
+        _close(envr, envd[rows], 1e-12, "sym da envelope at rows")
         dx, da, db = oracle.general_backward(a, b, xb, g, lib=lib)
         dxd, dad, dbd = odense.dense_backward(a, xb, g, b=b)
         _close(dx, dxd, 1e-12, "general dx brute force")

@@ -53,6 +53,8 @@ C_MUTANTS = [
      "acc += (double)g[i * m + c] * sx[i * m + c];", 0),
     ("bwd_general_db_sign", "db[j] = -acc;", "db[j] = acc;", 0),
     ("bwd_general_da_unweighted", "acc += (double)g[i * m + c] * sa[i * m + c];", "acc += sa[i * m + c];", 0),
+    ("bwd_rows_tie_sign", "const double sg = d > 0.0 ? 1.0 : (d < 0.0 ? -1.0 : 0.0);", "const double sg = d >= 0.0 ? 1.0 : -1.0;", 0),
+    ("bwd_rows_one_term", "acc += sg * w * (gi * xj + xi * gj);", "acc += sg * w * (gi * xj);", 0),
 ]
 
 
