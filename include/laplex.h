@@ -59,7 +59,8 @@ enum {
   LAPLEX_OP_SYM = 1,
   LAPLEX_OP_GENERAL = 2,
   LAPLEX_OP_PHASED = 3,         /* symmetric phased operator (b = a, psi = phi) */
-  LAPLEX_OP_PHASED_GENERAL = 4  /* phased operator with a != b */
+  LAPLEX_OP_PHASED_GENERAL = 4, /* phased operator with a != b */
+  LAPLEX_OP_SYM_BACKWARD = 5    /* backward of the symmetric operator */
 };
 
 /* Bytes of workspace one call of `op` needs for n output anchors, k input
@@ -126,6 +127,24 @@ laplex_status laplex_matvec_phased(const float* a_sorted, const uint32_t* perm_a
                                    uint64_t n, const float* b_sorted, const uint32_t* perm_b, const void* route_b,
                                    const float* psi, uint64_t k, uint32_t m, const float* x, float* y, void* ws, size_t ws_bytes,
                                    hipStream_t stream);
+
+/* Backward of the symmetric operator y = LAPLEX(a, a) x.  The operator is
+ * differentiable in its anchors (technical summary, section 2.3, relation to
+ * the FFT); for an upstream gradient g = dL/dy the chain rule on
+ * exp(-|a_i - a_j|) gives
+ *     dx   = LAPLEX(a, a) g                                        (n x m)
+ *     da_i = - sum_c [ g_ic S(x_c)_i + x_ic S(g_c)_i ]             (n)
+ *     S(v)_i = sum_j sign(a_i - a_j) exp(-|a_i - a_j|) v_j,  sign(0) = 0,
+ * so tied anchors contribute nothing to each other's gradient (the value a
+ * central difference gives at the kink of |t|).  S is computed with the same
+ * prefix/suffix scans, once with the kernel's decay and once summing over
+ * tied anchors only.
+ * a_sorted, perm, route: the sort handle of a (route may be NULL);
+ * x, g: n x m (inputs, original order); dx: n x m and da: n (outputs,
+ * original order); ws: laplex_workspace_bytes(LAPLEX_OP_SYM_BACKWARD, n, 0, m). */
+laplex_status laplex_backward_sym(const float* a_sorted, const uint32_t* perm, const void* route, uint64_t n, uint32_t m,
+                                  const float* x, const float* g, float* dx, float* da, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
 
 /* Short English description of a status code (static storage). */
 const char* laplex_status_string(laplex_status s);

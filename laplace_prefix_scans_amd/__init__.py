@@ -9,6 +9,7 @@ not been built the calls raise -- there is no fallback.
     y = laplex_matvec_sym(a_sorted, perm, x)         # y_i = sum_j exp(-|a_i - a_j|) x_j
     y = laplex_matvec_general(a_sorted, perm, b_sorted, perm_b, xb)
     y = laplex_matvec_phased(a_sorted, perm, phi, x)  # extra cos(phi_i - phi_j)
+    dx, da = laplex_backward_sym(a_sorted, perm, x, g)  # gradients for g = dL/dy
 """
 from ._binding import (  # noqa: F401
     LAPLEX_OP_GENERAL,
@@ -16,9 +17,11 @@ from ._binding import (  # noqa: F401
     LAPLEX_OP_PHASED_GENERAL,
     LAPLEX_OP_SORT,
     LAPLEX_OP_SYM,
+    LAPLEX_OP_SYM_BACKWARD,
     LaplexError,
     lib,
     lib_path,
+    laplex_backward_sym,
     laplex_matvec_general,
     laplex_matvec_phased,
     laplex_matvec_sym,

@@ -12,6 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblaplex.so")
 
 LAPLEX_OP_SORT, LAPLEX_OP_SYM, LAPLEX_OP_GENERAL, LAPLEX_OP_PHASED, LAPLEX_OP_PHASED_GENERAL = 0, 1, 2, 3, 4
+LAPLEX_OP_SYM_BACKWARD = 5
 
 _STATUS = {
     0: "LAPLEX_OK", 1: "LAPLEX_ERR_NULL", 2: "LAPLEX_ERR_SIZE", 3: "LAPLEX_ERR_ALIGN", 4: "LAPLEX_ERR_WORKSPACE",
@@ -52,6 +53,8 @@ def lib():
         L.laplex_matvec_sym.argtypes = [vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
         L.laplex_matvec_general.argtypes = [vp, vp, vp, u64, vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
         L.laplex_matvec_phased.argtypes = [vp, vp, vp, vp, u64, vp, vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
+        L.laplex_backward_sym.argtypes = [vp, vp, vp, u64, u32, vp, vp, vp, vp, vp, sz, vp]
+        L.laplex_backward_sym.restype = i32
         for f in (L.laplex_sort_anchors, L.laplex_status_poll, L.laplex_matvec_sym, L.laplex_matvec_general,
                   L.laplex_matvec_phased):
             f.restype = i32
@@ -174,6 +177,26 @@ def laplex_matvec_sym(a_sorted: torch.Tensor, perm: torch.Tensor, x: torch.Tenso
     _check(lib().laplex_matvec_sym(_ptr(a_sorted), _ptr(perm), _ptr(route), n, m, _ptr(x), _ptr(y), _ptr(ws), ws.numel(),
                                    _stream(dev)), "laplex_matvec_sym")
     return y
+
+
+def laplex_backward_sym(a_sorted: torch.Tensor, perm: torch.Tensor, x: torch.Tensor, g: torch.Tensor,
+                        dx: Optional[torch.Tensor] = None, da: Optional[torch.Tensor] = None,
+                        ws: Optional[torch.Tensor] = None, route: Optional[torch.Tensor] = None):
+    """Backward of y = LAPLEX(a, a) x for the upstream gradient g = dL/dy:
+    returns (dx = K g, same shape as x; da, (n,))."""
+    _vec(a_sorted, "a_sorted")
+    _vec(perm, "perm", torch.uint32)
+    n, dev = a_sorted.shape[0], a_sorted.device
+    m = _cols(x, n)
+    if _cols(g, n, "g") != m:
+        raise ValueError("g must have the shape of x")
+    dx = torch.empty_like(g) if dx is None else dx
+    _cols(dx, n, "dx")
+    da = torch.empty(n, dtype=torch.float32, device=dev) if da is None else _vec(da, "da")
+    ws = _ws(ws, LAPLEX_OP_SYM_BACKWARD, n, 0, m, dev)
+    _check(lib().laplex_backward_sym(_ptr(a_sorted), _ptr(perm), _ptr(route), n, m, _ptr(x), _ptr(g), _ptr(dx), _ptr(da),
+                                     _ptr(ws), ws.numel(), _stream(dev)), "laplex_backward_sym")
+    return dx, da
 
 
 def laplex_matvec_general(a_sorted: torch.Tensor, perm_a: torch.Tensor, b_sorted: torch.Tensor, perm_b: torch.Tensor,

@@ -83,6 +83,35 @@ ApplyWorkspace carve_apply(void* ws, uint64_t rows_in, uint64_t rows_out, uint64
   return w;
 }
 
+BackwardWorkspace carve_backward(void* ws, uint64_t n, uint32_t m, size_t* total) {
+  Carver c(ws);
+  BackwardWorkspace bw{};
+  ApplyWorkspace& w = bw.w;
+  const uint64_t T = backward_tiles(n, m);
+  const uint64_t M = 4ull * m;
+  w.xs = c.take<float>(n * m * 4);
+  bw.gs = c.take<float>(n * m * 4);
+  w.zs = c.take<float>(n * m * 4);
+  bw.das = c.take<float>(n * 4);
+  w.bf = c.take<float>(T * M * 4);
+  w.bb = c.take<float>(T * M * 4);
+  w.cf = c.take<float>(T * M * 4);
+  w.cb = c.take<float>(T * M * 4);
+  w.tanch = c.take<float2>(T * 8);
+  const uint64_t G = (T + 1023) / 1024;
+  w.gbf = c.take<float>(G * M * 4);
+  w.gbb = c.take<float>(G * M * 4);
+  w.gcf = c.take<float>(G * M * 4);
+  w.gcb = c.take<float>(G * M * 4);
+  w.ganch = c.take<float2>(G * 8);
+  if (m <= kRouteMaxCols) {
+    w.t0 = c.take<float>(n * m * 4);
+    w.t1 = c.take<float>(n * m * 4);
+  }
+  if (total) *total = (c.off + 255) & ~size_t(255);
+  return bw;
+}
+
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
 bool overlaps(const void* p, size_t pb, const void* q, size_t qb) {
@@ -106,6 +135,7 @@ extern "C" size_t laplex_workspace_bytes(int op, uint64_t n, uint64_t k, uint32_
     case LAPLEX_OP_PHASED: carve_apply(nullptr, n, n, n, m, Variant::Phased, false, &total); return total;
     case LAPLEX_OP_GENERAL: carve_apply(nullptr, k, n, n + k, m, Variant::Sym, true, &total); return total;
     case LAPLEX_OP_PHASED_GENERAL: carve_apply(nullptr, k, n, n + k, m, Variant::Phased, true, &total); return total;
+    case LAPLEX_OP_SYM_BACKWARD: carve_backward(nullptr, n, m, &total); return total;
     default: return 0;
   }
 }
@@ -176,6 +206,31 @@ extern "C" laplex_status laplex_matvec_sym(const float* a_sorted, const uint32_t
   SortRoute r{};
   if (route) r = carve_route(route, n);
   return from_hip(apply_sym(w, Variant::Sym, a_sorted, perm, route ? &r : nullptr, nullptr, n, m, x, y, stream));
+}
+
+extern "C" laplex_status laplex_backward_sym(const float* a_sorted, const uint32_t* perm, const void* route, uint64_t n,
+                                             uint32_t m, const float* x, const float* g, float* dx, float* da, void* ws,
+                                             size_t ws_bytes, hipStream_t stream) {
+  if (n == 0 || m == 0) return LAPLEX_OK;
+  laplex_status st = check_apply_common(a_sorted, perm, n, m, x, dx, ws);
+  if (st != LAPLEX_OK) return st;
+  if (!g || !da) return LAPLEX_ERR_NULL;
+  if (misaligned(g, 4) || misaligned(da, 4) || (route && misaligned(route, 256))) return LAPLEX_ERR_ALIGN;
+  size_t need = 0;
+  carve_backward(nullptr, n, m, &need);
+  if (ws_bytes < need) return LAPLEX_ERR_WORKSPACE;
+  const size_t xb = n * (size_t)m * 4, vb = n * 4, rb = route ? route_bytes(n) : 0;
+  for (const void* out : {static_cast<const void*>(dx), static_cast<const void*>(da)}) {
+    const size_t ob = out == dx ? xb : vb;
+    if (overlaps(out, ob, x, xb) || overlaps(out, ob, g, xb) || overlaps(out, ob, a_sorted, vb) || overlaps(out, ob, perm, vb) ||
+        overlaps(out, ob, ws, ws_bytes) || overlaps(out, ob, route, rb))
+      return LAPLEX_ERR_OVERLAP;
+  }
+  if (overlaps(dx, xb, da, vb)) return LAPLEX_ERR_OVERLAP;
+  const BackwardWorkspace bw = carve_backward(ws, n, m, nullptr);
+  SortRoute r{};
+  if (route) r = carve_route(route, n);
+  return from_hip(backward_sym(bw, a_sorted, perm, route ? &r : nullptr, n, m, x, g, dx, da, stream));
 }
 
 extern "C" laplex_status laplex_matvec_general(const float* a_sorted, const uint32_t* perm_a, const void* route_a, uint64_t n,

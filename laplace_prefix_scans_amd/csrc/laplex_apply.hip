@@ -54,15 +54,17 @@ __device__ __forceinline__ void block_sum2(float (&a)[CC], float (&b)[CC], float
 // In: v[e][j] injections of this thread's E consecutive elements (anchors
 // ae[], nondecreasing across the whole tile); carries into the tile from the
 // left (cf, anchored at sf) and right (cb, anchored at sb).
-// Out: v[e][j] = strict forward value + inclusive backward value.
-template <int E, int CC, int NW>
-__device__ __forceinline__ void tile_scan(const float (&ae)[E], float (&v)[E][CC], const float (&cf)[CC], float sf,
-                                          const float (&cb)[CC], float sb, float* s_wf, float* s_wfs, float* s_wb,
-                                          float* s_wbs) {
+// Out: F[e][j] the strict forward value (earlier elements only, tied ones
+// included), U[e][j] the inclusive backward value.  TIE selects the decay
+// (see decay_m).
+template <int E, int CC, int NW, bool TIE>
+__device__ __forceinline__ void tile_scan_fu(const float (&ae)[E], const float (&v)[E][CC], const float (&cf)[CC],
+                                             float sf, const float (&cb)[CC], float sb, float* s_wf, float* s_wfs,
+                                             float* s_wb, float* s_wbs, float (&F)[E][CC], float (&Uo)[E][CC]) {
   const int lane = lane_id(), wid = threadIdx.x / kWave;
   float d[E];  // d[e] = exp(ae[e-1] - ae[e]) for e >= 1
 #pragma unroll
-  for (int e = 1; e < E; ++e) d[e] = decay(ae[e - 1] - ae[e]);
+  for (int e = 1; e < E; ++e) d[e] = decay_m<TIE>(ae[e - 1] - ae[e]);
 
   // thread-local aggregates
   float B[CC], D[CC];
@@ -81,8 +83,8 @@ __device__ __forceinline__ void tile_scan(const float (&ae)[E], float (&v)[E][CC
     for (int j = 0; j < CC; ++j) D[j] = fmaf(d[e + 1], D[j], v[e][j]);
 
   // wave scans (forward: by last anchor; backward: by first anchor)
-  wave_scan_fwd<CC>(B, ae[E - 1]);
-  wave_scan_bwd<CC>(D, ae[0]);
+  wave_scan_fwd<CC, TIE>(B, ae[E - 1]);
+  wave_scan_bwd<CC, TIE>(D, ae[0]);
   if (lane == kWave - 1) {
 #pragma unroll
     for (int j = 0; j < CC; ++j) s_wf[wid * CC + j] = B[j];
@@ -117,8 +119,8 @@ __device__ __forceinline__ void tile_scan(const float (&ae)[E], float (&v)[E][CC
   {
     const bool fw = lane < wid, bw = lane > wid && lane < NW;
     const int lf = fw ? lane : 0, lb = bw ? lane : 0;
-    const float gf = fw ? decay(s_wfs[lf] - sw) : (lane == kWave - 1 ? decay(sf - sw) : 0.f);
-    const float gb = bw ? decay(sz2 - s_wbs[lb]) : (lane == kWave - 1 ? decay(sz2 - sb) : 0.f);
+    const float gf = fw ? decay_m<TIE>(s_wfs[lf] - sw) : (lane == kWave - 1 ? decay_m<TIE>(sf - sw) : 0.f);
+    const float gb = bw ? decay_m<TIE>(sz2 - s_wbs[lb]) : (lane == kWave - 1 ? decay_m<TIE>(sz2 - sb) : 0.f);
 #pragma unroll
     for (int j = 0; j < CC; ++j) {
       cw[j] = fw ? gf * s_wf[lf * CC + j] : (lane == kWave - 1 ? gf * cf[j] : 0.f);
@@ -129,21 +131,20 @@ __device__ __forceinline__ void tile_scan(const float (&ae)[E], float (&v)[E][CC
   }
   float swl = sw, szl = sz2;
   if (lane > 0) {
-    const float g = decay(swl - sx);
+    const float g = decay_m<TIE>(swl - sx);
 #pragma unroll
     for (int j = 0; j < CC; ++j) cw[j] = fmaf(g, cw[j], X[j]);
     swl = sx;
   }
   if (lane < kWave - 1) {
-    const float g = decay(sz - szl);
+    const float g = decay_m<TIE>(sz - szl);
 #pragma unroll
     for (int j = 0; j < CC; ++j) cz[j] = fmaf(g, cz[j], Z[j]);
     szl = sz;
   }
 
   // full forward pass: strict lower part of each element
-  const float d0 = decay(swl - ae[0]);
-  float F[E][CC];
+  const float d0 = decay_m<TIE>(swl - ae[0]);
 #pragma unroll
   for (int j = 0; j < CC; ++j) {
     float L = cw[j];
@@ -154,16 +155,30 @@ __device__ __forceinline__ void tile_scan(const float (&ae)[E], float (&v)[E][CC
     }
   }
   // full backward pass, combined
-  const float dl = decay(ae[E - 1] - szl);
+  const float dl = decay_m<TIE>(ae[E - 1] - szl);
 #pragma unroll
   for (int j = 0; j < CC; ++j) {
     float U = cz[j];
 #pragma unroll
     for (int e = E - 1; e >= 0; --e) {
       U = fmaf(e == E - 1 ? dl : d[e + 1], U, v[e][j]);
-      v[e][j] = F[e][j] + U;
+      Uo[e][j] = U;
     }
   }
+}
+
+// The operator's tile scan: v[e][j] becomes strict forward + inclusive
+// backward, i.e. lower + upper - diagonal.
+template <int E, int CC, int NW>
+__device__ __forceinline__ void tile_scan(const float (&ae)[E], float (&v)[E][CC], const float (&cf)[CC], float sf,
+                                          const float (&cb)[CC], float sb, float* s_wf, float* s_wfs, float* s_wb,
+                                          float* s_wbs) {
+  float F[E][CC], U[E][CC];
+  tile_scan_fu<E, CC, NW, false>(ae, v, cf, sf, cb, sb, s_wf, s_wfs, s_wb, s_wbs, F, U);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+#pragma unroll
+    for (int j = 0; j < CC; ++j) v[e][j] = F[e][j] + U[e][j];
 }
 
 // ---------------------------------------------------------------- carries
@@ -179,9 +194,10 @@ constexpr int kCarryBatch = 8;
 // loads of each batch of tiles issued before its dependent chain.
 __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restrict__ bf, const float* __restrict__ bb,
                                                             const float2* __restrict__ tanch, uint64_t T, uint32_t M,
-                                                            float* __restrict__ cf, float* __restrict__ cb) {
+                                                            uint32_t tie_from, float* __restrict__ cf, float* __restrict__ cb) {
   __shared__ float sB[kCarryBlock], sS[kCarryBlock];
   const uint32_t c = blockIdx.x;
+  const bool tie = c >= tie_from;  // columns from tie_from on scan with the tie decay
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
   const uint64_t q = (T + kCarryBlock - 1) / kCarryBlock;
   const uint64_t t0 = std::min<uint64_t>(T, (uint64_t)tid * q), t1 = std::min<uint64_t>(T, t0 + q);
@@ -192,7 +208,7 @@ __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restr
   if (t0 < t1) {
     s = tanch[t1 - 1].y;
 #pragma unroll 8
-    for (uint64_t t = t0; t < t1; ++t) B = fmaf(decay(tanch[t].y - s), bf[t * M + c], B);
+    for (uint64_t t = t0; t < t1; ++t) B = fmaf(decay_r(tanch[t].y - s, tie), bf[t * M + c], B);
   }
   sB[tid] = B;
   sS[tid] = s;
@@ -203,8 +219,11 @@ __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restr
       const int i = r * kWave + lane;
       float b1[1] = {sB[i]};
       const float s1 = sS[i];
-      wave_scan_fwd<1>(b1, s1);
-      const float inc = fmaf(decay(cS - s1), cB, b1[0]);
+      if (tie)
+        wave_scan_fwd<1, true>(b1, s1);
+      else
+        wave_scan_fwd<1, false>(b1, s1);
+      const float inc = fmaf(decay_r(cS - s1, tie), cB, b1[0]);
       float ex = __shfl_up(inc, 1), es = __shfl_up(s1, 1);
       if (lane == 0) {
         ex = cB;
@@ -231,7 +250,7 @@ __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restr
       for (int u = 0; u < kCarryBatch; ++u) {
         if (tb + u < t1) {
           cf[(tb + u) * M + c] = C;
-          C = fmaf(decay(sc - sl[u]), C, bv[u]);
+          C = fmaf(decay_r(sc - sl[u], tie), C, bv[u]);
           sc = sl[u];
         }
       }
@@ -245,7 +264,7 @@ __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restr
   if (t0 < t1) {
     s = tanch[t0].x;
 #pragma unroll 8
-    for (uint64_t t = t0; t < t1; ++t) B = fmaf(decay(s - tanch[t].x), bb[t * M + c], B);
+    for (uint64_t t = t0; t < t1; ++t) B = fmaf(decay_r(s - tanch[t].x, tie), bb[t * M + c], B);
   }
   sB[tid] = B;
   sS[tid] = s;
@@ -256,8 +275,11 @@ __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restr
       const int i = r * kWave + lane;
       float b1[1] = {sB[i]};
       const float s1 = sS[i];
-      wave_scan_bwd<1>(b1, s1);
-      const float inc = fmaf(decay(s1 - cS), cB, b1[0]);
+      if (tie)
+        wave_scan_bwd<1, true>(b1, s1);
+      else
+        wave_scan_bwd<1, false>(b1, s1);
+      const float inc = fmaf(decay_r(s1 - cS, tie), cB, b1[0]);
       float ex = __shfl_down(inc, 1), es = __shfl_down(s1, 1);
       if (lane == kWave - 1) {
         ex = cB;
@@ -285,7 +307,7 @@ __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restr
       for (int u = kCarryBatch - 1; u >= 0; --u) {
         if (tb + u < te) {
           cb[(tb + u) * M + c] = C;
-          C = fmaf(decay(sf[u] - sc), C, bv[u]);
+          C = fmaf(decay_r(sf[u] - sc, tie), C, bv[u]);
           sc = sf[u];
         }
       }
@@ -303,12 +325,13 @@ constexpr int kCarryGroup = 1024;
 
 __global__ __launch_bounds__(kCarryGroup) void k_carry_up(const float* __restrict__ bf, const float* __restrict__ bb,
                                                           const float2* __restrict__ tanch, uint64_t T, uint32_t M,
-                                                          float* __restrict__ gbf, float* __restrict__ gbb,
+                                                          uint32_t tie_from, float* __restrict__ gbf, float* __restrict__ gbb,
                                                           float2* __restrict__ ganch) {
   constexpr int NW = kCarryGroup / kWave;
   __shared__ float s_red[2 * NW];
   const uint64_t g = blockIdx.x;
   const uint32_t c = blockIdx.y;
+  const bool tie = c >= tie_from;
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
   const uint64_t t0 = g * kCarryGroup, t1 = std::min<uint64_t>(T, t0 + kCarryGroup);
   const uint64_t t = t0 + tid;
@@ -316,8 +339,8 @@ __global__ __launch_bounds__(kCarryGroup) void k_carry_up(const float* __restric
   float vf[1] = {0.f}, vb[1] = {0.f};
   if (t < t1) {
     const float2 ta = tanch[t];
-    vf[0] = decay(ta.y - s_last) * bf[t * M + c];
-    vb[0] = decay(s_first - ta.x) * bb[t * M + c];
+    vf[0] = decay_r(ta.y - s_last, tie) * bf[t * M + c];
+    vb[0] = decay_r(s_first - ta.x, tie) * bb[t * M + c];
   }
   wave_sum<1>(vf);
   wave_sum<1>(vb);
@@ -342,11 +365,12 @@ __global__ __launch_bounds__(kCarryGroup) void k_carry_down(const float* __restr
                                                             const float2* __restrict__ tanch, uint64_t T, uint32_t M,
                                                             const float* __restrict__ gcf, const float* __restrict__ gcb,
                                                             const float2* __restrict__ ganch, uint64_t G,
-                                                            float* __restrict__ cf, float* __restrict__ cb) {
+                                                            uint32_t tie_from, float* __restrict__ cf, float* __restrict__ cb) {
   constexpr int NW = kCarryGroup / kWave;
   __shared__ float s_f[NW], s_fs[NW], s_b[NW], s_bs[NW];
   const uint64_t g = blockIdx.x;
   const uint32_t c = blockIdx.y;
+  const bool tie = c >= tie_from;
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
   const uint64_t t0 = g * kCarryGroup, t1 = std::min<uint64_t>(T, t0 + kCarryGroup);
   const uint64_t t = t0 + tid;
@@ -356,8 +380,14 @@ __global__ __launch_bounds__(kCarryGroup) void k_carry_down(const float* __restr
   float B[1] = {valid ? bf[t * M + c] : 0.f};
   float D[1] = {valid ? bb[t * M + c] : 0.f};
   // inclusive scans within the wave (forward by last anchors, backward by first)
-  wave_scan_fwd<1>(B, ta.y);
-  wave_scan_bwd<1>(D, ta.x);
+  if (tie)
+        wave_scan_fwd<1, true>(B, ta.y);
+      else
+        wave_scan_fwd<1, false>(B, ta.y);
+  if (tie)
+        wave_scan_bwd<1, true>(D, ta.x);
+      else
+        wave_scan_bwd<1, false>(D, ta.x);
   if (lane == kWave - 1) {
     s_f[wid] = B[0];
     s_fs[wid] = ta.y;
@@ -373,22 +403,22 @@ __global__ __launch_bounds__(kCarryGroup) void k_carry_down(const float* __restr
   float C = gcf[g * M + c];
   float sc = g > 0 ? ganch[g - 1].y : ganch[0].x;
   for (int w = 0; w < wid; ++w) {
-    C = fmaf(decay(sc - s_fs[w]), C, s_f[w]);
+    C = fmaf(decay_r(sc - s_fs[w], tie), C, s_f[w]);
     sc = s_fs[w];
   }
   if (lane > 0) {
-    C = fmaf(decay(sc - sx), C, X);
+    C = fmaf(decay_r(sc - sx, tie), C, X);
     sc = sx;
   }
   // backward: group carry, later waves, then later lanes of this wave
   float Cb = gcb[g * M + c];
   float sb = g + 1 < G ? ganch[g + 1].x : ganch[G - 1].y;
   for (int w = NW - 1; w > wid; --w) {
-    Cb = fmaf(decay(s_bs[w] - sb), Cb, s_b[w]);
+    Cb = fmaf(decay_r(s_bs[w] - sb, tie), Cb, s_b[w]);
     sb = s_bs[w];
   }
   if (lane < kWave - 1) {
-    Cb = fmaf(decay(sz - sb), Cb, Z);
+    Cb = fmaf(decay_r(sz - sb, tie), Cb, Z);
     sb = sz;
   }
   if (valid) {
@@ -399,21 +429,23 @@ __global__ __launch_bounds__(kCarryGroup) void k_carry_down(const float* __restr
 
 // Carries for T tiles: one level when T is small, three levels otherwise.
 // g_* hold the group aggregates and carries (ceil(T / 1024) x M each).
+// Columns from tie_from on use the tie decay (M: no such column).
 static hipError_t tile_carries(const float* bf, const float* bb, const float2* tanch, uint64_t T, uint32_t M, float* cf,
-                               float* cb, float* gbf, float* gbb, float* gcf, float* gcb, float2* ganch, hipStream_t s) {
+                               float* cb, float* gbf, float* gbb, float* gcf, float* gcb, float2* ganch, hipStream_t s,
+                               uint32_t tie_from = ~0u) {
   if (T <= (uint64_t)kCarryGroup * 4) {
-    LAPLEX_LAUNCH("k_tile_carry", T, s, k_tile_carry<<<M, kCarryBlock, 0, s>>>(bf, bb, tanch, T, M, cf, cb));
+    LAPLEX_LAUNCH("k_tile_carry", T, s, k_tile_carry<<<M, kCarryBlock, 0, s>>>(bf, bb, tanch, T, M, tie_from, cf, cb));
     return hipGetLastError();
   }
   const uint64_t G = (T + kCarryGroup - 1) / kCarryGroup;
   const dim3 grid((unsigned)G, M);
-  LAPLEX_LAUNCH("k_carry_up", T, s, k_carry_up<<<grid, kCarryGroup, 0, s>>>(bf, bb, tanch, T, M, gbf, gbb, ganch));
+  LAPLEX_LAUNCH("k_carry_up", T, s, k_carry_up<<<grid, kCarryGroup, 0, s>>>(bf, bb, tanch, T, M, tie_from, gbf, gbb, ganch));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  LAPLEX_LAUNCH("k_tile_carry", G, s, k_tile_carry<<<M, kCarryBlock, 0, s>>>(gbf, gbb, ganch, G, M, gcf, gcb));
+  LAPLEX_LAUNCH("k_tile_carry", G, s, k_tile_carry<<<M, kCarryBlock, 0, s>>>(gbf, gbb, ganch, G, M, tie_from, gcf, gcb));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   LAPLEX_LAUNCH("k_carry_down", T, s,
-                k_carry_down<<<grid, kCarryGroup, 0, s>>>(bf, bb, tanch, T, M, gcf, gcb, ganch, G, cf, cb));
+                k_carry_down<<<grid, kCarryGroup, 0, s>>>(bf, bb, tanch, T, M, gcf, gcb, ganch, G, tie_from, cf, cb));
   return hipGetLastError();
 }
 
@@ -826,6 +858,232 @@ hipError_t apply_sym(const ApplyWorkspace& w, Variant var, const float* a_s, con
     default: LAPLEX_SYM(1);
   }
 #undef LAPLEX_SYM
+}
+
+__global__ void k_gather_rows(const float* __restrict__ x, const uint32_t* __restrict__ perm, const float* __restrict__ ph,
+                              uint64_t rows, uint32_t m, float* __restrict__ xs, float* __restrict__ phs);
+
+// ---------------------------------------------------------------- backward (symmetric)
+// With y = K x and an upstream gradient g = dL/dy (technical summary,
+// section 2.3: the operator is differentiable in its anchors), the chain rule
+// on K_ij = exp(-|a_i - a_j|) gives
+//     dx   = K g,
+//     da_i = - sum_c [ g_ic S(x_c)_i + x_ic S(g_c)_i ],
+//     S(v)_i = sum_j sign(a_i - a_j) exp(-|a_i - a_j|) v_j   (sign(0) = 0).
+// In sorted order S(v) = (F - F0) - (U - U0): F, U are the strict forward and
+// inclusive backward scans of v (tied anchors counted with weight 1), F0, U0
+// the same scans with the tie decay (sums over tied anchors only), so the
+// differences keep exactly the anchors strictly below and above.
+//
+// Summary columns (M = 4m): [0, m) x and [m, 2m) g with the kernel's decay,
+// [2m, 3m) x and [3m, 4m) g with the tie decay.
+template <int C>
+__device__ __forceinline__ uint32_t bwdcol(uint32_t m, uint32_t cc, int j) {
+  const uint32_t mode = (uint32_t)j / (2 * C), which = ((uint32_t)j / C) % 2, col = (uint32_t)j % C;
+  return mode * 2 * m + which * m + cc * C + col;
+}
+
+// Gathered inputs (or their rows moved by route) -> tile aggregates of x and g
+// under both decays, as direct weighted sums.
+template <int C>
+__global__ __launch_bounds__(apply_block(2 * C)) void k_bwd_reduce(const float* __restrict__ a_s, const float* __restrict__ xs,
+                                                                   const float* __restrict__ gs, uint64_t n, uint32_t m,
+                                                                   float* __restrict__ bf, float* __restrict__ bb,
+                                                                   float2* __restrict__ tanch, bool vec) {
+  constexpr int CC = 4 * C;
+  constexpr int E = apply_items(2 * C);
+  constexpr int BLOCK = apply_block(2 * C);
+  constexpr int NW = BLOCK / kWave;
+  constexpr int P = BLOCK * E;
+  __shared__ float s_red[2 * NW * CC];
+  const uint32_t M = 4 * m;
+  const int tid = threadIdx.x;
+  const uint64_t tile = blockIdx.x;
+  const uint64_t lo = tile * P;
+  const uint64_t hi = std::min<uint64_t>(n, lo + P);
+  const float s_first = a_s[lo], s_last = a_s[hi - 1];
+  if (tid == 0) tanch[tile] = make_float2(s_first, s_last);
+  const uint64_t p0 = lo + (uint64_t)tid * E;
+  float ae[E], wf[E], wb[E], tf[E], tb[E];
+  load_anchors<E>(a_s, p0, n, s_last, vec, ae);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool valid = p0 + e < n;
+    wf[e] = valid ? decay(ae[e] - s_last) : 0.f;
+    wb[e] = valid ? decay(s_first - ae[e]) : 0.f;
+    tf[e] = valid ? decay_m<true>(ae[e] - s_last) : 0.f;
+    tb[e] = valid ? decay_m<true>(s_first - ae[e]) : 0.f;
+  }
+  for (uint32_t cc = 0; cc < m / C; ++cc) {
+    float xv[E][C], gv[E][C];
+    load_rows<E, C>(xs, p0, n, m, cc, true, xv);
+    load_rows<E, C>(gs, p0, n, m, cc, true, gv);
+    float sf[CC], sb[CC];
+#pragma unroll
+    for (int j = 0; j < CC; ++j) sf[j] = sb[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        sf[j] = fmaf(wf[e], xv[e][j], sf[j]);
+        sf[C + j] = fmaf(wf[e], gv[e][j], sf[C + j]);
+        sf[2 * C + j] = fmaf(tf[e], xv[e][j], sf[2 * C + j]);
+        sf[3 * C + j] = fmaf(tf[e], gv[e][j], sf[3 * C + j]);
+        sb[j] = fmaf(wb[e], xv[e][j], sb[j]);
+        sb[C + j] = fmaf(wb[e], gv[e][j], sb[C + j]);
+        sb[2 * C + j] = fmaf(tb[e], xv[e][j], sb[2 * C + j]);
+        sb[3 * C + j] = fmaf(tb[e], gv[e][j], sb[3 * C + j]);
+      }
+    }
+    int writer = 0;
+    block_sum2<CC, NW>(sf, sb, s_red, writer);
+    if (writer) {
+      float f = 0.f, b = 0.f;
+      for (int w = 0; w < NW; ++w) {
+        f += s_red[(0 * NW + w) * CC + tid];
+        b += s_red[(1 * NW + w) * CC + tid];
+      }
+      const uint32_t col = bwdcol<C>(m, cc, tid);
+      bf[tile * M + col] = f;
+      bb[tile * M + col] = b;
+    }
+    __syncthreads();
+  }
+}
+
+// Tile scans of (x, g) under both decays -> dx = K g (rows in sorted order)
+// and da (sorted order).
+template <int C>
+__global__ __launch_bounds__(apply_block(2 * C)) void k_bwd_apply(const float* __restrict__ a_s, const float* __restrict__ xs,
+                                                                  const float* __restrict__ gs, const float* __restrict__ cfw,
+                                                                  const float* __restrict__ cbw,
+                                                                  const float2* __restrict__ tanch, uint64_t n, uint32_t m,
+                                                                  uint64_t T, float* __restrict__ dxs, float* __restrict__ das,
+                                                                  bool vec) {
+  constexpr int CC = 2 * C;  // columns of one scan (x then g)
+  constexpr int E = apply_items(CC);
+  constexpr int BLOCK = apply_block(CC);
+  constexpr int NW = BLOCK / kWave;
+  constexpr int P = BLOCK * E;
+  __shared__ float s_wf[NW * CC], s_wb[NW * CC], s_wfs[NW], s_wbs[NW];
+  const uint32_t M = 4 * m;
+  const int tid = threadIdx.x;
+  const uint64_t tile = blockIdx.x;
+  const uint64_t p0 = tile * P + (uint64_t)tid * E;
+  float ae[E];
+  load_anchors<E>(a_s, p0, n, a_s[n - 1], vec, ae);
+  const float2 ta = tanch[tile];
+  const float sf = tile > 0 ? tanch[tile - 1].y : ta.x;
+  const float sb = tile + 1 < T ? tanch[tile + 1].x : ta.y;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (uint32_t cc = 0; cc < m / C; ++cc) {
+    float xv[E][C], gv[E][C];
+    load_rows<E, C>(xs, p0, n, m, cc, true, xv);
+    load_rows<E, C>(gs, p0, n, m, cc, true, gv);
+    float v[E][CC];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        v[e][j] = xv[e][j];
+        v[e][C + j] = gv[e][j];
+      }
+    float ce_f[CC], ce_b[CC], ct_f[CC], ct_b[CC];
+#pragma unroll
+    for (int j = 0; j < CC; ++j) {
+      ce_f[j] = cfw[tile * M + bwdcol<C>(m, cc, j)];
+      ce_b[j] = cbw[tile * M + bwdcol<C>(m, cc, j)];
+      ct_f[j] = cfw[tile * M + bwdcol<C>(m, cc, CC + j)];
+      ct_b[j] = cbw[tile * M + bwdcol<C>(m, cc, CC + j)];
+    }
+    float F[E][CC], U[E][CC], F0[E][CC], U0[E][CC];
+    tile_scan_fu<E, CC, NW, false>(ae, v, ce_f, sf, ce_b, sb, s_wf, s_wfs, s_wb, s_wbs, F, U);
+    __syncthreads();  // the second scan reuses the wave summaries
+    tile_scan_fu<E, CC, NW, true>(ae, v, ct_f, sf, ct_b, sb, s_wf, s_wfs, s_wb, s_wbs, F0, U0);
+    float dx[E][C];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        const float sx = (F[e][j] - F0[e][j]) - (U[e][j] - U0[e][j]);
+        const float sg = (F[e][C + j] - F0[e][C + j]) - (U[e][C + j] - U0[e][C + j]);
+        acc[e] = fmaf(gv[e][j], sx, acc[e]);
+        acc[e] = fmaf(xv[e][j], sg, acc[e]);
+        dx[e][j] = F[e][C + j] + U[e][C + j];
+      }
+    }
+    store_rows<E, C>(dxs, p0, n, m, cc, true, dx);
+    __syncthreads();
+  }
+  float dav[E][1];
+#pragma unroll
+  for (int e = 0; e < E; ++e) dav[e][0] = -acc[e];
+  store_rows<E, 1>(das, p0, n, 1, 0, true, dav);
+}
+
+// dst[perm[r]] = src[r] for rows of m floats (rows in sorted order -> original)
+__global__ void k_scatter_rows(const float* __restrict__ src, const uint32_t* __restrict__ perm, uint64_t rows, uint32_t m,
+                               float* __restrict__ dst) {
+  uint64_t r = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (; r < rows; r += stride) {
+    const uint32_t d = perm[r];
+    if ((uint64_t)d >= rows) continue;  // a handle from the sort is always in range
+    for (uint32_t c = 0; c < m; ++c) dst[(uint64_t)d * m + c] = src[r * m + c];
+  }
+}
+
+static unsigned rows_grid(uint64_t rows) { return (unsigned)std::min<uint64_t>((rows + 255) / 256, 8192); }
+
+template <int C>
+static hipError_t run_bwd_sym(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm, const SortRoute* route,
+                              uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da, hipStream_t s) {
+  const ApplyWorkspace& w = bw.w;
+  constexpr int CC = 2 * C;
+  constexpr int P = apply_tile(CC);
+  const uint64_t T = (n + P - 1) / P;
+  const uint32_t M = 4 * m;
+  const dim3 grid((unsigned)T), block(apply_block(CC));
+  const bool routed = route != nullptr && m <= kRouteMaxCols;
+  const bool vec = (reinterpret_cast<uintptr_t>(a_s) & 15) == 0;
+  hipError_t e;
+  if (routed) {
+    if ((e = route_forward(*route, n, m, x, w.xs, w.t0, w.t1, s)) != hipSuccess) return e;
+    if ((e = route_forward(*route, n, m, g, bw.gs, w.t0, w.t1, s)) != hipSuccess) return e;
+  } else {
+    LAPLEX_LAUNCH("k_gather_rows", n, s, k_gather_rows<<<rows_grid(n), 256, 0, s>>>(x, perm, nullptr, n, m, w.xs, nullptr));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    LAPLEX_LAUNCH("k_gather_rows", n, s, k_gather_rows<<<rows_grid(n), 256, 0, s>>>(g, perm, nullptr, n, m, bw.gs, nullptr));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  LAPLEX_LAUNCH("k_bwd_reduce", n, s,
+                k_bwd_reduce<C><<<grid, block, 0, s>>>(a_s, w.xs, bw.gs, n, m, w.bf, w.bb, w.tanch, vec));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = tile_carries(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb, w.gbf, w.gbb, w.gcf, w.gcb, w.ganch, s, 2 * m)) != hipSuccess)
+    return e;
+  LAPLEX_LAUNCH("k_bwd_apply", n, s,
+                k_bwd_apply<C><<<grid, block, 0, s>>>(a_s, w.xs, bw.gs, w.cf, w.cb, w.tanch, n, m, T, w.zs, bw.das, vec));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (routed) {
+    if ((e = route_inverse(*route, n, m, w.zs, dx, w.t0, w.t1, s)) != hipSuccess) return e;
+    return route_inverse(*route, n, 1, bw.das, da, w.t0, w.t1, s);
+  }
+  LAPLEX_LAUNCH("k_scatter_rows", n, s, k_scatter_rows<<<rows_grid(n), 256, 0, s>>>(w.zs, perm, n, m, dx));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  LAPLEX_LAUNCH("k_scatter_rows", n, s, k_scatter_rows<<<rows_grid(n), 256, 0, s>>>(bw.das, perm, n, 1, da));
+  return hipGetLastError();
+}
+
+hipError_t backward_sym(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm, const SortRoute* route,
+                        uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da, hipStream_t s) {
+  switch (column_chunk(m)) {
+    case 8: return run_bwd_sym<8>(bw, a_s, perm, route, n, m, x, g, dx, da, s);
+    case 4: return run_bwd_sym<4>(bw, a_s, perm, route, n, m, x, g, dx, da, s);
+    case 2: return run_bwd_sym<2>(bw, a_s, perm, route, n, m, x, g, dx, da, s);
+    default: return run_bwd_sym<1>(bw, a_s, perm, route, n, m, x, g, dx, da, s);
+  }
 }
 
 // ---------------------------------------------------------------- general (merged a and b)

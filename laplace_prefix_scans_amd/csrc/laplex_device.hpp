@@ -58,6 +58,19 @@ __device__ __forceinline__ void store_agent(T* p, T v) {
 // is <= 1 and never a product of decays.
 __device__ __forceinline__ float decay(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
+// Decay in one of two modes.  TIE: the zero-temperature limit of the kernel,
+// exp(x / T) as T -> 0 for x <= 0, i.e. 1 between equal anchors and 0 otherwise;
+// scanned with it, the recurrences sum within groups of tied anchors only.
+template <bool TIE>
+__device__ __forceinline__ float decay_m(float x) {
+  if constexpr (TIE)
+    return x == 0.f ? 1.f : 0.f;
+  else
+    return decay(x);
+}
+// the same with the mode chosen at run time (uniform per block)
+__device__ __forceinline__ float decay_r(float x, bool tie) { return tie ? (x == 0.f ? 1.f : 0.f) : decay(x); }
+
 // ---------------------------------------------------------------- affine segment scans
 // A segment of the forward recurrence L_i = x_i + exp(s_{i-1} - s_i) L_{i-1}
 // is summarised by (B, s): its last value with zero carry-in, and the anchor
@@ -67,13 +80,13 @@ __device__ __forceinline__ float decay(float x) { return __builtin_amdgcn_exp2f(
 
 // Inclusive forward scan across the wave, lane order.  `s` is this lane's
 // segment-end anchor (it does not change).
-template <int C>
+template <int C, bool TIE = false>
 __device__ __forceinline__ void wave_scan_fwd(float (&B)[C], float s) {
   const int lane = lane_id();
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
     const float sl = __shfl_up(s, off);
-    const float w = decay(sl - s);
+    const float w = decay_m<TIE>(sl - s);
     const bool take = lane >= off;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -85,13 +98,13 @@ __device__ __forceinline__ void wave_scan_fwd(float (&B)[C], float s) {
 
 // Inclusive backward scan across the wave (from the last lane down).  `s` is
 // this lane's segment-start anchor.
-template <int C>
+template <int C, bool TIE = false>
 __device__ __forceinline__ void wave_scan_bwd(float (&B)[C], float s) {
   const int lane = lane_id();
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
     const float sr = __shfl_down(s, off);
-    const float w = decay(s - sr);
+    const float w = decay_m<TIE>(s - sr);
     const bool take = lane + off < kWave;
 #pragma unroll
     for (int c = 0; c < C; ++c) {

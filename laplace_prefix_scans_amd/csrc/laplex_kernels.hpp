@@ -107,6 +107,17 @@ hipError_t apply_general(const ApplyWorkspace& w, Variant var, const float* a_s,
                          const float* phi, uint64_t n, const float* b_s, const uint32_t* perm_b, const SortRoute* route_b,
                          const float* psi, uint64_t k, uint32_t m, const float* x, float* y, hipStream_t s);
 
+// Backward of the symmetric operator: dx = K g and the anchor gradient da.
+// Uses an apply workspace whose summary width is M = 4m (x and g, each with
+// the kernel's decay and with the tie decay); zs holds dx in sorted order.
+struct BackwardWorkspace {
+  ApplyWorkspace w;
+  float* gs;   // upstream gradient gathered into sorted order (n x m)
+  float* das;  // anchor gradient in sorted order (n)
+};
+hipError_t backward_sym(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm, const SortRoute* route,
+                        uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da, hipStream_t s);
+
 // tile count and summary width of an apply
 inline uint64_t apply_tiles(uint64_t len, uint32_t m, Variant var) {
   const uint32_t c = column_chunk(m);
@@ -114,5 +125,8 @@ inline uint64_t apply_tiles(uint64_t len, uint32_t m, Variant var) {
   const uint64_t tile = (uint64_t)apply_tile(cc);
   return (len + tile - 1) / tile;
 }
+
+// tile count of a symmetric backward (the tile shape of a 2m-column scan)
+inline uint64_t backward_tiles(uint64_t n, uint32_t m) { return apply_tiles(n, m, Variant::Phased); }
 
 }  // namespace laplex

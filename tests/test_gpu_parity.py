@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import TOL, assert_perm_is_stable_argsort, dev, gpu_sort, have_gpu, host
+from gpu_util import TOL, assert_perm_is_stable_argsort, describe_nonfinite, dev, gpu_sort, have_gpu, host
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
 
@@ -80,7 +80,8 @@ def test_sym_parity(n, m):
         bad = np.nonzero(pa != oracle.stable_argsort(a))[0]
         assert bad.size == 0, "sym n=%d m=%d ties=%s: perm differs at %d positions, first %d" % (n, m, ties, bad.size, bad[0])
         y = host(lp.laplex_matvec_sym(a_s, perm, dev(x)))
-        assert np.isfinite(y).all(), "sym n=%d m=%d ties=%s: non-finite output" % (n, m, ties)
+        assert np.isfinite(y).all(), "sym n=%d m=%d ties=%s: %s" % (
+            n, m, ties, describe_nonfinite(y, pa, rerun=lambda: host(lp.laplex_matvec_sym(a_s, perm, dev(x)))))
         ref = oracle.sym_apply(a, x)
         env = oracle.sym_apply(a, np.abs(x))
         err = oracle.normwise_error(y, ref, env)

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import TOL, assert_perm_is_stable_argsort, dev, have_gpu, host
+from gpu_util import TOL, assert_perm_is_stable_argsort, describe_nonfinite, dev, have_gpu, host
 from synth import make_workload
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
@@ -61,6 +61,8 @@ def test_workload_full_parity(name):
     else:
         ref = oracle.sym_apply(w.a, w.x)
         env = oracle.sym_apply(w.a, np.abs(w.x))
+    if not np.isfinite(y).all():
+        pytest.fail("workload %s: %s" % (name, describe_nonfinite(y, pa, rerun=lambda: host(_run(w)["y"]))))
     err = oracle.normwise_error(y, ref, env)
     print("normwise error %.3e" % err, flush=True)
     assert err <= TOL
