@@ -69,6 +69,9 @@ def kernel_bytes(name: str, units: int, m: int, k: int = 0) -> float:
         "k_gather_rows": 4.0 + 8.0 * m,
         "k_gen_reduce": 4.0 + 4.0 * m,
         "k_phased_gen_reduce": 8.0 + 4.0 * m,
+        "k_bwd_reduce": 4.0 + 8.0 * m,           # sorted anchors, sorted x and g rows
+        "k_bwd_apply": 8.0 + 12.0 * m,           # sorted anchors, x and g rows in; dx rows and da out
+        "k_scatter_rows": 4.0 + 8.0 * m,         # perm, sorted rows in, rows out (random)
     }
     for w in (1, 2, 3, 4):
         table["k_route_fwd_w%d" % w] = route + 8.0 * w   # position, row in, row out
@@ -239,6 +242,44 @@ def cpu_baseline(workload: str, log2_sample: int):
     }
 
 
+def time_backward(lp, torch, a_s, pa, x, ra, n, m, args, dev):
+    """The backward (dx = K g, anchor gradient) for the sort handle of the
+    timed steps and a seeded upstream gradient: its own timed loop, reported
+    beside the forward step."""
+    gen = torch.Generator(device=dev).manual_seed(0x6AAD)
+    g = torch.randn(x.shape, generator=gen, device=dev)
+    dx = torch.empty_like(g)
+    da = torch.empty(n, dtype=torch.float32, device=dev)
+    ws = lp.workspace(lp.LAPLEX_OP_SYM_BACKWARD, n, 0, m, device=dev)
+
+    def bstep():
+        lp.laplex_backward_sym(a_s, pa, x, g, dx=dx, da=da, ws=ws, route=ra)
+
+    for _ in range(args.warmup):
+        bstep()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with lp.profile_launches(capacity=64 * max(1, args.steps)) as prof:
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            bstep()
+        e1.record()
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    kern_ms, kern_bytes = 0.0, 0.0
+    for name, kms, units in prof.records:
+        kern_ms += kms
+        kern_bytes += kernel_bytes(name, units, m)
+    kern_ms /= args.steps
+    kern_bytes /= args.steps
+    gbps = kern_bytes / (kern_ms * 1e-3) / 1e9 if kern_ms > 0 else None
+    return {"ms_per_call": round(ms, 4), "kernel_ms": round(kern_ms, 4), "alg_GB": round(kern_bytes / 1e9, 3),
+            "alg_GBps": round(gbps, 1) if gbps else None,
+            "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4) if gbps else None,
+            "Gelem_per_s": round(n * m / (ms * 1e-3) / 1e9, 4), "outputs": "dx = K g and da, from x and g"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,6 +289,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-route", action="store_true", help="move x and y by index instead of along the sort route")
     ap.add_argument("--cpu-sample-log2", type=int, default=25)
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the backward of the symmetric workloads")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--rocprof-summary", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
@@ -396,6 +438,8 @@ def main():
         "source_hash": src,
         "host_gen_s": round(t_gen, 1),
     }
+    if w.kind == "sym" and not args.no_backward:
+        line["backward_part"] = time_backward(lp, torch, a_s, pa, x, ra, n, m, args, dev)
     if args.calib_copy:
         src_t = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst_t = torch.empty_like(src_t)
