@@ -886,13 +886,13 @@ __device__ __forceinline__ uint32_t bwdcol(uint32_t m, uint32_t cc, int j) {
 // Gathered inputs (or their rows moved by route) -> tile aggregates of x and g
 // under both decays, as direct weighted sums.
 template <int C>
-__global__ __launch_bounds__(apply_block(2 * C)) void k_bwd_reduce(const float* __restrict__ a_s, const float* __restrict__ xs,
+__global__ __launch_bounds__(bwd_block(C)) void k_bwd_reduce(const float* __restrict__ a_s, const float* __restrict__ xs,
                                                                    const float* __restrict__ gs, uint64_t n, uint32_t m,
                                                                    float* __restrict__ bf, float* __restrict__ bb,
                                                                    float2* __restrict__ tanch, bool vec) {
   constexpr int CC = 4 * C;
-  constexpr int E = apply_items(2 * C);
-  constexpr int BLOCK = apply_block(2 * C);
+  constexpr int E = bwd_items(C);
+  constexpr int BLOCK = bwd_block(C);
   constexpr int NW = BLOCK / kWave;
   constexpr int P = BLOCK * E;
   __shared__ float s_red[2 * NW * CC];
@@ -952,17 +952,17 @@ __global__ __launch_bounds__(apply_block(2 * C)) void k_bwd_reduce(const float* 
 }
 
 // Tile scans of (x, g) under both decays -> dx = K g (rows in sorted order)
-// and da (sorted order).
+// and da (sorted order).  By linearity da_i = -(A_i - A0_i) with
+// A = sum_c g_c (F - U)(x_c) + x_c (F - U)(g_c) under the kernel's decay and A0
+// the same under the tie decay; the tie scan runs first and only its per-element
+// sum stays live through the second scan.
 template <int C>
-__global__ __launch_bounds__(apply_block(2 * C)) void k_bwd_apply(const float* __restrict__ a_s, const float* __restrict__ xs,
-                                                                  const float* __restrict__ gs, const float* __restrict__ cfw,
-                                                                  const float* __restrict__ cbw,
-                                                                  const float2* __restrict__ tanch, uint64_t n, uint32_t m,
-                                                                  uint64_t T, float* __restrict__ dxs, float* __restrict__ das,
-                                                                  bool vec) {
+__global__ __launch_bounds__(bwd_block(C)) void k_bwd_apply(const float* __restrict__ a_s, const float* __restrict__ xs, const float* __restrict__ gs,
+                 const float* __restrict__ cfw, const float* __restrict__ cbw, const float2* __restrict__ tanch,
+                 uint64_t n, uint32_t m, uint64_t T, float* __restrict__ dxs, float* __restrict__ das, bool vec) {
   constexpr int CC = 2 * C;  // columns of one scan (x then g)
-  constexpr int E = apply_items(CC);
-  constexpr int BLOCK = apply_block(CC);
+  constexpr int E = bwd_items(C);
+  constexpr int BLOCK = bwd_block(C);
   constexpr int NW = BLOCK / kWave;
   constexpr int P = BLOCK * E;
   __shared__ float s_wf[NW * CC], s_wb[NW * CC], s_wfs[NW], s_wbs[NW];
@@ -975,51 +975,66 @@ __global__ __launch_bounds__(apply_block(2 * C)) void k_bwd_apply(const float* _
   const float2 ta = tanch[tile];
   const float sf = tile > 0 ? tanch[tile - 1].y : ta.x;
   const float sb = tile + 1 < T ? tanch[tile + 1].x : ta.y;
-  float acc[E];
+  float acc[E], acc0[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int e = 0; e < E; ++e) acc[e] = acc0[e] = 0.f;
   for (uint32_t cc = 0; cc < m / C; ++cc) {
-    float xv[E][C], gv[E][C];
-    load_rows<E, C>(xs, p0, n, m, cc, true, xv);
-    load_rows<E, C>(gs, p0, n, m, cc, true, gv);
     float v[E][CC];
+    {
+      float xv[E][C], gv[E][C];
+      load_rows<E, C>(xs, p0, n, m, cc, true, xv);
+      load_rows<E, C>(gs, p0, n, m, cc, true, gv);
 #pragma unroll
-    for (int e = 0; e < E; ++e)
+      for (int e = 0; e < E; ++e)
 #pragma unroll
-      for (int j = 0; j < C; ++j) {
-        v[e][j] = xv[e][j];
-        v[e][C + j] = gv[e][j];
-      }
-    float ce_f[CC], ce_b[CC], ct_f[CC], ct_b[CC];
-#pragma unroll
-    for (int j = 0; j < CC; ++j) {
-      ce_f[j] = cfw[tile * M + bwdcol<C>(m, cc, j)];
-      ce_b[j] = cbw[tile * M + bwdcol<C>(m, cc, j)];
-      ct_f[j] = cfw[tile * M + bwdcol<C>(m, cc, CC + j)];
-      ct_b[j] = cbw[tile * M + bwdcol<C>(m, cc, CC + j)];
+        for (int j = 0; j < C; ++j) {
+          v[e][j] = xv[e][j];
+          v[e][C + j] = gv[e][j];
+        }
     }
-    float F[E][CC], U[E][CC], F0[E][CC], U0[E][CC];
-    tile_scan_fu<E, CC, NW, false>(ae, v, ce_f, sf, ce_b, sb, s_wf, s_wfs, s_wb, s_wbs, F, U);
+    {
+      float ct_f[CC], ct_b[CC];
+#pragma unroll
+      for (int j = 0; j < CC; ++j) {
+        ct_f[j] = cfw[tile * M + bwdcol<C>(m, cc, CC + j)];
+        ct_b[j] = cbw[tile * M + bwdcol<C>(m, cc, CC + j)];
+      }
+      float F0[E][CC], U0[E][CC];
+      tile_scan_fu<E, CC, NW, true>(ae, v, ct_f, sf, ct_b, sb, s_wf, s_wfs, s_wb, s_wbs, F0, U0);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+          acc0[e] = fmaf(v[e][C + j], F0[e][j] - U0[e][j], acc0[e]);
+          acc0[e] = fmaf(v[e][j], F0[e][C + j] - U0[e][C + j], acc0[e]);
+        }
+    }
     __syncthreads();  // the second scan reuses the wave summaries
-    tile_scan_fu<E, CC, NW, true>(ae, v, ct_f, sf, ct_b, sb, s_wf, s_wfs, s_wb, s_wbs, F0, U0);
-    float dx[E][C];
+    {
+      float ce_f[CC], ce_b[CC];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-#pragma unroll
-      for (int j = 0; j < C; ++j) {
-        const float sx = (F[e][j] - F0[e][j]) - (U[e][j] - U0[e][j]);
-        const float sg = (F[e][C + j] - F0[e][C + j]) - (U[e][C + j] - U0[e][C + j]);
-        acc[e] = fmaf(gv[e][j], sx, acc[e]);
-        acc[e] = fmaf(xv[e][j], sg, acc[e]);
-        dx[e][j] = F[e][C + j] + U[e][C + j];
+      for (int j = 0; j < CC; ++j) {
+        ce_f[j] = cfw[tile * M + bwdcol<C>(m, cc, j)];
+        ce_b[j] = cbw[tile * M + bwdcol<C>(m, cc, j)];
       }
+      float F[E][CC], U[E][CC];
+      tile_scan_fu<E, CC, NW, false>(ae, v, ce_f, sf, ce_b, sb, s_wf, s_wfs, s_wb, s_wbs, F, U);
+      float dx[E][C];
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+          acc[e] = fmaf(v[e][C + j], F[e][j] - U[e][j], acc[e]);
+          acc[e] = fmaf(v[e][j], F[e][C + j] - U[e][C + j], acc[e]);
+          dx[e][j] = F[e][C + j] + U[e][C + j];
+        }
+      store_rows<E, C>(dxs, p0, n, m, cc, true, dx);
     }
-    store_rows<E, C>(dxs, p0, n, m, cc, true, dx);
     __syncthreads();
   }
   float dav[E][1];
 #pragma unroll
-  for (int e = 0; e < E; ++e) dav[e][0] = -acc[e];
+  for (int e = 0; e < E; ++e) dav[e][0] = acc0[e] - acc[e];
   store_rows<E, 1>(das, p0, n, 1, 0, true, dav);
 }
 
@@ -1041,11 +1056,10 @@ template <int C>
 static hipError_t run_bwd_sym(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm, const SortRoute* route,
                               uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da, hipStream_t s) {
   const ApplyWorkspace& w = bw.w;
-  constexpr int CC = 2 * C;
-  constexpr int P = apply_tile(CC);
+  constexpr int P = bwd_tile(C);
   const uint64_t T = (n + P - 1) / P;
   const uint32_t M = 4 * m;
-  const dim3 grid((unsigned)T), block(apply_block(CC));
+  const dim3 grid((unsigned)T), block(bwd_block(C));
   const bool routed = route != nullptr && m <= kRouteMaxCols;
   const bool vec = (reinterpret_cast<uintptr_t>(a_s) & 15) == 0;
   hipError_t e;

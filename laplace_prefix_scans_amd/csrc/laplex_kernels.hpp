@@ -126,7 +126,18 @@ inline uint64_t apply_tiles(uint64_t len, uint32_t m, Variant var) {
   return (len + tile - 1) / tile;
 }
 
-// tile count of a symmetric backward (the tile shape of a 2m-column scan)
-inline uint64_t backward_tiles(uint64_t n, uint32_t m) { return apply_tiles(n, m, Variant::Phased); }
+// Tile shape of the symmetric backward for a chunk of c columns (2c scanned
+// columns, x and g).  One column: 512-thread workgroups of 4 items each, so
+// two workgroups share a compute unit without spilling and one's loads
+// overlap the other's scans.
+constexpr int bwd_items(int c) { return c == 1 ? 4 : apply_items(2 * c); }
+constexpr int bwd_block(int c) { return c == 1 ? 512 : apply_block(2 * c); }
+constexpr int bwd_tile(int c) { return bwd_items(c) * bwd_block(c); }
+
+// tile count of a symmetric backward
+inline uint64_t backward_tiles(uint64_t n, uint32_t m) {
+  const uint64_t tile = (uint64_t)bwd_tile((int)column_chunk(m));
+  return (n + tile - 1) / tile;
+}
 
 }  // namespace laplex
