@@ -72,12 +72,15 @@ def kernel_bytes(name: str, units: int, m: int, k: int = 0) -> float:
         "k_bwd_reduce": 4.0 + 8.0 * m,           # sorted anchors, sorted x and g rows
         "k_bwd_apply": 8.0 + 12.0 * m,           # sorted anchors, x and g rows in; dx rows and da out
         "k_scatter_rows": 4.0 + 8.0 * m,         # perm, sorted rows in, rows out (random)
+        "k_gbwd_reduce": 4.0 + 4.0 * m,          # merged anchors, x rows (at b) and g rows (at a)
     }
     for w in (1, 2, 3, 4):
         table["k_route_fwd_w%d" % w] = route + 8.0 * w   # position, row in, row out
         table["k_route_inv_w%d" % w] = route + 8.0 * w
     if name in table:
         return table[name] * units
+    if name == "k_gbwd_apply":  # merged anchors, x and g rows in; da (n), db and dx rows (k) out
+        return (8.0 + 4.0 * m) * units + 4.0 * m * k
     if name in ("k_gen_apply", "k_phased_gen_apply"):
         return (8.0 + 4.0 * m) * units + (4.0 + 4.0 * m) * k
     if name in ("k_gen_apply_sorted", "k_phased_gen_apply_sorted"):
@@ -242,19 +245,10 @@ def cpu_baseline(workload: str, log2_sample: int):
     }
 
 
-def time_backward(lp, torch, a_s, pa, x, ra, n, m, args, dev):
-    """The backward (dx = K g, anchor gradient) for the sort handle of the
-    timed steps and a seeded upstream gradient: its own timed loop, reported
-    beside the forward step."""
-    gen = torch.Generator(device=dev).manual_seed(0x6AAD)
-    g = torch.randn(x.shape, generator=gen, device=dev)
-    dx = torch.empty_like(g)
-    da = torch.empty(n, dtype=torch.float32, device=dev)
-    ws = lp.workspace(lp.LAPLEX_OP_SYM_BACKWARD, n, 0, m, device=dev)
-
-    def bstep():
-        lp.laplex_backward_sym(a_s, pa, x, g, dx=dx, da=da, ws=ws, route=ra)
-
+def time_backward(lp, torch, bstep, n, m, k, args):
+    """The backward call `bstep` (for the sort handles of the timed steps and
+    a seeded upstream gradient): its own timed loop, reported beside the
+    forward step."""
     for _ in range(args.warmup):
         bstep()
     torch.cuda.synchronize()
@@ -268,16 +262,25 @@ def time_backward(lp, torch, a_s, pa, x, ra, n, m, args, dev):
         torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     kern_ms, kern_bytes = 0.0, 0.0
+    per = {}
     for name, kms, units in prof.records:
+        b = kernel_bytes(name, units, m, k)
         kern_ms += kms
-        kern_bytes += kernel_bytes(name, units, m)
+        kern_bytes += b
+        r = per.setdefault(name, [0.0, 0, 0.0])
+        r[0] += kms
+        r[1] += 1
+        r[2] += b
     kern_ms /= args.steps
     kern_bytes /= args.steps
     gbps = kern_bytes / (kern_ms * 1e-3) / 1e9 if kern_ms > 0 else None
+    kernels = {name: {"ms_per_call": round(v[0] / args.steps, 4), "launches_per_call": v[1] // args.steps,
+                      "alg_GBps": round(v[2] / (v[0] * 1e-3) / 1e9, 1) if v[0] > 0 else None}
+               for name, v in per.items()}
     return {"ms_per_call": round(ms, 4), "kernel_ms": round(kern_ms, 4), "alg_GB": round(kern_bytes / 1e9, 3),
             "alg_GBps": round(gbps, 1) if gbps else None,
             "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4) if gbps else None,
-            "Gelem_per_s": round(n * m / (ms * 1e-3) / 1e9, 4), "outputs": "dx = K g and da, from x and g"}
+            "Gelem_per_s": round(n * m / (ms * 1e-3) / 1e9, 4), "kernels": kernels}
 
 
 def main():
@@ -438,8 +441,28 @@ def main():
         "source_hash": src,
         "host_gen_s": round(t_gen, 1),
     }
-    if w.kind == "sym" and not args.no_backward:
-        line["backward_part"] = time_backward(lp, torch, a_s, pa, x, ra, n, m, args, dev)
+    if w.kind in ("sym", "general") and not args.no_backward:
+        gen = torch.Generator(device=dev).manual_seed(0x6AAD)
+        g = torch.randn((n,) if x.dim() == 1 else (n, m), generator=gen, device=dev)
+        da = torch.empty(n, dtype=torch.float32, device=dev)
+        dx = torch.empty_like(x)
+        if w.kind == "sym":
+            ws_b = lp.workspace(lp.LAPLEX_OP_SYM_BACKWARD, n, 0, m, device=dev)
+
+            def bstep():
+                lp.laplex_backward_sym(a_s, pa, x, g, dx=dx, da=da, ws=ws_b, route=ra)
+            what = "dx = K g and da, from x and g"
+        else:
+            ws_b = lp.workspace(lp.LAPLEX_OP_GENERAL_BACKWARD, n, k, m, device=dev)
+            db = torch.empty(k, dtype=torch.float32, device=dev)
+
+            def bstep():
+                lp.laplex_backward_general(a_s, pa, b_s, pb, x, g, dx=dx, da=da, db=db, ws=ws_b, route_a=ra,
+                                           route_b=rb)
+            what = "dx = K^T g, da and db, from x and g"
+        line["backward_part"] = time_backward(lp, torch, bstep, n, m, k, args)
+        line["backward_part"]["outputs"] = what
+        del ws_b
     if args.calib_copy:
         src_t = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst_t = torch.empty_like(src_t)

@@ -60,7 +60,8 @@ enum {
   LAPLEX_OP_GENERAL = 2,
   LAPLEX_OP_PHASED = 3,         /* symmetric phased operator (b = a, psi = phi) */
   LAPLEX_OP_PHASED_GENERAL = 4, /* phased operator with a != b */
-  LAPLEX_OP_SYM_BACKWARD = 5    /* backward of the symmetric operator */
+  LAPLEX_OP_SYM_BACKWARD = 5,   /* backward of the symmetric operator */
+  LAPLEX_OP_GENERAL_BACKWARD = 6 /* backward of the general operator */
 };
 
 /* Bytes of workspace one call of `op` needs for n output anchors, k input
@@ -145,6 +146,23 @@ laplex_status laplex_matvec_phased(const float* a_sorted, const uint32_t* perm_a
 laplex_status laplex_backward_sym(const float* a_sorted, const uint32_t* perm, const void* route, uint64_t n, uint32_t m,
                                   const float* x, const float* g, float* dx, float* da, void* ws, size_t ws_bytes,
                                   hipStream_t stream);
+
+/* Backward of the general operator y = LAPLEX(a, b) x (rows a, n; columns b,
+ * k; same section and chain rule as the symmetric backward): for g = dL/dy,
+ *     dx_j = sum_i exp(-|a_i - b_j|) g_i           = LAPLEX(b, a) g   (k x m)
+ *     da_i = - sum_c g_ic sum_j sign(a_i - b_j) exp(-|a_i - b_j|) x_jc   (n)
+ *     db_j = - sum_c x_jc sum_i sign(b_j - a_i) exp(-|a_i - b_j|) g_ic   (k)
+ * with sign(0) = 0 (an a anchor equal to a b anchor adds nothing to either
+ * gradient).  All three come from one pass over the merge of sorted a and b.
+ * a_sorted, perm_a, route_a: sort handle of a; b_sorted, perm_b, route_b: sort
+ * handle of b (routes may be NULL); x: k x m, g: n x m (inputs, original
+ * order); dx: k x m, da: n, db: k (outputs, original order, none overlapping
+ * another array).  k == 0 sets da to zero; n == 0 sets dx and db to zero.
+ * ws: laplex_workspace_bytes(LAPLEX_OP_GENERAL_BACKWARD, n, k, m) bytes. */
+laplex_status laplex_backward_general(const float* a_sorted, const uint32_t* perm_a, const void* route_a, uint64_t n,
+                                      const float* b_sorted, const uint32_t* perm_b, const void* route_b, uint64_t k,
+                                      uint32_t m, const float* x, const float* g, float* dx, float* da, float* db, void* ws,
+                                      size_t ws_bytes, hipStream_t stream);
 
 /* Short English description of a status code (static storage). */
 const char* laplex_status_string(laplex_status s);

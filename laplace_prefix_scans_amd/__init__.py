@@ -10,9 +10,11 @@ not been built the calls raise -- there is no fallback.
     y = laplex_matvec_general(a_sorted, perm, b_sorted, perm_b, xb)
     y = laplex_matvec_phased(a_sorted, perm, phi, x)  # extra cos(phi_i - phi_j)
     dx, da = laplex_backward_sym(a_sorted, perm, x, g)  # gradients for g = dL/dy
+    dxb, da, db = laplex_backward_general(a_sorted, perm, b_sorted, perm_b, xb, g)
 """
 from ._binding import (  # noqa: F401
     LAPLEX_OP_GENERAL,
+    LAPLEX_OP_GENERAL_BACKWARD,
     LAPLEX_OP_PHASED,
     LAPLEX_OP_PHASED_GENERAL,
     LAPLEX_OP_SORT,
@@ -21,6 +23,7 @@ from ._binding import (  # noqa: F401
     LaplexError,
     lib,
     lib_path,
+    laplex_backward_general,
     laplex_backward_sym,
     laplex_matvec_general,
     laplex_matvec_phased,

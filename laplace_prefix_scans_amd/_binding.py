@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(HERE, "liblaplex.so")
 
 LAPLEX_OP_SORT, LAPLEX_OP_SYM, LAPLEX_OP_GENERAL, LAPLEX_OP_PHASED, LAPLEX_OP_PHASED_GENERAL = 0, 1, 2, 3, 4
 LAPLEX_OP_SYM_BACKWARD = 5
+LAPLEX_OP_GENERAL_BACKWARD = 6
 
 _STATUS = {
     0: "LAPLEX_OK", 1: "LAPLEX_ERR_NULL", 2: "LAPLEX_ERR_SIZE", 3: "LAPLEX_ERR_ALIGN", 4: "LAPLEX_ERR_WORKSPACE",
@@ -55,6 +56,8 @@ def lib():
         L.laplex_matvec_phased.argtypes = [vp, vp, vp, vp, u64, vp, vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
         L.laplex_backward_sym.argtypes = [vp, vp, vp, u64, u32, vp, vp, vp, vp, vp, sz, vp]
         L.laplex_backward_sym.restype = i32
+        L.laplex_backward_general.argtypes = [vp, vp, vp, u64, vp, vp, vp, u64, u32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.laplex_backward_general.restype = i32
         for f in (L.laplex_sort_anchors, L.laplex_status_poll, L.laplex_matvec_sym, L.laplex_matvec_general,
                   L.laplex_matvec_phased):
             f.restype = i32
@@ -197,6 +200,33 @@ def laplex_backward_sym(a_sorted: torch.Tensor, perm: torch.Tensor, x: torch.Ten
     _check(lib().laplex_backward_sym(_ptr(a_sorted), _ptr(perm), _ptr(route), n, m, _ptr(x), _ptr(g), _ptr(dx), _ptr(da),
                                      _ptr(ws), ws.numel(), _stream(dev)), "laplex_backward_sym")
     return dx, da
+
+
+def laplex_backward_general(a_sorted: torch.Tensor, perm_a: torch.Tensor, b_sorted: torch.Tensor, perm_b: torch.Tensor,
+                            x: torch.Tensor, g: torch.Tensor, dx: Optional[torch.Tensor] = None,
+                            da: Optional[torch.Tensor] = None, db: Optional[torch.Tensor] = None,
+                            ws: Optional[torch.Tensor] = None, route_a: Optional[torch.Tensor] = None,
+                            route_b: Optional[torch.Tensor] = None):
+    """Backward of y = LAPLEX(a, b) x for the upstream gradient g = dL/dy
+    (x: (k,) or (k, m); g: (n,) or (n, m)): returns (dx = K^T g, shape of x;
+    da, (n,); db, (k,))."""
+    _vec(a_sorted, "a_sorted")
+    _vec(perm_a, "perm_a", torch.uint32)
+    _vec(b_sorted, "b_sorted")
+    _vec(perm_b, "perm_b", torch.uint32)
+    n, k, dev = a_sorted.shape[0], b_sorted.shape[0], a_sorted.device
+    m = _cols(x, k)
+    if _cols(g, n, "g") != m or g.dim() != x.dim():
+        raise ValueError("g must have n rows and the columns of x")
+    dx = torch.empty_like(x) if dx is None else dx
+    _cols(dx, k, "dx")
+    da = torch.empty(n, dtype=torch.float32, device=dev) if da is None else _vec(da, "da")
+    db = torch.empty(k, dtype=torch.float32, device=dev) if db is None else _vec(db, "db")
+    ws = _ws(ws, LAPLEX_OP_GENERAL_BACKWARD, n, k, m, dev)
+    _check(lib().laplex_backward_general(_ptr(a_sorted), _ptr(perm_a), _ptr(route_a), n, _ptr(b_sorted), _ptr(perm_b),
+                                         _ptr(route_b), k, m, _ptr(x), _ptr(g), _ptr(dx), _ptr(da), _ptr(db), _ptr(ws),
+                                         ws.numel(), _stream(dev)), "laplex_backward_general")
+    return dx, da, db
 
 
 def laplex_matvec_general(a_sorted: torch.Tensor, perm_a: torch.Tensor, b_sorted: torch.Tensor, perm_b: torch.Tensor,

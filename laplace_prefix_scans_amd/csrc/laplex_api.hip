@@ -83,16 +83,21 @@ ApplyWorkspace carve_apply(void* ws, uint64_t rows_in, uint64_t rows_out, uint64
   return w;
 }
 
-BackwardWorkspace carve_backward(void* ws, uint64_t n, uint32_t m, size_t* total) {
+// Symmetric (k = 0, general false) or general backward: gathered inputs,
+// sorted-order outputs, tile summaries of width 4m over the n (+ k) scanned
+// elements, and route scratch when m is small enough for routes.
+BackwardWorkspace carve_backward(void* ws, uint64_t n, uint64_t k, uint32_t m, bool general, size_t* total) {
   Carver c(ws);
   BackwardWorkspace bw{};
   ApplyWorkspace& w = bw.w;
-  const uint64_t T = backward_tiles(n, m);
+  const uint64_t rows_x = general ? k : n;  // rows of x and dx
+  const uint64_t T = backward_tiles(general ? n + k : n, m);
   const uint64_t M = 4ull * m;
-  w.xs = c.take<float>(n * m * 4);
+  w.xs = c.take<float>(rows_x * m * 4);
   bw.gs = c.take<float>(n * m * 4);
-  w.zs = c.take<float>(n * m * 4);
+  w.zs = c.take<float>(rows_x * m * 4);
   bw.das = c.take<float>(n * 4);
+  bw.dbs = general ? c.take<float>(k * 4) : nullptr;
   w.bf = c.take<float>(T * M * 4);
   w.bb = c.take<float>(T * M * 4);
   w.cf = c.take<float>(T * M * 4);
@@ -104,9 +109,11 @@ BackwardWorkspace carve_backward(void* ws, uint64_t n, uint32_t m, size_t* total
   w.gcf = c.take<float>(G * M * 4);
   w.gcb = c.take<float>(G * M * 4);
   w.ganch = c.take<float2>(G * 8);
+  w.tsplit = general ? c.take<uint2>((T + 1) * 8) : nullptr;
   if (m <= kRouteMaxCols) {
-    w.t0 = c.take<float>(n * m * 4);
-    w.t1 = c.take<float>(n * m * 4);
+    const uint64_t rmax = std::max(n, rows_x);
+    w.t0 = c.take<float>(rmax * m * 4);
+    w.t1 = c.take<float>(rmax * m * 4);
   }
   if (total) *total = (c.off + 255) & ~size_t(255);
   return bw;
@@ -135,7 +142,8 @@ extern "C" size_t laplex_workspace_bytes(int op, uint64_t n, uint64_t k, uint32_
     case LAPLEX_OP_PHASED: carve_apply(nullptr, n, n, n, m, Variant::Phased, false, &total); return total;
     case LAPLEX_OP_GENERAL: carve_apply(nullptr, k, n, n + k, m, Variant::Sym, true, &total); return total;
     case LAPLEX_OP_PHASED_GENERAL: carve_apply(nullptr, k, n, n + k, m, Variant::Phased, true, &total); return total;
-    case LAPLEX_OP_SYM_BACKWARD: carve_backward(nullptr, n, m, &total); return total;
+    case LAPLEX_OP_SYM_BACKWARD: carve_backward(nullptr, n, 0, m, false, &total); return total;
+    case LAPLEX_OP_GENERAL_BACKWARD: carve_backward(nullptr, n, k, m, true, &total); return total;
     default: return 0;
   }
 }
@@ -217,7 +225,7 @@ extern "C" laplex_status laplex_backward_sym(const float* a_sorted, const uint32
   if (!g || !da) return LAPLEX_ERR_NULL;
   if (misaligned(g, 4) || misaligned(da, 4) || (route && misaligned(route, 256))) return LAPLEX_ERR_ALIGN;
   size_t need = 0;
-  carve_backward(nullptr, n, m, &need);
+  carve_backward(nullptr, n, 0, m, false, &need);
   if (ws_bytes < need) return LAPLEX_ERR_WORKSPACE;
   const size_t xb = n * (size_t)m * 4, vb = n * 4, rb = route ? route_bytes(n) : 0;
   for (const void* out : {static_cast<const void*>(dx), static_cast<const void*>(da)}) {
@@ -227,10 +235,60 @@ extern "C" laplex_status laplex_backward_sym(const float* a_sorted, const uint32
       return LAPLEX_ERR_OVERLAP;
   }
   if (overlaps(dx, xb, da, vb)) return LAPLEX_ERR_OVERLAP;
-  const BackwardWorkspace bw = carve_backward(ws, n, m, nullptr);
+  const BackwardWorkspace bw = carve_backward(ws, n, 0, m, false, nullptr);
   SortRoute r{};
   if (route) r = carve_route(route, n);
   return from_hip(backward_sym(bw, a_sorted, perm, route ? &r : nullptr, n, m, x, g, dx, da, stream));
+}
+
+extern "C" laplex_status laplex_backward_general(const float* a_sorted, const uint32_t* perm_a, const void* route_a, uint64_t n,
+                                                 const float* b_sorted, const uint32_t* perm_b, const void* route_b, uint64_t k,
+                                                 uint32_t m, const float* x, const float* g, float* dx, float* da, float* db,
+                                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (m == 0 || (n == 0 && k == 0)) return LAPLEX_OK;
+  if (n > kMaxLen || k > kMaxLen || m > kMaxCols) return LAPLEX_ERR_SIZE;
+  const size_t xb = k * (size_t)m * 4, gb = n * (size_t)m * 4, nb = n * 4, kb = k * 4;
+  if (n == 0 || k == 0) {
+    // no pairs: every gradient is zero (dx and db when n == 0, da when k == 0)
+    if (n == 0) {
+      if (!dx || !db) return LAPLEX_ERR_NULL;
+      if (misaligned(dx, 4) || misaligned(db, 4)) return LAPLEX_ERR_ALIGN;
+      if (overlaps(dx, xb, db, kb)) return LAPLEX_ERR_OVERLAP;
+      hipError_t e = fill_zero_u32(dx, k * (uint64_t)m, stream);
+      if (e == hipSuccess) e = fill_zero_u32(db, k, stream);
+      return from_hip(e);
+    }
+    if (!da) return LAPLEX_ERR_NULL;
+    if (misaligned(da, 4)) return LAPLEX_ERR_ALIGN;
+    return from_hip(fill_zero_u32(da, n, stream));
+  }
+  if (!a_sorted || !perm_a || !b_sorted || !perm_b || !x || !g || !dx || !da || !db || !ws) return LAPLEX_ERR_NULL;
+  if (misaligned(a_sorted, 4) || misaligned(perm_a, 4) || misaligned(b_sorted, 4) || misaligned(perm_b, 4) ||
+      misaligned(x, 4) || misaligned(g, 4) || misaligned(dx, 4) || misaligned(da, 4) || misaligned(db, 4) ||
+      misaligned(ws, 256) || (route_a && misaligned(route_a, 256)) || (route_b && misaligned(route_b, 256)))
+    return LAPLEX_ERR_ALIGN;
+  size_t need = 0;
+  carve_backward(nullptr, n, k, m, true, &need);
+  if (ws_bytes < need) return LAPLEX_ERR_WORKSPACE;
+  const size_t rab = route_a ? route_bytes(n) : 0, rbb = route_b ? route_bytes(k) : 0;
+  const void* outs[3] = {dx, da, db};
+  const size_t outb[3] = {xb, nb, kb};
+  for (int o = 0; o < 3; ++o) {
+    const void* p = outs[o];
+    const size_t pb = outb[o];
+    if (overlaps(p, pb, x, xb) || overlaps(p, pb, g, gb) || overlaps(p, pb, a_sorted, nb) || overlaps(p, pb, perm_a, nb) ||
+        overlaps(p, pb, b_sorted, kb) || overlaps(p, pb, perm_b, kb) || overlaps(p, pb, ws, ws_bytes) ||
+        overlaps(p, pb, route_a, rab) || overlaps(p, pb, route_b, rbb))
+      return LAPLEX_ERR_OVERLAP;
+    for (int q = o + 1; q < 3; ++q)
+      if (overlaps(p, pb, outs[q], outb[q])) return LAPLEX_ERR_OVERLAP;
+  }
+  const BackwardWorkspace bw = carve_backward(ws, n, k, m, true, nullptr);
+  SortRoute ra{}, rb{};
+  if (route_a) ra = carve_route(route_a, n);
+  if (route_b) rb = carve_route(route_b, k);
+  return from_hip(backward_general(bw, a_sorted, perm_a, route_a ? &ra : nullptr, n, b_sorted, perm_b, route_b ? &rb : nullptr,
+                                   k, m, x, g, dx, da, db, stream));
 }
 
 extern "C" laplex_status laplex_matvec_general(const float* a_sorted, const uint32_t* perm_a, const void* route_a, uint64_t n,

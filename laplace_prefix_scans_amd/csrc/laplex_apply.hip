@@ -1375,4 +1375,295 @@ hipError_t apply_general(const ApplyWorkspace& w, Variant var, const float* a_s,
 #undef LAPLEX_GEN
 }
 
+
+// ---------------------------------------------------------------- general backward
+// Backward of y = K(a, b) x with K_ij = exp(-|a_i - b_j|) (rows a, n; columns
+// b, k) for the upstream gradient g = dL/dy:
+//     dx_j = sum_i K_ij g_i                                  (K^T g),
+//     da_i = -sum_c g_ic sum_j sign(a_i - b_j) K_ij x_jc,
+//     db_j = -sum_c x_jc sum_i sign(b_j - a_i) K_ij g_ic       (sign(0) = 0).
+// All three come from one pass over the merge of sorted a and sorted b (b first
+// on equal anchors), with x injected at b elements and g at a elements.  With
+// F, U the strict forward / inclusive backward scans and F0, U0 the same under
+// the tie decay, S = (F - U) - (F0 - U0) keeps exactly the anchors strictly
+// below minus those strictly above, at either kind of element (at an a element
+// the tied b's all lie before it, at a b element the tied a's all lie after).
+// So at every element A = sum_c g S(x) + x S(g) (one of the two is zero there)
+// gives da at a elements and db at b elements, and dx_j = F + U of g at b_j.
+// Summary columns (M = 4m) as in the symmetric backward: [0, m) x, [m, 2m) g
+// with the kernel's decay, [2m, 4m) the same with the tie decay.
+template <int C>
+__global__ __launch_bounds__(bwd_block(C)) void k_gbwd_reduce(const float* __restrict__ a_s, uint64_t n,
+                                                               const float* __restrict__ b_s, uint64_t k,
+                                                               const float* __restrict__ xbs, const float* __restrict__ gas,
+                                                               uint32_t m, uint64_t T, float* __restrict__ bf,
+                                                               float* __restrict__ bb, float2* __restrict__ tanch,
+                                                               uint2* __restrict__ tsplit) {
+  constexpr int CC = 4 * C;
+  constexpr int BLOCK = bwd_block(C);
+  constexpr int NW = BLOCK / kWave;
+  constexpr int P = BLOCK * bwd_items(C);
+  __shared__ float s_red[2 * NW * CC];
+  __shared__ uint64_t s_split[4];
+  const uint32_t M = 4 * m;
+  const int tid = threadIdx.x;
+  const uint64_t tile = blockIdx.x;
+  const uint64_t N = n + k;
+  const uint64_t d0 = tile * P, d1 = std::min<uint64_t>(N, d0 + P);
+  if (tid == 0) {
+    s_split[0] = merge_split(a_s, n, b_s, k, d0);
+    s_split[1] = d0 - s_split[0];
+  } else if (tid == kWave) {
+    s_split[2] = merge_split(a_s, n, b_s, k, d1);
+    s_split[3] = d1 - s_split[2];
+  }
+  __syncthreads();
+  const uint64_t i0 = s_split[0], j0 = s_split[1], i1 = s_split[2], j1 = s_split[3];
+  float s_first = INFINITY, s_last = -INFINITY;
+  if (i0 < i1) {
+    s_first = a_s[i0];
+    s_last = a_s[i1 - 1];
+  }
+  if (j0 < j1) {
+    s_first = fminf(s_first, b_s[j0]);
+    s_last = fmaxf(s_last, b_s[j1 - 1]);
+  }
+  if (tid == 0) {
+    tanch[tile] = make_float2(s_first, s_last);
+    tsplit[tile] = make_uint2((uint32_t)i0, (uint32_t)j0);
+    if (tile + 1 == T) tsplit[T] = make_uint2((uint32_t)n, (uint32_t)k);
+  }
+  for (uint32_t cc = 0; cc < m / C; ++cc) {
+    float sf[CC], sb[CC];
+#pragma unroll
+    for (int j = 0; j < CC; ++j) sf[j] = sb[j] = 0.f;
+    // x at the b elements of the tile: columns [0, C) and [2C, 3C)
+    for (uint64_t jb = j0 + tid; jb < j1; jb += BLOCK) {
+      const float s = b_s[jb];
+      const float wf = decay(s - s_last), wb = decay(s_first - s);
+      const float tf = decay_m<true>(s - s_last), tb = decay_m<true>(s_first - s);
+      const float* xr = xbs + jb * m + cc * C;
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        const float v = xr[j];
+        sf[j] = fmaf(wf, v, sf[j]);
+        sb[j] = fmaf(wb, v, sb[j]);
+        sf[2 * C + j] = fmaf(tf, v, sf[2 * C + j]);
+        sb[2 * C + j] = fmaf(tb, v, sb[2 * C + j]);
+      }
+    }
+    // g at the a elements: columns [C, 2C) and [3C, 4C)
+    for (uint64_t ia = i0 + tid; ia < i1; ia += BLOCK) {
+      const float s = a_s[ia];
+      const float wf = decay(s - s_last), wb = decay(s_first - s);
+      const float tf = decay_m<true>(s - s_last), tb = decay_m<true>(s_first - s);
+      const float* gr = gas + ia * m + cc * C;
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        const float v = gr[j];
+        sf[C + j] = fmaf(wf, v, sf[C + j]);
+        sb[C + j] = fmaf(wb, v, sb[C + j]);
+        sf[3 * C + j] = fmaf(tf, v, sf[3 * C + j]);
+        sb[3 * C + j] = fmaf(tb, v, sb[3 * C + j]);
+      }
+    }
+    int writer = 0;
+    block_sum2<CC, NW>(sf, sb, s_red, writer);
+    if (writer) {
+      float f = 0.f, b = 0.f;
+      for (int w = 0; w < NW; ++w) {
+        f += s_red[(0 * NW + w) * CC + tid];
+        b += s_red[(1 * NW + w) * CC + tid];
+      }
+      const uint32_t col = bwdcol<C>(m, cc, tid);
+      bf[tile * M + col] = f;
+      bb[tile * M + col] = b;
+    }
+    __syncthreads();
+  }
+}
+
+// Merged tile scans -> dx (sorted-b order), da (sorted-a order), db (sorted-b
+// order).
+template <int C>
+__global__ __launch_bounds__(bwd_block(C)) void k_gbwd_apply(const float* __restrict__ a_s, uint64_t n,
+                                                              const float* __restrict__ b_s, uint64_t k,
+                                                              const float* __restrict__ xbs, const float* __restrict__ gas,
+                                                              uint32_t m, uint64_t T, const float* __restrict__ cfw,
+                                                              const float* __restrict__ cbw, const float2* __restrict__ tanch,
+                                                              const uint2* __restrict__ tsplit, float* __restrict__ dxs,
+                                                              float* __restrict__ das, float* __restrict__ dbs) {
+  constexpr int CC = 2 * C;  // columns of one scan (x then g)
+  constexpr int E = bwd_items(C);
+  constexpr int BLOCK = bwd_block(C);
+  constexpr int NW = BLOCK / kWave;
+  constexpr int P = BLOCK * E;
+  __shared__ float s_a[P], s_b[P];
+  __shared__ float s_wf[NW * CC], s_wb[NW * CC], s_wfs[NW], s_wbs[NW];
+  const uint32_t M = 4 * m;
+  const int tid = threadIdx.x;
+  const uint64_t tile = blockIdx.x;
+  const uint2 sp0 = tsplit[tile], sp1 = tsplit[tile + 1];
+  const uint32_t na = std::min<uint32_t>(sp1.x - sp0.x, P), nb = std::min<uint32_t>(sp1.y - sp0.y, P - na);
+  for (uint32_t i = tid; i < na; i += BLOCK) s_a[i] = a_s[(uint64_t)sp0.x + i];
+  for (uint32_t i = tid; i < nb; i += BLOCK) s_b[i] = b_s[(uint64_t)sp0.y + i];
+  __syncthreads();
+  const float s_max = fmaxf(a_s[n - 1], b_s[k - 1]);
+  // this thread's E merged elements (merge path inside the tile)
+  const uint32_t tot = na + nb;
+  const uint32_t dd = std::min<uint32_t>(tot, (uint32_t)tid * E);
+  uint32_t lo = dd > nb ? dd - nb : 0u, hi = std::min(dd, na);
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (s_a[mid] < s_b[dd - 1 - mid])
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  uint32_t ii = lo, jj = dd - lo;
+  float ae[E];
+  int kind[E];  // 0 pad, 1 a element (g injected, da out), 2 b element (x injected, dx and db out)
+  uint32_t idx[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool real = (uint32_t)tid * E + e < tot;
+    const float va = ii < na ? s_a[ii] : INFINITY;
+    const float vb = jj < nb ? s_b[jj] : INFINITY;
+    const bool take_b = real && (jj < nb) && (vb <= va);
+    const bool take_a = real && !take_b;
+    ae[e] = take_b ? vb : (take_a ? va : s_max);
+    kind[e] = take_b ? 2 : (take_a ? 1 : 0);
+    idx[e] = take_b ? sp0.y + jj : (take_a ? sp0.x + ii : 0u);
+    jj += take_b ? 1u : 0u;
+    ii += take_a ? 1u : 0u;
+  }
+  const float2 ta = tanch[tile];
+  const float sf = tile > 0 ? tanch[tile - 1].y : ta.x;
+  const float sb = tile + 1 < T ? tanch[tile + 1].x : ta.y;
+  float acc[E], acc0[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = acc0[e] = 0.f;
+  for (uint32_t cc = 0; cc < m / C; ++cc) {
+    float v[E][CC];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        v[e][j] = kind[e] == 2 ? xbs[(uint64_t)idx[e] * m + cc * C + j] : 0.f;
+        v[e][C + j] = kind[e] == 1 ? gas[(uint64_t)idx[e] * m + cc * C + j] : 0.f;
+      }
+    {
+      float ct_f[CC], ct_b[CC];
+#pragma unroll
+      for (int j = 0; j < CC; ++j) {
+        ct_f[j] = cfw[tile * M + bwdcol<C>(m, cc, CC + j)];
+        ct_b[j] = cbw[tile * M + bwdcol<C>(m, cc, CC + j)];
+      }
+      float F0[E][CC], U0[E][CC];
+      tile_scan_fu<E, CC, NW, true>(ae, v, ct_f, sf, ct_b, sb, s_wf, s_wfs, s_wb, s_wbs, F0, U0);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+          acc0[e] = fmaf(v[e][C + j], F0[e][j] - U0[e][j], acc0[e]);
+          acc0[e] = fmaf(v[e][j], F0[e][C + j] - U0[e][C + j], acc0[e]);
+        }
+    }
+    __syncthreads();  // the second scan reuses the wave summaries
+    {
+      float ce_f[CC], ce_b[CC];
+#pragma unroll
+      for (int j = 0; j < CC; ++j) {
+        ce_f[j] = cfw[tile * M + bwdcol<C>(m, cc, j)];
+        ce_b[j] = cbw[tile * M + bwdcol<C>(m, cc, j)];
+      }
+      float F[E][CC], U[E][CC];
+      tile_scan_fu<E, CC, NW, false>(ae, v, ce_f, sf, ce_b, sb, s_wf, s_wfs, s_wb, s_wbs, F, U);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+          acc[e] = fmaf(v[e][C + j], F[e][j] - U[e][j], acc[e]);
+          acc[e] = fmaf(v[e][j], F[e][C + j] - U[e][C + j], acc[e]);
+        }
+        if (kind[e] == 2) {
+          float* dr = dxs + (uint64_t)idx[e] * m + cc * C;
+#pragma unroll
+          for (int j = 0; j < C; ++j) dr[j] = F[e][C + j] + U[e][C + j];
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (kind[e] == 1) das[idx[e]] = acc0[e] - acc[e];
+    if (kind[e] == 2) dbs[idx[e]] = acc0[e] - acc[e];
+  }
+}
+
+template <int C>
+static hipError_t run_bwd_general(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm_a,
+                                  const SortRoute* route_a, uint64_t n, const float* b_s, const uint32_t* perm_b,
+                                  const SortRoute* route_b, uint64_t k, uint32_t m, const float* x, const float* g, float* dx,
+                                  float* da, float* db, hipStream_t s) {
+  const ApplyWorkspace& w = bw.w;
+  constexpr int P = bwd_tile(C);
+  const uint64_t T = (n + k + P - 1) / P;
+  const uint32_t M = 4 * m;
+  const dim3 grid((unsigned)T), block(bwd_block(C));
+  const bool routed_a = route_a != nullptr && m <= kRouteMaxCols;
+  const bool routed_b = route_b != nullptr && m <= kRouteMaxCols;
+  hipError_t e;
+  // x into sorted-b order, g into sorted-a order
+  if (routed_b) {
+    if ((e = route_forward(*route_b, k, m, x, w.xs, w.t0, w.t1, s)) != hipSuccess) return e;
+  } else {
+    LAPLEX_LAUNCH("k_gather_rows", k, s, k_gather_rows<<<rows_grid(k), 256, 0, s>>>(x, perm_b, nullptr, k, m, w.xs, nullptr));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (routed_a) {
+    if ((e = route_forward(*route_a, n, m, g, bw.gs, w.t0, w.t1, s)) != hipSuccess) return e;
+  } else {
+    LAPLEX_LAUNCH("k_gather_rows", n, s, k_gather_rows<<<rows_grid(n), 256, 0, s>>>(g, perm_a, nullptr, n, m, bw.gs, nullptr));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  LAPLEX_LAUNCH("k_gbwd_reduce", n + k, s,
+                k_gbwd_reduce<C><<<grid, block, 0, s>>>(a_s, n, b_s, k, w.xs, bw.gs, m, T, w.bf, w.bb, w.tanch, w.tsplit));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = tile_carries(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb, w.gbf, w.gbb, w.gcf, w.gcb, w.ganch, s, 2 * m)) != hipSuccess)
+    return e;
+  LAPLEX_LAUNCH("k_gbwd_apply", n + k, s,
+                k_gbwd_apply<C><<<grid, block, 0, s>>>(a_s, n, b_s, k, w.xs, bw.gs, m, T, w.cf, w.cb, w.tanch, w.tsplit, w.zs,
+                                                       bw.das, bw.dbs));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // back to original order: dx and db along b's route, da along a's
+  if (routed_b) {
+    if ((e = route_inverse(*route_b, k, m, w.zs, dx, w.t0, w.t1, s)) != hipSuccess) return e;
+    if ((e = route_inverse(*route_b, k, 1, bw.dbs, db, w.t0, w.t1, s)) != hipSuccess) return e;
+  } else {
+    LAPLEX_LAUNCH("k_scatter_rows", k, s, k_scatter_rows<<<rows_grid(k), 256, 0, s>>>(w.zs, perm_b, k, m, dx));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    LAPLEX_LAUNCH("k_scatter_rows", k, s, k_scatter_rows<<<rows_grid(k), 256, 0, s>>>(bw.dbs, perm_b, k, 1, db));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (routed_a) return route_inverse(*route_a, n, 1, bw.das, da, w.t0, w.t1, s);
+  LAPLEX_LAUNCH("k_scatter_rows", n, s, k_scatter_rows<<<rows_grid(n), 256, 0, s>>>(bw.das, perm_a, n, 1, da));
+  return hipGetLastError();
+}
+
+hipError_t backward_general(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm_a, const SortRoute* route_a,
+                            uint64_t n, const float* b_s, const uint32_t* perm_b, const SortRoute* route_b, uint64_t k,
+                            uint32_t m, const float* x, const float* g, float* dx, float* da, float* db, hipStream_t s) {
+#define LAPLEX_GBWD(CW) \
+  return run_bwd_general<CW>(bw, a_s, perm_a, route_a, n, b_s, perm_b, route_b, k, m, x, g, dx, da, db, s)
+  switch (column_chunk(m)) {
+    case 8: LAPLEX_GBWD(8);
+    case 4: LAPLEX_GBWD(4);
+    case 2: LAPLEX_GBWD(2);
+    default: LAPLEX_GBWD(1);
+  }
+#undef LAPLEX_GBWD
+}
+
 }  // namespace laplex

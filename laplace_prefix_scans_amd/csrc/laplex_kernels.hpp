@@ -112,11 +112,20 @@ hipError_t apply_general(const ApplyWorkspace& w, Variant var, const float* a_s,
 // the kernel's decay and with the tie decay); zs holds dx in sorted order.
 struct BackwardWorkspace {
   ApplyWorkspace w;
-  float* gs;   // upstream gradient gathered into sorted order (n x m)
-  float* das;  // anchor gradient in sorted order (n)
+  float* gs;   // upstream gradient gathered into sorted(-a) order (n x m)
+  float* das;  // anchor gradient in sorted(-a) order (n)
+  float* dbs;  // column-anchor gradient in sorted-b order (k; general only)
 };
 hipError_t backward_sym(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm, const SortRoute* route,
                         uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da, hipStream_t s);
+
+// Backward of the general operator (rows a, n; columns b, k): dx = K^T g
+// (k x m), da (n), db (k).  One scan over the merge of a and b with summary
+// width M = 4m; xs holds x in sorted-b order, gs g in sorted-a order, zs dx in
+// sorted-b order.  Requires n, k >= 1.
+hipError_t backward_general(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm_a, const SortRoute* route_a,
+                            uint64_t n, const float* b_s, const uint32_t* perm_b, const SortRoute* route_b, uint64_t k,
+                            uint32_t m, const float* x, const float* g, float* dx, float* da, float* db, hipStream_t s);
 
 // tile count and summary width of an apply
 inline uint64_t apply_tiles(uint64_t len, uint32_t m, Variant var) {

@@ -44,7 +44,9 @@ def test_workspace_sizes(L):
     assert lp.laplex_workspace_bytes(lp.LAPLEX_OP_GENERAL, 1 << 24, 1 << 16, 1) > 0
     assert lp.laplex_workspace_bytes(lp.LAPLEX_OP_SORT, 1 << 32) == 0  # n out of range
     assert lp.laplex_workspace_bytes(99, 10) == 0
-    for op in range(5):
+    assert lp.laplex_workspace_bytes(lp.LAPLEX_OP_GENERAL_BACKWARD, 1 << 20, 1 << 10, 2) > \
+        lp.laplex_workspace_bytes(lp.LAPLEX_OP_GENERAL, 1 << 20, 1 << 10, 2)
+    for op in range(7):
         a = lp.laplex_workspace_bytes(op, 4096, 100, 1)
         b = lp.laplex_workspace_bytes(op, 1 << 22, 1 << 20, 1)
         assert a % 256 == 0 and b % 256 == 0 and b >= a
@@ -82,6 +84,23 @@ def test_host_argument_errors(L):
     assert L.laplex_matvec_general(A, vp(0x300000), None, 100, None, None, None, 50, 1, vp(0x500000), vp(0x600000), W, need, None) == NULL
     assert L.laplex_matvec_phased(A, vp(0x300000), None, None, 100, None, None, None, None, 0, 1, vp(0x500000),
                                   vp(0x600000), W, need, None) == NULL
+    # general backward: no-ops, NULL, workspace, overlap (dx on top of g)
+    GB = L.laplex_backward_general
+    assert GB(None, None, None, 0, None, None, None, 0, 1, None, None, None, None, None, None, 0, None) == OK
+    assert GB(A, B, None, 10, A, B, None, 5, 0, A, A, B, B, B, W, 0, None) == OK
+    assert GB(A, B, None, 10, None, None, None, 0, 1, None, None, None, None, None, None, 0, None) == NULL  # k = 0 needs da
+    assert GB(A, B, None, 10, A, B, None, 5, 1, None, A, B, B, B, W, 1 << 30, None) == NULL
+    assert GB(A, B, None, 1 << 32, A, B, None, 5, 1, A, A, B, B, B, W, 1 << 40, None) == SIZE
+    need = L.laplex_workspace_bytes(6, 1000, 300, 1)
+    args = [A, vp(0x300000), None, 1000, vp(0x500000), vp(0x600000), None, 300, 1, vp(0x700000), vp(0x800000),
+            vp(0x900000), vp(0xA00000), vp(0xB00000), vp(0x10000000)]
+    assert GB(*args, 64, None) == WS
+    bad = list(args)
+    bad[11] = vp(0x800100)  # dx inside g
+    assert GB(*bad, need, None) == OVERLAP
+    bad = list(args)
+    bad[12] = vp(0xA00002)  # da misaligned
+    assert GB(*bad, need, None) == ALIGN
     # route: too small, misaligned, overlapping
     assert L.laplex_sort_anchors(A, 1000, B, vp(0x300000), vp(0x20000000), 16, vp(0x10000000), 1 << 30, None) == WS
     assert L.laplex_sort_anchors(A, 1000, B, vp(0x300000), vp(0x20000010), 1 << 20, vp(0x10000000), 1 << 30, None) == ALIGN
