@@ -10,6 +10,9 @@ Two parts, both float64:
   Learnable Laplace Kernels" (technical summary, section 2.1 "The Operator"),
   ``y_i = sum_j exp(-|a_i - b_j|) [cos(phi_i - psi_j)] x_j``, written out with
   NumPy in row chunks and no sort.  O(n k m); for small sizes and spot rows.
+* ``gram_dense`` / ``gram_block``: the weighted Gram matrix M = A diag(D) A^T
+  of section 2.2 ("Gram operators") by its plain definition, whole or a block
+  of entries.
 * ``sym_apply`` / ``general_apply`` / ``phased_apply`` / ``stable_argsort``:
   the sequential scan algebra of section 2.2 ("Exact Scan Algebra") in plain C
   (``laplex_oracle.c``), O(n log n).
@@ -220,4 +223,5 @@ def dense_rows_c(rows, a, x, b=None, phi=None, psi=None, lib=None):
     return y, env
 
 
-from .dense import dense_apply, dense_backward, dense_envelope, dense_rows, normwise_error  # noqa: E402,F401
+from .dense import (dense_apply, dense_backward, dense_envelope, dense_rows, gram_block, gram_dense,  # noqa: E402,F401
+                    normwise_error)

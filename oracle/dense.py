@@ -123,3 +123,38 @@ def dense_backward(a, x, g, b=None):
     if sym:
         return dx, da + db
     return dx, da, db
+
+
+# ----------------------------------------------------------------------------- weighted Gram
+def _gram_combine(ar_w, ac_w, d):
+    """sum_j ar_w[p, j] d_j ac_w[q, j] for one chunk of input anchors."""
+    return (ar_w * d[None, :]) @ ac_w.T
+
+
+def gram_block(rows, cols, a, b, D, absolute: bool = False, col_chunk: int = 1 << 14) -> np.ndarray:
+    """Entries M[rows][:, cols] of the weighted Gram matrix M = A diag(D) A^T,
+    A = LAPLEX(a, b) (technical summary, section 2.2, Gram operators), by the
+    plain definition  M_pq = sum_j D_j exp(-|a_p - b_j|) exp(-|a_q - b_j|),
+    O(|rows| |cols| k), float64.  ``absolute`` uses |D| (the envelope that
+    scales the normwise error)."""
+    rows = np.asarray(rows, np.int64)
+    cols = np.asarray(cols, np.int64)
+    a = np.asarray(a).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    D = np.asarray(D, np.float64).ravel()
+    if absolute:
+        D = np.abs(D)
+    ar = a[rows].astype(np.float64)
+    ac = a[cols].astype(np.float64)
+    out = np.zeros((rows.size, cols.size), np.float64)
+    for lo in range(0, b.size, col_chunk):
+        hi = min(b.size, lo + col_chunk)
+        out += _gram_combine(_weights(ar, b[lo:hi]), _weights(ac, b[lo:hi]), D[lo:hi])
+    return out
+
+
+def gram_dense(a, b, D, absolute: bool = False) -> np.ndarray:
+    """The whole n x n weighted Gram matrix by the plain definition (small n)."""
+    n = np.asarray(a).size
+    idx = np.arange(n)
+    return gram_block(idx, idx, a, b, D, absolute=absolute)

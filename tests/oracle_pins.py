@@ -511,6 +511,90 @@ def pin_backward_brute_force(lib):
         _close(db, dbd, 1e-12, "general db brute force")
 
 
+# ----------------------------------------------------------------------------- weighted Gram
+def _gram_golden_cases():
+    with open(os.path.join(GOLDEN, "gram_examples.json")) as f:
+        return json.load(f)["cases"]
+
+
+def pin_gram_hand_examples(lib):
+    """Weighted Gram matrices worked out by hand from M = A diag(D) A^T."""
+    for case in _gram_golden_cases():
+        a = np.array(case["a"], np.float32)
+        b = np.array(case["b"], np.float32)
+        D = np.array(case["D"], np.float32)
+        want = np.array([[sum(c * math.exp(-d) for c, d in ent) for ent in row] for row in case["m_terms"]])
+        _close(odense.gram_dense(a, b, D), want, 1e-15, "gram " + case["name"])
+
+
+def pin_gram_scan_products(lib):
+    """M v = A (D * (A^T v)), with A and A^T applied by the scan oracle (a
+    different computation: sort, interval sums, recurrences), for weights of
+    both signs, ties between a and b, and a block of rows and columns."""
+    r = _rng(70)
+    for ties in (False, True):
+        n, k = 300, 500
+        a = r.uniform(0, 60, n).astype(np.float32)
+        b = r.uniform(0, 60, k).astype(np.float32)
+        if ties:
+            a, b = np.round(a), np.round(b)
+        D = r.standard_normal(k).astype(np.float32)
+        v = r.standard_normal((n, 2))
+        M = odense.gram_dense(a, b, D)
+        atv = oracle.general_apply(b, a, v.astype(np.float32), lib=lib)
+        want = oracle.general_apply(a, b, (D[:, None] * atv).astype(np.float64).astype(np.float32), lib=lib)
+        # the fp32 round trip of D * A^T v above is the only rounding: compare at its scale
+        env = oracle.general_apply(a, b, np.abs(D[:, None] * atv).astype(np.float32), lib=lib)
+        err = float(np.max(np.abs(M @ v.astype(np.float32).astype(np.float64) - want)) / np.max(env))
+        assert err <= 1e-6, "gram M v vs A D A^T v (ties=%s): %.3e" % (ties, err)
+        rows, cols = np.array([0, 7, 299]), np.array([3, 0, 150, 298])
+        _close(odense.gram_block(rows, cols, a, b, D), M[np.ix_(rows, cols)], 1e-14, "gram block")
+
+
+def pin_gram_kms(lib):
+    """a = b = equispaced (spacing h), D = 1: M = K^2 with K the Kac-Murdock-
+    Szego matrix, so its closed-form tridiagonal inverse applied twice gives I."""
+    for h in (0.25, 1.0):
+        n = 200
+        a = (np.arange(n) * h).astype(np.float32)
+        M = odense.gram_dense(a, a, np.ones(n, np.float32))
+        back = _kms_inverse_apply(h, _kms_inverse_apply(h, M))
+        _close(back, np.eye(n), 1e-9, "gram KMS h=%g" % h)
+
+
+def pin_gram_continuum(lib):
+    """Input anchors on a fine grid over [-L, L] with trapezoid weights: M_pq
+    tends to the integral of exp(-|a_p - t| - |a_q - t|) dt over the line,
+    which is (1 + |a_p - a_q|) exp(-|a_p - a_q|)."""
+    h, L = 2.0 ** -8, 24.0
+    t = np.arange(-L, L + h / 2, h).astype(np.float32)
+    w = np.full(t.size, h, np.float32)
+    w[0] = w[-1] = h / 2
+    r = _rng(71)
+    a = (np.round(r.uniform(-4, 4, 40) / h) * h).astype(np.float32)  # on grid nodes: kinks fall on nodes
+    M = odense.gram_dense(a, t, w)
+    d = np.abs(a[:, None].astype(np.float64) - a[None, :])
+    _close(M, (1.0 + d) * np.exp(-d), 1e-5, "gram continuum limit")
+
+
+def pin_gram_symmetric_psd(lib):
+    """Nonnegative weights: M is symmetric positive semidefinite (a Gram
+    matrix); with some weights negative it stays symmetric."""
+    r = _rng(72)
+    a = r.uniform(0, 30, 150).astype(np.float32)
+    b = r.uniform(0, 30, 90).astype(np.float32)
+    M = odense.gram_dense(a, b, r.uniform(0, 2, 90).astype(np.float32))
+    _close(M, M.T, 1e-15, "gram symmetry")
+    ev = np.linalg.eigvalsh((M + M.T) / 2)
+    assert ev.min() >= -1e-12 * ev.max(), "gram not PSD: %.3e" % ev.min()
+    # rank at most k
+    k = 20
+    b2 = r.uniform(0, 30, k).astype(np.float32)
+    M2 = odense.gram_dense(a, b2, r.uniform(0.5, 2, k).astype(np.float32))
+    sv = np.linalg.svd(M2, compute_uv=False)
+    assert sv[k] <= 1e-12 * sv[0], "gram rank exceeds k"
+
+
 ALL_PINS = [
     pin_sort_definition,
     pin_sort_rejects_nonfinite,
@@ -529,4 +613,9 @@ ALL_PINS = [
     pin_dense_rows_c,
     pin_backward_finite_differences,
     pin_backward_brute_force,
+    pin_gram_hand_examples,
+    pin_gram_scan_products,
+    pin_gram_kms,
+    pin_gram_continuum,
+    pin_gram_symmetric_psd,
 ]

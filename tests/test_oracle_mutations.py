@@ -108,3 +108,20 @@ def test_dense_mutant_is_caught(name, monkeypatch, oracle_lib):
     monkeypatch.setattr(odense, "_weights", DENSE_MUTANTS[name])
     failed = _any_pin_fails(oracle_lib)
     assert failed, "planted mistake %s in the dense oracle passed every pin" % name
+
+
+GRAM_MUTANTS = {
+    "no_weights": lambda ar, ac, d: ar @ ac.T,
+    "weights_twice": lambda ar, ac, d: (ar * d[None, :]) @ (ac * d[None, :]).T,
+    "abs_weights": lambda ar, ac, d: (ar * np.abs(d)[None, :]) @ ac.T,
+    "weights_reversed": lambda ar, ac, d: (ar * d[None, ::-1]) @ ac.T,
+    "weights_shifted": lambda ar, ac, d: (ar * np.roll(d, 1)[None, :]) @ ac.T,
+    "squared_entries": lambda ar, ac, d: (ar * ar * d[None, :]) @ ac.T,
+}
+
+
+@pytest.mark.parametrize("name", sorted(GRAM_MUTANTS))
+def test_gram_mutant_is_caught(name, monkeypatch, oracle_lib):
+    monkeypatch.setattr(odense, "_gram_combine", GRAM_MUTANTS[name])
+    failed = _any_pin_fails(oracle_lib)
+    assert failed, "planted mistake %s in the Gram oracle passed every pin" % name
