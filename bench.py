@@ -73,6 +73,10 @@ def kernel_bytes(name: str, units: int, m: int, k: int = 0) -> float:
         "k_bwd_apply": 8.0 + 12.0 * m,           # sorted anchors, x and g rows in; dx rows and da out
         "k_scatter_rows": 4.0 + 8.0 * m,         # perm, sorted rows in, rows out (random)
         "k_gbwd_reduce": 4.0 + 4.0 * m,          # merged anchors, x rows (at b) and g rows (at a)
+        "k_gram_fill": 4.0,                      # per entry of M: written once (row/column families are O(n))
+        "k_gram_families": 8.0,                  # merged anchors and weights in; families out at a (20 B per a)
+        "k_gram_double": 8.0,                    # anchors in and doubled anchors out
+        "k_gram_dprefix": 24.0,                  # weights (random through perm_b), sorted weights, float64 prefix
     }
     for w in (1, 2, 3, 4):
         table["k_route_fwd_w%d" % w] = route + 8.0 * w   # position, row in, row out
@@ -215,33 +219,41 @@ def cpu_baseline(workload: str, log2_sample: int):
 
     full = make_workload(workload, scale=0) if workload in ("sym4096",) else None
     n_full = {"sym4096": 4096, "sym2p20m16": 1 << 20, "gen2p24k2p16": 1 << 24, "phased3x1024x1024m8": 3 << 20,
-              "sym2p30": 1 << 30}[workload]
+              "sym2p30": 1 << 30, "gram2p16k2p16": 1 << 16}[workload]
+    if workload == "gram2p16k2p16":
+        log2_sample = min(log2_sample, 12)  # the oracle's Gram is the O(n^2 k) definition
     scale = 0
     while (n_full >> scale) > (1 << log2_sample):
         scale += 1
     w = full if full is not None else make_workload(workload, scale=scale)
     lib = oracle.load()
+    from threadpoolctl import threadpool_limits
     t0 = time.perf_counter()
     reps = 0
-    while True:
-        if w.kind == "sym":
-            oracle.sym_apply(w.a, w.x, lib=lib)
-        elif w.kind == "general":
-            oracle.general_apply(w.a, w.b, w.x, lib=lib)
-        else:
-            oracle.phased_apply(w.a, w.phi, w.x, lib=lib)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0 or reps >= 1000:
-            break
-    elems = w.n * w.m * reps
+    with threadpool_limits(limits=1):  # one core for every leg (NumPy's BLAS in the Gram one)
+        while True:
+            if w.kind == "sym":
+                oracle.sym_apply(w.a, w.x, lib=lib)
+            elif w.kind == "general":
+                oracle.general_apply(w.a, w.b, w.x, lib=lib)
+            elif w.kind == "gram":
+                oracle.gram_dense(w.a, w.b, w.D)
+            else:
+                oracle.phased_apply(w.a, w.phi, w.x, lib=lib)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= 10.0 or reps >= 1000:
+                break
+    elems = (w.n * w.n if w.kind == "gram" else w.n * w.m) * reps
+    what = ("float64 dense definition of A diag(D) A^T (NumPy, one BLAS thread)" if w.kind == "gram"
+            else "float64 C oracle incl. its sort")
     return {
         "value": elems / dt / 1e9,
         "unit": "Gelem/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": "%s scaled to n=%d m=%d%s (same distributions), %d run(s) in %.1f s, float64 C oracle incl. its sort" % (
-            workload, w.n, w.m, (" k=%d" % w.k) if w.kind == "general" else "", reps, dt),
+        "sample": "%s scaled to n=%d m=%d%s (same distributions), %d run(s) in %.1f s, %s" % (
+            workload, w.n, w.m, (" k=%d" % w.k) if w.kind in ("general", "gram") else "", reps, dt, what),
     }
 
 
@@ -331,8 +343,18 @@ def main():
     a_s = torch.empty_like(a)
     pa = torch.empty(n, dtype=torch.uint32, device=dev)
     ws_sort_a = lp.workspace(lp.LAPLEX_OP_SORT, n, device=dev)
-    y = torch.empty((n, m), dtype=torch.float32, device=dev)
-    if w.kind == "general":
+    y = torch.empty((n, m), dtype=torch.float32, device=dev) if w.kind != "gram" else None
+    if w.kind == "gram":
+        b = torch.from_numpy(w.b).to(dev)
+        Dw = torch.from_numpy(w.D).to(dev)
+        b_s = torch.empty_like(b)
+        pb = torch.empty(k, dtype=torch.uint32, device=dev)
+        rb = None
+        ws_sort_b = lp.workspace(lp.LAPLEX_OP_SORT, k, device=dev)
+        ws_apply = lp.workspace(lp.LAPLEX_OP_GRAM, n, k, 1, device=dev)
+        Mg = torch.empty((n, n), dtype=torch.float32, device=dev)
+        ra = None
+    elif w.kind == "general":
         b = torch.from_numpy(w.b).to(dev)
         b_s = torch.empty_like(b)
         pb = torch.empty(k, dtype=torch.uint32, device=dev)
@@ -348,7 +370,10 @@ def main():
 
     def step():
         lp.laplex_sort_anchors(a, a_s, pa, route=ra, ws=ws_sort_a)
-        if w.kind == "general":
+        if w.kind == "gram":
+            lp.laplex_sort_anchors(b, b_s, pb, ws=ws_sort_b)
+            lp.laplex_gram_weighted(a_s, pa, b_s, pb, Dw, M=Mg, ws=ws_apply)
+        elif w.kind == "general":
             lp.laplex_sort_anchors(b, b_s, pb, route=rb, ws=ws_sort_b)
             lp.laplex_matvec_general(a_s, pa, b_s, pb, x, y=y, ws=ws_apply, route_a=ra, route_b=rb)
         elif w.kind == "phased":
@@ -415,12 +440,13 @@ def main():
         gbps = by / (ms * 1e-3) / 1e9 if ms > 0 else None
         return {"kernel_ms": round(ms, 4), "alg_GB": round(by / 1e9, 3), "alg_GBps": round(gbps, 1) if gbps else None,
                 "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4) if gbps else None,
-                "Gelem_per_s": round(n * m / (ms * 1e-3) / 1e9, 4) if ms > 0 else None}
+                "Gelem_per_s": round(out_elems / (ms * 1e-3) / 1e9, 4) if ms > 0 else None}
     sort_names = [q for q in stats if q.startswith(("k_sort", "k_onesweep", "k_fill"))]
     apply_names = [q for q in stats if q not in sort_names]
+    out_elems = n * n if w.kind == "gram" else n * m
     line = {
         "metric": METRIC,
-        "value": round(n * m / (ms_per_step * 1e-3) / 1e9, 4),
+        "value": round(out_elems / (ms_per_step * 1e-3) / 1e9, 4),
         "unit": "Gelem/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -431,8 +457,10 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "kind": w.kind, "n": n, "m": m, "k": k if w.kind == "general" else None,
-                   "step": "sort + apply", "route": use_route, "recipe": w.recipe},
+        "config": {"workload": args.workload, "kind": w.kind, "n": n, "m": m,
+                   "k": k if w.kind in ("general", "gram") else None,
+                   "step": "sort a and b + all n^2 entries of M" if w.kind == "gram" else "sort + apply",
+                   "route": use_route and w.kind != "gram", "recipe": w.recipe},
         "roofline": roofline,
         "step_alg_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "sort_part": part(sort_names),

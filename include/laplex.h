@@ -61,7 +61,8 @@ enum {
   LAPLEX_OP_PHASED = 3,         /* symmetric phased operator (b = a, psi = phi) */
   LAPLEX_OP_PHASED_GENERAL = 4, /* phased operator with a != b */
   LAPLEX_OP_SYM_BACKWARD = 5,   /* backward of the symmetric operator */
-  LAPLEX_OP_GENERAL_BACKWARD = 6 /* backward of the general operator */
+  LAPLEX_OP_GENERAL_BACKWARD = 6, /* backward of the general operator */
+  LAPLEX_OP_GRAM = 7              /* weighted Gram matrix */
 };
 
 /* Bytes of workspace one call of `op` needs for n output anchors, k input
@@ -163,6 +164,27 @@ laplex_status laplex_backward_general(const float* a_sorted, const uint32_t* per
                                       const float* b_sorted, const uint32_t* perm_b, const void* route_b, uint64_t k,
                                       uint32_t m, const float* x, const float* g, float* dx, float* da, float* db, void* ws,
                                       size_t ws_bytes, hipStream_t stream);
+
+/* Weighted Gram matrix M = A diag(D) A^T with A = LAPLEX(a, b) (n x k), so
+ *     M_pq = sum_j D_j exp(-|a_p - b_j|) exp(-|a_q - b_j|)           (n x n),
+ * computed exactly in O(n^2 + k log k) instead of O(n^2 k) (technical
+ * summary, section 2.2, Gram operators): for lo <= hi the two anchors of an
+ * entry, each b_j lies below lo, between them or above hi, and
+ *     M = exp(-(hi - lo)) [P(lo) + C(hi) - C(lo) + Q(hi)]
+ * with P(s) = sum_{b<=s} D e^{2(b-s)}, C(s) = sum_{b<=s} D (float64) and
+ * Q(s) = sum_{b>s} D e^{-2(b-s)}, all taken by scans over the sorted anchors.
+ * a_sorted, perm_a: sort handle of a (n); b_sorted, perm_b: sort handle of b
+ * (k; for the symmetric Gram pass the handle of a again); D: k weights in the
+ * original order of b.  Writes rows [row_begin, row_begin + row_count) of M,
+ * rows and columns in the original order of a, row p at M + (p - row_begin) *
+ * ldm (ldm >= n floats), so a matrix too large for memory can be produced in
+ * slabs.  M is exactly symmetric.  k == 0 writes zeros.  Anchors must satisfy
+ * |a|, |b| < 2^126 (they are doubled in float32); n <= 65535 * 1024.
+ * Errors: LAPLEX_ERR_ARG for a row range past n or ldm < n.
+ * ws: laplex_workspace_bytes(LAPLEX_OP_GRAM, n, k, 1) bytes. */
+laplex_status laplex_gram_weighted(const float* a_sorted, const uint32_t* perm_a, uint64_t n, const float* b_sorted,
+                                   const uint32_t* perm_b, uint64_t k, const float* D, uint64_t row_begin, uint64_t row_count,
+                                   float* M, uint64_t ldm, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Short English description of a status code (static storage). */
 const char* laplex_status_string(laplex_status s);

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "liblaplex.so")
 LAPLEX_OP_SORT, LAPLEX_OP_SYM, LAPLEX_OP_GENERAL, LAPLEX_OP_PHASED, LAPLEX_OP_PHASED_GENERAL = 0, 1, 2, 3, 4
 LAPLEX_OP_SYM_BACKWARD = 5
 LAPLEX_OP_GENERAL_BACKWARD = 6
+LAPLEX_OP_GRAM = 7
 
 _STATUS = {
     0: "LAPLEX_OK", 1: "LAPLEX_ERR_NULL", 2: "LAPLEX_ERR_SIZE", 3: "LAPLEX_ERR_ALIGN", 4: "LAPLEX_ERR_WORKSPACE",
@@ -58,6 +59,8 @@ def lib():
         L.laplex_backward_sym.restype = i32
         L.laplex_backward_general.argtypes = [vp, vp, vp, u64, vp, vp, vp, u64, u32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.laplex_backward_general.restype = i32
+        L.laplex_gram_weighted.argtypes = [vp, vp, u64, vp, vp, u64, vp, u64, u64, vp, u64, vp, sz, vp]
+        L.laplex_gram_weighted.restype = i32
         for f in (L.laplex_sort_anchors, L.laplex_status_poll, L.laplex_matvec_sym, L.laplex_matvec_general,
                   L.laplex_matvec_phased):
             f.restype = i32
@@ -227,6 +230,34 @@ def laplex_backward_general(a_sorted: torch.Tensor, perm_a: torch.Tensor, b_sort
                                          _ptr(route_b), k, m, _ptr(x), _ptr(g), _ptr(dx), _ptr(da), _ptr(db), _ptr(ws),
                                          ws.numel(), _stream(dev)), "laplex_backward_general")
     return dx, da, db
+
+
+def laplex_gram_weighted(a_sorted: torch.Tensor, perm_a: torch.Tensor, b_sorted: torch.Tensor, perm_b: torch.Tensor,
+                         D: torch.Tensor, M: Optional[torch.Tensor] = None, row_begin: int = 0,
+                         row_count: Optional[int] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rows [row_begin, row_begin + row_count) of M = A diag(D) A^T, A = LAPLEX(a, b), rows and columns in
+    the original order of a.  M: (row_count, >= n) float32 with unit column stride (a new (row_count, n)
+    tensor if None)."""
+    _vec(a_sorted, "a_sorted")
+    _vec(perm_a, "perm_a", torch.uint32)
+    _vec(b_sorted, "b_sorted")
+    _vec(perm_b, "perm_b", torch.uint32)
+    _vec(D, "D")
+    n, k, dev = a_sorted.shape[0], b_sorted.shape[0], a_sorted.device
+    if D.shape[0] != k:
+        raise ValueError("D must have one weight per anchor of b")
+    rc = n - row_begin if row_count is None else row_count
+    if M is None:
+        M = torch.empty((rc, n), dtype=torch.float32, device=dev)
+    if M.dim() != 2 or M.shape[0] != rc or M.shape[1] < n or M.stride(1) != 1 or M.dtype != torch.float32 \
+            or M.device != dev:
+        raise ValueError("M must be a float32 (row_count, >= n) tensor with unit column stride on %s" % dev)
+    ldm = M.stride(0) if rc > 1 else max(n, M.stride(0))  # one row: the stride is never used
+    ws = _ws(ws, LAPLEX_OP_GRAM, n, k, 1, dev)
+    _check(lib().laplex_gram_weighted(_ptr(a_sorted), _ptr(perm_a), n, _ptr(b_sorted), _ptr(perm_b), k, _ptr(D),
+                                      row_begin, rc, _ptr(M), ldm, _ptr(ws), ws.numel(), _stream(dev)),
+           "laplex_gram_weighted")
+    return M
 
 
 def laplex_matvec_general(a_sorted: torch.Tensor, perm_a: torch.Tensor, b_sorted: torch.Tensor, perm_b: torch.Tensor,

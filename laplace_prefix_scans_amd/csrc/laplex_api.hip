@@ -14,6 +14,7 @@ using namespace laplex;
 
 constexpr uint64_t kMaxLen = 0xFFFFFFFFull;  // uint32 permutations
 constexpr uint32_t kMaxCols = 1u << 16;
+constexpr uint64_t kGramMaxLen = 65535ull * 1024;  // columns of the Gram fill grid
 
 // Carves 256-byte aligned regions out of a workspace (base 0: sizing only).
 struct Carver {
@@ -119,6 +120,37 @@ BackwardWorkspace carve_backward(void* ws, uint64_t n, uint64_t k, uint32_t m, b
   return bw;
 }
 
+// Weighted Gram: merged-scan tiles of the n + k anchors (one summary column)
+// and the per-anchor families.
+GramWorkspace carve_gram(void* ws, uint64_t n, uint64_t k, size_t* total) {
+  Carver c(ws);
+  GramWorkspace g{};
+  ApplyWorkspace& w = g.w;
+  const uint64_t T = (n + k + apply_tile(1) - 1) / apply_tile(1);
+  w.bf = c.take<float>(T * 4);
+  w.bb = c.take<float>(T * 4);
+  w.cf = c.take<float>(T * 4);
+  w.cb = c.take<float>(T * 4);
+  w.tanch = c.take<float2>(T * 8);
+  const uint64_t G = (T + 1023) / 1024;
+  w.gbf = c.take<float>(G * 4);
+  w.gbb = c.take<float>(G * 4);
+  w.gcf = c.take<float>(G * 4);
+  w.gcb = c.take<float>(G * 4);
+  w.ganch = c.take<float2>(G * 8);
+  w.tsplit = c.take<uint2>((T + 1) * 8);
+  g.a2 = c.take<float>(n * 4);
+  g.b2 = c.take<float>(k * 4);
+  g.Ds = c.take<float>(k * 4);
+  g.Cpre = c.take<double>((k + 1) * 8);
+  g.Ao = c.take<float>(n * 4);
+  g.Po = c.take<float>(n * 4);
+  g.Qo = c.take<float>(n * 4);
+  g.Co = c.take<double>(n * 8);
+  if (total) *total = (c.off + 255) & ~size_t(255);
+  return g;
+}
+
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
 bool overlaps(const void* p, size_t pb, const void* q, size_t qb) {
@@ -144,6 +176,7 @@ extern "C" size_t laplex_workspace_bytes(int op, uint64_t n, uint64_t k, uint32_
     case LAPLEX_OP_PHASED_GENERAL: carve_apply(nullptr, k, n, n + k, m, Variant::Phased, true, &total); return total;
     case LAPLEX_OP_SYM_BACKWARD: carve_backward(nullptr, n, 0, m, false, &total); return total;
     case LAPLEX_OP_GENERAL_BACKWARD: carve_backward(nullptr, n, k, m, true, &total); return total;
+    case LAPLEX_OP_GRAM: carve_gram(nullptr, n, k, &total); return total;
     default: return 0;
   }
 }
@@ -289,6 +322,29 @@ extern "C" laplex_status laplex_backward_general(const float* a_sorted, const ui
   if (route_b) rb = carve_route(route_b, k);
   return from_hip(backward_general(bw, a_sorted, perm_a, route_a ? &ra : nullptr, n, b_sorted, perm_b, route_b ? &rb : nullptr,
                                    k, m, x, g, dx, da, db, stream));
+}
+
+extern "C" laplex_status laplex_gram_weighted(const float* a_sorted, const uint32_t* perm_a, uint64_t n, const float* b_sorted,
+                                              const uint32_t* perm_b, uint64_t k, const float* D, uint64_t row_begin,
+                                              uint64_t row_count, float* M, uint64_t ldm, void* ws, size_t ws_bytes,
+                                              hipStream_t stream) {
+  if (n == 0 || row_count == 0) return LAPLEX_OK;
+  if (n > kMaxLen || k > kMaxLen || n > kGramMaxLen) return LAPLEX_ERR_SIZE;
+  if (row_begin > n || row_count > n - row_begin || ldm < n) return LAPLEX_ERR_ARG;
+  if (!a_sorted || !perm_a || !M || !ws) return LAPLEX_ERR_NULL;
+  if (k > 0 && (!b_sorted || !perm_b || !D)) return LAPLEX_ERR_NULL;
+  if (misaligned(a_sorted, 4) || misaligned(perm_a, 4) || misaligned(M, 4) || misaligned(ws, 256) ||
+      (k > 0 && (misaligned(b_sorted, 4) || misaligned(perm_b, 4) || misaligned(D, 4))))
+    return LAPLEX_ERR_ALIGN;
+  size_t need = 0;
+  carve_gram(nullptr, n, k, &need);
+  if (ws_bytes < need) return LAPLEX_ERR_WORKSPACE;
+  const size_t mb = ((row_count - 1) * ldm + n) * 4, nb = n * 4, kb = k * 4;
+  if (overlaps(M, mb, a_sorted, nb) || overlaps(M, mb, perm_a, nb) || overlaps(M, mb, b_sorted, kb) ||
+      overlaps(M, mb, perm_b, kb) || overlaps(M, mb, D, kb) || overlaps(M, mb, ws, ws_bytes))
+    return LAPLEX_ERR_OVERLAP;
+  const GramWorkspace g = carve_gram(ws, n, k, nullptr);
+  return from_hip(gram_weighted(g, a_sorted, perm_a, n, b_sorted, perm_b, k, D, row_begin, row_count, M, ldm, stream));
 }
 
 extern "C" laplex_status laplex_matvec_general(const float* a_sorted, const uint32_t* perm_a, const void* route_a, uint64_t n,

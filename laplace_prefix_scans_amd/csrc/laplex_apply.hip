@@ -860,6 +860,43 @@ hipError_t apply_sym(const ApplyWorkspace& w, Variant var, const float* a_s, con
 #undef LAPLEX_SYM
 }
 
+// This thread's E consecutive elements of a merged tile (s_a: the tile's na a
+// anchors, s_b: its nb b anchors, b first on equal anchors; sp0: global index
+// of the tile's first a and first b): anchor (pad past the end), kind (0 pad,
+// 1 a, 2 b), global index into a_s or b_s, and the number of b elements that
+// precede the element in the whole merge.  Written without branches: every
+// per-element value is selected from the same predicate.
+template <int E>
+__device__ __forceinline__ void merge_tile_items(const float* s_a, const float* s_b, uint32_t na, uint32_t nb, uint2 sp0,
+                                                 float pad, float (&ae)[E], int (&kind)[E], uint32_t (&idx)[E],
+                                                 uint32_t (&bbefore)[E]) {
+  const uint32_t tot = na + nb;
+  const uint32_t dd = std::min<uint32_t>(tot, (uint32_t)threadIdx.x * E);
+  uint32_t lo = dd > nb ? dd - nb : 0u, hi = std::min(dd, na);
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (s_a[mid] < s_b[dd - 1 - mid])
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  uint32_t ii = lo, jj = dd - lo;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool real = (uint32_t)threadIdx.x * E + e < tot;
+    const float va = ii < na ? s_a[ii] : INFINITY;
+    const float vb = jj < nb ? s_b[jj] : INFINITY;
+    const bool take_b = real && (jj < nb) && (vb <= va);
+    const bool take_a = real && !take_b;
+    ae[e] = take_b ? vb : (take_a ? va : pad);
+    kind[e] = take_b ? 2 : (take_a ? 1 : 0);
+    idx[e] = take_b ? sp0.y + jj : (take_a ? sp0.x + ii : 0u);
+    bbefore[e] = sp0.y + jj;
+    jj += take_b ? 1u : 0u;
+    ii += take_a ? 1u : 0u;
+  }
+}
+
 __global__ void k_gather_rows(const float* __restrict__ x, const uint32_t* __restrict__ perm, const float* __restrict__ ph,
                               uint64_t rows, uint32_t m, float* __restrict__ xs, float* __restrict__ phs);
 
@@ -1234,36 +1271,10 @@ __global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_gen_apply(const
   for (uint32_t i = tid; i < nb; i += BLOCK) s_b[i] = b_s[(uint64_t)sp0.y + i];
   __syncthreads();
   const float s_max = fmaxf(a_s[n - 1], b_s[k - 1]);
-  // this thread's E merged elements
-  const uint32_t tot = na + nb;
-  const uint32_t dd = std::min<uint32_t>(tot, (uint32_t)tid * E);
-  uint32_t lo = dd > nb ? dd - nb : 0u, hi = std::min(dd, na);
-  while (lo < hi) {
-    const uint32_t mid = (lo + hi) >> 1;
-    if (s_a[mid] < s_b[dd - 1 - mid])
-      lo = mid + 1;
-    else
-      hi = mid;
-  }
-  uint32_t ii = lo, jj = dd - lo;
   float ae[E];
   int kind[E];  // 0 pad, 1 a (output), 2 b (input)
-  uint32_t idx[E];
-  // serial merge of E elements, written without branches: every per-element
-  // value is selected from the same predicate
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const bool real = (uint32_t)tid * E + e < tot;
-    const float va = ii < na ? s_a[ii] : INFINITY;
-    const float vb = jj < nb ? s_b[jj] : INFINITY;
-    const bool take_b = real && (jj < nb) && (vb <= va);
-    const bool take_a = real && !take_b;
-    ae[e] = take_b ? vb : (take_a ? va : s_max);
-    kind[e] = take_b ? 2 : (take_a ? 1 : 0);
-    idx[e] = take_b ? sp0.y + jj : (take_a ? sp0.x + ii : 0u);
-    jj += take_b ? 1u : 0u;
-    ii += take_a ? 1u : 0u;
-  }
+  uint32_t idx[E], bbefore[E];
+  merge_tile_items<E>(s_a, s_b, na, nb, sp0, s_max, ae, kind, idx, bbefore);
   float cs[E], sn[E];
   uint32_t dst[E];
 #pragma unroll
@@ -1509,34 +1520,10 @@ __global__ __launch_bounds__(bwd_block(C)) void k_gbwd_apply(const float* __rest
   for (uint32_t i = tid; i < nb; i += BLOCK) s_b[i] = b_s[(uint64_t)sp0.y + i];
   __syncthreads();
   const float s_max = fmaxf(a_s[n - 1], b_s[k - 1]);
-  // this thread's E merged elements (merge path inside the tile)
-  const uint32_t tot = na + nb;
-  const uint32_t dd = std::min<uint32_t>(tot, (uint32_t)tid * E);
-  uint32_t lo = dd > nb ? dd - nb : 0u, hi = std::min(dd, na);
-  while (lo < hi) {
-    const uint32_t mid = (lo + hi) >> 1;
-    if (s_a[mid] < s_b[dd - 1 - mid])
-      lo = mid + 1;
-    else
-      hi = mid;
-  }
-  uint32_t ii = lo, jj = dd - lo;
   float ae[E];
   int kind[E];  // 0 pad, 1 a element (g injected, da out), 2 b element (x injected, dx and db out)
-  uint32_t idx[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const bool real = (uint32_t)tid * E + e < tot;
-    const float va = ii < na ? s_a[ii] : INFINITY;
-    const float vb = jj < nb ? s_b[jj] : INFINITY;
-    const bool take_b = real && (jj < nb) && (vb <= va);
-    const bool take_a = real && !take_b;
-    ae[e] = take_b ? vb : (take_a ? va : s_max);
-    kind[e] = take_b ? 2 : (take_a ? 1 : 0);
-    idx[e] = take_b ? sp0.y + jj : (take_a ? sp0.x + ii : 0u);
-    jj += take_b ? 1u : 0u;
-    ii += take_a ? 1u : 0u;
-  }
+  uint32_t idx[E], bbefore[E];
+  merge_tile_items<E>(s_a, s_b, na, nb, sp0, s_max, ae, kind, idx, bbefore);
   const float2 ta = tanch[tile];
   const float sf = tile > 0 ? tanch[tile - 1].y : ta.x;
   const float sb = tile + 1 < T ? tanch[tile + 1].x : ta.y;
@@ -1664,6 +1651,205 @@ hipError_t backward_general(const BackwardWorkspace& bw, const float* a_s, const
     default: LAPLEX_GBWD(1);
   }
 #undef LAPLEX_GBWD
+}
+
+
+// ---------------------------------------------------------------- weighted Gram matrix
+// M = A diag(D) A^T, A = LAPLEX(a, b) (n x n; technical summary, section 2.2,
+// Gram operators).  For two output anchors lo <= hi every input anchor b_j
+// falls below lo, between them, or above hi, and in each region the product
+// exp(-|lo - b_j|) exp(-|hi - b_j|) factors as exp(-(hi - lo)) times a term of
+// one anchor only:
+//     M = exp(-(hi - lo)) [ P(lo) + (C(hi) - C(lo)) + Q(hi) ],
+//     P(s) = sum_{b_j <= s} D_j exp(2 (b_j - s)),   C(s) = sum_{b_j <= s} D_j,
+//     Q(s) = sum_{b_j > s} D_j exp(-2 (b_j - s)).
+// P and Q are the strict forward and the backward scan of the merge of a and b
+// (b first on ties) with the anchors doubled and D injected at b; C is a
+// float64 prefix sum of D read at each a (its differences would cancel in
+// float32).  Every weight is <= 1.  O(n + k) for these families, then the n^2
+// entries, each one exp and a few adds: the fill is bound by writing M.
+
+// D in sorted-b order (Ds) and its float64 exclusive prefix sums (k + 1).
+// One workgroup: each thread sums a contiguous run, the 1024 run sums are
+// scanned in LDS (fixed tree, deterministic), the runs are walked again.
+__global__ __launch_bounds__(1024) void k_gram_dprefix(const float* __restrict__ D, const uint32_t* __restrict__ perm_b,
+                                                       uint64_t k, float* __restrict__ Ds, double* __restrict__ Cpre) {
+  __shared__ double s_part[1024];
+  const uint32_t tid = threadIdx.x;
+  const uint64_t q = (k + 1023) / 1024;
+  const uint64_t j0 = std::min<uint64_t>(k, (uint64_t)tid * q), j1 = std::min<uint64_t>(k, j0 + q);
+  double sum = 0.0;
+  for (uint64_t j = j0; j < j1; ++j) {
+    uint32_t src = perm_b[j];
+    if ((uint64_t)src >= k) src = 0;  // a handle from the sort is always in range
+    const float d = D[src];
+    Ds[j] = d;
+    sum += (double)d;
+  }
+  s_part[tid] = sum;
+  __syncthreads();
+  for (uint32_t off = 1; off < 1024; off <<= 1) {
+    const double v = tid >= off ? s_part[tid - off] : 0.0;
+    __syncthreads();
+    s_part[tid] += v;
+    __syncthreads();
+  }
+  double run = tid > 0 ? s_part[tid - 1] : 0.0;
+  for (uint64_t j = j0; j < j1; ++j) {
+    Cpre[j] = run;
+    run += (double)Ds[j];
+  }
+  if (tid == 1023) Cpre[k] = s_part[1023];
+}
+
+// Doubled anchors (exact in float32 for |anchor| < 2^127).
+__global__ void k_gram_double(const float* __restrict__ a_s, uint64_t n, const float* __restrict__ b_s, uint64_t k,
+                              float* __restrict__ a2, float* __restrict__ b2) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n + k; i += stride) {
+    if (i < n)
+      a2[i] = 2.f * a_s[i];
+    else
+      b2[i - n] = 2.f * b_s[i - n];
+  }
+}
+
+// Merged tile scans with the doubled anchors -> per output anchor, in the
+// original order of a: the anchor, P, Q and C.
+__global__ __launch_bounds__(apply_block(1)) void k_gram_families(const float* __restrict__ a_s, const float* __restrict__ a2,
+                                                                  const uint32_t* __restrict__ perm_a, uint64_t n,
+                                                                  const float* __restrict__ b2, uint64_t k,
+                                                                  const float* __restrict__ Ds, const double* __restrict__ Cpre,
+                                                                  uint64_t T, const float* __restrict__ cfw,
+                                                                  const float* __restrict__ cbw, const float2* __restrict__ tanch,
+                                                                  const uint2* __restrict__ tsplit, float* __restrict__ Ao,
+                                                                  float* __restrict__ Po, float* __restrict__ Qo,
+                                                                  double* __restrict__ Co) {
+  constexpr int E = apply_items(1);
+  constexpr int BLOCK = apply_block(1);
+  constexpr int NW = BLOCK / kWave;
+  constexpr int P = BLOCK * E;
+  __shared__ float s_a[P], s_b[P];
+  __shared__ float s_wf[NW], s_wb[NW], s_wfs[NW], s_wbs[NW];
+  const int tid = threadIdx.x;
+  const uint64_t tile = blockIdx.x;
+  const uint2 sp0 = tsplit[tile], sp1 = tsplit[tile + 1];
+  const uint32_t na = std::min<uint32_t>(sp1.x - sp0.x, P), nb = std::min<uint32_t>(sp1.y - sp0.y, P - na);
+  for (uint32_t i = tid; i < na; i += BLOCK) s_a[i] = a2[(uint64_t)sp0.x + i];
+  for (uint32_t i = tid; i < nb; i += BLOCK) s_b[i] = b2[(uint64_t)sp0.y + i];
+  __syncthreads();
+  const float s_max = fmaxf(a2[n - 1], b2[k - 1]);
+  float ae[E];
+  int kind[E];
+  uint32_t idx[E], bbefore[E];
+  merge_tile_items<E>(s_a, s_b, na, nb, sp0, s_max, ae, kind, idx, bbefore);
+  float v[E][1];
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e][0] = kind[e] == 2 ? Ds[idx[e]] : 0.f;
+  const float2 ta = tanch[tile];
+  const float sf = tile > 0 ? tanch[tile - 1].y : ta.x;
+  const float sb = tile + 1 < T ? tanch[tile + 1].x : ta.y;
+  const float cin_f[1] = {cfw[tile]}, cin_b[1] = {cbw[tile]};
+  float F[E][1], U[E][1];
+  tile_scan_fu<E, 1, NW, false>(ae, v, cin_f, sf, cin_b, sb, s_wf, s_wfs, s_wb, s_wbs, F, U);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (kind[e] == 1) {
+      const uint32_t dst = perm_a[idx[e]];
+      if ((uint64_t)dst < n) {
+        Ao[dst] = a_s[idx[e]];
+        Po[dst] = F[e][0];
+        Qo[dst] = U[e][0];
+        Co[dst] = Cpre[bbefore[e]];
+      }
+    }
+  }
+}
+
+// Rows [r0, r0 + rc) of M (original order) into M[(p - r0) * ldm + q].  Each
+// thread owns 4 consecutive columns for kGramRows rows; the row's families are
+// uniform across the workgroup.  For a pair with equal anchors the lower
+// index plays lo, so both orders of a pair compute the same bits (M is
+// exactly symmetric).  zero: k == 0, every entry is 0.
+constexpr int kGramRows = 16;
+constexpr int kGramBlock = 256;
+__global__ __launch_bounds__(kGramBlock) void k_gram_fill(const float* __restrict__ Ao, const float* __restrict__ Po,
+                                                          const float* __restrict__ Qo, const double* __restrict__ Co,
+                                                          uint64_t n, uint64_t r0, uint64_t rc, float* __restrict__ M,
+                                                          uint64_t ldm, bool zero) {
+  const uint64_t q0 = ((uint64_t)blockIdx.y * kGramBlock + threadIdx.x) * 4;
+  const uint64_t rb = (uint64_t)blockIdx.x * kGramRows;
+  if (q0 >= n) return;  // no barrier below
+  float aq[4], pq[4], qq[4];
+  double cq[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint64_t q = std::min<uint64_t>(q0 + c, n - 1);
+    aq[c] = Ao[q];
+    pq[c] = Po[q];
+    qq[c] = Qo[q];
+    cq[c] = Co[q];
+  }
+  const bool full = q0 + 4 <= n;
+  const bool vec = full && (ldm % 4 == 0) && (reinterpret_cast<uintptr_t>(M) % 16 == 0);
+  for (int r = 0; r < kGramRows; ++r) {
+    const uint64_t rr = rb + r;
+    if (rr >= rc) break;
+    const uint64_t p = r0 + rr;
+    const float ap = Ao[p], pp = Po[p], qp = Qo[p];
+    const double cp = Co[p];
+    float out[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint64_t q = q0 + c;
+      const bool p_lo = (ap < aq[c]) || (ap == aq[c] && p <= q);
+      const float w = decay(-fabsf(aq[c] - ap));
+      const float plo = p_lo ? pp : pq[c];
+      const float qhi = p_lo ? qq[c] : qp;
+      const double dc = p_lo ? (cq[c] - cp) : (cp - cq[c]);
+      out[c] = zero ? 0.f : w * ((plo + (float)dc) + qhi);
+    }
+    float* row = M + rr * ldm + q0;
+    if (vec) {
+      *reinterpret_cast<float4*>(row) = make_float4(out[0], out[1], out[2], out[3]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (q0 + c < n) row[c] = out[c];
+    }
+  }
+}
+
+hipError_t gram_weighted(const GramWorkspace& g, const float* a_s, const uint32_t* perm_a, uint64_t n, const float* b_s,
+                         const uint32_t* perm_b, uint64_t k, const float* D, uint64_t r0, uint64_t rc, float* M, uint64_t ldm,
+                         hipStream_t s) {
+  hipError_t e;
+  const dim3 fill_grid((unsigned)((rc + kGramRows - 1) / kGramRows), (unsigned)((n + 4 * kGramBlock - 1) / (4 * kGramBlock)));
+  if (k == 0) {
+    LAPLEX_LAUNCH("k_gram_fill", rc * n, s,
+                  k_gram_fill<<<fill_grid, kGramBlock, 0, s>>>(g.Ao, g.Po, g.Qo, g.Co, n, r0, rc, M, ldm, true));
+    return hipGetLastError();
+  }
+  const ApplyWorkspace& w = g.w;
+  constexpr int P = apply_tile(1);
+  const uint64_t T = (n + k + P - 1) / P;
+  const dim3 grid((unsigned)T), block(apply_block(1));
+  LAPLEX_LAUNCH("k_gram_dprefix", k, s, k_gram_dprefix<<<1, 1024, 0, s>>>(D, perm_b, k, g.Ds, g.Cpre));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  LAPLEX_LAUNCH("k_gram_double", n + k, s,
+                k_gram_double<<<rows_grid(n + k), 256, 0, s>>>(a_s, n, b_s, k, g.a2, g.b2));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  LAPLEX_LAUNCH("k_gen_reduce", k, s,
+                k_gen_reduce<1, false><<<grid, block, 0, s>>>(g.a2, n, g.b2, k, g.Ds, nullptr, 1, T, w.bf, w.bb, w.tanch, w.tsplit));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = tile_carries(w.bf, w.bb, w.tanch, T, 1, w.cf, w.cb, w.gbf, w.gbb, w.gcf, w.gcb, w.ganch, s)) != hipSuccess) return e;
+  LAPLEX_LAUNCH("k_gram_families", n + k, s,
+                k_gram_families<<<grid, block, 0, s>>>(a_s, g.a2, perm_a, n, g.b2, k, g.Ds, g.Cpre, T, w.cf, w.cb, w.tanch,
+                                                       w.tsplit, g.Ao, g.Po, g.Qo, g.Co));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  LAPLEX_LAUNCH("k_gram_fill", rc * n, s,
+                k_gram_fill<<<fill_grid, kGramBlock, 0, s>>>(g.Ao, g.Po, g.Qo, g.Co, n, r0, rc, M, ldm, false));
+  return hipGetLastError();
 }
 
 }  // namespace laplex

@@ -127,6 +127,26 @@ hipError_t backward_general(const BackwardWorkspace& bw, const float* a_s, const
                             uint64_t n, const float* b_s, const uint32_t* perm_b, const SortRoute* route_b, uint64_t k,
                             uint32_t m, const float* x, const float* g, float* dx, float* da, float* db, hipStream_t s);
 
+// Weighted Gram matrix M = A diag(D) A^T (A = LAPLEX(a, b)): rows
+// [r0, r0 + rc) of M in the original order of a, written to M[(p - r0) * ldm + q].
+// Uses the merged-scan part of an apply workspace (tiles of the merge of n + k
+// anchors, one summary column) plus the families below.  Requires n >= 1; with
+// k == 0 it writes zeros.
+struct GramWorkspace {
+  ApplyWorkspace w;
+  float* a2;     // doubled sorted a (n)
+  float* b2;     // doubled sorted b (k)
+  float* Ds;     // D in sorted-b order (k)
+  double* Cpre;  // exclusive prefix sums of Ds (k + 1)
+  float* Ao;     // per output anchor, original order: the anchor (n)
+  float* Po;     //   P (n)
+  float* Qo;     //   Q (n)
+  double* Co;    //   C (n)
+};
+hipError_t gram_weighted(const GramWorkspace& g, const float* a_s, const uint32_t* perm_a, uint64_t n, const float* b_s,
+                         const uint32_t* perm_b, uint64_t k, const float* D, uint64_t r0, uint64_t rc, float* M, uint64_t ldm,
+                         hipStream_t s);
+
 // tile count and summary width of an apply
 inline uint64_t apply_tiles(uint64_t len, uint32_t m, Variant var) {
   const uint32_t c = column_chunk(m);

@@ -29,7 +29,7 @@ ROOT = 0x1A91E
 CHUNK = 1 << 22
 
 # stream ids
-S_A, S_B, S_X, S_PHI, S_PSI, S_JIT = 1, 2, 3, 4, 5, 6
+S_A, S_B, S_X, S_PHI, S_PSI, S_JIT, S_D = 1, 2, 3, 4, 5, 6, 7
 
 
 def _fill(out: np.ndarray, wid: int, sid: int, draw: Callable[[np.random.Generator, int, int], np.ndarray]) -> np.ndarray:
@@ -95,7 +95,7 @@ def phases_uniform(n: int, wid: int, sid: int = S_PHI, out: Optional[np.ndarray]
 class Workload:
     """One synthetic workload: anchors ``a`` (n), optional ``b`` (k), phases, and x."""
     name: str
-    kind: str              # "sym" | "general" | "phased"
+    kind: str              # "sym" | "general" | "phased" | "gram"
     n: int
     m: int
     k: int
@@ -104,6 +104,7 @@ class Workload:
     b: Optional[np.ndarray] = None
     phi: Optional[np.ndarray] = None
     psi: Optional[np.ndarray] = None
+    D: Optional[np.ndarray] = None   # Gram weights (k)
     recipe: str = ""
 
 
@@ -114,6 +115,7 @@ WORKLOADS = {
     "gen2p24k2p16": (3, "general", "general, n=2^24 a~N(0,var 2^12), k=2^16 b~N(0,var 2^12), x~N(0,1), m=1"),
     "phased3x1024x1024m8": (4, "phased", "phased symmetric, n=3*2^20 flattened 3x1024x1024, a=raster index + N(0,var 0.1), phi~U(0,2pi), m=8"),
     "sym2p30": (5, "sym", "symmetric, n=2^30, m=1, a~U(0,2^27), x~N(0,1)"),
+    "gram2p16k2p16": (6, "gram", "weighted Gram A diag(D) A^T, n=2^16 a~U(0,2^13), k=2^16 b~U(0,2^13), D~U(0,1)"),
 }
 
 
@@ -146,4 +148,10 @@ def make_workload(name: str, scale: int = 0) -> Workload:
         n, m = (1 << 30) // s, 1
         a = anchors_uniform(n, 0.0, float(1 << 27) / s, wid)
         return Workload(name, kind, n, m, n, a, columns_normal(n, m, wid), recipe=desc)
+    if name == "gram2p16k2p16":
+        n, k = (1 << 16) // s, (1 << 16) // s
+        a = anchors_uniform(n, 0.0, float(1 << 13) / s, wid, S_A)
+        b = anchors_uniform(k, 0.0, float(1 << 13) / s, wid, S_B)
+        D = anchors_uniform(k, 0.0, 1.0, wid, S_D)
+        return Workload(name, kind, n, 1, k, a, np.zeros((0, 1), np.float32), b=b, D=D, recipe=desc)
     raise KeyError(name)

@@ -46,7 +46,7 @@ def test_workspace_sizes(L):
     assert lp.laplex_workspace_bytes(99, 10) == 0
     assert lp.laplex_workspace_bytes(lp.LAPLEX_OP_GENERAL_BACKWARD, 1 << 20, 1 << 10, 2) > \
         lp.laplex_workspace_bytes(lp.LAPLEX_OP_GENERAL, 1 << 20, 1 << 10, 2)
-    for op in range(7):
+    for op in range(8):
         a = lp.laplex_workspace_bytes(op, 4096, 100, 1)
         b = lp.laplex_workspace_bytes(op, 1 << 22, 1 << 20, 1)
         assert a % 256 == 0 and b % 256 == 0 and b >= a
@@ -101,6 +101,20 @@ def test_host_argument_errors(L):
     bad = list(args)
     bad[12] = vp(0xA00002)  # da misaligned
     assert GB(*bad, need, None) == ALIGN
+    # weighted Gram: no-ops, row range, NULL, workspace, overlap of M with the weights
+    GW = L.laplex_gram_weighted
+    assert GW(None, None, 0, None, None, 0, None, 0, 1, None, 0, None, 0, None) == OK
+    assert GW(A, B, 10, A, B, 5, A, 0, 0, B, 10, W, 0, None) == OK
+    assert GW(A, B, 10, A, B, 5, A, 8, 3, vp(0x900000), 10, W, 1 << 30, None) == 9  # rows past n
+    assert GW(A, B, 10, A, B, 5, A, 0, 3, vp(0x900000), 9, W, 1 << 30, None) == 9   # ldm < n
+    assert GW(A, B, 10, None, B, 5, A, 0, 3, vp(0x900000), 10, W, 1 << 30, None) == NULL
+    assert GW(A, B, 1 << 32, A, B, 5, A, 0, 3, vp(0x900000), 1 << 32, W, 1 << 40, None) == SIZE
+    need = L.laplex_workspace_bytes(7, 1000, 300, 1)
+    assert need > 0
+    assert GW(A, vp(0x300000), 1000, vp(0x500000), vp(0x600000), 300, vp(0x700000), 0, 2, vp(0x900000), 1000,
+              vp(0x10000000), 64, None) == WS
+    assert GW(A, vp(0x300000), 1000, vp(0x500000), vp(0x600000), 300, vp(0x700000), 0, 2, vp(0x700100), 1000,
+              vp(0x10000000), need, None) == OVERLAP
     # route: too small, misaligned, overlapping
     assert L.laplex_sort_anchors(A, 1000, B, vp(0x300000), vp(0x20000000), 16, vp(0x10000000), 1 << 30, None) == WS
     assert L.laplex_sort_anchors(A, 1000, B, vp(0x300000), vp(0x20000010), 1 << 20, vp(0x10000000), 1 << 30, None) == ALIGN
