@@ -76,7 +76,7 @@ def kernel_bytes(name: str, units: int, m: int, k: int = 0) -> float:
         "k_gram_fill": 4.0,                      # per entry of M: written once (row/column families are O(n))
         "k_gram_families": 8.0,                  # merged anchors and weights in; families out at a (20 B per a)
         "k_gram_double": 8.0,                    # anchors in and doubled anchors out
-        "k_gram_dprefix": 24.0,                  # weights (random through perm_b), sorted weights, float64 prefix
+        "k_gram_dprefix": 12.0,                  # sorted weights in, float64 prefix out
     }
     for w in (1, 2, 3, 4):
         table["k_route_fwd_w%d" % w] = route + 8.0 * w   # position, row in, row out

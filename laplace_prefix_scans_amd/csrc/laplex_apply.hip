@@ -1669,23 +1669,18 @@ hipError_t backward_general(const BackwardWorkspace& bw, const float* a_s, const
 // float32).  Every weight is <= 1.  O(n + k) for these families, then the n^2
 // entries, each one exp and a few adds: the fill is bound by writing M.
 
-// D in sorted-b order (Ds) and its float64 exclusive prefix sums (k + 1).
-// One workgroup: each thread sums a contiguous run, the 1024 run sums are
-// scanned in LDS (fixed tree, deterministic), the runs are walked again.
-__global__ __launch_bounds__(1024) void k_gram_dprefix(const float* __restrict__ D, const uint32_t* __restrict__ perm_b,
-                                                       uint64_t k, float* __restrict__ Ds, double* __restrict__ Cpre) {
+// Float64 exclusive prefix sums (k + 1) of the weights in sorted-b order.
+// One workgroup: each thread sums a contiguous run (independent loads, 8 in
+// flight), the 1024 run sums are scanned in LDS (a fixed tree, so the result
+// is deterministic), and each run is walked again to write its prefixes.
+__global__ __launch_bounds__(1024) void k_gram_dprefix(const float* __restrict__ Ds, uint64_t k, double* __restrict__ Cpre) {
   __shared__ double s_part[1024];
   const uint32_t tid = threadIdx.x;
   const uint64_t q = (k + 1023) / 1024;
   const uint64_t j0 = std::min<uint64_t>(k, (uint64_t)tid * q), j1 = std::min<uint64_t>(k, j0 + q);
   double sum = 0.0;
-  for (uint64_t j = j0; j < j1; ++j) {
-    uint32_t src = perm_b[j];
-    if ((uint64_t)src >= k) src = 0;  // a handle from the sort is always in range
-    const float d = D[src];
-    Ds[j] = d;
-    sum += (double)d;
-  }
+#pragma unroll 8
+  for (uint64_t j = j0; j < j1; ++j) sum += (double)Ds[j];
   s_part[tid] = sum;
   __syncthreads();
   for (uint32_t off = 1; off < 1024; off <<= 1) {
@@ -1695,6 +1690,7 @@ __global__ __launch_bounds__(1024) void k_gram_dprefix(const float* __restrict__
     __syncthreads();
   }
   double run = tid > 0 ? s_part[tid - 1] : 0.0;
+#pragma unroll 8
   for (uint64_t j = j0; j < j1; ++j) {
     Cpre[j] = run;
     run += (double)Ds[j];
@@ -1768,7 +1764,9 @@ __global__ __launch_bounds__(apply_block(1)) void k_gram_families(const float* _
 
 // Rows [r0, r0 + rc) of M (original order) into M[(p - r0) * ldm + q].  Each
 // thread owns 4 consecutive columns for kGramRows rows; the row's families are
-// uniform across the workgroup.  For a pair with equal anchors the lower
+// uniform across the workgroup.  Workgroups run along the columns first
+// (block b: column block b mod ncb, row group b / ncb), so the workgroups in
+// flight together write whole rows, one contiguous stretch of M.  For a pair with equal anchors the lower
 // index plays lo, so both orders of a pair compute the same bits (M is
 // exactly symmetric).  zero: k == 0, every entry is 0.
 constexpr int kGramRows = 16;
@@ -1777,8 +1775,9 @@ __global__ __launch_bounds__(kGramBlock) void k_gram_fill(const float* __restric
                                                           const float* __restrict__ Qo, const double* __restrict__ Co,
                                                           uint64_t n, uint64_t r0, uint64_t rc, float* __restrict__ M,
                                                           uint64_t ldm, bool zero) {
-  const uint64_t q0 = ((uint64_t)blockIdx.y * kGramBlock + threadIdx.x) * 4;
-  const uint64_t rb = (uint64_t)blockIdx.x * kGramRows;
+  const uint64_t ncb = (n + 4 * kGramBlock - 1) / (4 * kGramBlock);
+  const uint64_t q0 = ((uint64_t)(blockIdx.x % ncb) * kGramBlock + threadIdx.x) * 4;
+  const uint64_t rb = (uint64_t)(blockIdx.x / ncb) * kGramRows;
   if (q0 >= n) return;  // no barrier below
   float aq[4], pq[4], qq[4];
   double cq[4];
@@ -1824,17 +1823,29 @@ hipError_t gram_weighted(const GramWorkspace& g, const float* a_s, const uint32_
                          const uint32_t* perm_b, uint64_t k, const float* D, uint64_t r0, uint64_t rc, float* M, uint64_t ldm,
                          hipStream_t s) {
   hipError_t e;
-  const dim3 fill_grid((unsigned)((rc + kGramRows - 1) / kGramRows), (unsigned)((n + 4 * kGramBlock - 1) / (4 * kGramBlock)));
-  if (k == 0) {
-    LAPLEX_LAUNCH("k_gram_fill", rc * n, s,
-                  k_gram_fill<<<fill_grid, kGramBlock, 0, s>>>(g.Ao, g.Po, g.Qo, g.Co, n, r0, rc, M, ldm, true));
-    return hipGetLastError();
-  }
+  // the fill in launches of at most 2^30 workgroups (rows of M in chunks)
+  auto fill = [&](bool zero) -> hipError_t {
+    const uint64_t ncb = (n + 4 * kGramBlock - 1) / (4 * kGramBlock);
+    const uint64_t rows_per = std::max<uint64_t>(1, (1ull << 30) / ncb) * kGramRows;
+    for (uint64_t lo = 0; lo < rc; lo += rows_per) {
+      const uint64_t cnt = std::min(rows_per, rc - lo);
+      const unsigned blocks = (unsigned)(((cnt + kGramRows - 1) / kGramRows) * ncb);
+      LAPLEX_LAUNCH("k_gram_fill", cnt * n, s,
+                    k_gram_fill<<<blocks, kGramBlock, 0, s>>>(g.Ao, g.Po, g.Qo, g.Co, n, r0 + lo, cnt, M + lo * ldm, ldm,
+                                                              zero));
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+  };
+  if (k == 0) return fill(true);
   const ApplyWorkspace& w = g.w;
   constexpr int P = apply_tile(1);
   const uint64_t T = (n + k + P - 1) / P;
   const dim3 grid((unsigned)T), block(apply_block(1));
-  LAPLEX_LAUNCH("k_gram_dprefix", k, s, k_gram_dprefix<<<1, 1024, 0, s>>>(D, perm_b, k, g.Ds, g.Cpre));
+  LAPLEX_LAUNCH("k_gather_rows", k, s, k_gather_rows<<<rows_grid(k), 256, 0, s>>>(D, perm_b, nullptr, k, 1, g.Ds, nullptr));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  LAPLEX_LAUNCH("k_gram_dprefix", k, s, k_gram_dprefix<<<1, 1024, 0, s>>>(g.Ds, k, g.Cpre));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   LAPLEX_LAUNCH("k_gram_double", n + k, s,
                 k_gram_double<<<rows_grid(n + k), 256, 0, s>>>(a_s, n, b_s, k, g.a2, g.b2));
@@ -1847,9 +1858,7 @@ hipError_t gram_weighted(const GramWorkspace& g, const float* a_s, const uint32_
                 k_gram_families<<<grid, block, 0, s>>>(a_s, g.a2, perm_a, n, g.b2, k, g.Ds, g.Cpre, T, w.cf, w.cb, w.tanch,
                                                        w.tsplit, g.Ao, g.Po, g.Qo, g.Co));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  LAPLEX_LAUNCH("k_gram_fill", rc * n, s,
-                k_gram_fill<<<fill_grid, kGramBlock, 0, s>>>(g.Ao, g.Po, g.Qo, g.Co, n, r0, rc, M, ldm, false));
-  return hipGetLastError();
+  return fill(false);
 }
 
 }  // namespace laplex
