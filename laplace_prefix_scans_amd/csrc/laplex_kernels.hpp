@@ -30,6 +30,9 @@ constexpr int kSortTile = kSortBlock * kSortItems;
 // header words of the sort workspace
 constexpr int kHdrFlags = 0;    // sticky error bits (below)
 constexpr int kHdrTicket0 = 1;  // one tile ticket per radix pass (4 words)
+// per radix pass: 1 when tiles publish their counts before ranking (4 words;
+// a cache line of their own, away from the tickets every workgroup increments)
+constexpr int kHdrEarly0 = 64;
 constexpr uint32_t kFlagNonFinite = 1u, kFlagWatchdog = 2u;
 constexpr size_t kSortHeaderBytes = 16384;  // control words, 4x256 histograms, 4x256 offsets
 constexpr size_t kSortHistOffset = 1024;

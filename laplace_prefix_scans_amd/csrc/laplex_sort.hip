@@ -90,22 +90,34 @@ __global__ __launch_bounds__(kHistBlock) void k_sort_hist(const uint32_t* __rest
 
 // Exclusive prefix of each digit histogram -> global start of each bucket.
 // One block of 256 threads; thread d handles digit value d of every pass.
-__global__ __launch_bounds__(256) void k_sort_offsets(const uint32_t* __restrict__ hist, uint32_t* __restrict__ offs) {
-  __shared__ uint32_t wsum[4];
+// Exclusive digit offsets of every pass, and per pass whether its tiles
+// publish their digit counts before ranking: only when no digit value holds
+// more than 1/16 of the keys, since the early count takes LDS atomic adds that
+// serialise when many lanes share a digit (the ranking itself does not).
+__global__ __launch_bounds__(256) void k_sort_offsets(const uint32_t* __restrict__ hist, uint32_t* __restrict__ offs,
+                                                      uint32_t* __restrict__ header) {
+  __shared__ uint32_t wsum[4], wmax[4];
   const int d = threadIdx.x, lane = lane_id(), w = d / kWave;
   for (int p = 0; p < 4; ++p) {
     const uint32_t v = hist[p * 256 + d];
-    uint32_t x = v;
+    uint32_t x = v, mx = v;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
       const uint32_t t = __shfl_up(x, off);
       if (lane >= off) x += t;
+      mx = max(mx, (uint32_t)__shfl_xor(mx, off));
     }
     if (lane == kWave - 1) wsum[w] = x;
+    if (lane == 0) wmax[w] = mx;
     __syncthreads();
-    uint32_t pre = 0;
-    for (int i = 0; i < w; ++i) pre += wsum[i];
+    uint32_t pre = 0, total = 0, top = 0;
+    for (int i = 0; i < 4; ++i) {
+      if (i < w) pre += wsum[i];
+      total += wsum[i];
+      top = max(top, wmax[i]);
+    }
     offs[p * 256 + d] = pre + x - v;
+    if (d == 0) header[kHdrEarly0 + p] = (top <= total / 16) ? 1u : 0u;
     __syncthreads();
   }
 }
@@ -136,6 +148,7 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
   __shared__ uint32_t s_gbase[256];
   __shared__ uint32_t s_wsum[4];
   __shared__ uint32_t s_tile;
+  __shared__ uint32_t s_thist[256];
 
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
   const uint32_t shift = 8u * (uint32_t)pass;
@@ -146,8 +159,11 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
   uint4* s_match = reinterpret_cast<uint4*>(s_kv);
   if (tid == 0) s_tile = atomicAdd(&header[kHdrTicket0 + pass], 1u);
   for (int i = tid; i < NW * 256; i += kSortBlock) s_match[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < 256) s_thist[tid] = 0u;
   __syncthreads();
   const uint32_t tile = s_tile;
+  // uniform: one scalar value for the whole workgroup
+  const bool early = __builtin_amdgcn_readfirstlane(header[kHdrEarly0 + pass]) != 0u;
   const uint64_t base = (uint64_t)tile * TILE;
 
   // load: wave w owns the contiguous run [w*64*E, (w+1)*64*E) of the tile;
@@ -175,6 +191,19 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
       const uint64_t idx = base + (uint64_t)wid * (kWave * E) + (uint64_t)e * kWave + lane;
       k[e] = idx < n ? float_to_key(k[e]) : 0xFFFFFFFFu;
     }
+  }
+  // With a spread-out digit, the tile's counts first: published before the
+  // ranking, they reach successors' look-backs sooner.
+  if (early) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint64_t idx = base + (uint64_t)wid * (kWave * E) + (uint64_t)e * kWave + lane;
+      if (idx < n) atomicAdd(&s_thist[(k[e] >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 256)
+      store_agent(status + (uint64_t)tile * 256 + tid,
+                  Status<ST>::pack(tile == 0 ? kFlagInclusive : kFlagAggregate, s_thist[tid]));
   }
   // stable rank within the wave's run: earlier iterations first, then lower
   // lanes.  The lanes sharing a digit are found by each lane OR-ing its bit
@@ -235,7 +264,7 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
   uint32_t excl = 0;
   if (digit_owner) {
     ST* my = status + (uint64_t)tile * 256 + d;
-    store_agent(my, Status<ST>::pack(tile == 0 ? kFlagInclusive : kFlagAggregate, cnt));
+    if (!early) store_agent(my, Status<ST>::pack(tile == 0 ? kFlagInclusive : kFlagAggregate, cnt));
     if (tile > 0) {
       int64_t t = (int64_t)tile - 1;
       uint32_t spins = 0;
@@ -409,7 +438,7 @@ hipError_t sort_anchors(const SortWorkspace& w, const float* a, uint64_t n, floa
   LAPLEX_LAUNCH("k_sort_hist", n, s,
                 k_sort_hist<<<hist_blocks, kHistBlock, 0, s>>>(reinterpret_cast<const uint32_t*>(a), n, w.hist, w.header));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  LAPLEX_LAUNCH("k_sort_offsets", 1024, s, k_sort_offsets<<<1, 256, 0, s>>>(w.hist, w.offsets));
+  LAPLEX_LAUNCH("k_sort_offsets", 1024, s, k_sort_offsets<<<1, 256, 0, s>>>(w.hist, w.offsets, w.header));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (n <= (1ull << 30)) return launch_sort_passes<uint32_t>(w, a, n, a_sorted, perm, route, s);
   return launch_sort_passes<uint64_t>(w, a, n, a_sorted, perm, route, s);
