@@ -308,6 +308,7 @@ def main():
     ap.add_argument("--no-route", action="store_true", help="move x and y by index instead of along the sort route")
     ap.add_argument("--cpu-sample-log2", type=int, default=25)
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward of the symmetric workloads")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing (steps after a 512 MiB scrub)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--rocprof-summary", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
@@ -399,6 +400,25 @@ def main():
         torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
+    # cold caches: each step timed alone after writing a 512 MiB scrub buffer
+    # (larger than the L2s and the 256 MiB Infinity Cache); for workloads whose
+    # working set could stay cached between steps
+    cold = None
+    if not args.no_cold and n * max(1, m) <= (1 << 26):
+        scrub = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+        times = []
+        for i in range(max(3, min(args.steps, 10))):
+            scrub.fill_(float(i))
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            step()
+            c1.record()
+            torch.cuda.synchronize()
+            times.append(c0.elapsed_time(c1))
+        del scrub
+        cold = {"ms_per_step_median": round(float(sorted(times)[len(times) // 2]), 4), "steps": len(times),
+                "scrub_MiB": 512}
+
     # per-kernel statistics from the launch events (each records its element count)
     stats = {}
     for name, ms, units in prof.records:
@@ -469,6 +489,7 @@ def main():
         "sort_part": part(sort_names),
         "apply_part": part(apply_names),
         "kernels": kernels,
+        "cold": cold,
         "source_hash": src,
         "host_gen_s": round(t_gen, 1),
     }

@@ -851,7 +851,7 @@ hipError_t apply_sym(const ApplyWorkspace& w, Variant var, const float* a_s, con
 #define LAPLEX_SYM(CW)                                                               \
   return ph ? run_sym<CW, true>(w, a_s, perm, route, phi, n, m, x, y, s)          \
             : run_sym<CW, false>(w, a_s, perm, route, phi, n, m, x, y, s)
-  switch (column_chunk(m)) {
+  switch (ph ? phased_chunk(m) : column_chunk(m)) {
     case 8: LAPLEX_SYM(8);
     case 4: LAPLEX_SYM(4);
     case 2: LAPLEX_SYM(2);
@@ -1377,7 +1377,7 @@ hipError_t apply_general(const ApplyWorkspace& w, Variant var, const float* a_s,
 #define LAPLEX_GEN(CW)                                                                                                   \
   return ph ? run_general<CW, true>(w, a_s, perm_a, route_a, phi, n, b_s, perm_b, route_b, psi, k, m, x, y, s)          \
             : run_general<CW, false>(w, a_s, perm_a, route_a, phi, n, b_s, perm_b, route_b, psi, k, m, x, y, s)
-  switch (column_chunk(m)) {
+  switch (ph ? phased_chunk(m) : column_chunk(m)) {
     case 8: LAPLEX_GEN(8);
     case 4: LAPLEX_GEN(4);
     case 2: LAPLEX_GEN(2);

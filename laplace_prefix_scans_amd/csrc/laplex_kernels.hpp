@@ -80,6 +80,9 @@ constexpr int apply_tile(int cc) { return apply_block(cc) * apply_items(cc); }
 
 // column chunk: the largest of 8, 4, 2, 1 that divides m
 inline uint32_t column_chunk(uint32_t m) { return (m % 8 == 0) ? 8 : (m % 4 == 0) ? 4 : (m % 2 == 0) ? 2 : 1; }
+// phased applies scan a cos and a sin column per input column: chunks of at
+// most 4 (8 scanned columns) keep a tile's state in registers
+inline uint32_t phased_chunk(uint32_t m) { const uint32_t c = column_chunk(m); return c > 4 ? 4 : c; }
 
 struct ApplyWorkspace {
   float* xs;       // gathered inputs in sorted order (rows x m)
@@ -152,7 +155,7 @@ hipError_t gram_weighted(const GramWorkspace& g, const float* a_s, const uint32_
 
 // tile count and summary width of an apply
 inline uint64_t apply_tiles(uint64_t len, uint32_t m, Variant var) {
-  const uint32_t c = column_chunk(m);
+  const uint32_t c = (var == Variant::Phased) ? phased_chunk(m) : column_chunk(m);
   const int cc = (var == Variant::Phased) ? 2 * (int)c : (int)c;
   const uint64_t tile = (uint64_t)apply_tile(cc);
   return (len + tile - 1) / tile;
