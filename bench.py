@@ -309,6 +309,7 @@ def main():
     ap.add_argument("--cpu-sample-log2", type=int, default=25)
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward of the symmetric workloads")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing (steps after a 512 MiB scrub)")
+    ap.add_argument("--no-graph", action="store_true", help="skip timing the step replayed from a HIP graph")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--rocprof-summary", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
@@ -419,6 +420,33 @@ def main():
         cold = {"ms_per_step_median": round(float(sorted(times)[len(times) // 2]), 4), "steps": len(times),
                 "scrub_MiB": 512}
 
+    # the same step captured once in a HIP graph and replayed: no host launch
+    # cost between kernels (for workloads small enough for that to matter)
+    graph = None
+    if not args.no_graph and n * max(1, m) <= (1 << 26):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg):
+            step()
+        for _ in range(max(1, args.warmup)):
+            cg.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            cg.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1) / args.steps
+        graph = {"ms_per_step": round(gms, 4), "Gelem_per_s": round(n * m / (gms * 1e-3) / 1e9, 4) if w.kind != "gram"
+                 else round(n * n / (gms * 1e-3) / 1e9, 4), "replays": args.steps}
+        del cg
+
     # per-kernel statistics from the launch events (each records its element count)
     stats = {}
     for name, ms, units in prof.records:
@@ -490,6 +518,7 @@ def main():
         "apply_part": part(apply_names),
         "kernels": kernels,
         "cold": cold,
+        "graph": graph,
         "source_hash": src,
         "host_gen_s": round(t_gen, 1),
     }
