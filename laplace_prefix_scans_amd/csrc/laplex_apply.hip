@@ -184,14 +184,17 @@ __device__ __forceinline__ void tile_scan(const float (&ae)[E], float (&v)[E][CC
 // ---------------------------------------------------------------- carries
 constexpr int kCarryBlock = 1024;
 constexpr int kCarryBatch = 8;
+constexpr uint64_t kCarryMinRun = 8;
 
 // Scan of the tile aggregates into the carry entering each tile from the left
 // (cf: value at the previous tile's last element) and from the right (cb:
 // value at the next tile's first element).  One workgroup per column: each
 // thread owns a contiguous run of tiles, folds it as a direct weighted sum
-// (every weight exp(s - s_end) <= 1), wave 0 scans the 1024 run aggregates in
-// 16 rounds, then each thread walks its run again writing carries, with the
-// loads of each batch of tiles issued before its dependent chain.
+// (every weight exp(s - s_end) <= 1), wave 0 scans the run aggregates 64 per
+// round (at most 16 rounds; runs hold at least 8 tiles, so a few thousand
+// tiles take a few rounds), then each thread walks its run again writing
+// carries, with the loads of each batch of tiles issued before its dependent
+// chain.
 __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restrict__ bf, const float* __restrict__ bb,
                                                             const float2* __restrict__ tanch, uint64_t T, uint32_t M,
                                                             uint32_t tie_from, float* __restrict__ cf, float* __restrict__ cb) {
@@ -199,7 +202,9 @@ __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restr
   const uint32_t c = blockIdx.x;
   const bool tie = c >= tie_from;  // columns from tie_from on scan with the tie decay
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
-  const uint64_t q = (T + kCarryBlock - 1) / kCarryBlock;
+  // runs of at least kCarryMinRun tiles, so that few tiles need few scan rounds
+  const uint64_t q = std::max<uint64_t>(kCarryMinRun, (T + kCarryBlock - 1) / kCarryBlock);
+  const int rounds = (int)std::min<uint64_t>(kCarryBlock / kWave, ((T + q - 1) / q + kWave - 1) / kWave);
   const uint64_t t0 = std::min<uint64_t>(T, (uint64_t)tid * q), t1 = std::min<uint64_t>(T, t0 + q);
   const float s_min = tanch[0].y, s_maxf = tanch[T - 1].x, s_maxl = tanch[T - 1].y;
 
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restr
   __syncthreads();
   if (wid == 0) {
     float cB = 0.f, cS = s_min;
-    for (int r = 0; r < kCarryBlock / kWave; ++r) {
+    for (int r = 0; r < rounds; ++r) {  // runs past the last hold nothing
       const int i = r * kWave + lane;
       float b1[1] = {sB[i]};
       const float s1 = sS[i];
@@ -271,7 +276,7 @@ __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restr
   __syncthreads();
   if (wid == 0) {
     float cB = 0.f, cS = s_maxf;
-    for (int r = kCarryBlock / kWave - 1; r >= 0; --r) {
+    for (int r = rounds - 1; r >= 0; --r) {
       const int i = r * kWave + lane;
       float b1[1] = {sB[i]};
       const float s1 = sS[i];
