@@ -94,7 +94,9 @@ BackwardWorkspace carve_backward(void* ws, uint64_t n, uint64_t k, uint32_t m, b
   const uint64_t rows_x = general ? k : n;  // rows of x and dx
   const uint64_t T = backward_tiles(general ? n + k : n, m);
   const uint64_t M = 4ull * m;
-  w.xs = c.take<float>(rows_x * m * 4);
+  // one symmetric column moves x with g as rows of two
+  const uint64_t mp = (!general && m == 1) ? 2 : m;
+  w.xs = c.take<float>(rows_x * mp * 4);
   bw.gs = c.take<float>(n * m * 4);
   w.zs = c.take<float>(rows_x * m * 4);
   bw.das = c.take<float>(n * 4);
@@ -113,8 +115,8 @@ BackwardWorkspace carve_backward(void* ws, uint64_t n, uint64_t k, uint32_t m, b
   w.tsplit = general ? c.take<uint2>((T + 1) * 8) : nullptr;
   if (m <= kRouteMaxCols) {
     const uint64_t rmax = std::max(n, rows_x);
-    w.t0 = c.take<float>(rmax * m * 4);
-    w.t1 = c.take<float>(rmax * m * 4);
+    w.t0 = c.take<float>(rmax * mp * 4);
+    w.t1 = c.take<float>(rmax * mp * 4);
   }
   if (total) *total = (c.off + 255) & ~size_t(255);
   return bw;

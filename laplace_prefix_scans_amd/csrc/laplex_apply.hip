@@ -926,8 +926,9 @@ __device__ __forceinline__ uint32_t bwdcol(uint32_t m, uint32_t cc, int j) {
 }
 
 // Gathered inputs (or their rows moved by route) -> tile aggregates of x and g
-// under both decays, as direct weighted sums.
-template <int C>
+// under both decays, as direct weighted sums.  PAIR (one column): x and g
+// arrive interleaved as rows (x_i, g_i) in xs.
+template <int C, bool PAIR>
 __global__ __launch_bounds__(bwd_block(C)) void k_bwd_reduce(const float* __restrict__ a_s, const float* __restrict__ xs,
                                                                    const float* __restrict__ gs, uint64_t n, uint32_t m,
                                                                    float* __restrict__ bf, float* __restrict__ bb,
@@ -956,10 +957,21 @@ __global__ __launch_bounds__(bwd_block(C)) void k_bwd_reduce(const float* __rest
     tf[e] = valid ? decay_m<true>(ae[e] - s_last) : 0.f;
     tb[e] = valid ? decay_m<true>(s_first - ae[e]) : 0.f;
   }
+  static_assert(!PAIR || C == 1, "pairs carry one column");
   for (uint32_t cc = 0; cc < m / C; ++cc) {
     float xv[E][C], gv[E][C];
-    load_rows<E, C>(xs, p0, n, m, cc, true, xv);
-    load_rows<E, C>(gs, p0, n, m, cc, true, gv);
+    if constexpr (PAIR) {
+      float xg[E][2];
+      load_rows<E, 2>(xs, p0, n, 2, 0, true, xg);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        xv[e][0] = xg[e][0];
+        gv[e][0] = xg[e][1];
+      }
+    } else {
+      load_rows<E, C>(xs, p0, n, m, cc, true, xv);
+      load_rows<E, C>(gs, p0, n, m, cc, true, gv);
+    }
     float sf[CC], sb[CC];
 #pragma unroll
     for (int j = 0; j < CC; ++j) sf[j] = sb[j] = 0.f;
@@ -997,8 +1009,9 @@ __global__ __launch_bounds__(bwd_block(C)) void k_bwd_reduce(const float* __rest
 // and da (sorted order).  By linearity da_i = -(A_i - A0_i) with
 // A = sum_c g_c (F - U)(x_c) + x_c (F - U)(g_c) under the kernel's decay and A0
 // the same under the tie decay; the tie scan runs first and only its per-element
-// sum stays live through the second scan.
-template <int C>
+// sum stays live through the second scan.  PAIR (one column): x and g arrive
+// interleaved as rows (x_i, g_i) in xs.
+template <int C, bool PAIR>
 __global__ __launch_bounds__(bwd_block(C)) void k_bwd_apply(const float* __restrict__ a_s, const float* __restrict__ xs, const float* __restrict__ gs,
                  const float* __restrict__ cfw, const float* __restrict__ cbw, const float2* __restrict__ tanch,
                  uint64_t n, uint32_t m, uint64_t T, float* __restrict__ dxs, float* __restrict__ das, bool vec) {
@@ -1017,6 +1030,7 @@ __global__ __launch_bounds__(bwd_block(C)) void k_bwd_apply(const float* __restr
   const float2 ta = tanch[tile];
   const float sf = tile > 0 ? tanch[tile - 1].y : ta.x;
   const float sb = tile + 1 < T ? tanch[tile + 1].x : ta.y;
+  static_assert(!PAIR || C == 1, "pairs carry one column");
   float acc[E], acc0[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = acc0[e] = 0.f;
@@ -1024,8 +1038,18 @@ __global__ __launch_bounds__(bwd_block(C)) void k_bwd_apply(const float* __restr
     float v[E][CC];
     {
       float xv[E][C], gv[E][C];
-      load_rows<E, C>(xs, p0, n, m, cc, true, xv);
-      load_rows<E, C>(gs, p0, n, m, cc, true, gv);
+      if constexpr (PAIR) {
+        float xg[E][2];
+        load_rows<E, 2>(xs, p0, n, 2, 0, true, xg);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          xv[e][0] = xg[e][0];
+          gv[e][0] = xg[e][1];
+        }
+      } else {
+        load_rows<E, C>(xs, p0, n, m, cc, true, xv);
+        load_rows<E, C>(gs, p0, n, m, cc, true, gv);
+      }
 #pragma unroll
       for (int e = 0; e < E; ++e)
 #pragma unroll
@@ -1105,6 +1129,24 @@ static hipError_t run_bwd_sym(const BackwardWorkspace& bw, const float* a_s, con
   const bool routed = route != nullptr && m <= kRouteMaxCols;
   const bool vec = (reinterpret_cast<uintptr_t>(a_s) & 15) == 0;
   hipError_t e;
+  if (C == 1 && m == 1 && routed) {
+    // one column: x and g travel as pairs (one read of each route table for
+    // both); dx and da go back one by one (an inverse pass of pairs stages
+    // twice the LDS and fits half the workgroups)
+    if ((e = route_forward_pair(*route, n, x, g, w.xs, w.t0, w.t1, s)) != hipSuccess) return e;
+    LAPLEX_LAUNCH("k_bwd_reduce", n, s,
+                  k_bwd_reduce<C, C == 1><<<grid, block, 0, s>>>(a_s, w.xs, nullptr, n, m, w.bf, w.bb, w.tanch, vec));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = tile_carries(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb, w.gbf, w.gbb, w.gcf, w.gcb, w.ganch, s, 2 * m)) !=
+        hipSuccess)
+      return e;
+    LAPLEX_LAUNCH("k_bwd_apply", n, s,
+                  k_bwd_apply<C, C == 1><<<grid, block, 0, s>>>(a_s, w.xs, nullptr, w.cf, w.cb, w.tanch, n, m, T, w.zs, bw.das,
+                                                                vec));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = route_inverse(*route, n, 1, w.zs, dx, w.t0, w.t1, s)) != hipSuccess) return e;
+    return route_inverse(*route, n, 1, bw.das, da, w.t0, w.t1, s);
+  }
   if (routed) {
     if ((e = route_forward(*route, n, m, x, w.xs, w.t0, w.t1, s)) != hipSuccess) return e;
     if ((e = route_forward(*route, n, m, g, bw.gs, w.t0, w.t1, s)) != hipSuccess) return e;
@@ -1115,12 +1157,12 @@ static hipError_t run_bwd_sym(const BackwardWorkspace& bw, const float* a_s, con
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   LAPLEX_LAUNCH("k_bwd_reduce", n, s,
-                k_bwd_reduce<C><<<grid, block, 0, s>>>(a_s, w.xs, bw.gs, n, m, w.bf, w.bb, w.tanch, vec));
+                k_bwd_reduce<C, false><<<grid, block, 0, s>>>(a_s, w.xs, bw.gs, n, m, w.bf, w.bb, w.tanch, vec));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = tile_carries(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb, w.gbf, w.gbb, w.gcf, w.gcb, w.ganch, s, 2 * m)) != hipSuccess)
     return e;
   LAPLEX_LAUNCH("k_bwd_apply", n, s,
-                k_bwd_apply<C><<<grid, block, 0, s>>>(a_s, w.xs, bw.gs, w.cf, w.cb, w.tanch, n, m, T, w.zs, bw.das, vec));
+                k_bwd_apply<C, false><<<grid, block, 0, s>>>(a_s, w.xs, bw.gs, w.cf, w.cb, w.tanch, n, m, T, w.zs, bw.das, vec));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (routed) {
     if ((e = route_inverse(*route, n, m, w.zs, dx, w.t0, w.t1, s)) != hipSuccess) return e;

@@ -70,6 +70,10 @@ hipError_t route_forward(const SortRoute& r, uint64_t n, uint32_t W, const float
 hipError_t route_inverse(const SortRoute& r, uint64_t n, uint32_t W, const float* in, float* out, float* t0, float* t1,
                          hipStream_t s);
 constexpr uint32_t kRouteMaxCols = 4;
+// Two arrays of n floats moved together as interleaved rows of two, original
+// order -> sorted (out: n x 2).  t0, t1: scratch of n x 2 floats each.
+hipError_t route_forward_pair(const SortRoute& r, uint64_t n, const float* in0, const float* in1, float* out, float* t0,
+                              float* t1, hipStream_t s);
 
 // ------------------------------------------------------------------ apply
 // Tile shape for CC injected columns: E consecutive items per thread (the

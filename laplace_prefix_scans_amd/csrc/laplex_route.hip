@@ -53,6 +53,55 @@ __device__ __forceinline__ void st_group(float* __restrict__ p, const float (&v)
   }
 }
 
+// The input-order side as rows of W floats: interleaved (row i at p + i W) or,
+// with PLANES (W == 2), two separate arrays p[i], p_b[i] forming row i.  vec:
+// every array of the side is 16-byte aligned.
+template <int W, bool PLANES>
+__device__ __forceinline__ void ld_rows(const float* __restrict__ p, const float* __restrict__ p_b, uint64_t i0,
+                                        float (&v)[kGroup * W], bool vec) {
+  if constexpr (PLANES) {
+    static_assert(W == 2, "two planes make rows of two floats");
+    float x0[kGroup], x1[kGroup];
+    ld_group<1>(p + i0, x0, vec);
+    ld_group<1>(p_b + i0, x1, vec);
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) {
+      v[2 * g] = x0[g];
+      v[2 * g + 1] = x1[g];
+    }
+  } else {
+    ld_group<W>(p + i0 * W, v, vec);
+  }
+}
+template <int W, bool PLANES>
+__device__ __forceinline__ void st_rows(float* __restrict__ p, float* __restrict__ p_b, uint64_t i0, const float (&v)[kGroup * W],
+                                        bool vec) {
+  if constexpr (PLANES) {
+    static_assert(W == 2, "two planes make rows of two floats");
+    float x0[kGroup], x1[kGroup];
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) {
+      x0[g] = v[2 * g];
+      x1[g] = v[2 * g + 1];
+    }
+    st_group<1>(p + i0, x0, vec);
+    st_group<1>(p_b + i0, x1, vec);
+  } else {
+    st_group<W>(p + i0 * W, v, vec);
+  }
+}
+template <int W, bool PLANES>
+__device__ __forceinline__ float ld_one(const float* __restrict__ p, const float* __restrict__ p_b, uint64_t i, int c) {
+  return PLANES ? (c == 0 ? p[i] : p_b[i]) : p[i * W + c];
+}
+template <int W, bool PLANES>
+__device__ __forceinline__ void st_one(float* __restrict__ p, float* __restrict__ p_b, uint64_t i, int c, float v) {
+  if (PLANES)
+    (c == 0 ? p : p_b)[i] = v;
+  else
+    p[i * W + c] = v;
+}
+
 // Tile tables into LDS: run starts (clamped to the tile) and run positions.
 __device__ __forceinline__ void load_tables(const uint16_t* __restrict__ dstart, const uint32_t* __restrict__ gbase, uint64_t tile,
                                             uint32_t count, uint16_t* s_start, uint32_t* s_gb) {
@@ -75,9 +124,11 @@ __device__ __forceinline__ bool xcd_tile(uint64_t tiles, uint64_t& tile) {
   return tile < tiles;
 }
 
-// vec: `in` (fwd) or `out` (inv), the input-order side, is 16-byte aligned.
-template <int W>
-__global__ __launch_bounds__(kSortBlock) void k_route_fwd(const float* __restrict__ in, float* __restrict__ out,
+// vec: `in` (fwd) or `out` (inv), the input-order side, is 16-byte aligned
+// (and in_b / out_b with PLANES).
+template <int W, bool PLANES>
+__global__ __launch_bounds__(kSortBlock) void k_route_fwd(const float* __restrict__ in, const float* __restrict__ in_b,
+                                                          float* __restrict__ out,
                                                           const uint16_t* __restrict__ lpos, const uint16_t* __restrict__ dstart,
                                                           const uint32_t* __restrict__ gbase, uint64_t n, bool vec) {
   constexpr int TILE = kSortTile;
@@ -102,7 +153,7 @@ __global__ __launch_bounds__(kSortBlock) void k_route_fwd(const float* __restric
     const uint32_t i0 = (uint32_t)(r * kSortBlock + tid) * kGroup;
     if (i0 + kGroup <= count) {
       lp2[r] = *reinterpret_cast<const uint2*>(lpos + base + i0);
-      ld_group<W>(in + (base + i0) * W, vv[r], vec);
+      ld_rows<W, PLANES>(in, in_b, base + i0, vv[r], vec);
     }
   }
   load_tables(dstart, gbase, tile, count, s_start, s_gb);
@@ -123,7 +174,7 @@ __global__ __launch_bounds__(kSortBlock) void k_route_fwd(const float* __restric
         const uint32_t lp = lpos[base + i];
         if (lp < count) {
 #pragma unroll
-          for (int c = 0; c < W; ++c) s_val[lp * W + c] = in[(base + i) * W + c];
+          for (int c = 0; c < W; ++c) s_val[lp * W + c] = ld_one<W, PLANES>(in, in_b, base + i, c);
         }
       }
     }
@@ -145,8 +196,9 @@ __global__ __launch_bounds__(kSortBlock) void k_route_fwd(const float* __restric
   }
 }
 
-template <int W>
+template <int W, bool PLANES>
 __global__ __launch_bounds__(kSortBlock) void k_route_inv(const float* __restrict__ in, float* __restrict__ out,
+                                                          float* __restrict__ out_b,
                                                           const uint16_t* __restrict__ lpos, const uint16_t* __restrict__ dstart,
                                                           const uint32_t* __restrict__ gbase, uint64_t n, bool vec) {
   constexpr int TILE = kSortTile;
@@ -199,12 +251,12 @@ __global__ __launch_bounds__(kSortBlock) void k_route_inv(const float* __restric
 #pragma unroll
         for (int c = 0; c < W; ++c) v[g * W + c] = s_val[q * W + c];
       }
-      st_group<W>(out + (base + i0) * W, v, vec);
+      st_rows<W, PLANES>(out, out_b, base + i0, v, vec);
     } else {
       for (uint32_t i = i0; i < count && i < i0 + kGroup; ++i) {
         const uint32_t q = std::min<uint32_t>(lpos[base + i], count - 1);
 #pragma unroll
-        for (int c = 0; c < W; ++c) out[(base + i) * W + c] = s_val[q * W + c];
+        for (int c = 0; c < W; ++c) st_one<W, PLANES>(out, out_b, base + i, c, s_val[q * W + c]);
       }
     }
   }
@@ -273,8 +325,9 @@ __device__ __forceinline__ void build_chunks(RunChunks<W>& rc, const uint16_t* s
 // lie outside the run belong to neighbouring runs and are discarded; a chunk
 // reaching past the end of the array is read float by float.  vec: `out` is
 // 16-byte aligned.
-template <int W>
+template <int W, bool PLANES>
 __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(W == 1 ? 8 : 1))) void k_route_inv_chunked(const float* __restrict__ in, float* __restrict__ out,
+                                                                  float* __restrict__ out_b,
                                                                   const uint16_t* __restrict__ lpos,
                                                                   const uint16_t* __restrict__ dstart,
                                                                   const uint32_t* __restrict__ gbase, uint64_t n, bool vec) {
@@ -357,12 +410,12 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(W ==
 #pragma unroll
         for (int c = 0; c < W; ++c) v[g * W + c] = s_val[q * W + c];
       }
-      st_group<W>(out + (base + i0) * W, v, vec);
+      st_rows<W, PLANES>(out, out_b, base + i0, v, vec);
     } else {
       for (uint32_t i = i0; i < count && i < i0 + kGroup; ++i) {
         const uint32_t q = std::min<uint32_t>(lpos[base + i], count - 1);
 #pragma unroll
-        for (int c = 0; c < W; ++c) out[(base + i) * W + c] = s_val[q * W + c];
+        for (int c = 0; c < W; ++c) st_one<W, PLANES>(out, out_b, base + i, c, s_val[q * W + c]);
       }
     }
   }
@@ -391,36 +444,40 @@ SortRoute carve_route(const void* base, uint64_t n) {
   return r;
 }
 
-template <int W>
-static hipError_t route_pass(bool fwd, const SortRoute& r, int k, uint64_t n, const float* in, float* out, hipStream_t s) {
+// One pass of a route.  in_b (forward) / out_b (inverse), when given, make the
+// input-order side two separate arrays forming rows of W = 2 floats.
+template <int W, bool PLANES>
+static hipError_t route_pass(bool fwd, const SortRoute& r, int k, uint64_t n, const float* in, const float* in_b, float* out,
+                             float* out_b, hipStream_t s) {
   // the input-order side: `in` going forward, `out` going back
-  const bool vec = (reinterpret_cast<uintptr_t>(fwd ? in : out) & 15) == 0;
+  auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool vec = fwd ? (al(in) && (!PLANES || al(in_b))) : (al(out) && (!PLANES || al(out_b)));
   static const char* const kFwd[5] = {"", "k_route_fwd_w1", "k_route_fwd_w2", "k_route_fwd_w3", "k_route_fwd_w4"};
   static const char* const kInv[5] = {"", "k_route_inv_w1", "k_route_inv_w2", "k_route_inv_w3", "k_route_inv_w4"};
   const uint64_t tiles = (n + kSortTile - 1) / kSortTile;
   const uint64_t blocks = ((tiles + kXcds - 1) / kXcds) * kXcds;
   if (fwd)
     LAPLEX_LAUNCH(kFwd[W], n, s,
-                  k_route_fwd<W><<<dim3((unsigned)blocks), dim3(kSortBlock), 0, s>>>(in, out, r.lpos[k], r.dstart[k], r.gbase[k], n,
-                                                                                    vec));
-  else if (W != 3 && (reinterpret_cast<uintptr_t>(in) & 15) == 0 && n * W >= 4)
+                  k_route_fwd<W, PLANES><<<dim3((unsigned)blocks), dim3(kSortBlock), 0, s>>>(
+                      in, in_b, out, r.lpos[k], r.dstart[k], r.gbase[k], n, vec));
+  else if (W != 3 && al(in) && n * W >= 4)
     LAPLEX_LAUNCH(kInv[W], n, s,
-                  k_route_inv_chunked<W == 3 ? 1 : W><<<dim3((unsigned)blocks), dim3(kSortBlock), 0, s>>>(
-                      in, out, r.lpos[k], r.dstart[k], r.gbase[k], n, vec));
+                  k_route_inv_chunked<W == 3 ? 1 : W, PLANES><<<dim3((unsigned)blocks), dim3(kSortBlock), 0, s>>>(
+                      in, out, out_b, r.lpos[k], r.dstart[k], r.gbase[k], n, vec));
   else
     LAPLEX_LAUNCH(kInv[W], n, s,
-                  k_route_inv<W><<<dim3((unsigned)blocks), dim3(kSortBlock), 0, s>>>(in, out, r.lpos[k], r.dstart[k], r.gbase[k], n,
-                                                                                    vec));
+                  k_route_inv<W, PLANES><<<dim3((unsigned)blocks), dim3(kSortBlock), 0, s>>>(
+                      in, out, out_b, r.lpos[k], r.dstart[k], r.gbase[k], n, vec));
   return hipGetLastError();
 }
 
 static hipError_t route_pass_w(bool fwd, const SortRoute& r, int k, uint64_t n, uint32_t W, const float* in, float* out,
                                hipStream_t s) {
   switch (W) {
-    case 1: return route_pass<1>(fwd, r, k, n, in, out, s);
-    case 2: return route_pass<2>(fwd, r, k, n, in, out, s);
-    case 3: return route_pass<3>(fwd, r, k, n, in, out, s);
-    case 4: return route_pass<4>(fwd, r, k, n, in, out, s);
+    case 1: return route_pass<1, false>(fwd, r, k, n, in, nullptr, out, nullptr, s);
+    case 2: return route_pass<2, false>(fwd, r, k, n, in, nullptr, out, nullptr, s);
+    case 3: return route_pass<3, false>(fwd, r, k, n, in, nullptr, out, nullptr, s);
+    case 4: return route_pass<4, false>(fwd, r, k, n, in, nullptr, out, nullptr, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -444,6 +501,20 @@ hipError_t route_inverse(const SortRoute& r, uint64_t n, uint32_t W, const float
     hipError_t e = route_pass_w(false, r, 3 - i, n, W, src[i], dst[i], s);
     if (e != hipSuccess) return e;
   }
+  return hipSuccess;
+}
+
+// Two arrays of n floats moved together as rows of two (one pass reads each
+// route table once for both): original order -> interleaved sorted rows
+// (out: n x 2).  t0, t1: scratch of n x 2 floats each.
+hipError_t route_forward_pair(const SortRoute& r, uint64_t n, const float* in0, const float* in1, float* out, float* t0,
+                              float* t1, hipStream_t s) {
+  hipError_t e = route_pass<2, true>(true, r, 0, n, in0, in1, t0, nullptr, s);
+  if (e != hipSuccess) return e;
+  const float* src[3] = {t0, t1, t0};
+  float* dst[3] = {t1, t0, out};
+  for (int k = 1; k < 4; ++k)
+    if ((e = route_pass<2, false>(true, r, k, n, src[k - 1], nullptr, dst[k - 1], nullptr, s)) != hipSuccess) return e;
   return hipSuccess;
 }
 
