@@ -104,6 +104,9 @@ ROCPROF_LABELS = {
 
 def rocprof_label(name: str, pass_index: int = 0, routed: bool = True) -> str:
     import re
+    if "at::native::" in name:  # torch's own kernels (input fills in the timed program): name the functor
+        fm = re.search(r"(\w*Functor)", name) or re.search(r"at::native::(?:\w+::)*(\w+)", name)
+        return "torch_" + (fm.group(1) if fm else "kernel")
     base = re.sub(r"\(.*$", "", name).replace("void ", "").replace("laplex::", "").strip()
     m = re.match(r"(k_\w+)<(.*)>$", base)
     kern, targs = (m.group(1), [t.strip() for t in m.group(2).split(",")]) if m else (base, [])
