@@ -223,5 +223,5 @@ def dense_rows_c(rows, a, x, b=None, phi=None, psi=None, lib=None):
     return y, env
 
 
-from .dense import (dense_apply, dense_backward, dense_envelope, dense_rows, gram_block, gram_dense,  # noqa: E402,F401
-                    normwise_error)
+from .dense import (dense_apply, dense_backward, dense_envelope, dense_phased_backward, dense_rows, gram_block,  # noqa: E402,F401
+                    gram_dense, normwise_error, phased_backward_rows)

@@ -125,6 +125,86 @@ def dense_backward(a, x, g, b=None):
     return dx, da, db
 
 
+def dense_phased_backward(a, phi, x, g, b=None, psi=None):
+    """Backward of the phased operator y = LAPLEX(a, phi; b, psi) x by the plain
+    definition (float64), for g = dL/dy.  With W_ij = K_ij cos(phi_i - psi_j),
+    K_ij = exp(-|a_i - b_j|), the chain rule on each entry gives
+        dx     = W^T g,
+        da_i   = -sum_jc sign(a_i - b_j) W_ij g_ic x_jc,   db_j   = -(the same sum over i, with the opposite sign),
+        dphi_i = -sum_jc K_ij sin(phi_i - psi_j) g_ic x_jc, dpsi_j = +sum_ic K_ij sin(phi_i - psi_j) g_ic x_jc
+    (sign(0) = 0).  Symmetric (b None: b = a, psi = phi): each anchor and phase
+    receives both terms; returns (dx, da, dphi).  General: (dx, da, db, dphi, dpsi)."""
+    a = np.asarray(a, np.float64).ravel()
+    phi = np.asarray(phi, np.float64).ravel()
+    sym = b is None
+    b = a if sym else np.asarray(b, np.float64).ravel()
+    psi = phi if sym else np.asarray(psi, np.float64).ravel()
+    x2 = np.asarray(x, np.float64).reshape(b.size, -1)
+    g2 = np.asarray(g, np.float64).reshape(a.size, -1)
+    D = a[:, None] - b[None, :]
+    P = phi[:, None] - psi[None, :]
+    K = np.exp(-np.abs(D))
+    cosP, sinP = _phase_terms(P)
+    W = K * cosP
+    SW = np.sign(D) * W
+    KS = K * sinP
+    gx = g2 @ x2.T  # gx[i, j] = sum_c g_ic x_jc
+    dx = W.T @ g2
+    da = -(SW * gx).sum(axis=1)
+    db = (SW * gx).sum(axis=0)
+    dphi = -(KS * gx).sum(axis=1)
+    dpsi = (KS * gx).sum(axis=0)
+    if sym:
+        return dx, _sym_fold(da, db), _sym_fold(dphi, dpsi)
+    return dx, da, db, dphi, dpsi
+
+
+def _phase_terms(P):
+    """cos and sin of the phase differences."""
+    return np.cos(P), np.sin(P)
+
+
+def _sym_fold(row_term, col_term):
+    """With b = a (and psi = phi) an anchor or phase is both a row and a column
+    parameter: its gradient is the sum of the two terms."""
+    return row_term + col_term
+
+
+def phased_backward_rows(rows, a, phi, x, g, col_chunk: int = 1 << 20):
+    """Anchor and phase gradients of the symmetric phased backward at selected
+    rows by the plain definition, for sizes where only spot rows can be checked:
+        da_i   = -sum_j sign(a_i - a_j) K_ij cos(phi_i - phi_j) s_ij,
+        dphi_i = -sum_j K_ij sin(phi_i - phi_j) s_ij,   s_ij = sum_c (g_ic x_jc + x_ic g_jc),
+    and their envelope  sum_j K_ij sum_c (|g_ic||x_jc| + |x_ic||g_jc|).
+    Returns (da_rows, dphi_rows, env_rows), float64."""
+    rows = np.asarray(rows, np.int64)
+    a = np.asarray(a).ravel()
+    phi = np.asarray(phi).ravel()
+    n = a.size
+    x2 = np.asarray(x).reshape(n, -1)
+    g2 = np.asarray(g).reshape(n, -1)
+    ai = a[rows].astype(np.float64)
+    pi = phi[rows].astype(np.float64)
+    gi = g2[rows].astype(np.float64)
+    xi = x2[rows].astype(np.float64)
+    da = np.zeros(rows.size)
+    dphi = np.zeros(rows.size)
+    env = np.zeros(rows.size)
+    for lo in range(0, n, col_chunk):
+        hi = min(n, lo + col_chunk)
+        D = ai[:, None] - a[lo:hi].astype(np.float64)[None, :]
+        P = pi[:, None] - phi[lo:hi].astype(np.float64)[None, :]
+        K = np.exp(-np.abs(D))
+        xj = x2[lo:hi].astype(np.float64)
+        gj = g2[lo:hi].astype(np.float64)
+        S = gi @ xj.T + xi @ gj.T
+        E = np.abs(gi) @ np.abs(xj).T + np.abs(xi) @ np.abs(gj).T
+        da -= (np.sign(D) * K * np.cos(P) * S).sum(axis=1)
+        dphi -= (K * np.sin(P) * S).sum(axis=1)
+        env += (K * E).sum(axis=1)
+    return da, dphi, env
+
+
 # ----------------------------------------------------------------------------- weighted Gram
 def _gram_combine(ar_w, ac_w, d):
     """sum_j ar_w[p, j] d_j ac_w[q, j] for one chunk of input anchors."""

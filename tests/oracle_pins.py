@@ -595,6 +595,69 @@ def pin_gram_symmetric_psd(lib):
     assert sv[k] <= 1e-12 * sv[0], "gram rank exceeds k"
 
 
+def pin_phased_backward(lib):
+    """Phased backward (anchors and phases are parameters too): the plain
+    definition against central differences of <g, W x> in every anchor and
+    every phase, symmetric and general, with and without ties; phases all
+    zero reduce it to the scan oracle's symmetric backward (and give no phase
+    gradient); a common phase shift changes nothing; the spot-row form agrees
+    with the whole."""
+    r = _rng(63)
+    h = 1e-5
+    for ties in (False, True):
+        n, m = 24, 2
+        a = (r.integers(0, 9, n).astype(np.float32) if ties else _spread_anchors(r, n, 0.05))
+        phi = r.uniform(0, 2 * np.pi, n)
+        x = r.standard_normal((n, m)).astype(np.float32)
+        g = r.standard_normal((n, m)).astype(np.float32)
+        x64, g64 = x.astype(np.float64), g.astype(np.float64)
+        loss = lambda aa, pp: float(np.sum(g64 * odense.dense_apply(aa, x64, phi=pp)))
+        dx, da, dphi = odense.dense_phased_backward(a, phi, x, g)
+        _close(da, _fd_anchor_grad(lambda aa: loss(aa, phi), a, h), 1e-7, "phased sym da vs differences (ties=%s)" % ties)
+        _close(dphi, _fd_anchor_grad(lambda pp: loss(a, pp), phi, h), 1e-7, "phased sym dphi vs differences")
+        _close(dx, odense.dense_apply(a, g64, phi=phi).reshape(n, m), 1e-12, "phased sym dx vs W g")
+        j, c = 5, 0
+        xp, xm = x64.copy(), x64.copy()
+        xp[j, c] += 0.5
+        xm[j, c] -= 0.5
+        fdx = float(np.sum(g64 * odense.dense_apply(a, xp, phi=phi))) - float(np.sum(g64 * odense.dense_apply(a, xm, phi=phi)))
+        _close([dx[j, c]], [fdx], 1e-10, "phased sym dx vs difference in x")
+        # general: rows (a, phi), columns (b, psi)
+        k = 17
+        b = (r.integers(0, 9, k).astype(np.float32) if ties else _spread_anchors(r, k, 0.05) + np.float32(0.013))
+        psi = r.uniform(0, 2 * np.pi, k)
+        xb = r.standard_normal((k, m)).astype(np.float32)
+        xb64 = xb.astype(np.float64)
+        gl = lambda aa, pp, bb, qq: float(np.sum(g64 * odense.dense_apply(aa, xb64, b=bb, phi=pp, psi=qq)))
+        dxg, dag, dbg, dpg, dqg = odense.dense_phased_backward(a, phi, xb, g, b=b, psi=psi)
+        _close(dag, _fd_anchor_grad(lambda aa: gl(aa, phi, b, psi), a, h), 1e-7, "phased general da vs differences")
+        _close(dbg, _fd_anchor_grad(lambda bb: gl(a, phi, bb, psi), b, h), 1e-7, "phased general db vs differences")
+        _close(dpg, _fd_anchor_grad(lambda pp: gl(a, pp, b, psi), phi, h), 1e-7, "phased general dphi vs differences")
+        _close(dqg, _fd_anchor_grad(lambda qq: gl(a, phi, b, qq), psi, h), 1e-7, "phased general dpsi vs differences")
+        _close(dxg, odense.dense_apply(b, g64, b=a, phi=psi, psi=phi).reshape(k, m), 1e-12, "phased general dx vs W^T g")
+    # zero phases: the symmetric backward of the scan oracle, and no phase gradient
+    n, m = 300, 3
+    a = r.uniform(0, 40, n).astype(np.float32)
+    x = r.standard_normal((n, m)).astype(np.float32)
+    g = r.standard_normal((n, m)).astype(np.float32)
+    dx0, da0, dp0 = odense.dense_phased_backward(a, np.zeros(n), x, g)
+    dxs, das = oracle.sym_backward(a, x, g, lib=lib)
+    _close(da0, das, 1e-12, "phased backward at zero phase vs symmetric backward")
+    _close(dx0, dxs, 1e-12, "phased dx at zero phase vs K g")
+    assert np.all(dp0 == 0.0), "phase gradient at zero phase"
+    # a common shift of every phase leaves W, hence every gradient, unchanged
+    phi = r.uniform(0, 2 * np.pi, n)
+    r1 = odense.dense_phased_backward(a, phi, x, g)
+    r2 = odense.dense_phased_backward(a, phi + 0.7, x, g)
+    for u, v, nm in zip(r1, r2, ("dx", "da", "dphi")):
+        _close(u, v, 1e-12, "phased backward under a common phase shift: " + nm)
+    rows = np.array([0, 7, 150, n - 1])
+    dar, dpr, env = odense.phased_backward_rows(rows, a, phi, x, g)
+    _close(dar, r1[1][rows], 1e-12, "phased da at rows vs whole")
+    _close(dpr, r1[2][rows], 1e-12, "phased dphi at rows vs whole")
+    assert np.all(env >= np.abs(dar)) and np.all(env >= np.abs(dpr))
+
+
 ALL_PINS = [
     pin_sort_definition,
     pin_sort_rejects_nonfinite,
@@ -618,4 +681,5 @@ ALL_PINS = [
     pin_gram_kms,
     pin_gram_continuum,
     pin_gram_symmetric_psd,
+    pin_phased_backward,
 ]

@@ -125,3 +125,20 @@ def test_gram_mutant_is_caught(name, monkeypatch, oracle_lib):
     monkeypatch.setattr(odense, "_gram_combine", GRAM_MUTANTS[name])
     failed = _any_pin_fails(oracle_lib)
     assert failed, "planted mistake %s in the Gram oracle passed every pin" % name
+
+
+PHASED_BWD_MUTANTS = {
+    "phase_terms_swapped": ("_phase_terms", lambda P: (np.sin(P), np.cos(P))),
+    "phase_sine_sign": ("_phase_terms", lambda P: (np.cos(P), -np.sin(P))),
+    "phase_sum": ("_phase_terms", lambda P: (np.cos(P), np.sin(P) * np.cos(P))),
+    "row_term_only": ("_sym_fold", lambda row, col: row),
+    "column_term_subtracted": ("_sym_fold", lambda row, col: row - col),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PHASED_BWD_MUTANTS))
+def test_phased_backward_mutant_is_caught(name, monkeypatch, oracle_lib):
+    attr, fn = PHASED_BWD_MUTANTS[name]
+    monkeypatch.setattr(odense, attr, fn)
+    failed = _any_pin_fails(oracle_lib)
+    assert failed, "planted mistake %s in the phased backward passed every pin" % name
