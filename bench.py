@@ -73,6 +73,8 @@ def kernel_bytes(name: str, units: int, m: int, k: int = 0) -> float:
         "k_bwd_apply": 8.0 + 12.0 * m,           # sorted anchors, x and g rows in; dx rows and da out
         "k_scatter_rows": 4.0 + 8.0 * m,         # perm, sorted rows in, rows out (random)
         "k_gbwd_reduce": 4.0 + 4.0 * m,          # merged anchors, x rows (at b) and g rows (at a)
+        "k_pbwd_reduce": 8.0 + 8.0 * m,          # sorted anchors and phases, x and g rows
+        "k_pbwd_apply": 16.0 + 12.0 * m,         # anchors, phases, x and g rows in; dx rows, da, dphi out
         "k_gram_fill": 4.0,                      # per entry of M: written once (row/column families are O(n))
         "k_gram_families": 8.0,                  # merged anchors and weights in; families out at a (20 B per a)
         "k_gram_double": 8.0,                    # anchors in and doubled anchors out
@@ -310,7 +312,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-route", action="store_true", help="move x and y by index instead of along the sort route")
     ap.add_argument("--cpu-sample-log2", type=int, default=25)
-    ap.add_argument("--no-backward", action="store_true", help="skip timing the backward of the symmetric workloads")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the backward (symmetric, general, phased)")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing (steps after a 512 MiB scrub)")
     ap.add_argument("--no-graph", action="store_true", help="skip timing the step replayed from a HIP graph")
     ap.add_argument("--calib-copy", action="store_true",
@@ -525,7 +527,7 @@ def main():
         "source_hash": src,
         "host_gen_s": round(t_gen, 1),
     }
-    if w.kind in ("sym", "general") and not args.no_backward:
+    if w.kind in ("sym", "general", "phased") and not args.no_backward:
         gen = torch.Generator(device=dev).manual_seed(0x6AAD)
         g = torch.randn((n,) if x.dim() == 1 else (n, m), generator=gen, device=dev)
         da = torch.empty(n, dtype=torch.float32, device=dev)
@@ -536,6 +538,13 @@ def main():
             def bstep():
                 lp.laplex_backward_sym(a_s, pa, x, g, dx=dx, da=da, ws=ws_b, route=ra)
             what = "dx = K g and da, from x and g"
+        elif w.kind == "phased":
+            ws_b = lp.workspace(lp.LAPLEX_OP_PHASED_BACKWARD, n, 0, m, device=dev)
+            dphi = torch.empty(n, dtype=torch.float32, device=dev)
+
+            def bstep():
+                lp.laplex_backward_phased(a_s, pa, phi, x, g, dx=dx, da=da, dphi=dphi, ws=ws_b, route=ra)
+            what = "dx = W g, da and dphi, from x and g"
         else:
             ws_b = lp.workspace(lp.LAPLEX_OP_GENERAL_BACKWARD, n, k, m, device=dev)
             db = torch.empty(k, dtype=torch.float32, device=dev)

@@ -62,7 +62,8 @@ enum {
   LAPLEX_OP_PHASED_GENERAL = 4, /* phased operator with a != b */
   LAPLEX_OP_SYM_BACKWARD = 5,   /* backward of the symmetric operator */
   LAPLEX_OP_GENERAL_BACKWARD = 6, /* backward of the general operator */
-  LAPLEX_OP_GRAM = 7              /* weighted Gram matrix */
+  LAPLEX_OP_GRAM = 7,             /* weighted Gram matrix */
+  LAPLEX_OP_PHASED_BACKWARD = 8   /* backward of the symmetric phased operator */
 };
 
 /* Bytes of workspace one call of `op` needs for n output anchors, k input
@@ -147,6 +148,22 @@ laplex_status laplex_matvec_phased(const float* a_sorted, const uint32_t* perm_a
 laplex_status laplex_backward_sym(const float* a_sorted, const uint32_t* perm, const void* route, uint64_t n, uint32_t m,
                                   const float* x, const float* g, float* dx, float* da, void* ws, size_t ws_bytes,
                                   hipStream_t stream);
+
+/* Backward of the symmetric phased operator y = LAPLEX(a, phi; a, phi) x
+ * (technical summary, section 2.1, phased extension; anchors and phases are
+ * both trainable).  For g = dL/dy, with W_ij = exp(-|a_i - a_j|) cos(phi_i - phi_j):
+ *     dx     = W g                                                    (n x m)
+ *     da_i   = - sum_jc sign(a_i - a_j) W_ij (g_ic x_jc + x_ic g_jc)   (n)
+ *     dphi_i = - sum_jc exp(-|a_i - a_j|) sin(phi_i - phi_j) (g_ic x_jc + x_ic g_jc)   (n)
+ * with sign(0) = 0.  Computed from scans of cos(phi) x, sin(phi) x,
+ * cos(phi) g and sin(phi) g, each with the kernel's decay and summed over tied
+ * anchors only.  a_sorted, perm, route: sort handle of a (route may be NULL);
+ * phi: n phases, x, g: n x m (inputs, original order); dx: n x m, da, dphi: n
+ * (outputs, original order, overlapping nothing).
+ * ws: laplex_workspace_bytes(LAPLEX_OP_PHASED_BACKWARD, n, 0, m) bytes. */
+laplex_status laplex_backward_phased(const float* a_sorted, const uint32_t* perm, const void* route, const float* phi,
+                                     uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da,
+                                     float* dphi, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Backward of the general operator y = LAPLEX(a, b) x (rows a, n; columns b,
  * k; same section and chain rule as the symmetric backward): for g = dL/dy,

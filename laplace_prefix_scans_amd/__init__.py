@@ -11,6 +11,7 @@ not been built the calls raise -- there is no fallback.
     y = laplex_matvec_phased(a_sorted, perm, phi, x)  # extra cos(phi_i - phi_j)
     dx, da = laplex_backward_sym(a_sorted, perm, x, g)  # gradients for g = dL/dy
     dxb, da, db = laplex_backward_general(a_sorted, perm, b_sorted, perm_b, xb, g)
+    dx, da, dphi = laplex_backward_phased(a_sorted, perm, phi, x, g)
     M = laplex_gram_weighted(a_sorted, perm, b_sorted, perm_b, D)  # A diag(D) A^T
 """
 from ._binding import (  # noqa: F401
@@ -18,6 +19,7 @@ from ._binding import (  # noqa: F401
     LAPLEX_OP_GENERAL_BACKWARD,
     LAPLEX_OP_GRAM,
     LAPLEX_OP_PHASED,
+    LAPLEX_OP_PHASED_BACKWARD,
     LAPLEX_OP_PHASED_GENERAL,
     LAPLEX_OP_SORT,
     LAPLEX_OP_SYM,
@@ -26,6 +28,7 @@ from ._binding import (  # noqa: F401
     lib,
     lib_path,
     laplex_backward_general,
+    laplex_backward_phased,
     laplex_backward_sym,
     laplex_gram_weighted,
     laplex_matvec_general,

@@ -15,6 +15,7 @@ LAPLEX_OP_SORT, LAPLEX_OP_SYM, LAPLEX_OP_GENERAL, LAPLEX_OP_PHASED, LAPLEX_OP_PH
 LAPLEX_OP_SYM_BACKWARD = 5
 LAPLEX_OP_GENERAL_BACKWARD = 6
 LAPLEX_OP_GRAM = 7
+LAPLEX_OP_PHASED_BACKWARD = 8
 
 _STATUS = {
     0: "LAPLEX_OK", 1: "LAPLEX_ERR_NULL", 2: "LAPLEX_ERR_SIZE", 3: "LAPLEX_ERR_ALIGN", 4: "LAPLEX_ERR_WORKSPACE",
@@ -61,6 +62,8 @@ def lib():
         L.laplex_backward_general.restype = i32
         L.laplex_gram_weighted.argtypes = [vp, vp, u64, vp, vp, u64, vp, u64, u64, vp, u64, vp, sz, vp]
         L.laplex_gram_weighted.restype = i32
+        L.laplex_backward_phased.argtypes = [vp, vp, vp, vp, u64, u32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.laplex_backward_phased.restype = i32
         for f in (L.laplex_sort_anchors, L.laplex_status_poll, L.laplex_matvec_sym, L.laplex_matvec_general,
                   L.laplex_matvec_phased):
             f.restype = i32
@@ -203,6 +206,32 @@ def laplex_backward_sym(a_sorted: torch.Tensor, perm: torch.Tensor, x: torch.Ten
     _check(lib().laplex_backward_sym(_ptr(a_sorted), _ptr(perm), _ptr(route), n, m, _ptr(x), _ptr(g), _ptr(dx), _ptr(da),
                                      _ptr(ws), ws.numel(), _stream(dev)), "laplex_backward_sym")
     return dx, da
+
+
+def laplex_backward_phased(a_sorted: torch.Tensor, perm: torch.Tensor, phi: torch.Tensor, x: torch.Tensor, g: torch.Tensor,
+                           dx: Optional[torch.Tensor] = None, da: Optional[torch.Tensor] = None,
+                           dphi: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                           route: Optional[torch.Tensor] = None):
+    """Backward of the symmetric phased operator y = LAPLEX(a, phi; a, phi) x for g = dL/dy:
+    returns (dx, same shape as x; da, (n,); dphi, (n,))."""
+    _vec(a_sorted, "a_sorted")
+    _vec(perm, "perm", torch.uint32)
+    _vec(phi, "phi")
+    n, dev = a_sorted.shape[0], a_sorted.device
+    if phi.shape[0] != n:
+        raise ValueError("phi must have one phase per anchor")
+    m = _cols(x, n)
+    if _cols(g, n, "g") != m:
+        raise ValueError("g must have the shape of x")
+    dx = torch.empty_like(g) if dx is None else dx
+    _cols(dx, n, "dx")
+    da = torch.empty(n, dtype=torch.float32, device=dev) if da is None else _vec(da, "da")
+    dphi = torch.empty(n, dtype=torch.float32, device=dev) if dphi is None else _vec(dphi, "dphi")
+    ws = _ws(ws, LAPLEX_OP_PHASED_BACKWARD, n, 0, m, dev)
+    _check(lib().laplex_backward_phased(_ptr(a_sorted), _ptr(perm), _ptr(route), _ptr(phi), n, m, _ptr(x), _ptr(g),
+                                        _ptr(dx), _ptr(da), _ptr(dphi), _ptr(ws), ws.numel(), _stream(dev)),
+           "laplex_backward_phased")
+    return dx, da, dphi
 
 
 def laplex_backward_general(a_sorted: torch.Tensor, perm_a: torch.Tensor, b_sorted: torch.Tensor, perm_b: torch.Tensor,

@@ -84,23 +84,27 @@ ApplyWorkspace carve_apply(void* ws, uint64_t rows_in, uint64_t rows_out, uint64
   return w;
 }
 
-// Symmetric (k = 0, general false) or general backward: gathered inputs,
-// sorted-order outputs, tile summaries of width 4m over the n (+ k) scanned
-// elements, and route scratch when m is small enough for routes.
-BackwardWorkspace carve_backward(void* ws, uint64_t n, uint64_t k, uint32_t m, bool general, size_t* total) {
+// Symmetric (k = 0, general false), general, or symmetric phased backward:
+// gathered inputs, sorted-order outputs, tile summaries (width 4m, or 8m
+// phased) over the n (+ k) scanned elements, and route scratch when m is small
+// enough for routes.
+BackwardWorkspace carve_backward(void* ws, uint64_t n, uint64_t k, uint32_t m, bool general, size_t* total,
+                                 bool phased = false) {
   Carver c(ws);
   BackwardWorkspace bw{};
   ApplyWorkspace& w = bw.w;
   const uint64_t rows_x = general ? k : n;  // rows of x and dx
-  const uint64_t T = backward_tiles(general ? n + k : n, m);
-  const uint64_t M = 4ull * m;
+  const uint64_t T = phased ? phased_backward_tiles(n, m) : backward_tiles(general ? n + k : n, m);
+  const uint64_t M = (phased ? 8ull : 4ull) * m;
   // one symmetric column moves x with g as rows of two
-  const uint64_t mp = (!general && m == 1) ? 2 : m;
+  const uint64_t mp = (!general && !phased && m == 1) ? 2 : m;
   w.xs = c.take<float>(rows_x * mp * 4);
   bw.gs = c.take<float>(n * m * 4);
   w.zs = c.take<float>(rows_x * m * 4);
   bw.das = c.take<float>(n * 4);
   bw.dbs = general ? c.take<float>(k * 4) : nullptr;
+  w.phs = phased ? c.take<float>(n * 4) : nullptr;
+  bw.dphs = phased ? c.take<float>(n * 4) : nullptr;
   w.bf = c.take<float>(T * M * 4);
   w.bb = c.take<float>(T * M * 4);
   w.cf = c.take<float>(T * M * 4);
@@ -179,6 +183,7 @@ extern "C" size_t laplex_workspace_bytes(int op, uint64_t n, uint64_t k, uint32_
     case LAPLEX_OP_SYM_BACKWARD: carve_backward(nullptr, n, 0, m, false, &total); return total;
     case LAPLEX_OP_GENERAL_BACKWARD: carve_backward(nullptr, n, k, m, true, &total); return total;
     case LAPLEX_OP_GRAM: carve_gram(nullptr, n, k, &total); return total;
+    case LAPLEX_OP_PHASED_BACKWARD: carve_backward(nullptr, n, 0, m, false, &total, true); return total;
     default: return 0;
   }
 }
@@ -274,6 +279,36 @@ extern "C" laplex_status laplex_backward_sym(const float* a_sorted, const uint32
   SortRoute r{};
   if (route) r = carve_route(route, n);
   return from_hip(backward_sym(bw, a_sorted, perm, route ? &r : nullptr, n, m, x, g, dx, da, stream));
+}
+
+extern "C" laplex_status laplex_backward_phased(const float* a_sorted, const uint32_t* perm, const void* route, const float* phi,
+                                                uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da,
+                                                float* dphi, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (n == 0 || m == 0) return LAPLEX_OK;
+  laplex_status st = check_apply_common(a_sorted, perm, n, m, x, dx, ws);
+  if (st != LAPLEX_OK) return st;
+  if (!phi || !g || !da || !dphi) return LAPLEX_ERR_NULL;
+  if (misaligned(phi, 4) || misaligned(g, 4) || misaligned(da, 4) || misaligned(dphi, 4) || (route && misaligned(route, 256)))
+    return LAPLEX_ERR_ALIGN;
+  size_t need = 0;
+  carve_backward(nullptr, n, 0, m, false, &need, true);
+  if (ws_bytes < need) return LAPLEX_ERR_WORKSPACE;
+  const size_t xb = n * (size_t)m * 4, vb = n * 4, rb = route ? route_bytes(n) : 0;
+  const void* outs[3] = {dx, da, dphi};
+  const size_t outb[3] = {xb, vb, vb};
+  for (int o = 0; o < 3; ++o) {
+    const void* p = outs[o];
+    const size_t pb = outb[o];
+    if (overlaps(p, pb, x, xb) || overlaps(p, pb, g, xb) || overlaps(p, pb, phi, vb) || overlaps(p, pb, a_sorted, vb) ||
+        overlaps(p, pb, perm, vb) || overlaps(p, pb, ws, ws_bytes) || overlaps(p, pb, route, rb))
+      return LAPLEX_ERR_OVERLAP;
+    for (int q = o + 1; q < 3; ++q)
+      if (overlaps(p, pb, outs[q], outb[q])) return LAPLEX_ERR_OVERLAP;
+  }
+  const BackwardWorkspace bw = carve_backward(ws, n, 0, m, false, nullptr, true);
+  SortRoute r{};
+  if (route) r = carve_route(route, n);
+  return from_hip(backward_phased(bw, a_sorted, perm, route ? &r : nullptr, phi, n, m, x, g, dx, da, dphi, stream));
 }
 
 extern "C" laplex_status laplex_backward_general(const float* a_sorted, const uint32_t* perm_a, const void* route_a, uint64_t n,

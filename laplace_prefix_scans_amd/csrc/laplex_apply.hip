@@ -1184,6 +1184,249 @@ hipError_t backward_sym(const BackwardWorkspace& bw, const float* a_s, const uin
   }
 }
 
+// ---------------------------------------------------------------- phased backward
+// Backward of the symmetric phased operator y_i = sum_j K_ij cos(phi_i - phi_j) x_j
+// (K_ij = exp(-|a_i - a_j|)) for g = dL/dy.  Per input column four real columns
+// are scanned: cx = cos(phi) x, sx = sin(phi) x, cg = cos(phi) g, sg = sin(phi) g.
+// With K(v) = F + U and S(v) = (F - U) - (F0 - U0) as in the symmetric backward
+// (angle-difference identity applied to every entry and its derivatives):
+//     dx_i   = cos phi_i K(cg)_i + sin phi_i K(sg)_i,
+//     da_i   = -sum_c [ g (cos S(cx) + sin S(sx)) + x (cos S(cg) + sin S(sg)) ]_i,
+//     dphi_i =  sum_c [ -g (sin K(cx) - cos K(sx)) + x (cos K(sg) - sin K(cg)) ]_i.
+// Summary columns (M = 8m): kind q (cx, sx, cg, sg) at [q m, (q + 1) m) with
+// the kernel's decay, and 4m + the same with the tie decay.
+template <int C>
+__device__ __forceinline__ uint32_t pbwdcol(uint32_t m, uint32_t cc, int j) {
+  const uint32_t mode = (uint32_t)j / (4 * C), kind = ((uint32_t)j / C) % 4, col = (uint32_t)j % C;
+  return mode * 4 * m + kind * m + cc * C + col;
+}
+constexpr int pbwd_items(int c) { return apply_items(4 * c); }
+constexpr int pbwd_block(int c) { return apply_block(4 * c); }
+
+// the four scanned values of element e, column j
+template <int E, int C>
+__device__ __forceinline__ void phased_quad(const float (&cs)[E], const float (&sn)[E], const float (&xv)[E][C],
+                                            const float (&gv)[E][C], float (&v)[E][4 * C]) {
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      v[e][j] = cs[e] * xv[e][j];
+      v[e][C + j] = sn[e] * xv[e][j];
+      v[e][2 * C + j] = cs[e] * gv[e][j];
+      v[e][3 * C + j] = sn[e] * gv[e][j];
+    }
+}
+
+template <int C>
+__global__ __launch_bounds__(pbwd_block(C)) void k_pbwd_reduce(const float* __restrict__ a_s, const float* __restrict__ xs,
+                                                               const float* __restrict__ gs, const float* __restrict__ phs,
+                                                               uint64_t n, uint32_t m, float* __restrict__ bf,
+                                                               float* __restrict__ bb, float2* __restrict__ tanch, bool vec) {
+  constexpr int CC = 8 * C;
+  constexpr int E = pbwd_items(C);
+  constexpr int BLOCK = pbwd_block(C);
+  constexpr int NW = BLOCK / kWave;
+  constexpr int P = BLOCK * E;
+  __shared__ float s_red[2 * NW * CC];
+  const uint32_t M = 8 * m;
+  const int tid = threadIdx.x;
+  const uint64_t tile = blockIdx.x;
+  const uint64_t lo = tile * P;
+  const uint64_t hi = std::min<uint64_t>(n, lo + P);
+  const float s_first = a_s[lo], s_last = a_s[hi - 1];
+  if (tid == 0) tanch[tile] = make_float2(s_first, s_last);
+  const uint64_t p0 = lo + (uint64_t)tid * E;
+  float ae[E], ph[E], cs[E], sn[E], wf[E], wb[E], tf[E], tb[E];
+  load_anchors<E>(a_s, p0, n, s_last, vec, ae);
+  load_anchors<E>(phs, p0, n, 0.f, true, ph);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    sincosf(ph[e], &sn[e], &cs[e]);
+    const bool valid = p0 + e < n;
+    wf[e] = valid ? decay(ae[e] - s_last) : 0.f;
+    wb[e] = valid ? decay(s_first - ae[e]) : 0.f;
+    tf[e] = valid ? decay_m<true>(ae[e] - s_last) : 0.f;
+    tb[e] = valid ? decay_m<true>(s_first - ae[e]) : 0.f;
+  }
+  for (uint32_t cc = 0; cc < m / C; ++cc) {
+    float xv[E][C], gv[E][C], v[E][4 * C];
+    load_rows<E, C>(xs, p0, n, m, cc, true, xv);
+    load_rows<E, C>(gs, p0, n, m, cc, true, gv);
+    phased_quad<E, C>(cs, sn, xv, gv, v);
+    float sf[CC], sb[CC];
+#pragma unroll
+    for (int j = 0; j < CC; ++j) sf[j] = sb[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int j = 0; j < 4 * C; ++j) {
+        sf[j] = fmaf(wf[e], v[e][j], sf[j]);
+        sb[j] = fmaf(wb[e], v[e][j], sb[j]);
+        sf[4 * C + j] = fmaf(tf[e], v[e][j], sf[4 * C + j]);
+        sb[4 * C + j] = fmaf(tb[e], v[e][j], sb[4 * C + j]);
+      }
+    int writer = 0;
+    block_sum2<CC, NW>(sf, sb, s_red, writer);
+    if (writer) {
+      float f = 0.f, b = 0.f;
+      for (int w = 0; w < NW; ++w) {
+        f += s_red[(0 * NW + w) * CC + tid];
+        b += s_red[(1 * NW + w) * CC + tid];
+      }
+      const uint32_t col = pbwdcol<C>(m, cc, tid);
+      bf[tile * M + col] = f;
+      bb[tile * M + col] = b;
+    }
+    __syncthreads();
+  }
+}
+
+template <int C>
+__global__ __launch_bounds__(pbwd_block(C)) void k_pbwd_apply(const float* __restrict__ a_s, const float* __restrict__ xs,
+                                                              const float* __restrict__ gs, const float* __restrict__ phs,
+                                                              const float* __restrict__ cfw, const float* __restrict__ cbw,
+                                                              const float2* __restrict__ tanch, uint64_t n, uint32_t m, uint64_t T,
+                                                              float* __restrict__ dxs, float* __restrict__ das,
+                                                              float* __restrict__ dphs, bool vec) {
+  constexpr int CC = 4 * C;  // columns of one scan (cx, sx, cg, sg)
+  constexpr int E = pbwd_items(C);
+  constexpr int BLOCK = pbwd_block(C);
+  constexpr int NW = BLOCK / kWave;
+  constexpr int P = BLOCK * E;
+  __shared__ float s_wf[NW * CC], s_wb[NW * CC], s_wfs[NW], s_wbs[NW];
+  const uint32_t M = 8 * m;
+  const int tid = threadIdx.x;
+  const uint64_t tile = blockIdx.x;
+  const uint64_t p0 = tile * P + (uint64_t)tid * E;
+  float ae[E], ph[E], cs[E], sn[E];
+  load_anchors<E>(a_s, p0, n, a_s[n - 1], vec, ae);
+  load_anchors<E>(phs, p0, n, 0.f, true, ph);
+#pragma unroll
+  for (int e = 0; e < E; ++e) sincosf(ph[e], &sn[e], &cs[e]);
+  const float2 ta = tanch[tile];
+  const float sf = tile > 0 ? tanch[tile - 1].y : ta.x;
+  const float sb = tile + 1 < T ? tanch[tile + 1].x : ta.y;
+  float acc[E], acc0[E], dph[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = acc0[e] = dph[e] = 0.f;
+  for (uint32_t cc = 0; cc < m / C; ++cc) {
+    float xv[E][C], gv[E][C], v[E][CC];
+    load_rows<E, C>(xs, p0, n, m, cc, true, xv);
+    load_rows<E, C>(gs, p0, n, m, cc, true, gv);
+    phased_quad<E, C>(cs, sn, xv, gv, v);
+    {
+      float ct_f[CC], ct_b[CC];
+#pragma unroll
+      for (int j = 0; j < CC; ++j) {
+        ct_f[j] = cfw[tile * M + pbwdcol<C>(m, cc, CC + j)];
+        ct_b[j] = cbw[tile * M + pbwdcol<C>(m, cc, CC + j)];
+      }
+      float F0[E][CC], U0[E][CC];
+      tile_scan_fu<E, CC, NW, true>(ae, v, ct_f, sf, ct_b, sb, s_wf, s_wfs, s_wb, s_wbs, F0, U0);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+          const float scx = F0[e][j] - U0[e][j], ssx = F0[e][C + j] - U0[e][C + j];
+          const float scg = F0[e][2 * C + j] - U0[e][2 * C + j], ssg = F0[e][3 * C + j] - U0[e][3 * C + j];
+          acc0[e] = fmaf(gv[e][j], fmaf(cs[e], scx, sn[e] * ssx), acc0[e]);
+          acc0[e] = fmaf(xv[e][j], fmaf(cs[e], scg, sn[e] * ssg), acc0[e]);
+        }
+    }
+    __syncthreads();  // the second scan reuses the wave summaries
+    {
+      float ce_f[CC], ce_b[CC];
+#pragma unroll
+      for (int j = 0; j < CC; ++j) {
+        ce_f[j] = cfw[tile * M + pbwdcol<C>(m, cc, j)];
+        ce_b[j] = cbw[tile * M + pbwdcol<C>(m, cc, j)];
+      }
+      float F[E][CC], U[E][CC];
+      tile_scan_fu<E, CC, NW, false>(ae, v, ce_f, sf, ce_b, sb, s_wf, s_wfs, s_wb, s_wbs, F, U);
+      float dx[E][C];
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+          const float scx = F[e][j] - U[e][j], ssx = F[e][C + j] - U[e][C + j];
+          const float scg = F[e][2 * C + j] - U[e][2 * C + j], ssg = F[e][3 * C + j] - U[e][3 * C + j];
+          acc[e] = fmaf(gv[e][j], fmaf(cs[e], scx, sn[e] * ssx), acc[e]);
+          acc[e] = fmaf(xv[e][j], fmaf(cs[e], scg, sn[e] * ssg), acc[e]);
+          const float kcx = F[e][j] + U[e][j], ksx = F[e][C + j] + U[e][C + j];
+          const float kcg = F[e][2 * C + j] + U[e][2 * C + j], ksg = F[e][3 * C + j] + U[e][3 * C + j];
+          dph[e] = fmaf(-gv[e][j], fmaf(sn[e], kcx, -cs[e] * ksx), dph[e]);
+          dph[e] = fmaf(xv[e][j], fmaf(cs[e], ksg, -sn[e] * kcg), dph[e]);
+          dx[e][j] = fmaf(cs[e], kcg, sn[e] * ksg);
+        }
+      store_rows<E, C>(dxs, p0, n, m, cc, true, dx);
+    }
+    __syncthreads();
+  }
+  float dav[E][1], dpv[E][1];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    dav[e][0] = acc0[e] - acc[e];
+    dpv[e][0] = dph[e];
+  }
+  store_rows<E, 1>(das, p0, n, 1, 0, true, dav);
+  store_rows<E, 1>(dphs, p0, n, 1, 0, true, dpv);
+}
+
+template <int C>
+static hipError_t run_pbwd_sym(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm, const SortRoute* route,
+                               const float* phi, uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da,
+                               float* dphi, hipStream_t s) {
+  const ApplyWorkspace& w = bw.w;
+  constexpr int P = pbwd_block(C) * pbwd_items(C);
+  const uint64_t T = (n + P - 1) / P;
+  const uint32_t M = 8 * m;
+  const dim3 grid((unsigned)T), block(pbwd_block(C));
+  const bool routed = route != nullptr && m <= kRouteMaxCols;
+  const bool vec = (reinterpret_cast<uintptr_t>(a_s) & 15) == 0;
+  hipError_t e;
+  if (routed) {
+    if ((e = route_forward(*route, n, m, x, w.xs, w.t0, w.t1, s)) != hipSuccess) return e;
+    if ((e = route_forward(*route, n, m, g, bw.gs, w.t0, w.t1, s)) != hipSuccess) return e;
+    if ((e = route_forward(*route, n, 1, phi, w.phs, w.t0, w.t1, s)) != hipSuccess) return e;
+  } else {
+    LAPLEX_LAUNCH("k_gather_rows", n, s, k_gather_rows<<<rows_grid(n), 256, 0, s>>>(x, perm, phi, n, m, w.xs, w.phs));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    LAPLEX_LAUNCH("k_gather_rows", n, s, k_gather_rows<<<rows_grid(n), 256, 0, s>>>(g, perm, nullptr, n, m, bw.gs, nullptr));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  LAPLEX_LAUNCH("k_pbwd_reduce", n, s,
+                k_pbwd_reduce<C><<<grid, block, 0, s>>>(a_s, w.xs, bw.gs, w.phs, n, m, w.bf, w.bb, w.tanch, vec));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = tile_carries(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb, w.gbf, w.gbb, w.gcf, w.gcb, w.ganch, s, 4 * m)) != hipSuccess)
+    return e;
+  LAPLEX_LAUNCH("k_pbwd_apply", n, s,
+                k_pbwd_apply<C><<<grid, block, 0, s>>>(a_s, w.xs, bw.gs, w.phs, w.cf, w.cb, w.tanch, n, m, T, w.zs, bw.das,
+                                                       bw.dphs, vec));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (routed) {
+    if ((e = route_inverse(*route, n, m, w.zs, dx, w.t0, w.t1, s)) != hipSuccess) return e;
+    if ((e = route_inverse(*route, n, 1, bw.das, da, w.t0, w.t1, s)) != hipSuccess) return e;
+    return route_inverse(*route, n, 1, bw.dphs, dphi, w.t0, w.t1, s);
+  }
+  LAPLEX_LAUNCH("k_scatter_rows", n, s, k_scatter_rows<<<rows_grid(n), 256, 0, s>>>(w.zs, perm, n, m, dx));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  LAPLEX_LAUNCH("k_scatter_rows", n, s, k_scatter_rows<<<rows_grid(n), 256, 0, s>>>(bw.das, perm, n, 1, da));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  LAPLEX_LAUNCH("k_scatter_rows", n, s, k_scatter_rows<<<rows_grid(n), 256, 0, s>>>(bw.dphs, perm, n, 1, dphi));
+  return hipGetLastError();
+}
+
+hipError_t backward_phased(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm, const SortRoute* route,
+                           const float* phi, uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da,
+                           float* dphi, hipStream_t s) {
+  switch (phased_chunk(m)) {
+    case 4: return run_pbwd_sym<4>(bw, a_s, perm, route, phi, n, m, x, g, dx, da, dphi, s);
+    case 2: return run_pbwd_sym<2>(bw, a_s, perm, route, phi, n, m, x, g, dx, da, dphi, s);
+    default: return run_pbwd_sym<1>(bw, a_s, perm, route, phi, n, m, x, g, dx, da, dphi, s);
+  }
+}
+
 // ---------------------------------------------------------------- general (merged a and b)
 // Number of a elements among the first d elements of the merge of sorted a
 // (length n) and sorted b (length k), b placed first on equal anchors.

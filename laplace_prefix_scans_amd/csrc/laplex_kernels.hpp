@@ -125,9 +125,22 @@ struct BackwardWorkspace {
   float* gs;   // upstream gradient gathered into sorted(-a) order (n x m)
   float* das;  // anchor gradient in sorted(-a) order (n)
   float* dbs;  // column-anchor gradient in sorted-b order (k; general only)
+  float* dphs; // phase gradient in sorted order (n; phased only)
 };
 hipError_t backward_sym(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm, const SortRoute* route,
                         uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da, hipStream_t s);
+
+// Backward of the symmetric phased operator: dx (n x m), da, dphi (n).  Scans
+// four columns per input column (cos/sin phase times x and g) under both
+// decays: summary width M = 8m, tiles of the 4-column shape; xs, gs, phs hold
+// x, g, phi in sorted order, zs dx in sorted order.
+hipError_t backward_phased(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm, const SortRoute* route,
+                           const float* phi, uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da,
+                           float* dphi, hipStream_t s);
+inline uint64_t phased_backward_tiles(uint64_t n, uint32_t m) {
+  const uint64_t tile = (uint64_t)apply_tile(4 * (int)phased_chunk(m));
+  return (n + tile - 1) / tile;
+}
 
 // Backward of the general operator (rows a, n; columns b, k): dx = K^T g
 // (k x m), da (n), db (k).  One scan over the merge of a and b with summary

@@ -46,7 +46,7 @@ def test_workspace_sizes(L):
     assert lp.laplex_workspace_bytes(99, 10) == 0
     assert lp.laplex_workspace_bytes(lp.LAPLEX_OP_GENERAL_BACKWARD, 1 << 20, 1 << 10, 2) > \
         lp.laplex_workspace_bytes(lp.LAPLEX_OP_GENERAL, 1 << 20, 1 << 10, 2)
-    for op in range(8):
+    for op in range(9):
         a = lp.laplex_workspace_bytes(op, 4096, 100, 1)
         b = lp.laplex_workspace_bytes(op, 1 << 22, 1 << 20, 1)
         assert a % 256 == 0 and b % 256 == 0 and b >= a
@@ -101,6 +101,17 @@ def test_host_argument_errors(L):
     bad = list(args)
     bad[12] = vp(0xA00002)  # da misaligned
     assert GB(*bad, need, None) == ALIGN
+    # phased backward: no-op, NULL phases, workspace, overlap of dphi with phi
+    PB = L.laplex_backward_phased
+    assert PB(None, None, None, None, 0, 1, None, None, None, None, None, None, 0, None) == OK
+    assert PB(A, B, None, None, 10, 1, A, A, B, B, B, W, 1 << 30, None) == NULL
+    needp = L.laplex_workspace_bytes(8, 1000, 0, 2)
+    pargs = [A, vp(0x300000), None, vp(0x500000), 1000, 2, vp(0x600000), vp(0x700000), vp(0x800000), vp(0x900000),
+             vp(0xA00000), vp(0x10000000)]
+    assert PB(*pargs, 64, None) == WS
+    bad = list(pargs)
+    bad[10] = vp(0x500100)  # dphi inside phi
+    assert PB(*bad, needp, None) == OVERLAP
     # weighted Gram: no-ops, row range, NULL, workspace, overlap of M with the weights
     GW = L.laplex_gram_weighted
     assert GW(None, None, 0, None, None, 0, None, 0, 1, None, 0, None, 0, None) == OK
