@@ -1417,14 +1417,13 @@ static hipError_t run_pbwd_sym(const BackwardWorkspace& bw, const float* a_s, co
   return hipGetLastError();
 }
 
+// One input column per pass: its 4 scanned columns leave a thread 4 elements
+// (wider chunks put 8 or 16 scanned columns on 2 or 1 elements per thread and
+// ran up to twice as long).
 hipError_t backward_phased(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm, const SortRoute* route,
                            const float* phi, uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da,
                            float* dphi, hipStream_t s) {
-  switch (phased_chunk(m)) {
-    case 4: return run_pbwd_sym<4>(bw, a_s, perm, route, phi, n, m, x, g, dx, da, dphi, s);
-    case 2: return run_pbwd_sym<2>(bw, a_s, perm, route, phi, n, m, x, g, dx, da, dphi, s);
-    default: return run_pbwd_sym<1>(bw, a_s, perm, route, phi, n, m, x, g, dx, da, dphi, s);
-  }
+  return run_pbwd_sym<kPbwdChunk>(bw, a_s, perm, route, phi, n, m, x, g, dx, da, dphi, s);
 }
 
 // ---------------------------------------------------------------- general (merged a and b)

@@ -137,8 +137,10 @@ hipError_t backward_sym(const BackwardWorkspace& bw, const float* a_s, const uin
 hipError_t backward_phased(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm, const SortRoute* route,
                            const float* phi, uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da,
                            float* dphi, hipStream_t s);
+constexpr int kPbwdChunk = 1;  // input columns per pass of the phased backward
 inline uint64_t phased_backward_tiles(uint64_t n, uint32_t m) {
-  const uint64_t tile = (uint64_t)apply_tile(4 * (int)phased_chunk(m));
+  (void)m;
+  const uint64_t tile = (uint64_t)apply_tile(4 * kPbwdChunk);
   return (n + tile - 1) / tile;
 }
 
