@@ -63,7 +63,8 @@ enum {
   LAPLEX_OP_SYM_BACKWARD = 5,   /* backward of the symmetric operator */
   LAPLEX_OP_GENERAL_BACKWARD = 6, /* backward of the general operator */
   LAPLEX_OP_GRAM = 7,             /* weighted Gram matrix */
-  LAPLEX_OP_PHASED_BACKWARD = 8   /* backward of the symmetric phased operator */
+  LAPLEX_OP_PHASED_BACKWARD = 8,  /* backward of the symmetric phased operator */
+  LAPLEX_OP_PHASED_GENERAL_BACKWARD = 9 /* backward of the phased operator with a != b */
 };
 
 /* Bytes of workspace one call of `op` needs for n output anchors, k input
@@ -164,6 +165,24 @@ laplex_status laplex_backward_sym(const float* a_sorted, const uint32_t* perm, c
 laplex_status laplex_backward_phased(const float* a_sorted, const uint32_t* perm, const void* route, const float* phi,
                                      uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da,
                                      float* dphi, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward of the phased operator y = LAPLEX(a, phi; b, psi) x with a != b
+ * (rows a, phi: n; columns b, psi: k).  For g = dL/dy, with
+ * W_ij = exp(-|a_i - b_j|) cos(phi_i - psi_j):
+ *     dx_j   = sum_i W_ij g_i                                         (k x m)
+ *     da_i   = - sum_jc sign(a_i - b_j) W_ij g_ic x_jc,       db_j   = + sum_ic sign(a_i - b_j) W_ij g_ic x_jc
+ *     dphi_i = - sum_jc exp(-|a_i - b_j|) sin(phi_i - psi_j) g_ic x_jc,
+ *     dpsi_j = + sum_ic exp(-|a_i - b_j|) sin(phi_i - psi_j) g_ic x_jc
+ * (sign(0) = 0), from one pass over the merge of sorted a and b.  Handles as
+ * in laplex_matvec_phased; x: k x m, g: n x m (inputs, original order);
+ * dx: k x m, da, dphi: n, db, dpsi: k (outputs, original order, overlapping
+ * nothing).  k == 0 sets da and dphi to zero; n == 0 sets dx, db, dpsi to zero.
+ * ws: laplex_workspace_bytes(LAPLEX_OP_PHASED_GENERAL_BACKWARD, n, k, m) bytes. */
+laplex_status laplex_backward_phased_general(const float* a_sorted, const uint32_t* perm_a, const void* route_a,
+                                             const float* phi, uint64_t n, const float* b_sorted, const uint32_t* perm_b,
+                                             const void* route_b, const float* psi, uint64_t k, uint32_t m, const float* x,
+                                             const float* g, float* dx, float* da, float* db, float* dphi, float* dpsi,
+                                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Backward of the general operator y = LAPLEX(a, b) x (rows a, n; columns b,
  * k; same section and chain rule as the symmetric backward): for g = dL/dy,

@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     LAPLEX_OP_GRAM,
     LAPLEX_OP_PHASED,
     LAPLEX_OP_PHASED_BACKWARD,
+    LAPLEX_OP_PHASED_GENERAL_BACKWARD,
     LAPLEX_OP_PHASED_GENERAL,
     LAPLEX_OP_SORT,
     LAPLEX_OP_SYM,
@@ -29,6 +30,7 @@ from ._binding import (  # noqa: F401
     lib_path,
     laplex_backward_general,
     laplex_backward_phased,
+    laplex_backward_phased_general,
     laplex_backward_sym,
     laplex_gram_weighted,
     laplex_matvec_general,

@@ -16,6 +16,7 @@ LAPLEX_OP_SYM_BACKWARD = 5
 LAPLEX_OP_GENERAL_BACKWARD = 6
 LAPLEX_OP_GRAM = 7
 LAPLEX_OP_PHASED_BACKWARD = 8
+LAPLEX_OP_PHASED_GENERAL_BACKWARD = 9
 
 _STATUS = {
     0: "LAPLEX_OK", 1: "LAPLEX_ERR_NULL", 2: "LAPLEX_ERR_SIZE", 3: "LAPLEX_ERR_ALIGN", 4: "LAPLEX_ERR_WORKSPACE",
@@ -64,6 +65,9 @@ def lib():
         L.laplex_gram_weighted.restype = i32
         L.laplex_backward_phased.argtypes = [vp, vp, vp, vp, u64, u32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.laplex_backward_phased.restype = i32
+        L.laplex_backward_phased_general.argtypes = [vp, vp, vp, vp, u64, vp, vp, vp, vp, u64, u32, vp, vp, vp, vp, vp, vp,
+                                                     vp, vp, sz, vp]
+        L.laplex_backward_phased_general.restype = i32
         for f in (L.laplex_sort_anchors, L.laplex_status_poll, L.laplex_matvec_sym, L.laplex_matvec_general,
                   L.laplex_matvec_phased):
             f.restype = i32
@@ -232,6 +236,41 @@ def laplex_backward_phased(a_sorted: torch.Tensor, perm: torch.Tensor, phi: torc
                                         _ptr(dx), _ptr(da), _ptr(dphi), _ptr(ws), ws.numel(), _stream(dev)),
            "laplex_backward_phased")
     return dx, da, dphi
+
+
+def laplex_backward_phased_general(a_sorted: torch.Tensor, perm_a: torch.Tensor, phi: torch.Tensor, b_sorted: torch.Tensor,
+                                   perm_b: torch.Tensor, psi: torch.Tensor, x: torch.Tensor, g: torch.Tensor,
+                                   ws: Optional[torch.Tensor] = None, route_a: Optional[torch.Tensor] = None,
+                                   route_b: Optional[torch.Tensor] = None, out=None):
+    """Backward of y = LAPLEX(a, phi; b, psi) x for g = dL/dy (x: (k,) or (k, m); g: (n,) or (n, m)):
+    returns (dx, shape of x; da, (n,); db, (k,); dphi, (n,); dpsi, (k,)).  `out`: optional tuple of
+    the five output tensors."""
+    _vec(a_sorted, "a_sorted")
+    _vec(perm_a, "perm_a", torch.uint32)
+    _vec(phi, "phi")
+    _vec(b_sorted, "b_sorted")
+    _vec(perm_b, "perm_b", torch.uint32)
+    _vec(psi, "psi")
+    n, k, dev = a_sorted.shape[0], b_sorted.shape[0], a_sorted.device
+    if phi.shape[0] != n or psi.shape[0] != k:
+        raise ValueError("phi and psi must have one phase per anchor")
+    m = _cols(x, k)
+    if _cols(g, n, "g") != m or g.dim() != x.dim():
+        raise ValueError("g must have n rows and the columns of x")
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = (torch.empty_like(x), torch.empty(n, **f32), torch.empty(k, **f32), torch.empty(n, **f32),
+               torch.empty(k, **f32))
+    dx, da, db, dphi, dpsi = out
+    _cols(dx, k, "dx")
+    for t, name in ((da, "da"), (db, "db"), (dphi, "dphi"), (dpsi, "dpsi")):
+        _vec(t, name)
+    ws = _ws(ws, LAPLEX_OP_PHASED_GENERAL_BACKWARD, n, k, m, dev)
+    _check(lib().laplex_backward_phased_general(_ptr(a_sorted), _ptr(perm_a), _ptr(route_a), _ptr(phi), n, _ptr(b_sorted),
+                                                _ptr(perm_b), _ptr(route_b), _ptr(psi), k, m, _ptr(x), _ptr(g), _ptr(dx),
+                                                _ptr(da), _ptr(db), _ptr(dphi), _ptr(dpsi), _ptr(ws), ws.numel(),
+                                                _stream(dev)), "laplex_backward_phased_general")
+    return dx, da, db, dphi, dpsi
 
 
 def laplex_backward_general(a_sorted: torch.Tensor, perm_a: torch.Tensor, b_sorted: torch.Tensor, perm_b: torch.Tensor,

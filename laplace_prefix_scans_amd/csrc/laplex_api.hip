@@ -94,7 +94,7 @@ BackwardWorkspace carve_backward(void* ws, uint64_t n, uint64_t k, uint32_t m, b
   BackwardWorkspace bw{};
   ApplyWorkspace& w = bw.w;
   const uint64_t rows_x = general ? k : n;  // rows of x and dx
-  const uint64_t T = phased ? phased_backward_tiles(n, m) : backward_tiles(general ? n + k : n, m);
+  const uint64_t T = phased ? phased_backward_tiles(general ? n + k : n, m) : backward_tiles(general ? n + k : n, m);
   const uint64_t M = (phased ? 8ull : 4ull) * m;
   // one symmetric column moves x with g as rows of two
   const uint64_t mp = (!general && !phased && m == 1) ? 2 : m;
@@ -103,8 +103,10 @@ BackwardWorkspace carve_backward(void* ws, uint64_t n, uint64_t k, uint32_t m, b
   w.zs = c.take<float>(rows_x * m * 4);
   bw.das = c.take<float>(n * 4);
   bw.dbs = general ? c.take<float>(k * 4) : nullptr;
-  w.phs = phased ? c.take<float>(n * 4) : nullptr;
+  w.phs = phased ? c.take<float>(rows_x * 4) : nullptr;           // phases of x's rows, sorted
+  w.phas = (phased && general) ? c.take<float>(n * 4) : nullptr;  // phases of the rows of a, sorted
   bw.dphs = phased ? c.take<float>(n * 4) : nullptr;
+  bw.dpsis = (phased && general) ? c.take<float>(k * 4) : nullptr;
   w.bf = c.take<float>(T * M * 4);
   w.bb = c.take<float>(T * M * 4);
   w.cf = c.take<float>(T * M * 4);
@@ -184,6 +186,7 @@ extern "C" size_t laplex_workspace_bytes(int op, uint64_t n, uint64_t k, uint32_
     case LAPLEX_OP_GENERAL_BACKWARD: carve_backward(nullptr, n, k, m, true, &total); return total;
     case LAPLEX_OP_GRAM: carve_gram(nullptr, n, k, &total); return total;
     case LAPLEX_OP_PHASED_BACKWARD: carve_backward(nullptr, n, 0, m, false, &total, true); return total;
+    case LAPLEX_OP_PHASED_GENERAL_BACKWARD: carve_backward(nullptr, n, k, m, true, &total, true); return total;
     default: return 0;
   }
 }
@@ -309,6 +312,64 @@ extern "C" laplex_status laplex_backward_phased(const float* a_sorted, const uin
   SortRoute r{};
   if (route) r = carve_route(route, n);
   return from_hip(backward_phased(bw, a_sorted, perm, route ? &r : nullptr, phi, n, m, x, g, dx, da, dphi, stream));
+}
+
+extern "C" laplex_status laplex_backward_phased_general(const float* a_sorted, const uint32_t* perm_a, const void* route_a,
+                                                        const float* phi, uint64_t n, const float* b_sorted,
+                                                        const uint32_t* perm_b, const void* route_b, const float* psi,
+                                                        uint64_t k, uint32_t m, const float* x, const float* g, float* dx,
+                                                        float* da, float* db, float* dphi, float* dpsi, void* ws,
+                                                        size_t ws_bytes, hipStream_t stream) {
+  if (m == 0 || (n == 0 && k == 0)) return LAPLEX_OK;
+  if (n > kMaxLen || k > kMaxLen || m > kMaxCols) return LAPLEX_ERR_SIZE;
+  const size_t xb = k * (size_t)m * 4, gb = n * (size_t)m * 4, nb = n * 4, kb = k * 4;
+  if (n == 0 || k == 0) {
+    // no pairs: every gradient is zero (dx, db, dpsi when n == 0; da, dphi when k == 0)
+    if (n == 0) {
+      if (!dx || !db || !dpsi) return LAPLEX_ERR_NULL;
+      if (misaligned(dx, 4) || misaligned(db, 4) || misaligned(dpsi, 4)) return LAPLEX_ERR_ALIGN;
+      if (overlaps(dx, xb, db, kb) || overlaps(dx, xb, dpsi, kb) || overlaps(db, kb, dpsi, kb)) return LAPLEX_ERR_OVERLAP;
+      hipError_t e = fill_zero_u32(dx, k * (uint64_t)m, stream);
+      if (e == hipSuccess) e = fill_zero_u32(db, k, stream);
+      if (e == hipSuccess) e = fill_zero_u32(dpsi, k, stream);
+      return from_hip(e);
+    }
+    if (!da || !dphi) return LAPLEX_ERR_NULL;
+    if (misaligned(da, 4) || misaligned(dphi, 4)) return LAPLEX_ERR_ALIGN;
+    if (overlaps(da, nb, dphi, nb)) return LAPLEX_ERR_OVERLAP;
+    hipError_t e = fill_zero_u32(da, n, stream);
+    if (e == hipSuccess) e = fill_zero_u32(dphi, n, stream);
+    return from_hip(e);
+  }
+  if (!a_sorted || !perm_a || !phi || !b_sorted || !perm_b || !psi || !x || !g || !dx || !da || !db || !dphi || !dpsi || !ws)
+    return LAPLEX_ERR_NULL;
+  const void* ins4[] = {a_sorted, perm_a, phi, b_sorted, perm_b, psi, x, g, dx, da, db, dphi, dpsi};
+  for (const void* p : ins4)
+    if (misaligned(p, 4)) return LAPLEX_ERR_ALIGN;
+  if (misaligned(ws, 256) || (route_a && misaligned(route_a, 256)) || (route_b && misaligned(route_b, 256)))
+    return LAPLEX_ERR_ALIGN;
+  size_t need = 0;
+  carve_backward(nullptr, n, k, m, true, &need, true);
+  if (ws_bytes < need) return LAPLEX_ERR_WORKSPACE;
+  const size_t rab = route_a ? route_bytes(n) : 0, rbb = route_b ? route_bytes(k) : 0;
+  const void* outs[5] = {dx, da, db, dphi, dpsi};
+  const size_t outb[5] = {xb, nb, kb, nb, kb};
+  for (int o = 0; o < 5; ++o) {
+    const void* p = outs[o];
+    const size_t pb = outb[o];
+    if (overlaps(p, pb, x, xb) || overlaps(p, pb, g, gb) || overlaps(p, pb, a_sorted, nb) || overlaps(p, pb, perm_a, nb) ||
+        overlaps(p, pb, phi, nb) || overlaps(p, pb, b_sorted, kb) || overlaps(p, pb, perm_b, kb) || overlaps(p, pb, psi, kb) ||
+        overlaps(p, pb, ws, ws_bytes) || overlaps(p, pb, route_a, rab) || overlaps(p, pb, route_b, rbb))
+      return LAPLEX_ERR_OVERLAP;
+    for (int q = o + 1; q < 5; ++q)
+      if (overlaps(p, pb, outs[q], outb[q])) return LAPLEX_ERR_OVERLAP;
+  }
+  const BackwardWorkspace bw = carve_backward(ws, n, k, m, true, nullptr, true);
+  SortRoute ra{}, rb{};
+  if (route_a) ra = carve_route(route_a, n);
+  if (route_b) rb = carve_route(route_b, k);
+  return from_hip(backward_phased_general(bw, a_sorted, perm_a, route_a ? &ra : nullptr, phi, n, b_sorted, perm_b,
+                                          route_b ? &rb : nullptr, psi, k, m, x, g, dx, da, db, dphi, dpsi, stream));
 }
 
 extern "C" laplex_status laplex_backward_general(const float* a_sorted, const uint32_t* perm_a, const void* route_a, uint64_t n,

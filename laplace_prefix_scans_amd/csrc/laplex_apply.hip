@@ -2150,4 +2150,273 @@ hipError_t gram_weighted(const GramWorkspace& g, const float* a_s, const uint32_
   return fill(false);
 }
 
+
+// ---------------------------------------------------------------- general phased backward
+// Backward of y = LAPLEX(a, phi; b, psi) x (rows a, n; columns b, k) for
+// g = dL/dy.  Over the merge of sorted a and b (b first on ties), cos(psi) x
+// and sin(psi) x are injected at b elements and cos(phi) g, sin(phi) g at a
+// elements; with each element's own phase (c, s) the symmetric phased
+// formulas hold at both kinds (x is zero at a elements, g at b elements):
+//     at a: da = -sum_c g (c S(cx) + s S(sx)),   dphi = -sum_c g (s K(cx) - c K(sx)),
+//     at b: db = -sum_c x (c S(cg) + s S(sg)),   dpsi =  sum_c x (c K(sg) - s K(cg)),
+//           dx = c K(cg) + s K(sg),
+// with K = F + U and S = (F - U) - (F0 - U0) as in the general backward (all
+// tied b's precede a tied a).  One input column per pass; summary columns as
+// in the symmetric phased backward (M = 8m).
+__global__ __launch_bounds__(pbwd_block(1)) void k_gpbwd_reduce(const float* __restrict__ a_s, uint64_t n,
+                                                                const float* __restrict__ b_s, uint64_t k,
+                                                                const float* __restrict__ xbs, const float* __restrict__ psis,
+                                                                const float* __restrict__ gas, const float* __restrict__ phas,
+                                                                uint32_t m, uint64_t T, float* __restrict__ bf,
+                                                                float* __restrict__ bb, float2* __restrict__ tanch,
+                                                                uint2* __restrict__ tsplit) {
+  constexpr int CC = 8;
+  constexpr int BLOCK = pbwd_block(1);
+  constexpr int NW = BLOCK / kWave;
+  constexpr int P = BLOCK * pbwd_items(1);
+  __shared__ float s_red[2 * NW * CC];
+  __shared__ uint64_t s_split[4];
+  const uint32_t M = 8 * m;
+  const int tid = threadIdx.x;
+  const uint64_t tile = blockIdx.x;
+  const uint64_t d0 = tile * P, d1 = std::min<uint64_t>(n + k, d0 + P);
+  if (tid == 0) {
+    s_split[0] = merge_split(a_s, n, b_s, k, d0);
+    s_split[1] = d0 - s_split[0];
+  } else if (tid == kWave) {
+    s_split[2] = merge_split(a_s, n, b_s, k, d1);
+    s_split[3] = d1 - s_split[2];
+  }
+  __syncthreads();
+  const uint64_t i0 = s_split[0], j0 = s_split[1], i1 = s_split[2], j1 = s_split[3];
+  float s_first = INFINITY, s_last = -INFINITY;
+  if (i0 < i1) {
+    s_first = a_s[i0];
+    s_last = a_s[i1 - 1];
+  }
+  if (j0 < j1) {
+    s_first = fminf(s_first, b_s[j0]);
+    s_last = fmaxf(s_last, b_s[j1 - 1]);
+  }
+  if (tid == 0) {
+    tanch[tile] = make_float2(s_first, s_last);
+    tsplit[tile] = make_uint2((uint32_t)i0, (uint32_t)j0);
+    if (tile + 1 == T) tsplit[T] = make_uint2((uint32_t)n, (uint32_t)k);
+  }
+  for (uint32_t cc = 0; cc < m; ++cc) {
+    float sf[CC], sb[CC];
+#pragma unroll
+    for (int j = 0; j < CC; ++j) sf[j] = sb[j] = 0.f;
+    // b elements: cos(psi) x, sin(psi) x (columns 0, 1; tie 4, 5)
+    for (uint64_t jb = j0 + tid; jb < j1; jb += BLOCK) {
+      const float t = b_s[jb];
+      const float wf = decay(t - s_last), wb = decay(s_first - t);
+      const float tf = decay_m<true>(t - s_last), tb = decay_m<true>(s_first - t);
+      float sn, cs;
+      sincosf(psis[jb], &sn, &cs);
+      const float xv = xbs[jb * m + cc];
+      const float v0 = cs * xv, v1 = sn * xv;
+      sf[0] = fmaf(wf, v0, sf[0]);
+      sf[1] = fmaf(wf, v1, sf[1]);
+      sb[0] = fmaf(wb, v0, sb[0]);
+      sb[1] = fmaf(wb, v1, sb[1]);
+      sf[4] = fmaf(tf, v0, sf[4]);
+      sf[5] = fmaf(tf, v1, sf[5]);
+      sb[4] = fmaf(tb, v0, sb[4]);
+      sb[5] = fmaf(tb, v1, sb[5]);
+    }
+    // a elements: cos(phi) g, sin(phi) g (columns 2, 3; tie 6, 7)
+    for (uint64_t ia = i0 + tid; ia < i1; ia += BLOCK) {
+      const float t = a_s[ia];
+      const float wf = decay(t - s_last), wb = decay(s_first - t);
+      const float tf = decay_m<true>(t - s_last), tb = decay_m<true>(s_first - t);
+      float sn, cs;
+      sincosf(phas[ia], &sn, &cs);
+      const float gv = gas[ia * m + cc];
+      const float v2 = cs * gv, v3 = sn * gv;
+      sf[2] = fmaf(wf, v2, sf[2]);
+      sf[3] = fmaf(wf, v3, sf[3]);
+      sb[2] = fmaf(wb, v2, sb[2]);
+      sb[3] = fmaf(wb, v3, sb[3]);
+      sf[6] = fmaf(tf, v2, sf[6]);
+      sf[7] = fmaf(tf, v3, sf[7]);
+      sb[6] = fmaf(tb, v2, sb[6]);
+      sb[7] = fmaf(tb, v3, sb[7]);
+    }
+    int writer = 0;
+    block_sum2<CC, NW>(sf, sb, s_red, writer);
+    if (writer) {
+      float f = 0.f, b = 0.f;
+      for (int w = 0; w < NW; ++w) {
+        f += s_red[(0 * NW + w) * CC + tid];
+        b += s_red[(1 * NW + w) * CC + tid];
+      }
+      const uint32_t col = pbwdcol<1>(m, cc, tid);
+      bf[tile * M + col] = f;
+      bb[tile * M + col] = b;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(pbwd_block(1)) void k_gpbwd_apply(const float* __restrict__ a_s, uint64_t n,
+                                                               const float* __restrict__ b_s, uint64_t k,
+                                                               const float* __restrict__ xbs, const float* __restrict__ psis,
+                                                               const float* __restrict__ gas, const float* __restrict__ phas,
+                                                               uint32_t m, uint64_t T, const float* __restrict__ cfw,
+                                                               const float* __restrict__ cbw, const float2* __restrict__ tanch,
+                                                               const uint2* __restrict__ tsplit, float* __restrict__ dxs,
+                                                               float* __restrict__ das, float* __restrict__ dphs,
+                                                               float* __restrict__ dbs, float* __restrict__ dpsis) {
+  constexpr int CC = 4;
+  constexpr int E = pbwd_items(1);
+  constexpr int BLOCK = pbwd_block(1);
+  constexpr int NW = BLOCK / kWave;
+  constexpr int P = BLOCK * E;
+  __shared__ float s_a[P], s_b[P];
+  __shared__ float s_wf[NW * CC], s_wb[NW * CC], s_wfs[NW], s_wbs[NW];
+  const uint32_t M = 8 * m;
+  const int tid = threadIdx.x;
+  const uint64_t tile = blockIdx.x;
+  const uint2 sp0 = tsplit[tile], sp1 = tsplit[tile + 1];
+  const uint32_t na = std::min<uint32_t>(sp1.x - sp0.x, P), nb = std::min<uint32_t>(sp1.y - sp0.y, P - na);
+  for (uint32_t i = tid; i < na; i += BLOCK) s_a[i] = a_s[(uint64_t)sp0.x + i];
+  for (uint32_t i = tid; i < nb; i += BLOCK) s_b[i] = b_s[(uint64_t)sp0.y + i];
+  __syncthreads();
+  const float s_max = fmaxf(a_s[n - 1], b_s[k - 1]);
+  float ae[E];
+  int kind[E];
+  uint32_t idx[E], bbefore[E];
+  merge_tile_items<E>(s_a, s_b, na, nb, sp0, s_max, ae, kind, idx, bbefore);
+  float cs[E], sn[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float ph = kind[e] == 1 ? phas[idx[e]] : (kind[e] == 2 ? psis[idx[e]] : 0.f);
+    sincosf(ph, &sn[e], &cs[e]);
+  }
+  const float2 ta = tanch[tile];
+  const float sf = tile > 0 ? tanch[tile - 1].y : ta.x;
+  const float sb = tile + 1 < T ? tanch[tile + 1].x : ta.y;
+  float acc[E], acc0[E], dph[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = acc0[e] = dph[e] = 0.f;
+  for (uint32_t cc = 0; cc < m; ++cc) {
+    float xv[E][1], gv[E][1], v[E][CC];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      xv[e][0] = kind[e] == 2 ? xbs[(uint64_t)idx[e] * m + cc] : 0.f;
+      gv[e][0] = kind[e] == 1 ? gas[(uint64_t)idx[e] * m + cc] : 0.f;
+    }
+    phased_quad<E, 1>(cs, sn, xv, gv, v);
+    {
+      float ct_f[CC], ct_b[CC];
+#pragma unroll
+      for (int j = 0; j < CC; ++j) {
+        ct_f[j] = cfw[tile * M + pbwdcol<1>(m, cc, CC + j)];
+        ct_b[j] = cbw[tile * M + pbwdcol<1>(m, cc, CC + j)];
+      }
+      float F0[E][CC], U0[E][CC];
+      tile_scan_fu<E, CC, NW, true>(ae, v, ct_f, sf, ct_b, sb, s_wf, s_wfs, s_wb, s_wbs, F0, U0);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        acc0[e] = fmaf(gv[e][0], fmaf(cs[e], F0[e][0] - U0[e][0], sn[e] * (F0[e][1] - U0[e][1])), acc0[e]);
+        acc0[e] = fmaf(xv[e][0], fmaf(cs[e], F0[e][2] - U0[e][2], sn[e] * (F0[e][3] - U0[e][3])), acc0[e]);
+      }
+    }
+    __syncthreads();  // the second scan reuses the wave summaries
+    {
+      float ce_f[CC], ce_b[CC];
+#pragma unroll
+      for (int j = 0; j < CC; ++j) {
+        ce_f[j] = cfw[tile * M + pbwdcol<1>(m, cc, j)];
+        ce_b[j] = cbw[tile * M + pbwdcol<1>(m, cc, j)];
+      }
+      float F[E][CC], U[E][CC];
+      tile_scan_fu<E, CC, NW, false>(ae, v, ce_f, sf, ce_b, sb, s_wf, s_wfs, s_wb, s_wbs, F, U);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        acc[e] = fmaf(gv[e][0], fmaf(cs[e], F[e][0] - U[e][0], sn[e] * (F[e][1] - U[e][1])), acc[e]);
+        acc[e] = fmaf(xv[e][0], fmaf(cs[e], F[e][2] - U[e][2], sn[e] * (F[e][3] - U[e][3])), acc[e]);
+        const float kcx = F[e][0] + U[e][0], ksx = F[e][1] + U[e][1];
+        const float kcg = F[e][2] + U[e][2], ksg = F[e][3] + U[e][3];
+        dph[e] = fmaf(-gv[e][0], fmaf(sn[e], kcx, -cs[e] * ksx), dph[e]);
+        dph[e] = fmaf(xv[e][0], fmaf(cs[e], ksg, -sn[e] * kcg), dph[e]);
+        if (kind[e] == 2) dxs[(uint64_t)idx[e] * m + cc] = fmaf(cs[e], kcg, sn[e] * ksg);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (kind[e] == 1) {
+      das[idx[e]] = acc0[e] - acc[e];
+      dphs[idx[e]] = dph[e];
+    } else if (kind[e] == 2) {
+      dbs[idx[e]] = acc0[e] - acc[e];
+      dpsis[idx[e]] = dph[e];
+    }
+  }
+}
+
+hipError_t backward_phased_general(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm_a,
+                                   const SortRoute* route_a, const float* phi, uint64_t n, const float* b_s,
+                                   const uint32_t* perm_b, const SortRoute* route_b, const float* psi, uint64_t k, uint32_t m,
+                                   const float* x, const float* g, float* dx, float* da, float* db, float* dphi, float* dpsi,
+                                   hipStream_t s) {
+  const ApplyWorkspace& w = bw.w;
+  constexpr int P = pbwd_block(1) * pbwd_items(1);
+  const uint64_t T = (n + k + P - 1) / P;
+  const uint32_t M = 8 * m;
+  const dim3 grid((unsigned)T), block(pbwd_block(1));
+  const bool routed_a = route_a != nullptr && m <= kRouteMaxCols;
+  const bool routed_b = route_b != nullptr && m <= kRouteMaxCols;
+  hipError_t e;
+  // x and psi into sorted-b order, g and phi into sorted-a order
+  if (routed_b) {
+    if ((e = route_forward(*route_b, k, m, x, w.xs, w.t0, w.t1, s)) != hipSuccess) return e;
+    if ((e = route_forward(*route_b, k, 1, psi, w.phs, w.t0, w.t1, s)) != hipSuccess) return e;
+  } else {
+    LAPLEX_LAUNCH("k_gather_rows", k, s, k_gather_rows<<<rows_grid(k), 256, 0, s>>>(x, perm_b, psi, k, m, w.xs, w.phs));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (routed_a) {
+    if ((e = route_forward(*route_a, n, m, g, bw.gs, w.t0, w.t1, s)) != hipSuccess) return e;
+    if ((e = route_forward(*route_a, n, 1, phi, w.phas, w.t0, w.t1, s)) != hipSuccess) return e;
+  } else {
+    LAPLEX_LAUNCH("k_gather_rows", n, s, k_gather_rows<<<rows_grid(n), 256, 0, s>>>(g, perm_a, phi, n, m, bw.gs, w.phas));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  LAPLEX_LAUNCH("k_gpbwd_reduce", n + k, s,
+                k_gpbwd_reduce<<<grid, block, 0, s>>>(a_s, n, b_s, k, w.xs, w.phs, bw.gs, w.phas, m, T, w.bf, w.bb, w.tanch,
+                                                      w.tsplit));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = tile_carries(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb, w.gbf, w.gbb, w.gcf, w.gcb, w.ganch, s, 4 * m)) != hipSuccess)
+    return e;
+  LAPLEX_LAUNCH("k_gpbwd_apply", n + k, s,
+                k_gpbwd_apply<<<grid, block, 0, s>>>(a_s, n, b_s, k, w.xs, w.phs, bw.gs, w.phas, m, T, w.cf, w.cb, w.tanch,
+                                                     w.tsplit, w.zs, bw.das, bw.dphs, bw.dbs, bw.dpsis));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // back to original order: dx, db, dpsi along b's route; da, dphi along a's
+  if (routed_b) {
+    if ((e = route_inverse(*route_b, k, m, w.zs, dx, w.t0, w.t1, s)) != hipSuccess) return e;
+    if ((e = route_inverse(*route_b, k, 1, bw.dbs, db, w.t0, w.t1, s)) != hipSuccess) return e;
+    if ((e = route_inverse(*route_b, k, 1, bw.dpsis, dpsi, w.t0, w.t1, s)) != hipSuccess) return e;
+  } else {
+    const float* src[3] = {w.zs, bw.dbs, bw.dpsis};
+    float* dst[3] = {dx, db, dpsi};
+    for (int i = 0; i < 3; ++i) {
+      LAPLEX_LAUNCH("k_scatter_rows", k, s, k_scatter_rows<<<rows_grid(k), 256, 0, s>>>(src[i], perm_b, k, i == 0 ? m : 1, dst[i]));
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  if (routed_a) {
+    if ((e = route_inverse(*route_a, n, 1, bw.das, da, w.t0, w.t1, s)) != hipSuccess) return e;
+    return route_inverse(*route_a, n, 1, bw.dphs, dphi, w.t0, w.t1, s);
+  }
+  LAPLEX_LAUNCH("k_scatter_rows", n, s, k_scatter_rows<<<rows_grid(n), 256, 0, s>>>(bw.das, perm_a, n, 1, da));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  LAPLEX_LAUNCH("k_scatter_rows", n, s, k_scatter_rows<<<rows_grid(n), 256, 0, s>>>(bw.dphs, perm_a, n, 1, dphi));
+  return hipGetLastError();
+}
+
 }  // namespace laplex

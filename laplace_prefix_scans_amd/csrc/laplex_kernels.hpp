@@ -125,7 +125,8 @@ struct BackwardWorkspace {
   float* gs;   // upstream gradient gathered into sorted(-a) order (n x m)
   float* das;  // anchor gradient in sorted(-a) order (n)
   float* dbs;  // column-anchor gradient in sorted-b order (k; general only)
-  float* dphs; // phase gradient in sorted order (n; phased only)
+  float* dphs;   // phase gradient in sorted(-a) order (n; phased only)
+  float* dpsis;  // column-phase gradient in sorted-b order (k; general phased only)
 };
 hipError_t backward_sym(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm, const SortRoute* route,
                         uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da, hipStream_t s);
@@ -143,6 +144,17 @@ inline uint64_t phased_backward_tiles(uint64_t n, uint32_t m) {
   const uint64_t tile = (uint64_t)apply_tile(4 * kPbwdChunk);
   return (n + tile - 1) / tile;
 }
+
+// Backward of the general phased operator (rows a, phi; columns b, psi):
+// dx (k x m), da, dphi (n), db, dpsi (k); one merged two-decay scan of four
+// columns per input column (M = 8m).  xs / phs: x and psi in sorted-b order;
+// gs / phas: g and phi in sorted-a order; zs: dx in sorted-b order.  Requires
+// n, k >= 1.
+hipError_t backward_phased_general(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm_a,
+                                   const SortRoute* route_a, const float* phi, uint64_t n, const float* b_s,
+                                   const uint32_t* perm_b, const SortRoute* route_b, const float* psi, uint64_t k, uint32_t m,
+                                   const float* x, const float* g, float* dx, float* da, float* db, float* dphi, float* dpsi,
+                                   hipStream_t s);
 
 // Backward of the general operator (rows a, n; columns b, k): dx = K^T g
 // (k x m), da (n), db (k).  One scan over the merge of a and b with summary

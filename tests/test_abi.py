@@ -46,7 +46,7 @@ def test_workspace_sizes(L):
     assert lp.laplex_workspace_bytes(99, 10) == 0
     assert lp.laplex_workspace_bytes(lp.LAPLEX_OP_GENERAL_BACKWARD, 1 << 20, 1 << 10, 2) > \
         lp.laplex_workspace_bytes(lp.LAPLEX_OP_GENERAL, 1 << 20, 1 << 10, 2)
-    for op in range(9):
+    for op in range(10):
         a = lp.laplex_workspace_bytes(op, 4096, 100, 1)
         b = lp.laplex_workspace_bytes(op, 1 << 22, 1 << 20, 1)
         assert a % 256 == 0 and b % 256 == 0 and b >= a

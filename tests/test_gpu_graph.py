@@ -27,13 +27,13 @@ def _setup(kind, n, k, m):
     ws_a = lp.workspace(lp.LAPLEX_OP_SORT, n, device=dev)
     ra = lp.route_buffer(n, device=dev) if m <= 4 else None
     st = {"a": a}
-    if kind in ("general", "gen_backward", "gram"):
+    if kind in ("general", "gen_backward", "gram", "phased_gen_backward"):
         b = torch.empty(k, device=dev)
         b_s, pb = torch.empty(k, device=dev), torch.empty(k, dtype=torch.uint32, device=dev)
         ws_b = lp.workspace(lp.LAPLEX_OP_SORT, k, device=dev)
         rb = lp.route_buffer(k, device=dev) if m <= 4 else None
         st["b"] = b
-    rows_x = k if kind in ("general", "gen_backward", "gram") else n
+    rows_x = k if kind in ("general", "gen_backward", "gram", "phased_gen_backward") else n
     x = torch.empty(rows_x, m, device=dev)
     st["x"] = x
     outs = []
@@ -80,6 +80,31 @@ def _setup(kind, n, k, m):
             lp.laplex_sort_anchors(b, b_s, pb, route=rb, ws=ws_b)
             lp.laplex_backward_general(a_s, pa, b_s, pb, x, g, dx=dx, da=da, db=db, ws=ws, route_a=ra, route_b=rb)
         outs = [dx, da, db]
+    elif kind == "phased_backward":
+        phi = torch.empty(n, device=dev)
+        g = torch.empty(n, m, device=dev)
+        st["phi"] = phi
+        st["g"] = g
+        dx, da, dphi = torch.empty(n, m, device=dev), torch.empty(n, device=dev), torch.empty(n, device=dev)
+        ws = lp.workspace(lp.LAPLEX_OP_PHASED_BACKWARD, n, 0, m, device=dev)
+
+        def op():
+            lp.laplex_backward_phased(a_s, pa, phi, x, g, dx=dx, da=da, dphi=dphi, ws=ws, route=ra)
+        outs = [dx, da, dphi]
+    elif kind == "phased_gen_backward":
+        phi, psi = torch.empty(n, device=dev), torch.empty(k, device=dev)
+        g = torch.empty(n, m, device=dev)
+        st["phi"] = phi
+        st["psi"] = psi
+        st["g"] = g
+        out = (torch.empty(k, m, device=dev), torch.empty(n, device=dev), torch.empty(k, device=dev),
+               torch.empty(n, device=dev), torch.empty(k, device=dev))
+        ws = lp.workspace(lp.LAPLEX_OP_PHASED_GENERAL_BACKWARD, n, k, m, device=dev)
+
+        def op():
+            lp.laplex_sort_anchors(b, b_s, pb, route=rb, ws=ws_b)
+            lp.laplex_backward_phased_general(a_s, pa, phi, b_s, pb, psi, x, g, ws=ws, route_a=ra, route_b=rb, out=out)
+        outs = list(out)
     else:  # gram
         D = torch.empty(k, device=dev)
         st["D"] = D
@@ -101,7 +126,7 @@ def _setup(kind, n, k, m):
             if name in ("a", "b"):
                 t.copy_(torch.from_numpy(np.round(g.uniform(0, t.numel() / 8.0 + 1, t.numel())).astype(np.float32)
                                          if r % 2 else g.uniform(0, t.numel() / 8.0 + 1, t.numel()).astype(np.float32)))
-            elif name == "phi":
+            elif name in ("phi", "psi"):
                 t.copy_(torch.from_numpy(g.uniform(0, 2 * np.pi, t.numel()).astype(np.float32)))
             elif name == "D":
                 t.copy_(torch.from_numpy(g.uniform(0, 1, t.numel()).astype(np.float32)))
@@ -112,7 +137,8 @@ def _setup(kind, n, k, m):
 
 @pytest.mark.parametrize("kind,n,k,m", [("sym", 100000, 0, 1), ("sym", 70001, 0, 8), ("phased", 50000, 0, 4),
                                         ("general", 90000, 7000, 1), ("sym_backward", 60000, 0, 2),
-                                        ("gen_backward", 40000, 9000, 1), ("gram", 3000, 5000, 1)])
+                                        ("gen_backward", 40000, 9000, 1), ("gram", 3000, 5000, 1),
+                                        ("phased_backward", 30000, 0, 3), ("phased_gen_backward", 20000, 6000, 2)])
 def test_graph_replays_match_eager(kind, n, k, m):
     import torch
     step, fill, outs, handle = _setup(kind, n, k, m)
