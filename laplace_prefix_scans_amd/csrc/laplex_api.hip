@@ -429,6 +429,8 @@ extern "C" laplex_status laplex_gram_weighted(const float* a_sorted, const uint3
   if (n == 0 || row_count == 0) return LAPLEX_OK;
   if (n > kMaxLen || k > kMaxLen || n > kGramMaxLen) return LAPLEX_ERR_SIZE;
   if (row_begin > n || row_count > n - row_begin || ldm < n) return LAPLEX_ERR_ARG;
+  // the extent of M in bytes, ((row_count - 1) ldm + n) 4, must not overflow
+  if (row_count > 1 && ldm > (UINT64_MAX / 4 - n) / (row_count - 1)) return LAPLEX_ERR_SIZE;
   if (!a_sorted || !perm_a || !M || !ws) return LAPLEX_ERR_NULL;
   if (k > 0 && (!b_sorted || !perm_b || !D)) return LAPLEX_ERR_NULL;
   if (misaligned(a_sorted, 4) || misaligned(perm_a, 4) || misaligned(M, 4) || misaligned(ws, 256) ||

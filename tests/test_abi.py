@@ -120,6 +120,7 @@ def test_host_argument_errors(L):
     assert GW(A, B, 10, A, B, 5, A, 0, 3, vp(0x900000), 9, W, 1 << 30, None) == 9   # ldm < n
     assert GW(A, B, 10, None, B, 5, A, 0, 3, vp(0x900000), 10, W, 1 << 30, None) == NULL
     assert GW(A, B, 1 << 32, A, B, 5, A, 0, 3, vp(0x900000), 1 << 32, W, 1 << 40, None) == SIZE
+    assert GW(A, B, 10, A, B, 5, A, 0, 3, vp(0x900000), 1 << 62, W, 1 << 40, None) == SIZE  # M's extent overflows
     need = L.laplex_workspace_bytes(7, 1000, 300, 1)
     assert need > 0
     assert GW(A, vp(0x300000), 1000, vp(0x500000), vp(0x600000), 300, vp(0x700000), 0, 2, vp(0x900000), 1000,
