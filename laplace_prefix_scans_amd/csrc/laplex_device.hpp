@@ -78,39 +78,90 @@ __device__ __forceinline__ float decay_r(float x, bool tie) { return tie ? (x ==
 // (B_r + exp(s_l - s_r) B_l, s_r).  The backward recurrence is the mirror
 // image, summarised by the anchor of the segment's first element.
 
+// Value of a lane in the same 16-lane row, by DPP: CTRL 0x110 | k reads lane
+// - k (row_shr), 0x100 | k reads lane + k (row_shl).  A lane whose source lies
+// outside its row reads 0 (the callers mask it).
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// One scan step: the lanes with `take` join the segment summary (bs, ss) that
+// precedes (forward) or follows (backward) them.
+template <int C, bool TIE, bool FWD>
+__device__ __forceinline__ void scan_join(float (&B)[C], float s, const float (&bs)[C], float ss, bool take) {
+  const float w = decay_m<TIE>(FWD ? ss - s : s - ss);
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+    if (take) B[c] = fmaf(w, bs[c], B[c]);
+}
+
 // Inclusive forward scan across the wave, lane order.  `s` is this lane's
-// segment-end anchor (it does not change).
+// segment-end anchor (it does not change).  Within each 16-lane row a
+// Hillis-Steele scan by DPP row shifts; then rows 1 and 3 join the total of
+// the row before (lanes 15 and 47), and rows 2 and 3 the total of rows 0-1
+// (lane 31).
 template <int C, bool TIE = false>
 __device__ __forceinline__ void wave_scan_fwd(float (&B)[C], float s) {
-  const int lane = lane_id();
+  const int lane = lane_id(), rl = lane & 15, row = lane >> 4;
+  float bs[C];
+#define LAPLEX_FWD_STEP(K)                                              \
+  {                                                                     \
+    const float ss = dpp_row<0x110 | K>(s);                             \
+    _Pragma("unroll") for (int c = 0; c < C; ++c) bs[c] = dpp_row<0x110 | K>(B[c]); \
+    scan_join<C, TIE, true>(B, s, bs, ss, rl >= K);                     \
+  }
+  LAPLEX_FWD_STEP(1)
+  LAPLEX_FWD_STEP(2)
+  LAPLEX_FWD_STEP(4)
+  LAPLEX_FWD_STEP(8)
+#undef LAPLEX_FWD_STEP
+  {
+    const int src = (lane & ~31) + 15;  // row 1 reads lane 15, row 3 lane 47
+    const float ss = __shfl(s, src);
 #pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const float sl = __shfl_up(s, off);
-    const float w = decay_m<TIE>(sl - s);
-    const bool take = lane >= off;
+    for (int c = 0; c < C; ++c) bs[c] = __shfl(B[c], src);
+    scan_join<C, TIE, true>(B, s, bs, ss, (row & 1) != 0);
+  }
+  {
+    const float ss = __shfl(s, 31);
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const float bl = __shfl_up(B[c], off);
-      if (take) B[c] = fmaf(w, bl, B[c]);
-    }
+    for (int c = 0; c < C; ++c) bs[c] = __shfl(B[c], 31);
+    scan_join<C, TIE, true>(B, s, bs, ss, row >= 2);
   }
 }
 
 // Inclusive backward scan across the wave (from the last lane down).  `s` is
-// this lane's segment-start anchor.
+// this lane's segment-start anchor.  The mirror image of the forward scan:
+// row_shl steps within rows, then rows 0 and 2 join the row after (lanes 16
+// and 48), and rows 0 and 1 the total of rows 2-3 (lane 32).
 template <int C, bool TIE = false>
 __device__ __forceinline__ void wave_scan_bwd(float (&B)[C], float s) {
-  const int lane = lane_id();
+  const int lane = lane_id(), rl = lane & 15, row = lane >> 4;
+  float bs[C];
+#define LAPLEX_BWD_STEP(K)                                              \
+  {                                                                     \
+    const float ss = dpp_row<0x100 | K>(s);                             \
+    _Pragma("unroll") for (int c = 0; c < C; ++c) bs[c] = dpp_row<0x100 | K>(B[c]); \
+    scan_join<C, TIE, false>(B, s, bs, ss, rl + K < 16);                \
+  }
+  LAPLEX_BWD_STEP(1)
+  LAPLEX_BWD_STEP(2)
+  LAPLEX_BWD_STEP(4)
+  LAPLEX_BWD_STEP(8)
+#undef LAPLEX_BWD_STEP
+  {
+    const int src = (lane & ~31) + 16;  // row 0 reads lane 16, row 2 lane 48
+    const float ss = __shfl(s, src);
 #pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const float sr = __shfl_down(s, off);
-    const float w = decay_m<TIE>(s - sr);
-    const bool take = lane + off < kWave;
+    for (int c = 0; c < C; ++c) bs[c] = __shfl(B[c], src);
+    scan_join<C, TIE, false>(B, s, bs, ss, (row & 1) == 0);
+  }
+  {
+    const float ss = __shfl(s, 32);
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const float br = __shfl_down(B[c], off);
-      if (take) B[c] = fmaf(w, br, B[c]);
-    }
+    for (int c = 0; c < C; ++c) bs[c] = __shfl(B[c], 32);
+    scan_join<C, TIE, false>(B, s, bs, ss, row < 2);
   }
 }
 
