@@ -165,13 +165,30 @@ __device__ __forceinline__ void wave_scan_bwd(float (&B)[C], float s) {
   }
 }
 
-// Deterministic wave sum (butterfly).
+// Deterministic wave sum: row prefix sums by DPP row shifts (lane 15 of each
+// 16-lane row then holds its row's total), and the four row totals read as
+// uniform values and added in a fixed order, so every lane gets the same bits.
 template <int C>
 __device__ __forceinline__ void wave_sum(float (&v)[C]) {
+  const int rl = lane_id() & 15;
+#define LAPLEX_SUM_STEP(K)                                   \
+  _Pragma("unroll") for (int c = 0; c < C; ++c) {            \
+    const float t = dpp_row<0x110 | K>(v[c]);                \
+    if (rl >= K) v[c] += t;                                  \
+  }
+  LAPLEX_SUM_STEP(1)
+  LAPLEX_SUM_STEP(2)
+  LAPLEX_SUM_STEP(4)
+  LAPLEX_SUM_STEP(8)
+#undef LAPLEX_SUM_STEP
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-#pragma unroll
-    for (int c = 0; c < C; ++c) v[c] += __shfl_xor(v[c], off);
+  for (int c = 0; c < C; ++c) {
+    const int b = __builtin_bit_cast(int, v[c]);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 15));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 31));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 47));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 63));
+    v[c] = (r0 + r1) + (r2 + r3);
   }
 }
 
