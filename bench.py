@@ -58,6 +58,10 @@ def kernel_bytes(name: str, units: int, m: int, k: int = 0) -> float:
         "k_onesweep_first_routed": 12.0 + route,
         "k_onesweep_mid_routed": 16.0 + route,
         "k_onesweep_last_routed": 16.0 + route,
+        "k_onesweep_first_pay": 16.0,            # read anchors and x; write keys and x
+        "k_onesweep_last_pay": 16.0,             # read key + x; write sorted anchors and sorted x
+        "k_onesweep_first_pay_routed": 16.0 + route,
+        "k_onesweep_last_pay_routed": 16.0 + route,
         "k_sym_gather_reduce": 8.0 + 8.0 * m,    # perm, sorted anchors, x rows in (random), sorted rows out
         "k_sym_apply": 8.0 + 8.0 * m,            # sorted anchors, perm, sorted rows in, y rows out (random)
         "k_sym_reduce": 4.0 + 4.0 * m,           # sorted anchors, sorted rows
@@ -114,7 +118,8 @@ def rocprof_label(name: str, pass_index: int = 0, routed: bool = True) -> str:
     kern, targs = (m.group(1), [t.strip() for t in m.group(2).split(",")]) if m else (base, [])
     if kern == "k_onesweep":
         label = {"0": "k_onesweep_first", "1": "k_onesweep_mid", "2": "k_onesweep_last"}[targs[0]]
-        return label + ("_routed" if routed else "")
+        pay = len(targs) > 2 and targs[2] == "true"
+        return label + ("_pay" if pay else "") + ("_routed" if routed else "")
     if kern in ("k_route_fwd", "k_route_inv", "k_route_inv_chunked"):
         return "%s_w%s" % (kern.replace("_chunked", ""), targs[0])
     if kern == "k_sym_gather_reduce":
@@ -311,6 +316,9 @@ def main():
     ap.add_argument("--workload", default="sym2p30")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-route", action="store_true", help="move x and y by index instead of along the sort route")
+    ap.add_argument("--two-call", action="store_true",
+                    help="symmetric m = 1: time laplex_sort_anchors + laplex_matvec_sym instead of the one-call "
+                         "laplex_sort_matvec_sym (which carries x through the sort)")
     ap.add_argument("--cpu-sample-log2", type=int, default=25)
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward (symmetric, general, phased)")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing (steps after a 512 MiB scrub)")
@@ -347,6 +355,9 @@ def main():
     t_gen = time.perf_counter() - t_gen
     n, m, k = w.n, w.m, w.k
     use_route = m <= 4 and not args.no_route
+    # symmetric, one column, routed: the sort and the apply in one call, x
+    # carried through the sort's passes as the keys' values
+    one_call = w.kind == "sym" and m == 1 and use_route and not args.two_call
     a = torch.from_numpy(w.a).to(dev)
     x = torch.from_numpy(w.x).to(dev)
     ra = lp.route_buffer(n, device=dev) if use_route else None
@@ -374,11 +385,16 @@ def main():
     elif w.kind == "phased":
         phi = torch.from_numpy(w.phi).to(dev)
         ws_apply = lp.workspace(lp.LAPLEX_OP_PHASED, n, 0, m, device=dev)
+    elif one_call:
+        ws_apply = lp.workspace(lp.LAPLEX_OP_SORT_SYM, n, 0, m, device=dev)
     else:
         ws_apply = lp.workspace(lp.LAPLEX_OP_SYM, n, 0, m, device=dev)
     del w.a, w.x
 
     def step():
+        if one_call:
+            lp.laplex_sort_matvec_sym(a, x, y=y, ws=ws_apply)
+            return
         lp.laplex_sort_anchors(a, a_s, pa, route=ra, ws=ws_sort_a)
         if w.kind == "gram":
             lp.laplex_sort_anchors(b, b_s, pb, ws=ws_sort_b)
@@ -394,7 +410,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    if lp.laplex_status_poll(ws_sort_a) != 0:
+    if lp.laplex_status_poll(ws_apply if one_call else ws_sort_a) != 0:
         raise RuntimeError("sort reported a device-side error")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with lp.profile_launches(capacity=64 * max(1, args.steps)) as prof:
@@ -489,7 +505,8 @@ def main():
     step_bytes = sum(s["bytes"] for s in stats.values()) / args.steps
 
     # the step split into its sort (row a1) and its apply (rows a2-a7, given
-    # the sort handle): kernel time and algorithmic bytes of each part
+    # the sort handle): kernel time and algorithmic bytes of each part (on the
+    # one-call path the sort passes also carry x into sorted order, row a2)
     def part(names):
         ms = sum(stats[q]["ms"] for q in names) / args.steps
         by = sum(stats[q]["bytes"] for q in names) / args.steps
@@ -515,7 +532,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "kind": w.kind, "n": n, "m": m,
                    "k": k if w.kind in ("general", "gram") else None,
-                   "step": "sort a and b + all n^2 entries of M" if w.kind == "gram" else "sort + apply",
+                   "step": "sort a and b + all n^2 entries of M" if w.kind == "gram" else
+                   "sort + apply in one call (x carried through the sort)" if one_call else "sort + apply",
                    "route": use_route and w.kind != "gram", "recipe": w.recipe},
         "roofline": roofline,
         "step_alg_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
@@ -528,6 +546,10 @@ def main():
         "host_gen_s": round(t_gen, 1),
     }
     if w.kind in ("sym", "general", "phased") and not args.no_backward:
+        if one_call:  # the backward takes a sort handle: build it (untimed)
+            del ws_apply
+            torch.cuda.empty_cache()
+            lp.laplex_sort_anchors(a, a_s, pa, route=ra, ws=ws_sort_a)
         gen = torch.Generator(device=dev).manual_seed(0x6AAD)
         g = torch.randn((n,) if x.dim() == 1 else (n, m), generator=gen, device=dev)
         da = torch.empty(n, dtype=torch.float32, device=dev)

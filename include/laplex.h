@@ -64,7 +64,8 @@ enum {
   LAPLEX_OP_GENERAL_BACKWARD = 6, /* backward of the general operator */
   LAPLEX_OP_GRAM = 7,             /* weighted Gram matrix */
   LAPLEX_OP_PHASED_BACKWARD = 8,  /* backward of the symmetric phased operator */
-  LAPLEX_OP_PHASED_GENERAL_BACKWARD = 9 /* backward of the phased operator with a != b */
+  LAPLEX_OP_PHASED_GENERAL_BACKWARD = 9, /* backward of the phased operator with a != b */
+  LAPLEX_OP_SORT_SYM = 10                /* sort and symmetric operator in one call */
 };
 
 /* Bytes of workspace one call of `op` needs for n output anchors, k input
@@ -105,6 +106,20 @@ laplex_status laplex_status_poll(const void* ws, hipStream_t stream);
  * ws: laplex_workspace_bytes(LAPLEX_OP_SYM, n, 0, m) bytes. */
 laplex_status laplex_matvec_sym(const float* a_sorted, const uint32_t* perm, const void* route, uint64_t n, uint32_t m,
                                 const float* x, float* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The symmetric operator from unsorted anchors in one call: the sort of
+ * laplex_sort_anchors followed by laplex_matvec_sym (section 2.2, symmetric
+ * case: sort, then the two scans), for callers that apply K(a) once.  With
+ * m == 1 the inputs ride through the sort's passes as the keys' values (no
+ * permutation is formed and x is not moved separately); otherwise the sort
+ * handle is built inside the workspace and the apply takes it.  The result
+ * is bitwise the same as laplex_sort_anchors + laplex_matvec_sym with a route.
+ * a: n floats; x: n x m (inputs, original order); y: n x m (output, original
+ * order, must not overlap a, x or ws); ws: laplex_workspace_bytes(
+ * LAPLEX_OP_SORT_SYM, n, 0, m) bytes; it holds the sort workspace, so
+ * laplex_status_poll(ws) reports non-finite anchors and stalls as for a sort. */
+laplex_status laplex_sort_matvec_sym(const float* a, uint64_t n, uint32_t m, const float* x, float* y, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
 
 /* General operator y = LAPLEX(a, b) x with a != b (section 2.2, general case:
  * the input anchors b are placed into the intervals of the sorted output

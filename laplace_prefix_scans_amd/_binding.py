@@ -17,6 +17,7 @@ LAPLEX_OP_GENERAL_BACKWARD = 6
 LAPLEX_OP_GRAM = 7
 LAPLEX_OP_PHASED_BACKWARD = 8
 LAPLEX_OP_PHASED_GENERAL_BACKWARD = 9
+LAPLEX_OP_SORT_SYM = 10
 
 _STATUS = {
     0: "LAPLEX_OK", 1: "LAPLEX_ERR_NULL", 2: "LAPLEX_ERR_SIZE", 3: "LAPLEX_ERR_ALIGN", 4: "LAPLEX_ERR_WORKSPACE",
@@ -55,6 +56,8 @@ def lib():
         L.laplex_sort_anchors.argtypes = [vp, u64, vp, vp, vp, sz, vp, sz, vp]
         L.laplex_status_poll.argtypes = [vp, vp]
         L.laplex_matvec_sym.argtypes = [vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
+        L.laplex_sort_matvec_sym.argtypes = [vp, u64, u32, vp, vp, vp, sz, vp]
+        L.laplex_sort_matvec_sym.restype = i32
         L.laplex_matvec_general.argtypes = [vp, vp, vp, u64, vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
         L.laplex_matvec_phased.argtypes = [vp, vp, vp, vp, u64, vp, vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
         L.laplex_backward_sym.argtypes = [vp, vp, vp, u64, u32, vp, vp, vp, vp, vp, sz, vp]
@@ -189,6 +192,28 @@ def laplex_matvec_sym(a_sorted: torch.Tensor, perm: torch.Tensor, x: torch.Tenso
     ws = _ws(ws, LAPLEX_OP_SYM, n, 0, m, dev)
     _check(lib().laplex_matvec_sym(_ptr(a_sorted), _ptr(perm), _ptr(route), n, m, _ptr(x), _ptr(y), _ptr(ws), ws.numel(),
                                    _stream(dev)), "laplex_matvec_sym")
+    return y
+
+
+def laplex_sort_matvec_sym(a: torch.Tensor, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                           ws: Optional[torch.Tensor] = None, check: bool = False) -> torch.Tensor:
+    """y = LAPLEX(a, a) x from unsorted anchors in one call (the sort and the
+    apply; with one column x rides through the sort).  ``ws``: optional
+    workspace of laplex_workspace_bytes(LAPLEX_OP_SORT_SYM, n, 0, m) bytes;
+    ``check=True`` waits and raises LaplexError if an anchor was NaN/Inf."""
+    _vec(a, "a")
+    if a.dim() != 1:
+        raise ValueError("a must be 1-D")
+    n, dev = a.shape[0], a.device
+    m = _cols(x, n)
+    y = torch.empty_like(x) if y is None else y
+    _cols(y, n, "y")
+    ws = _ws(ws, LAPLEX_OP_SORT_SYM, n, 0, m, dev)
+    L = lib()
+    _check(L.laplex_sort_matvec_sym(_ptr(a), n, m, _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(dev)),
+           "laplex_sort_matvec_sym")
+    if check:
+        _check(L.laplex_status_poll(_ptr(ws), _stream(dev)), "laplex_sort_matvec_sym")
     return y
 
 

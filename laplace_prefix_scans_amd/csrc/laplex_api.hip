@@ -159,6 +159,32 @@ GramWorkspace carve_gram(void* ws, uint64_t n, uint64_t k, size_t* total) {
   return g;
 }
 
+// Sort and symmetric apply in one call: the sort workspace first (so that
+// laplex_status_poll finds its flags at the start), then the sorted anchors,
+// the route and the apply workspace; the permutation only when m != 1.
+struct SortSymWorkspace {
+  SortWorkspace sort;
+  float* a_s;
+  uint32_t* perm;
+  void* route;
+  ApplyWorkspace apply;
+};
+SortSymWorkspace carve_sort_sym(void* ws, uint64_t n, uint32_t m, size_t* total) {
+  Carver c(ws);
+  SortSymWorkspace w{};
+  char* sort_base = c.take<char>(sort_bytes(n));
+  if (ws) w.sort = carve_sort(sort_base, n);
+  w.a_s = c.take<float>(n * 4);
+  w.perm = m == 1 ? nullptr : c.take<uint32_t>(n * 4);
+  w.route = m <= kRouteMaxCols ? c.take<void>(route_bytes(n)) : nullptr;
+  char* apply_base = c.take<char>(0);
+  size_t apply_total = 0;
+  w.apply = carve_apply(ws ? apply_base : nullptr, n, n, n, m, Variant::Sym, false, &apply_total);
+  c.off += apply_total;
+  if (total) *total = (c.off + 255) & ~size_t(255);
+  return w;
+}
+
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
 bool overlaps(const void* p, size_t pb, const void* q, size_t qb) {
@@ -187,6 +213,7 @@ extern "C" size_t laplex_workspace_bytes(int op, uint64_t n, uint64_t k, uint32_
     case LAPLEX_OP_GRAM: carve_gram(nullptr, n, k, &total); return total;
     case LAPLEX_OP_PHASED_BACKWARD: carve_backward(nullptr, n, 0, m, false, &total, true); return total;
     case LAPLEX_OP_PHASED_GENERAL_BACKWARD: carve_backward(nullptr, n, k, m, true, &total, true); return total;
+    case LAPLEX_OP_SORT_SYM: carve_sort_sym(nullptr, n, m, &total); return total;
     default: return 0;
   }
 }
@@ -257,6 +284,31 @@ extern "C" laplex_status laplex_matvec_sym(const float* a_sorted, const uint32_t
   SortRoute r{};
   if (route) r = carve_route(route, n);
   return from_hip(apply_sym(w, Variant::Sym, a_sorted, perm, route ? &r : nullptr, nullptr, n, m, x, y, stream));
+}
+
+extern "C" laplex_status laplex_sort_matvec_sym(const float* a, uint64_t n, uint32_t m, const float* x, float* y, void* ws,
+                                                size_t ws_bytes, hipStream_t stream) {
+  if (n == 0 || m == 0) return LAPLEX_OK;
+  if (n > kMaxLen || m > kMaxCols) return LAPLEX_ERR_SIZE;
+  if (!a || !x || !y || !ws) return LAPLEX_ERR_NULL;
+  if (misaligned(a, 4) || misaligned(x, 4) || misaligned(y, 4) || misaligned(ws, 256)) return LAPLEX_ERR_ALIGN;
+  size_t need = 0;
+  carve_sort_sym(nullptr, n, m, &need);
+  if (ws_bytes < need) return LAPLEX_ERR_WORKSPACE;
+  const size_t yb = n * (size_t)m * 4, vb = n * 4;
+  if (overlaps(y, yb, x, yb) || overlaps(y, yb, a, vb) || overlaps(y, yb, ws, ws_bytes) || overlaps(a, vb, ws, ws_bytes) ||
+      overlaps(x, yb, ws, ws_bytes))
+    return LAPLEX_ERR_OVERLAP;
+  const SortSymWorkspace w = carve_sort_sym(ws, n, m, nullptr);
+  SortRoute r{};
+  if (w.route) r = carve_route(w.route, n);
+  hipError_t e;
+  if (m == 1) {
+    if ((e = sort_anchors_payload(w.sort, a, x, n, w.a_s, w.apply.xs, &r, stream)) != hipSuccess) return from_hip(e);
+    return from_hip(apply_sym_presorted(w.apply, w.a_s, r, n, y, stream));
+  }
+  if ((e = sort_anchors(w.sort, a, n, w.a_s, w.perm, w.route ? &r : nullptr, stream)) != hipSuccess) return from_hip(e);
+  return from_hip(apply_sym(w.apply, Variant::Sym, w.a_s, w.perm, w.route ? &r : nullptr, nullptr, n, m, x, y, stream));
 }
 
 extern "C" laplex_status laplex_backward_sym(const float* a_sorted, const uint32_t* perm, const void* route, uint64_t n,

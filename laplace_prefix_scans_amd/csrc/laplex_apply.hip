@@ -815,9 +815,11 @@ __attribute__((amdgpu_waves_per_eu(!PH && C == 1 ? 8 : 1))) void k_sym_apply(
     sym_apply_tile<C, PH, SCATTER, false>(a_s, perm, xs, phs, cfw, cbw, tanch, n, m, T, y, vec, s_wf, s_wb, s_wfs, s_wbs);
 }
 
+// x_sorted: w.xs already holds x in sorted order (routed, one column).
 template <int C, bool PH>
 static hipError_t run_sym(const ApplyWorkspace& w, const float* a_s, const uint32_t* perm, const SortRoute* route,
-                          const float* phi, uint64_t n, uint32_t m, const float* x, float* y, hipStream_t s) {
+                          const float* phi, uint64_t n, uint32_t m, const float* x, float* y, hipStream_t s,
+                          bool x_sorted = false) {
   constexpr int CC = PH ? 2 * C : C;
   constexpr int P = apply_tile(CC);
   const uint64_t T = (n + P - 1) / P;
@@ -827,7 +829,7 @@ static hipError_t run_sym(const ApplyWorkspace& w, const float* a_s, const uint3
   const bool vec = (reinterpret_cast<uintptr_t>(a_s) & 15) == 0;
   hipError_t e;
   if (routed) {
-    if ((e = route_forward(*route, n, m, x, w.xs, w.t0, w.t1, s)) != hipSuccess) return e;
+    if (!x_sorted && (e = route_forward(*route, n, m, x, w.xs, w.t0, w.t1, s)) != hipSuccess) return e;
     if (PH && (e = route_forward(*route, n, 1, phi, w.phs, w.t0, w.t1, s)) != hipSuccess) return e;
     LAPLEX_LAUNCH(PH ? "k_phased_reduce" : "k_sym_reduce", n, s,
                   k_sym_gather_reduce<C, PH, false><<<grid, block, 0, s>>>(a_s, perm, phi, x, n, m, w.xs, w.phs, w.bf, w.bb,
@@ -848,6 +850,11 @@ static hipError_t run_sym(const ApplyWorkspace& w, const float* a_s, const uint3
   LAPLEX_LAUNCH(PH ? "k_phased_apply" : "k_sym_apply", n, s,
                 k_sym_apply<C, PH, true><<<grid, block, 0, s>>>(a_s, perm, w.xs, w.phs, w.cf, w.cb, w.tanch, n, m, T, y, vec));
   return hipGetLastError();
+}
+
+hipError_t apply_sym_presorted(const ApplyWorkspace& w, const float* a_s, const SortRoute& route, uint64_t n, float* y,
+                               hipStream_t s) {
+  return run_sym<1, false>(w, a_s, nullptr, &route, nullptr, n, 1, nullptr, y, s, true);
 }
 
 hipError_t apply_sym(const ApplyWorkspace& w, Variant var, const float* a_s, const uint32_t* perm, const SortRoute* route,

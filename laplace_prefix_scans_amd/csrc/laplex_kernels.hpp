@@ -62,6 +62,12 @@ SortRoute carve_route(const void* base, uint64_t n);
 size_t sort_status_bytes(uint64_t n);
 hipError_t sort_anchors(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,
                         const SortRoute* route, hipStream_t s);
+// The same sort with x (n floats, original order) carried along as the
+// value of each key in place of its index: writes x in sorted order to
+// x_sorted, and no permutation (the route, if given, still records the
+// passes).  -0.0 anchors come out as +0.0.
+hipError_t sort_anchors_payload(const SortWorkspace& w, const float* a, const float* x, uint64_t n, float* a_sorted,
+                                float* x_sorted, const SortRoute* route, hipStream_t s);
 
 // Move rows of W floats through the sort's passes: forward (original ->
 // sorted order) or inverse (sorted -> original).  t0, t1: scratch, n rows each.
@@ -113,6 +119,10 @@ enum class Variant { Sym, Phased };
 // route / route_a / route_b may be null (then x and y move by index).
 hipError_t apply_sym(const ApplyWorkspace& w, Variant var, const float* a_s, const uint32_t* perm, const SortRoute* route,
                      const float* phi, uint64_t n, uint32_t m, const float* x, float* y, hipStream_t s);
+// Symmetric apply, one column, with w.xs already holding x in sorted order
+// (from sort_anchors_payload): scans, then y back along the route.
+hipError_t apply_sym_presorted(const ApplyWorkspace& w, const float* a_s, const SortRoute& route, uint64_t n, float* y,
+                               hipStream_t s);
 hipError_t apply_general(const ApplyWorkspace& w, Variant var, const float* a_s, const uint32_t* perm_a, const SortRoute* route_a,
                          const float* phi, uint64_t n, const float* b_s, const uint32_t* perm_b, const SortRoute* route_b,
                          const float* psi, uint64_t k, uint32_t m, const float* x, float* y, hipStream_t s);

@@ -126,19 +126,25 @@ __global__ __launch_bounds__(256) void k_sort_offsets(const uint32_t* __restrict
 // MODE 0: input is the anchors' float bits (keys computed here, values are the
 //         input indices); MODE 1: (key, value) pairs to pairs;
 // MODE 2: pairs in; writes float bits of the sorted anchors and the permutation.
+// PAY (MODE 0 and 2): the values are a payload of one 32-bit word per anchor
+// (read from `pay` in input order) instead of the input indices, so pass 4
+// writes the payload in sorted order where the permutation would go, and the
+// sorted anchors carry +0.0 for -0.0 (no index to look the sign up by).
 // Keys and values travel as interleaved pairs so that each digit run is one
 // contiguous stretch of 8-byte elements.
 // Threads 0..255 also own one digit value each for the per-digit steps.
 constexpr int kLookback = 4;  // predecessor status words read per round trip (more costs more status traffic than it saves)
 
-template <int MODE, typename ST>
+template <int MODE, typename ST, bool PAY>
 __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6))) void k_onesweep(const uint2* __restrict__ kvin, uint2* __restrict__ kvout,
                                                          uint32_t* __restrict__ kout, uint32_t* __restrict__ vout,
                                                          const uint32_t* __restrict__ a_bits, ST* __restrict__ status,
                                                          uint32_t* __restrict__ header, int pass,
                                                          const uint32_t* __restrict__ digit_start, uint64_t n,
                                                          uint16_t* __restrict__ r_lpos, uint16_t* __restrict__ r_dstart,
-                                                         uint32_t* __restrict__ r_gbase) {
+                                                         uint32_t* __restrict__ r_gbase, const uint32_t* __restrict__ pay) {
+  static_assert(!PAY || MODE != 1, "the payload enters in pass 1 and leaves in pass 4");
+  constexpr bool HOLDV = MODE != 0 || PAY;  // values held in registers (else recomputed input indices)
   static_assert(kSortBlock % 256 == 0, "at least one thread per digit value");
   constexpr int E = kSortItems;
   constexpr int TILE = kSortTile;
@@ -172,17 +178,18 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
   // positions (< 2^13) are kept two per register, and the first pass
   // recomputes its values (the input indices) instead of holding them.
   static_assert(E % 2 == 0 && TILE <= 65536, "16-bit packed ranks");
-  uint32_t k[E], v[MODE == 0 ? 1 : E], rkp[E / 2];
+  uint32_t k[E], v[HOLDV ? E : 1], rkp[E / 2];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint64_t idx = base + (uint64_t)wid * (kWave * E) + (uint64_t)e * kWave + lane;
     const bool valid = idx < n;
     if (MODE == 0) {
       k[e] = valid ? a_bits[idx] : 0u;
+      if (PAY) v[HOLDV ? e : 0] = valid ? pay[idx] : 0u;
     } else {
       const uint2 kv = valid ? kvin[idx] : make_uint2(0xFFFFFFFFu, 0u);
       k[e] = kv.x;
-      v[MODE == 0 ? 0 : e] = kv.y;
+      v[HOLDV ? e : 0] = kv.y;
     }
   }
   if (MODE == 0) {
@@ -335,7 +342,7 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
   }
   auto pos_of = [&](int e) -> uint32_t { return (e % 2 == 0) ? (posp[e / 2] & 0xFFFFu) : (posp[e / 2] >> 16); };
   auto val_of = [&](int e) -> uint32_t {
-    return MODE == 0 ? (uint32_t)(base + first + (uint32_t)(e * kWave)) : v[MODE == 0 ? 0 : e];
+    return HOLDV ? v[HOLDV ? e : 0] : (uint32_t)(base + first + (uint32_t)(e * kWave));
   };
   constexpr uint32_t HALF = TILE / 2;
   constexpr int kOutSteps = HALF / kSortBlock;  // slots per thread and half
@@ -372,7 +379,10 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
         if (i < count && (uint64_t)o[j] < n) {
           if (MODE == 2) {
             const uint32_t key = kv[j].x, val = kv[j].y;
-            kout[o[j]] = (key == kKeyPlusZero && (uint64_t)val < n) ? a_bits[val] : key_to_float_bits(key);
+            if (PAY)
+              kout[o[j]] = key_to_float_bits(key);
+            else
+              kout[o[j]] = (key == kKeyPlusZero && (uint64_t)val < n) ? a_bits[val] : key_to_float_bits(key);
             vout[o[j]] = val;
           } else {
             kvout[o[j]] = kv[j];
@@ -385,9 +395,11 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
 }
 
 // ------------------------------------------------------------------ host side
+// pay: NULL (pass 4 writes the permutation to perm) or n payload words that
+// ride along with the keys (pass 4 writes them, sorted, to perm).
 template <typename ST>
 static hipError_t launch_sort_passes(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,
-                                     const SortRoute* route, hipStream_t s) {
+                                     const SortRoute* route, const uint32_t* pay, hipStream_t s) {
   const uint32_t* a_bits = reinterpret_cast<const uint32_t*>(a);
   const uint64_t tiles = (n + kSortTile - 1) / kSortTile;
   ST* st = reinterpret_cast<ST*>(w.status);
@@ -400,18 +412,22 @@ static hipError_t launch_sort_passes(const SortWorkspace& w, const float* a, uin
     uint16_t* rl = route ? route->lpos[p] : nullptr;
     uint16_t* rd = route ? route->dstart[p] : nullptr;
     uint32_t* rg = route ? route->gbase[p] : nullptr;
-    if (p == 0)
-      LAPLEX_LAUNCH(route ? "k_onesweep_first_routed" : "k_onesweep_first", n, s,
-                    k_onesweep<0, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(
-                        nullptr, dst, fk, fv, a_bits, stp, w.header, p, w.offsets + p * 256, n, rl, rd, rg));
+    const dim3 grid((unsigned)tiles), block(kSortBlock);
+#define LAPLEX_PASS(MODE, PAY, NAME)                                                                                  \
+  LAPLEX_LAUNCH(NAME, n, s,                                                                                          \
+                (k_onesweep<MODE, ST, PAY><<<grid, block, 0, s>>>(src, dst, fk, fv, a_bits, stp, w.header, p,          \
+                                                                  w.offsets + p * 256, n, rl, rd, rg, pay)))
+    if (p == 0 && pay)
+      LAPLEX_PASS(0, true, route ? "k_onesweep_first_pay_routed" : "k_onesweep_first_pay");
+    else if (p == 0)
+      LAPLEX_PASS(0, false, route ? "k_onesweep_first_routed" : "k_onesweep_first");
+    else if (p == 3 && pay)
+      LAPLEX_PASS(2, true, route ? "k_onesweep_last_pay_routed" : "k_onesweep_last_pay");
     else if (p == 3)
-      LAPLEX_LAUNCH(route ? "k_onesweep_last_routed" : "k_onesweep_last", n, s,
-                    k_onesweep<2, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(
-                        src, dst, fk, fv, a_bits, stp, w.header, p, w.offsets + p * 256, n, rl, rd, rg));
+      LAPLEX_PASS(2, false, route ? "k_onesweep_last_routed" : "k_onesweep_last");
     else
-      LAPLEX_LAUNCH(route ? "k_onesweep_mid_routed" : "k_onesweep_mid", n, s,
-                    k_onesweep<1, ST><<<dim3((unsigned)tiles), dim3(kSortBlock), 0, s>>>(
-                        src, dst, fk, fv, a_bits, stp, w.header, p, w.offsets + p * 256, n, rl, rd, rg));
+      LAPLEX_PASS(1, false, route ? "k_onesweep_mid_routed" : "k_onesweep_mid");
+#undef LAPLEX_PASS
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     src = dst;
@@ -425,8 +441,8 @@ size_t sort_status_bytes(uint64_t n) {
   return (size_t)(4 * tiles * 256) * word;
 }
 
-hipError_t sort_anchors(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,
-                        const SortRoute* route, hipStream_t s) {
+static hipError_t sort_impl(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,
+                            const SortRoute* route, const uint32_t* pay, hipStream_t s) {
   // clear the header, histograms and look-back status with a fill kernel
   const uint64_t clear_words = (uint64_t)(kSortHeaderBytes / 4) + sort_status_bytes(n) / 4;
   const unsigned fill_blocks = (unsigned)std::min<uint64_t>((clear_words + 255) / 256, 4096);
@@ -440,8 +456,18 @@ hipError_t sort_anchors(const SortWorkspace& w, const float* a, uint64_t n, floa
   if ((e = hipGetLastError()) != hipSuccess) return e;
   LAPLEX_LAUNCH("k_sort_offsets", 1024, s, k_sort_offsets<<<1, 256, 0, s>>>(w.hist, w.offsets, w.header));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (n <= (1ull << 30)) return launch_sort_passes<uint32_t>(w, a, n, a_sorted, perm, route, s);
-  return launch_sort_passes<uint64_t>(w, a, n, a_sorted, perm, route, s);
+  if (n <= (1ull << 30)) return launch_sort_passes<uint32_t>(w, a, n, a_sorted, perm, route, pay, s);
+  return launch_sort_passes<uint64_t>(w, a, n, a_sorted, perm, route, pay, s);
+}
+
+hipError_t sort_anchors(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,
+                        const SortRoute* route, hipStream_t s) {
+  return sort_impl(w, a, n, a_sorted, perm, route, nullptr, s);
+}
+
+hipError_t sort_anchors_payload(const SortWorkspace& w, const float* a, const float* x, uint64_t n, float* a_sorted,
+                                float* x_sorted, const SortRoute* route, hipStream_t s) {
+  return sort_impl(w, a, n, a_sorted, reinterpret_cast<uint32_t*>(x_sorted), route, reinterpret_cast<const uint32_t*>(x), s);
 }
 
 }  // namespace laplex

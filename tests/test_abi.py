@@ -46,7 +46,7 @@ def test_workspace_sizes(L):
     assert lp.laplex_workspace_bytes(99, 10) == 0
     assert lp.laplex_workspace_bytes(lp.LAPLEX_OP_GENERAL_BACKWARD, 1 << 20, 1 << 10, 2) > \
         lp.laplex_workspace_bytes(lp.LAPLEX_OP_GENERAL, 1 << 20, 1 << 10, 2)
-    for op in range(10):
+    for op in range(11):
         a = lp.laplex_workspace_bytes(op, 4096, 100, 1)
         b = lp.laplex_workspace_bytes(op, 1 << 22, 1 << 20, 1)
         assert a % 256 == 0 and b % 256 == 0 and b >= a
@@ -127,6 +127,20 @@ def test_host_argument_errors(L):
               vp(0x10000000), 64, None) == WS
     assert GW(A, vp(0x300000), 1000, vp(0x500000), vp(0x600000), 300, vp(0x700000), 0, 2, vp(0x700100), 1000,
               vp(0x10000000), need, None) == OVERLAP
+    # one-call sort + symmetric apply: no-ops, NULL, size, alignment, workspace, overlaps
+    SM = L.laplex_sort_matvec_sym
+    assert SM(None, 0, 1, None, None, None, 0, None) == OK
+    assert SM(A, 10, 0, None, None, None, 0, None) == OK
+    assert SM(A, 10, 1, None, B, W, 1 << 30, None) == NULL
+    assert SM(A, 1 << 32, 1, A, B, W, 1 << 40, None) == SIZE
+    assert SM(A, 10, 1 << 17, A, B, W, 1 << 40, None) == SIZE
+    assert SM(A, 10, 1, vp(0x300002), B, W, 1 << 30, None) == ALIGN
+    needs = L.laplex_workspace_bytes(10, 1000, 0, 1)
+    assert needs > L.laplex_workspace_bytes(0, 1000, 0, 1)
+    assert SM(A, 1000, 1, vp(0x500000), vp(0x600000), vp(0x10000000), needs - 256, None) == WS
+    assert SM(A, 1000, 1, vp(0x500000), vp(0x500100), vp(0x10000000), needs, None) == OVERLAP  # y on x
+    assert SM(A, 1000, 1, vp(0x500000), vp(0x100100), vp(0x10000000), needs, None) == OVERLAP  # y on a
+    assert SM(vp(0x10000100), 1000, 1, vp(0x500000), vp(0x600000), vp(0x10000000), needs, None) == OVERLAP  # a in ws
     # route: too small, misaligned, overlapping
     assert L.laplex_sort_anchors(A, 1000, B, vp(0x300000), vp(0x20000000), 16, vp(0x10000000), 1 << 30, None) == WS
     assert L.laplex_sort_anchors(A, 1000, B, vp(0x300000), vp(0x20000010), 1 << 20, vp(0x10000000), 1 << 30, None) == ALIGN
