@@ -40,6 +40,20 @@ __device__ __forceinline__ uint64_t match_digit8(uint32_t d, uint64_t valid) {
   return peers;
 }
 
+// ---------------------------------------------------------------- tile placement
+// Tile of this block.  Workgroups are dispatched to the 8 XCDs round-robin, so
+// block b runs on XCD b % 8; giving each XCD a contiguous range of tiles puts
+// neighbouring tiles -- whose digit runs share cache lines at their ends --
+// behind the same L2.  Launch ceil(tiles / 8) * 8 blocks; returns false for
+// the few padding blocks.
+constexpr unsigned kXcds = 8;
+__device__ __forceinline__ bool xcd_tile(uint64_t tiles, uint64_t& tile) {
+  const uint64_t per = (tiles + kXcds - 1) / kXcds;
+  tile = (uint64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  return tile < tiles;
+}
+inline uint64_t xcd_blocks(uint64_t tiles) { return ((tiles + kXcds - 1) / kXcds) * kXcds; }
+
 // ---------------------------------------------------------------- coherent status words
 // Relaxed agent-scope atomics: the value read is the one in the device's
 // coherent memory, visible across XCDs.

@@ -44,7 +44,11 @@ struct SortWorkspace {
   uint32_t* offsets;  // [4][256]
   void* status;       // [4][tiles][256] u32 (n <= 2^30) or u64
   uint2* kv[2];       // ping-pong buffers of (key, value) pairs, n each
+  uint32_t* tcount;   // [tiles][256] first-pass digit counts of the tiles before each tile in its histogram block's range
+  uint32_t* gsum;     // [kHistMaxBlocks][256] per histogram block: its range's digit counts, then their exclusive prefix
 };
+inline uint64_t sort_tiles(uint64_t n) { return (n + kSortTile - 1) / kSortTile; }
+constexpr int kHistMaxBlocks = 256;  // workgroups of the histogram read (rows of gsum)
 
 // Route of a sort: for every radix pass, the tile-local sorted position of
 // each element of the pass's input, and per tile the start of each digit's

@@ -113,17 +113,6 @@ __device__ __forceinline__ void load_tables(const uint16_t* __restrict__ dstart,
   if (tid == 0) s_start[256] = (uint16_t)count;
 }
 
-// Tile of this block.  Workgroups are dispatched to the 8 XCDs round-robin, so
-// block b runs on XCD b % 8; giving each XCD a contiguous range of tiles puts
-// neighbouring tiles -- whose digit runs share cache lines at their ends --
-// behind the same L2.  Returns false for the few padding blocks.
-constexpr unsigned kXcds = 8;
-__device__ __forceinline__ bool xcd_tile(uint64_t tiles, uint64_t& tile) {
-  const uint64_t per = (tiles + kXcds - 1) / kXcds;
-  tile = (uint64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-  return tile < tiles;
-}
-
 // vec: `in` (fwd) or `out` (inv), the input-order side, is 16-byte aligned
 // (and in_b / out_b with PLANES).
 template <int W, bool PLANES>

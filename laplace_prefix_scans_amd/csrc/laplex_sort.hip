@@ -3,11 +3,13 @@
 //
 // Keys are the order-preserving unsigned image of the float bits (-0.0 made
 // equal to +0.0).  One read of the anchors builds all four 8-bit digit
-// histograms; then four single-pass ("onesweep") scatter passes, each tile
-// ranking its keys stably in LDS, publishing per-digit counts and looking back
-// over earlier tiles (decoupled look-back) to find its global offsets.  Pass
-// 1 generates the identity permutation itself; pass 4 writes the sorted
-// anchors and the permutation.
+// histograms and, for the first pass, each tile's digit counts; then four
+// single-pass ("onesweep") scatter passes, each tile ranking its keys stably
+// in LDS.  The first pass takes its tiles' global offsets from a scan of the
+// per-tile counts; the later passes, whose tiles' contents are only known once
+// the previous pass has run, publish per-digit counts and look back over
+// earlier tiles (decoupled look-back).  Pass 1 generates the identity
+// permutation itself; pass 4 writes the sorted anchors and the permutation.
 #include "laplex_kernels.hpp"
 
 namespace laplex {
@@ -44,46 +46,103 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, uint64_t count, uint32_t va
 // One replica of every histogram per lane position (lane mod 32), so the 32
 // lanes an LDS cycle serves always hit 32 different banks; 1024 threads keep
 // enough loads in flight with one block per CU.
+// The same read also counts the first pass's digit in each sort tile: block
+// b reads a contiguous range of chunks (two tiles each), keeps a running
+// count per digit, and writes each tile's count of the tiles before it in
+// the block's range (tcount) and the range's total (bsum[b]); an exclusive
+// scan of bsum over blocks then completes the first pass's offsets, so that
+// pass needs no look-back.  Tile counts are double-buffered by chunk parity
+// (one barrier per chunk) and the next chunk's keys are loaded before it.
+// The low digit's global histogram is the sum of the blocks' totals, so the
+// per-key LDS atomics are the same four as for the four histograms alone.
 constexpr int kHistRep = 32;
 constexpr int kHistBlock = 1024;
 constexpr int kHistItems = 16;
+constexpr int kTileRep = 8;
+static_assert(kHistBlock * kHistItems == 2 * kSortTile, "a histogram chunk is two sort tiles");
 
 __global__ __launch_bounds__(kHistBlock) void k_sort_hist(const uint32_t* __restrict__ a_bits, uint64_t n,
-                                                          uint32_t* __restrict__ hist, uint32_t* __restrict__ header) {
-  __shared__ uint32_t sh[4][256][kHistRep];
-  for (int i = threadIdx.x; i < 4 * 256 * kHistRep; i += kHistBlock) (&sh[0][0][0])[i] = 0;
+                                                          uint32_t* __restrict__ hist, uint32_t* __restrict__ header,
+                                                          uint32_t* __restrict__ tcount, uint32_t* __restrict__ bsum,
+                                                          uint64_t chunks_per_block) {
+  __shared__ uint32_t sh[3][256][kHistRep];     // digits 2..4
+  __shared__ uint32_t st[2][2][256][kTileRep];  // digit 1: [chunk parity][tile of the chunk][digit][replica]
+  for (int i = threadIdx.x; i < 3 * 256 * kHistRep; i += kHistBlock) (&sh[0][0][0])[i] = 0;
+  for (int i = threadIdx.x; i < 2 * 2 * 256 * kTileRep; i += kHistBlock) (&st[0][0][0][0])[i] = 0;
   __syncthreads();
-  const int rep = lane_id() % kHistRep;
-  uint32_t bad = 0;
+  const int rep = lane_id() % kHistRep, trep = lane_id() % kTileRep;
+  const uint64_t tiles = (n + kSortTile - 1) / kSortTile;
+  uint32_t bad = 0, run = 0;  // run: thread d < 256's count of digit d so far in this block's range
   const uint64_t chunk = (uint64_t)kHistBlock * kHistItems;
   const uint64_t nchunks = (n + chunk - 1) / chunk;
-  for (uint64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+  const uint64_t c0 = (uint64_t)blockIdx.x * chunks_per_block;
+  const uint64_t c1 = c0 + chunks_per_block < nchunks ? c0 + chunks_per_block : nchunks;
+  // the next chunk's keys are loaded (clamped into range, so every load is
+  // issued unconditionally) before this chunk's keys are counted; full
+  // chunks are counted without per-key conditions, so that the compiler
+  // waits only for this chunk's loads
+  uint32_t nxt[kHistItems];
+#pragma unroll
+  for (int it = 0; it < kHistItems; ++it) {
+    const uint64_t i = c0 * chunk + (uint64_t)it * kHistBlock + threadIdx.x;
+    nxt[it] = a_bits[i < n ? i : n - 1];
+  }
+  for (uint64_t c = c0; c < c1; ++c) {
     const uint64_t base = c * chunk;
+    const int par = (int)(c & 1);
     uint32_t u[kHistItems];
 #pragma unroll
-    for (int it = 0; it < kHistItems; ++it) {
-      const uint64_t i = base + (uint64_t)it * kHistBlock + threadIdx.x;
-      u[it] = i < n ? a_bits[i] : 0u;
-    }
+    for (int it = 0; it < kHistItems; ++it) u[it] = nxt[it];
 #pragma unroll
     for (int it = 0; it < kHistItems; ++it) {
-      const uint64_t i = base + (uint64_t)it * kHistBlock + threadIdx.x;
-      if (i < n) {
-        bad |= bits_nonfinite(u[it]) ? 1u : 0u;
-        const uint32_t k = float_to_key(u[it]);
-        atomicAdd(&sh[0][k & 255u][rep], 1u);
-        atomicAdd(&sh[1][(k >> 8) & 255u][rep], 1u);
-        atomicAdd(&sh[2][(k >> 16) & 255u][rep], 1u);
-        atomicAdd(&sh[3][k >> 24][rep], 1u);
+      const uint64_t i = base + chunk + (uint64_t)it * kHistBlock + threadIdx.x;
+      nxt[it] = a_bits[i < n ? i : n - 1];
+    }
+    auto count = [&](int it, uint32_t bits) {
+      bad |= bits_nonfinite(bits) ? 1u : 0u;
+      const uint32_t k = float_to_key(bits);
+      atomicAdd(&sh[0][(k >> 8) & 255u][rep], 1u);
+      atomicAdd(&sh[1][(k >> 16) & 255u][rep], 1u);
+      atomicAdd(&sh[2][k >> 24][rep], 1u);
+      atomicAdd(&st[par][it / (kHistItems / 2)][k & 255u][trep], 1u);
+    };
+    if (base + chunk <= n) {
+#pragma unroll
+      for (int it = 0; it < kHistItems; ++it) count(it, u[it]);
+    } else {
+#pragma unroll
+      for (int it = 0; it < kHistItems; ++it)
+        if (base + (uint64_t)it * kHistBlock + threadIdx.x < n) count(it, u[it]);
+    }
+    __syncthreads();
+    // (the buffer of this parity is next written two chunks on, after the
+    // next iteration's barrier, which every thread reaches after this)
+    if (threadIdx.x < 256) {
+      const int d = threadIdx.x;
+      uint32_t s0 = 0, s1 = 0;
+#pragma unroll
+      for (int r = 0; r < kTileRep; ++r) {
+        s0 += st[par][0][d][(r + d) % kTileRep];
+        s1 += st[par][1][d][(r + d) % kTileRep];
       }
+#pragma unroll
+      for (int r = 0; r < kTileRep; ++r) st[par][0][d][r] = st[par][1][d][r] = 0;
+      const uint64_t t = 2 * c;
+      if (t < tiles) tcount[t * 256 + d] = run;
+      if (t + 1 < tiles) tcount[(t + 1) * 256 + d] = run + s0;
+      run += s0 + s1;
     }
   }
+  if (threadIdx.x < 256) {
+    bsum[(uint64_t)blockIdx.x * 256 + threadIdx.x] = run;
+    if (run) atomicAdd(&hist[threadIdx.x], run);
+  }
   __syncthreads();
-  for (int i = threadIdx.x; i < 4 * 256; i += kHistBlock) {
+  for (int i = threadIdx.x; i < 3 * 256; i += kHistBlock) {
     uint32_t s = 0;
 #pragma unroll
     for (int r = 0; r < kHistRep; ++r) s += sh[i >> 8][i & 255][(r + i) % kHistRep];
-    if (s) atomicAdd(&hist[i], s);
+    if (s) atomicAdd(&hist[256 + i], s);
   }
   if (__ballot(bad) != 0ull && lane_id() == 0) atomicOr(&header[kHdrFlags], kFlagNonFinite);
 }
@@ -122,6 +181,45 @@ __global__ __launch_bounds__(256) void k_sort_offsets(const uint32_t* __restrict
   }
 }
 
+// ------------------------------------------------------------------ first-pass offsets
+// In place: bsum[b][d] (digit d's count in histogram block b's range) becomes
+// its exclusive prefix over blocks.  One 1024-thread block: thread (q, d)
+// scans digit d over the q-th quarter of the rows.
+constexpr int kScanThreads = 1024;
+constexpr int kScanQuarters = kScanThreads / 256;
+constexpr uint64_t kTableMinTiles = 64;
+
+__global__ __launch_bounds__(kScanThreads) void k_block_sum_scan(uint32_t* __restrict__ bsum, uint64_t rows) {
+  __shared__ uint32_t part[kScanQuarters][256];
+  const int q = threadIdx.x >> 8, d = threadIdx.x & 255;
+  const uint64_t seg = (rows + kScanQuarters - 1) / kScanQuarters;
+  const uint64_t g0 = (uint64_t)q * seg < rows ? (uint64_t)q * seg : rows;
+  const uint64_t g1 = g0 + seg < rows ? g0 + seg : rows;
+  constexpr int B = 16;
+  uint32_t s = 0;
+  for (uint64_t g = g0; g < g1; g += B) {
+    uint32_t v[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) v[j] = (g + j < g1) ? bsum[(g + j) * 256 + d] : 0u;
+#pragma unroll
+    for (int j = 0; j < B; ++j) s += v[j];
+  }
+  part[q][d] = s;
+  __syncthreads();
+  uint32_t run = 0;
+  for (int i = 0; i < q; ++i) run += part[i][d];
+  for (uint64_t g = g0; g < g1; g += B) {
+    uint32_t v[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) v[j] = (g + j < g1) ? bsum[(g + j) * 256 + d] : 0u;
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      if (g + j < g1) bsum[(g + j) * 256 + d] = run;
+      run += v[j];
+    }
+  }
+}
+
 // ------------------------------------------------------------------ onesweep pass
 // MODE 0: input is the anchors' float bits (keys computed here, values are the
 //         input indices); MODE 1: (key, value) pairs to pairs;
@@ -142,7 +240,9 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
                                                          uint32_t* __restrict__ header, int pass,
                                                          const uint32_t* __restrict__ digit_start, uint64_t n,
                                                          uint16_t* __restrict__ r_lpos, uint16_t* __restrict__ r_dstart,
-                                                         uint32_t* __restrict__ r_gbase, const uint32_t* __restrict__ pay) {
+                                                         uint32_t* __restrict__ r_gbase, const uint32_t* __restrict__ pay,
+                                                         const uint32_t* __restrict__ tcount, const uint32_t* __restrict__ bpre,
+                                                         uint64_t chunks_per_block) {
   static_assert(!PAY || MODE != 1, "the payload enters in pass 1 and leaves in pass 4");
   constexpr bool HOLDV = MODE != 0 || PAY;  // values held in registers (else recomputed input indices)
   static_assert(kSortBlock % 256 == 0, "at least one thread per digit value");
@@ -163,13 +263,20 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
   // iteration (64 bits), the wave's running count of that digit, unused}.
   static_assert(NW * 256 * sizeof(uint4) <= sizeof(s_kv), "ranking scratch fits in the staging buffer");
   uint4* s_match = reinterpret_cast<uint4*>(s_kv);
-  if (tid == 0) s_tile = atomicAdd(&header[kHdrTicket0 + pass], 1u);
+  // With tcount (large first passes) the offsets come from the table made
+  // by the histogram read, so tiles depend on no other tile and are placed
+  // by block index; otherwise tiles are taken in ticket order for the
+  // look-back.
+  const bool table = MODE == 0 && tcount != nullptr;
+  uint64_t xtile = 0;
+  if (table && !xcd_tile((n + TILE - 1) / TILE, xtile)) return;
+  if (!table && tid == 0) s_tile = atomicAdd(&header[kHdrTicket0 + pass], 1u);
   for (int i = tid; i < NW * 256; i += kSortBlock) s_match[i] = make_uint4(0u, 0u, 0u, 0u);
   if (tid < 256) s_thist[tid] = 0u;
   __syncthreads();
-  const uint32_t tile = s_tile;
+  const uint32_t tile = table ? (uint32_t)xtile : s_tile;
   // uniform: one scalar value for the whole workgroup
-  const bool early = __builtin_amdgcn_readfirstlane(header[kHdrEarly0 + pass]) != 0u;
+  const bool early = !table && __builtin_amdgcn_readfirstlane(header[kHdrEarly0 + pass]) != 0u;
   const uint64_t base = (uint64_t)tile * TILE;
 
   // load: wave w owns the contiguous run [w*64*E, (w+1)*64*E) of the tile;
@@ -269,7 +376,9 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
   // each round reads up to kLookback predecessors at once and consumes them
   // newest first until an inclusive prefix (or a not-yet-published tile)
   uint32_t excl = 0;
-  if (digit_owner) {
+  if (table) {
+    if (digit_owner) excl = bpre[((uint64_t)(tile >> 1) / chunks_per_block) * 256 + d] + tcount[(uint64_t)tile * 256 + d];
+  } else if (digit_owner) {
     ST* my = status + (uint64_t)tile * 256 + d;
     if (!early) store_agent(my, Status<ST>::pack(tile == 0 ? kFlagInclusive : kFlagAggregate, cnt));
     if (tile > 0) {
@@ -397,9 +506,12 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
 // ------------------------------------------------------------------ host side
 // pay: NULL (pass 4 writes the permutation to perm) or n payload words that
 // ride along with the keys (pass 4 writes them, sorted, to perm).
+// table: the first pass takes its offsets from the histogram's tables
+// (tcount and the scanned block sums, cpb chunks per histogram block).
 template <typename ST>
 static hipError_t launch_sort_passes(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,
-                                     const SortRoute* route, const uint32_t* pay, hipStream_t s) {
+                                     const SortRoute* route, const uint32_t* pay, bool table, uint64_t cpb,
+                                     hipStream_t s) {
   const uint32_t* a_bits = reinterpret_cast<const uint32_t*>(a);
   const uint64_t tiles = (n + kSortTile - 1) / kSortTile;
   ST* st = reinterpret_cast<ST*>(w.status);
@@ -412,11 +524,12 @@ static hipError_t launch_sort_passes(const SortWorkspace& w, const float* a, uin
     uint16_t* rl = route ? route->lpos[p] : nullptr;
     uint16_t* rd = route ? route->dstart[p] : nullptr;
     uint32_t* rg = route ? route->gbase[p] : nullptr;
-    const dim3 grid((unsigned)tiles), block(kSortBlock);
+    const dim3 grid((unsigned)tiles), grid0((unsigned)xcd_blocks(tiles)), block(kSortBlock);
 #define LAPLEX_PASS(MODE, PAY, NAME)                                                                                  \
   LAPLEX_LAUNCH(NAME, n, s,                                                                                          \
-                (k_onesweep<MODE, ST, PAY><<<grid, block, 0, s>>>(src, dst, fk, fv, a_bits, stp, w.header, p,          \
-                                                                  w.offsets + p * 256, n, rl, rd, rg, pay)))
+                (k_onesweep<MODE, ST, PAY><<<(MODE == 0 && table ? grid0 : grid), block, 0, s>>>(                     \
+                    src, dst, fk, fv, a_bits, stp, w.header, p, w.offsets + p * 256, n, rl, rd, rg, pay,                \
+                    MODE == 0 && table ? w.tcount : nullptr, w.gsum, cpb)))
     if (p == 0 && pay)
       LAPLEX_PASS(0, true, route ? "k_onesweep_first_pay_routed" : "k_onesweep_first_pay");
     else if (p == 0)
@@ -443,6 +556,7 @@ size_t sort_status_bytes(uint64_t n) {
 
 static hipError_t sort_impl(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,
                             const SortRoute* route, const uint32_t* pay, hipStream_t s) {
+  if (n == 0) return hipSuccess;
   // clear the header, histograms and look-back status with a fill kernel
   const uint64_t clear_words = (uint64_t)(kSortHeaderBytes / 4) + sort_status_bytes(n) / 4;
   const unsigned fill_blocks = (unsigned)std::min<uint64_t>((clear_words + 255) / 256, 4096);
@@ -450,14 +564,23 @@ static hipError_t sort_impl(const SortWorkspace& w, const float* a, uint64_t n, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint64_t chunk = (uint64_t)kHistBlock * kHistItems;
-  const unsigned hist_blocks = (unsigned)std::min<uint64_t>((n + chunk - 1) / chunk, 256);
+  const uint64_t nchunks = (n + chunk - 1) / chunk;
+  const uint64_t hist_blocks = std::min<uint64_t>(nchunks, kHistMaxBlocks);
+  const uint64_t cpb = (nchunks + hist_blocks - 1) / hist_blocks;
   LAPLEX_LAUNCH("k_sort_hist", n, s,
-                k_sort_hist<<<hist_blocks, kHistBlock, 0, s>>>(reinterpret_cast<const uint32_t*>(a), n, w.hist, w.header));
+                k_sort_hist<<<(unsigned)hist_blocks, kHistBlock, 0, s>>>(reinterpret_cast<const uint32_t*>(a), n, w.hist,
+                                                                         w.header, w.tcount, w.gsum, cpb));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   LAPLEX_LAUNCH("k_sort_offsets", 1024, s, k_sort_offsets<<<1, 256, 0, s>>>(w.hist, w.offsets, w.header));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (n <= (1ull << 30)) return launch_sort_passes<uint32_t>(w, a, n, a_sorted, perm, route, pay, s);
-  return launch_sort_passes<uint64_t>(w, a, n, a_sorted, perm, route, pay, s);
+  // small sorts keep the first pass's look-back (one launch fewer)
+  const bool table = sort_tiles(n) >= kTableMinTiles;
+  if (table) {
+    LAPLEX_LAUNCH("k_block_sum_scan", hist_blocks, s, k_block_sum_scan<<<1, kScanThreads, 0, s>>>(w.gsum, hist_blocks));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (n <= (1ull << 30)) return launch_sort_passes<uint32_t>(w, a, n, a_sorted, perm, route, pay, table, cpb, s);
+  return launch_sort_passes<uint64_t>(w, a, n, a_sorted, perm, route, pay, table, cpb, s);
 }
 
 hipError_t sort_anchors(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,

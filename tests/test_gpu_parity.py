@@ -34,6 +34,13 @@ def _anchor_cases():
         "wide_range_30000": (r.standard_normal(30000) * 1e30).astype(np.float32),
         "dense_ties_2p20": r.uniform(0, 2 ** 17, 1 << 20).astype(np.float32),
         "ragged_300001": r.uniform(-1e4, 1e4, 300001).astype(np.float32),
+        # around the size (64 tiles of 8192) from which the first pass takes
+        # its offsets from the histogram's per-tile tables
+        "tiles63_ties": r.integers(-3000, 3000, 63 * 8192).astype(np.float32),
+        "tiles64_ragged": r.uniform(0, 1e5, 64 * 8192 - 5).astype(np.float32),
+        "signed_zero_600000": r.choice(np.array([0.0, -0.0, 2.0, -2.0], np.float32), 600000),
+        # 257 histogram chunks: two chunks per histogram block, some blocks empty
+        "chunks257_int_ties": r.integers(0, 1 << 12, 16384 * 257 + 3).astype(np.float32),
     }
 
 

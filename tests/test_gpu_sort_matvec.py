@@ -35,7 +35,7 @@ def _two_call(a, x, route):
     return host(lp.laplex_matvec_sym(a_s, perm, dev(x), route=ra))
 
 
-CASES = [(1, 1), (2, 1), (3, 2), (1000, 1), (4096, 1), (8192, 1), (8193, 1), (70001, 1), (300000, 1), (5000, 2),
+CASES = [(1, 1), (2, 1), (3, 2), (1000, 1), (4096, 1), (8192, 1), (8193, 1), (70001, 1), (300000, 1), (600001, 1), (5000, 2),
          (9001, 3), (8191, 4), (6000, 5), (3001, 8)]
 
 
