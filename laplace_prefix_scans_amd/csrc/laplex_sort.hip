@@ -378,7 +378,10 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
   uint32_t excl = 0;
   if (table) {
     if (digit_owner) excl = bpre[((uint64_t)(tile >> 1) / chunks_per_block) * 256 + d] + tcount[(uint64_t)tile * 256 + d];
-  } else if (digit_owner) {
+  } else if (digit_owner && (d < 255 ? digit_start[d + 1] : (uint32_t)n) != digit_start[d]) {
+    // (a digit value no key has needs no prefix: its owner neither publishes
+    // nor looks back, which spares most of the status traffic of a pass
+    // whose digit takes few values)
     ST* my = status + (uint64_t)tile * 256 + d;
     if (!early) store_agent(my, Status<ST>::pack(tile == 0 ? kFlagInclusive : kFlagAggregate, cnt));
     if (tile > 0) {
