@@ -39,6 +39,29 @@ def test_sym_route_bitwise(n, m):
     assert err <= TOL
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("n,m", [((1 << 25) + 12345, 1), ((1 << 25) + 777, 2), ((1 << 25) + 3, 4)])
+def test_sym_route_bitwise_large(n, m):
+    """Past 4096 sort tiles (three-level carries, many workgroups per XCD in
+    every route pass): the route path gives the same bits as the index path,
+    and the one-call path (m = 1) the same bits as both."""
+    import laplace_prefix_scans_amd as lp
+    r = _rng(n * 10 + m)
+    a = r.uniform(0, n / 6.0 + 1.0, n).astype(np.float32)
+    a[::11] = a[0]
+    x = r.standard_normal((n, m)).astype(np.float32)
+    a_s, perm, route = _sorted_with_route(a)
+    x_d = dev(x)
+    y_route = lp.laplex_matvec_sym(a_s, perm, x_d, route=route)
+    y_index = lp.laplex_matvec_sym(a_s, perm, x_d)
+    assert np.array_equal(host(y_route).view(np.uint32), host(y_index).view(np.uint32)), "route and index paths differ"
+    if m == 1:
+        y_one = lp.laplex_sort_matvec_sym(dev(a), x_d, check=True)
+        assert np.array_equal(host(y_one).view(np.uint32), host(y_route).view(np.uint32)), "one-call path differs"
+        err = oracle.normwise_error(host(y_one), oracle.sym_apply(a, x), oracle.sym_apply(a, np.abs(x)))
+        assert err <= TOL
+
+
 @pytest.mark.parametrize("n,m", [(4096, 1), (70001, 2), (9999, 4)])
 def test_phased_route_bitwise(n, m):
     import laplace_prefix_scans_amd as lp
