@@ -360,10 +360,11 @@ def main():
     one_call = w.kind == "sym" and m == 1 and use_route and not args.two_call
     a = torch.from_numpy(w.a).to(dev)
     x = torch.from_numpy(w.x).to(dev)
-    ra = lp.route_buffer(n, device=dev) if use_route else None
-    a_s = torch.empty_like(a)
-    pa = torch.empty(n, dtype=torch.uint32, device=dev)
-    ws_sort_a = lp.workspace(lp.LAPLEX_OP_SORT, n, device=dev)
+    # the sort handle of a (the one-call path keeps its own in its workspace)
+    ra = lp.route_buffer(n, device=dev) if use_route and not one_call else None
+    a_s = torch.empty_like(a) if not one_call else None
+    pa = torch.empty(n, dtype=torch.uint32, device=dev) if not one_call else None
+    ws_sort_a = lp.workspace(lp.LAPLEX_OP_SORT, n, device=dev) if not one_call else None
     y = torch.empty((n, m), dtype=torch.float32, device=dev) if w.kind != "gram" else None
     if w.kind == "gram":
         b = torch.from_numpy(w.b).to(dev)
@@ -546,15 +547,19 @@ def main():
         "host_gen_s": round(t_gen, 1),
     }
     if w.kind in ("sym", "general", "phased") and not args.no_backward:
-        if one_call:  # the backward takes a sort handle: build it (untimed)
-            del ws_apply
-            torch.cuda.empty_cache()
-            lp.laplex_sort_anchors(a, a_s, pa, route=ra, ws=ws_sort_a)
         gen = torch.Generator(device=dev).manual_seed(0x6AAD)
         g = torch.randn((n,) if x.dim() == 1 else (n, m), generator=gen, device=dev)
         da = torch.empty(n, dtype=torch.float32, device=dev)
         dx = torch.empty_like(x)
-        if w.kind == "sym":
+        if w.kind == "sym" and one_call:
+            # the backward of the timed one-call forward, from what it left
+            # in its workspace (sorted anchors, route, x in sorted order)
+            ws_b = lp.workspace(lp.LAPLEX_OP_SYM_BACKWARD, n, 0, m, device=dev)
+
+            def bstep():
+                lp.laplex_sort_matvec_sym_backward(ws_apply, g, dx=dx, da=da, ws=ws_b)
+            what = "dx = K g and da, from g and the one-call forward's workspace"
+        elif w.kind == "sym":
             ws_b = lp.workspace(lp.LAPLEX_OP_SYM_BACKWARD, n, 0, m, device=dev)
 
             def bstep():

@@ -121,6 +121,20 @@ laplex_status laplex_matvec_sym(const float* a_sorted, const uint32_t* perm, con
 laplex_status laplex_sort_matvec_sym(const float* a, uint64_t n, uint32_t m, const float* x, float* y, void* ws, size_t ws_bytes,
                                      hipStream_t stream);
 
+/* Backward of laplex_sort_matvec_sym from what that call left in its
+ * workspace (the sorted anchors, the route or permutation, and x in sorted
+ * order): dx = K g and the anchor gradient da (section 2.3: the operator is
+ * differentiable in its anchors; da_i = -sum_j sign(a_i - a_j) K_ij
+ * sum_c (g_ic x_jc + x_ic g_jc), ties contributing nothing), as
+ * laplex_backward_sym computes them.  Only g is moved into sorted order.
+ * fwd_ws: the workspace of a laplex_sort_matvec_sym call with the same a, x, n
+ * and m, unchanged since (fwd_ws_bytes as passed to it); g: n x m (input,
+ * original order); dx: n x m, da: n (outputs, original order); ws:
+ * laplex_workspace_bytes(LAPLEX_OP_SYM_BACKWARD, n, 0, m) bytes, not
+ * overlapping fwd_ws. */
+laplex_status laplex_sort_matvec_sym_backward(const void* fwd_ws, size_t fwd_ws_bytes, uint64_t n, uint32_t m, const float* g,
+                                              float* dx, float* da, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* General operator y = LAPLEX(a, b) x with a != b (section 2.2, general case:
  * the input anchors b are placed into the intervals of the sorted output
  * anchors a and propagated with the same scan primitive; here the two sorted

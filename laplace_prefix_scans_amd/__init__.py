@@ -7,7 +7,8 @@ not been built the calls raise -- there is no fallback.
 
     a_sorted, perm = laplex_sort_anchors(a)          # sort handle of a
     y = laplex_matvec_sym(a_sorted, perm, x)         # y_i = sum_j exp(-|a_i - a_j|) x_j
-    y = laplex_sort_matvec_sym(a, x)                 # the same from unsorted anchors, in one call
+    y = laplex_sort_matvec_sym(a, x, ws=ws)          # the same from unsorted anchors, in one call
+    dx, da = laplex_sort_matvec_sym_backward(ws, g)  # its backward, from what the call left in ws
     y = laplex_matvec_general(a_sorted, perm, b_sorted, perm_b, xb)
     y = laplex_matvec_phased(a_sorted, perm, phi, x)  # extra cos(phi_i - phi_j)
     dx, da = laplex_backward_sym(a_sorted, perm, x, g)  # gradients for g = dL/dy
@@ -39,6 +40,7 @@ from ._binding import (  # noqa: F401
     laplex_matvec_phased,
     laplex_matvec_sym,
     laplex_sort_matvec_sym,
+    laplex_sort_matvec_sym_backward,
     laplex_sort_anchors,
     laplex_status_poll,
     laplex_route_bytes,

@@ -58,6 +58,8 @@ def lib():
         L.laplex_matvec_sym.argtypes = [vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
         L.laplex_sort_matvec_sym.argtypes = [vp, u64, u32, vp, vp, vp, sz, vp]
         L.laplex_sort_matvec_sym.restype = i32
+        L.laplex_sort_matvec_sym_backward.argtypes = [vp, sz, u64, u32, vp, vp, vp, vp, sz, vp]
+        L.laplex_sort_matvec_sym_backward.restype = i32
         L.laplex_matvec_general.argtypes = [vp, vp, vp, u64, vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
         L.laplex_matvec_phased.argtypes = [vp, vp, vp, vp, u64, vp, vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
         L.laplex_backward_sym.argtypes = [vp, vp, vp, u64, u32, vp, vp, vp, vp, vp, sz, vp]
@@ -215,6 +217,27 @@ def laplex_sort_matvec_sym(a: torch.Tensor, x: torch.Tensor, y: Optional[torch.T
     if check:
         _check(L.laplex_status_poll(_ptr(ws), _stream(dev)), "laplex_sort_matvec_sym")
     return y
+
+
+def laplex_sort_matvec_sym_backward(fwd_ws: torch.Tensor, g: torch.Tensor, dx: Optional[torch.Tensor] = None,
+                                    da: Optional[torch.Tensor] = None,
+                                    ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(dx, da) for the upstream gradient g of y = laplex_sort_matvec_sym(a, x, ws=fwd_ws), from what that
+    call left in fwd_ws (sorted anchors, route or permutation, x in sorted order); g is (n,) or (n, m)
+    like x.  ``ws``: optional workspace of laplex_workspace_bytes(LAPLEX_OP_SYM_BACKWARD, n, 0, m) bytes."""
+    _vec(fwd_ws, "fwd_ws", torch.uint8)
+    _vec(g, "g")
+    n, dev = g.shape[0], g.device
+    m = _cols(g, n, "g")
+    dx = torch.empty_like(g) if dx is None else dx
+    _cols(dx, n, "dx")
+    da = torch.empty(n, dtype=torch.float32, device=dev) if da is None else _vec(da, "da")
+    if da.dim() != 1 or da.shape[0] != n:
+        raise ValueError("da must be (%d,)" % n)
+    ws = _ws(ws, LAPLEX_OP_SYM_BACKWARD, n, 0, m, dev)
+    _check(lib().laplex_sort_matvec_sym_backward(_ptr(fwd_ws), fwd_ws.numel(), n, m, _ptr(g), _ptr(dx), _ptr(da), _ptr(ws),
+                                                 ws.numel(), _stream(dev)), "laplex_sort_matvec_sym_backward")
+    return dx, da
 
 
 def laplex_backward_sym(a_sorted: torch.Tensor, perm: torch.Tensor, x: torch.Tensor, g: torch.Tensor,

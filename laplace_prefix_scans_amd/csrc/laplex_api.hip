@@ -314,6 +314,34 @@ extern "C" laplex_status laplex_sort_matvec_sym(const float* a, uint64_t n, uint
   return from_hip(apply_sym(w.apply, Variant::Sym, w.a_s, w.perm, w.route ? &r : nullptr, nullptr, n, m, x, y, stream));
 }
 
+extern "C" laplex_status laplex_sort_matvec_sym_backward(const void* fwd_ws, size_t fwd_ws_bytes, uint64_t n, uint32_t m,
+                                                         const float* g, float* dx, float* da, void* ws, size_t ws_bytes,
+                                                         hipStream_t stream) {
+  if (n == 0 || m == 0) return LAPLEX_OK;
+  if (n > kMaxLen || m > kMaxCols) return LAPLEX_ERR_SIZE;
+  if (!fwd_ws || !g || !dx || !da || !ws) return LAPLEX_ERR_NULL;
+  if (misaligned(fwd_ws, 256) || misaligned(g, 4) || misaligned(dx, 4) || misaligned(da, 4) || misaligned(ws, 256))
+    return LAPLEX_ERR_ALIGN;
+  size_t need_f = 0, need = 0;
+  carve_sort_sym(nullptr, n, m, &need_f);
+  carve_backward(nullptr, n, 0, m, false, &need);
+  if (fwd_ws_bytes < need_f || ws_bytes < need) return LAPLEX_ERR_WORKSPACE;
+  const size_t xb = n * (size_t)m * 4, vb = n * 4;
+  for (const void* out : {static_cast<const void*>(dx), static_cast<const void*>(da)}) {
+    const size_t ob = out == dx ? xb : vb;
+    if (overlaps(out, ob, g, xb) || overlaps(out, ob, fwd_ws, fwd_ws_bytes) || overlaps(out, ob, ws, ws_bytes)) return LAPLEX_ERR_OVERLAP;
+  }
+  if (overlaps(dx, xb, da, vb) || overlaps(ws, ws_bytes, fwd_ws, fwd_ws_bytes) || overlaps(g, xb, ws, ws_bytes))
+    return LAPLEX_ERR_OVERLAP;
+  // the forward's sorted anchors, permutation (m != 1), route (m <= 4) and
+  // x in sorted order (left in its apply workspace)
+  const SortSymWorkspace f = carve_sort_sym(const_cast<void*>(fwd_ws), n, m, nullptr);
+  SortRoute r{};
+  if (f.route) r = carve_route(f.route, n);
+  const BackwardWorkspace bw = carve_backward(ws, n, 0, m, false, nullptr);
+  return from_hip(backward_sym(bw, f.a_s, f.perm, f.route ? &r : nullptr, n, m, nullptr, g, dx, da, stream, f.apply.xs));
+}
+
 extern "C" laplex_status laplex_backward_sym(const float* a_sorted, const uint32_t* perm, const void* route, uint64_t n,
                                              uint32_t m, const float* x, const float* g, float* dx, float* da, void* ws,
                                              size_t ws_bytes, hipStream_t stream) {

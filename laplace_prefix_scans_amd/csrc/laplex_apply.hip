@@ -1126,9 +1126,13 @@ __global__ void k_scatter_rows(const float* __restrict__ src, const uint32_t* __
 static unsigned rows_grid(uint64_t rows) { return (unsigned)std::min<uint64_t>((rows + 255) / 256, 8192); }
 
 template <int C>
+// xs_sorted: x already in sorted order (kept by a one-call forward); then
+// only g is moved into sorted order.
 static hipError_t run_bwd_sym(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm, const SortRoute* route,
-                              uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da, hipStream_t s) {
+                              uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da, hipStream_t s,
+                              const float* xs_sorted = nullptr) {
   const ApplyWorkspace& w = bw.w;
+  const float* xs = xs_sorted ? xs_sorted : w.xs;
   constexpr int P = bwd_tile(C);
   const uint64_t T = (n + P - 1) / P;
   const uint32_t M = 4 * m;
@@ -1136,7 +1140,7 @@ static hipError_t run_bwd_sym(const BackwardWorkspace& bw, const float* a_s, con
   const bool routed = route != nullptr && m <= kRouteMaxCols;
   const bool vec = (reinterpret_cast<uintptr_t>(a_s) & 15) == 0;
   hipError_t e;
-  if (C == 1 && m == 1 && routed) {
+  if (C == 1 && m == 1 && routed && !xs_sorted) {
     // one column: x and g travel as pairs (one read of each route table for
     // both); dx and da go back one by one (an inverse pass of pairs stages
     // twice the LDS and fits half the workgroups)
@@ -1155,21 +1159,23 @@ static hipError_t run_bwd_sym(const BackwardWorkspace& bw, const float* a_s, con
     return route_inverse(*route, n, 1, bw.das, da, w.t0, w.t1, s);
   }
   if (routed) {
-    if ((e = route_forward(*route, n, m, x, w.xs, w.t0, w.t1, s)) != hipSuccess) return e;
+    if (!xs_sorted && (e = route_forward(*route, n, m, x, w.xs, w.t0, w.t1, s)) != hipSuccess) return e;
     if ((e = route_forward(*route, n, m, g, bw.gs, w.t0, w.t1, s)) != hipSuccess) return e;
   } else {
-    LAPLEX_LAUNCH("k_gather_rows", n, s, k_gather_rows<<<rows_grid(n), 256, 0, s>>>(x, perm, nullptr, n, m, w.xs, nullptr));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!xs_sorted) {
+      LAPLEX_LAUNCH("k_gather_rows", n, s, k_gather_rows<<<rows_grid(n), 256, 0, s>>>(x, perm, nullptr, n, m, w.xs, nullptr));
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     LAPLEX_LAUNCH("k_gather_rows", n, s, k_gather_rows<<<rows_grid(n), 256, 0, s>>>(g, perm, nullptr, n, m, bw.gs, nullptr));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   LAPLEX_LAUNCH("k_bwd_reduce", n, s,
-                k_bwd_reduce<C, false><<<grid, block, 0, s>>>(a_s, w.xs, bw.gs, n, m, w.bf, w.bb, w.tanch, vec));
+                k_bwd_reduce<C, false><<<grid, block, 0, s>>>(a_s, xs, bw.gs, n, m, w.bf, w.bb, w.tanch, vec));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = tile_carries(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb, w.gbf, w.gbb, w.gcf, w.gcb, w.ganch, s, 2 * m)) != hipSuccess)
     return e;
   LAPLEX_LAUNCH("k_bwd_apply", n, s,
-                k_bwd_apply<C, false><<<grid, block, 0, s>>>(a_s, w.xs, bw.gs, w.cf, w.cb, w.tanch, n, m, T, w.zs, bw.das, vec));
+                k_bwd_apply<C, false><<<grid, block, 0, s>>>(a_s, xs, bw.gs, w.cf, w.cb, w.tanch, n, m, T, w.zs, bw.das, vec));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (routed) {
     if ((e = route_inverse(*route, n, m, w.zs, dx, w.t0, w.t1, s)) != hipSuccess) return e;
@@ -1182,12 +1188,13 @@ static hipError_t run_bwd_sym(const BackwardWorkspace& bw, const float* a_s, con
 }
 
 hipError_t backward_sym(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm, const SortRoute* route,
-                        uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da, hipStream_t s) {
+                        uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da, hipStream_t s,
+                        const float* xs_sorted) {
   switch (column_chunk(m)) {
-    case 8: return run_bwd_sym<8>(bw, a_s, perm, route, n, m, x, g, dx, da, s);
-    case 4: return run_bwd_sym<4>(bw, a_s, perm, route, n, m, x, g, dx, da, s);
-    case 2: return run_bwd_sym<2>(bw, a_s, perm, route, n, m, x, g, dx, da, s);
-    default: return run_bwd_sym<1>(bw, a_s, perm, route, n, m, x, g, dx, da, s);
+    case 8: return run_bwd_sym<8>(bw, a_s, perm, route, n, m, x, g, dx, da, s, xs_sorted);
+    case 4: return run_bwd_sym<4>(bw, a_s, perm, route, n, m, x, g, dx, da, s, xs_sorted);
+    case 2: return run_bwd_sym<2>(bw, a_s, perm, route, n, m, x, g, dx, da, s, xs_sorted);
+    default: return run_bwd_sym<1>(bw, a_s, perm, route, n, m, x, g, dx, da, s, xs_sorted);
   }
 }
 

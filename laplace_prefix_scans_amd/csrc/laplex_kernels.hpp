@@ -142,8 +142,11 @@ struct BackwardWorkspace {
   float* dphs;   // phase gradient in sorted(-a) order (n; phased only)
   float* dpsis;  // column-phase gradient in sorted-b order (k; general phased only)
 };
+// xs_sorted: x already in sorted order (n x m, e.g. kept by a forward apply);
+// then x is not read and only g is moved.
 hipError_t backward_sym(const BackwardWorkspace& bw, const float* a_s, const uint32_t* perm, const SortRoute* route,
-                        uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da, hipStream_t s);
+                        uint64_t n, uint32_t m, const float* x, const float* g, float* dx, float* da, hipStream_t s,
+                        const float* xs_sorted = nullptr);
 
 // Backward of the symmetric phased operator: dx (n x m), da, dphi (n).  Scans
 // four columns per input column (cos/sin phase times x and g) under both

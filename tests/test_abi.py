@@ -141,6 +141,16 @@ def test_host_argument_errors(L):
     assert SM(A, 1000, 1, vp(0x500000), vp(0x500100), vp(0x10000000), needs, None) == OVERLAP  # y on x
     assert SM(A, 1000, 1, vp(0x500000), vp(0x100100), vp(0x10000000), needs, None) == OVERLAP  # y on a
     assert SM(vp(0x10000100), 1000, 1, vp(0x500000), vp(0x600000), vp(0x10000000), needs, None) == OVERLAP  # a in ws
+    # backward from a one-call forward's workspace
+    SB = L.laplex_sort_matvec_sym_backward
+    assert SB(None, 0, 0, 1, None, None, None, None, 0, None) == OK
+    assert SB(W, 1 << 30, 10, 1, None, B, A, W, 1 << 30, None) == NULL
+    assert SB(W, 1 << 40, 1 << 32, 1, A, B, vp(0x300000), vp(0x20000000), 1 << 40, None) == SIZE
+    needb = L.laplex_workspace_bytes(5, 1000, 0, 1)
+    assert SB(vp(0x10000000), needs, 1000, 1, A, B, vp(0x300000), vp(0x20000000), needb - 256, None) == WS
+    assert SB(vp(0x10000000), needs - 256, 1000, 1, A, B, vp(0x300000), vp(0x20000000), needb, None) == WS
+    assert SB(vp(0x10000000), needs, 1000, 1, A, vp(0x100100), vp(0x300000), vp(0x20000000), needb, None) == OVERLAP  # dx on g
+    assert SB(vp(0x10000000), needs, 1000, 1, A, vp(0x10000100), vp(0x300000), vp(0x20000000), needb, None) == OVERLAP
     # route: too small, misaligned, overlapping
     assert L.laplex_sort_anchors(A, 1000, B, vp(0x300000), vp(0x20000000), 16, vp(0x10000000), 1 << 30, None) == WS
     assert L.laplex_sort_anchors(A, 1000, B, vp(0x300000), vp(0x20000010), 1 << 20, vp(0x10000000), 1 << 30, None) == ALIGN

@@ -102,6 +102,49 @@ def test_backward_two_far_clusters():
     assert e1 <= TOL and e2 <= TOL
 
 
+def _run_one_call(a, x, g):
+    """Forward in one call (laplex_sort_matvec_sym with a kept workspace),
+    then the backward from that workspace."""
+    import laplace_prefix_scans_amd as lp
+    n, m = x.shape
+    ws = lp.workspace(lp.LAPLEX_OP_SORT_SYM, n, 0, m)
+    y = lp.laplex_sort_matvec_sym(dev(a), dev(x), ws=ws, check=True)
+    dx, da = lp.laplex_sort_matvec_sym_backward(ws, dev(g))
+    return host(y), host(dx), host(da)
+
+
+@pytest.mark.parametrize("n,m", [(1, 1), (2, 1), (7, 2), (2049, 1), (4097, 3), (70001, 1), (65536, 4), (12345, 8),
+                                 (600001, 1)])
+@pytest.mark.parametrize("ties", [False, True])
+def test_backward_from_one_call_forward(n, m, ties):
+    """The backward from a one-call forward's workspace (x kept in sorted
+    order, only g moved): the oracle's gradients, and the same bits as the
+    backward given the sort handle (routed when m <= 4, by index above)."""
+    a, x, g = _case(n, m, 500 + n + 7 * m, ties)
+    y, dx, da = _run_one_call(a, x, g)
+    e_dx, e_da = _errors(a, x, g, dx, da)
+    assert e_dx <= TOL and e_da <= TOL, "n=%d m=%d ties=%s: dx %.2e da %.2e" % (n, m, ties, e_dx, e_da)
+    dx2, da2 = _run(a, x, g, m <= 4)
+    assert np.array_equal(dx.view(np.uint32), dx2.reshape(dx.shape).view(np.uint32))
+    assert np.array_equal(da.view(np.uint32), da2.view(np.uint32))
+
+
+def test_backward_from_one_call_rejects_bad_arguments():
+    import torch
+    import laplace_prefix_scans_amd as lp
+    n = 1000
+    a, x, g = _case(n, 1, 9, False)
+    ws = lp.workspace(lp.LAPLEX_OP_SORT_SYM, n, 0, 1)
+    lp.laplex_sort_matvec_sym(dev(a), dev(x), ws=ws)
+    with pytest.raises(lp.LaplexError):  # forward workspace of fewer anchors
+        lp.laplex_sort_matvec_sym_backward(ws[:1024], dev(g))
+    gd = dev(g)
+    with pytest.raises(lp.LaplexError):  # dx on top of g
+        lp.laplex_sort_matvec_sym_backward(ws, gd, dx=gd)
+    with pytest.raises(ValueError):
+        lp.laplex_sort_matvec_sym_backward(ws, gd, da=torch.empty(n - 1, device="cuda"))
+
+
 def test_backward_rejects_bad_arguments():
     import torch
     import laplace_prefix_scans_amd as lp
@@ -119,7 +162,8 @@ def test_backward_rejects_bad_arguments():
 def test_backward_sym2p30_sampled():
     """The n = 2^30 workload (m = 1, routes): da at spot rows (extreme anchors,
     tile boundaries, random rows) against the plain definition, and dx = K g
-    through the symmetry <u, dx(g)> = <K u, g>."""
+    through the symmetry <u, dx(g)> = <K u, g>; the backward from a one-call
+    forward's workspace gives the same bits."""
     import torch
     import laplace_prefix_scans_amd as lp
     from synth import make_workload
@@ -147,3 +191,12 @@ def test_backward_sym2p30_sampled():
     scale = float(torch.dot(u.abs().double(), kabs.double()))
     print("dx symmetry |lhs-rhs|/scale = %.3e" % (abs(lhs - rhs) / scale), flush=True)
     assert abs(lhs - rhs) <= TOL * scale
+    # the backward the benchmark times: from a one-call forward's workspace
+    del ku, kabs, u, a_s, pa, route
+    torch.cuda.empty_cache()
+    ws = lp.workspace(lp.LAPLEX_OP_SORT_SYM, w.n, 0, 1)
+    lp.laplex_sort_matvec_sym(dev(w.a), dev(w.x), ws=ws, check=True)
+    dx1, da1 = lp.laplex_sort_matvec_sym_backward(ws, dev(g))
+    assert torch.equal(dx1.view(torch.int32), dx.view(torch.int32)), "one-call backward dx differs"
+    assert torch.equal(da1.view(torch.int32), da.view(torch.int32)), "one-call backward da differs"
+    print("one-call backward: same bits", flush=True)

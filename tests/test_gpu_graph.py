@@ -37,7 +37,19 @@ def _setup(kind, n, k, m):
     x = torch.empty(rows_x, m, device=dev)
     st["x"] = x
     outs = []
-    if kind == "sort_sym":
+    if kind == "sort_sym_backward":
+        g = torch.empty(n, m, device=dev)
+        st["g"] = g
+        y = torch.empty(n, m, device=dev)
+        dx, da = torch.empty(n, m, device=dev), torch.empty(n, device=dev)
+        ws = lp.workspace(lp.LAPLEX_OP_SORT_SYM, n, 0, m, device=dev)
+        ws_b = lp.workspace(lp.LAPLEX_OP_SYM_BACKWARD, n, 0, m, device=dev)
+
+        def op():
+            lp.laplex_sort_matvec_sym(a, x, y=y, ws=ws)
+            lp.laplex_sort_matvec_sym_backward(ws, g, dx=dx, da=da, ws=ws_b)
+        outs = [y, dx, da]
+    elif kind == "sort_sym":
         y = torch.empty(n, m, device=dev)
         ws = lp.workspace(lp.LAPLEX_OP_SORT_SYM, n, 0, m, device=dev)
 
@@ -142,7 +154,7 @@ def _setup(kind, n, k, m):
     return step, fill, outs, [a_s, pa]
 
 
-@pytest.mark.parametrize("kind,n,k,m", [("sort_sym", 100000, 0, 1), ("sym", 100000, 0, 1), ("sym", 70001, 0, 8), ("phased", 50000, 0, 4),
+@pytest.mark.parametrize("kind,n,k,m", [("sort_sym", 100000, 0, 1), ("sort_sym_backward", 80000, 0, 1), ("sym", 100000, 0, 1), ("sym", 70001, 0, 8), ("phased", 50000, 0, 4),
                                         ("general", 90000, 7000, 1), ("sym_backward", 60000, 0, 2),
                                         ("gen_backward", 40000, 9000, 1), ("gram", 3000, 5000, 1),
                                         ("phased_backward", 30000, 0, 3), ("phased_gen_backward", 20000, 6000, 2)])
