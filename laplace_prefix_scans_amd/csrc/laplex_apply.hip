@@ -110,8 +110,8 @@ __device__ __forceinline__ void tile_scan_fu(const float (&ae)[E], const float (
   // forward, at the last anchor s_ref of the previous wave (the tile carry's
   // anchor for wave 0): lane l < wid holds wave l's aggregate weighted by
   // exp(s_end(l) - s_ref), lane kWave-1 the tile carry weighted by
-  // exp(sf - s_ref); backward, mirrored.  Lane sums are butterflies, so every
-  // lane gets the same bits.
+  // exp(sf - s_ref); backward, mirrored.  The lane sums give every lane the
+  // same bits.
   static_assert(NW < kWave, "one lane per wave aggregate plus one for the tile carry");
   const float sw = wid > 0 ? s_wfs[wid - 1] : sf;
   const float sz2 = wid < NW - 1 ? s_wbs[wid + 1] : sb;
@@ -189,16 +189,17 @@ constexpr uint64_t kCarryMinRun = 8;
 // Scan of the tile aggregates into the carry entering each tile from the left
 // (cf: value at the previous tile's last element) and from the right (cb:
 // value at the next tile's first element).  One workgroup per column: each
-// thread owns a contiguous run of tiles, folds it as a direct weighted sum
-// (every weight exp(s - s_end) <= 1), wave 0 scans the run aggregates 64 per
-// round (at most 16 rounds; runs hold at least 8 tiles, so a few thousand
-// tiles take a few rounds), then each thread walks its run again writing
-// carries, with the loads of each batch of tiles issued before its dependent
-// chain.
+// thread owns a contiguous run of tiles and folds it in both directions as
+// direct weighted sums (every weight exp(-|s - s_end|) <= 1); wave 0 scans
+// the forward run aggregates and wave 1 the backward ones, 64 per round, at
+// the same time (at most 16 rounds; runs hold at least 8 tiles, so a few
+// thousand tiles take a few rounds); then each thread walks its run once more
+// writing both carries, with the loads of each batch of tiles issued before
+// their dependent chains.
 __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restrict__ bf, const float* __restrict__ bb,
                                                             const float2* __restrict__ tanch, uint64_t T, uint32_t M,
                                                             uint32_t tie_from, float* __restrict__ cf, float* __restrict__ cb) {
-  __shared__ float sB[kCarryBlock], sS[kCarryBlock];
+  __shared__ float sB[kCarryBlock], sS[kCarryBlock], sD[kCarryBlock], sT[kCarryBlock];
   const uint32_t c = blockIdx.x;
   const bool tie = c >= tie_from;  // columns from tie_from on scan with the tie decay
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
@@ -208,16 +209,24 @@ __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restr
   const uint64_t t0 = std::min<uint64_t>(T, (uint64_t)tid * q), t1 = std::min<uint64_t>(T, t0 + q);
   const float s_min = tanch[0].y, s_maxf = tanch[T - 1].x, s_maxl = tanch[T - 1].y;
 
-  // ---- forward: fold, scan, walk
-  float B = 0.f, s = s_maxl;
+  // ---- fold both directions
+  float B = 0.f, s = s_maxl, D = 0.f, sd = s_maxf;
   if (t0 < t1) {
     s = tanch[t1 - 1].y;
+    sd = tanch[t0].x;
 #pragma unroll 8
-    for (uint64_t t = t0; t < t1; ++t) B = fmaf(decay_r(tanch[t].y - s, tie), bf[t * M + c], B);
+    for (uint64_t t = t0; t < t1; ++t) {
+      const float2 an = tanch[t];
+      B = fmaf(decay_r(an.y - s, tie), bf[t * M + c], B);
+      D = fmaf(decay_r(sd - an.x, tie), bb[t * M + c], D);
+    }
   }
   sB[tid] = B;
   sS[tid] = s;
+  sD[tid] = D;
+  sT[tid] = sd;
   __syncthreads();
+  // ---- scan the run aggregates: wave 0 forward, wave 1 backward
   if (wid == 0) {
     float cB = 0.f, cS = s_min;
     for (int r = 0; r < rounds; ++r) {  // runs past the last hold nothing
@@ -239,8 +248,30 @@ __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restr
       cB = __shfl(inc, kWave - 1);
       cS = __shfl(s1, kWave - 1);
     }
+  } else if (wid == 1) {
+    float cB = 0.f, cS = s_maxf;
+    for (int r = rounds - 1; r >= 0; --r) {
+      const int i = r * kWave + lane;
+      float b1[1] = {sD[i]};
+      const float s1 = sT[i];
+      if (tie)
+        wave_scan_bwd<1, true>(b1, s1);
+      else
+        wave_scan_bwd<1, false>(b1, s1);
+      const float inc = fmaf(decay_r(s1 - cS, tie), cB, b1[0]);
+      float ex = __shfl_down(inc, 1), es = __shfl_down(s1, 1);
+      if (lane == kWave - 1) {
+        ex = cB;
+        es = cS;
+      }
+      sD[i] = ex;
+      sT[i] = es;
+      cB = __shfl(inc, 0);
+      cS = __shfl(s1, 0);
+    }
   }
   __syncthreads();
+  // ---- walk: forward carries upward, backward carries downward
   if (t0 < t1) {
     float C = sB[tid], sc = sS[tid];
     for (uint64_t tb = t0; tb < t1; tb += kCarryBatch) {
@@ -260,45 +291,8 @@ __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restr
         }
       }
     }
-  }
-  __syncthreads();
-
-  // ---- backward
-  B = 0.f;
-  s = s_maxf;
-  if (t0 < t1) {
-    s = tanch[t0].x;
-#pragma unroll 8
-    for (uint64_t t = t0; t < t1; ++t) B = fmaf(decay_r(s - tanch[t].x, tie), bb[t * M + c], B);
-  }
-  sB[tid] = B;
-  sS[tid] = s;
-  __syncthreads();
-  if (wid == 0) {
-    float cB = 0.f, cS = s_maxf;
-    for (int r = rounds - 1; r >= 0; --r) {
-      const int i = r * kWave + lane;
-      float b1[1] = {sB[i]};
-      const float s1 = sS[i];
-      if (tie)
-        wave_scan_bwd<1, true>(b1, s1);
-      else
-        wave_scan_bwd<1, false>(b1, s1);
-      const float inc = fmaf(decay_r(s1 - cS, tie), cB, b1[0]);
-      float ex = __shfl_down(inc, 1), es = __shfl_down(s1, 1);
-      if (lane == kWave - 1) {
-        ex = cB;
-        es = cS;
-      }
-      sB[i] = ex;
-      sS[i] = es;
-      cB = __shfl(inc, 0);
-      cS = __shfl(s1, 0);
-    }
-  }
-  __syncthreads();
-  if (t0 < t1) {
-    float C = sB[tid], sc = sS[tid];
+    C = sD[tid];
+    sc = sT[tid];
     for (uint64_t te = t1; te > t0;) {
       const uint64_t tb = te > t0 + kCarryBatch ? te - kCarryBatch : t0;
       float sf[kCarryBatch], bv[kCarryBatch];

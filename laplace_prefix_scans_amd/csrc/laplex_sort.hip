@@ -147,75 +147,81 @@ __global__ __launch_bounds__(kHistBlock) void k_sort_hist(const uint32_t* __rest
   if (__ballot(bad) != 0ull && lane_id() == 0) atomicOr(&header[kHdrFlags], kFlagNonFinite);
 }
 
-// Exclusive prefix of each digit histogram -> global start of each bucket.
-// One block of 256 threads; thread d handles digit value d of every pass.
-// Exclusive digit offsets of every pass, and per pass whether its tiles
-// publish their digit counts before ranking: only when no digit value holds
-// more than 1/16 of the keys, since the early count takes LDS atomic adds that
-// serialise when many lanes share a digit (the ranking itself does not).
-__global__ __launch_bounds__(256) void k_sort_offsets(const uint32_t* __restrict__ hist, uint32_t* __restrict__ offs,
-                                                      uint32_t* __restrict__ header) {
-  __shared__ uint32_t wsum[4], wmax[4];
-  const int d = threadIdx.x, lane = lane_id(), w = d / kWave;
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t v = hist[p * 256 + d];
-    uint32_t x = v, mx = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const uint32_t t = __shfl_up(x, off);
-      if (lane >= off) x += t;
-      mx = max(mx, (uint32_t)__shfl_xor(mx, off));
-    }
-    if (lane == kWave - 1) wsum[w] = x;
-    if (lane == 0) wmax[w] = mx;
-    __syncthreads();
-    uint32_t pre = 0, total = 0, top = 0;
-    for (int i = 0; i < 4; ++i) {
-      if (i < w) pre += wsum[i];
-      total += wsum[i];
-      top = max(top, wmax[i]);
-    }
-    offs[p * 256 + d] = pre + x - v;
-    if (d == 0) header[kHdrEarly0 + p] = (top <= total / 16) ? 1u : 0u;
-    __syncthreads();
-  }
-}
 
-// ------------------------------------------------------------------ first-pass offsets
-// In place: bsum[b][d] (digit d's count in histogram block b's range) becomes
-// its exclusive prefix over blocks.  One 1024-thread block: thread (q, d)
-// scans digit d over the q-th quarter of the rows.
+// ------------------------------------------------------------------ offsets
+// One 1024-thread block, after the histogram read:
+//  * exclusive digit offsets of every pass (threads 0..255, thread d owning
+//    digit value d), and per pass whether its tiles publish their digit
+//    counts before ranking: only when no digit value holds more than 1/16 of
+//    the keys, since the early count takes LDS atomic adds that serialise
+//    when many lanes share a digit (the ranking itself does not);
+//  * with `rows` > 0, the first pass's table: bsum[b][d] (digit d's count in
+//    histogram block b's range) becomes its exclusive prefix over blocks,
+//    thread (q, d) scanning digit d over the q-th quarter of the rows.
 constexpr int kScanThreads = 1024;
 constexpr int kScanQuarters = kScanThreads / 256;
 constexpr uint64_t kTableMinTiles = 64;
 
-__global__ __launch_bounds__(kScanThreads) void k_block_sum_scan(uint32_t* __restrict__ bsum, uint64_t rows) {
+__global__ __launch_bounds__(kScanThreads) void k_sort_offsets(const uint32_t* __restrict__ hist, uint32_t* __restrict__ offs,
+                                                               uint32_t* __restrict__ header, uint32_t* __restrict__ bsum,
+                                                               uint64_t rows) {
+  __shared__ uint32_t wsum[4], wmax[4];
   __shared__ uint32_t part[kScanQuarters][256];
-  const int q = threadIdx.x >> 8, d = threadIdx.x & 255;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int q = tid >> 8, d = tid & 255;
+  for (int p = 0; p < 4; ++p) {
+    uint32_t v = 0, x = 0;
+    if (tid < 256) {
+      v = hist[p * 256 + d];
+      x = v;
+      uint32_t mx = v;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t t = __shfl_up(x, off);
+        if (lane >= off) x += t;
+        mx = max(mx, (uint32_t)__shfl_xor(mx, off));
+      }
+      if (lane == kWave - 1) wsum[w] = x;
+      if (lane == 0) wmax[w] = mx;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t pre = 0, total = 0, top = 0;
+      for (int i = 0; i < 4; ++i) {
+        if (i < w) pre += wsum[i];
+        total += wsum[i];
+        top = max(top, wmax[i]);
+      }
+      offs[p * 256 + d] = pre + x - v;
+      if (d == 0) header[kHdrEarly0 + p] = (top <= total / 16) ? 1u : 0u;
+    }
+    __syncthreads();
+  }
+  if (rows == 0) return;
   const uint64_t seg = (rows + kScanQuarters - 1) / kScanQuarters;
   const uint64_t g0 = (uint64_t)q * seg < rows ? (uint64_t)q * seg : rows;
   const uint64_t g1 = g0 + seg < rows ? g0 + seg : rows;
   constexpr int B = 16;
-  uint32_t s = 0;
+  uint32_t sum = 0;
   for (uint64_t g = g0; g < g1; g += B) {
-    uint32_t v[B];
+    uint32_t vv[B];
 #pragma unroll
-    for (int j = 0; j < B; ++j) v[j] = (g + j < g1) ? bsum[(g + j) * 256 + d] : 0u;
+    for (int j = 0; j < B; ++j) vv[j] = (g + j < g1) ? bsum[(g + j) * 256 + d] : 0u;
 #pragma unroll
-    for (int j = 0; j < B; ++j) s += v[j];
+    for (int j = 0; j < B; ++j) sum += vv[j];
   }
-  part[q][d] = s;
+  part[q][d] = sum;
   __syncthreads();
   uint32_t run = 0;
   for (int i = 0; i < q; ++i) run += part[i][d];
   for (uint64_t g = g0; g < g1; g += B) {
-    uint32_t v[B];
+    uint32_t vv[B];
 #pragma unroll
-    for (int j = 0; j < B; ++j) v[j] = (g + j < g1) ? bsum[(g + j) * 256 + d] : 0u;
+    for (int j = 0; j < B; ++j) vv[j] = (g + j < g1) ? bsum[(g + j) * 256 + d] : 0u;
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       if (g + j < g1) bsum[(g + j) * 256 + d] = run;
-      run += v[j];
+      run += vv[j];
     }
   }
 }
@@ -574,14 +580,11 @@ static hipError_t sort_impl(const SortWorkspace& w, const float* a, uint64_t n, 
                 k_sort_hist<<<(unsigned)hist_blocks, kHistBlock, 0, s>>>(reinterpret_cast<const uint32_t*>(a), n, w.hist,
                                                                          w.header, w.tcount, w.gsum, cpb));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  LAPLEX_LAUNCH("k_sort_offsets", 1024, s, k_sort_offsets<<<1, 256, 0, s>>>(w.hist, w.offsets, w.header));
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  // small sorts keep the first pass's look-back (one launch fewer)
+  // small sorts keep the first pass's look-back
   const bool table = sort_tiles(n) >= kTableMinTiles;
-  if (table) {
-    LAPLEX_LAUNCH("k_block_sum_scan", hist_blocks, s, k_block_sum_scan<<<1, kScanThreads, 0, s>>>(w.gsum, hist_blocks));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  LAPLEX_LAUNCH("k_sort_offsets", 1024, s,
+                k_sort_offsets<<<1, kScanThreads, 0, s>>>(w.hist, w.offsets, w.header, w.gsum, table ? hist_blocks : 0));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (n <= (1ull << 30)) return launch_sort_passes<uint32_t>(w, a, n, a_sorted, perm, route, pay, table, cpb, s);
   return launch_sort_passes<uint64_t>(w, a, n, a_sorted, perm, route, pay, table, cpb, s);
 }
