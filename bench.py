@@ -62,15 +62,14 @@ def kernel_bytes(name: str, units: int, m: int, k: int = 0) -> float:
         "k_onesweep_last_pay": 16.0,             # read key + x; write sorted anchors and sorted x
         "k_onesweep_first_pay_routed": 16.0 + route,
         "k_onesweep_last_pay_routed": 16.0 + route,
-        "k_sym_gather_reduce": 8.0 + 8.0 * m,    # perm, sorted anchors, x rows in (random), sorted rows out
         "k_sym_apply": 8.0 + 8.0 * m,            # sorted anchors, perm, sorted rows in, y rows out (random)
         "k_sym_reduce": 4.0 + 4.0 * m,           # sorted anchors, sorted rows
         "k_sym_apply_sorted": 4.0 + 8.0 * m,     # sorted anchors, sorted rows in, sorted rows out
-        "k_phased_gather_reduce": 16.0 + 8.0 * m,
         "k_phased_apply": 12.0 + 8.0 * m,
         "k_phased_reduce": 8.0 + 4.0 * m,
         "k_phased_apply_sorted": 8.0 + 8.0 * m,
-        "k_gather_rows": 4.0 + 8.0 * m,
+        "k_gather_rows": 4.0 + 8.0 * m,          # perm, rows in (random), sorted rows out
+        "k_gather_rows_ph": 12.0 + 8.0 * m,      # the same plus the phases
         "k_gen_reduce": 4.0 + 4.0 * m,
         "k_phased_gen_reduce": 8.0 + 4.0 * m,
         "k_bwd_reduce": 4.0 + 8.0 * m,           # sorted anchors, sorted x and g rows
@@ -122,9 +121,8 @@ def rocprof_label(name: str, pass_index: int = 0, routed: bool = True) -> str:
         return label + ("_pay" if pay else "") + ("_routed" if routed else "")
     if kern in ("k_route_fwd", "k_route_inv", "k_route_inv_chunked"):
         return "%s_w%s" % (kern.replace("_chunked", ""), targs[0])
-    if kern == "k_sym_gather_reduce":
-        ph, gather = targs[1] == "true", targs[2] == "true"
-        return ("k_phased" if ph else "k_sym") + ("_gather_reduce" if gather else "_reduce")
+    if kern == "k_sym_reduce":
+        return "k_phased_reduce" if targs[1] == "true" else "k_sym_reduce"
     if kern == "k_sym_apply":
         ph, scatter = targs[1] == "true", targs[2] == "true"
         return ("k_phased_apply" if ph else "k_sym_apply") + ("" if scatter else "_sorted")

@@ -550,14 +550,12 @@ __device__ __forceinline__ void store_rows(float* __restrict__ y, uint64_t p0, u
       for (int j = 0; j < C; ++j) y[(p0 + e) * m + cc * C + j] = yv[e][j];
 }
 
-// GATHER: inputs in original order, gathered through perm and stored to xs
-// (and phs); otherwise xs (and phs) already hold them in sorted order.
-// vec: a_s is 16-byte aligned (workspace buffers always are).
-template <int C, bool PH, bool GATHER>
-__global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_sym_gather_reduce(
-    const float* __restrict__ a_s, const uint32_t* __restrict__ perm, const float* __restrict__ phi, const float* __restrict__ x,
-    uint64_t n, uint32_t m, float* __restrict__ xs, float* __restrict__ phs, float* __restrict__ bf, float* __restrict__ bb,
-    float2* __restrict__ tanch, bool vec) {
+// Tile aggregates of the inputs in sorted order (xs, and phs for the phased
+// operator).  vec: a_s is 16-byte aligned (workspace buffers always are).
+template <int C, bool PH>
+__global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_sym_reduce(
+    const float* __restrict__ a_s, uint64_t n, uint32_t m, const float* __restrict__ xs, const float* __restrict__ phs,
+    float* __restrict__ bf, float* __restrict__ bb, float2* __restrict__ tanch, bool vec) {
   constexpr int CC = PH ? 2 * C : C;
   constexpr int E = apply_items(CC);
   constexpr int BLOCK = apply_block(CC);
@@ -573,14 +571,10 @@ __global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_sym_gather_redu
   if (tid == 0) tanch[tile] = make_float2(s_first, s_last);
   const uint64_t p0 = lo + (uint64_t)tid * E;
   float ae[E], wf[E], wb[E], cs[E], sn[E];
-  uint32_t src[E];
   load_anchors<E>(a_s, p0, n, s_last, vec, ae);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const uint64_t p = p0 + e;
-    const bool valid = p < n;
-    src[e] = (GATHER && valid) ? perm[p] : 0u;
-    if ((uint64_t)src[e] >= n) src[e] = 0;  // a handle from the sort is always in range
+    const bool valid = p0 + e < n;
     wf[e] = valid ? decay(ae[e] - s_last) : 0.f;
     wb[e] = valid ? decay(s_first - ae[e]) : 0.f;
     cs[e] = 1.f;
@@ -588,29 +582,13 @@ __global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_sym_gather_redu
   }
   if (PH) {
     float ph[E];
-    if (GATHER) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        ph[e] = (p0 + e < n) ? phi[src[e]] : 0.f;
-        if (p0 + e < n) phs[p0 + e] = ph[e];
-      }
-    } else {
-      load_anchors<E>(phs, p0, n, 0.f, true, ph);
-    }
+    load_anchors<E>(phs, p0, n, 0.f, true, ph);
 #pragma unroll
     for (int e = 0; e < E; ++e) sincosf(ph[e], &sn[e], &cs[e]);
   }
   for (uint32_t cc = 0; cc < m / C; ++cc) {
     float xv[E][C];
-    if (GATHER) {
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-#pragma unroll
-        for (int j = 0; j < C; ++j) xv[e][j] = (p0 + e < n) ? x[(uint64_t)src[e] * m + cc * C + j] : 0.f;
-      store_rows<E, C>(xs, p0, n, m, cc, true, xv);
-    } else {
-      load_rows<E, C>(xs, p0, n, m, cc, true, xv);
-    }
+    load_rows<E, C>(xs, p0, n, m, cc, true, xv);
     float sf[CC], sb[CC];
 #pragma unroll
     for (int j = 0; j < CC; ++j) sf[j] = sb[j] = 0.f;
@@ -809,6 +787,90 @@ __attribute__((amdgpu_waves_per_eu(!PH && C == 1 ? 8 : 1))) void k_sym_apply(
     sym_apply_tile<C, PH, SCATTER, false>(a_s, perm, xs, phs, cfw, cbw, tanch, n, m, T, y, vec, s_wf, s_wb, s_wfs, s_wbs);
 }
 
+// Rows of m floats moved by index: pieces of V floats (one vector access
+// each), consecutive threads taking consecutive pieces, so a row is read or
+// written whole by neighbouring lanes and the sorted-order side is one
+// contiguous stream.
+template <int V> struct RowPiece;
+template <> struct RowPiece<1> { using T = float; };
+template <> struct RowPiece<2> { using T = float2; };
+template <> struct RowPiece<4> { using T = float4; };
+
+// row and piece of flat piece index i (P pieces per row)
+__device__ __forceinline__ uint64_t piece_row(uint64_t i, uint32_t P, uint64_t items) {
+  return items < (1ull << 32) ? (uint64_t)((uint32_t)i / P) : i / P;
+}
+
+template <int V>
+__global__ void k_scatter_rows(const float* __restrict__ src, const uint32_t* __restrict__ perm, uint64_t rows, uint32_t m,
+                               float* __restrict__ dst) {
+  using T = typename RowPiece<V>::T;
+  const uint32_t P = m / V;
+  const uint64_t items = rows * P;
+  uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (; i < items; i += stride) {
+    const uint64_t r = piece_row(i, P, items);
+    const uint32_t c = (uint32_t)(i - r * P);
+    const uint32_t d = perm[r];
+    if ((uint64_t)d >= rows) continue;  // a handle from the sort is always in range
+    *reinterpret_cast<T*>(dst + (uint64_t)d * m + (uint64_t)c * V) = *reinterpret_cast<const T*>(src + r * m + (uint64_t)c * V);
+  }
+}
+template <int V>
+__global__ void k_gather_rows(const float* __restrict__ x, const uint32_t* __restrict__ perm, const float* __restrict__ ph,
+                              uint64_t rows, uint32_t m, float* __restrict__ xs, float* __restrict__ phs) {
+  using T = typename RowPiece<V>::T;
+  const uint32_t P = m / V;
+  const uint64_t items = rows * P;
+  uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (; i < items; i += stride) {
+    const uint64_t r = piece_row(i, P, items);
+    const uint32_t c = (uint32_t)(i - r * P);
+    uint32_t src = perm[r];
+    if ((uint64_t)src >= rows) src = 0;
+    *reinterpret_cast<T*>(xs + r * m + (uint64_t)c * V) = *reinterpret_cast<const T*>(x + (uint64_t)src * m + (uint64_t)c * V);
+    if (ph && c == 0) phs[r] = ph[src];
+  }
+}
+
+// piece width for rows of m floats between x and y (16- or 8-byte vectors
+// when m and both arrays allow)
+static int row_piece(uint32_t m, const void* x, const void* y) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y);
+  if (m % 4 == 0 && a % 16 == 0) return 4;
+  if (m % 2 == 0 && a % 8 == 0) return 2;
+  return 1;
+}
+static unsigned piece_grid(uint64_t rows, uint32_t m, int V) {
+  return (unsigned)std::min<uint64_t>((rows * (m / V) + 255) / 256, 16384);
+}
+// xs[r] = x[perm[r]] (and phs[r] = ph[perm[r]] when ph is given), rows of m floats
+static void gather_rows(const float* x, const uint32_t* perm, const float* ph, uint64_t rows, uint32_t m, float* xs, float* phs,
+                        hipStream_t s) {
+  const int V = row_piece(m, x, xs);
+  const unsigned g = piece_grid(rows, m, V);
+  const char* name = ph ? "k_gather_rows_ph" : "k_gather_rows";
+  if (V == 4)
+    LAPLEX_LAUNCH(name, rows, s, k_gather_rows<4><<<g, 256, 0, s>>>(x, perm, ph, rows, m, xs, phs));
+  else if (V == 2)
+    LAPLEX_LAUNCH(name, rows, s, k_gather_rows<2><<<g, 256, 0, s>>>(x, perm, ph, rows, m, xs, phs));
+  else
+    LAPLEX_LAUNCH(name, rows, s, k_gather_rows<1><<<g, 256, 0, s>>>(x, perm, ph, rows, m, xs, phs));
+}
+// dst[perm[r]] = src[r], rows of m floats
+static void scatter_rows(const float* src, const uint32_t* perm, uint64_t rows, uint32_t m, float* dst, hipStream_t s) {
+  const int V = row_piece(m, src, dst);
+  const unsigned g = piece_grid(rows, m, V);
+  if (V == 4)
+    LAPLEX_LAUNCH("k_scatter_rows", rows, s, k_scatter_rows<4><<<g, 256, 0, s>>>(src, perm, rows, m, dst));
+  else if (V == 2)
+    LAPLEX_LAUNCH("k_scatter_rows", rows, s, k_scatter_rows<2><<<g, 256, 0, s>>>(src, perm, rows, m, dst));
+  else
+    LAPLEX_LAUNCH("k_scatter_rows", rows, s, k_scatter_rows<1><<<g, 256, 0, s>>>(src, perm, rows, m, dst));
+}
+
 // x_sorted: w.xs already holds x in sorted order (routed, one column).
 template <int C, bool PH>
 static hipError_t run_sym(const ApplyWorkspace& w, const float* a_s, const uint32_t* perm, const SortRoute* route,
@@ -822,17 +884,16 @@ static hipError_t run_sym(const ApplyWorkspace& w, const float* a_s, const uint3
   const bool routed = route != nullptr && m <= kRouteMaxCols;
   const bool vec = (reinterpret_cast<uintptr_t>(a_s) & 15) == 0;
   hipError_t e;
+  // x (and phi) into sorted order: along the route, or as whole rows by index
   if (routed) {
     if (!x_sorted && (e = route_forward(*route, n, m, x, w.xs, w.t0, w.t1, s)) != hipSuccess) return e;
     if (PH && (e = route_forward(*route, n, 1, phi, w.phs, w.t0, w.t1, s)) != hipSuccess) return e;
-    LAPLEX_LAUNCH(PH ? "k_phased_reduce" : "k_sym_reduce", n, s,
-                  k_sym_gather_reduce<C, PH, false><<<grid, block, 0, s>>>(a_s, perm, phi, x, n, m, w.xs, w.phs, w.bf, w.bb,
-                                                                           w.tanch, vec));
   } else {
-    LAPLEX_LAUNCH(PH ? "k_phased_gather_reduce" : "k_sym_gather_reduce", n, s,
-                  k_sym_gather_reduce<C, PH, true><<<grid, block, 0, s>>>(a_s, perm, phi, x, n, m, w.xs, w.phs, w.bf, w.bb,
-                                                                          w.tanch, vec));
+    gather_rows(x, perm, PH ? phi : nullptr, n, m, w.xs, w.phs, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  LAPLEX_LAUNCH(PH ? "k_phased_reduce" : "k_sym_reduce", n, s,
+                k_sym_reduce<C, PH><<<grid, block, 0, s>>>(a_s, n, m, w.xs, w.phs, w.bf, w.bb, w.tanch, vec));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = tile_carries(w.bf, w.bb, w.tanch, T, M, w.cf, w.cb, w.gbf, w.gbb, w.gcf, w.gcb, w.ganch, s)) != hipSuccess) return e;
   if (routed) {
@@ -902,9 +963,6 @@ __device__ __forceinline__ void merge_tile_items(const float* s_a, const float* 
     ii += take_a ? 1u : 0u;
   }
 }
-
-__global__ void k_gather_rows(const float* __restrict__ x, const uint32_t* __restrict__ perm, const float* __restrict__ ph,
-                              uint64_t rows, uint32_t m, float* __restrict__ xs, float* __restrict__ phs);
 
 // ---------------------------------------------------------------- backward (symmetric)
 // With y = K x and an upstream gradient g = dL/dy (technical summary,
@@ -1106,17 +1164,6 @@ __global__ __launch_bounds__(bwd_block(C)) void k_bwd_apply(const float* __restr
 }
 
 // dst[perm[r]] = src[r] for rows of m floats (rows in sorted order -> original)
-__global__ void k_scatter_rows(const float* __restrict__ src, const uint32_t* __restrict__ perm, uint64_t rows, uint32_t m,
-                               float* __restrict__ dst) {
-  uint64_t r = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  for (; r < rows; r += stride) {
-    const uint32_t d = perm[r];
-    if ((uint64_t)d >= rows) continue;  // a handle from the sort is always in range
-    for (uint32_t c = 0; c < m; ++c) dst[(uint64_t)d * m + c] = src[r * m + c];
-  }
-}
-
 static unsigned rows_grid(uint64_t rows) { return (unsigned)std::min<uint64_t>((rows + 255) / 256, 8192); }
 
 template <int C>
@@ -1157,10 +1204,10 @@ static hipError_t run_bwd_sym(const BackwardWorkspace& bw, const float* a_s, con
     if ((e = route_forward(*route, n, m, g, bw.gs, w.t0, w.t1, s)) != hipSuccess) return e;
   } else {
     if (!xs_sorted) {
-      LAPLEX_LAUNCH("k_gather_rows", n, s, k_gather_rows<<<rows_grid(n), 256, 0, s>>>(x, perm, nullptr, n, m, w.xs, nullptr));
+      gather_rows(x, perm, nullptr, n, m, w.xs, nullptr, s);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    LAPLEX_LAUNCH("k_gather_rows", n, s, k_gather_rows<<<rows_grid(n), 256, 0, s>>>(g, perm, nullptr, n, m, bw.gs, nullptr));
+    gather_rows(g, perm, nullptr, n, m, bw.gs, nullptr, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   LAPLEX_LAUNCH("k_bwd_reduce", n, s,
@@ -1175,9 +1222,9 @@ static hipError_t run_bwd_sym(const BackwardWorkspace& bw, const float* a_s, con
     if ((e = route_inverse(*route, n, m, w.zs, dx, w.t0, w.t1, s)) != hipSuccess) return e;
     return route_inverse(*route, n, 1, bw.das, da, w.t0, w.t1, s);
   }
-  LAPLEX_LAUNCH("k_scatter_rows", n, s, k_scatter_rows<<<rows_grid(n), 256, 0, s>>>(w.zs, perm, n, m, dx));
+  scatter_rows(w.zs, perm, n, m, dx, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  LAPLEX_LAUNCH("k_scatter_rows", n, s, k_scatter_rows<<<rows_grid(n), 256, 0, s>>>(bw.das, perm, n, 1, da));
+  scatter_rows(bw.das, perm, n, 1, da, s);
   return hipGetLastError();
 }
 
@@ -1398,9 +1445,9 @@ static hipError_t run_pbwd_sym(const BackwardWorkspace& bw, const float* a_s, co
     if ((e = route_forward(*route, n, m, g, bw.gs, w.t0, w.t1, s)) != hipSuccess) return e;
     if ((e = route_forward(*route, n, 1, phi, w.phs, w.t0, w.t1, s)) != hipSuccess) return e;
   } else {
-    LAPLEX_LAUNCH("k_gather_rows", n, s, k_gather_rows<<<rows_grid(n), 256, 0, s>>>(x, perm, phi, n, m, w.xs, w.phs));
+    gather_rows(x, perm, phi, n, m, w.xs, w.phs, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    LAPLEX_LAUNCH("k_gather_rows", n, s, k_gather_rows<<<rows_grid(n), 256, 0, s>>>(g, perm, nullptr, n, m, bw.gs, nullptr));
+    gather_rows(g, perm, nullptr, n, m, bw.gs, nullptr, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   LAPLEX_LAUNCH("k_pbwd_reduce", n, s,
@@ -1417,11 +1464,11 @@ static hipError_t run_pbwd_sym(const BackwardWorkspace& bw, const float* a_s, co
     if ((e = route_inverse(*route, n, 1, bw.das, da, w.t0, w.t1, s)) != hipSuccess) return e;
     return route_inverse(*route, n, 1, bw.dphs, dphi, w.t0, w.t1, s);
   }
-  LAPLEX_LAUNCH("k_scatter_rows", n, s, k_scatter_rows<<<rows_grid(n), 256, 0, s>>>(w.zs, perm, n, m, dx));
+  scatter_rows(w.zs, perm, n, m, dx, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  LAPLEX_LAUNCH("k_scatter_rows", n, s, k_scatter_rows<<<rows_grid(n), 256, 0, s>>>(bw.das, perm, n, 1, da));
+  scatter_rows(bw.das, perm, n, 1, da, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  LAPLEX_LAUNCH("k_scatter_rows", n, s, k_scatter_rows<<<rows_grid(n), 256, 0, s>>>(bw.dphs, perm, n, 1, dphi));
+  scatter_rows(bw.dphs, perm, n, 1, dphi, s);
   return hipGetLastError();
 }
 
@@ -1447,18 +1494,6 @@ __device__ __forceinline__ uint64_t merge_split(const float* a, uint64_t n, cons
       hi = mid;
   }
   return lo;
-}
-
-__global__ void k_gather_rows(const float* __restrict__ x, const uint32_t* __restrict__ perm, const float* __restrict__ ph,
-                              uint64_t rows, uint32_t m, float* __restrict__ xs, float* __restrict__ phs) {
-  uint64_t r = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  for (; r < rows; r += stride) {
-    uint32_t src = perm[r];
-    if ((uint64_t)src >= rows) src = 0;
-    for (uint32_t c = 0; c < m; ++c) xs[r * m + c] = x[(uint64_t)src * m + c];
-    if (ph) phs[r] = ph[src];
-  }
 }
 
 template <int C, bool PH>
@@ -1640,9 +1675,7 @@ static hipError_t run_general(const ApplyWorkspace& w, const float* a_s, const u
     if ((e = route_forward(*route_b, k, m, x, w.xs, w.t0, w.t1, s)) != hipSuccess) return e;
     if (PH && (e = route_forward(*route_b, k, 1, psi, w.phs, w.t0, w.t1, s)) != hipSuccess) return e;
   } else {
-    const unsigned gblocks = (unsigned)std::min<uint64_t>((k + 255) / 256, 8192);
-    LAPLEX_LAUNCH("k_gather_rows", k, s,
-                  k_gather_rows<<<gblocks, 256, 0, s>>>(x, perm_b, PH ? psi : nullptr, k, m, w.xs, w.phs));
+    gather_rows(x, perm_b, PH ? psi : nullptr, k, m, w.xs, w.phs, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   LAPLEX_LAUNCH(PH ? "k_phased_gen_reduce" : "k_gen_reduce", k, s,
@@ -1903,13 +1936,13 @@ static hipError_t run_bwd_general(const BackwardWorkspace& bw, const float* a_s,
   if (routed_b) {
     if ((e = route_forward(*route_b, k, m, x, w.xs, w.t0, w.t1, s)) != hipSuccess) return e;
   } else {
-    LAPLEX_LAUNCH("k_gather_rows", k, s, k_gather_rows<<<rows_grid(k), 256, 0, s>>>(x, perm_b, nullptr, k, m, w.xs, nullptr));
+    gather_rows(x, perm_b, nullptr, k, m, w.xs, nullptr, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (routed_a) {
     if ((e = route_forward(*route_a, n, m, g, bw.gs, w.t0, w.t1, s)) != hipSuccess) return e;
   } else {
-    LAPLEX_LAUNCH("k_gather_rows", n, s, k_gather_rows<<<rows_grid(n), 256, 0, s>>>(g, perm_a, nullptr, n, m, bw.gs, nullptr));
+    gather_rows(g, perm_a, nullptr, n, m, bw.gs, nullptr, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   LAPLEX_LAUNCH("k_gbwd_reduce", n + k, s,
@@ -1926,13 +1959,13 @@ static hipError_t run_bwd_general(const BackwardWorkspace& bw, const float* a_s,
     if ((e = route_inverse(*route_b, k, m, w.zs, dx, w.t0, w.t1, s)) != hipSuccess) return e;
     if ((e = route_inverse(*route_b, k, 1, bw.dbs, db, w.t0, w.t1, s)) != hipSuccess) return e;
   } else {
-    LAPLEX_LAUNCH("k_scatter_rows", k, s, k_scatter_rows<<<rows_grid(k), 256, 0, s>>>(w.zs, perm_b, k, m, dx));
+    scatter_rows(w.zs, perm_b, k, m, dx, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    LAPLEX_LAUNCH("k_scatter_rows", k, s, k_scatter_rows<<<rows_grid(k), 256, 0, s>>>(bw.dbs, perm_b, k, 1, db));
+    scatter_rows(bw.dbs, perm_b, k, 1, db, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (routed_a) return route_inverse(*route_a, n, 1, bw.das, da, w.t0, w.t1, s);
-  LAPLEX_LAUNCH("k_scatter_rows", n, s, k_scatter_rows<<<rows_grid(n), 256, 0, s>>>(bw.das, perm_a, n, 1, da));
+  scatter_rows(bw.das, perm_a, n, 1, da, s);
   return hipGetLastError();
 }
 
@@ -2140,7 +2173,7 @@ hipError_t gram_weighted(const GramWorkspace& g, const float* a_s, const uint32_
   constexpr int P = apply_tile(1);
   const uint64_t T = (n + k + P - 1) / P;
   const dim3 grid((unsigned)T), block(apply_block(1));
-  LAPLEX_LAUNCH("k_gather_rows", k, s, k_gather_rows<<<rows_grid(k), 256, 0, s>>>(D, perm_b, nullptr, k, 1, g.Ds, nullptr));
+  gather_rows(D, perm_b, nullptr, k, 1, g.Ds, nullptr, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   LAPLEX_LAUNCH("k_gram_dprefix", k, s, k_gram_dprefix<<<1, 1024, 0, s>>>(g.Ds, k, g.Cpre));
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -2384,14 +2417,14 @@ hipError_t backward_phased_general(const BackwardWorkspace& bw, const float* a_s
     if ((e = route_forward(*route_b, k, m, x, w.xs, w.t0, w.t1, s)) != hipSuccess) return e;
     if ((e = route_forward(*route_b, k, 1, psi, w.phs, w.t0, w.t1, s)) != hipSuccess) return e;
   } else {
-    LAPLEX_LAUNCH("k_gather_rows", k, s, k_gather_rows<<<rows_grid(k), 256, 0, s>>>(x, perm_b, psi, k, m, w.xs, w.phs));
+    gather_rows(x, perm_b, psi, k, m, w.xs, w.phs, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (routed_a) {
     if ((e = route_forward(*route_a, n, m, g, bw.gs, w.t0, w.t1, s)) != hipSuccess) return e;
     if ((e = route_forward(*route_a, n, 1, phi, w.phas, w.t0, w.t1, s)) != hipSuccess) return e;
   } else {
-    LAPLEX_LAUNCH("k_gather_rows", n, s, k_gather_rows<<<rows_grid(n), 256, 0, s>>>(g, perm_a, phi, n, m, bw.gs, w.phas));
+    gather_rows(g, perm_a, phi, n, m, bw.gs, w.phas, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   LAPLEX_LAUNCH("k_gpbwd_reduce", n + k, s,
@@ -2413,7 +2446,7 @@ hipError_t backward_phased_general(const BackwardWorkspace& bw, const float* a_s
     const float* src[3] = {w.zs, bw.dbs, bw.dpsis};
     float* dst[3] = {dx, db, dpsi};
     for (int i = 0; i < 3; ++i) {
-      LAPLEX_LAUNCH("k_scatter_rows", k, s, k_scatter_rows<<<rows_grid(k), 256, 0, s>>>(src[i], perm_b, k, i == 0 ? m : 1, dst[i]));
+      scatter_rows(src[i], perm_b, k, i == 0 ? m : 1, dst[i], s);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
@@ -2421,9 +2454,9 @@ hipError_t backward_phased_general(const BackwardWorkspace& bw, const float* a_s
     if ((e = route_inverse(*route_a, n, 1, bw.das, da, w.t0, w.t1, s)) != hipSuccess) return e;
     return route_inverse(*route_a, n, 1, bw.dphs, dphi, w.t0, w.t1, s);
   }
-  LAPLEX_LAUNCH("k_scatter_rows", n, s, k_scatter_rows<<<rows_grid(n), 256, 0, s>>>(bw.das, perm_a, n, 1, da));
+  scatter_rows(bw.das, perm_a, n, 1, da, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  LAPLEX_LAUNCH("k_scatter_rows", n, s, k_scatter_rows<<<rows_grid(n), 256, 0, s>>>(bw.dphs, perm_a, n, 1, dphi));
+  scatter_rows(bw.dphs, perm_a, n, 1, dphi, s);
   return hipGetLastError();
 }
 
