@@ -65,6 +65,7 @@ def kernel_bytes(name: str, units: int, m: int, k: int = 0) -> float:
         "k_sym_apply": 8.0 + 8.0 * m,            # sorted anchors, perm, sorted rows in, y rows out (random)
         "k_sym_reduce": 4.0 + 4.0 * m,           # sorted anchors, sorted rows
         "k_sym_apply_sorted": 4.0 + 8.0 * m,     # sorted anchors, sorted rows in, sorted rows out
+        "k_sym_fu": 4.0 + 12.0 * m,              # sorted anchors and rows in; both scans out
         "k_phased_apply": 12.0 + 8.0 * m,
         "k_phased_reduce": 8.0 + 4.0 * m,
         "k_phased_apply_sorted": 8.0 + 8.0 * m,
@@ -90,6 +91,8 @@ def kernel_bytes(name: str, units: int, m: int, k: int = 0) -> float:
         return table[name] * units
     if name == "k_gbwd_apply":  # merged anchors, x and g rows in; da (n), db and dx rows (k) out
         return (8.0 + 4.0 * m) * units + 4.0 * m * k
+    if name == "k_gen_search":  # outputs' anchors in, y rows out; sorted b and both scans read once
+        return (4.0 + 4.0 * m) * units + (4.0 + 8.0 * m) * k
     if name in ("k_gen_apply", "k_phased_gen_apply"):
         return (8.0 + 4.0 * m) * units + (4.0 + 4.0 * m) * k
     if name in ("k_gen_apply_sorted", "k_phased_gen_apply_sorted"):
@@ -315,8 +318,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-route", action="store_true", help="move x and y by index instead of along the sort route")
     ap.add_argument("--two-call", action="store_true",
-                    help="symmetric m = 1: time laplex_sort_anchors + laplex_matvec_sym instead of the one-call "
-                         "laplex_sort_matvec_sym (which carries x through the sort)")
+                    help="time the sort handles + laplex_matvec_sym / laplex_matvec_general instead of the one-call "
+                         "laplex_sort_matvec_sym (symmetric, m = 1: x carried through the sort) or "
+                         "laplex_sort_matvec_general (general: only b sorted, outputs search their interval)")
     ap.add_argument("--cpu-sample-log2", type=int, default=25)
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward (symmetric, general, phased)")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing (steps after a 512 MiB scrub)")
@@ -356,6 +360,8 @@ def main():
     # symmetric, one column, routed: the sort and the apply in one call, x
     # carried through the sort's passes as the keys' values
     one_call = w.kind == "sym" and m == 1 and use_route and not args.two_call
+    # general: only b sorted, the scans over b, each output searching its interval
+    one_call_gen = w.kind == "general" and not args.two_call
     a = torch.from_numpy(w.a).to(dev)
     x = torch.from_numpy(w.x).to(dev)
     # the sort handle of a (the one-call path keeps its own in its workspace)
@@ -380,7 +386,7 @@ def main():
         pb = torch.empty(k, dtype=torch.uint32, device=dev)
         rb = lp.route_buffer(k, device=dev) if use_route else None
         ws_sort_b = lp.workspace(lp.LAPLEX_OP_SORT, k, device=dev)
-        ws_apply = lp.workspace(lp.LAPLEX_OP_GENERAL, n, k, m, device=dev)
+        ws_apply = lp.workspace(lp.LAPLEX_OP_SORT_GENERAL if one_call_gen else lp.LAPLEX_OP_GENERAL, n, k, m, device=dev)
     elif w.kind == "phased":
         phi = torch.from_numpy(w.phi).to(dev)
         ws_apply = lp.workspace(lp.LAPLEX_OP_PHASED, n, 0, m, device=dev)
@@ -393,6 +399,9 @@ def main():
     def step():
         if one_call:
             lp.laplex_sort_matvec_sym(a, x, y=y, ws=ws_apply)
+            return
+        if one_call_gen:
+            lp.laplex_sort_matvec_general(a, b, x, y=y, ws=ws_apply)
             return
         lp.laplex_sort_anchors(a, a_s, pa, route=ra, ws=ws_sort_a)
         if w.kind == "gram":
@@ -409,7 +418,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    if lp.laplex_status_poll(ws_apply if one_call else ws_sort_a) != 0:
+    if lp.laplex_status_poll(ws_apply if one_call or one_call_gen else ws_sort_a) != 0:
         raise RuntimeError("sort reported a device-side error")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with lp.profile_launches(capacity=64 * max(1, args.steps)) as prof:
@@ -532,7 +541,9 @@ def main():
         "config": {"workload": args.workload, "kind": w.kind, "n": n, "m": m,
                    "k": k if w.kind in ("general", "gram") else None,
                    "step": "sort a and b + all n^2 entries of M" if w.kind == "gram" else
-                   "sort + apply in one call (x carried through the sort)" if one_call else "sort + apply",
+                   "sort + apply in one call (x carried through the sort)" if one_call else
+                   "sort of b + apply in one call (scans over b, each output searches its interval)" if one_call_gen
+                   else "sort + apply",
                    "route": use_route and w.kind != "gram", "recipe": w.recipe},
         "roofline": roofline,
         "step_alg_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
@@ -545,6 +556,9 @@ def main():
         "host_gen_s": round(t_gen, 1),
     }
     if w.kind in ("sym", "general", "phased") and not args.no_backward:
+        if one_call_gen:  # the backward takes sort handles of a and b: build them (untimed)
+            lp.laplex_sort_anchors(a, a_s, pa, route=ra, ws=ws_sort_a)
+            lp.laplex_sort_anchors(b, b_s, pb, route=rb, ws=ws_sort_b)
         gen = torch.Generator(device=dev).manual_seed(0x6AAD)
         g = torch.randn((n,) if x.dim() == 1 else (n, m), generator=gen, device=dev)
         da = torch.empty(n, dtype=torch.float32, device=dev)

@@ -65,7 +65,8 @@ enum {
   LAPLEX_OP_GRAM = 7,             /* weighted Gram matrix */
   LAPLEX_OP_PHASED_BACKWARD = 8,  /* backward of the symmetric phased operator */
   LAPLEX_OP_PHASED_GENERAL_BACKWARD = 9, /* backward of the phased operator with a != b */
-  LAPLEX_OP_SORT_SYM = 10                /* sort and symmetric operator in one call */
+  LAPLEX_OP_SORT_SYM = 10,               /* sort and symmetric operator in one call */
+  LAPLEX_OP_SORT_GENERAL = 11            /* sort of b and general operator in one call */
 };
 
 /* Bytes of workspace one call of `op` needs for n output anchors, k input
@@ -120,6 +121,24 @@ laplex_status laplex_matvec_sym(const float* a_sorted, const uint32_t* perm, con
  * laplex_status_poll(ws) reports non-finite anchors and stalls as for a sort. */
 laplex_status laplex_sort_matvec_sym(const float* a, uint64_t n, uint32_t m, const float* x, float* y, void* ws, size_t ws_bytes,
                                      hipStream_t stream);
+
+/* The general operator y = LAPLEX(a, b) x from unsorted anchors in one call
+ * (section 2.2, general case), for few input anchors: only b is sorted.  The
+ * two scans run over sorted b, Fi_j = sum_{j' <= j} exp(-(b_j - b_j')) x_j'
+ * and U_j = sum_{j' >= j} exp(-(b_j' - b_j)) x_j', and each output anchor a_i
+ * finds p = #{b_j <= a_i} by binary search (b before a on ties, as in
+ * laplex_matvec_general) and takes y_i = exp(-(a_i - b_{p-1})) Fi_{p-1} +
+ * exp(-(b_p - a_i)) U_p.  The same sum split at the same place as the merged
+ * scan, with no sort of a: O(k log k + n log k).  Best while b and the two
+ * scans fit in the caches (k up to about 2^18 at m = 1); otherwise sort both
+ * and use laplex_matvec_general.  The result equals laplex_matvec_general's
+ * within rounding (not bitwise).
+ * a: n floats; b: k floats; x: k x m (original order of b); y: n x m (output,
+ * original order of a; must not overlap a, b, x or ws); k == 0 gives y = 0;
+ * ws: laplex_workspace_bytes(LAPLEX_OP_SORT_GENERAL, n, k, m) bytes (it holds
+ * b's sort workspace: laplex_status_poll(ws) reports non-finite a or b). */
+laplex_status laplex_sort_matvec_general(const float* a, uint64_t n, const float* b, uint64_t k, uint32_t m, const float* x,
+                                         float* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Backward of laplex_sort_matvec_sym from what that call left in its
  * workspace (the sorted anchors, the route or permutation, and x in sorted

@@ -10,6 +10,7 @@ not been built the calls raise -- there is no fallback.
     y = laplex_sort_matvec_sym(a, x, ws=ws)          # the same from unsorted anchors, in one call
     dx, da = laplex_sort_matvec_sym_backward(ws, g)  # its backward, from what the call left in ws
     y = laplex_matvec_general(a_sorted, perm, b_sorted, perm_b, xb)
+    y = laplex_sort_matvec_general(a, b, xb)         # the same, sorting only b (few inputs b)
     y = laplex_matvec_phased(a_sorted, perm, phi, x)  # extra cos(phi_i - phi_j)
     dx, da = laplex_backward_sym(a_sorted, perm, x, g)  # gradients for g = dL/dy
     dxb, da, db = laplex_backward_general(a_sorted, perm, b_sorted, perm_b, xb, g)
@@ -26,6 +27,7 @@ from ._binding import (  # noqa: F401
     LAPLEX_OP_PHASED_GENERAL,
     LAPLEX_OP_SORT,
     LAPLEX_OP_SORT_SYM,
+    LAPLEX_OP_SORT_GENERAL,
     LAPLEX_OP_SYM,
     LAPLEX_OP_SYM_BACKWARD,
     LaplexError,
@@ -39,6 +41,7 @@ from ._binding import (  # noqa: F401
     laplex_matvec_general,
     laplex_matvec_phased,
     laplex_matvec_sym,
+    laplex_sort_matvec_general,
     laplex_sort_matvec_sym,
     laplex_sort_matvec_sym_backward,
     laplex_sort_anchors,

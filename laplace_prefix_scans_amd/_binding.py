@@ -18,6 +18,7 @@ LAPLEX_OP_GRAM = 7
 LAPLEX_OP_PHASED_BACKWARD = 8
 LAPLEX_OP_PHASED_GENERAL_BACKWARD = 9
 LAPLEX_OP_SORT_SYM = 10
+LAPLEX_OP_SORT_GENERAL = 11
 
 _STATUS = {
     0: "LAPLEX_OK", 1: "LAPLEX_ERR_NULL", 2: "LAPLEX_ERR_SIZE", 3: "LAPLEX_ERR_ALIGN", 4: "LAPLEX_ERR_WORKSPACE",
@@ -59,6 +60,8 @@ def lib():
         L.laplex_sort_matvec_sym.argtypes = [vp, u64, u32, vp, vp, vp, sz, vp]
         L.laplex_sort_matvec_sym.restype = i32
         L.laplex_sort_matvec_sym_backward.argtypes = [vp, sz, u64, u32, vp, vp, vp, vp, sz, vp]
+        L.laplex_sort_matvec_general.argtypes = [vp, u64, vp, u64, u32, vp, vp, vp, sz, vp]
+        L.laplex_sort_matvec_general.restype = i32
         L.laplex_sort_matvec_sym_backward.restype = i32
         L.laplex_matvec_general.argtypes = [vp, vp, vp, u64, vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
         L.laplex_matvec_phased.argtypes = [vp, vp, vp, vp, u64, vp, vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
@@ -216,6 +219,30 @@ def laplex_sort_matvec_sym(a: torch.Tensor, x: torch.Tensor, y: Optional[torch.T
            "laplex_sort_matvec_sym")
     if check:
         _check(L.laplex_status_poll(_ptr(ws), _stream(dev)), "laplex_sort_matvec_sym")
+    return y
+
+
+def laplex_sort_matvec_general(a: torch.Tensor, b: torch.Tensor, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                               ws: Optional[torch.Tensor] = None, check: bool = False) -> torch.Tensor:
+    """y = LAPLEX(a, b) x from unsorted anchors in one call, sorting only b (for few input anchors b);
+    x is (k,) or (k, m), y (n,) or (n, m).  ``check=True`` waits and raises LaplexError if an anchor
+    was NaN/Inf."""
+    _vec(a, "a")
+    _vec(b, "b")
+    if a.dim() != 1 or b.dim() != 1:
+        raise ValueError("a and b must be 1-D")
+    n, k, dev = a.shape[0], b.shape[0], a.device
+    m = _cols(x, k)
+    if y is None:
+        y = torch.empty((n,) if x.dim() == 1 else (n, m), dtype=torch.float32, device=dev)
+    if _cols(y, n, "y") != m:
+        raise ValueError("y must have m = %d columns" % m)
+    ws = _ws(ws, LAPLEX_OP_SORT_GENERAL, n, k, m, dev)
+    L = lib()
+    _check(L.laplex_sort_matvec_general(_ptr(a), n, _ptr(b), k, m, _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(dev)),
+           "laplex_sort_matvec_general")
+    if check:
+        _check(L.laplex_status_poll(_ptr(ws), _stream(dev)), "laplex_sort_matvec_general")
     return y
 
 

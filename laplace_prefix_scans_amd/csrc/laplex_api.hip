@@ -188,6 +188,36 @@ SortSymWorkspace carve_sort_sym(void* ws, uint64_t n, uint32_t m, size_t* total)
   return w;
 }
 
+// Sort of b and the general operator with the scans over b, in one call: the
+// sort workspace of b first (so that laplex_status_poll finds its flags at
+// the start), b's sort handle, the apply workspace over b, and Fi, U.
+struct SortGeneralWorkspace {
+  SortWorkspace sort;
+  float* b_s;
+  uint32_t* perm_b;
+  ApplyWorkspace apply;
+  float* fo;
+  float* uo;
+  float2* fu;
+};
+SortGeneralWorkspace carve_sort_general(void* ws, uint64_t k, uint32_t m, size_t* total) {
+  Carver c(ws);
+  SortGeneralWorkspace w{};
+  char* sort_base = c.take<char>(sort_bytes(k));
+  if (ws) w.sort = carve_sort(sort_base, k);
+  w.b_s = c.take<float>(k * 4);
+  w.perm_b = c.take<uint32_t>(k * 4);
+  w.fo = c.take<float>(k * m * 4);
+  w.uo = c.take<float>(k * m * 4);
+  w.fu = m == 1 ? c.take<float2>((k + 1) * 8) : nullptr;
+  char* apply_base = c.take<char>(0);
+  size_t apply_total = 0;
+  w.apply = carve_apply(ws ? apply_base : nullptr, k, k, k, m, Variant::Sym, false, &apply_total);
+  c.off += apply_total;
+  if (total) *total = (c.off + 255) & ~size_t(255);
+  return w;
+}
+
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
 bool overlaps(const void* p, size_t pb, const void* q, size_t qb) {
@@ -217,6 +247,7 @@ extern "C" size_t laplex_workspace_bytes(int op, uint64_t n, uint64_t k, uint32_
     case LAPLEX_OP_PHASED_BACKWARD: carve_backward(nullptr, n, 0, m, false, &total, true); return total;
     case LAPLEX_OP_PHASED_GENERAL_BACKWARD: carve_backward(nullptr, n, k, m, true, &total, true); return total;
     case LAPLEX_OP_SORT_SYM: carve_sort_sym(nullptr, n, m, &total); return total;
+    case LAPLEX_OP_SORT_GENERAL: carve_sort_general(nullptr, k, m, &total); return total;
     default: return 0;
   }
 }
@@ -312,6 +343,30 @@ extern "C" laplex_status laplex_sort_matvec_sym(const float* a, uint64_t n, uint
   }
   if ((e = sort_anchors(w.sort, a, n, w.a_s, w.perm, w.route ? &r : nullptr, stream)) != hipSuccess) return from_hip(e);
   return from_hip(apply_sym(w.apply, Variant::Sym, w.a_s, w.perm, w.route ? &r : nullptr, nullptr, n, m, x, y, stream));
+}
+
+extern "C" laplex_status laplex_sort_matvec_general(const float* a, uint64_t n, const float* b, uint64_t k, uint32_t m,
+                                                    const float* x, float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (n == 0 || m == 0) return LAPLEX_OK;
+  if (n > kMaxLen || k > kMaxLen || m > kMaxCols) return LAPLEX_ERR_SIZE;
+  if (!a || !y || !ws || (k > 0 && (!b || !x))) return LAPLEX_ERR_NULL;
+  if (misaligned(a, 4) || misaligned(b, 4) || misaligned(x, 4) || misaligned(y, 4) || misaligned(ws, 256))
+    return LAPLEX_ERR_ALIGN;
+  size_t need = 0;
+  carve_sort_general(nullptr, k, m, &need);
+  if (ws_bytes < need) return LAPLEX_ERR_WORKSPACE;
+  const size_t yb = n * (size_t)m * 4, xb = k * (size_t)m * 4;
+  if (overlaps(y, yb, a, n * 4) || overlaps(y, yb, b, k * 4) || overlaps(y, yb, x, xb) || overlaps(y, yb, ws, ws_bytes) ||
+      overlaps(a, n * 4, ws, ws_bytes) || overlaps(b, k * 4, ws, ws_bytes) || overlaps(x, xb, ws, ws_bytes))
+    return LAPLEX_ERR_OVERLAP;
+  hipError_t e;
+  if (k == 0) {  // no inputs: y = 0, and no stale flags for laplex_status_poll
+    if ((e = fill_zero_u32(ws, kSortHeaderBytes / 4, stream)) != hipSuccess) return from_hip(e);
+    return from_hip(fill_zero_u32(y, n * (uint64_t)m, stream));
+  }
+  const SortGeneralWorkspace w = carve_sort_general(ws, k, m, nullptr);
+  if ((e = sort_anchors(w.sort, b, k, w.b_s, w.perm_b, nullptr, stream)) != hipSuccess) return from_hip(e);
+  return from_hip(apply_general_search(w.apply, w.fo, w.uo, w.fu, a, n, w.b_s, w.perm_b, k, m, x, y, w.sort.header, stream));
 }
 
 extern "C" laplex_status laplex_sort_matvec_sym_backward(const void* fwd_ws, size_t fwd_ws_bytes, uint64_t n, uint32_t m,

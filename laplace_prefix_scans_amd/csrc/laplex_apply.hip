@@ -912,6 +912,262 @@ hipError_t apply_sym_presorted(const ApplyWorkspace& w, const float* a_s, const 
   return run_sym<1, false>(w, a_s, nullptr, &route, nullptr, n, 1, nullptr, y, s, true);
 }
 
+// ---------------------------------------------------------------- general case: scans over b
+// With few input anchors the scans can run over the sorted inputs alone
+// (the split of the general sum at an output anchor that the merged scan
+// makes, with the roles of the two sides exchanged): in sorted-b order
+//     Fi_j = sum_{j' <= j} exp(-(b_j - b_j')) x_j'     (inclusive forward)
+//     U_j  = sum_{j' >= j} exp(-(b_j' - b_j)) x_j'     (inclusive backward)
+// and for an output anchor a with p = #{b_j <= a} (b before a on ties)
+//     y = exp(-(a - b_{p-1})) Fi_{p-1} + exp(-(b_p - a)) U_p,
+// every factor <= 1.  The output anchors need no sort: each finds p by a
+// binary search, first over a sample of b staged in LDS, then inside one
+// group of b.
+
+// Fi and U of the sorted inputs (k rows of m columns), from the tile carries
+// of k_sym_reduce.
+template <int C>
+__global__ __launch_bounds__(apply_block(C)) void k_sym_fu(const float* __restrict__ b_s, const float* __restrict__ xs,
+                                                           const float* __restrict__ cfw, const float* __restrict__ cbw,
+                                                           const float2* __restrict__ tanch, uint64_t k, uint32_t m, uint64_t T,
+                                                           float* __restrict__ fo, float* __restrict__ uo, bool vec) {
+  constexpr int E = apply_items(C);
+  constexpr int NW = apply_block(C) / kWave;
+  constexpr int P = apply_tile(C);
+  __shared__ float s_wf[NW * C], s_wb[NW * C], s_wfs[NW], s_wbs[NW];
+  const uint64_t tile = blockIdx.x;
+  const uint64_t p0 = tile * P + (uint64_t)threadIdx.x * E;
+  float ae[E];
+  load_anchors<E>(b_s, p0, k, b_s[k - 1], vec, ae);
+  const float2 ta = tanch[tile];
+  const float sf = tile > 0 ? tanch[tile - 1].y : ta.x;
+  const float sb = tile + 1 < T ? tanch[tile + 1].x : ta.y;
+  for (uint32_t cc = 0; cc < m / C; ++cc) {
+    float v[E][C], cin_f[C], cin_b[C];
+    load_rows<E, C>(xs, p0, k, m, cc, true, v);
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      cin_f[j] = cfw[tile * m + cc * C + j];
+      cin_b[j] = cbw[tile * m + cc * C + j];
+    }
+    float F[E][C], U[E][C];
+    tile_scan_fu<E, C, NW, false>(ae, v, cin_f, sf, cin_b, sb, s_wf, s_wfs, s_wb, s_wbs, F, U);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int j = 0; j < C; ++j) F[e][j] += v[e][j];
+    store_rows<E, C>(fo, p0, k, m, cc, true, F);
+    store_rows<E, C>(uo, p0, k, m, cc, true, U);
+    __syncthreads();
+  }
+}
+
+constexpr int kSearchSamples = 4096;  // b values staged in LDS per workgroup
+constexpr int kSearchBlock = 512;
+constexpr int kSearchItems = 16;      // outputs per thread, one at a time (each holds its group's S values;
+                                      // more side by side measured slower: fewer waves per SIMD)
+constexpr uint32_t kSearchGroup = 16; // b values per sample at the least (64 bytes, loaded whole)
+constexpr uint32_t kSearchGroupMax = 64;
+
+// (Fi_{q-1}, U_q) for each interval q = 0..k of the sorted inputs (zero where
+// the neighbour does not exist), one column: an output in interval q reads
+// both with one load.
+__global__ void k_gen_pairs(const float* __restrict__ fo, const float* __restrict__ uo, uint64_t k, float2* __restrict__ fu) {
+  uint64_t q = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (; q <= k; q += stride) fu[q] = make_float2(q > 0 ? fo[q - 1] : 0.f, q < k ? uo[q] : 0.f);
+}
+
+// y (n x m, original order) for the output anchors a: q = #{b_j <= a} by a
+// search over the samples t_g = b_s[min(k, (g+1) S) - 1] (the last of each
+// group of S, a power of two from 16 to 64) in LDS, then a count over the
+// group's S values loaded whole; b_{q-1} and b_q come from the group or the
+// samples.  G = ceil(k / S) <= kSearchSamples.  One column takes (Fi_{q-1},
+// U_q) from fu, more columns the rows of fo and uo.  Non-finite anchors
+// raise the sort workspace's flag.
+template <int S>
+__global__ __launch_bounds__(kSearchBlock) void k_gen_search(const float* __restrict__ a, uint64_t n,
+                                                             const float* __restrict__ b_s, uint64_t k, uint32_t G,
+                                                             const float* __restrict__ fo, const float* __restrict__ uo,
+                                                             const float2* __restrict__ fu, uint32_t m, float* __restrict__ y,
+                                                             uint32_t* __restrict__ header) {
+  static_assert(S % 4 == 0 && S <= (int)kSearchGroupMax, "groups of whole 16-byte pieces");
+  constexpr int kSearchBatch = 1;
+  __shared__ float s_t[kSearchSamples];
+  const int tid = threadIdx.x;
+  for (uint32_t g = tid; g < G; g += kSearchBlock) s_t[g] = b_s[std::min<uint64_t>(k, (uint64_t)(g + 1) * S) - 1];
+  __syncthreads();
+  const uint64_t base = (uint64_t)blockIdx.x * (kSearchBlock * kSearchItems);
+  uint32_t bad = 0;
+  for (int b0 = 0; b0 < kSearchItems; b0 += kSearchBatch) {
+    float av[kSearchBatch];
+    uint32_t cnt[kSearchBatch];
+#pragma unroll
+    for (int it = 0; it < kSearchBatch; ++it) {
+      const uint64_t i = base + (uint64_t)(b0 + it) * kSearchBlock + tid;
+      av[it] = a[i < n ? i : n - 1];
+      bad |= (i < n && bits_nonfinite(__float_as_uint(av[it]))) ? 1u : 0u;
+      cnt[it] = 0;
+    }
+    // groups lying wholly at or below a (samples <= a), by descending powers
+    // of two (branch-free: the step is taken or not by a select)
+#pragma unroll
+    for (uint32_t step = kSearchSamples; step >= 1; step >>= 1) {
+#pragma unroll
+      for (int it = 0; it < kSearchBatch; ++it) {
+        const uint32_t t = cnt[it] + step;
+        const float v = s_t[(t < G ? t : G) - 1];
+        cnt[it] = (t <= G && v <= av[it]) ? t : cnt[it];
+      }
+    }
+    // the next group's values, loaded whole (rows past k read as +inf; with
+    // every group at or below a there is none and q = k)
+    float gv[kSearchBatch][S];
+#pragma unroll
+    for (int it = 0; it < kSearchBatch; ++it) {
+      const uint64_t p = (uint64_t)(cnt[it] < G ? cnt[it] : G - 1) * S;
+      if (p + S <= k) {
+#pragma unroll
+        for (int u = 0; u < S / 4; ++u) {
+          const float4 q4 = reinterpret_cast<const float4*>(b_s + p)[u];
+          gv[it][4 * u] = q4.x;
+          gv[it][4 * u + 1] = q4.y;
+          gv[it][4 * u + 2] = q4.z;
+          gv[it][4 * u + 3] = q4.w;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < S; ++u) gv[it][u] = p + u < k ? b_s[p + u] : __builtin_inff();
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < kSearchBatch; ++it) {
+      const uint64_t i = base + (uint64_t)(b0 + it) * kSearchBlock + tid;
+      const bool all = cnt[it] >= G;  // every b at or below a
+      uint32_t c2 = 0;
+      float bl = cnt[it] > 0 ? s_t[(cnt[it] < G ? cnt[it] : G) - 1] : 0.f, br = 0.f;
+#pragma unroll
+      for (int u = 0; u < S; ++u) {
+        const bool le = gv[it][u] <= av[it];
+        c2 += le ? 1u : 0u;
+        bl = (le && !all) ? gv[it][u] : bl;  // the last value <= a
+      }
+#pragma unroll
+      for (int u = S - 1; u >= 0; --u) br = gv[it][u] > av[it] ? gv[it][u] : br;  // the first value > a
+      const uint64_t q = all ? k : (uint64_t)cnt[it] * S + c2;  // #{b_j <= a}
+      const bool left = q > 0, right = q < k;
+      const float wl = left ? decay(bl - av[it]) : 0.f;
+      const float wr = right ? decay(av[it] - br) : 0.f;
+      if (i >= n) continue;
+      if (m == 1) {
+        const float2 f = fu[q];
+        y[i] = fmaf(wr, f.y, wl * f.x);
+      } else {
+        const uint64_t ql = left ? q - 1 : 0, qr = right ? q : k - 1;
+        for (uint32_t c = 0; c < m; ++c) {
+          const float yl = left ? wl * fo[ql * m + c] : 0.f;
+          y[i * m + c] = right ? fmaf(wr, uo[qr * m + c], yl) : yl;
+        }
+      }
+    }
+  }
+  if (__ballot(bad) != 0ull && lane_id() == 0) atomicOr(&header[kHdrFlags], kFlagNonFinite);
+}
+
+// the same search for more than kSearchSamples * kSearchGroupMax inputs: the
+// group by binary search in b_s (S a power of two)
+__global__ __launch_bounds__(kSearchBlock) void k_gen_search_wide(const float* __restrict__ a, uint64_t n,
+                                                                  const float* __restrict__ b_s, uint64_t k, uint64_t S, uint32_t G,
+                                                                  const float* __restrict__ fo, const float* __restrict__ uo,
+                                                                  uint32_t m, float* __restrict__ y, uint32_t* __restrict__ header) {
+  __shared__ float s_t[kSearchSamples];
+  const int tid = threadIdx.x;
+  for (uint32_t g = tid; g < G; g += kSearchBlock) s_t[g] = b_s[std::min<uint64_t>(k, (uint64_t)(g + 1) * S) - 1];
+  __syncthreads();
+  const uint64_t base = (uint64_t)blockIdx.x * (kSearchBlock * kSearchItems);
+  uint32_t bad = 0;
+#pragma unroll
+  for (int it = 0; it < kSearchItems; ++it) {
+    const uint64_t i = base + (uint64_t)it * kSearchBlock + tid;
+    const float av = a[i < n ? i : n - 1];
+    bad |= (i < n && bits_nonfinite(__float_as_uint(av))) ? 1u : 0u;
+    uint32_t cnt = 0;
+    for (uint32_t step = kSearchSamples; step >= 1; step >>= 1) {
+      const uint32_t t = cnt + step;
+      cnt = (t <= G && s_t[(t < G ? t : G) - 1] <= av) ? t : cnt;
+    }
+    const uint64_t p = std::min<uint64_t>(k, (uint64_t)cnt * S);
+    uint64_t c2 = 0;
+    for (uint64_t step = S; step >= 1; step >>= 1) {
+      const uint64_t t = p + c2 + step;
+      c2 = (t <= k && c2 + step <= S && b_s[(t < k ? t : k) - 1] <= av) ? c2 + step : c2;
+    }
+    const uint64_t q = p + c2;
+    const bool left = q > 0, right = q < k;
+    const uint64_t ql = left ? q - 1 : 0, qr = right ? q : k - 1;
+    const float wl = left ? decay(b_s[ql] - av) : 0.f;
+    const float wr = right ? decay(av - b_s[qr]) : 0.f;
+    if (i >= n) continue;
+    for (uint32_t c = 0; c < m; ++c) {
+      const float yl = left ? wl * fo[ql * m + c] : 0.f;
+      y[i * m + c] = right ? fmaf(wr, uo[qr * m + c], yl) : yl;
+    }
+  }
+  if (__ballot(bad) != 0ull && lane_id() == 0) atomicOr(&header[kHdrFlags], kFlagNonFinite);
+}
+
+template <int C>
+static hipError_t run_general_search(const ApplyWorkspace& w, float* fo, float* uo, float2* fu, const float* a, uint64_t n, const float* b_s,
+                                     const uint32_t* perm_b, uint64_t k, uint32_t m, const float* x, float* y, uint32_t* header,
+                                     hipStream_t s) {
+  constexpr int P = apply_tile(C);
+  const uint64_t T = (k + P - 1) / P;
+  const bool vec = (reinterpret_cast<uintptr_t>(b_s) & 15) == 0;
+  hipError_t e;
+  gather_rows(x, perm_b, nullptr, k, m, w.xs, nullptr, s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  LAPLEX_LAUNCH("k_sym_reduce", k, s,
+                k_sym_reduce<C, false><<<dim3((unsigned)T), dim3(apply_block(C)), 0, s>>>(b_s, k, m, w.xs, nullptr, w.bf, w.bb,
+                                                                                         w.tanch, vec));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = tile_carries(w.bf, w.bb, w.tanch, T, m, w.cf, w.cb, w.gbf, w.gbb, w.gcf, w.gcb, w.ganch, s)) != hipSuccess) return e;
+  LAPLEX_LAUNCH("k_sym_fu", k, s,
+                k_sym_fu<C><<<dim3((unsigned)T), dim3(apply_block(C)), 0, s>>>(b_s, w.xs, w.cf, w.cb, w.tanch, k, m, T, fo, uo, vec));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  uint64_t S = kSearchGroup;
+  while ((k + S - 1) / S > (uint64_t)kSearchSamples) S <<= 1;
+  const uint32_t G = (uint32_t)((k + S - 1) / S);
+  const unsigned blocks = (unsigned)((n + (uint64_t)kSearchBlock * kSearchItems - 1) / ((uint64_t)kSearchBlock * kSearchItems));
+  if (m == 1 && S <= kSearchGroupMax) {
+    LAPLEX_LAUNCH("k_gen_pairs", k + 1, s, k_gen_pairs<<<(unsigned)std::min<uint64_t>((k + 256) / 256, 4096), 256, 0, s>>>(fo, uo, k, fu));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+#define LAPLEX_SEARCH(SS)                                                                                             \
+  LAPLEX_LAUNCH("k_gen_search", n, s, k_gen_search<SS><<<blocks, kSearchBlock, 0, s>>>(a, n, b_s, k, G, fo, uo, fu, m, y, header))
+  if (S == 16)
+    LAPLEX_SEARCH(16);
+  else if (S == 32)
+    LAPLEX_SEARCH(32);
+  else if (S == 64)
+    LAPLEX_SEARCH(64);
+  else
+    LAPLEX_LAUNCH("k_gen_search", n, s,
+                  k_gen_search_wide<<<blocks, kSearchBlock, 0, s>>>(a, n, b_s, k, S, G, fo, uo, m, y, header));
+#undef LAPLEX_SEARCH
+  return hipGetLastError();
+}
+
+hipError_t apply_general_search(const ApplyWorkspace& w, float* fo, float* uo, float2* fu, const float* a, uint64_t n, const float* b_s,
+                                const uint32_t* perm_b, uint64_t k, uint32_t m, const float* x, float* y, uint32_t* header,
+                                hipStream_t s) {
+  switch (column_chunk(m)) {
+    case 8: return run_general_search<8>(w, fo, uo, fu, a, n, b_s, perm_b, k, m, x, y, header, s);
+    case 4: return run_general_search<4>(w, fo, uo, fu, a, n, b_s, perm_b, k, m, x, y, header, s);
+    case 2: return run_general_search<2>(w, fo, uo, fu, a, n, b_s, perm_b, k, m, x, y, header, s);
+    default: return run_general_search<1>(w, fo, uo, fu, a, n, b_s, perm_b, k, m, x, y, header, s);
+  }
+}
+
 hipError_t apply_sym(const ApplyWorkspace& w, Variant var, const float* a_s, const uint32_t* perm, const SortRoute* route,
                      const float* phi, uint64_t n, uint32_t m, const float* x, float* y, hipStream_t s) {
   const bool ph = var == Variant::Phased;

@@ -127,6 +127,14 @@ hipError_t apply_sym(const ApplyWorkspace& w, Variant var, const float* a_s, con
 // (from sort_anchors_payload): scans, then y back along the route.
 hipError_t apply_sym_presorted(const ApplyWorkspace& w, const float* a_s, const SortRoute& route, uint64_t n, float* y,
                                hipStream_t s);
+// General operator from unsorted output anchors a (n) and sorted inputs
+// b_s (k >= 1, sort handle perm_b): the scans run over b alone (Fi into fo,
+// U into uo, k x m each; for one column also (Fi_{q-1}, U_q) per interval
+// into fu, k + 1) and each output searches its interval in b_s; y in the
+// original order of a.  Non-finite a raise kFlagNonFinite in header.
+hipError_t apply_general_search(const ApplyWorkspace& w, float* fo, float* uo, float2* fu, const float* a, uint64_t n, const float* b_s,
+                                const uint32_t* perm_b, uint64_t k, uint32_t m, const float* x, float* y, uint32_t* header,
+                                hipStream_t s);
 hipError_t apply_general(const ApplyWorkspace& w, Variant var, const float* a_s, const uint32_t* perm_a, const SortRoute* route_a,
                          const float* phi, uint64_t n, const float* b_s, const uint32_t* perm_b, const SortRoute* route_b,
                          const float* psi, uint64_t k, uint32_t m, const float* x, float* y, hipStream_t s);

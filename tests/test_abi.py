@@ -46,7 +46,7 @@ def test_workspace_sizes(L):
     assert lp.laplex_workspace_bytes(99, 10) == 0
     assert lp.laplex_workspace_bytes(lp.LAPLEX_OP_GENERAL_BACKWARD, 1 << 20, 1 << 10, 2) > \
         lp.laplex_workspace_bytes(lp.LAPLEX_OP_GENERAL, 1 << 20, 1 << 10, 2)
-    for op in range(11):
+    for op in range(12):
         a = lp.laplex_workspace_bytes(op, 4096, 100, 1)
         b = lp.laplex_workspace_bytes(op, 1 << 22, 1 << 20, 1)
         assert a % 256 == 0 and b % 256 == 0 and b >= a
@@ -141,6 +141,16 @@ def test_host_argument_errors(L):
     assert SM(A, 1000, 1, vp(0x500000), vp(0x500100), vp(0x10000000), needs, None) == OVERLAP  # y on x
     assert SM(A, 1000, 1, vp(0x500000), vp(0x100100), vp(0x10000000), needs, None) == OVERLAP  # y on a
     assert SM(vp(0x10000100), 1000, 1, vp(0x500000), vp(0x600000), vp(0x10000000), needs, None) == OVERLAP  # a in ws
+    # one-call general operator
+    SG = L.laplex_sort_matvec_general
+    assert SG(None, 0, None, 0, 1, None, None, None, 0, None) == OK
+    assert SG(A, 10, None, 5, 1, B, vp(0x300000), W, 1 << 30, None) == NULL  # k > 0 needs b
+    assert SG(A, 10, A, 1 << 32, 1, B, vp(0x300000), W, 1 << 40, None) == SIZE
+    needg = L.laplex_workspace_bytes(11, 1000, 300, 1)
+    assert needg > 0
+    assert SG(A, 1000, B, 300, 1, vp(0x300000), vp(0x400000), vp(0x10000000), needg - 256, None) == WS
+    assert SG(A, 1000, B, 300, 1, vp(0x300000), vp(0x300100), vp(0x10000000), needg, None) == OVERLAP  # y on x
+    assert SG(A, 1000, B, 300, 1, vp(0x300002), vp(0x400000), vp(0x10000000), needg, None) == ALIGN
     # backward from a one-call forward's workspace
     SB = L.laplex_sort_matvec_sym_backward
     assert SB(None, 0, 0, 1, None, None, None, None, 0, None) == OK

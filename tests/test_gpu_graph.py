@@ -33,11 +33,20 @@ def _setup(kind, n, k, m):
         ws_b = lp.workspace(lp.LAPLEX_OP_SORT, k, device=dev)
         rb = lp.route_buffer(k, device=dev) if m <= 4 else None
         st["b"] = b
-    rows_x = k if kind in ("general", "gen_backward", "gram", "phased_gen_backward") else n
+    rows_x = k if kind in ("general", "gen_backward", "gram", "phased_gen_backward", "sort_general") else n
     x = torch.empty(rows_x, m, device=dev)
     st["x"] = x
     outs = []
-    if kind == "sort_sym_backward":
+    if kind == "sort_general":
+        b = torch.empty(k, device=dev)
+        st["b"] = b
+        y = torch.empty(n, m, device=dev)
+        ws = lp.workspace(lp.LAPLEX_OP_SORT_GENERAL, n, k, m, device=dev)
+
+        def op():
+            lp.laplex_sort_matvec_general(a, b, x, y=y, ws=ws)
+        outs = [y]
+    elif kind == "sort_sym_backward":
         g = torch.empty(n, m, device=dev)
         st["g"] = g
         y = torch.empty(n, m, device=dev)
@@ -154,7 +163,7 @@ def _setup(kind, n, k, m):
     return step, fill, outs, [a_s, pa]
 
 
-@pytest.mark.parametrize("kind,n,k,m", [("sort_sym", 100000, 0, 1), ("sort_sym_backward", 80000, 0, 1), ("sym", 100000, 0, 1), ("sym", 70001, 0, 8), ("phased", 50000, 0, 4),
+@pytest.mark.parametrize("kind,n,k,m", [("sort_sym", 100000, 0, 1), ("sort_general", 90000, 7000, 2), ("sort_sym_backward", 80000, 0, 1), ("sym", 100000, 0, 1), ("sym", 70001, 0, 8), ("phased", 50000, 0, 4),
                                         ("general", 90000, 7000, 1), ("sym_backward", 60000, 0, 2),
                                         ("gen_backward", 40000, 9000, 1), ("gram", 3000, 5000, 1),
                                         ("phased_backward", 30000, 0, 3), ("phased_gen_backward", 20000, 6000, 2)])
