@@ -100,6 +100,31 @@ __device__ __forceinline__ float dpp_row(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+// Inclusive prefix sum of u32 values over the wave: DPP row shifts within
+// each 16-lane row, then the row totals joined (lane 15 of each row, and of
+// the lower half, read by shuffles).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_row_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_sum_u32(uint32_t x) {
+  const int lane = lane_id(), rl = lane & 15, row = lane >> 4;
+  uint32_t t;
+  t = dpp_row_u32<0x110 | 1>(x);
+  x += rl >= 1 ? t : 0u;
+  t = dpp_row_u32<0x110 | 2>(x);
+  x += rl >= 2 ? t : 0u;
+  t = dpp_row_u32<0x110 | 4>(x);
+  x += rl >= 4 ? t : 0u;
+  t = dpp_row_u32<0x110 | 8>(x);
+  x += rl >= 8 ? t : 0u;
+  t = (uint32_t)__shfl(x, (lane & ~31) + 15);
+  x += (row & 1) ? t : 0u;
+  t = (uint32_t)__shfl(x, 31);
+  x += row >= 2 ? t : 0u;
+  return x;
+}
+
 // One scan step: the lanes with `take` join the segment summary (bs, ss) that
 // precedes (forward) or follows (backward) them.
 template <int C, bool TIE, bool FWD>

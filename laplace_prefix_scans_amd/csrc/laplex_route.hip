@@ -254,17 +254,27 @@ __global__ __launch_bounds__(kSortBlock) void k_route_inv(const float* __restric
 // Chunk cover of a tile's digit runs, for rows of W floats (W = 1, 2, 4):
 // run d covers global rows [G, G + L); the aligned 4-float chunks that overlap
 // it are numbered block-locally from cs[d], the first being global chunk
-// c0[d]; cdig[c] is the run of block-local chunk c.  L is clipped to the
-// array, so no chunk lies wholly past it.
+// c0[d] (chunk_run finds the run of a block-local chunk).  L is clipped to
+// the array, so no chunk lies wholly past it.
 template <int W>
 struct RunChunks {
   static constexpr int kMax = kSortTile * W / 4 + 512;  // sum over runs of (L W + 6) / 4
-  uint8_t cdig[kMax];
   uint32_t cs[257];
   uint32_t c0[256];
   uint32_t len[256];
   uint32_t wsum[4];
 };
+
+// The run of block-local chunk c (cs[d] <= c < cs[d + 1]; empty runs have
+// cs[d] == cs[d + 1] and are passed over): a branch-free binary search over
+// the 257 prefix entries in LDS.
+template <int W>
+__device__ __forceinline__ uint32_t chunk_run(const RunChunks<W>& rc, uint32_t c) {
+  uint32_t d = 0;
+#pragma unroll
+  for (uint32_t step = 128; step >= 1; step >>= 1) d = rc.cs[d + step] <= c ? d + step : d;
+  return d;
+}
 
 // Called by every thread of the block after s_start / s_gb are written (and
 // not yet synchronised); ends with a barrier.
@@ -283,12 +293,7 @@ __device__ __forceinline__ void build_chunks(RunChunks<W>& rc, const uint16_t* s
     nch = L ? (uint32_t)(c1 - c0) : 0u;
     rc.c0[tid] = (uint32_t)c0;
     rc.len[tid] = (uint32_t)L;
-    x = nch;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const uint32_t t = __shfl_up(x, off);
-      if (lane >= off) x += t;
-    }
+    x = wave_incl_sum_u32(nch);
     if (lane == kWave - 1) rc.wsum[wid] = x;
   }
   __syncthreads();
@@ -297,11 +302,6 @@ __device__ __forceinline__ void build_chunks(RunChunks<W>& rc, const uint16_t* s
     for (int i = 0; i < wid; ++i) pre += rc.wsum[i];
     rc.cs[tid] = pre + x - nch;
     if (tid == 255) rc.cs[256] = pre + x;
-  }
-  __syncthreads();
-  for (int d = wid; d < 256; d += NW) {
-    const uint32_t lo = rc.cs[d], hi = rc.cs[d + 1];
-    for (uint32_t c = lo + lane; c < hi; c += kWave) rc.cdig[c] = (uint8_t)d;
   }
   __syncthreads();
 }
@@ -350,13 +350,14 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(W ==
   const uint64_t nfl = n * W;  // >= 4 (the host launches this kernel only then)
   // all chunk loads are issued before any is consumed; a chunk that is not
   // loaded whole (past `total`, or reaching past the array) loads chunk 0.
-  // The run and global index of each chunk are looked up again afterwards
-  // rather than held in registers across the loads.
+  // Each chunk's run is kept; its global index is formed again afterwards.
   float4 q[CSTEPS];
+  uint32_t dr[CSTEPS];
 #pragma unroll
   for (int r = 0; r < CSTEPS; ++r) {
     const uint32_t c = (uint32_t)(r * kSortBlock + tid);
-    const uint32_t d = rc.cdig[std::min<uint32_t>(c, MAXCH - 1)];
+    const uint32_t d = chunk_run(rc, c < total ? c : 0u);
+    dr[r] = d;
     const uint32_t g = rc.c0[d] + (c - rc.cs[d]);  // global chunk index (< n W / 4 + 1 <= 2^32)
     const bool whole = c < total && 4 * (uint64_t)g + 4 <= nfl;
     q[r] = reinterpret_cast<const float4*>(in)[whole ? g : 0u];
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(W ==
   for (int r = 0; r < CSTEPS; ++r) {
     const uint32_t c = (uint32_t)(r * kSortBlock + tid);
     if (c < total) {
-      const uint32_t d = rc.cdig[c];
+      const uint32_t d = dr[r];
       const uint64_t g = rc.c0[d] + (c - rc.cs[d]);
       const uint32_t gb = s_gb[d];
       const uint64_t G = (uint64_t)(uint32_t)(gb + s_start[d]);
