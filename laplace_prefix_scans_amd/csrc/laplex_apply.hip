@@ -55,16 +55,23 @@ __device__ __forceinline__ void block_sum2(float (&a)[CC], float (&b)[CC], float
 // ae[], nondecreasing across the whole tile); carries into the tile from the
 // left (cf, anchored at sf) and right (cb, anchored at sb).
 // Out: F[e][j] the strict forward value (earlier elements only, tied ones
-// included), U[e][j] the inclusive backward value.  TIE selects the decay
-// (see decay_m).
-template <int E, int CC, int NW, bool TIE>
-__device__ __forceinline__ void tile_scan_fu(const float (&ae)[E], const float (&v)[E][CC], const float (&cf)[CC],
-                                             float sf, const float (&cb)[CC], float sb, float* s_wf, float* s_wfs,
-                                             float* s_wb, float* s_wbs, float (&F)[E][CC], float (&Uo)[E][CC]) {
+// included), U[e][j] the inclusive backward value.  Columns [0, NT) scan with
+// the tie decay (see decay_m), columns [NT, CC) with the kernel's decay, in
+// one pass (the anchor differences, wave exchanges and barriers shared).
+template <int E, int CC, int NW, int NT>
+__device__ __forceinline__ void tile_scan_fu_mix(const float (&ae)[E], const float (&v)[E][CC], const float (&cf)[CC],
+                                                 float sf, const float (&cb)[CC], float sb, float* s_wf, float* s_wfs,
+                                                 float* s_wb, float* s_wbs, float (&F)[E][CC], float (&Uo)[E][CC]) {
   const int lane = lane_id(), wid = threadIdx.x / kWave;
-  float d[E];  // d[e] = exp(ae[e-1] - ae[e]) for e >= 1
+  // the decay of column j for anchor difference x
+  auto dk = [](float x, int j) -> float { return j < NT ? decay_m<true>(x) : decay_m<false>(x); };
+  float dt[E], de[E];  // d[e] = exp(ae[e-1] - ae[e]) for e >= 1, tie and kernel
 #pragma unroll
-  for (int e = 1; e < E; ++e) d[e] = decay_m<TIE>(ae[e - 1] - ae[e]);
+  for (int e = 1; e < E; ++e) {
+    dt[e] = NT > 0 ? decay_m<true>(ae[e - 1] - ae[e]) : 0.f;
+    de[e] = NT < CC ? decay_m<false>(ae[e - 1] - ae[e]) : 0.f;
+  }
+  auto dcol = [&](int e, int j) -> float { return j < NT ? dt[e] : de[e]; };
 
   // thread-local aggregates
   float B[CC], D[CC];
@@ -76,15 +83,15 @@ __device__ __forceinline__ void tile_scan_fu(const float (&ae)[E], const float (
 #pragma unroll
   for (int e = 1; e < E; ++e)
 #pragma unroll
-    for (int j = 0; j < CC; ++j) B[j] = fmaf(d[e], B[j], v[e][j]);
+    for (int j = 0; j < CC; ++j) B[j] = fmaf(dcol(e, j), B[j], v[e][j]);
 #pragma unroll
   for (int e = E - 2; e >= 0; --e)
 #pragma unroll
-    for (int j = 0; j < CC; ++j) D[j] = fmaf(d[e + 1], D[j], v[e][j]);
+    for (int j = 0; j < CC; ++j) D[j] = fmaf(dcol(e + 1, j), D[j], v[e][j]);
 
   // wave scans (forward: by last anchor; backward: by first anchor)
-  wave_scan_fwd<CC, TIE>(B, ae[E - 1]);
-  wave_scan_bwd<CC, TIE>(D, ae[0]);
+  wave_scan_fwd_mix<CC, NT>(B, ae[E - 1]);
+  wave_scan_bwd_mix<CC, NT>(D, ae[0]);
   if (lane == kWave - 1) {
 #pragma unroll
     for (int j = 0; j < CC; ++j) s_wf[wid * CC + j] = B[j];
@@ -119,52 +126,59 @@ __device__ __forceinline__ void tile_scan_fu(const float (&ae)[E], const float (
   {
     const bool fw = lane < wid, bw = lane > wid && lane < NW;
     const int lf = fw ? lane : 0, lb = bw ? lane : 0;
-    const float gf = fw ? decay_m<TIE>(s_wfs[lf] - sw) : (lane == kWave - 1 ? decay_m<TIE>(sf - sw) : 0.f);
-    const float gb = bw ? decay_m<TIE>(sz2 - s_wbs[lb]) : (lane == kWave - 1 ? decay_m<TIE>(sz2 - sb) : 0.f);
+    const float xf = fw ? s_wfs[lf] - sw : sf - sw;
+    const float xb = bw ? sz2 - s_wbs[lb] : sz2 - sb;
+    const bool cf_lane = !fw && lane == kWave - 1, cb_lane = !bw && lane == kWave - 1;
 #pragma unroll
     for (int j = 0; j < CC; ++j) {
-      cw[j] = fw ? gf * s_wf[lf * CC + j] : (lane == kWave - 1 ? gf * cf[j] : 0.f);
-      cz[j] = bw ? gb * s_wb[lb * CC + j] : (lane == kWave - 1 ? gb * cb[j] : 0.f);
+      const float gf = (fw || cf_lane) ? dk(xf, j) : 0.f;
+      const float gb = (bw || cb_lane) ? dk(xb, j) : 0.f;
+      cw[j] = fw ? gf * s_wf[lf * CC + j] : (cf_lane ? gf * cf[j] : 0.f);
+      cz[j] = bw ? gb * s_wb[lb * CC + j] : (cb_lane ? gb * cb[j] : 0.f);
     }
     wave_sum<CC>(cw);
     wave_sum<CC>(cz);
   }
   float swl = sw, szl = sz2;
   if (lane > 0) {
-    const float g = decay_m<TIE>(swl - sx);
 #pragma unroll
-    for (int j = 0; j < CC; ++j) cw[j] = fmaf(g, cw[j], X[j]);
+    for (int j = 0; j < CC; ++j) cw[j] = fmaf(dk(swl - sx, j), cw[j], X[j]);
     swl = sx;
   }
   if (lane < kWave - 1) {
-    const float g = decay_m<TIE>(sz - szl);
 #pragma unroll
-    for (int j = 0; j < CC; ++j) cz[j] = fmaf(g, cz[j], Z[j]);
+    for (int j = 0; j < CC; ++j) cz[j] = fmaf(dk(sz - szl, j), cz[j], Z[j]);
     szl = sz;
   }
 
   // full forward pass: strict lower part of each element
-  const float d0 = decay_m<TIE>(swl - ae[0]);
 #pragma unroll
   for (int j = 0; j < CC; ++j) {
+    const float d0 = dk(swl - ae[0], j);
     float L = cw[j];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      F[e][j] = (e == 0 ? d0 : d[e]) * L;
+      F[e][j] = (e == 0 ? d0 : dcol(e, j)) * L;
       L = v[e][j] + F[e][j];
     }
   }
   // full backward pass, combined
-  const float dl = decay_m<TIE>(ae[E - 1] - szl);
 #pragma unroll
   for (int j = 0; j < CC; ++j) {
+    const float dl = dk(ae[E - 1] - szl, j);
     float U = cz[j];
 #pragma unroll
     for (int e = E - 1; e >= 0; --e) {
-      U = fmaf(e == E - 1 ? dl : d[e + 1], U, v[e][j]);
+      U = fmaf(e == E - 1 ? dl : dcol(e + 1, j), U, v[e][j]);
       Uo[e][j] = U;
     }
   }
+}
+template <int E, int CC, int NW, bool TIE>
+__device__ __forceinline__ void tile_scan_fu(const float (&ae)[E], const float (&v)[E][CC], const float (&cf)[CC], float sf,
+                                             const float (&cb)[CC], float sb, float* s_wf, float* s_wfs, float* s_wb,
+                                             float* s_wbs, float (&F)[E][CC], float (&Uo)[E][CC]) {
+  tile_scan_fu_mix<E, CC, NW, TIE ? CC : 0>(ae, v, cf, sf, cb, sb, s_wf, s_wfs, s_wb, s_wbs, F, Uo);
 }
 
 // The operator's tile scan: v[e][j] becomes strict forward + inclusive
@@ -1323,8 +1337,9 @@ __global__ __launch_bounds__(bwd_block(C)) void k_bwd_reduce(const float* __rest
 // Tile scans of (x, g) under both decays -> dx = K g (rows in sorted order)
 // and da (sorted order).  By linearity da_i = -(A_i - A0_i) with
 // A = sum_c g_c (F - U)(x_c) + x_c (F - U)(g_c) under the kernel's decay and A0
-// the same under the tie decay; the tie scan runs first and only its per-element
-// sum stays live through the second scan.  PAIR (one column): x and g arrive
+// the same under the tie decay.  One column scans both decays in one pass
+// (four columns, the tie half first); wider chunks run the tie scan first and
+// keep only its per-element sum through the second.  PAIR (one column): x and g arrive
 // interleaved as rows (x_i, g_i) in xs.
 template <int C, bool PAIR>
 __global__ __launch_bounds__(bwd_block(C)) void k_bwd_apply(const float* __restrict__ a_s, const float* __restrict__ xs, const float* __restrict__ gs,
@@ -1335,7 +1350,7 @@ __global__ __launch_bounds__(bwd_block(C)) void k_bwd_apply(const float* __restr
   constexpr int BLOCK = bwd_block(C);
   constexpr int NW = BLOCK / kWave;
   constexpr int P = BLOCK * E;
-  __shared__ float s_wf[NW * CC], s_wb[NW * CC], s_wfs[NW], s_wbs[NW];
+  __shared__ float s_wf[NW * 2 * CC], s_wb[NW * 2 * CC], s_wfs[NW], s_wbs[NW];
   const uint32_t M = 4 * m;
   const int tid = threadIdx.x;
   const uint64_t tile = blockIdx.x;
@@ -1373,7 +1388,9 @@ __global__ __launch_bounds__(bwd_block(C)) void k_bwd_apply(const float* __restr
           v[e][C + j] = gv[e][j];
         }
     }
-    {
+    if constexpr (C > 1) {
+      // wider chunks: the tie scan, then the kernel's scan (one mixed scan of
+      // twice the columns would hold too many registers)
       float ct_f[CC], ct_b[CC];
 #pragma unroll
       for (int j = 0; j < CC; ++j) {
@@ -1389,9 +1406,7 @@ __global__ __launch_bounds__(bwd_block(C)) void k_bwd_apply(const float* __restr
           acc0[e] = fmaf(v[e][C + j], F0[e][j] - U0[e][j], acc0[e]);
           acc0[e] = fmaf(v[e][j], F0[e][C + j] - U0[e][C + j], acc0[e]);
         }
-    }
-    __syncthreads();  // the second scan reuses the wave summaries
-    {
+      __syncthreads();  // the second scan reuses the wave summaries
       float ce_f[CC], ce_b[CC];
 #pragma unroll
       for (int j = 0; j < CC; ++j) {
@@ -1408,6 +1423,36 @@ __global__ __launch_bounds__(bwd_block(C)) void k_bwd_apply(const float* __restr
           acc[e] = fmaf(v[e][C + j], F[e][j] - U[e][j], acc[e]);
           acc[e] = fmaf(v[e][j], F[e][C + j] - U[e][C + j], acc[e]);
           dx[e][j] = F[e][C + j] + U[e][C + j];
+        }
+      store_rows<E, C>(dxs, p0, n, m, cc, true, dx);
+    } else {
+      // one column: one scan of [x, g | x, g], the first half with the tie
+      // decay (sums over tied anchors, F0 and U0), the second with the
+      // kernel's decay
+      float v2[E][2 * CC], c2f[2 * CC], c2b[2 * CC];
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int j = 0; j < CC; ++j) v2[e][j] = v2[e][CC + j] = v[e][j];
+#pragma unroll
+      for (int j = 0; j < CC; ++j) {
+        c2f[j] = cfw[tile * M + bwdcol<C>(m, cc, CC + j)];
+        c2b[j] = cbw[tile * M + bwdcol<C>(m, cc, CC + j)];
+        c2f[CC + j] = cfw[tile * M + bwdcol<C>(m, cc, j)];
+        c2b[CC + j] = cbw[tile * M + bwdcol<C>(m, cc, j)];
+      }
+      float F2[E][2 * CC], U2[E][2 * CC];
+      tile_scan_fu_mix<E, 2 * CC, NW, CC>(ae, v2, c2f, sf, c2b, sb, s_wf, s_wfs, s_wb, s_wbs, F2, U2);
+      float dx[E][C];
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+          acc0[e] = fmaf(v[e][C + j], F2[e][j] - U2[e][j], acc0[e]);
+          acc0[e] = fmaf(v[e][j], F2[e][C + j] - U2[e][C + j], acc0[e]);
+          acc[e] = fmaf(v[e][C + j], F2[e][CC + j] - U2[e][CC + j], acc[e]);
+          acc[e] = fmaf(v[e][j], F2[e][CC + C + j] - U2[e][CC + C + j], acc[e]);
+          dx[e][j] = F2[e][CC + C + j] + U2[e][CC + C + j];
         }
       store_rows<E, C>(dxs, p0, n, m, cc, true, dx);
     }

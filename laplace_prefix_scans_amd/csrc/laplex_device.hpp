@@ -127,28 +127,33 @@ __device__ __forceinline__ uint32_t wave_incl_sum_u32(uint32_t x) {
 
 // One scan step: the lanes with `take` join the segment summary (bs, ss) that
 // precedes (forward) or follows (backward) them.
-template <int C, bool TIE, bool FWD>
+// Columns [0, NT) of a scan use the tie decay, columns [NT, C) the kernel's
+// decay (NT = C: all tie; NT = 0: all kernel); both weights come from the
+// same anchor difference.
+template <int C, int NT, bool FWD>
 __device__ __forceinline__ void scan_join(float (&B)[C], float s, const float (&bs)[C], float ss, bool take) {
-  const float w = decay_m<TIE>(FWD ? ss - s : s - ss);
+  const float x = FWD ? ss - s : s - ss;
+  const float wt = NT > 0 ? decay_m<true>(x) : 0.f;
+  const float we = NT < C ? decay_m<false>(x) : 0.f;
 #pragma unroll
   for (int c = 0; c < C; ++c)
-    if (take) B[c] = fmaf(w, bs[c], B[c]);
+    if (take) B[c] = fmaf(c < NT ? wt : we, bs[c], B[c]);
 }
 
 // Inclusive forward scan across the wave, lane order.  `s` is this lane's
 // segment-end anchor (it does not change).  Within each 16-lane row a
 // Hillis-Steele scan by DPP row shifts; then rows 1 and 3 join the total of
 // the row before (lanes 15 and 47), and rows 2 and 3 the total of rows 0-1
-// (lane 31).
-template <int C, bool TIE = false>
-__device__ __forceinline__ void wave_scan_fwd(float (&B)[C], float s) {
+// (lane 31).  NT: leading columns with the tie decay.
+template <int C, int NT>
+__device__ __forceinline__ void wave_scan_fwd_mix(float (&B)[C], float s) {
   const int lane = lane_id(), rl = lane & 15, row = lane >> 4;
   float bs[C];
 #define LAPLEX_FWD_STEP(K)                                              \
   {                                                                     \
     const float ss = dpp_row<0x110 | K>(s);                             \
     _Pragma("unroll") for (int c = 0; c < C; ++c) bs[c] = dpp_row<0x110 | K>(B[c]); \
-    scan_join<C, TIE, true>(B, s, bs, ss, rl >= K);                     \
+    scan_join<C, NT, true>(B, s, bs, ss, rl >= K);                      \
   }
   LAPLEX_FWD_STEP(1)
   LAPLEX_FWD_STEP(2)
@@ -160,29 +165,33 @@ __device__ __forceinline__ void wave_scan_fwd(float (&B)[C], float s) {
     const float ss = __shfl(s, src);
 #pragma unroll
     for (int c = 0; c < C; ++c) bs[c] = __shfl(B[c], src);
-    scan_join<C, TIE, true>(B, s, bs, ss, (row & 1) != 0);
+    scan_join<C, NT, true>(B, s, bs, ss, (row & 1) != 0);
   }
   {
     const float ss = __shfl(s, 31);
 #pragma unroll
     for (int c = 0; c < C; ++c) bs[c] = __shfl(B[c], 31);
-    scan_join<C, TIE, true>(B, s, bs, ss, row >= 2);
+    scan_join<C, NT, true>(B, s, bs, ss, row >= 2);
   }
+}
+template <int C, bool TIE = false>
+__device__ __forceinline__ void wave_scan_fwd(float (&B)[C], float s) {
+  wave_scan_fwd_mix<C, TIE ? C : 0>(B, s);
 }
 
 // Inclusive backward scan across the wave (from the last lane down).  `s` is
 // this lane's segment-start anchor.  The mirror image of the forward scan:
 // row_shl steps within rows, then rows 0 and 2 join the row after (lanes 16
 // and 48), and rows 0 and 1 the total of rows 2-3 (lane 32).
-template <int C, bool TIE = false>
-__device__ __forceinline__ void wave_scan_bwd(float (&B)[C], float s) {
+template <int C, int NT>
+__device__ __forceinline__ void wave_scan_bwd_mix(float (&B)[C], float s) {
   const int lane = lane_id(), rl = lane & 15, row = lane >> 4;
   float bs[C];
 #define LAPLEX_BWD_STEP(K)                                              \
   {                                                                     \
     const float ss = dpp_row<0x100 | K>(s);                             \
     _Pragma("unroll") for (int c = 0; c < C; ++c) bs[c] = dpp_row<0x100 | K>(B[c]); \
-    scan_join<C, TIE, false>(B, s, bs, ss, rl + K < 16);                \
+    scan_join<C, NT, false>(B, s, bs, ss, rl + K < 16);                 \
   }
   LAPLEX_BWD_STEP(1)
   LAPLEX_BWD_STEP(2)
@@ -194,14 +203,18 @@ __device__ __forceinline__ void wave_scan_bwd(float (&B)[C], float s) {
     const float ss = __shfl(s, src);
 #pragma unroll
     for (int c = 0; c < C; ++c) bs[c] = __shfl(B[c], src);
-    scan_join<C, TIE, false>(B, s, bs, ss, (row & 1) == 0);
+    scan_join<C, NT, false>(B, s, bs, ss, (row & 1) == 0);
   }
   {
     const float ss = __shfl(s, 32);
 #pragma unroll
     for (int c = 0; c < C; ++c) bs[c] = __shfl(B[c], 32);
-    scan_join<C, TIE, false>(B, s, bs, ss, row < 2);
+    scan_join<C, NT, false>(B, s, bs, ss, row < 2);
   }
+}
+template <int C, bool TIE = false>
+__device__ __forceinline__ void wave_scan_bwd(float (&B)[C], float s) {
+  wave_scan_bwd_mix<C, TIE ? C : 0>(B, s);
 }
 
 // Deterministic wave sum: row prefix sums by DPP row shifts (lane 15 of each
