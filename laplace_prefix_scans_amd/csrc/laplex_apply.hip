@@ -1650,7 +1650,7 @@ __global__ __launch_bounds__(pbwd_block(C)) void k_pbwd_apply(const float* __res
   constexpr int BLOCK = pbwd_block(C);
   constexpr int NW = BLOCK / kWave;
   constexpr int P = BLOCK * E;
-  __shared__ float s_wf[NW * CC], s_wb[NW * CC], s_wfs[NW], s_wbs[NW];
+  __shared__ float s_wf[NW * 2 * CC], s_wb[NW * 2 * CC], s_wfs[NW], s_wbs[NW];
   const uint32_t M = 8 * m;
   const int tid = threadIdx.x;
   const uint64_t tile = blockIdx.x;
@@ -1672,45 +1672,42 @@ __global__ __launch_bounds__(pbwd_block(C)) void k_pbwd_apply(const float* __res
     load_rows<E, C>(gs, p0, n, m, cc, true, gv);
     phased_quad<E, C>(cs, sn, xv, gv, v);
     {
-      float ct_f[CC], ct_b[CC];
-#pragma unroll
-      for (int j = 0; j < CC; ++j) {
-        ct_f[j] = cfw[tile * M + pbwdcol<C>(m, cc, CC + j)];
-        ct_b[j] = cbw[tile * M + pbwdcol<C>(m, cc, CC + j)];
-      }
-      float F0[E][CC], U0[E][CC];
-      tile_scan_fu<E, CC, NW, true>(ae, v, ct_f, sf, ct_b, sb, s_wf, s_wfs, s_wb, s_wbs, F0, U0);
+      // both decays in one scan of [v | v]: the tie half first (F0, U0),
+      // then the kernel's
+      float v2[E][2 * CC], c2f[2 * CC], c2b[2 * CC];
 #pragma unroll
       for (int e = 0; e < E; ++e)
 #pragma unroll
-        for (int j = 0; j < C; ++j) {
-          const float scx = F0[e][j] - U0[e][j], ssx = F0[e][C + j] - U0[e][C + j];
-          const float scg = F0[e][2 * C + j] - U0[e][2 * C + j], ssg = F0[e][3 * C + j] - U0[e][3 * C + j];
-          acc0[e] = fmaf(gv[e][j], fmaf(cs[e], scx, sn[e] * ssx), acc0[e]);
-          acc0[e] = fmaf(xv[e][j], fmaf(cs[e], scg, sn[e] * ssg), acc0[e]);
-        }
-    }
-    __syncthreads();  // the second scan reuses the wave summaries
-    {
-      float ce_f[CC], ce_b[CC];
+        for (int j = 0; j < CC; ++j) v2[e][j] = v2[e][CC + j] = v[e][j];
 #pragma unroll
       for (int j = 0; j < CC; ++j) {
-        ce_f[j] = cfw[tile * M + pbwdcol<C>(m, cc, j)];
-        ce_b[j] = cbw[tile * M + pbwdcol<C>(m, cc, j)];
+        c2f[j] = cfw[tile * M + pbwdcol<C>(m, cc, CC + j)];
+        c2b[j] = cbw[tile * M + pbwdcol<C>(m, cc, CC + j)];
+        c2f[CC + j] = cfw[tile * M + pbwdcol<C>(m, cc, j)];
+        c2b[CC + j] = cbw[tile * M + pbwdcol<C>(m, cc, j)];
       }
-      float F[E][CC], U[E][CC];
-      tile_scan_fu<E, CC, NW, false>(ae, v, ce_f, sf, ce_b, sb, s_wf, s_wfs, s_wb, s_wbs, F, U);
+      float F2[E][2 * CC], U2[E][2 * CC];
+      tile_scan_fu_mix<E, 2 * CC, NW, CC>(ae, v2, c2f, sf, c2b, sb, s_wf, s_wfs, s_wb, s_wbs, F2, U2);
       float dx[E][C];
 #pragma unroll
       for (int e = 0; e < E; ++e)
 #pragma unroll
         for (int j = 0; j < C; ++j) {
-          const float scx = F[e][j] - U[e][j], ssx = F[e][C + j] - U[e][C + j];
-          const float scg = F[e][2 * C + j] - U[e][2 * C + j], ssg = F[e][3 * C + j] - U[e][3 * C + j];
+          {
+            const float scx = F2[e][j] - U2[e][j], ssx = F2[e][C + j] - U2[e][C + j];
+            const float scg = F2[e][2 * C + j] - U2[e][2 * C + j], ssg = F2[e][3 * C + j] - U2[e][3 * C + j];
+            acc0[e] = fmaf(gv[e][j], fmaf(cs[e], scx, sn[e] * ssx), acc0[e]);
+            acc0[e] = fmaf(xv[e][j], fmaf(cs[e], scg, sn[e] * ssg), acc0[e]);
+          }
+          const float(&F)[2 * CC] = F2[e];  // the kernel's half starts at column CC
+          const float(&U)[2 * CC] = U2[e];
+          constexpr int o = CC;
+          const float scx = F[o + j] - U[o + j], ssx = F[o + C + j] - U[o + C + j];
+          const float scg = F[o + 2 * C + j] - U[o + 2 * C + j], ssg = F[o + 3 * C + j] - U[o + 3 * C + j];
           acc[e] = fmaf(gv[e][j], fmaf(cs[e], scx, sn[e] * ssx), acc[e]);
           acc[e] = fmaf(xv[e][j], fmaf(cs[e], scg, sn[e] * ssg), acc[e]);
-          const float kcx = F[e][j] + U[e][j], ksx = F[e][C + j] + U[e][C + j];
-          const float kcg = F[e][2 * C + j] + U[e][2 * C + j], ksg = F[e][3 * C + j] + U[e][3 * C + j];
+          const float kcx = F[o + j] + U[o + j], ksx = F[o + C + j] + U[o + C + j];
+          const float kcg = F[o + 2 * C + j] + U[o + 2 * C + j], ksg = F[o + 3 * C + j] + U[o + 3 * C + j];
           dph[e] = fmaf(-gv[e][j], fmaf(sn[e], kcx, -cs[e] * ksx), dph[e]);
           dph[e] = fmaf(xv[e][j], fmaf(cs[e], ksg, -sn[e] * kcg), dph[e]);
           dx[e][j] = fmaf(cs[e], kcg, sn[e] * ksg);
@@ -2141,7 +2138,8 @@ __global__ __launch_bounds__(bwd_block(C)) void k_gbwd_apply(const float* __rest
   constexpr int NW = BLOCK / kWave;
   constexpr int P = BLOCK * E;
   __shared__ float s_a[P], s_b[P];
-  __shared__ float s_wf[NW * CC], s_wb[NW * CC], s_wfs[NW], s_wbs[NW];
+  constexpr int SW = C == 1 ? 2 * CC : CC;  // columns of one wave summary
+  __shared__ float s_wf[NW * SW], s_wb[NW * SW], s_wfs[NW], s_wbs[NW];
   const uint32_t M = 4 * m;
   const int tid = threadIdx.x;
   const uint64_t tile = blockIdx.x;
@@ -2170,44 +2168,77 @@ __global__ __launch_bounds__(bwd_block(C)) void k_gbwd_apply(const float* __rest
         v[e][j] = kind[e] == 2 ? xbs[(uint64_t)idx[e] * m + cc * C + j] : 0.f;
         v[e][C + j] = kind[e] == 1 ? gas[(uint64_t)idx[e] * m + cc * C + j] : 0.f;
       }
-    {
-      float ct_f[CC], ct_b[CC];
-#pragma unroll
-      for (int j = 0; j < CC; ++j) {
-        ct_f[j] = cfw[tile * M + bwdcol<C>(m, cc, CC + j)];
-        ct_b[j] = cbw[tile * M + bwdcol<C>(m, cc, CC + j)];
-      }
-      float F0[E][CC], U0[E][CC];
-      tile_scan_fu<E, CC, NW, true>(ae, v, ct_f, sf, ct_b, sb, s_wf, s_wfs, s_wb, s_wbs, F0, U0);
+    if constexpr (C == 1) {
+      // one column: both decays in one scan of [v | v], the tie half first
+      float v2[E][2 * CC], c2f[2 * CC], c2b[2 * CC];
 #pragma unroll
       for (int e = 0; e < E; ++e)
 #pragma unroll
-        for (int j = 0; j < C; ++j) {
-          acc0[e] = fmaf(v[e][C + j], F0[e][j] - U0[e][j], acc0[e]);
-          acc0[e] = fmaf(v[e][j], F0[e][C + j] - U0[e][C + j], acc0[e]);
-        }
-    }
-    __syncthreads();  // the second scan reuses the wave summaries
-    {
-      float ce_f[CC], ce_b[CC];
+        for (int j = 0; j < CC; ++j) v2[e][j] = v2[e][CC + j] = v[e][j];
 #pragma unroll
       for (int j = 0; j < CC; ++j) {
-        ce_f[j] = cfw[tile * M + bwdcol<C>(m, cc, j)];
-        ce_b[j] = cbw[tile * M + bwdcol<C>(m, cc, j)];
+        c2f[j] = cfw[tile * M + bwdcol<C>(m, cc, CC + j)];
+        c2b[j] = cbw[tile * M + bwdcol<C>(m, cc, CC + j)];
+        c2f[CC + j] = cfw[tile * M + bwdcol<C>(m, cc, j)];
+        c2b[CC + j] = cbw[tile * M + bwdcol<C>(m, cc, j)];
       }
-      float F[E][CC], U[E][CC];
-      tile_scan_fu<E, CC, NW, false>(ae, v, ce_f, sf, ce_b, sb, s_wf, s_wfs, s_wb, s_wbs, F, U);
+      float F2[E][2 * CC], U2[E][2 * CC];
+      tile_scan_fu_mix<E, 2 * CC, NW, CC>(ae, v2, c2f, sf, c2b, sb, s_wf, s_wfs, s_wb, s_wbs, F2, U2);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
 #pragma unroll
         for (int j = 0; j < C; ++j) {
-          acc[e] = fmaf(v[e][C + j], F[e][j] - U[e][j], acc[e]);
-          acc[e] = fmaf(v[e][j], F[e][C + j] - U[e][C + j], acc[e]);
+          acc0[e] = fmaf(v[e][C + j], F2[e][j] - U2[e][j], acc0[e]);
+          acc0[e] = fmaf(v[e][j], F2[e][C + j] - U2[e][C + j], acc0[e]);
+          acc[e] = fmaf(v[e][C + j], F2[e][CC + j] - U2[e][CC + j], acc[e]);
+          acc[e] = fmaf(v[e][j], F2[e][CC + C + j] - U2[e][CC + C + j], acc[e]);
         }
         if (kind[e] == 2) {
           float* dr = dxs + (uint64_t)idx[e] * m + cc * C;
 #pragma unroll
-          for (int j = 0; j < C; ++j) dr[j] = F[e][C + j] + U[e][C + j];
+          for (int j = 0; j < C; ++j) dr[j] = F2[e][CC + C + j] + U2[e][CC + C + j];
+        }
+      }
+    } else {
+      {
+        float ct_f[CC], ct_b[CC];
+#pragma unroll
+        for (int j = 0; j < CC; ++j) {
+          ct_f[j] = cfw[tile * M + bwdcol<C>(m, cc, CC + j)];
+          ct_b[j] = cbw[tile * M + bwdcol<C>(m, cc, CC + j)];
+        }
+        float F0[E][CC], U0[E][CC];
+        tile_scan_fu<E, CC, NW, true>(ae, v, ct_f, sf, ct_b, sb, s_wf, s_wfs, s_wb, s_wbs, F0, U0);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+#pragma unroll
+          for (int j = 0; j < C; ++j) {
+            acc0[e] = fmaf(v[e][C + j], F0[e][j] - U0[e][j], acc0[e]);
+            acc0[e] = fmaf(v[e][j], F0[e][C + j] - U0[e][C + j], acc0[e]);
+          }
+      }
+      __syncthreads();  // the second scan reuses the wave summaries
+      {
+        float ce_f[CC], ce_b[CC];
+#pragma unroll
+        for (int j = 0; j < CC; ++j) {
+          ce_f[j] = cfw[tile * M + bwdcol<C>(m, cc, j)];
+          ce_b[j] = cbw[tile * M + bwdcol<C>(m, cc, j)];
+        }
+        float F[E][CC], U[E][CC];
+        tile_scan_fu<E, CC, NW, false>(ae, v, ce_f, sf, ce_b, sb, s_wf, s_wfs, s_wb, s_wbs, F, U);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+#pragma unroll
+          for (int j = 0; j < C; ++j) {
+            acc[e] = fmaf(v[e][C + j], F[e][j] - U[e][j], acc[e]);
+            acc[e] = fmaf(v[e][j], F[e][C + j] - U[e][C + j], acc[e]);
+          }
+          if (kind[e] == 2) {
+            float* dr = dxs + (uint64_t)idx[e] * m + cc * C;
+#pragma unroll
+            for (int j = 0; j < C; ++j) dr[j] = F[e][C + j] + U[e][C + j];
+          }
         }
       }
     }
