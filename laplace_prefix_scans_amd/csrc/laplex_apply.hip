@@ -976,11 +976,12 @@ __global__ __launch_bounds__(apply_block(C)) void k_sym_fu(const float* __restri
   }
 }
 
-constexpr int kSearchSamples = 4096;  // b values staged in LDS per workgroup
+constexpr int kSearchSamples = 4096;  // b values staged in LDS per workgroup (binary search in b_s after)
+constexpr int kSearchSamplesGroup = 8192;  // tree slots when the search ends in a group loaded whole
 constexpr int kSearchBlock = 512;
 constexpr int kSearchItems = 16;      // outputs per thread, one at a time (each holds its group's S values;
                                       // more side by side measured slower: fewer waves per SIMD)
-constexpr uint32_t kSearchGroup = 16; // b values per sample at the least (64 bytes, loaded whole)
+constexpr uint32_t kSearchGroup = 8;  // b values per sample at the least (32 bytes, loaded whole)
 constexpr uint32_t kSearchGroupMax = 64;
 
 // (Fi_{q-1}, U_q) for each interval q = 0..k of the sorted inputs (zero where
@@ -992,13 +993,20 @@ __global__ void k_gen_pairs(const float* __restrict__ fo, const float* __restric
   for (; q <= k; q += stride) fu[q] = make_float2(q > 0 ? fo[q - 1] : 0.f, q < k ? uo[q] : 0.f);
 }
 
-// y (n x m, original order) for the output anchors a: q = #{b_j <= a} by a
-// search over the samples t_g = b_s[min(k, (g+1) S) - 1] (the last of each
-// group of S, a power of two from 16 to 64) in LDS, then a count over the
-// group's S values loaded whole; b_{q-1} and b_q come from the group or the
-// samples.  G = ceil(k / S) <= kSearchSamples.  One column takes (Fi_{q-1},
-// U_q) from fu, more columns the rows of fo and uo.  Non-finite anchors
-// raise the sort workspace's flag.
+// y (n x m, original order) for the output anchors a: q = #{b_j <= a}.  The
+// first G - 1 of the samples t_g = b_s[(g+1) S - 1] (the last of each group
+// of S, a power of two from 8 to 64; G = ceil(k / S) <= kSearchSamplesGroup)
+// sit in LDS as an implicit search tree in heap order (node 1 the root, the
+// children of node i at 2i and 2i+1, in-order = sorted order, +inf past the
+// samples).  Descending it counts the groups lying wholly at or below a in
+// one LDS read per level; the lanes of a wave read one level's nodes, which
+// are consecutive words, so the reads spread over the banks (a binary search
+// over the sorted samples reads words a power of two apart, all in one bank).
+// That group's S values, loaded whole, give the rest of the count and b_q;
+// b_{q-1} comes from the group or, when none of it is at or below a, is the
+// previous group's sample, read from its node.  One
+// column takes (Fi_{q-1}, U_q) from fu, more columns the rows of fo and uo.
+// Non-finite anchors raise the sort workspace's flag.
 template <int S>
 __global__ __launch_bounds__(kSearchBlock) void k_gen_search(const float* __restrict__ a, uint64_t n,
                                                              const float* __restrict__ b_s, uint64_t k, uint32_t G,
@@ -1006,82 +1014,88 @@ __global__ __launch_bounds__(kSearchBlock) void k_gen_search(const float* __rest
                                                              const float2* __restrict__ fu, uint32_t m, float* __restrict__ y,
                                                              uint32_t* __restrict__ header) {
   static_assert(S % 4 == 0 && S <= (int)kSearchGroupMax, "groups of whole 16-byte pieces");
-  constexpr int kSearchBatch = 1;
-  __shared__ float s_t[kSearchSamples];
+  constexpr uint32_t NS = kSearchSamplesGroup;
+  constexpr int L = __builtin_ctz(NS);  // levels of the tree (NS - 1 nodes)
+  static_assert((NS & (NS - 1)) == 0, "a complete tree");
+  __shared__ float s_e[NS];  // tree nodes 1..NS-1
+  // the node of sorted position r (1-based): depth L-1-tz(r), the
+  // (r >> (tz(r)+1))-th node of its level
+  auto node_of = [](uint32_t r) -> uint32_t {
+    const uint32_t tz = (uint32_t)__builtin_ctz(r);
+    return (1u << (L - 1 - tz)) + (r >> (tz + 1));
+  };
   const int tid = threadIdx.x;
-  for (uint32_t g = tid; g < G; g += kSearchBlock) s_t[g] = b_s[std::min<uint64_t>(k, (uint64_t)(g + 1) * S) - 1];
+  for (uint32_t j = tid; j + 1 < NS; j += kSearchBlock) {
+    s_e[node_of(j + 1)] = j + 1 < G ? b_s[(uint64_t)(j + 1) * S - 1] : __builtin_inff();
+  }
   __syncthreads();
   const uint64_t base = (uint64_t)blockIdx.x * (kSearchBlock * kSearchItems);
   uint32_t bad = 0;
-  for (int b0 = 0; b0 < kSearchItems; b0 += kSearchBatch) {
-    float av[kSearchBatch];
-    uint32_t cnt[kSearchBatch];
+  // With small groups every output anchor of this thread is loaded up front,
+  // so that no search waits on HBM for its anchor, and the outputs are
+  // unrolled; larger groups take the registers that this would need.
+  constexpr bool kAhead = S <= 16;
+  constexpr int kUnroll = kAhead ? kSearchItems : 1;
+  float a_all[kAhead ? kSearchItems : 1];
+  if constexpr (kAhead) {
 #pragma unroll
-    for (int it = 0; it < kSearchBatch; ++it) {
-      const uint64_t i = base + (uint64_t)(b0 + it) * kSearchBlock + tid;
-      av[it] = a[i < n ? i : n - 1];
-      bad |= (i < n && bits_nonfinite(__float_as_uint(av[it]))) ? 1u : 0u;
-      cnt[it] = 0;
+    for (int it = 0; it < kSearchItems; ++it) {
+      const uint64_t i = base + (uint64_t)it * kSearchBlock + tid;
+      a_all[it] = a[i < n ? i : n - 1];
     }
-    // groups lying wholly at or below a (samples <= a), by descending powers
-    // of two (branch-free: the step is taken or not by a select)
+  }
+#pragma unroll kUnroll
+  for (int it = 0; it < kSearchItems; ++it) {
+    const uint64_t i = base + (uint64_t)it * kSearchBlock + tid;
+    float av;
+    if constexpr (kAhead)
+      av = a_all[it];
+    else
+      av = a[i < n ? i : n - 1];
+    bad |= (i < n && bits_nonfinite(__float_as_uint(av))) ? 1u : 0u;
+    uint32_t node = 1;
 #pragma unroll
-    for (uint32_t step = kSearchSamples; step >= 1; step >>= 1) {
+    for (int l = 0; l < L; ++l) node = 2 * node + (s_e[node] <= av ? 1u : 0u);
+    const uint32_t cnt = node - NS;  // groups wholly at or below a: at most G - 1
+    // that group's values, loaded whole (rows past k read as +inf)
+    const uint64_t p = (uint64_t)cnt * S;
+    float gv[S];
+    if (p + S <= k) {
 #pragma unroll
-      for (int it = 0; it < kSearchBatch; ++it) {
-        const uint32_t t = cnt[it] + step;
-        const float v = s_t[(t < G ? t : G) - 1];
-        cnt[it] = (t <= G && v <= av[it]) ? t : cnt[it];
+      for (int u = 0; u < S / 4; ++u) {
+        const float4 q4 = reinterpret_cast<const float4*>(b_s + p)[u];
+        gv[4 * u] = q4.x;
+        gv[4 * u + 1] = q4.y;
+        gv[4 * u + 2] = q4.z;
+        gv[4 * u + 3] = q4.w;
       }
+    } else {
+#pragma unroll
+      for (int u = 0; u < S; ++u) gv[u] = p + u < k ? b_s[p + u] : __builtin_inff();
     }
-    // the next group's values, loaded whole (rows past k read as +inf; with
-    // every group at or below a there is none and q = k)
-    float gv[kSearchBatch][S];
+    uint32_t c2 = 0;
+    float bl = cnt > 0 ? s_e[node_of(cnt)] : 0.f, br = 0.f;
 #pragma unroll
-    for (int it = 0; it < kSearchBatch; ++it) {
-      const uint64_t p = (uint64_t)(cnt[it] < G ? cnt[it] : G - 1) * S;
-      if (p + S <= k) {
-#pragma unroll
-        for (int u = 0; u < S / 4; ++u) {
-          const float4 q4 = reinterpret_cast<const float4*>(b_s + p)[u];
-          gv[it][4 * u] = q4.x;
-          gv[it][4 * u + 1] = q4.y;
-          gv[it][4 * u + 2] = q4.z;
-          gv[it][4 * u + 3] = q4.w;
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < S; ++u) gv[it][u] = p + u < k ? b_s[p + u] : __builtin_inff();
-      }
+    for (int u = 0; u < S; ++u) {
+      const bool le = gv[u] <= av;
+      c2 += le ? 1u : 0u;
+      bl = le ? gv[u] : bl;  // the last value <= a
     }
 #pragma unroll
-    for (int it = 0; it < kSearchBatch; ++it) {
-      const uint64_t i = base + (uint64_t)(b0 + it) * kSearchBlock + tid;
-      const bool all = cnt[it] >= G;  // every b at or below a
-      uint32_t c2 = 0;
-      float bl = cnt[it] > 0 ? s_t[(cnt[it] < G ? cnt[it] : G) - 1] : 0.f, br = 0.f;
-#pragma unroll
-      for (int u = 0; u < S; ++u) {
-        const bool le = gv[it][u] <= av[it];
-        c2 += le ? 1u : 0u;
-        bl = (le && !all) ? gv[it][u] : bl;  // the last value <= a
-      }
-#pragma unroll
-      for (int u = S - 1; u >= 0; --u) br = gv[it][u] > av[it] ? gv[it][u] : br;  // the first value > a
-      const uint64_t q = all ? k : (uint64_t)cnt[it] * S + c2;  // #{b_j <= a}
-      const bool left = q > 0, right = q < k;
-      const float wl = left ? decay(bl - av[it]) : 0.f;
-      const float wr = right ? decay(av[it] - br) : 0.f;
-      if (i >= n) continue;
-      if (m == 1) {
-        const float2 f = fu[q];
-        y[i] = fmaf(wr, f.y, wl * f.x);
-      } else {
-        const uint64_t ql = left ? q - 1 : 0, qr = right ? q : k - 1;
-        for (uint32_t c = 0; c < m; ++c) {
-          const float yl = left ? wl * fo[ql * m + c] : 0.f;
-          y[i * m + c] = right ? fmaf(wr, uo[qr * m + c], yl) : yl;
-        }
+    for (int u = S - 1; u >= 0; --u) br = gv[u] > av ? gv[u] : br;  // the first value > a
+    const uint64_t q = p + c2;  // #{b_j <= a}
+    const bool left = q > 0, right = q < k;
+    const float wl = left ? decay(bl - av) : 0.f;
+    const float wr = right ? decay(av - br) : 0.f;
+    if (i >= n) continue;
+    if (m == 1) {
+      const float2 f = fu[q];
+      y[i] = fmaf(wr, f.y, wl * f.x);
+    } else {
+      const uint64_t ql = left ? q - 1 : 0, qr = right ? q : k - 1;
+      for (uint32_t c = 0; c < m; ++c) {
+        const float yl = left ? wl * fo[ql * m + c] : 0.f;
+        y[i * m + c] = right ? fmaf(wr, uo[qr * m + c], yl) : yl;
       }
     }
   }
@@ -1149,7 +1163,9 @@ static hipError_t run_general_search(const ApplyWorkspace& w, float* fo, float* 
                 k_sym_fu<C><<<dim3((unsigned)T), dim3(apply_block(C)), 0, s>>>(b_s, w.xs, w.cf, w.cb, w.tanch, k, m, T, fo, uo, vec));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   uint64_t S = kSearchGroup;
-  while ((k + S - 1) / S > (uint64_t)kSearchSamples) S <<= 1;
+  while ((k + S - 1) / S > (uint64_t)kSearchSamplesGroup) S <<= 1;
+  if (S > kSearchGroupMax)
+    while ((k + S - 1) / S > (uint64_t)kSearchSamples) S <<= 1;
   const uint32_t G = (uint32_t)((k + S - 1) / S);
   const unsigned blocks = (unsigned)((n + (uint64_t)kSearchBlock * kSearchItems - 1) / ((uint64_t)kSearchBlock * kSearchItems));
   if (m == 1 && S <= kSearchGroupMax) {
@@ -1158,7 +1174,9 @@ static hipError_t run_general_search(const ApplyWorkspace& w, float* fo, float* 
   }
 #define LAPLEX_SEARCH(SS)                                                                                             \
   LAPLEX_LAUNCH("k_gen_search", n, s, k_gen_search<SS><<<blocks, kSearchBlock, 0, s>>>(a, n, b_s, k, G, fo, uo, fu, m, y, header))
-  if (S == 16)
+  if (S == 8)
+    LAPLEX_SEARCH(8);
+  else if (S == 16)
     LAPLEX_SEARCH(16);
   else if (S == 32)
     LAPLEX_SEARCH(32);

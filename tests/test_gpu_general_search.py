@@ -3,9 +3,10 @@ which sorts only the input anchors b, runs the two scans over sorted b and
 lets every output anchor find its interval in b by binary search, against
 the float64 oracle (the pages' u/v form) and against the sort-handle path.
 
-Cases cover the search's two levels (a sample of b staged in LDS, then one
-group of b): k from 1 to above 4096 samples, ties between a and b (b before
-a), outputs below and above every input, and k larger than n."""
+Cases cover the search's two levels (a sample of b staged in LDS as a search
+tree, then one group of b): k from 1 to past the largest group size, every
+group size at both ends of its range, ties between a and b (b before a),
+outputs below and above every input, and k larger than n."""
 import numpy as np
 import pytest
 
@@ -36,9 +37,12 @@ def _case(n, k, m, seed, kind):
     return a, b, x
 
 
-# k: groups of 16 (k <= 2^16), 32, 64 (k <= 2^18) and the wide fallback above
+# k: groups of 8 (k <= 2^16), 16 (k <= 2^17), 32, 64 (k <= 2^19) and the
+# wide fallback above
 CASES = [(1, 1, 1), (5, 1, 1), (1, 5, 2), (1000, 37, 1), (70001, 4096, 1), (70001, 4097, 2), (300000, 70001, 3),
-         (200000, (1 << 16) + 5, 8), (150000, 200000, 1), (50000, 300000, 1), (4097, 8193, 4)]
+         (200000, (1 << 16) + 5, 8), (150000, 200000, 1), (50000, 300000, 1), (4097, 8193, 4),
+         (30000, 1 << 16, 1), (30000, 1 << 17, 1), (20000, (1 << 17) + 1, 2), (30000, 1 << 19, 1),
+         (40000, (1 << 19) + 3, 1), (20000, 700001, 2)]
 
 
 @pytest.mark.parametrize("n,k,m", CASES)
