@@ -209,7 +209,7 @@ SortGeneralWorkspace carve_sort_general(void* ws, uint64_t k, uint32_t m, size_t
   w.perm_b = c.take<uint32_t>(k * 4);
   w.fo = c.take<float>(k * m * 4);
   w.uo = c.take<float>(k * m * 4);
-  w.fu = m == 1 ? c.take<float2>((k + 1) * 8) : nullptr;
+  w.fu = m == 1 ? c.take<float2>(search_table_bytes(k)) : nullptr;
   char* apply_base = c.take<char>(0);
   size_t apply_total = 0;
   w.apply = carve_apply(ws ? apply_base : nullptr, k, k, k, m, Variant::Sym, false, &apply_total);

@@ -977,7 +977,7 @@ __global__ __launch_bounds__(apply_block(C)) void k_sym_fu(const float* __restri
 }
 
 constexpr int kSearchSamples = 4096;  // b values staged in LDS per workgroup (binary search in b_s after)
-constexpr int kSearchSamplesGroup = 8192;  // tree slots when the search ends in a group loaded whole
+constexpr int kSearchSamplesGroup = kSearchTree;  // tree slots when the search ends in a group loaded whole
 constexpr int kSearchBlock = 512;
 constexpr int kSearchItems = 16;      // outputs per thread, one at a time (each holds its group's S values;
                                       // more side by side measured slower: fewer waves per SIMD)
@@ -987,10 +987,24 @@ constexpr uint32_t kSearchGroupMax = 64;
 // (Fi_{q-1}, U_q) for each interval q = 0..k of the sorted inputs (zero where
 // the neighbour does not exist), one column: an output in interval q reads
 // both with one load.
-__global__ void k_gen_pairs(const float* __restrict__ fo, const float* __restrict__ uo, uint64_t k, float2* __restrict__ fu) {
-  uint64_t q = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// The same launch writes the search's sample tree (see k_gen_search) in heap
+// order once, so that every search workgroup copies it contiguously instead
+// of gathering one sample per group of b.
+__device__ __forceinline__ uint32_t heap_node(uint32_t r, int L) {
+  // sorted position r (1-based) of a complete tree of 2^L - 1 nodes: depth
+  // L-1-tz(r), the (r >> (tz(r)+1))-th node of its level
+  const uint32_t tz = (uint32_t)__builtin_ctz(r);
+  return (1u << (L - 1 - tz)) + (r >> (tz + 1));
+}
+__global__ void k_gen_pairs(const float* __restrict__ fo, const float* __restrict__ uo, uint64_t k, float2* __restrict__ fu,
+                            const float* __restrict__ b_s, uint64_t S, uint32_t G, float* __restrict__ tree) {
+  constexpr uint32_t NS = kSearchTree;
+  const uint64_t t0 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  for (; q <= k; q += stride) fu[q] = make_float2(q > 0 ? fo[q - 1] : 0.f, q < k ? uo[q] : 0.f);
+  for (uint64_t q = t0; q <= k; q += stride) fu[q] = make_float2(q > 0 ? fo[q - 1] : 0.f, q < k ? uo[q] : 0.f);
+  if (tree != nullptr)
+    for (uint64_t j = t0; j + 1 < NS; j += stride)
+      tree[heap_node((uint32_t)j + 1, __builtin_ctz(NS))] = j + 1 < G ? b_s[(j + 1) * S - 1] : __builtin_inff();
 }
 
 // y (n x m, original order) for the output anchors a: q = #{b_j <= a}.  The
@@ -1011,22 +1025,20 @@ template <int S>
 __global__ __launch_bounds__(kSearchBlock) void k_gen_search(const float* __restrict__ a, uint64_t n,
                                                              const float* __restrict__ b_s, uint64_t k, uint32_t G,
                                                              const float* __restrict__ fo, const float* __restrict__ uo,
-                                                             const float2* __restrict__ fu, uint32_t m, float* __restrict__ y,
-                                                             uint32_t* __restrict__ header) {
+                                                             const float2* __restrict__ fu, const float* __restrict__ tree, uint32_t m,
+                                                             float* __restrict__ y, uint32_t* __restrict__ header) {
   static_assert(S % 4 == 0 && S <= (int)kSearchGroupMax, "groups of whole 16-byte pieces");
   constexpr uint32_t NS = kSearchSamplesGroup;
   constexpr int L = __builtin_ctz(NS);  // levels of the tree (NS - 1 nodes)
   static_assert((NS & (NS - 1)) == 0, "a complete tree");
   __shared__ float s_e[NS];  // tree nodes 1..NS-1
-  // the node of sorted position r (1-based): depth L-1-tz(r), the
-  // (r >> (tz(r)+1))-th node of its level
-  auto node_of = [](uint32_t r) -> uint32_t {
-    const uint32_t tz = (uint32_t)__builtin_ctz(r);
-    return (1u << (L - 1 - tz)) + (r >> (tz + 1));
-  };
+  auto node_of = [](uint32_t r) -> uint32_t { return heap_node(r, L); };
   const int tid = threadIdx.x;
-  for (uint32_t j = tid; j + 1 < NS; j += kSearchBlock) {
-    s_e[node_of(j + 1)] = j + 1 < G ? b_s[(uint64_t)(j + 1) * S - 1] : __builtin_inff();
+  if (tree != nullptr) {  // the tree made once by k_gen_pairs (16-byte aligned; slot 0 unused)
+    for (uint32_t j = tid; j < NS / 4; j += kSearchBlock)
+      reinterpret_cast<float4*>(s_e)[j] = reinterpret_cast<const float4*>(tree)[j];
+  } else {
+    for (uint32_t j = tid; j + 1 < NS; j += kSearchBlock) s_e[node_of(j + 1)] = j + 1 < G ? b_s[(uint64_t)(j + 1) * S - 1] : __builtin_inff();
   }
   __syncthreads();
   const uint64_t base = (uint64_t)blockIdx.x * (kSearchBlock * kSearchItems);
@@ -1168,12 +1180,16 @@ static hipError_t run_general_search(const ApplyWorkspace& w, float* fo, float* 
     while ((k + S - 1) / S > (uint64_t)kSearchSamples) S <<= 1;
   const uint32_t G = (uint32_t)((k + S - 1) / S);
   const unsigned blocks = (unsigned)((n + (uint64_t)kSearchBlock * kSearchItems - 1) / ((uint64_t)kSearchBlock * kSearchItems));
+  // one column: the pairs and the sample tree, after the pairs in fu's table
+  float* tree = m == 1 && S <= kSearchGroupMax ? search_tree(fu, k) : nullptr;
   if (m == 1 && S <= kSearchGroupMax) {
-    LAPLEX_LAUNCH("k_gen_pairs", k + 1, s, k_gen_pairs<<<(unsigned)std::min<uint64_t>((k + 256) / 256, 4096), 256, 0, s>>>(fo, uo, k, fu));
+    LAPLEX_LAUNCH("k_gen_pairs", k + 1, s,
+                  k_gen_pairs<<<(unsigned)std::min<uint64_t>((std::max<uint64_t>(k + 1, kSearchTree) + 255) / 256, 4096), 256, 0, s>>>(
+                      fo, uo, k, fu, b_s, S, G, tree));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
 #define LAPLEX_SEARCH(SS)                                                                                             \
-  LAPLEX_LAUNCH("k_gen_search", n, s, k_gen_search<SS><<<blocks, kSearchBlock, 0, s>>>(a, n, b_s, k, G, fo, uo, fu, m, y, header))
+  LAPLEX_LAUNCH("k_gen_search", n, s, k_gen_search<SS><<<blocks, kSearchBlock, 0, s>>>(a, n, b_s, k, G, fo, uo, fu, tree, m, y, header))
   if (S == 8)
     LAPLEX_SEARCH(8);
   else if (S == 16)

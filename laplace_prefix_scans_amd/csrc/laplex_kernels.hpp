@@ -129,9 +129,15 @@ hipError_t apply_sym_presorted(const ApplyWorkspace& w, const float* a_s, const 
                                hipStream_t s);
 // General operator from unsorted output anchors a (n) and sorted inputs
 // b_s (k >= 1, sort handle perm_b): the scans run over b alone (Fi into fo,
-// U into uo, k x m each; for one column also (Fi_{q-1}, U_q) per interval
-// into fu, k + 1) and each output searches its interval in b_s; y in the
-// original order of a.  Non-finite a raise kFlagNonFinite in header.
+// U into uo, k x m each; for one column also a table in fu of
+// search_table_bytes(k): (Fi_{q-1}, U_q) per interval, k + 1, then the
+// search's sample tree) and each output searches its interval in b_s; y in
+// the original order of a.  Non-finite a raise kFlagNonFinite in header.
+constexpr int kSearchTree = 8192;  // slots of the search's sample tree (a power of two)
+inline size_t search_table_bytes(uint64_t k) { return (size_t)(k + 1) * 8 + 256 + (size_t)kSearchTree * 4; }
+inline float* search_tree(float2* fu, uint64_t k) {
+  return reinterpret_cast<float*>((reinterpret_cast<uintptr_t>(fu + k + 1) + 255) & ~uintptr_t(255));
+}
 hipError_t apply_general_search(const ApplyWorkspace& w, float* fo, float* uo, float2* fu, const float* a, uint64_t n, const float* b_s,
                                 const uint32_t* perm_b, uint64_t k, uint32_t m, const float* x, float* y, uint32_t* header,
                                 hipStream_t s);
