@@ -981,6 +981,9 @@ constexpr int kSearchSamplesGroup = kSearchTree;  // tree slots when the search 
 constexpr int kSearchBlock = 512;
 constexpr int kSearchItems = 16;      // outputs per thread, one at a time (each holds its group's S values;
                                       // more side by side measured slower: fewer waves per SIMD)
+// outputs per thread of k_gen_search: more for the smallest groups, which
+// leave registers for them (fewer workgroups copy the sample tree)
+constexpr int search_items(int S) { return S <= 8 ? 32 : kSearchItems; }
 constexpr uint32_t kSearchGroup = 8;  // b values per sample at the least (32 bytes, loaded whole)
 constexpr uint32_t kSearchGroupMax = 64;
 
@@ -1041,23 +1044,24 @@ __global__ __launch_bounds__(kSearchBlock) void k_gen_search(const float* __rest
     for (uint32_t j = tid; j + 1 < NS; j += kSearchBlock) s_e[node_of(j + 1)] = j + 1 < G ? b_s[(uint64_t)(j + 1) * S - 1] : __builtin_inff();
   }
   __syncthreads();
-  const uint64_t base = (uint64_t)blockIdx.x * (kSearchBlock * kSearchItems);
+  constexpr int IT = search_items(S);
+  const uint64_t base = (uint64_t)blockIdx.x * (kSearchBlock * IT);
   uint32_t bad = 0;
   // With small groups every output anchor of this thread is loaded up front,
   // so that no search waits on HBM for its anchor, and the outputs are
   // unrolled; larger groups take the registers that this would need.
   constexpr bool kAhead = S <= 16;
-  constexpr int kUnroll = kAhead ? kSearchItems : 1;
-  float a_all[kAhead ? kSearchItems : 1];
+  constexpr int kUnroll = kAhead ? IT : 1;
+  float a_all[kAhead ? IT : 1];
   if constexpr (kAhead) {
 #pragma unroll
-    for (int it = 0; it < kSearchItems; ++it) {
+    for (int it = 0; it < IT; ++it) {
       const uint64_t i = base + (uint64_t)it * kSearchBlock + tid;
       a_all[it] = a[i < n ? i : n - 1];
     }
   }
 #pragma unroll kUnroll
-  for (int it = 0; it < kSearchItems; ++it) {
+  for (int it = 0; it < IT; ++it) {
     const uint64_t i = base + (uint64_t)it * kSearchBlock + tid;
     float av;
     if constexpr (kAhead)
@@ -1179,7 +1183,8 @@ static hipError_t run_general_search(const ApplyWorkspace& w, float* fo, float* 
   if (S > kSearchGroupMax)
     while ((k + S - 1) / S > (uint64_t)kSearchSamples) S <<= 1;
   const uint32_t G = (uint32_t)((k + S - 1) / S);
-  const unsigned blocks = (unsigned)((n + (uint64_t)kSearchBlock * kSearchItems - 1) / ((uint64_t)kSearchBlock * kSearchItems));
+  const uint64_t per_block = (uint64_t)kSearchBlock * (S <= kSearchGroupMax ? search_items((int)S) : kSearchItems);
+  const unsigned blocks = (unsigned)((n + per_block - 1) / per_block);
   // one column: the pairs and the sample tree, after the pairs in fu's table
   float* tree = m == 1 && S <= kSearchGroupMax ? search_tree(fu, k) : nullptr;
   if (m == 1 && S <= kSearchGroupMax) {
