@@ -14,7 +14,7 @@ the indices between the two formulas; the first index is always the output).
 """
 from __future__ import annotations
 
-from typing import Optional, Sequence
+from typing import Optional
 
 import numpy as np
 
@@ -53,50 +53,35 @@ def dense_envelope(a, x, b=None) -> np.ndarray:
     return dense_apply(a, np.abs(np.asarray(x, np.float64)), b=b)
 
 
-def dense_rows(rows: Sequence[int], a, x, b=None, phi=None, psi=None, col_chunk: int = 1 << 22):
-    """Selected rows of y and of K0|x| by the plain definition, for inputs too large
-    for a full dense product.  Returns (y_rows, env_rows), each len(rows) x m."""
-    rows = np.asarray(rows, np.int64)
-    a = np.asarray(a).ravel()
-    b = a if b is None else np.asarray(b).ravel()
-    ai = a[rows].astype(np.float64)
-    phi_i = None
-    if phi is not None:
-        phi = np.asarray(phi).ravel()
-        psi = phi if psi is None else np.asarray(psi).ravel()
-        phi_i = phi[rows].astype(np.float64)
-    x2 = np.asarray(x).reshape(b.size, -1)
-    m = x2.shape[1]
-    y = np.zeros((rows.size, m), np.float64)
-    env = np.zeros((rows.size, m), np.float64)
-    for lo in range(0, b.size, col_chunk):
-        hi = min(b.size, lo + col_chunk)
-        bj = b[lo:hi].astype(np.float64)
-        xc = x2[lo:hi].astype(np.float64)
-        env += _weights(ai, bj) @ np.abs(xc)
-        if phi_i is None:
-            y += _weights(ai, bj) @ xc
-        else:
-            y += _weights(ai, bj, phi_i, psi[lo:hi].astype(np.float64)) @ xc
-    return y, env
-
-
 def normwise_error(y, y_ref, env, env_scale: Optional[np.ndarray] = None) -> float:
     """max over columns c of ||y_c - y_ref_c||_inf / ||(K0|x|)_c||_inf.
 
-    ``env_scale`` may supply the per-column denominators directly (e.g. the
-    maximum over sampled rows, which is a lower bound and so a stricter test)."""
-    y = np.asarray(y, np.float64).reshape(np.shape(y_ref))
-    y_ref = np.asarray(y_ref, np.float64)
-    if y_ref.ndim == 1:
-        y_ref = y_ref[:, None]
-        y = y.reshape(y_ref.shape)
-    num = np.max(np.abs(y - y_ref), axis=0)
+    y, y_ref and env are (rows,) or (rows, m) with the same shape ((rows,)
+    and (rows, 1) count as the same); anything else raises ValueError.  A
+    column whose envelope is zero (x_c = 0) is measured by its absolute
+    error.  ``env_scale`` may supply the per-column denominators directly
+    (e.g. the maximum over sampled rows, which is a lower bound and so a
+    stricter test); env is then not used."""
+    def cols(v, what):
+        v = np.asarray(v, np.float64)
+        if v.ndim == 1:
+            return v[:, None]
+        if v.ndim != 2:
+            raise ValueError("%s must be 1-D or 2-D, got shape %s" % (what, v.shape))
+        return v
+    y2, r2 = cols(y, "y"), cols(y_ref, "y_ref")
+    if y2.shape != r2.shape:
+        raise ValueError("y has shape %s, y_ref %s" % (np.shape(y), np.shape(y_ref)))
+    num = np.max(np.abs(y2 - r2), axis=0) if r2.shape[0] else np.zeros(r2.shape[1])
     if env_scale is None:
-        env = np.asarray(env, np.float64).reshape(y_ref.shape)
-        den = np.max(np.abs(env), axis=0)
+        e2 = cols(env, "env")
+        if e2.shape != r2.shape:
+            raise ValueError("env has shape %s, y_ref %s" % (np.shape(env), np.shape(y_ref)))
+        den = np.max(np.abs(e2), axis=0) if e2.shape[0] else np.zeros(e2.shape[1])
     else:
         den = np.asarray(env_scale, np.float64).ravel()
+        if den.size != r2.shape[1]:
+            raise ValueError("env_scale has %d values for %d columns" % (den.size, r2.shape[1]))
     den = np.where(den > 0, den, 1.0)
     return float(np.max(num / den)) if num.size else 0.0
 

@@ -52,10 +52,10 @@ def assert_perm_is_stable_argsort(a: np.ndarray, perm: np.ndarray, a_sorted: np.
     assert np.all(perm[1:][ties] > perm[:-1][ties]), "equal anchors out of input order"
 
 
-def describe_nonfinite(y: np.ndarray, perm: np.ndarray, rerun=None) -> str:
-    """Where the non-finite rows of y (original order) sit in sorted order,
-    and whether a second identical call (`rerun`, returning y again) repeats
-    them -- so that a failure names its rows, tiles and reproducibility."""
+def describe_nonfinite(y: np.ndarray, perm: np.ndarray, tile_rows: int = 0) -> str:
+    """Where the non-finite rows of y (original order) sit in sorted order:
+    their sorted positions, the tiles those fall in (tile_rows rows per tile,
+    when given) and the columns involved, so that a failure names its rows."""
     y2 = y.reshape(y.shape[0], -1)
     bad = np.nonzero(~np.isfinite(y2).all(axis=1))[0]
     if bad.size == 0:
@@ -65,9 +65,6 @@ def describe_nonfinite(y: np.ndarray, perm: np.ndarray, rerun=None) -> str:
     pos = np.sort(pinv[bad])
     msg = "%d non-finite rows; sorted positions %s; columns %s" % (
         bad.size, pos[:8].tolist(), np.unique(np.nonzero(~np.isfinite(y2[bad]))[1]).tolist()[:8])
-    if rerun is not None:
-        again = rerun().reshape(y2.shape)
-        msg += "; a second call gives %d non-finite rows, %s" % (
-            int((~np.isfinite(again).all(axis=1)).sum()),
-            "identical bits" if np.array_equal(again.view(np.uint32), y2.view(np.uint32)) else "different bits")
+    if tile_rows:
+        msg += "; tiles %s" % np.unique(pos // tile_rows)[:8].tolist()
     return msg

@@ -658,7 +658,44 @@ def pin_phased_backward(lib):
     assert np.all(env >= np.abs(dar)) and np.all(env >= np.abs(dpr))
 
 
+# ----------------------------------------------------------------------------- error measure
+
+def _normwise_cases():
+    with open(os.path.join(GOLDEN, "normwise_examples.json")) as f:
+        return json.load(f)["cases"]
+
+
+def pin_normwise_error(lib):
+    """The parity tests' error measure against hand-computed values: per-column
+    denominators, explicit denominators, zero envelopes, the worst row, vectors,
+    and the envelope K0|x| of a two-anchor operator; shape mismatches raise."""
+    for case in _normwise_cases():
+        if "a" in case:
+            a = np.array(case["a"], np.float32)
+            x = np.array(case["x"], np.float32)
+            env = odense.dense_envelope(a, x)
+            env_hand = np.array([[sum(c * math.exp(-d) for c, d in col) for col in row] for row in case["env_terms"]])
+            _close(env, env_hand, 1e-15, "envelope " + case["name"])
+            y_ref = odense.dense_apply(a, x)
+            y = y_ref + np.array(case["delta"])
+            want = case["want_num"] / sum(c * math.exp(-d) for c, d in case["want_den_terms"])
+            got = odense.normwise_error(y, y_ref, env)
+        else:
+            scale = np.array(case["env_scale"]) if "env_scale" in case else None
+            got = odense.normwise_error(np.array(case["y"]), np.array(case["y_ref"]), np.array(case["env"]),
+                                        env_scale=scale)
+            want = case["want"]
+        assert abs(got - want) <= 1e-15 * max(1.0, abs(want)), "%s: %r, expected %r" % (case["name"], got, want)
+    for y, y_ref in ((np.zeros((3, 2)), np.zeros((2, 3))), (np.zeros(4), np.zeros(3)), (np.zeros((4, 2)), np.zeros(8))):
+        try:
+            odense.normwise_error(y, y_ref, np.ones_like(y_ref))
+        except ValueError:
+            continue
+        raise AssertionError("shape mismatch %s vs %s accepted" % (y.shape, y_ref.shape))
+
+
 ALL_PINS = [
+    pin_normwise_error,
     pin_sort_definition,
     pin_sort_rejects_nonfinite,
     pin_hand_examples,

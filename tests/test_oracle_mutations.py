@@ -142,3 +142,45 @@ def test_phased_backward_mutant_is_caught(name, monkeypatch, oracle_lib):
     monkeypatch.setattr(odense, attr, fn)
     failed = _any_pin_fails(oracle_lib)
     assert failed, "planted mistake %s in the phased backward passed every pin" % name
+
+
+def _nw_mutant(kind):
+    """A copy of the normwise error measure with one planted mistake."""
+    def f(y, y_ref, env, env_scale=None):
+        def cols(v):
+            v = np.asarray(v, np.float64)
+            return v[:, None] if v.ndim == 1 else v
+        if kind == "reshapes_silently":
+            y = np.asarray(y, np.float64).reshape(np.shape(y_ref))
+        y2, r2 = cols(y), cols(y_ref)
+        if y2.shape != r2.shape:
+            raise ValueError("shape")
+        diff = (y2 - r2) if kind == "signed_numerator" else np.abs(y2 - r2)
+        num = np.mean(diff, axis=0) if kind == "mean_over_rows" else np.max(diff, axis=0)
+        e2 = np.abs(np.asarray(env, np.float64).reshape(r2.shape))
+        den = np.max(e2, axis=0)
+        if kind == "global_denominator":
+            den = np.full_like(den, np.max(e2))
+        if kind == "columns_swapped":
+            den = den[::-1]
+        if env_scale is not None and kind != "ignores_env_scale":
+            den = np.asarray(env_scale, np.float64).ravel()
+        if kind != "zero_envelope_divides":
+            den = np.where(den > 0, den, 1.0)
+        if kind == "vacuous":
+            return 0.0
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q = num / den
+        return float(np.sum(q) if kind == "sum_over_columns" else np.max(q))
+    return f
+
+
+NORMWISE_MUTANTS = ["vacuous", "global_denominator", "ignores_env_scale", "mean_over_rows", "signed_numerator",
+                    "columns_swapped", "sum_over_columns", "zero_envelope_divides", "reshapes_silently"]
+
+
+@pytest.mark.parametrize("kind", NORMWISE_MUTANTS)
+def test_normwise_mutant_is_caught(kind, monkeypatch, oracle_lib):
+    monkeypatch.setattr(odense, "normwise_error", _nw_mutant(kind))
+    failed = _any_pin_fails(oracle_lib)
+    assert failed, "planted mistake %s in the error measure passed every pin" % kind
