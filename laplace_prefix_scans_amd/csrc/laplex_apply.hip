@@ -22,423 +22,9 @@
 //      shuffles, cross-wave combine through LDS, tile carry, and the result
 //      written back to original order.
 #include "laplex_kernels.hpp"
+#include "laplex_scan.hpp"
 
 namespace laplex {
-
-// summary/carry column of injected column j of chunk cc (phased: cos part at
-// [0, m), sin part at [m, 2m))
-template <int C, bool PH>
-__device__ __forceinline__ uint32_t sumcol(uint32_t m, uint32_t cc, int j) {
-  if (!PH) return cc * C + (uint32_t)j;
-  return (j < C) ? cc * C + (uint32_t)j : m + cc * C + (uint32_t)(j - C);
-}
-
-// Sum CC values over the block; totals land in out0[col(j)], out1[col(j)].
-template <int CC, int NW>
-__device__ __forceinline__ void block_sum2(float (&a)[CC], float (&b)[CC], float* s_red /* [2][NW][CC] */, int& jcol_valid) {
-  const int lane = lane_id(), wid = threadIdx.x / kWave;
-  wave_sum<CC>(a);
-  wave_sum<CC>(b);
-  if (lane == 0) {
-#pragma unroll
-    for (int j = 0; j < CC; ++j) {
-      s_red[(0 * NW + wid) * CC + j] = a[j];
-      s_red[(1 * NW + wid) * CC + j] = b[j];
-    }
-  }
-  __syncthreads();
-  jcol_valid = threadIdx.x < CC;
-}
-
-// ---------------------------------------------------------------- tile scan
-// In: v[e][j] injections of this thread's E consecutive elements (anchors
-// ae[], nondecreasing across the whole tile); carries into the tile from the
-// left (cf, anchored at sf) and right (cb, anchored at sb).
-// Out: F[e][j] the strict forward value (earlier elements only, tied ones
-// included), U[e][j] the inclusive backward value.  Columns [0, NT) scan with
-// the tie decay (see decay_m), columns [NT, CC) with the kernel's decay, in
-// one pass (the anchor differences, wave exchanges and barriers shared).
-template <int E, int CC, int NW, int NT>
-__device__ __forceinline__ void tile_scan_fu_mix(const float (&ae)[E], const float (&v)[E][CC], const float (&cf)[CC],
-                                                 float sf, const float (&cb)[CC], float sb, float* s_wf, float* s_wfs,
-                                                 float* s_wb, float* s_wbs, float (&F)[E][CC], float (&Uo)[E][CC]) {
-  const int lane = lane_id(), wid = threadIdx.x / kWave;
-  // the decay of column j for anchor difference x
-  auto dk = [](float x, int j) -> float { return j < NT ? decay_m<true>(x) : decay_m<false>(x); };
-  float dt[E], de[E];  // d[e] = exp(ae[e-1] - ae[e]) for e >= 1, tie and kernel
-#pragma unroll
-  for (int e = 1; e < E; ++e) {
-    dt[e] = NT > 0 ? decay_m<true>(ae[e - 1] - ae[e]) : 0.f;
-    de[e] = NT < CC ? decay_m<false>(ae[e - 1] - ae[e]) : 0.f;
-  }
-  auto dcol = [&](int e, int j) -> float { return j < NT ? dt[e] : de[e]; };
-
-  // thread-local aggregates
-  float B[CC], D[CC];
-#pragma unroll
-  for (int j = 0; j < CC; ++j) {
-    B[j] = v[0][j];
-    D[j] = v[E - 1][j];
-  }
-#pragma unroll
-  for (int e = 1; e < E; ++e)
-#pragma unroll
-    for (int j = 0; j < CC; ++j) B[j] = fmaf(dcol(e, j), B[j], v[e][j]);
-#pragma unroll
-  for (int e = E - 2; e >= 0; --e)
-#pragma unroll
-    for (int j = 0; j < CC; ++j) D[j] = fmaf(dcol(e + 1, j), D[j], v[e][j]);
-
-  // wave scans (forward: by last anchor; backward: by first anchor)
-  wave_scan_fwd_mix<CC, NT>(B, ae[E - 1]);
-  wave_scan_bwd_mix<CC, NT>(D, ae[0]);
-  if (lane == kWave - 1) {
-#pragma unroll
-    for (int j = 0; j < CC; ++j) s_wf[wid * CC + j] = B[j];
-    s_wfs[wid] = ae[E - 1];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int j = 0; j < CC; ++j) s_wb[wid * CC + j] = D[j];
-    s_wbs[wid] = ae[0];
-  }
-  // exclusive values from the neighbouring lanes
-  float X[CC], Z[CC];
-#pragma unroll
-  for (int j = 0; j < CC; ++j) {
-    X[j] = __shfl_up(B[j], 1);
-    Z[j] = __shfl_down(D[j], 1);
-  }
-  const float sx = __shfl_up(ae[E - 1], 1);
-  const float sz = __shfl_down(ae[0], 1);
-  __syncthreads();
-
-  // Carries into the wave, as direct weighted sums (every weight <= 1):
-  // forward, at the last anchor s_ref of the previous wave (the tile carry's
-  // anchor for wave 0): lane l < wid holds wave l's aggregate weighted by
-  // exp(s_end(l) - s_ref), lane kWave-1 the tile carry weighted by
-  // exp(sf - s_ref); backward, mirrored.  The lane sums give every lane the
-  // same bits.
-  static_assert(NW < kWave, "one lane per wave aggregate plus one for the tile carry");
-  const float sw = wid > 0 ? s_wfs[wid - 1] : sf;
-  const float sz2 = wid < NW - 1 ? s_wbs[wid + 1] : sb;
-  float cw[CC], cz[CC];
-  {
-    const bool fw = lane < wid, bw = lane > wid && lane < NW;
-    const int lf = fw ? lane : 0, lb = bw ? lane : 0;
-    const float xf = fw ? s_wfs[lf] - sw : sf - sw;
-    const float xb = bw ? sz2 - s_wbs[lb] : sz2 - sb;
-    const bool cf_lane = !fw && lane == kWave - 1, cb_lane = !bw && lane == kWave - 1;
-#pragma unroll
-    for (int j = 0; j < CC; ++j) {
-      const float gf = (fw || cf_lane) ? dk(xf, j) : 0.f;
-      const float gb = (bw || cb_lane) ? dk(xb, j) : 0.f;
-      cw[j] = fw ? gf * s_wf[lf * CC + j] : (cf_lane ? gf * cf[j] : 0.f);
-      cz[j] = bw ? gb * s_wb[lb * CC + j] : (cb_lane ? gb * cb[j] : 0.f);
-    }
-    wave_sum<CC>(cw);
-    wave_sum<CC>(cz);
-  }
-  float swl = sw, szl = sz2;
-  if (lane > 0) {
-#pragma unroll
-    for (int j = 0; j < CC; ++j) cw[j] = fmaf(dk(swl - sx, j), cw[j], X[j]);
-    swl = sx;
-  }
-  if (lane < kWave - 1) {
-#pragma unroll
-    for (int j = 0; j < CC; ++j) cz[j] = fmaf(dk(sz - szl, j), cz[j], Z[j]);
-    szl = sz;
-  }
-
-  // full forward pass: strict lower part of each element
-#pragma unroll
-  for (int j = 0; j < CC; ++j) {
-    const float d0 = dk(swl - ae[0], j);
-    float L = cw[j];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      F[e][j] = (e == 0 ? d0 : dcol(e, j)) * L;
-      L = v[e][j] + F[e][j];
-    }
-  }
-  // full backward pass, combined
-#pragma unroll
-  for (int j = 0; j < CC; ++j) {
-    const float dl = dk(ae[E - 1] - szl, j);
-    float U = cz[j];
-#pragma unroll
-    for (int e = E - 1; e >= 0; --e) {
-      U = fmaf(e == E - 1 ? dl : dcol(e + 1, j), U, v[e][j]);
-      Uo[e][j] = U;
-    }
-  }
-}
-template <int E, int CC, int NW, bool TIE>
-__device__ __forceinline__ void tile_scan_fu(const float (&ae)[E], const float (&v)[E][CC], const float (&cf)[CC], float sf,
-                                             const float (&cb)[CC], float sb, float* s_wf, float* s_wfs, float* s_wb,
-                                             float* s_wbs, float (&F)[E][CC], float (&Uo)[E][CC]) {
-  tile_scan_fu_mix<E, CC, NW, TIE ? CC : 0>(ae, v, cf, sf, cb, sb, s_wf, s_wfs, s_wb, s_wbs, F, Uo);
-}
-
-// The operator's tile scan: v[e][j] becomes strict forward + inclusive
-// backward, i.e. lower + upper - diagonal.
-template <int E, int CC, int NW>
-__device__ __forceinline__ void tile_scan(const float (&ae)[E], float (&v)[E][CC], const float (&cf)[CC], float sf,
-                                          const float (&cb)[CC], float sb, float* s_wf, float* s_wfs, float* s_wb,
-                                          float* s_wbs) {
-  float F[E][CC], U[E][CC];
-  tile_scan_fu<E, CC, NW, false>(ae, v, cf, sf, cb, sb, s_wf, s_wfs, s_wb, s_wbs, F, U);
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-#pragma unroll
-    for (int j = 0; j < CC; ++j) v[e][j] = F[e][j] + U[e][j];
-}
-
-// ---------------------------------------------------------------- carries
-constexpr int kCarryBlock = 1024;
-constexpr int kCarryBatch = 8;
-constexpr uint64_t kCarryMinRun = 8;
-
-// Scan of the tile aggregates into the carry entering each tile from the left
-// (cf: value at the previous tile's last element) and from the right (cb:
-// value at the next tile's first element).  One workgroup per column: each
-// thread owns a contiguous run of tiles and folds it in both directions as
-// direct weighted sums (every weight exp(-|s - s_end|) <= 1); wave 0 scans
-// the forward run aggregates and wave 1 the backward ones, 64 per round, at
-// the same time (at most 16 rounds; runs hold at least 8 tiles, so a few
-// thousand tiles take a few rounds); then each thread walks its run once more
-// writing both carries, with the loads of each batch of tiles issued before
-// their dependent chains.
-__global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restrict__ bf, const float* __restrict__ bb,
-                                                            const float2* __restrict__ tanch, uint64_t T, uint32_t M,
-                                                            uint32_t tie_from, float* __restrict__ cf, float* __restrict__ cb) {
-  __shared__ float sB[kCarryBlock], sS[kCarryBlock], sD[kCarryBlock], sT[kCarryBlock];
-  const uint32_t c = blockIdx.x;
-  const bool tie = c >= tie_from;  // columns from tie_from on scan with the tie decay
-  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
-  // runs of at least kCarryMinRun tiles, so that few tiles need few scan rounds
-  const uint64_t q = std::max<uint64_t>(kCarryMinRun, (T + kCarryBlock - 1) / kCarryBlock);
-  const int rounds = (int)std::min<uint64_t>(kCarryBlock / kWave, ((T + q - 1) / q + kWave - 1) / kWave);
-  const uint64_t t0 = std::min<uint64_t>(T, (uint64_t)tid * q), t1 = std::min<uint64_t>(T, t0 + q);
-  const float s_min = tanch[0].y, s_maxf = tanch[T - 1].x, s_maxl = tanch[T - 1].y;
-
-  // ---- fold both directions
-  float B = 0.f, s = s_maxl, D = 0.f, sd = s_maxf;
-  if (t0 < t1) {
-    s = tanch[t1 - 1].y;
-    sd = tanch[t0].x;
-#pragma unroll 8
-    for (uint64_t t = t0; t < t1; ++t) {
-      const float2 an = tanch[t];
-      B = fmaf(decay_r(an.y - s, tie), bf[t * M + c], B);
-      D = fmaf(decay_r(sd - an.x, tie), bb[t * M + c], D);
-    }
-  }
-  sB[tid] = B;
-  sS[tid] = s;
-  sD[tid] = D;
-  sT[tid] = sd;
-  __syncthreads();
-  // ---- scan the run aggregates: wave 0 forward, wave 1 backward
-  if (wid == 0) {
-    float cB = 0.f, cS = s_min;
-    for (int r = 0; r < rounds; ++r) {  // runs past the last hold nothing
-      const int i = r * kWave + lane;
-      float b1[1] = {sB[i]};
-      const float s1 = sS[i];
-      if (tie)
-        wave_scan_fwd<1, true>(b1, s1);
-      else
-        wave_scan_fwd<1, false>(b1, s1);
-      const float inc = fmaf(decay_r(cS - s1, tie), cB, b1[0]);
-      float ex = __shfl_up(inc, 1), es = __shfl_up(s1, 1);
-      if (lane == 0) {
-        ex = cB;
-        es = cS;
-      }
-      sB[i] = ex;
-      sS[i] = es;
-      cB = __shfl(inc, kWave - 1);
-      cS = __shfl(s1, kWave - 1);
-    }
-  } else if (wid == 1) {
-    float cB = 0.f, cS = s_maxf;
-    for (int r = rounds - 1; r >= 0; --r) {
-      const int i = r * kWave + lane;
-      float b1[1] = {sD[i]};
-      const float s1 = sT[i];
-      if (tie)
-        wave_scan_bwd<1, true>(b1, s1);
-      else
-        wave_scan_bwd<1, false>(b1, s1);
-      const float inc = fmaf(decay_r(s1 - cS, tie), cB, b1[0]);
-      float ex = __shfl_down(inc, 1), es = __shfl_down(s1, 1);
-      if (lane == kWave - 1) {
-        ex = cB;
-        es = cS;
-      }
-      sD[i] = ex;
-      sT[i] = es;
-      cB = __shfl(inc, 0);
-      cS = __shfl(s1, 0);
-    }
-  }
-  __syncthreads();
-  // ---- walk: forward carries upward, backward carries downward
-  if (t0 < t1) {
-    float C = sB[tid], sc = sS[tid];
-    for (uint64_t tb = t0; tb < t1; tb += kCarryBatch) {
-      float sl[kCarryBatch], bv[kCarryBatch];
-#pragma unroll
-      for (int u = 0; u < kCarryBatch; ++u) {
-        const uint64_t t = std::min<uint64_t>(tb + u, t1 - 1);
-        sl[u] = tanch[t].y;
-        bv[u] = bf[t * M + c];
-      }
-#pragma unroll
-      for (int u = 0; u < kCarryBatch; ++u) {
-        if (tb + u < t1) {
-          cf[(tb + u) * M + c] = C;
-          C = fmaf(decay_r(sc - sl[u], tie), C, bv[u]);
-          sc = sl[u];
-        }
-      }
-    }
-    C = sD[tid];
-    sc = sT[tid];
-    for (uint64_t te = t1; te > t0;) {
-      const uint64_t tb = te > t0 + kCarryBatch ? te - kCarryBatch : t0;
-      float sf[kCarryBatch], bv[kCarryBatch];
-#pragma unroll
-      for (int u = 0; u < kCarryBatch; ++u) {
-        const uint64_t t = std::min<uint64_t>(tb + u, te - 1);
-        sf[u] = tanch[t].x;
-        bv[u] = bb[t * M + c];
-      }
-#pragma unroll
-      for (int u = kCarryBatch - 1; u >= 0; --u) {
-        if (tb + u < te) {
-          cb[(tb + u) * M + c] = C;
-          C = fmaf(decay_r(sf[u] - sc, tie), C, bv[u]);
-          sc = sf[u];
-        }
-      }
-      te = tb;
-    }
-  }
-}
-
-// Large tile counts: the tiles are grouped by 1024.  k_carry_up folds each
-// group into one aggregate per direction (direct weighted sums), k_tile_carry
-// scans the group aggregates, and k_carry_down turns each group's carry into
-// the carries of its tiles with a block-wide scan (wave shuffles, then the
-// waves' totals in order).  All three run one block per (group, column).
-constexpr int kCarryGroup = 1024;
-
-__global__ __launch_bounds__(kCarryGroup) void k_carry_up(const float* __restrict__ bf, const float* __restrict__ bb,
-                                                          const float2* __restrict__ tanch, uint64_t T, uint32_t M,
-                                                          uint32_t tie_from, float* __restrict__ gbf, float* __restrict__ gbb,
-                                                          float2* __restrict__ ganch) {
-  constexpr int NW = kCarryGroup / kWave;
-  __shared__ float s_red[2 * NW];
-  const uint64_t g = blockIdx.x;
-  const uint32_t c = blockIdx.y;
-  const bool tie = c >= tie_from;
-  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
-  const uint64_t t0 = g * kCarryGroup, t1 = std::min<uint64_t>(T, t0 + kCarryGroup);
-  const uint64_t t = t0 + tid;
-  const float s_first = tanch[t0].x, s_last = tanch[t1 - 1].y;
-  float vf[1] = {0.f}, vb[1] = {0.f};
-  if (t < t1) {
-    const float2 ta = tanch[t];
-    vf[0] = decay_r(ta.y - s_last, tie) * bf[t * M + c];
-    vb[0] = decay_r(s_first - ta.x, tie) * bb[t * M + c];
-  }
-  wave_sum<1>(vf);
-  wave_sum<1>(vb);
-  if (lane == 0) {
-    s_red[wid] = vf[0];
-    s_red[NW + wid] = vb[0];
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float f = 0.f, b = 0.f;
-    for (int w = 0; w < NW; ++w) {
-      f += s_red[w];
-      b += s_red[NW + w];
-    }
-    gbf[g * M + c] = f;
-    gbb[g * M + c] = b;
-    if (c == 0) ganch[g] = make_float2(s_first, s_last);
-  }
-}
-
-__global__ __launch_bounds__(kCarryGroup) void k_carry_down(const float* __restrict__ bf, const float* __restrict__ bb,
-                                                            const float2* __restrict__ tanch, uint64_t T, uint32_t M,
-                                                            const float* __restrict__ gcf, const float* __restrict__ gcb,
-                                                            const float2* __restrict__ ganch, uint64_t G,
-                                                            uint32_t tie_from, float* __restrict__ cf, float* __restrict__ cb) {
-  constexpr int NW = kCarryGroup / kWave;
-  __shared__ float s_f[NW], s_fs[NW], s_b[NW], s_bs[NW];
-  const uint64_t g = blockIdx.x;
-  const uint32_t c = blockIdx.y;
-  const bool tie = c >= tie_from;
-  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
-  const uint64_t t0 = g * kCarryGroup, t1 = std::min<uint64_t>(T, t0 + kCarryGroup);
-  const uint64_t t = t0 + tid;
-  const bool valid = t < t1;
-  const float2 last_tile = tanch[t1 - 1];
-  const float2 ta = valid ? tanch[t] : last_tile;
-  float B[1] = {valid ? bf[t * M + c] : 0.f};
-  float D[1] = {valid ? bb[t * M + c] : 0.f};
-  // inclusive scans within the wave (forward by last anchors, backward by first)
-  if (tie)
-        wave_scan_fwd<1, true>(B, ta.y);
-      else
-        wave_scan_fwd<1, false>(B, ta.y);
-  if (tie)
-        wave_scan_bwd<1, true>(D, ta.x);
-      else
-        wave_scan_bwd<1, false>(D, ta.x);
-  if (lane == kWave - 1) {
-    s_f[wid] = B[0];
-    s_fs[wid] = ta.y;
-  }
-  if (lane == 0) {
-    s_b[wid] = D[0];
-    s_bs[wid] = ta.x;
-  }
-  const float X = __shfl_up(B[0], 1), sx = __shfl_up(ta.y, 1);
-  const float Z = __shfl_down(D[0], 1), sz = __shfl_down(ta.x, 1);
-  __syncthreads();
-  // forward: group carry, earlier waves, then earlier lanes of this wave
-  float C = gcf[g * M + c];
-  float sc = g > 0 ? ganch[g - 1].y : ganch[0].x;
-  for (int w = 0; w < wid; ++w) {
-    C = fmaf(decay_r(sc - s_fs[w], tie), C, s_f[w]);
-    sc = s_fs[w];
-  }
-  if (lane > 0) {
-    C = fmaf(decay_r(sc - sx, tie), C, X);
-    sc = sx;
-  }
-  // backward: group carry, later waves, then later lanes of this wave
-  float Cb = gcb[g * M + c];
-  float sb = g + 1 < G ? ganch[g + 1].x : ganch[G - 1].y;
-  for (int w = NW - 1; w > wid; --w) {
-    Cb = fmaf(decay_r(s_bs[w] - sb, tie), Cb, s_b[w]);
-    sb = s_bs[w];
-  }
-  if (lane < kWave - 1) {
-    Cb = fmaf(decay_r(sz - sb, tie), Cb, Z);
-    sb = sz;
-  }
-  if (valid) {
-    cf[t * M + c] = C;
-    cb[t * M + c] = Cb;
-  }
-}
 
 // Carries for T tiles: one level when T is small, three levels otherwise.
 // g_* hold the group aggregates and carries (ceil(T / 1024) x M each).
@@ -460,393 +46,6 @@ static hipError_t tile_carries(const float* bf, const float* bb, const float2* t
   LAPLEX_LAUNCH("k_carry_down", T, s,
                 k_carry_down<<<grid, kCarryGroup, 0, s>>>(bf, bb, tanch, T, M, gcf, gcb, ganch, G, tie_from, cf, cb));
   return hipGetLastError();
-}
-
-// ---------------------------------------------------------------- symmetric
-// Contiguous loads and stores of N floats; vector instructions when the
-// caller knows the address is 16-byte (N % 4 == 0) or 8-byte (N % 2 == 0)
-// aligned.
-template <int N>
-__device__ __forceinline__ void ld_contig(const float* __restrict__ p, float (&v)[N], bool vec) {
-  if constexpr (N % 4 == 0) {
-    if (vec) {
-#pragma unroll
-      for (int i = 0; i < N / 4; ++i) {
-        const float4 q = reinterpret_cast<const float4*>(p)[i];
-        v[4 * i] = q.x;
-        v[4 * i + 1] = q.y;
-        v[4 * i + 2] = q.z;
-        v[4 * i + 3] = q.w;
-      }
-      return;
-    }
-  } else if constexpr (N % 2 == 0) {
-    if (vec) {
-#pragma unroll
-      for (int i = 0; i < N / 2; ++i) {
-        const float2 q = reinterpret_cast<const float2*>(p)[i];
-        v[2 * i] = q.x;
-        v[2 * i + 1] = q.y;
-      }
-      return;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = p[i];
-}
-template <int N>
-__device__ __forceinline__ void st_contig(float* __restrict__ p, const float (&v)[N], bool vec) {
-  if constexpr (N % 4 == 0) {
-    if (vec) {
-#pragma unroll
-      for (int i = 0; i < N / 4; ++i) reinterpret_cast<float4*>(p)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-      return;
-    }
-  } else if constexpr (N % 2 == 0) {
-    if (vec) {
-#pragma unroll
-      for (int i = 0; i < N / 2; ++i) reinterpret_cast<float2*>(p)[i] = make_float2(v[2 * i], v[2 * i + 1]);
-      return;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < N; ++i) p[i] = v[i];
-}
-
-// Anchors of this thread's E consecutive sorted positions (pad: `pad`).
-template <int E>
-__device__ __forceinline__ void load_anchors(const float* __restrict__ a_s, uint64_t p0, uint64_t n, float pad, bool vec,
-                                             float (&ae)[E]) {
-  if (p0 + E <= n) {
-    ld_contig<E>(a_s + p0, ae, vec && (E % 4 == 0 || E % 2 == 0));
-  } else {
-#pragma unroll
-    for (int e = 0; e < E; ++e) ae[e] = (p0 + e < n) ? a_s[p0 + e] : pad;
-  }
-}
-
-// Rows p0 .. p0+E-1, columns [cc*C, cc*C + C) of a row-major n x m array;
-// rows past n read as zero.  When m == C the thread's E*C floats are
-// contiguous and are loaded as one block.
-template <int E, int C>
-__device__ __forceinline__ void load_rows(const float* __restrict__ x, uint64_t p0, uint64_t n, uint32_t m, uint32_t cc, bool vec,
-                                          float (&xv)[E][C]) {
-  if (m == C && p0 + E <= n) {
-    float flat[E * C];
-    ld_contig<E * C>(x + p0 * C, flat, vec);
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-#pragma unroll
-      for (int j = 0; j < C; ++j) xv[e][j] = flat[e * C + j];
-    return;
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-#pragma unroll
-    for (int j = 0; j < C; ++j) xv[e][j] = (p0 + e < n) ? x[(p0 + e) * m + cc * C + j] : 0.f;
-}
-template <int E, int C>
-__device__ __forceinline__ void store_rows(float* __restrict__ y, uint64_t p0, uint64_t n, uint32_t m, uint32_t cc, bool vec,
-                                           const float (&yv)[E][C]) {
-  if (m == C && p0 + E <= n) {
-    float flat[E * C];
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-#pragma unroll
-      for (int j = 0; j < C; ++j) flat[e * C + j] = yv[e][j];
-    st_contig<E * C>(y + p0 * C, flat, vec);
-    return;
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (p0 + e < n)
-#pragma unroll
-      for (int j = 0; j < C; ++j) y[(p0 + e) * m + cc * C + j] = yv[e][j];
-}
-
-// Tile aggregates of the inputs in sorted order (xs, and phs for the phased
-// operator).  vec: a_s is 16-byte aligned (workspace buffers always are).
-template <int C, bool PH>
-__global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_sym_reduce(
-    const float* __restrict__ a_s, uint64_t n, uint32_t m, const float* __restrict__ xs, const float* __restrict__ phs,
-    float* __restrict__ bf, float* __restrict__ bb, float2* __restrict__ tanch, bool vec) {
-  constexpr int CC = PH ? 2 * C : C;
-  constexpr int E = apply_items(CC);
-  constexpr int BLOCK = apply_block(CC);
-  constexpr int NW = BLOCK / kWave;
-  constexpr int P = BLOCK * E;
-  __shared__ float s_red[2 * NW * CC];
-  const uint32_t M = PH ? 2 * m : m;
-  const int tid = threadIdx.x;
-  const uint64_t tile = blockIdx.x;
-  const uint64_t lo = tile * P;
-  const uint64_t hi = std::min<uint64_t>(n, lo + P);
-  const float s_first = a_s[lo], s_last = a_s[hi - 1];
-  if (tid == 0) tanch[tile] = make_float2(s_first, s_last);
-  const uint64_t p0 = lo + (uint64_t)tid * E;
-  float ae[E], wf[E], wb[E], cs[E], sn[E];
-  load_anchors<E>(a_s, p0, n, s_last, vec, ae);
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const bool valid = p0 + e < n;
-    wf[e] = valid ? decay(ae[e] - s_last) : 0.f;
-    wb[e] = valid ? decay(s_first - ae[e]) : 0.f;
-    cs[e] = 1.f;
-    sn[e] = 0.f;
-  }
-  if (PH) {
-    float ph[E];
-    load_anchors<E>(phs, p0, n, 0.f, true, ph);
-#pragma unroll
-    for (int e = 0; e < E; ++e) sincosf(ph[e], &sn[e], &cs[e]);
-  }
-  for (uint32_t cc = 0; cc < m / C; ++cc) {
-    float xv[E][C];
-    load_rows<E, C>(xs, p0, n, m, cc, true, xv);
-    float sf[CC], sb[CC];
-#pragma unroll
-    for (int j = 0; j < CC; ++j) sf[j] = sb[j] = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-#pragma unroll
-      for (int j = 0; j < C; ++j) {
-        const float v = xv[e][j];
-        if (PH) {
-          const float vc = cs[e] * v, vs = sn[e] * v;
-          sf[j] = fmaf(wf[e], vc, sf[j]);
-          sf[C + j] = fmaf(wf[e], vs, sf[C + j]);
-          sb[j] = fmaf(wb[e], vc, sb[j]);
-          sb[C + j] = fmaf(wb[e], vs, sb[C + j]);
-        } else {
-          sf[j] = fmaf(wf[e], v, sf[j]);
-          sb[j] = fmaf(wb[e], v, sb[j]);
-        }
-      }
-    }
-    int writer = 0;
-    block_sum2<CC, NW>(sf, sb, s_red, writer);
-    if (writer) {
-      float tf = 0.f, tb = 0.f;
-      for (int w = 0; w < NW; ++w) {
-        tf += s_red[(0 * NW + w) * CC + tid];
-        tb += s_red[(1 * NW + w) * CC + tid];
-      }
-      const uint32_t col = sumcol<C, PH>(m, cc, tid);
-      bf[tile * M + col] = tf;
-      bb[tile * M + col] = tb;
-    }
-    __syncthreads();
-  }
-}
-
-// Row loads and stores of a thread's E consecutive rows.  FAST: the block's
-// rows are all in range, m == C, and the arrays are aligned for vector access.
-template <int E, int C, bool FAST>
-__device__ __forceinline__ void load_rows_t(const float* __restrict__ x, uint64_t p0, uint64_t n, uint32_t m, uint32_t cc,
-                                            float (&xv)[E][C]) {
-  if constexpr (FAST) {
-    float flat[E * C];
-    ld_contig<E * C>(x + p0 * C, flat, true);
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-#pragma unroll
-      for (int j = 0; j < C; ++j) xv[e][j] = flat[e * C + j];
-  } else {
-    load_rows<E, C>(x, p0, n, m, cc, true, xv);
-  }
-}
-template <int E, int C, bool FAST>
-__device__ __forceinline__ void store_rows_t(float* __restrict__ y, uint64_t p0, uint64_t n, uint32_t m, uint32_t cc,
-                                             const float (&yv)[E][C]) {
-  if constexpr (FAST) {
-    float flat[E * C];
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-#pragma unroll
-      for (int j = 0; j < C; ++j) flat[e * C + j] = yv[e][j];
-    st_contig<E * C>(y + p0 * C, flat, true);
-  } else {
-    store_rows<E, C>(y, p0, n, m, cc, true, yv);
-  }
-}
-
-// SCATTER: y rows written to original order through perm; otherwise to
-// sorted order (row p of y).
-template <int C, bool PH, bool SCATTER, bool FAST>
-__device__ __forceinline__ void sym_apply_tile(const float* __restrict__ a_s, const uint32_t* __restrict__ perm,
-                                               const float* __restrict__ xs, const float* __restrict__ phs,
-                                               const float* __restrict__ cfw, const float* __restrict__ cbw,
-                                               const float2* __restrict__ tanch, uint64_t n, uint32_t m, uint64_t T,
-                                               float* __restrict__ y, bool vec, float* s_wf, float* s_wb, float* s_wfs,
-                                               float* s_wbs) {
-  constexpr int CC = PH ? 2 * C : C;
-  constexpr int E = apply_items(CC);
-  constexpr int BLOCK = apply_block(CC);
-  constexpr int NW = BLOCK / kWave;
-  constexpr int P = BLOCK * E;
-  const uint32_t M = PH ? 2 * m : m;
-  const int tid = threadIdx.x;
-  const uint64_t tile = blockIdx.x;
-  const uint64_t p0 = tile * P + (uint64_t)tid * E;
-  // the first column chunk's rows and carries are requested before anything
-  // else, so that all of the thread's loads are in flight together
-  float xv_n[E][C], cinf_n[CC], cinb_n[CC];
-  load_rows_t<E, C, FAST>(xs, p0, n, m, 0, xv_n);
-#pragma unroll
-  for (int j = 0; j < CC; ++j) {
-    const uint32_t col = sumcol<C, PH>(m, 0, j);
-    cinf_n[j] = cfw[tile * M + col];
-    cinb_n[j] = cbw[tile * M + col];
-  }
-  float ae[E], cs[E], sn[E];
-  uint32_t dst[E];
-  if constexpr (FAST) {
-    ld_contig<E>(a_s + p0, ae, true);
-  } else {
-    load_anchors<E>(a_s, p0, n, a_s[n - 1], vec, ae);
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint64_t p = p0 + e;
-    const bool valid = FAST || p < n;
-    dst[e] = 0u;
-    if (SCATTER) {
-      dst[e] = valid ? perm[p] : 0u;
-      if ((uint64_t)dst[e] >= n) dst[e] = 0;
-    }
-    cs[e] = 1.f;
-    sn[e] = 0.f;
-  }
-  if (PH) {
-    float ph[E];
-    if constexpr (FAST) {
-      ld_contig<E>(phs + p0, ph, true);
-    } else {
-      load_anchors<E>(phs, p0, n, 0.f, true, ph);
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) sincosf(ph[e], &sn[e], &cs[e]);
-  }
-  const float2 ta = tanch[tile];
-  const float sf = tile > 0 ? tanch[tile - 1].y : ta.x;
-  const float sb = tile + 1 < T ? tanch[tile + 1].x : ta.y;
-  for (uint32_t cc = 0; cc < m / C; ++cc) {
-    float xv[E][C], cin_f[CC], cin_b[CC];
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-#pragma unroll
-      for (int j = 0; j < C; ++j) xv[e][j] = xv_n[e][j];
-#pragma unroll
-    for (int j = 0; j < CC; ++j) {
-      cin_f[j] = cinf_n[j];
-      cin_b[j] = cinb_n[j];
-    }
-    if (cc + 1 < m / C) {  // next chunk's loads overlap this chunk's scan
-      load_rows_t<E, C, FAST>(xs, p0, n, m, cc + 1, xv_n);
-#pragma unroll
-      for (int j = 0; j < CC; ++j) {
-        const uint32_t col = sumcol<C, PH>(m, cc + 1, j);
-        cinf_n[j] = cfw[tile * M + col];
-        cinb_n[j] = cbw[tile * M + col];
-      }
-    }
-    float v[E][CC];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-#pragma unroll
-      for (int j = 0; j < C; ++j) {
-        if (PH) {
-          v[e][j] = cs[e] * xv[e][j];
-          v[e][C + j] = sn[e] * xv[e][j];
-        } else {
-          v[e][j] = xv[e][j];
-        }
-      }
-    }
-    tile_scan<E, CC, NW>(ae, v, cin_f, sf, cin_b, sb, s_wf, s_wfs, s_wb, s_wbs);
-    float yv[E][C];
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-#pragma unroll
-      for (int j = 0; j < C; ++j) yv[e][j] = PH ? fmaf(cs[e], v[e][j], sn[e] * v[e][C + j]) : v[e][j];
-    if (SCATTER) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        if (FAST || p0 + e < n) {
-          float* yr = y + (uint64_t)dst[e] * m + cc * C;
-#pragma unroll
-          for (int j = 0; j < C; ++j) yr[j] = yv[e][j];
-        }
-      }
-    } else {
-      store_rows_t<E, C, FAST>(y, p0, n, m, cc, yv);
-    }
-    __syncthreads();
-  }
-}
-
-template <int C, bool PH, bool SCATTER>
-__global__ __launch_bounds__(apply_block(PH ? 2 * C : C))
-__attribute__((amdgpu_waves_per_eu(!PH && C == 1 ? 8 : 1))) void k_sym_apply(
-    const float* __restrict__ a_s, const uint32_t* __restrict__ perm, const float* __restrict__ xs,
-    const float* __restrict__ phs, const float* __restrict__ cfw, const float* __restrict__ cbw,
-    const float2* __restrict__ tanch, uint64_t n, uint32_t m, uint64_t T, float* __restrict__ y, bool vec) {
-  constexpr int CC = PH ? 2 * C : C;
-  constexpr int NW = apply_block(CC) / kWave;
-  constexpr int P = apply_tile(CC);
-  __shared__ float s_wf[NW * CC], s_wb[NW * CC], s_wfs[NW], s_wbs[NW];
-  if (vec && m == C && ((uint64_t)blockIdx.x + 1) * P <= n)
-    sym_apply_tile<C, PH, SCATTER, true>(a_s, perm, xs, phs, cfw, cbw, tanch, n, m, T, y, vec, s_wf, s_wb, s_wfs, s_wbs);
-  else
-    sym_apply_tile<C, PH, SCATTER, false>(a_s, perm, xs, phs, cfw, cbw, tanch, n, m, T, y, vec, s_wf, s_wb, s_wfs, s_wbs);
-}
-
-// Rows of m floats moved by index: pieces of V floats (one vector access
-// each), consecutive threads taking consecutive pieces, so a row is read or
-// written whole by neighbouring lanes and the sorted-order side is one
-// contiguous stream.
-template <int V> struct RowPiece;
-template <> struct RowPiece<1> { using T = float; };
-template <> struct RowPiece<2> { using T = float2; };
-template <> struct RowPiece<4> { using T = float4; };
-
-// row and piece of flat piece index i (P pieces per row)
-__device__ __forceinline__ uint64_t piece_row(uint64_t i, uint32_t P, uint64_t items) {
-  return items < (1ull << 32) ? (uint64_t)((uint32_t)i / P) : i / P;
-}
-
-template <int V>
-__global__ void k_scatter_rows(const float* __restrict__ src, const uint32_t* __restrict__ perm, uint64_t rows, uint32_t m,
-                               float* __restrict__ dst) {
-  using T = typename RowPiece<V>::T;
-  const uint32_t P = m / V;
-  const uint64_t items = rows * P;
-  uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  for (; i < items; i += stride) {
-    const uint64_t r = piece_row(i, P, items);
-    const uint32_t c = (uint32_t)(i - r * P);
-    const uint32_t d = perm[r];
-    if ((uint64_t)d >= rows) continue;  // a handle from the sort is always in range
-    *reinterpret_cast<T*>(dst + (uint64_t)d * m + (uint64_t)c * V) = *reinterpret_cast<const T*>(src + r * m + (uint64_t)c * V);
-  }
-}
-template <int V>
-__global__ void k_gather_rows(const float* __restrict__ x, const uint32_t* __restrict__ perm, const float* __restrict__ ph,
-                              uint64_t rows, uint32_t m, float* __restrict__ xs, float* __restrict__ phs) {
-  using T = typename RowPiece<V>::T;
-  const uint32_t P = m / V;
-  const uint64_t items = rows * P;
-  uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  for (; i < items; i += stride) {
-    const uint64_t r = piece_row(i, P, items);
-    const uint32_t c = (uint32_t)(i - r * P);
-    uint32_t src = perm[r];
-    if ((uint64_t)src >= rows) src = 0;
-    *reinterpret_cast<T*>(xs + r * m + (uint64_t)c * V) = *reinterpret_cast<const T*>(x + (uint64_t)src * m + (uint64_t)c * V);
-    if (ph && c == 0) phs[r] = ph[src];
-  }
 }
 
 // piece width for rows of m floats between x and y (16- or 8-byte vectors
