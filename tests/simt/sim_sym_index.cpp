@@ -1,0 +1,208 @@
+// The symmetric operator's index path (rows moved by the permutation; the
+// path taken for m > 4 columns), run on the CPU by the SIMT emulation in
+// simt.hpp from the library's own device code (laplex_scan.hpp):
+//   k_gather_rows -> k_sym_reduce -> tile carries -> k_sym_apply (scatter)
+// with the launch shapes the library's host code uses.  Test infrastructure.
+//
+// Every workspace buffer, the output and shared memory start filled with a
+// poison value, and each buffer sits between guard zones of the same poison.
+// The program prints, as key=value lines:
+//   nonfinite_rows  rows of y holding a non-finite value
+//   err             max over columns of |y - y_ref|_inf / |K |x||_inf, with
+//                   y_ref from a float64 recurrence over the sorted anchors
+//   guards_ok       1 if no byte of any guard zone changed
+//   y_hash          FNV-1a hash of y's bits (equal across poison values when
+//                   no read of unwritten memory reaches y)
+// Usage: sim_sym_index n m ties seed poison_hex [apply_stride]
+//   apply_stride s > 1 runs only every s-th tile of k_sym_apply (and the
+//   first and last); err and nonfinite_rows then cover those tiles' rows.
+#include "hip/hip_runtime.h"
+#include "laplex_scan.hpp"
+
+#include <map>
+#include <random>
+#include <string>
+
+using namespace laplex;
+
+namespace {
+
+constexpr size_t kGuard = 4096;  // bytes of poison before and after each buffer
+uint32_t g_poison;
+std::vector<std::pair<unsigned char*, size_t>> g_allocs;
+
+template <typename T>
+T* alloc(size_t count) {
+  const size_t bytes = count * sizeof(T);
+  const size_t total = (kGuard + bytes + kGuard + 255) & ~size_t(255);
+  unsigned char* base = static_cast<unsigned char*>(std::aligned_alloc(256, total));
+  for (size_t i = 0; i + 4 <= total; i += 4) std::memcpy(base + i, &g_poison, 4);
+  g_allocs.push_back({base, bytes});
+  return reinterpret_cast<T*>(base + kGuard);
+}
+bool guards_intact() {
+  for (auto& [base, bytes] : g_allocs) {
+    const size_t total = (kGuard + bytes + kGuard + 255) & ~size_t(255);
+    for (size_t i = 0; i + 4 <= total; i += 4) {
+      if (i >= kGuard && i < kGuard + bytes) continue;
+      uint32_t v;
+      std::memcpy(&v, base + i, 4);
+      if (v != g_poison) return false;
+    }
+  }
+  return true;
+}
+
+template <int C>
+void run_index_path(const float* a_s, const uint32_t* perm, uint64_t n, uint32_t m, const float* x, float* y,
+                    uint64_t apply_stride) {
+  constexpr int P = apply_tile(C);
+  const uint64_t T = (n + P - 1) / P;
+  const uint32_t M = m;
+  float* xs = alloc<float>(n * m);
+  float* bf = alloc<float>(T * M);
+  float* bb = alloc<float>(T * M);
+  float* cf = alloc<float>(T * M);
+  float* cb = alloc<float>(T * M);
+  float2* tanch = alloc<float2>(T);
+  const uint64_t G = (T + 1023) / 1024;
+  float* gbf = alloc<float>(G * M);
+  float* gbb = alloc<float>(G * M);
+  float* gcf = alloc<float>(G * M);
+  float* gcb = alloc<float>(G * M);
+  float2* ganch = alloc<float2>(G);
+  const bool vec = (reinterpret_cast<uintptr_t>(a_s) & 15) == 0;
+
+  // rows into sorted order: pieces of 4 floats when m allows (all buffers here are 256-byte aligned)
+  const int V = (m % 4 == 0) ? 4 : (m % 2 == 0) ? 2 : 1;
+  const unsigned gg = (unsigned)std::min<uint64_t>((n * (m / V) + 255) / 256, 16384);
+  if (V == 4)
+    simt::launch(dim3(gg), dim3(256), [&] { k_gather_rows<4>(x, perm, nullptr, n, m, xs, nullptr); });
+  else if (V == 2)
+    simt::launch(dim3(gg), dim3(256), [&] { k_gather_rows<2>(x, perm, nullptr, n, m, xs, nullptr); });
+  else
+    simt::launch(dim3(gg), dim3(256), [&] { k_gather_rows<1>(x, perm, nullptr, n, m, xs, nullptr); });
+  std::fprintf(stderr, "gather done\n");
+
+  simt::launch(dim3((unsigned)T), dim3(apply_block(C)),
+               [&] { k_sym_reduce<C, false>(a_s, n, m, xs, nullptr, bf, bb, tanch, vec); });
+  std::fprintf(stderr, "reduce done (%llu tiles)\n", (unsigned long long)T);
+
+  if (T <= (uint64_t)kCarryGroup * 4) {
+    simt::launch(dim3(M), dim3(kCarryBlock), [&] { k_tile_carry(bf, bb, tanch, T, M, ~0u, cf, cb); });
+  } else {
+    simt::launch(dim3((unsigned)G, M), dim3(kCarryGroup),
+                 [&] { k_carry_up(bf, bb, tanch, T, M, ~0u, gbf, gbb, ganch); });
+    simt::launch(dim3(M), dim3(kCarryBlock), [&] { k_tile_carry(gbf, gbb, ganch, G, M, ~0u, gcf, gcb); });
+    simt::launch(dim3((unsigned)G, M), dim3(kCarryGroup),
+                 [&] { k_carry_down(bf, bb, tanch, T, M, gcf, gcb, ganch, G, ~0u, cf, cb); });
+  }
+  std::fprintf(stderr, "carries done\n");
+
+  simt::launch(
+      dim3((unsigned)T), dim3(apply_block(C)),
+      [&] { k_sym_apply<C, false, true>(a_s, perm, xs, nullptr, cf, cb, tanch, n, m, T, y, vec); },
+      [&](uint64_t b) { return apply_stride <= 1 || b % apply_stride == 0 || b + 1 == T; });
+  std::fprintf(stderr, "apply done\n");
+}
+
+}  // namespace
+
+int main(int argc, char** argv) {
+  if (argc < 6) {
+    std::fprintf(stderr, "usage: %s n m ties seed poison_hex [apply_stride]\n", argv[0]);
+    return 2;
+  }
+  const uint64_t n = std::strtoull(argv[1], nullptr, 10);
+  const uint32_t m = (uint32_t)std::strtoul(argv[2], nullptr, 10);
+  const bool ties = std::atoi(argv[3]) != 0;
+  const uint64_t seed = std::strtoull(argv[4], nullptr, 10);
+  g_poison = (uint32_t)std::strtoul(argv[5], nullptr, 16);
+  const uint64_t stride = argc > 6 ? std::strtoull(argv[6], nullptr, 10) : 1;
+  simt::lds_poison() = g_poison;
+
+  // inputs: anchors U(0, n/8 + 1) (rounded to integers for ties), x ~ N(0, 1)
+  std::mt19937_64 rng(seed);
+  std::uniform_real_distribution<double> ua(0.0, n / 8.0 + 1.0);
+  std::normal_distribution<double> nx(0.0, 1.0);
+  float* a = alloc<float>(n);
+  float* x = alloc<float>(n * m);
+  for (uint64_t i = 0; i < n; ++i) a[i] = ties ? (float)std::round(ua(rng)) : (float)ua(rng);
+  for (uint64_t i = 0; i < n * m; ++i) x[i] = (float)nx(rng);
+  // the sort handle: stable ascending argsort
+  std::vector<uint32_t> pv(n);
+  for (uint64_t i = 0; i < n; ++i) pv[i] = (uint32_t)i;
+  std::stable_sort(pv.begin(), pv.end(), [&](uint32_t p, uint32_t q) { return a[p] < a[q]; });
+  uint32_t* perm = alloc<uint32_t>(n);
+  float* a_s = alloc<float>(n);
+  for (uint64_t i = 0; i < n; ++i) {
+    perm[i] = pv[i];
+    a_s[i] = a[pv[i]];
+  }
+  float* y = alloc<float>(n * m);
+
+  switch (column_chunk(m)) {
+    case 8: run_index_path<8>(a_s, perm, n, m, x, y, stride); break;
+    case 4: run_index_path<4>(a_s, perm, n, m, x, y, stride); break;
+    case 2: run_index_path<2>(a_s, perm, n, m, x, y, stride); break;
+    default: run_index_path<1>(a_s, perm, n, m, x, y, stride); break;
+  }
+
+  // float64 reference over the sorted order: lower + upper - diagonal
+  const uint64_t P = (uint64_t)apply_tile((int)column_chunk(m));
+  std::vector<char> checked(n, 1);
+  if (stride > 1) {
+    const uint64_t T = (n + P - 1) / P;
+    for (uint64_t i = 0; i < n; ++i) {
+      const uint64_t t = i / P;
+      checked[i] = (t % stride == 0 || t + 1 == T);
+    }
+  }
+  double err = 0.0;
+  uint64_t nonfinite = 0;
+  for (uint32_t c = 0; c < m; ++c) {
+    std::vector<double> L(n), U(n), La(n), Ua(n);
+    for (uint64_t i = 0; i < n; ++i) {
+      const double v = x[(uint64_t)perm[i] * m + c];
+      const double d = i ? std::exp((double)a_s[i - 1] - (double)a_s[i]) : 0.0;
+      L[i] = v + (i ? d * L[i - 1] : 0.0);
+      La[i] = std::fabs(v) + (i ? d * La[i - 1] : 0.0);
+    }
+    for (uint64_t i = n; i-- > 0;) {
+      const double v = x[(uint64_t)perm[i] * m + c];
+      const double d = i + 1 < n ? std::exp((double)a_s[i] - (double)a_s[i + 1]) : 0.0;
+      U[i] = v + (i + 1 < n ? d * U[i + 1] : 0.0);
+      Ua[i] = std::fabs(v) + (i + 1 < n ? d * Ua[i + 1] : 0.0);
+    }
+    double num = 0.0, den = 0.0;
+    for (uint64_t i = 0; i < n; ++i) {
+      const double v = x[(uint64_t)perm[i] * m + c];
+      den = std::max(den, La[i] + Ua[i] - std::fabs(v));
+      if (!checked[i]) continue;
+      const double g = y[(uint64_t)perm[i] * m + c];
+      if (!std::isfinite(g)) continue;
+      num = std::max(num, std::fabs(g - (L[i] + U[i] - v)));
+    }
+    err = std::max(err, den > 0 ? num / den : num);
+  }
+  for (uint64_t i = 0; i < n; ++i) {
+    if (!checked[i]) continue;
+    bool bad = false;
+    for (uint32_t c = 0; c < m; ++c) bad |= !std::isfinite(y[(uint64_t)perm[i] * m + c]);
+    nonfinite += bad;
+  }
+  uint64_t h = 1469598103934665603ull;
+  for (uint64_t i = 0; i < n; ++i) {
+    if (!checked[i]) continue;
+    for (uint32_t c = 0; c < m; ++c) {
+      uint32_t b;
+      std::memcpy(&b, &y[(uint64_t)perm[i] * m + c], 4);
+      for (int k = 0; k < 4; ++k) h = (h ^ ((b >> (8 * k)) & 0xFF)) * 1099511628211ull;
+    }
+  }
+  std::printf("nonfinite_rows=%llu\nerr=%.3e\nguards_ok=%d\ny_hash=%016llx\n", (unsigned long long)nonfinite, err,
+              guards_intact() ? 1 : 0, (unsigned long long)h);
+  std::fflush(stdout);
+  for (auto& al : g_allocs) std::free(al.first);
+  return 0;
+}
