@@ -44,24 +44,31 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+SORT_TILE = 8192                       # keys per sort tile (512 threads x 16 keys)
+ROUTE_BYTES = 2.0 + 1536.0 / SORT_TILE  # per element per routed pass: u16 tile-local position, plus
+                                       # u16 run starts and u32 run positions (256 digits) per tile
+
+
 def kernel_bytes(name: str, units: int, m: int, k: int = 0) -> float:
     """Algorithmic bytes of one launch: every array the kernel must touch, once,
     at its useful size (a random row access counts its 4m useful bytes).
     ``units`` = elements (rows) the launch processes; ``k`` = input anchors of
-    the general operator."""
-    route = 2.0 + 1536.0 / 4096.0   # u16 position per element + 1.5 KiB of digit tables per 4096-element tile
+    the general operator.  A sort pass moves 16 bytes per key (key and value
+    in and out; 12 in the first pass, which makes the indices), the figures of
+    the planned byte model; the route a pass records and the route passes
+    that move rows along it are bookkeeping, counted by overhead_bytes."""
     table = {
         "k_sort_hist": 4.0,                      # read anchors
         "k_onesweep_first": 12.0,                # read anchors; write keys and indices
         "k_onesweep_mid": 16.0,                  # read and write key + value
         "k_onesweep_last": 16.0,
-        "k_onesweep_first_routed": 12.0 + route,
-        "k_onesweep_mid_routed": 16.0 + route,
-        "k_onesweep_last_routed": 16.0 + route,
+        "k_onesweep_first_routed": 12.0,
+        "k_onesweep_mid_routed": 16.0,
+        "k_onesweep_last_routed": 16.0,
         "k_onesweep_first_pay": 16.0,            # read anchors and x; write keys and x
         "k_onesweep_last_pay": 16.0,             # read key + x; write sorted anchors and sorted x
-        "k_onesweep_first_pay_routed": 16.0 + route,
-        "k_onesweep_last_pay_routed": 16.0 + route,
+        "k_onesweep_first_pay_routed": 16.0,
+        "k_onesweep_last_pay_routed": 16.0,
         "k_sym_apply": 8.0 + 8.0 * m,            # sorted anchors, perm, sorted rows in, y rows out (random)
         "k_sym_reduce": 4.0 + 4.0 * m,           # sorted anchors, sorted rows
         "k_sym_apply_sorted": 4.0 + 8.0 * m,     # sorted anchors, sorted rows in, sorted rows out
@@ -85,8 +92,8 @@ def kernel_bytes(name: str, units: int, m: int, k: int = 0) -> float:
         "k_gram_dprefix": 12.0,                  # sorted weights in, float64 prefix out
     }
     for w in (1, 2, 3, 4):
-        table["k_route_fwd_w%d" % w] = route + 8.0 * w   # position, row in, row out
-        table["k_route_inv_w%d" % w] = route + 8.0 * w
+        table["k_route_fwd_w%d" % w] = 8.0 * w   # row in, row out
+        table["k_route_inv_w%d" % w] = 8.0 * w
     if name in table:
         return table[name] * units
     if name == "k_gbwd_apply":  # merged anchors, x and g rows in; da (n), db and dx rows (k) out
@@ -98,6 +105,31 @@ def kernel_bytes(name: str, units: int, m: int, k: int = 0) -> float:
     if name in ("k_gen_apply_sorted", "k_phased_gen_apply_sorted"):
         return (4.0 + 4.0 * m) * units + (4.0 + 4.0 * m) * k
     return 0.0
+
+
+def overhead_bytes(name: str, units: int) -> float:
+    """Route bookkeeping of one launch: the positions and run tables a routed
+    sort pass writes, or a route pass reads, ROUTE_BYTES per element."""
+    if name.startswith(("k_route_fwd", "k_route_inv")) or (name.startswith("k_onesweep") and name.endswith("_routed")):
+        return ROUTE_BYTES * units
+    return 0.0
+
+
+def model_step_bytes(kind: str, n: int, m: int, k: int) -> dict:
+    """Bytes one step must move by the planned byte model, whatever kernels
+    run: the sort 64 B per anchor (histogram 4, first pass 12, three passes of
+    16) and the apply (symmetric 16 + 28m per anchor: gather 4 + 8m, forward
+    scan 4 + 8m, suffix scan with combine and scatter 8 + 12m; phased
+    32 + 36m; general with sparse injections 24 per output anchor + O(k))."""
+    if kind == "sym":
+        sort, apply_ = 64.0 * n, (16.0 + 28.0 * m) * n
+    elif kind == "phased":
+        sort, apply_ = 64.0 * n, (32.0 + 36.0 * m) * n
+    elif kind == "general":
+        sort, apply_ = 64.0 * (n + k), 24.0 * n + (4.0 + 8.0 * m) * k
+    else:
+        return {}
+    return {"sort": sort, "apply": apply_, "step": sort + apply_}
 
 
 # rocprofv3 kernel names (template arguments stripped) -> launch labels
@@ -226,10 +258,34 @@ def rocprof_summary(stats_csv: str, fetch_csv: str, write_csv: str, workload: st
     return kernels_txt, "\n".join(c) + "\n"
 
 
+def host_info() -> dict:
+    """Host cores, CPU model and available memory, for the CPU baseline."""
+    info = {"nproc": os.cpu_count()}
+    try:
+        info["affinity_cores"] = len(os.sched_getaffinity(0))
+    except AttributeError:
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemAvailable"):
+                    info["mem_available_GB"] = round(int(line.split()[1]) / 2 ** 20, 1)
+    except OSError:
+        pass
+    return info
+
+
 def cpu_baseline(workload: str, log2_sample: int):
-    """The float64 oracle (sort + scans, one host core) on a bounded sample."""
+    """The float64 oracle on a bounded sample of the workload: on all host
+    cores (the OpenMP oracle, symmetric operator) and on one core (the
+    sequential C oracle, every operator), each repeated for about 10 s."""
     import oracle
-    from synth import make_workload, WORKLOADS
+    from synth import make_workload
 
     full = make_workload(workload, scale=0) if workload in ("sym4096",) else None
     n_full = {"sym4096": 4096, "sym2p20m16": 1 << 20, "gen2p24k2p16": 1 << 24, "phased3x1024x1024m8": 3 << 20,
@@ -242,39 +298,64 @@ def cpu_baseline(workload: str, log2_sample: int):
     w = full if full is not None else make_workload(workload, scale=scale)
     lib = oracle.load()
     from threadpoolctl import threadpool_limits
-    t0 = time.perf_counter()
-    reps = 0
-    with threadpool_limits(limits=1):  # one core for every leg (NumPy's BLAS in the Gram one)
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        reps = 0
         while True:
-            if w.kind == "sym":
-                oracle.sym_apply(w.a, w.x, lib=lib)
-            elif w.kind == "general":
-                oracle.general_apply(w.a, w.b, w.x, lib=lib)
-            elif w.kind == "gram":
-                oracle.gram_dense(w.a, w.b, w.D)
-            else:
-                oracle.phased_apply(w.a, w.phi, w.x, lib=lib)
+            fn()
             reps += 1
             dt = time.perf_counter() - t0
             if dt >= 10.0 or reps >= 1000:
-                break
-    elems = (w.n * w.n if w.kind == "gram" else w.n * w.m) * reps
+                return reps, dt
+
+    with threadpool_limits(limits=1):  # one core for the sequential leg (NumPy's BLAS in the Gram one)
+        if w.kind == "sym":
+            reps, dt = timed(lambda: oracle.sym_apply(w.a, w.x, lib=lib))
+        elif w.kind == "general":
+            reps, dt = timed(lambda: oracle.general_apply(w.a, w.b, w.x, lib=lib))
+        elif w.kind == "gram":
+            reps, dt = timed(lambda: oracle.gram_dense(w.a, w.b, w.D))
+        else:
+            reps, dt = timed(lambda: oracle.phased_apply(w.a, w.phi, w.x, lib=lib))
+    elems = (w.n * w.n if w.kind == "gram" else w.n * w.m)
     what = ("float64 dense definition of A diag(D) A^T (NumPy, one BLAS thread)" if w.kind == "gram"
             else "float64 C oracle incl. its sort")
-    return {
-        "value": elems / dt / 1e9,
-        "unit": "Gelem/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": "%s scaled to n=%d m=%d%s (same distributions), %d run(s) in %.1f s, %s" % (
-            workload, w.n, w.m, (" k=%d" % w.k) if w.kind in ("general", "gram") else "", reps, dt, what),
-    }
+    sample = "%s scaled to n=%d m=%d%s (same distributions)" % (
+        workload, w.n, w.m, (" k=%d" % w.k) if w.kind in ("general", "gram") else "")
+    single = {"value": elems * reps / dt / 1e9, "unit": "Gelem/s", "cores": 1, "kind": "oracle",
+              "sample": "%s, %d run(s) in %.1f s, %s" % (sample, reps, dt, what)}
+    if w.kind != "sym":
+        single["note"] = "the all-cores oracle covers the symmetric operator; this workload's baseline is one core"
+        single["host"] = host_info()
+        return single
+    threads = oracle.par_threads()
+    reps_p, dt_p = timed(lambda: oracle.sym_apply_par(w.a, w.x))
+    return {"value": elems * reps_p / dt_p / 1e9, "unit": "Gelem/s", "cores": threads, "kind": "oracle",
+            "sample": "%s, %d run(s) in %.1f s, float64 OpenMP oracle incl. its sort (merge sort split among the "
+                      "threads, chunked two-pass scan)" % (sample, reps_p, dt_p),
+            "single_core": single, "host": host_info()}
 
 
-def time_backward(lp, torch, bstep, n, m, k, args):
-    """The backward call `bstep` (for the sort handles of the timed steps and
-    a seeded upstream gradient): its own timed loop, reported beside the
-    forward step."""
+STEP_TARGET_FRAC = 0.60  # sustained fraction of peak HBM bandwidth the n = 2^30 symmetric step is held to
+
+
+def step_model(kind: str, n: int, m: int, k: int, ms: float):
+    """The step against the planned byte model: its bytes over the measured
+    step time, as a fraction of peak, beside the 60 % target."""
+    b = model_step_bytes(kind, n, m, k)
+    if not b:
+        return None
+    gbps = b["step"] / (ms * 1e-3) / 1e9
+    return {"bytes_per_step": b["step"], "sort_bytes": b["sort"], "apply_bytes": b["apply"],
+            "achieved_GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4), "target_frac": STEP_TARGET_FRAC,
+            "roofline_ms": round(b["step"] / (HBM_PEAK_GBPS * 1e9) * 1e3, 4)}
+
+
+def time_call(lp, torch, bstep, n, m, k, args):
+    """A call `bstep` other than the step (the backward for a seeded upstream
+    gradient, or the apply alone given a sort handle): its own timed loop,
+    reported beside the step."""
     for _ in range(args.warmup):
         bstep()
     torch.cuda.synchronize()
@@ -323,6 +404,7 @@ def main():
                          "laplex_sort_matvec_general (general: only b sorted, outputs search their interval)")
     ap.add_argument("--cpu-sample-log2", type=int, default=25)
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward (symmetric, general, phased)")
+    ap.add_argument("--no-apply-only", action="store_true", help="skip timing the apply alone given a sort handle")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing (steps after a 512 MiB scrub)")
     ap.add_argument("--no-graph", action="store_true", help="skip timing the step replayed from a HIP graph")
     ap.add_argument("--calib-copy", action="store_true",
@@ -479,10 +561,11 @@ def main():
     # per-kernel statistics from the launch events (each records its element count)
     stats = {}
     for name, ms, units in prof.records:
-        s_ = stats.setdefault(name, {"ms": 0.0, "launches": 0, "bytes": 0.0})
+        s_ = stats.setdefault(name, {"ms": 0.0, "launches": 0, "bytes": 0.0, "over": 0.0})
         s_["ms"] += ms
         s_["launches"] += 1
         s_["bytes"] += kernel_bytes(name, units, m, k)
+        s_["over"] += overhead_bytes(name, units)
     kernels = {}
     for name, s in stats.items():
         avg = s["ms"] / s["launches"]
@@ -493,6 +576,7 @@ def main():
             "avg_launch_ms": round(avg, 4),
             "alg_bytes_per_launch": bpl,
             "alg_GBps": round(bpl / (avg * 1e-3) / 1e9, 1) if avg > 0 else None,
+            "overhead_bytes_per_launch": s["over"] / s["launches"],
         }
     dom = max(stats, key=lambda q: stats[q]["ms"])
     dk = kernels[dom]
@@ -509,6 +593,8 @@ def main():
         "traffic": traffic,
         "alg_bytes_per_launch": dk["alg_bytes_per_launch"],
         "avg_launch_ms": dk["avg_launch_ms"],
+        # route bookkeeping the launch also moves (not algorithmic)
+        "overhead_bytes_per_launch": dk["overhead_bytes_per_launch"],
     }
     step_bytes = sum(s["bytes"] for s in stats.values()) / args.steps
 
@@ -547,6 +633,7 @@ def main():
                    "route": use_route and w.kind != "gram", "recipe": w.recipe},
         "roofline": roofline,
         "step_alg_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_model": step_model(w.kind, n, m, k, ms_per_step),
         "sort_part": part(sort_names),
         "apply_part": part(apply_names),
         "kernels": kernels,
@@ -592,9 +679,46 @@ def main():
                 lp.laplex_backward_general(a_s, pa, b_s, pb, x, g, dx=dx, da=da, db=db, ws=ws_b, route_a=ra,
                                            route_b=rb)
             what = "dx = K^T g, da and db, from x and g"
-        line["backward_part"] = time_backward(lp, torch, bstep, n, m, k, args)
+        line["backward_part"] = time_call(lp, torch, bstep, n, m, k, args)
         line["backward_part"]["outputs"] = what
         del ws_b
+    if w.kind in ("sym", "general", "phased") and not args.no_apply_only:
+        # the apply alone, given sort handles built beforehand (untimed): the
+        # figure for callers that sort once and apply many times
+        if one_call or one_call_gen:
+            del ws_apply
+            torch.cuda.empty_cache()
+            ra = lp.route_buffer(n, device=dev) if use_route else None
+            a_s, pa = torch.empty_like(a), torch.empty(n, dtype=torch.uint32, device=dev)
+            ws_sort_a = lp.workspace(lp.LAPLEX_OP_SORT, n, device=dev)
+        lp.laplex_sort_anchors(a, a_s, pa, route=ra, ws=ws_sort_a)
+        if w.kind == "general":
+            lp.laplex_sort_anchors(b, b_s, pb, route=rb, ws=ws_sort_b)
+            ws_ap = lp.workspace(lp.LAPLEX_OP_GENERAL, n, k, m, device=dev)
+
+            def astep():
+                lp.laplex_matvec_general(a_s, pa, b_s, pb, x, y=y, ws=ws_ap, route_a=ra, route_b=rb)
+        elif w.kind == "phased":
+            ws_ap = lp.workspace(lp.LAPLEX_OP_PHASED, n, 0, m, device=dev)
+
+            def astep():
+                lp.laplex_matvec_phased(a_s, pa, phi, x, y=y, ws=ws_ap, route_a=ra)
+        else:
+            ws_ap = lp.workspace(lp.LAPLEX_OP_SYM, n, 0, m, device=dev)
+
+            def astep():
+                lp.laplex_matvec_sym(a_s, pa, x, y=y, ws=ws_ap, route=ra)
+        torch.cuda.synchronize()
+        del ws_sort_a
+        ap = time_call(lp, torch, astep, n, m, k, args)
+        mb = model_step_bytes(w.kind, n, m, k)["apply"]
+        gbps = mb / (ap["ms_per_call"] * 1e-3) / 1e9
+        ap["model_bytes"] = mb
+        ap["model_GBps"] = round(gbps, 1)
+        ap["model_frac"] = round(gbps / HBM_PEAK_GBPS, 4)
+        ap["what"] = "y = K x given the sort handle%s" % (" and its route" if use_route else "")
+        line["apply_only"] = ap
+        del ws_ap
     if args.calib_copy:
         src_t = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst_t = torch.empty_like(src_t)

@@ -16,6 +16,10 @@ Two parts, both float64:
 * ``sym_apply`` / ``general_apply`` / ``phased_apply`` / ``stable_argsort``:
   the sequential scan algebra of section 2.2 ("Exact Scan Algebra") in plain C
   (``laplex_oracle.c``), O(n log n).
+* ``sym_apply_par`` / ``stable_argsort_par``: the same symmetric operator on
+  all host cores (``laplex_oracle_par.c``, OpenMP: a merge sort split among
+  the threads and a chunked two-pass scan), the CPU baseline of the
+  benchmark; checked against the one-core functions.
 
 Pins (the test-suite checks these against facts other than the oracle
 itself): the closed-form Kac-Murdock-Szego inverse for equispaced anchors, the
@@ -51,6 +55,59 @@ def build(force: bool = False, out: Optional[str] = None, src: Optional[str] = N
         subprocess.run(["gcc", "-O2", "-std=gnu11", "-fPIC", "-shared", "-o", tmp, src, "-lm"], check=True)
         os.replace(tmp, out)
     return out
+
+
+_SRC_PAR = os.path.join(_HERE, "laplex_oracle_par.c")
+_SO_PAR = os.path.join(_HERE, "liblaplex_oracle_par.so")
+_par_handle = None
+
+
+def build_par(force: bool = False) -> str:
+    """Compile the all-cores oracle with gcc -fopenmp."""
+    if force or not os.path.exists(_SO_PAR) or os.path.getmtime(_SO_PAR) < os.path.getmtime(_SRC_PAR):
+        tmp = _SO_PAR + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-std=gnu11", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC_PAR, "-lm"], check=True)
+        os.replace(tmp, _SO_PAR)
+    return _SO_PAR
+
+
+def load_par():
+    """Load (building if needed) the all-cores oracle."""
+    global _par_handle
+    with _lock:
+        if _par_handle is None:
+            lib = ctypes.CDLL(build_par())
+            i64 = ctypes.c_int64
+            lib.lop_stable_argsort.argtypes = [ctypes.POINTER(ctypes.c_float), i64, ctypes.POINTER(ctypes.c_uint32)]
+            lib.lop_sym_apply.argtypes = [ctypes.POINTER(ctypes.c_float), i64, i64, ctypes.POINTER(ctypes.c_float),
+                                          ctypes.POINTER(ctypes.c_double)]
+            for fn in (lib.lop_stable_argsort, lib.lop_sym_apply, lib.lop_threads):
+                fn.restype = ctypes.c_int
+            _par_handle = lib
+        return _par_handle
+
+
+def par_threads() -> int:
+    """OpenMP threads the all-cores oracle runs on (OMP_NUM_THREADS or the host's cores)."""
+    return int(load_par().lop_threads())
+
+
+def stable_argsort_par(a) -> np.ndarray:
+    """stable_argsort on all host cores."""
+    a = _f32(a).ravel()
+    perm = np.empty(a.size, np.uint32)
+    _check(load_par().lop_stable_argsort(_ptr(a, ctypes.c_float), a.size, _ptr(perm, ctypes.c_uint32)))
+    return perm
+
+
+def sym_apply_par(a, x) -> np.ndarray:
+    """sym_apply on all host cores (float64, n x m)."""
+    a = _f32(a).ravel()
+    x2 = _as2d(x, a.size)
+    y = np.empty(x2.shape, np.float64)
+    _check(load_par().lop_sym_apply(_ptr(a, ctypes.c_float), a.size, x2.shape[1], _ptr(x2, ctypes.c_float),
+                                    _ptr(y, ctypes.c_double)))
+    return y
 
 
 def load(path: Optional[str] = None):
