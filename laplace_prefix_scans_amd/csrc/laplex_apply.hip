@@ -797,6 +797,63 @@ __device__ __forceinline__ uint32_t pbwdcol(uint32_t m, uint32_t cc, int j) {
 constexpr int pbwd_items(int c) { return apply_items(4 * c); }
 constexpr int pbwd_block(int c) { return apply_block(4 * c); }
 
+// Column slices of a tile's rows staged in LDS.  The phased backward scans
+// one input column per pass; reading that column straight from the
+// row-major arrays would fetch every row once per column.  Instead the
+// tile's rows [lo, lo + P), columns [c0, c0 + w) (w <= kStageCols) are
+// loaded once, as 16-byte pieces when the layout allows, and kept column by
+// column: s[j * P + r] = x[(lo + r) * m + c0 + j], zero past row n; a
+// thread's E consecutive rows of one column are then one LDS vector read.
+constexpr uint32_t kStageCols = 4;
+template <int P, int BLOCK>
+__device__ __forceinline__ void stage_cols(const float* __restrict__ x, uint64_t lo, uint64_t n, uint32_t m, uint32_t c0,
+                                           uint32_t w, bool vec4, float* __restrict__ s) {
+  const uint32_t rows = (uint32_t)std::min<uint64_t>((uint64_t)P, n - lo);
+  if (vec4 && w == 4) {
+    for (uint32_t r = threadIdx.x; r < (uint32_t)P; r += BLOCK) {
+      const float4 q = r < rows ? *reinterpret_cast<const float4*>(x + (lo + r) * m + c0) : make_float4(0.f, 0.f, 0.f, 0.f);
+      s[0 * P + r] = q.x;
+      s[1 * P + r] = q.y;
+      s[2 * P + r] = q.z;
+      s[3 * P + r] = q.w;
+    }
+  } else {
+    for (uint32_t q = threadIdx.x; q < (uint32_t)P * w; q += BLOCK) {
+      const uint32_t r = q / w, j = q - r * w;
+      s[j * P + r] = r < rows ? x[(lo + r) * m + c0 + j] : 0.f;
+    }
+  }
+}
+// The reverse: rows [lo, lo + P) (up to n), columns [c0, c0 + w) of y from s.
+template <int P, int BLOCK>
+__device__ __forceinline__ void unstage_cols(float* __restrict__ y, uint64_t lo, uint64_t n, uint32_t m, uint32_t c0, uint32_t w,
+                                             bool vec4, const float* __restrict__ s) {
+  const uint32_t rows = (uint32_t)std::min<uint64_t>((uint64_t)P, n - lo);
+  if (vec4 && w == 4) {
+    for (uint32_t r = threadIdx.x; r < rows; r += BLOCK)
+      *reinterpret_cast<float4*>(y + (lo + r) * m + c0) = make_float4(s[r], s[P + r], s[2 * P + r], s[3 * P + r]);
+  } else {
+    for (uint32_t q = threadIdx.x; q < rows * w; q += BLOCK) {
+      const uint32_t r = q / w, j = q - r * w;
+      y[(lo + r) * m + c0 + j] = s[j * P + r];
+    }
+  }
+}
+// a thread's E consecutive rows (local p) of staged column j
+template <int E, int P>
+__device__ __forceinline__ void staged_rows(const float* s, uint32_t j, uint32_t p, float (&v)[E][1]) {
+  if constexpr (E == 4) {
+    const float4 q = *reinterpret_cast<const float4*>(s + j * P + p);
+    v[0][0] = q.x;
+    v[1][0] = q.y;
+    v[2][0] = q.z;
+    v[3][0] = q.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e][0] = s[j * P + p + e];
+  }
+}
+
 // the four scanned values of element e, column j
 template <int E, int C>
 __device__ __forceinline__ void phased_quad(const float (&cs)[E], const float (&sn)[E], const float (&xv)[E][C],
@@ -843,10 +900,21 @@ __global__ __launch_bounds__(pbwd_block(C)) void k_pbwd_reduce(const float* __re
     tf[e] = valid ? decay_m<true>(ae[e] - s_last) : 0.f;
     tb[e] = valid ? decay_m<true>(s_first - ae[e]) : 0.f;
   }
-  for (uint32_t cc = 0; cc < m / C; ++cc) {
+  static_assert(C == 1, "one input column per pass");
+  __shared__ float s_x[kStageCols * P], s_g[kStageCols * P];
+  const bool vec4 = (m % 4 == 0) && (reinterpret_cast<uintptr_t>(xs) % 16 == 0) && (reinterpret_cast<uintptr_t>(gs) % 16 == 0);
+  for (uint32_t cc = 0; cc < m; ++cc) {
+    const uint32_t j0 = cc % kStageCols;
+    if (j0 == 0) {  // the next slice of columns, loaded once for the whole tile
+      const uint32_t w = std::min<uint32_t>(kStageCols, m - cc);
+      __syncthreads();
+      stage_cols<P, BLOCK>(xs, lo, n, m, cc, w, vec4, s_x);
+      stage_cols<P, BLOCK>(gs, lo, n, m, cc, w, vec4, s_g);
+      __syncthreads();
+    }
     float xv[E][C], gv[E][C], v[E][4 * C];
-    load_rows<E, C>(xs, p0, n, m, cc, true, xv);
-    load_rows<E, C>(gs, p0, n, m, cc, true, gv);
+    staged_rows<E, P>(s_x, j0, (uint32_t)tid * E, xv);
+    staged_rows<E, P>(s_g, j0, (uint32_t)tid * E, gv);
     phased_quad<E, C>(cs, sn, xv, gv, v);
     float sf[CC], sb[CC];
 #pragma unroll
@@ -904,10 +972,23 @@ __global__ __launch_bounds__(pbwd_block(C)) void k_pbwd_apply(const float* __res
   float acc[E], acc0[E], dph[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = acc0[e] = dph[e] = 0.f;
-  for (uint32_t cc = 0; cc < m / C; ++cc) {
+  static_assert(C == 1, "one input column per pass");
+  __shared__ float s_x[kStageCols * P], s_g[kStageCols * P], s_dx[kStageCols * P];
+  const uint64_t lo = tile * P;
+  const bool vec4 = (m % 4 == 0) && (reinterpret_cast<uintptr_t>(xs) % 16 == 0) && (reinterpret_cast<uintptr_t>(gs) % 16 == 0) &&
+                    (reinterpret_cast<uintptr_t>(dxs) % 16 == 0);
+  for (uint32_t cc = 0; cc < m; ++cc) {
+    const uint32_t j0 = cc % kStageCols;
+    if (j0 == 0) {  // the next slice of columns, loaded once for the whole tile
+      const uint32_t w = std::min<uint32_t>(kStageCols, m - cc);
+      __syncthreads();
+      stage_cols<P, BLOCK>(xs, lo, n, m, cc, w, vec4, s_x);
+      stage_cols<P, BLOCK>(gs, lo, n, m, cc, w, vec4, s_g);
+      __syncthreads();
+    }
     float xv[E][C], gv[E][C], v[E][CC];
-    load_rows<E, C>(xs, p0, n, m, cc, true, xv);
-    load_rows<E, C>(gs, p0, n, m, cc, true, gv);
+    staged_rows<E, P>(s_x, j0, (uint32_t)tid * E, xv);
+    staged_rows<E, P>(s_g, j0, (uint32_t)tid * E, gv);
     phased_quad<E, C>(cs, sn, xv, gv, v);
     {
       // both decays in one scan of [v | v]: the tie half first (F0, U0),
@@ -950,9 +1031,13 @@ __global__ __launch_bounds__(pbwd_block(C)) void k_pbwd_apply(const float* __res
           dph[e] = fmaf(xv[e][j], fmaf(cs[e], ksg, -sn[e] * kcg), dph[e]);
           dx[e][j] = fmaf(cs[e], kcg, sn[e] * ksg);
         }
-      store_rows<E, C>(dxs, p0, n, m, cc, true, dx);
+#pragma unroll
+      for (int e = 0; e < E; ++e) s_dx[j0 * P + (uint32_t)tid * E + e] = dx[e][0];
     }
     __syncthreads();
+    const uint32_t w = std::min<uint32_t>(kStageCols, m - (cc - j0));
+    if (j0 + 1 == w)  // the slice's dx, written back as row pieces
+      unstage_cols<P, BLOCK>(dxs, lo, n, m, cc - j0, w, vec4, s_dx);
   }
   float dav[E][1], dpv[E][1];
 #pragma unroll

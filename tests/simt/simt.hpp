@@ -142,7 +142,9 @@ inline void poison_lds() {
 }
 
 // Run `body` for every workgroup of grid (x, y) whose flat index `keep`
-// accepts, one workgroup at a time, each with block.x threads.
+// accepts, one workgroup at a time: block.x threads are started once per
+// launch and step through the workgroups together (a barrier before and
+// after each, the shared memory poisoned in between).
 template <typename F, typename K>
 void launch(dim3 grid, dim3 block, F body, K keep) {
   const unsigned nt = block.x;
@@ -150,34 +152,42 @@ void launch(dim3 grid, dim3 block, F body, K keep) {
     std::fprintf(stderr, "simt: workgroup size %u is not a multiple of %d\n", nt, kLanes);
     std::abort();
   }
-  const unsigned nw = nt / kLanes;
+  std::vector<dim3> blocks;
   for (unsigned by = 0; by < grid.y; ++by)
-    for (unsigned bx = 0; bx < grid.x; ++bx) {
-      if (!keep((uint64_t)by * grid.x + bx)) continue;
-      poison_lds();
-      Block b;
-      pthread_barrier_init(&b.bar, nullptr, nt);
-      std::vector<Wave> waves(nw);
-      for (auto& w : waves) pthread_barrier_init(&w.bar, nullptr, kLanes);
-      std::vector<std::thread> ts;
-      ts.reserve(nt);
-      for (unsigned t = 0; t < nt; ++t)
-        ts.emplace_back([&, t] {
-          Ctx& c = g_ctx;
-          c.tid = dim3(t);
-          c.bid = dim3(bx, by);
-          c.bdim = block;
-          c.gdim = grid;
-          c.lane = (int)(t % kLanes);
-          c.parity = 0;
-          c.wave = &waves[t / kLanes];
-          c.block = &b;
-          body();
-        });
-      for (auto& th : ts) th.join();
-      for (auto& w : waves) pthread_barrier_destroy(&w.bar);
-      pthread_barrier_destroy(&b.bar);
-    }
+    for (unsigned bx = 0; bx < grid.x; ++bx)
+      if (keep((uint64_t)by * grid.x + bx)) blocks.push_back(dim3(bx, by));
+  if (blocks.empty()) return;
+  const unsigned nw = nt / kLanes;
+  Block b;
+  pthread_barrier_init(&b.bar, nullptr, nt);
+  pthread_barrier_t step;
+  pthread_barrier_init(&step, nullptr, nt);
+  std::vector<Wave> waves(nw);
+  for (auto& w : waves) pthread_barrier_init(&w.bar, nullptr, kLanes);
+  std::vector<std::thread> ts;
+  ts.reserve(nt);
+  for (unsigned t = 0; t < nt; ++t)
+    ts.emplace_back([&, t] {
+      Ctx& c = g_ctx;
+      c.tid = dim3(t);
+      c.bdim = block;
+      c.gdim = grid;
+      c.lane = (int)(t % kLanes);
+      c.wave = &waves[t / kLanes];
+      c.block = &b;
+      for (const dim3& bid : blocks) {
+        if (t == 0) poison_lds();
+        pthread_barrier_wait(&step);
+        c.bid = bid;
+        c.parity = 0;
+        body();
+        pthread_barrier_wait(&step);
+      }
+    });
+  for (auto& th : ts) th.join();
+  for (auto& w : waves) pthread_barrier_destroy(&w.bar);
+  pthread_barrier_destroy(&step);
+  pthread_barrier_destroy(&b.bar);
 }
 template <typename F>
 void launch(dim3 grid, dim3 block, F body) {
