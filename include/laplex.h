@@ -50,7 +50,8 @@ typedef enum {
   LAPLEX_ERR_HIP = 6,        /* a HIP launch or runtime call failed */
   LAPLEX_ERR_OVERLAP = 7,    /* an output overlaps an input or the workspace */
   LAPLEX_ERR_STALLED = 8,    /* a look-back wait hit its spin limit (reported by laplex_status_poll) */
-  LAPLEX_ERR_ARG = 9         /* any other invalid argument */
+  LAPLEX_ERR_ARG = 9,        /* any other invalid argument */
+  LAPLEX_ERR_SCRATCH = 10    /* the call needs more than LAPLEX_SCRATCH_BYTES of static scratch */
 } laplex_status;
 
 /* Operations, for laplex_workspace_bytes. */
@@ -107,6 +108,24 @@ laplex_status laplex_status_poll(const void* ws, hipStream_t stream);
  * ws: laplex_workspace_bytes(LAPLEX_OP_SYM, n, 0, m) bytes. */
 laplex_status laplex_matvec_sym(const float* a_sorted, const uint32_t* perm, const void* route, uint64_t n, uint32_t m,
                                 const float* x, float* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* laplex_matvec_sym without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is the library's static
+ * device scratch array of LAPLEX_SCRATCH_BYTES, one per GPU, held from the
+ * first call on that GPU until the process ends; its device address is
+ * looked up once per GPU (hipGetSymbolAddress, on the stream's device) and
+ * the call allocates nothing.  Arguments, layout and results as
+ * laplex_matvec_sym (bitwise the same output).  The call fits when
+ * laplex_workspace_bytes(LAPLEX_OP_SYM, n, 0, m) <= LAPLEX_SCRATCH_BYTES
+ * (e.g. n * m up to about 4 * 2^20 with a route); larger calls return
+ * LAPLEX_ERR_SCRATCH before launching anything.  Every call on one GPU uses
+ * the same scratch and keeps nothing from the last call in it: calls that
+ * overlap in time on one GPU (different streams, or host threads) race and
+ * must be serialised by the caller. */
+#define LAPLEX_SCRATCH_BYTES (64ull << 20)
+laplex_status laplex_matvec_sym_noalloc(const float* a_sorted, const uint32_t* perm, const void* route, uint64_t n, uint32_t m,
+                                        const float* x, float* y, hipStream_t stream);
 
 /* The symmetric operator from unsorted anchors in one call: the sort of
  * laplex_sort_anchors followed by laplex_matvec_sym (section 2.2, symmetric

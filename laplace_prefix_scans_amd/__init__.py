@@ -41,6 +41,8 @@ from ._binding import (  # noqa: F401
     laplex_matvec_general,
     laplex_matvec_phased,
     laplex_matvec_sym,
+    laplex_matvec_sym_noalloc,
+    LAPLEX_SCRATCH_BYTES,
     laplex_sort_matvec_general,
     laplex_sort_matvec_sym,
     laplex_sort_matvec_sym_backward,

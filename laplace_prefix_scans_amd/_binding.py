@@ -23,7 +23,9 @@ LAPLEX_OP_SORT_GENERAL = 11
 _STATUS = {
     0: "LAPLEX_OK", 1: "LAPLEX_ERR_NULL", 2: "LAPLEX_ERR_SIZE", 3: "LAPLEX_ERR_ALIGN", 4: "LAPLEX_ERR_WORKSPACE",
     5: "LAPLEX_ERR_NONFINITE", 6: "LAPLEX_ERR_HIP", 7: "LAPLEX_ERR_OVERLAP", 8: "LAPLEX_ERR_STALLED", 9: "LAPLEX_ERR_ARG",
+    10: "LAPLEX_ERR_SCRATCH",
 }
+LAPLEX_SCRATCH_BYTES = 64 << 20  # include/laplex.h
 
 _lock = threading.Lock()
 _lib = None
@@ -57,6 +59,8 @@ def lib():
         L.laplex_sort_anchors.argtypes = [vp, u64, vp, vp, vp, sz, vp, sz, vp]
         L.laplex_status_poll.argtypes = [vp, vp]
         L.laplex_matvec_sym.argtypes = [vp, vp, vp, u64, u32, vp, vp, vp, sz, vp]
+        L.laplex_matvec_sym_noalloc.argtypes = [vp, vp, vp, u64, u32, vp, vp, vp]
+        L.laplex_matvec_sym_noalloc.restype = i32
         L.laplex_sort_matvec_sym.argtypes = [vp, u64, u32, vp, vp, vp, sz, vp]
         L.laplex_sort_matvec_sym.restype = i32
         L.laplex_sort_matvec_sym_backward.argtypes = [vp, sz, u64, u32, vp, vp, vp, vp, sz, vp]
@@ -197,6 +201,23 @@ def laplex_matvec_sym(a_sorted: torch.Tensor, perm: torch.Tensor, x: torch.Tenso
     ws = _ws(ws, LAPLEX_OP_SYM, n, 0, m, dev)
     _check(lib().laplex_matvec_sym(_ptr(a_sorted), _ptr(perm), _ptr(route), n, m, _ptr(x), _ptr(y), _ptr(ws), ws.numel(),
                                    _stream(dev)), "laplex_matvec_sym")
+    return y
+
+
+def laplex_matvec_sym_noalloc(a_sorted: torch.Tensor, perm: torch.Tensor, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                              route: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """laplex_matvec_sym with the library's static device scratch as its
+    workspace: the library call allocates nothing (pass y to allocate
+    nothing here either).  Fits when laplex_workspace_bytes(LAPLEX_OP_SYM, n,
+    0, m) <= LAPLEX_SCRATCH_BYTES; calls overlapping in time on one GPU race."""
+    _vec(a_sorted, "a_sorted")
+    _vec(perm, "perm", torch.uint32)
+    n, dev = a_sorted.shape[0], a_sorted.device
+    m = _cols(x, n)
+    y = torch.empty_like(x) if y is None else y
+    _cols(y, n, "y")
+    _check(lib().laplex_matvec_sym_noalloc(_ptr(a_sorted), _ptr(perm), _ptr(route), n, m, _ptr(x), _ptr(y), _stream(dev)),
+           "laplex_matvec_sym_noalloc")
     return y
 
 

@@ -1,6 +1,8 @@
 // C-ABI entry points: argument checks, workspace layout, launches.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "../../include/laplex.h"
 #include "laplex_kernels.hpp"
 
@@ -318,6 +320,53 @@ extern "C" laplex_status laplex_matvec_sym(const float* a_sorted, const uint32_t
   SortRoute r{};
   if (route) r = carve_route(route, n);
   return from_hip(apply_sym(w, Variant::Sym, a_sorted, perm, route ? &r : nullptr, nullptr, n, m, x, y, stream));
+}
+
+// ------------------------------------------------------------------ allocation-free variant
+// The workspace of laplex_matvec_sym_noalloc: one static array per GPU.  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// its device address comes from hipGetSymbolAddress, looked up once per
+// device with that device current, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[LAPLEX_SCRATCH_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// Device address of the scratch array on the device of `stream` (the current
+// device for the null stream).
+laplex_status scratch_address(hipStream_t stream, void** out) {
+  int cur = -1, dev = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return LAPLEX_ERR_HIP;
+  dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return LAPLEX_ERR_HIP;
+  if (dev < 0 || dev >= kScratchDevices) return LAPLEX_ERR_ARG;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return LAPLEX_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return LAPLEX_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LAPLEX_OK;
+}
+}  // namespace
+
+extern "C" laplex_status laplex_matvec_sym_noalloc(const float* a_sorted, const uint32_t* perm, const void* route, uint64_t n,
+                                                   uint32_t m, const float* x, float* y, hipStream_t stream) {
+  if (n == 0 || m == 0) return LAPLEX_OK;
+  if (n > kMaxLen || m > kMaxCols) return LAPLEX_ERR_SIZE;
+  size_t need = 0;
+  carve_apply(nullptr, n, n, n, m, Variant::Sym, false, &need);
+  if (need > LAPLEX_SCRATCH_BYTES) return LAPLEX_ERR_SCRATCH;
+  void* ws = nullptr;
+  const laplex_status st = scratch_address(stream, &ws);
+  if (st != LAPLEX_OK) return st;
+  return laplex_matvec_sym(a_sorted, perm, route, n, m, x, y, ws, LAPLEX_SCRATCH_BYTES, stream);
 }
 
 extern "C" laplex_status laplex_sort_matvec_sym(const float* a, uint64_t n, uint32_t m, const float* x, float* y, void* ws,
@@ -676,6 +725,7 @@ extern "C" const char* laplex_status_string(laplex_status s) {
     case LAPLEX_ERR_OVERLAP: return "an output overlaps an input or the workspace";
     case LAPLEX_ERR_STALLED: return "a look-back wait hit its spin limit";
     case LAPLEX_ERR_ARG: return "invalid argument";
+    case LAPLEX_ERR_SCRATCH: return "call too large for the static scratch (LAPLEX_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

@@ -78,6 +78,13 @@ def test_host_argument_errors(L):
     # overlap: y on top of x
     need = L.laplex_workspace_bytes(1, 1000, 0, 1)
     assert L.laplex_matvec_sym(A, vp(0x300000), None, 1000, 1, vp(0x500000), vp(0x500100), vp(0x10000000), need, None) == OVERLAP
+    # the allocation-free variant refuses calls larger than its static scratch before any HIP call
+    import laplace_prefix_scans_amd as lp
+    big = 1 << 22
+    assert lp.laplex_workspace_bytes(lp.LAPLEX_OP_SYM, big, 0, 4) > lp.LAPLEX_SCRATCH_BYTES
+    assert L.laplex_matvec_sym_noalloc(A, B, None, big, 4, A, B, None) == 10
+    assert L.laplex_matvec_sym_noalloc(A, B, None, 0, 4, A, B, None) == OK
+    assert L.laplex_matvec_sym_noalloc(A, B, None, 1 << 32, 1, A, B, None) == SIZE
     assert L.laplex_sort_anchors(A, 1000, vp(0x100100), vp(0x300000), None, 0, vp(0x10000000), 1 << 30, None) == OVERLAP
     # general without b
     need = L.laplex_workspace_bytes(2, 100, 50, 1)
