@@ -97,7 +97,13 @@ laplex_status laplex_sort_anchors(const float* a, uint64_t n, float* a_sorted, u
                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Waits for `stream`, then returns the sticky device-side status of the last
- * sort that used `ws` (LAPLEX_OK, LAPLEX_ERR_NONFINITE or LAPLEX_ERR_STALLED). */
+ * sort that used `ws` (LAPLEX_OK, LAPLEX_ERR_NONFINITE or LAPLEX_ERR_STALLED).
+ * A look-back wait that reaches its spin limit gives up: the watchdog flag is
+ * raised, the remaining passes stop at once, every kernel exits, and the
+ * sort's outputs are undefined.  For failure-path tests,
+ * LAPLEX_DEBUG_STALL=<k> in the environment makes laplex_sort_anchors (only
+ * this entry point) run its look-back passes without publishing and with a
+ * spin limit of k, which forces that path. */
 laplex_status laplex_status_poll(const void* ws, hipStream_t stream);
 
 /* Symmetric operator y = LAPLEX(a, a) x (section 2.2, symmetric case: lower

@@ -279,7 +279,7 @@ extern "C" laplex_status laplex_sort_anchors(const float* a, uint64_t n, float* 
   const SortWorkspace w = carve_sort(ws, n);
   SortRoute r{};
   if (route) r = carve_route(route, n);
-  return from_hip(sort_anchors(w, a, n, a_sorted, perm, route ? &r : nullptr, stream));
+  return from_hip(sort_anchors(w, a, n, a_sorted, perm, route ? &r : nullptr, stream, true));
 }
 
 extern "C" laplex_status laplex_status_poll(const void* ws, hipStream_t stream) {

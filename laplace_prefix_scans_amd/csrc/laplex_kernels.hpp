@@ -64,8 +64,10 @@ size_t route_bytes(uint64_t n);
 SortRoute carve_route(const void* base, uint64_t n);
 
 size_t sort_status_bytes(uint64_t n);
+// debug_stall: honour LAPLEX_DEBUG_STALL (only the standalone sort entry
+// point does, so that no apply ever runs on a stalled sort's outputs).
 hipError_t sort_anchors(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,
-                        const SortRoute* route, hipStream_t s);
+                        const SortRoute* route, hipStream_t s, bool debug_stall = false);
 // The same sort with x (n floats, original order) carried along as the
 // value of each key in place of its index: writes x in sorted order to
 // x_sorted, and no permutation (the route, if given, still records the

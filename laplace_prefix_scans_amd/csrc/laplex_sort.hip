@@ -10,6 +10,8 @@
 // the previous pass has run, publish per-digit counts and look back over
 // earlier tiles (decoupled look-back).  Pass 1 generates the identity
 // permutation itself; pass 4 writes the sorted anchors and the permutation.
+#include <cstdlib>
+
 #include "laplex_kernels.hpp"
 
 namespace laplex {
@@ -248,7 +250,7 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
                                                          uint16_t* __restrict__ r_lpos, uint16_t* __restrict__ r_dstart,
                                                          uint32_t* __restrict__ r_gbase, const uint32_t* __restrict__ pay,
                                                          const uint32_t* __restrict__ tcount, const uint32_t* __restrict__ bpre,
-                                                         uint64_t chunks_per_block) {
+                                                         uint64_t chunks_per_block, uint32_t spin_limit, bool publish) {
   static_assert(!PAY || MODE != 1, "the payload enters in pass 1 and leaves in pass 4");
   constexpr bool HOLDV = MODE != 0 || PAY;  // values held in registers (else recomputed input indices)
   static_assert(kSortBlock % 256 == 0, "at least one thread per digit value");
@@ -260,6 +262,7 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
   __shared__ uint32_t s_gbase[256];
   __shared__ uint32_t s_wsum[4];
   __shared__ uint32_t s_tile;
+  __shared__ uint32_t s_stop;
   __shared__ uint32_t s_thist[256];
 
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
@@ -277,9 +280,14 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
   uint64_t xtile = 0;
   if (table && !xcd_tile((n + TILE - 1) / TILE, xtile)) return;
   if (!table && tid == 0) s_tile = atomicAdd(&header[kHdrTicket0 + pass], 1u);
+  // after a look-back that gave up (watchdog flag) the keys are no longer a
+  // permutation of the input: this pass stops at once, the whole workgroup
+  // together (its successors' bounded waits then give up too)
+  if (tid == 0) s_stop = (load_agent(&header[kHdrFlags]) & kFlagWatchdog) != 0u;
   for (int i = tid; i < NW * 256; i += kSortBlock) s_match[i] = make_uint4(0u, 0u, 0u, 0u);
   if (tid < 256) s_thist[tid] = 0u;
   __syncthreads();
+  if (s_stop) return;
   const uint32_t tile = table ? (uint32_t)xtile : s_tile;
   // uniform: one scalar value for the whole workgroup
   const bool early = !table && __builtin_amdgcn_readfirstlane(header[kHdrEarly0 + pass]) != 0u;
@@ -321,7 +329,7 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
       if (idx < n) atomicAdd(&s_thist[(k[e] >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid < 256)
+    if (tid < 256 && publish)
       store_agent(status + (uint64_t)tile * 256 + tid,
                   Status<ST>::pack(tile == 0 ? kFlagInclusive : kFlagAggregate, s_thist[tid]));
   }
@@ -389,7 +397,7 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
     // nor looks back, which spares most of the status traffic of a pass
     // whose digit takes few values)
     ST* my = status + (uint64_t)tile * 256 + d;
-    if (!early) store_agent(my, Status<ST>::pack(tile == 0 ? kFlagInclusive : kFlagAggregate, cnt));
+    if (!early && publish) store_agent(my, Status<ST>::pack(tile == 0 ? kFlagInclusive : kFlagAggregate, cnt));
     if (tile > 0) {
       int64_t t = (int64_t)tile - 1;
       uint32_t spins = 0;
@@ -412,7 +420,7 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
         if (!done) {
           t -= used;
           if (used == 0) {
-            if (++spins > kSpinLimit) {
+            if (++spins > spin_limit) {
               atomicOr(&header[kHdrFlags], kFlagWatchdog);
               break;
             }
@@ -420,7 +428,7 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
           }
         }
       }
-      store_agent(my, Status<ST>::pack(kFlagInclusive, excl + cnt));
+      if (publish) store_agent(my, Status<ST>::pack(kFlagInclusive, excl + cnt));
     }
   }
   __syncthreads();
@@ -517,10 +525,24 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
 // ride along with the keys (pass 4 writes them, sorted, to perm).
 // table: the first pass takes its offsets from the histogram's tables
 // (tcount and the scanned block sums, cpb chunks per histogram block).
+// Forced stall (failure-path tests): LAPLEX_DEBUG_STALL=<k> in the
+// environment makes the look-back passes publish nothing and give up after
+// k spins, so every look-back wait ends at its limit, the watchdog flag is
+// raised and laplex_status_poll reports a stall; every kernel still exits.
+static uint32_t debug_stall_spins() {
+  const char* e = std::getenv("LAPLEX_DEBUG_STALL");
+  if (!e || !*e) return 0;
+  const unsigned long v = std::strtoul(e, nullptr, 10);
+  return (uint32_t)std::min<unsigned long>(v, kSpinLimit);
+}
+
 template <typename ST>
 static hipError_t launch_sort_passes(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,
                                      const SortRoute* route, const uint32_t* pay, bool table, uint64_t cpb,
-                                     hipStream_t s) {
+                                     hipStream_t s, bool debug) {
+  const uint32_t dbg = debug ? debug_stall_spins() : 0u;
+  const uint32_t spin_limit = dbg ? dbg : kSpinLimit;
+  const bool publish = dbg == 0;
   const uint32_t* a_bits = reinterpret_cast<const uint32_t*>(a);
   const uint64_t tiles = (n + kSortTile - 1) / kSortTile;
   ST* st = reinterpret_cast<ST*>(w.status);
@@ -538,7 +560,7 @@ static hipError_t launch_sort_passes(const SortWorkspace& w, const float* a, uin
   LAPLEX_LAUNCH(NAME, n, s,                                                                                          \
                 (k_onesweep<MODE, ST, PAY><<<(MODE == 0 && table ? grid0 : grid), block, 0, s>>>(                     \
                     src, dst, fk, fv, a_bits, stp, w.header, p, w.offsets + p * 256, n, rl, rd, rg, pay,                \
-                    MODE == 0 && table ? w.tcount : nullptr, w.gsum, cpb)))
+                    MODE == 0 && table ? w.tcount : nullptr, w.gsum, cpb, spin_limit, publish)))
     if (p == 0 && pay)
       LAPLEX_PASS(0, true, route ? "k_onesweep_first_pay_routed" : "k_onesweep_first_pay");
     else if (p == 0)
@@ -564,7 +586,7 @@ size_t sort_status_bytes(uint64_t n) {
 }
 
 static hipError_t sort_impl(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,
-                            const SortRoute* route, const uint32_t* pay, hipStream_t s) {
+                            const SortRoute* route, const uint32_t* pay, hipStream_t s, bool debug) {
   if (n == 0) return hipSuccess;
   // clear the header, histograms and look-back status with a fill kernel
   const uint64_t clear_words = (uint64_t)(kSortHeaderBytes / 4) + sort_status_bytes(n) / 4;
@@ -585,18 +607,19 @@ static hipError_t sort_impl(const SortWorkspace& w, const float* a, uint64_t n, 
   LAPLEX_LAUNCH("k_sort_offsets", 1024, s,
                 k_sort_offsets<<<1, kScanThreads, 0, s>>>(w.hist, w.offsets, w.header, w.gsum, table ? hist_blocks : 0));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (n <= (1ull << 30)) return launch_sort_passes<uint32_t>(w, a, n, a_sorted, perm, route, pay, table, cpb, s);
-  return launch_sort_passes<uint64_t>(w, a, n, a_sorted, perm, route, pay, table, cpb, s);
+  if (n <= (1ull << 30)) return launch_sort_passes<uint32_t>(w, a, n, a_sorted, perm, route, pay, table, cpb, s, debug);
+  return launch_sort_passes<uint64_t>(w, a, n, a_sorted, perm, route, pay, table, cpb, s, debug);
 }
 
 hipError_t sort_anchors(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,
-                        const SortRoute* route, hipStream_t s) {
-  return sort_impl(w, a, n, a_sorted, perm, route, nullptr, s);
+                        const SortRoute* route, hipStream_t s, bool debug_stall) {
+  return sort_impl(w, a, n, a_sorted, perm, route, nullptr, s, debug_stall);
 }
 
 hipError_t sort_anchors_payload(const SortWorkspace& w, const float* a, const float* x, uint64_t n, float* a_sorted,
                                 float* x_sorted, const SortRoute* route, hipStream_t s) {
-  return sort_impl(w, a, n, a_sorted, reinterpret_cast<uint32_t*>(x_sorted), route, reinterpret_cast<const uint32_t*>(x), s);
+  return sort_impl(w, a, n, a_sorted, reinterpret_cast<uint32_t*>(x_sorted), route, reinterpret_cast<const uint32_t*>(x), s,
+                   false);
 }
 
 }  // namespace laplex

@@ -44,7 +44,8 @@ def test_sym_route_bitwise(n, m):
 def test_sym_route_bitwise_large(n, m):
     """Past 4096 sort tiles (three-level carries, many workgroups per XCD in
     every route pass): the route path gives the same bits as the index path,
-    and the one-call path (m = 1) the same bits as both."""
+    and the one-call path (m = 1) the same bits as both; every column is
+    within the parity bar of the float64 oracle."""
     import laplace_prefix_scans_amd as lp
     r = _rng(n * 10 + m)
     a = r.uniform(0, n / 6.0 + 1.0, n).astype(np.float32)
@@ -58,8 +59,9 @@ def test_sym_route_bitwise_large(n, m):
     if m == 1:
         y_one = lp.laplex_sort_matvec_sym(dev(a), x_d, check=True)
         assert np.array_equal(host(y_one).view(np.uint32), host(y_route).view(np.uint32)), "one-call path differs"
-        err = oracle.normwise_error(host(y_one), oracle.sym_apply(a, x), oracle.sym_apply(a, np.abs(x)))
-        assert err <= TOL
+    err = oracle.normwise_error(host(y_route), oracle.sym_apply(a, x), oracle.sym_apply(a, np.abs(x)))
+    print("n=%d m=%d normwise error %.3e" % (n, m, err), flush=True)
+    assert err <= TOL
 
 
 @pytest.mark.parametrize("n,m", [(4096, 1), (70001, 2), (9999, 4)])

@@ -117,3 +117,24 @@ def test_workload_sym2p30_sampled():
     scale = float(torch.dot(u.abs().double(), kabs.double()))
     print("symmetry |lhs-rhs|/scale = %.3e" % (abs(lhs - rhs) / scale), flush=True)
     assert abs(lhs - rhs) <= TOL * scale
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_sort_past_2p30_wide_status():
+    """n = 2^30 + 8193 anchors: past 2^30 the look-back status words are 64
+    bits wide (a 30-bit count no longer holds a prefix).  The permutation is
+    checked through the properties that make it the stable argsort."""
+    import torch
+    import laplace_prefix_scans_amd as lp
+    from synth.gen import anchors_uniform
+    n = (1 << 30) + 8193
+    a = anchors_uniform(n, 0.0, float(1 << 27), wid=91)
+    print("generated n=%d" % n, flush=True)
+    a_d = dev(a)
+    a_s, perm = lp.laplex_sort_anchors(a_d, check=True)
+    torch.cuda.synchronize()
+    print("gpu sort done", flush=True)
+    del a_d
+    assert_perm_is_stable_argsort(a, host(perm), host(a_s))
+    print("perm properties ok", flush=True)
