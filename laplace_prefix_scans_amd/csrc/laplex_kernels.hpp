@@ -33,6 +33,9 @@ constexpr int kHdrTicket0 = 1;  // one tile ticket per radix pass (4 words)
 // per radix pass: 1 when tiles publish their counts before ranking (4 words;
 // a cache line of their own, away from the tickets every workgroup increments)
 constexpr int kHdrEarly0 = 64;
+// set (with the watchdog flag) when a look-back gives up; read by every tile
+// of the later passes, so it too has a cache line of its own
+constexpr int kHdrStop = 128;
 constexpr uint32_t kFlagNonFinite = 1u, kFlagWatchdog = 2u;
 constexpr size_t kSortHeaderBytes = 16384;  // control words, 4x256 histograms, 4x256 offsets
 constexpr size_t kSortHistOffset = 1024;

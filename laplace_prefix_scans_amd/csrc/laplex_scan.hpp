@@ -638,7 +638,7 @@ __device__ __forceinline__ void sym_apply_tile(const float* __restrict__ a_s, co
                                                const float* __restrict__ cfw, const float* __restrict__ cbw,
                                                const float2* __restrict__ tanch, uint64_t n, uint32_t m, uint64_t T,
                                                float* __restrict__ y, bool vec, float* s_wf, float* s_wb, float* s_wfs,
-                                               float* s_wbs, float* s_y) {
+                                               float* s_wbs) {
   constexpr int CC = PH ? 2 * C : C;
   constexpr int E = apply_items(CC);
   constexpr int BLOCK = apply_block(CC);
@@ -729,13 +729,7 @@ __device__ __forceinline__ void sym_apply_tile(const float* __restrict__ a_s, co
     for (int e = 0; e < E; ++e)
 #pragma unroll
       for (int j = 0; j < C; ++j) yv[e][j] = PH ? fmaf(cs[e], v[e][j], sn[e] * v[e][C + j]) : v[e][j];
-    if (SCATTER && s_y) {
-      // rows collected whole in LDS, scattered after the last chunk
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-#pragma unroll
-        for (int j = 0; j < C; ++j) s_y[((uint32_t)tid * E + e) * m + cc * C + j] = yv[e][j];
-    } else if (SCATTER) {
+    if (SCATTER) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         if (FAST || p0 + e < n) {
@@ -749,28 +743,6 @@ __device__ __forceinline__ void sym_apply_tile(const float* __restrict__ a_s, co
     }
     __syncthreads();
   }
-  if (SCATTER && s_y) {
-    // each row of y written whole: consecutive lanes move consecutive
-    // 16-byte pieces (m % 4 == 0 and y 16-byte aligned; else floats)
-    const uint64_t lo = tile * P;
-    const uint32_t rows = (uint32_t)std::min<uint64_t>((uint64_t)P, n - lo);
-    if (m % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) {
-      const uint32_t pr = m / 4;
-      for (uint32_t q = threadIdx.x; q < rows * pr; q += BLOCK) {
-        const uint32_t r = q / pr, c = q - r * pr;
-        uint32_t d = perm[lo + r];
-        if ((uint64_t)d >= n) d = 0;
-        *reinterpret_cast<float4*>(y + (uint64_t)d * m + 4 * c) = *reinterpret_cast<const float4*>(s_y + r * m + 4 * c);
-      }
-    } else {
-      for (uint32_t q = threadIdx.x; q < rows * m; q += BLOCK) {
-        const uint32_t r = q / m, c = q - r * m;
-        uint32_t d = perm[lo + r];
-        if ((uint64_t)d >= n) d = 0;
-        y[(uint64_t)d * m + c] = s_y[r * m + c];
-      }
-    }
-  }
 }
 
 template <int C, bool PH, bool SCATTER>
@@ -783,17 +755,10 @@ __attribute__((amdgpu_waves_per_eu(!PH && C == 1 ? 8 : 1))) void k_sym_apply(
   constexpr int NW = apply_block(CC) / kWave;
   constexpr int P = apply_tile(CC);
   __shared__ float s_wf[NW * CC], s_wb[NW * CC], s_wfs[NW], s_wbs[NW];
-  // Scattering several column chunks: each chunk's part of a row would be a
-  // separate partial write of the row (1.66x the bytes of y measured for
-  // 32-byte rows in two halves), so the tile's rows are collected in LDS and
-  // written whole after the last chunk, when they fit.
-  constexpr uint32_t kRowStage = (SCATTER && C >= 4) ? 32768u / 4u : 1u;
-  __shared__ float s_rows[kRowStage];
-  float* s_y = (SCATTER && m > C && (uint64_t)m * P <= kRowStage) ? s_rows : nullptr;
   if (vec && m == C && ((uint64_t)blockIdx.x + 1) * P <= n)
-    sym_apply_tile<C, PH, SCATTER, true>(a_s, perm, xs, phs, cfw, cbw, tanch, n, m, T, y, vec, s_wf, s_wb, s_wfs, s_wbs, s_y);
+    sym_apply_tile<C, PH, SCATTER, true>(a_s, perm, xs, phs, cfw, cbw, tanch, n, m, T, y, vec, s_wf, s_wb, s_wfs, s_wbs);
   else
-    sym_apply_tile<C, PH, SCATTER, false>(a_s, perm, xs, phs, cfw, cbw, tanch, n, m, T, y, vec, s_wf, s_wb, s_wfs, s_wbs, s_y);
+    sym_apply_tile<C, PH, SCATTER, false>(a_s, perm, xs, phs, cfw, cbw, tanch, n, m, T, y, vec, s_wf, s_wb, s_wfs, s_wbs);
 }
 
 // Rows of m floats moved by index: pieces of V floats (one vector access

@@ -280,10 +280,11 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
   uint64_t xtile = 0;
   if (table && !xcd_tile((n + TILE - 1) / TILE, xtile)) return;
   if (!table && tid == 0) s_tile = atomicAdd(&header[kHdrTicket0 + pass], 1u);
-  // after a look-back that gave up (watchdog flag) the keys are no longer a
-  // permutation of the input: this pass stops at once, the whole workgroup
-  // together (its successors' bounded waits then give up too)
-  if (tid == 0) s_stop = (load_agent(&header[kHdrFlags]) & kFlagWatchdog) != 0u;
+  // after a look-back that gave up (in an earlier pass) the keys are no
+  // longer a permutation of the input: this pass stops at once, the whole
+  // workgroup together (its successors' bounded waits then give up too).  A
+  // plain load: the word was written by an earlier kernel.
+  if (tid == 0) s_stop = header[kHdrStop];
   for (int i = tid; i < NW * 256; i += kSortBlock) s_match[i] = make_uint4(0u, 0u, 0u, 0u);
   if (tid < 256) s_thist[tid] = 0u;
   __syncthreads();
@@ -422,6 +423,7 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
           if (used == 0) {
             if (++spins > spin_limit) {
               atomicOr(&header[kHdrFlags], kFlagWatchdog);
+              atomicOr(&header[kHdrStop], 1u);
               break;
             }
             __builtin_amdgcn_s_sleep(1);
