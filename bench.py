@@ -390,6 +390,51 @@ def time_call(lp, torch, bstep, n, m, k, args):
             "Gelem_per_s": round(n * m / (ms * 1e-3) / 1e9, 4), "kernels": kernels}
 
 
+def micro(args):
+    """Memory-system rates behind the choice between moving rows by index and
+    moving them along the sort's route, on arrays of 2^30 floats (4 GiB):
+    a streaming copy, a random 4-byte gather y = x[p] and scatter y[p] = x
+    for a uniformly random permutation p (the order a sort of iid anchors
+    produces), and random 64-byte rows (16 floats) gathered by index.  Each
+    is timed with HIP events over repeated launches (torch's kernels)."""
+    import torch
+    n = 1 << 30
+    dev = torch.device("cuda:0")
+    x = torch.randn(n, device=dev)
+    y = torch.empty_like(x)
+    g = torch.Generator(device=dev).manual_seed(11)
+    p = torch.randperm(n, device=dev, generator=g)
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {}
+    ms = timed(lambda: y.copy_(x))
+    out["copy"] = {"ms": round(ms, 3), "GBps": round(2 * 4 * n / (ms * 1e-3) / 1e9, 1), "bytes": "4 B read + 4 B written per element"}
+    ms = timed(lambda: torch.index_select(x, 0, p, out=y))
+    out["gather_4B"] = {"ms": round(ms, 3), "useful_GBps": round(2 * 4 * n / (ms * 1e-3) / 1e9, 1),
+                        "bytes": "4 B read at random + 4 B written per element (index reads not counted)"}
+    ms = timed(lambda: y.index_copy_(0, p, x))
+    out["scatter_4B"] = {"ms": round(ms, 3), "useful_GBps": round(2 * 4 * n / (ms * 1e-3) / 1e9, 1),
+                         "bytes": "4 B read + 4 B written at random per element (index reads not counted)"}
+    del p
+    rows = n // 16
+    x2, y2 = x.view(rows, 16), y.view(rows, 16)
+    pr = torch.randperm(rows, device=dev, generator=g)
+    ms = timed(lambda: torch.index_select(x2, 0, pr, out=y2))
+    out["gather_64B_rows"] = {"ms": round(ms, 3), "useful_GBps": round(2 * 4 * n / (ms * 1e-3) / 1e9, 1),
+                              "bytes": "64-byte rows read at random + written in order"}
+    print(json.dumps({"micro": out, "n_floats": n, "peak_GBps": HBM_PEAK_GBPS}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -412,7 +457,12 @@ def main():
     ap.add_argument("--rocprof-summary", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/kernels_<workload>.txt and profiles/counters_<workload>.txt from rocprofv3 output")
     ap.add_argument("--rocprof-command", default="", help="the program command line the rocprofv3 runs profiled")
+    ap.add_argument("--micro", action="store_true",
+                    help="print the memory-system micro-benchmark (copy, random gather and scatter) and exit")
     args = ap.parse_args()
+    if args.micro:
+        micro(args)
+        return
     if args.rocprof_summary:
         ktxt, ctxt = rocprof_summary(*args.rocprof_summary, workload=args.workload, command=args.rocprof_command)
         os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
