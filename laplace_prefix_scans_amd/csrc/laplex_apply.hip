@@ -317,6 +317,140 @@ __global__ __launch_bounds__(kSearchBlock) void k_gen_search(const float* __rest
   if (__ballot(bad) != 0ull && lane_id() == 0) atomicOr(&header[kHdrFlags], kFlagNonFinite);
 }
 
+// The one-column search with the outputs of a workgroup taken in group
+// order.  In input order every lane's group load goes to a different random
+// cache line of b, so the search is bound by the rate of scattered L2
+// requests.  Here each workgroup takes kLocalItems outputs per thread:
+// (1) finds every output's group by the tree descent and keeps the anchor
+// and group in LDS; (2) counting-sorts the outputs by group / 8 in LDS; (3)
+// runs the rest of the search in that order, so neighbouring lanes load
+// neighbouring groups of b and neighbouring (Fi, U) pairs, and leaves each
+// result in LDS at the output's place; (4) writes y in input order.  The
+// arithmetic of every output is that of k_gen_search: the same bits.
+constexpr int kLocalItems = 8;                 // outputs per thread
+constexpr int kLocalBins = kSearchTree / 8;    // sort bins: 8 consecutive groups each
+template <int S>
+__global__ __launch_bounds__(kSearchBlock) void k_gen_search_local(const float* __restrict__ a, uint64_t n,
+                                                                   const float* __restrict__ b_s, uint64_t k,
+                                                                   const float2* __restrict__ fu, const float* __restrict__ tree,
+                                                                   float* __restrict__ y, uint32_t* __restrict__ header) {
+  static_assert(S % 4 == 0 && S <= (int)kSearchGroupMax, "groups of whole 16-byte pieces");
+  constexpr uint32_t NS = kSearchSamplesGroup;
+  constexpr int L = __builtin_ctz(NS);
+  constexpr int IT = kLocalItems;
+  constexpr uint32_t CH = kSearchBlock * IT;  // outputs per workgroup
+  __shared__ float s_e[NS];                     // tree nodes 1..NS-1
+  __shared__ float s_a[CH];                     // anchors, then results
+  __shared__ uint16_t s_g[CH];                  // group of each output
+  __shared__ uint16_t s_idx[CH];                // outputs in group order
+  __shared__ uint32_t s_bin[kLocalBins];
+  __shared__ uint32_t s_wsum[kSearchBlock / kWave];
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  for (uint32_t j = tid; j < NS / 4; j += kSearchBlock)
+    reinterpret_cast<float4*>(s_e)[j] = reinterpret_cast<const float4*>(tree)[j];
+  for (uint32_t j = tid; j < (uint32_t)kLocalBins; j += kSearchBlock) s_bin[j] = 0u;
+  const uint64_t base = (uint64_t)blockIdx.x * CH;
+  const uint32_t count = (uint32_t)std::min<uint64_t>(CH, n - base);
+  float av[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const uint32_t l = (uint32_t)(it * kSearchBlock + tid);
+    av[it] = a[base + (l < count ? l : count - 1)];
+  }
+  uint32_t bad = 0;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const uint32_t l = (uint32_t)(it * kSearchBlock + tid);
+    bad |= (l < count && bits_nonfinite(__float_as_uint(av[it]))) ? 1u : 0u;
+  }
+  __syncthreads();
+  // (1) groups by the tree descent; (2) bin counts
+  uint32_t gl[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    uint32_t node = 1;
+#pragma unroll
+    for (int l = 0; l < L; ++l) node = 2 * node + (s_e[node] <= av[it] ? 1u : 0u);
+    gl[it] = node - NS;
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const uint32_t l = (uint32_t)(it * kSearchBlock + tid);
+    s_a[l] = av[it];
+    s_g[l] = (uint16_t)gl[it];
+    if (l < count) atomicAdd(&s_bin[gl[it] >> 3], 1u);
+  }
+  __syncthreads();
+  // exclusive scan of the bins: two per thread, then the waves' totals
+  {
+    static_assert(kLocalBins == 2 * kSearchBlock, "two bins per thread");
+    const uint32_t b0 = s_bin[2 * tid], b1 = s_bin[2 * tid + 1];
+    const uint32_t x = wave_incl_sum_u32(b0 + b1);
+    if (lane == kWave - 1) s_wsum[wid] = x;
+    __syncthreads();
+    uint32_t pre = 0;
+    for (int w = 0; w < wid; ++w) pre += s_wsum[w];
+    const uint32_t ex = pre + x - (b0 + b1);
+    s_bin[2 * tid] = ex;
+    s_bin[2 * tid + 1] = ex + b0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const uint32_t l = (uint32_t)(it * kSearchBlock + tid);
+    if (l < count) s_idx[atomicAdd(&s_bin[gl[it] >> 3], 1u)] = (uint16_t)l;
+  }
+  __syncthreads();
+  // (3) the rest of the search in group order
+  auto node_of = [](uint32_t r) -> uint32_t { return heap_node(r, L); };
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const uint32_t slot = (uint32_t)(it * kSearchBlock + tid);
+    if (slot >= count) continue;
+    const uint32_t l = s_idx[slot];
+    const float v = s_a[l];
+    const uint32_t cnt = s_g[l];
+    const uint64_t p = (uint64_t)cnt * S;
+    float gv[S];
+    if (p + S <= k) {
+#pragma unroll
+      for (int u = 0; u < S / 4; ++u) {
+        const float4 q4 = reinterpret_cast<const float4*>(b_s + p)[u];
+        gv[4 * u] = q4.x;
+        gv[4 * u + 1] = q4.y;
+        gv[4 * u + 2] = q4.z;
+        gv[4 * u + 3] = q4.w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < S; ++u) gv[u] = p + u < k ? b_s[p + u] : __builtin_inff();
+    }
+    uint32_t c2 = 0;
+    float bl = cnt > 0 ? s_e[node_of(cnt)] : 0.f, br = 0.f;
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const bool le = gv[u] <= v;
+      c2 += le ? 1u : 0u;
+      bl = le ? gv[u] : bl;
+    }
+#pragma unroll
+    for (int u = S - 1; u >= 0; --u) br = gv[u] > v ? gv[u] : br;
+    const uint64_t q = p + c2;
+    const float wl = q > 0 ? decay(bl - v) : 0.f;
+    const float wr = q < k ? decay(v - br) : 0.f;
+    const float2 f = fu[q];
+    s_a[l] = fmaf(wr, f.y, wl * f.x);  // each output's slot is read and written by this thread alone
+  }
+  __syncthreads();
+  // (4) y in input order
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const uint32_t l = (uint32_t)(it * kSearchBlock + tid);
+    if (l < count) y[base + l] = s_a[l];
+  }
+  if (__ballot(bad) != 0ull && lane_id() == 0) atomicOr(&header[kHdrFlags], kFlagNonFinite);
+}
+
 // the same search for more than kSearchSamples * kSearchGroupMax inputs: the
 // group by binary search in b_s (S a power of two)
 __global__ __launch_bounds__(kSearchBlock) void k_gen_search_wide(const float* __restrict__ a, uint64_t n,
@@ -392,8 +526,13 @@ static hipError_t run_general_search(const ApplyWorkspace& w, float* fo, float* 
                       fo, uo, k, fu, b_s, S, G, tree));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  const unsigned lblocks = (unsigned)((n + (uint64_t)kSearchBlock * kLocalItems - 1) / ((uint64_t)kSearchBlock * kLocalItems));
 #define LAPLEX_SEARCH(SS)                                                                                             \
-  LAPLEX_LAUNCH("k_gen_search", n, s, k_gen_search<SS><<<blocks, kSearchBlock, 0, s>>>(a, n, b_s, k, G, fo, uo, fu, tree, m, y, header))
+  if (m == 1)                                                                                                         \
+    LAPLEX_LAUNCH("k_gen_search", n, s,                                                                               \
+                  k_gen_search_local<SS><<<lblocks, kSearchBlock, 0, s>>>(a, n, b_s, k, fu, tree, y, header));         \
+  else                                                                                                                \
+    LAPLEX_LAUNCH("k_gen_search", n, s, k_gen_search<SS><<<blocks, kSearchBlock, 0, s>>>(a, n, b_s, k, G, fo, uo, fu, tree, m, y, header))
   if (S == 8)
     LAPLEX_SEARCH(8);
   else if (S == 16)
