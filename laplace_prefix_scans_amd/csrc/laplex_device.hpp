@@ -140,6 +140,19 @@ __device__ __forceinline__ void scan_join(float (&B)[C], float s, const float (&
     if (take) B[c] = fmaf(c < NT ? wt : we, bs[c], B[c]);
 }
 
+// The same join for a DPP row step, whose lanes that do not take it read 0
+// (their source lies outside the row): masking the two weights then leaves
+// those lanes' values as they are (0 * 0 is added), without a select per
+// column.
+template <int C, int NT, bool FWD>
+__device__ __forceinline__ void scan_join_row(float (&B)[C], float s, const float (&bs)[C], float ss, bool take) {
+  const float x = FWD ? ss - s : s - ss;
+  const float wt = NT > 0 && take ? decay_m<true>(x) : 0.f;
+  const float we = NT < C && take ? decay_m<false>(x) : 0.f;
+#pragma unroll
+  for (int c = 0; c < C; ++c) B[c] = fmaf(c < NT ? wt : we, bs[c], B[c]);
+}
+
 // Inclusive forward scan across the wave, lane order.  `s` is this lane's
 // segment-end anchor (it does not change).  Within each 16-lane row a
 // Hillis-Steele scan by DPP row shifts; then rows 1 and 3 join the total of
@@ -153,7 +166,7 @@ __device__ __forceinline__ void wave_scan_fwd_mix(float (&B)[C], float s) {
   {                                                                     \
     const float ss = dpp_row<0x110 | K>(s);                             \
     _Pragma("unroll") for (int c = 0; c < C; ++c) bs[c] = dpp_row<0x110 | K>(B[c]); \
-    scan_join<C, NT, true>(B, s, bs, ss, rl >= K);                      \
+    scan_join_row<C, NT, true>(B, s, bs, ss, rl >= K);                  \
   }
   LAPLEX_FWD_STEP(1)
   LAPLEX_FWD_STEP(2)
@@ -191,7 +204,7 @@ __device__ __forceinline__ void wave_scan_bwd_mix(float (&B)[C], float s) {
   {                                                                     \
     const float ss = dpp_row<0x100 | K>(s);                             \
     _Pragma("unroll") for (int c = 0; c < C; ++c) bs[c] = dpp_row<0x100 | K>(B[c]); \
-    scan_join<C, NT, false>(B, s, bs, ss, rl + K < 16);                 \
+    scan_join_row<C, NT, false>(B, s, bs, ss, rl + K < 16);             \
   }
   LAPLEX_BWD_STEP(1)
   LAPLEX_BWD_STEP(2)
@@ -242,6 +255,59 @@ __device__ __forceinline__ void wave_sum(float (&v)[C]) {
     const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 63));
     v[c] = (r0 + r1) + (r2 + r3);
   }
+}
+
+// Sums over the wave of N values that every lane holds (N a power of two, at
+// most 32), transposed: at each of six levels a lane is paired with a
+// partner (32 lanes apart, then 16, by the lane-swap instructions; then 8
+// apart, within half-rows, within quads and in pairs, by DPP row
+// permutations).  While a lane holds more than one value, it keeps half of
+// them and adds the partner's copies of those, and the partner keeps the
+// other half; once one value is left, a level adds the partner's copy.  The
+// lane then holds the wave's sum of value (lane >> (6 - log2 N)); lanes that
+// hold the same value hold the same bits (a + b and b + a are equal), and
+// the order of the additions is fixed.  About 2N + 6 instructions, where
+// summing each value by its own row scan and lane reads takes 11 each.
+template <int CTRL, int NIN, int NOUT, int N>
+__device__ __forceinline__ void wave_sum_t_level(float (&v)[N], bool hi) {
+#pragma unroll
+  for (int j = 0; j < NOUT; ++j) {
+    if constexpr (NIN > 1) {
+      const float keep = hi ? v[j + NOUT] : v[j], send = hi ? v[j] : v[j + NOUT];
+      v[j] = keep + dpp_row<CTRL>(send);
+    } else {
+      v[j] = v[j] + dpp_row<CTRL>(v[j]);
+    }
+  }
+}
+template <int N>
+__device__ __forceinline__ float wave_sum_t(float (&v)[N]) {
+  static_assert(N >= 1 && N <= 32 && (N & (N - 1)) == 0, "a power of two, at most 32");
+  constexpr int N1 = N > 1 ? N / 2 : 1, N2 = N1 > 1 ? N1 / 2 : 1, N3 = N2 > 1 ? N2 / 2 : 1, N4 = N3 > 1 ? N3 / 2 : 1,
+                N5 = N4 > 1 ? N4 / 2 : 1;
+  const int lane = lane_id();
+  auto bits = [](float x) { return __builtin_bit_cast(unsigned, x); };
+  auto flt = [](unsigned x) { return __builtin_bit_cast(float, x); };
+  // 32 apart: the first result holds lanes 0-31 of the first operand and
+  // lanes 0-31 of the second; the other result their lanes 32-63
+#pragma unroll
+  for (int j = 0; j < N1; ++j) {
+    const auto r = __builtin_amdgcn_permlane32_swap(bits(v[j]), bits(v[N > 1 ? j + N1 : j]), false, false);
+    v[j] = flt(r[0]) + flt(r[1]);
+  }
+  // 16 apart: rows (16 lanes) 0 and 2 of the first result come from the
+  // first operand, rows 1 and 3 from the second; the other result likewise
+  // from the odd rows
+#pragma unroll
+  for (int j = 0; j < N2; ++j) {
+    const auto r = __builtin_amdgcn_permlane16_swap(bits(v[j]), bits(v[N1 > 1 ? j + N2 : j]), false, false);
+    v[j] = flt(r[0]) + flt(r[1]);
+  }
+  wave_sum_t_level<0x128, N2, N3>(v, (lane & 8) != 0);  // row rotated by 8: lanes 8 apart
+  wave_sum_t_level<0x141, N3, N4>(v, (lane & 4) != 0);  // half-row mirror: l and 7 - l
+  wave_sum_t_level<0x1B, N4, N5>(v, (lane & 2) != 0);   // quad [3,2,1,0]
+  wave_sum_t_level<0xB1, N5, 1>(v, (lane & 1) != 0);    // quad [1,0,3,2]
+  return v[0];
 }
 
 }  // namespace laplex

@@ -16,17 +16,29 @@ __device__ __forceinline__ uint32_t sumcol(uint32_t m, uint32_t cc, int j) {
 }
 
 // Sum CC values over the block; totals land in out0[col(j)], out1[col(j)].
+// Each wave sums the 2 CC values a then b by transposed wave sums of up to
+// 32 values (zeros past 2 CC), and one lane per value stores the wave's sum
+// in s_red; threads j < CC then add the waves' sums in wave order.
+constexpr int pow2_at_least(int x) { return x <= 1 ? 1 : 2 * pow2_at_least((x + 1) / 2); }
+constexpr int log2_exact(int x) { return x <= 1 ? 0 : 1 + log2_exact(x / 2); }
 template <int CC, int NW>
 __device__ __forceinline__ void block_sum2(float (&a)[CC], float (&b)[CC], float* s_red /* [2][NW][CC] */, int& jcol_valid) {
   const int lane = lane_id(), wid = threadIdx.x / kWave;
-  wave_sum<CC>(a);
-  wave_sum<CC>(b);
-  if (lane == 0) {
+  constexpr int N = 2 * CC;
+  constexpr int G = N <= 32 ? pow2_at_least(N) : 32;  // values per transposed sum
+  constexpr int NG = (N + G - 1) / G;
+  constexpr int SH = 6 - log2_exact(G);  // the lane holding value i of a group: i << SH
 #pragma unroll
-    for (int j = 0; j < CC; ++j) {
-      s_red[(0 * NW + wid) * CC + j] = a[j];
-      s_red[(1 * NW + wid) * CC + j] = b[j];
+  for (int g = 0; g < NG; ++g) {
+    float v[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int q = g * G + i;
+      v[i] = q < CC ? a[q] : (q < N ? b[q - CC] : 0.f);
     }
+    const float t = wave_sum_t<G>(v);
+    const int q = g * G + (lane >> SH);
+    if ((lane & ((1 << SH) - 1)) == 0 && q < N) s_red[(q < CC ? wid : NW + wid) * CC + (q < CC ? q : q - CC)] = t;
   }
   __syncthreads();
   jcol_valid = threadIdx.x < CC;
@@ -97,15 +109,41 @@ __device__ __forceinline__ void tile_scan_fu_mix(const float (&ae)[E], const flo
 
   // Carries into the wave, as direct weighted sums (every weight <= 1):
   // forward, at the last anchor s_ref of the previous wave (the tile carry's
-  // anchor for wave 0): lane l < wid holds wave l's aggregate weighted by
-  // exp(s_end(l) - s_ref), lane kWave-1 the tile carry weighted by
-  // exp(sf - s_ref); backward, mirrored.  The lane sums give every lane the
-  // same bits.
+  // anchor for wave 0), the tile carry weighted by exp(sf - s_ref) plus the
+  // aggregate of each wave l < wid weighted by exp(s_end(l) - s_ref);
+  // backward, mirrored.  With many waves, lane l < wid holds wave l's term
+  // and lane kWave-1 the carry's, and lane sums give every lane the same
+  // bits.
   static_assert(NW < kWave, "one lane per wave aggregate plus one for the tile carry");
   const float sw = wid > 0 ? s_wfs[wid - 1] : sf;
   const float sz2 = wid < NW - 1 ? s_wbs[wid + 1] : sb;
   float cw[CC], cz[CC];
-  {
+  if constexpr (NW <= 4) {
+    // Few waves: every lane forms the same sums itself, the tile carry first
+    // and then the waves in order, from broadcast reads of their aggregates
+    // (a wave-uniform loop of at most NW - 1 steps per direction).
+    const int wu = __builtin_amdgcn_readfirstlane(wid);
+    {
+      const float x = sf - sw, y = sz2 - sb;
+#pragma unroll
+      for (int j = 0; j < CC; ++j) {
+        cw[j] = dk(x, j) * cf[j];
+        cz[j] = dk(y, j) * cb[j];
+      }
+    }
+    for (int l = 0; l < wu; ++l) {
+      const float x = s_wfs[l] - sw;
+      const float wt = NT > 0 ? decay_m<true>(x) : 0.f, we = NT < CC ? decay_m<false>(x) : 0.f;
+#pragma unroll
+      for (int j = 0; j < CC; ++j) cw[j] = fmaf(j < NT ? wt : we, s_wf[l * CC + j], cw[j]);
+    }
+    for (int l = NW - 1; l > wu; --l) {
+      const float x = sz2 - s_wbs[l];
+      const float wt = NT > 0 ? decay_m<true>(x) : 0.f, we = NT < CC ? decay_m<false>(x) : 0.f;
+#pragma unroll
+      for (int j = 0; j < CC; ++j) cz[j] = fmaf(j < NT ? wt : we, s_wb[l * CC + j], cz[j]);
+    }
+  } else {
     const bool fw = lane < wid, bw = lane > wid && lane < NW;
     const int lf = fw ? lane : 0, lb = bw ? lane : 0;
     const float xf = fw ? s_wfs[lf] - sw : sf - sw;
