@@ -94,10 +94,11 @@ __device__ __forceinline__ float decay_r(float x, bool tie) { return tie ? (x ==
 
 // Value of a lane in the same 16-lane row, by DPP: CTRL 0x110 | k reads lane
 // - k (row_shr), 0x100 | k reads lane + k (row_shl).  A lane whose source lies
-// outside its row reads 0 (the callers mask it).
+// outside its row reads 0 (the callers mask it): the bound control makes the
+// hardware supply the 0, so no register has to be cleared first.
 template <int CTRL>
 __device__ __forceinline__ float dpp_row(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
 // Inclusive prefix sum of u32 values over the wave: DPP row shifts within
@@ -105,7 +106,7 @@ __device__ __forceinline__ float dpp_row(float x) {
 // the lower half, read by shuffles).
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_row_u32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
 }
 __device__ __forceinline__ uint32_t wave_incl_sum_u32(uint32_t x) {
   const int lane = lane_id(), rl = lane & 15, row = lane >> 4;
