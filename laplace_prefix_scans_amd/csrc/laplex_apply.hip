@@ -29,19 +29,44 @@ namespace laplex {
 // Carries for T tiles: one level when T is small, three levels otherwise.
 // g_* hold the group aggregates and carries (ceil(T / 1024) x M each).
 // Columns from tie_from on use the tie decay (M: no such column).
+// k_tile_carry with the fewest loads per thread that cover T tiles
+static hipError_t tile_carry_launch(const float* bf, const float* bb, const float2* tanch, uint64_t T, uint32_t M,
+                                    uint32_t tie_from, float* cf, float* cb, hipStream_t s) {
+  const uint64_t q = (T + kCarryBlock - 1) / kCarryBlock;
+#define LAPLEX_CARRY(QQ) \
+  LAPLEX_LAUNCH("k_tile_carry", T, s, k_tile_carry<QQ><<<M, kCarryBlock, 0, s>>>(bf, bb, tanch, T, M, tie_from, cf, cb))
+  if (q <= 1)
+    LAPLEX_CARRY(1);
+  else if (q <= 2)
+    LAPLEX_CARRY(2);
+  else if (q <= 4)
+    LAPLEX_CARRY(4);
+  else if (q <= 8)
+    LAPLEX_CARRY(8);
+  else if (q <= (uint64_t)kCarryMaxQ)
+    LAPLEX_CARRY(kCarryMaxQ);
+  else
+    return hipErrorInvalidValue;
+#undef LAPLEX_CARRY
+  return hipSuccess;
+}
+
 static hipError_t tile_carries(const float* bf, const float* bb, const float2* tanch, uint64_t T, uint32_t M, float* cf,
                                float* cb, float* gbf, float* gbb, float* gcf, float* gcb, float2* ganch, hipStream_t s,
                                uint32_t tie_from = ~0u) {
-  if (T <= (uint64_t)kCarryGroup * 4) {
-    LAPLEX_LAUNCH("k_tile_carry", T, s, k_tile_carry<<<M, kCarryBlock, 0, s>>>(bf, bb, tanch, T, M, tie_from, cf, cb));
-    return hipGetLastError();
+  // one level up to 4 tiles per thread (measured: more per thread is slower
+  // than the three-level path)
+  if (T <= (uint64_t)kCarryBlock * 4) {
+    const hipError_t e = tile_carry_launch(bf, bb, tanch, T, M, tie_from, cf, cb, s);
+    return e != hipSuccess ? e : hipGetLastError();
   }
   const uint64_t G = (T + kCarryGroup - 1) / kCarryGroup;
+  if (G > kCarryMaxTiles) return hipErrorInvalidValue;  // beyond 2^24 groups of tiles
   const dim3 grid((unsigned)G, M);
   LAPLEX_LAUNCH("k_carry_up", T, s, k_carry_up<<<grid, kCarryGroup, 0, s>>>(bf, bb, tanch, T, M, tie_from, gbf, gbb, ganch));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  LAPLEX_LAUNCH("k_tile_carry", G, s, k_tile_carry<<<M, kCarryBlock, 0, s>>>(gbf, gbb, ganch, G, M, tie_from, gcf, gcb));
+  if ((e = tile_carry_launch(gbf, gbb, ganch, G, M, tie_from, gcf, gcb, s)) != hipSuccess) return e;
   if ((e = hipGetLastError()) != hipSuccess) return e;
   LAPLEX_LAUNCH("k_carry_down", T, s,
                 k_carry_down<<<grid, kCarryGroup, 0, s>>>(bf, bb, tanch, T, M, gcf, gcb, ganch, G, tie_from, cf, cb));
@@ -1042,13 +1067,46 @@ __global__ __launch_bounds__(pbwd_block(C)) void k_pbwd_reduce(const float* __re
   static_assert(C == 1, "one input column per pass");
   __shared__ float s_x[kStageCols * P], s_g[kStageCols * P];
   const bool vec4 = (m % 4 == 0) && (reinterpret_cast<uintptr_t>(xs) % 16 == 0) && (reinterpret_cast<uintptr_t>(gs) % 16 == 0);
+  // With 16-byte row pieces the next slice's pieces are loaded into
+  // registers while the current slice is reduced, and written to LDS after
+  // the barrier that ends the current slice's reads.
+  static_assert(kStageCols == 4 && P % BLOCK == 0, "one 16-byte piece per row and slice");
+  constexpr int SR = P / BLOCK;  // rows of a slice per thread
+  const uint32_t rows = (uint32_t)std::min<uint64_t>((uint64_t)P, n - lo);
+  float4 nx[SR], ng[SR];
+  auto fetch = [&](uint32_t c0) {
+#pragma unroll
+    for (int r = 0; r < SR; ++r) {
+      const uint32_t row = (uint32_t)(r * BLOCK + tid);
+      const bool ok = row < rows;
+      nx[r] = ok ? *reinterpret_cast<const float4*>(xs + (lo + row) * m + c0) : make_float4(0.f, 0.f, 0.f, 0.f);
+      ng[r] = ok ? *reinterpret_cast<const float4*>(gs + (lo + row) * m + c0) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  if (vec4) fetch(0);
   for (uint32_t cc = 0; cc < m; ++cc) {
     const uint32_t j0 = cc % kStageCols;
     if (j0 == 0) {  // the next slice of columns, loaded once for the whole tile
-      const uint32_t w = std::min<uint32_t>(kStageCols, m - cc);
       __syncthreads();
-      stage_cols<P, BLOCK>(xs, lo, n, m, cc, w, vec4, s_x);
-      stage_cols<P, BLOCK>(gs, lo, n, m, cc, w, vec4, s_g);
+      if (vec4) {
+#pragma unroll
+        for (int r = 0; r < SR; ++r) {
+          const uint32_t row = (uint32_t)(r * BLOCK + tid);
+          s_x[0 * P + row] = nx[r].x;
+          s_x[1 * P + row] = nx[r].y;
+          s_x[2 * P + row] = nx[r].z;
+          s_x[3 * P + row] = nx[r].w;
+          s_g[0 * P + row] = ng[r].x;
+          s_g[1 * P + row] = ng[r].y;
+          s_g[2 * P + row] = ng[r].z;
+          s_g[3 * P + row] = ng[r].w;
+        }
+        if (cc + kStageCols < m) fetch(cc + kStageCols);
+      } else {
+        const uint32_t w = std::min<uint32_t>(kStageCols, m - cc);
+        stage_cols<P, BLOCK>(xs, lo, n, m, cc, w, false, s_x);
+        stage_cols<P, BLOCK>(gs, lo, n, m, cc, w, false, s_g);
+      }
       __syncthreads();
     }
     float xv[E][C], gv[E][C], v[E][4 * C];

@@ -217,134 +217,116 @@ __device__ __forceinline__ void tile_scan(const float (&ae)[E], float (&v)[E][CC
 
 // ---------------------------------------------------------------- carries
 constexpr int kCarryBlock = 1024;
-constexpr int kCarryBatch = 8;
-constexpr uint64_t kCarryMinRun = 8;
+constexpr int kCarryMaxQ = 16;  // tiles per thread of k_tile_carry at the most
+constexpr uint64_t kCarryMaxTiles = (uint64_t)kCarryBlock * kCarryMaxQ;
 
 // Scan of the tile aggregates into the carry entering each tile from the left
 // (cf: value at the previous tile's last element) and from the right (cb:
-// value at the next tile's first element).  One workgroup per column: each
-// thread owns a contiguous run of tiles and folds it in both directions as
-// direct weighted sums (every weight exp(-|s - s_end|) <= 1); wave 0 scans
-// the forward run aggregates and wave 1 the backward ones, 64 per round, at
-// the same time (at most 16 rounds; runs hold at least 8 tiles, so a few
-// thousand tiles take a few rounds); then each thread walks its run once more
-// writing both carries, with the loads of each batch of tiles issued before
-// their dependent chains.
+// value at the next tile's first element).  One workgroup per column: thread
+// i owns the q = ceil(T / kCarryBlock) consecutive tiles from i q, loads them
+// all at once and folds them in both directions as direct weighted sums
+// (every weight exp(-|s - s_end|) <= 1); the run aggregates are scanned
+// across the wave, the waves' totals reach the later (earlier) waves as
+// direct weighted sums through LDS, and each thread walks its run once more
+// writing both carries.  Q (a power of two) >= q: the loads per thread; T <=
+// kCarryBlock * Q (the caller checks).
+template <int Q>
 __global__ __launch_bounds__(kCarryBlock) void k_tile_carry(const float* __restrict__ bf, const float* __restrict__ bb,
                                                             const float2* __restrict__ tanch, uint64_t T, uint32_t M,
                                                             uint32_t tie_from, float* __restrict__ cf, float* __restrict__ cb) {
-  __shared__ float sB[kCarryBlock], sS[kCarryBlock], sD[kCarryBlock], sT[kCarryBlock];
+  constexpr int NW = kCarryBlock / kWave;
+  __shared__ float s_wf[NW], s_wfs[NW], s_wb[NW], s_wbs[NW];
   const uint32_t c = blockIdx.x;
   const bool tie = c >= tie_from;  // columns from tie_from on scan with the tie decay
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
-  // runs of at least kCarryMinRun tiles, so that few tiles need few scan rounds
-  const uint64_t q = std::max<uint64_t>(kCarryMinRun, (T + kCarryBlock - 1) / kCarryBlock);
-  const int rounds = (int)std::min<uint64_t>(kCarryBlock / kWave, ((T + q - 1) / q + kWave - 1) / kWave);
+  const uint64_t q = (T + kCarryBlock - 1) / kCarryBlock;
   const uint64_t t0 = std::min<uint64_t>(T, (uint64_t)tid * q), t1 = std::min<uint64_t>(T, t0 + q);
+  const int nt = (int)(t1 - t0);
   const float s_min = tanch[0].y, s_maxf = tanch[T - 1].x, s_maxl = tanch[T - 1].y;
 
-  // ---- fold both directions
-  float B = 0.f, s = s_maxl, D = 0.f, sd = s_maxf;
-  if (t0 < t1) {
-    s = tanch[t1 - 1].y;
-    sd = tanch[t0].x;
-#pragma unroll 8
-    for (uint64_t t = t0; t < t1; ++t) {
-      const float2 an = tanch[t];
-      B = fmaf(decay_r(an.y - s, tie), bf[t * M + c], B);
-      D = fmaf(decay_r(sd - an.x, tie), bb[t * M + c], D);
+  // ---- this thread's tiles (clamped into range, every load issued at once)
+  float af[Q], al[Q], vf[Q], vb[Q];
+#pragma unroll
+  for (int u = 0; u < Q; ++u) {
+    const uint64_t t = std::min<uint64_t>(t0 + (uint64_t)u, T - 1);
+    const float2 an = tanch[t];
+    af[u] = an.x;
+    al[u] = an.y;
+    vf[u] = bf[t * M + c];
+    vb[u] = bb[t * M + c];
+  }
+  // ---- fold both directions: (B, s) anchored at the run's last anchor, (D, sd) at its first
+  float s = s_maxl, sd = s_maxf;
+#pragma unroll
+  for (int u = 0; u < Q; ++u)
+    if (u + 1 == nt) s = al[u];
+  if (nt > 0) sd = af[0];
+  float B = 0.f, D = 0.f;
+#pragma unroll
+  for (int u = 0; u < Q; ++u) {
+    if (u < nt) {
+      B = fmaf(decay_r(al[u] - s, tie), vf[u], B);
+      D = fmaf(decay_r(sd - af[u], tie), vb[u], D);
     }
   }
-  sB[tid] = B;
-  sS[tid] = s;
-  sD[tid] = D;
-  sT[tid] = sd;
+  // ---- inclusive scans of the runs across the wave
+  float b1[1] = {B}, d1[1] = {D};
+  if (tie) {
+    wave_scan_fwd<1, true>(b1, s);
+    wave_scan_bwd<1, true>(d1, sd);
+  } else {
+    wave_scan_fwd<1, false>(b1, s);
+    wave_scan_bwd<1, false>(d1, sd);
+  }
+  if (lane == kWave - 1) {
+    s_wf[wid] = b1[0];
+    s_wfs[wid] = s;
+  }
+  if (lane == 0) {
+    s_wb[wid] = d1[0];
+    s_wbs[wid] = sd;
+  }
+  const float X = __shfl_up(b1[0], 1), sx = __shfl_up(s, 1);
+  const float Z = __shfl_down(d1[0], 1), sz = __shfl_down(sd, 1);
   __syncthreads();
-  // ---- scan the run aggregates: wave 0 forward, wave 1 backward
-  if (wid == 0) {
-    float cB = 0.f, cS = s_min;
-    for (int r = 0; r < rounds; ++r) {  // runs past the last hold nothing
-      const int i = r * kWave + lane;
-      float b1[1] = {sB[i]};
-      const float s1 = sS[i];
-      if (tie)
-        wave_scan_fwd<1, true>(b1, s1);
-      else
-        wave_scan_fwd<1, false>(b1, s1);
-      const float inc = fmaf(decay_r(cS - s1, tie), cB, b1[0]);
-      float ex = __shfl_up(inc, 1), es = __shfl_up(s1, 1);
-      if (lane == 0) {
-        ex = cB;
-        es = cS;
-      }
-      sB[i] = ex;
-      sS[i] = es;
-      cB = __shfl(inc, kWave - 1);
-      cS = __shfl(s1, kWave - 1);
-    }
-  } else if (wid == 1) {
-    float cB = 0.f, cS = s_maxf;
-    for (int r = rounds - 1; r >= 0; --r) {
-      const int i = r * kWave + lane;
-      float b1[1] = {sD[i]};
-      const float s1 = sT[i];
-      if (tie)
-        wave_scan_bwd<1, true>(b1, s1);
-      else
-        wave_scan_bwd<1, false>(b1, s1);
-      const float inc = fmaf(decay_r(s1 - cS, tie), cB, b1[0]);
-      float ex = __shfl_down(inc, 1), es = __shfl_down(s1, 1);
-      if (lane == kWave - 1) {
-        ex = cB;
-        es = cS;
-      }
-      sD[i] = ex;
-      sT[i] = es;
-      cB = __shfl(inc, 0);
-      cS = __shfl(s1, 0);
+  // ---- carries into the wave: the earlier (later) waves' totals, lane l
+  // holding wave l's term, summed so that every lane has the same bits
+  const float sw = wid > 0 ? s_wfs[wid - 1] : s_min;
+  const float sz2 = wid < NW - 1 ? s_wbs[wid + 1] : s_maxf;
+  float cw[1], cz[1];
+  {
+    const bool fw = lane < wid, bw = lane > wid && lane < NW;
+    const int lf = fw ? lane : 0, lb = bw ? lane : 0;
+    cw[0] = fw ? decay_r(s_wfs[lf] - sw, tie) * s_wf[lf] : 0.f;
+    cz[0] = bw ? decay_r(sz2 - s_wbs[lb], tie) * s_wb[lb] : 0.f;
+    wave_sum<1>(cw);
+    wave_sum<1>(cz);
+  }
+  // ---- exclusive values of this thread's run, then its tiles' carries
+  float C = cw[0], sc = sw;
+  if (lane > 0) {
+    C = fmaf(decay_r(sw - sx, tie), cw[0], X);
+    sc = sx;
+  }
+  float Cb = cz[0], scb = sz2;
+  if (lane < kWave - 1) {
+    Cb = fmaf(decay_r(sz - sz2, tie), cz[0], Z);
+    scb = sz;
+  }
+#pragma unroll
+  for (int u = 0; u < Q; ++u) {
+    if (u < nt) {
+      cf[(t0 + (uint64_t)u) * M + c] = C;
+      C = fmaf(decay_r(sc - al[u], tie), C, vf[u]);
+      sc = al[u];
     }
   }
-  __syncthreads();
-  // ---- walk: forward carries upward, backward carries downward
-  if (t0 < t1) {
-    float C = sB[tid], sc = sS[tid];
-    for (uint64_t tb = t0; tb < t1; tb += kCarryBatch) {
-      float sl[kCarryBatch], bv[kCarryBatch];
 #pragma unroll
-      for (int u = 0; u < kCarryBatch; ++u) {
-        const uint64_t t = std::min<uint64_t>(tb + u, t1 - 1);
-        sl[u] = tanch[t].y;
-        bv[u] = bf[t * M + c];
-      }
-#pragma unroll
-      for (int u = 0; u < kCarryBatch; ++u) {
-        if (tb + u < t1) {
-          cf[(tb + u) * M + c] = C;
-          C = fmaf(decay_r(sc - sl[u], tie), C, bv[u]);
-          sc = sl[u];
-        }
-      }
-    }
-    C = sD[tid];
-    sc = sT[tid];
-    for (uint64_t te = t1; te > t0;) {
-      const uint64_t tb = te > t0 + kCarryBatch ? te - kCarryBatch : t0;
-      float sf[kCarryBatch], bv[kCarryBatch];
-#pragma unroll
-      for (int u = 0; u < kCarryBatch; ++u) {
-        const uint64_t t = std::min<uint64_t>(tb + u, te - 1);
-        sf[u] = tanch[t].x;
-        bv[u] = bb[t * M + c];
-      }
-#pragma unroll
-      for (int u = kCarryBatch - 1; u >= 0; --u) {
-        if (tb + u < te) {
-          cb[(tb + u) * M + c] = C;
-          C = fmaf(decay_r(sf[u] - sc, tie), C, bv[u]);
-          sc = sf[u];
-        }
-      }
-      te = tb;
+  for (int u = Q - 1; u >= 0; --u) {
+    if (u < nt) {
+      cb[(t0 + (uint64_t)u) * M + c] = Cb;
+      Cb = fmaf(decay_r(af[u] - scb, tie), Cb, vb[u]);
+      scb = af[u];
     }
   }
 }

@@ -88,12 +88,26 @@ void run_index_path(const float* a_s, const uint32_t* perm, uint64_t n, uint32_t
                [&] { k_sym_reduce<C, false>(a_s, n, m, xs, nullptr, bf, bb, tanch, vec); });
   std::fprintf(stderr, "reduce done (%llu tiles)\n", (unsigned long long)T);
 
-  if (T <= (uint64_t)kCarryGroup * 4) {
-    simt::launch(dim3(M), dim3(kCarryBlock), [&] { k_tile_carry(bf, bb, tanch, T, M, ~0u, cf, cb); });
+  // the library's choice of loads per thread: the fewest that cover the tiles
+  auto tile_carry = [&](const float* tbf, const float* tbb, const float2* tan, uint64_t TT, float* tcf, float* tcb) {
+    const uint64_t q = (TT + kCarryBlock - 1) / kCarryBlock;
+    if (q <= 1)
+      simt::launch(dim3(M), dim3(kCarryBlock), [&] { k_tile_carry<1>(tbf, tbb, tan, TT, M, ~0u, tcf, tcb); });
+    else if (q <= 2)
+      simt::launch(dim3(M), dim3(kCarryBlock), [&] { k_tile_carry<2>(tbf, tbb, tan, TT, M, ~0u, tcf, tcb); });
+    else if (q <= 4)
+      simt::launch(dim3(M), dim3(kCarryBlock), [&] { k_tile_carry<4>(tbf, tbb, tan, TT, M, ~0u, tcf, tcb); });
+    else if (q <= 8)
+      simt::launch(dim3(M), dim3(kCarryBlock), [&] { k_tile_carry<8>(tbf, tbb, tan, TT, M, ~0u, tcf, tcb); });
+    else
+      simt::launch(dim3(M), dim3(kCarryBlock), [&] { k_tile_carry<kCarryMaxQ>(tbf, tbb, tan, TT, M, ~0u, tcf, tcb); });
+  };
+  if (T <= (uint64_t)kCarryBlock * 4) {
+    tile_carry(bf, bb, tanch, T, cf, cb);
   } else {
     simt::launch(dim3((unsigned)G, M), dim3(kCarryGroup),
                  [&] { k_carry_up(bf, bb, tanch, T, M, ~0u, gbf, gbb, ganch); });
-    simt::launch(dim3(M), dim3(kCarryBlock), [&] { k_tile_carry(gbf, gbb, ganch, G, M, ~0u, gcf, gcb); });
+    tile_carry(gbf, gbb, ganch, G, gcf, gcb);
     simt::launch(dim3((unsigned)G, M), dim3(kCarryGroup),
                  [&] { k_carry_down(bf, bb, tanch, T, M, gcf, gcb, ganch, G, ~0u, cf, cb); });
   }

@@ -103,24 +103,56 @@ inline T read_lane(T v, int src) {
   done();
   return r;
 }
-// DPP row_shr:k (0x110 | k) and row_shl:k (0x100 | k) within 16-lane rows;
-// a lane whose source lies outside its row keeps `old`.
-inline int dpp(int old, int src, int ctrl) {
-  const int l = g_ctx.lane, rl = l & 15;
+// DPP within 16-lane rows: row_shr:k (0x110 | k) and row_shl:k (0x100 | k),
+// where a lane whose source lies outside its row gets 0 with the bound
+// control (bc) and keeps `old` without it; row_ror:k (0x120 | k, lane i
+// reads lane i - k mod 16 of its row); row_mirror (0x140); row_half_mirror
+// (0x141, within each half-row); quad_perm (0x00-0xFF: lane i of a quad
+// reads lane (ctrl >> 2i) & 3 of it).
+inline int dpp(int old, int src, int ctrl, bool bc) {
+  const int l = g_ctx.lane, rl = l & 15, row0 = l & ~15;
   int from = -1;
-  if ((ctrl & 0xFF0) == 0x110) {
+  if (ctrl >= 0 && ctrl <= 0xFF) {
+    from = (l & ~3) | ((ctrl >> (2 * (l & 3))) & 3);
+  } else if ((ctrl & 0xFF0) == 0x110) {
     const int k = ctrl & 15;
     if (rl >= k) from = l - k;
   } else if ((ctrl & 0xFF0) == 0x100) {
     const int k = ctrl & 15;
     if (rl + k <= 15) from = l + k;
+  } else if ((ctrl & 0xFF0) == 0x120) {
+    from = row0 | ((rl - (ctrl & 15)) & 15);
+  } else if (ctrl == 0x140) {
+    from = row0 | (15 - rl);
+  } else if (ctrl == 0x141) {
+    from = (l & ~7) | (7 - (l & 7));
   } else {
     std::fprintf(stderr, "simt: DPP control 0x%x not emulated\n", ctrl);
     std::abort();
   }
   publish_wait(to_bits(src));
-  const int r = from >= 0 ? from_bits<int>(slot_of(from)) : old;
+  const int r = from >= 0 ? from_bits<int>(slot_of(from)) : (bc ? 0 : old);
   done();
+  return r;
+}
+// The lane-swap instructions: permlane32_swap(a, b) gives {lanes 0-31 of a
+// then lanes 0-31 of b, lanes 32-63 of a then lanes 32-63 of b};
+// permlane16_swap(a, b) gives {rows 0, 2 of a interleaved with rows 0, 2 of
+// b, rows 1, 3 of a interleaved with rows 1, 3 of b} (rows of 16 lanes).
+struct u32x2 {
+  unsigned v[2];
+  unsigned operator[](int i) const { return v[i]; }
+};
+inline u32x2 permlane_swap(unsigned a, unsigned b, int half) {
+  const int l = g_ctx.lane;
+  const bool hi = (l & half) != 0;
+  // r0: own a in the low part, b of the lane `half` below in the high part;
+  // r1: a of the lane `half` above in the low part, own b in the high part
+  const unsigned a_up = read_lane<unsigned>(a, hi ? l : l + half);
+  const unsigned b_dn = read_lane<unsigned>(b, hi ? l - half : l);
+  u32x2 r;
+  r.v[0] = hi ? b_dn : a;
+  r.v[1] = hi ? b : a_up;
   return r;
 }
 inline uint64_t ballot(bool p) {
@@ -202,7 +234,10 @@ void launch(dim3 grid, dim3 block, F body) {
 #define __syncthreads() pthread_barrier_wait(&::simt::g_ctx.block->bar)
 #define __lane_id() (::simt::g_ctx.lane)
 #define __builtin_amdgcn_exp2f(x) exp2f(x)
-#define __builtin_amdgcn_update_dpp(old, src, ctrl, rm, bm, bc) ::simt::dpp((old), (src), (ctrl))
+#define __builtin_amdgcn_update_dpp(old, src, ctrl, rm, bm, bc) ::simt::dpp((old), (src), (ctrl), (bc))
+#define __builtin_amdgcn_permlane32_swap(a, b, fi, bc) ::simt::permlane_swap((a), (b), 32)
+#define __builtin_amdgcn_permlane16_swap(a, b, fi, bc) ::simt::permlane_swap((a), (b), 16)
+#define __builtin_amdgcn_readfirstlane(x) ::simt::read_lane<int>((x), 0)
 #define __builtin_amdgcn_readlane(x, l) ::simt::read_lane<int>((x), (l))
 
 namespace simt {
