@@ -83,6 +83,10 @@ def kernel_bytes(name: str, units: int, m: int, k: int = 0) -> float:
         "k_bwd_reduce": 4.0 + 8.0 * m,           # sorted anchors, sorted x and g rows
         "k_bwd_apply": 8.0 + 12.0 * m,           # sorted anchors, x and g rows in; dx rows and da out
         "k_scatter_rows": 4.0 + 8.0 * m,         # perm, sorted rows in, rows out (random)
+        "k_scatter_rows2": 12.0 + 8.0 * m,       # the same plus one float per row (da) in and out
+        "k_scatter_rows3": 20.0 + 8.0 * m,       # the same plus two floats per row (da, dphi)
+        "k_gather_rows2": 4.0 + 16.0 * m,        # perm, x and g rows in (random), sorted rows out
+        "k_gather_rows2_ph": 12.0 + 16.0 * m,    # the same plus the phases
         "k_gbwd_reduce": 4.0 + 4.0 * m,          # merged anchors, x rows (at b) and g rows (at a)
         "k_pbwd_reduce": 8.0 + 8.0 * m,          # sorted anchors and phases, x and g rows
         "k_pbwd_apply": 16.0 + 12.0 * m,         # anchors, phases, x and g rows in; dx rows, da, dphi out

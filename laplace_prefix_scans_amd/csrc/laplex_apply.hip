@@ -109,6 +109,35 @@ static void scatter_rows(const float* src, const uint32_t* perm, uint64_t rows, 
     LAPLEX_LAUNCH("k_scatter_rows", rows, s, k_scatter_rows<1><<<g, 256, 0, s>>>(src, perm, rows, m, dst));
 }
 
+// xs = x by perm (when x is given), gs = g by perm, phs = ph by perm (when
+// ph is given), in one pass
+static void gather_rows2(const float* x, const float* g, const uint32_t* perm, const float* ph, uint64_t rows, uint32_t m,
+                         float* xs, float* gs, float* phs, hipStream_t s) {
+  const int V = std::min(row_piece(m, x ? x : g, x ? xs : gs), row_piece(m, g, gs));
+  const unsigned gr = piece_grid(rows, m, V);
+  const char* name = !x ? (ph ? "k_gather_rows_ph" : "k_gather_rows") : (ph ? "k_gather_rows2_ph" : "k_gather_rows2");
+  if (V == 4)
+    LAPLEX_LAUNCH(name, rows, s, k_gather_rows2<4><<<gr, 256, 0, s>>>(x, g, perm, ph, rows, m, xs, gs, phs));
+  else if (V == 2)
+    LAPLEX_LAUNCH(name, rows, s, k_gather_rows2<2><<<gr, 256, 0, s>>>(x, g, perm, ph, rows, m, xs, gs, phs));
+  else
+    LAPLEX_LAUNCH(name, rows, s, k_gather_rows2<1><<<gr, 256, 0, s>>>(x, g, perm, ph, rows, m, xs, gs, phs));
+}
+// dst[perm[r]] = src[r] (rows of m floats), d1[perm[r]] = s1[r] and
+// d2[perm[r]] = s2[r] (when given), in one pass
+static void scatter_rows3(const float* src, const uint32_t* perm, uint64_t rows, uint32_t m, float* dst, const float* s1,
+                          float* d1, const float* s2, float* d2, hipStream_t s) {
+  const int V = row_piece(m, src, dst);
+  const unsigned g = piece_grid(rows, m, V);
+  const char* name = s2 ? "k_scatter_rows3" : s1 ? "k_scatter_rows2" : "k_scatter_rows";
+  if (V == 4)
+    LAPLEX_LAUNCH(name, rows, s, k_scatter_rows3<4><<<g, 256, 0, s>>>(src, perm, rows, m, dst, s1, d1, s2, d2));
+  else if (V == 2)
+    LAPLEX_LAUNCH(name, rows, s, k_scatter_rows3<2><<<g, 256, 0, s>>>(src, perm, rows, m, dst, s1, d1, s2, d2));
+  else
+    LAPLEX_LAUNCH(name, rows, s, k_scatter_rows3<1><<<g, 256, 0, s>>>(src, perm, rows, m, dst, s1, d1, s2, d2));
+}
+
 // x_sorted: w.xs already holds x in sorted order (routed, one column).
 template <int C, bool PH>
 static hipError_t run_sym(const ApplyWorkspace& w, const float* a_s, const uint32_t* perm, const SortRoute* route,
@@ -906,11 +935,7 @@ static hipError_t run_bwd_sym(const BackwardWorkspace& bw, const float* a_s, con
     if (!xs_sorted && (e = route_forward(*route, n, m, x, w.xs, w.t0, w.t1, s)) != hipSuccess) return e;
     if ((e = route_forward(*route, n, m, g, bw.gs, w.t0, w.t1, s)) != hipSuccess) return e;
   } else {
-    if (!xs_sorted) {
-      gather_rows(x, perm, nullptr, n, m, w.xs, nullptr, s);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    gather_rows(g, perm, nullptr, n, m, bw.gs, nullptr, s);
+    gather_rows2(xs_sorted ? nullptr : x, g, perm, nullptr, n, m, w.xs, bw.gs, nullptr, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   LAPLEX_LAUNCH("k_bwd_reduce", n, s,
@@ -925,9 +950,7 @@ static hipError_t run_bwd_sym(const BackwardWorkspace& bw, const float* a_s, con
     if ((e = route_inverse(*route, n, m, w.zs, dx, w.t0, w.t1, s)) != hipSuccess) return e;
     return route_inverse(*route, n, 1, bw.das, da, w.t0, w.t1, s);
   }
-  scatter_rows(w.zs, perm, n, m, dx, s);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  scatter_rows(bw.das, perm, n, 1, da, s);
+  scatter_rows3(w.zs, perm, n, m, dx, bw.das, da, nullptr, nullptr, s);
   return hipGetLastError();
 }
 
@@ -1263,9 +1286,7 @@ static hipError_t run_pbwd_sym(const BackwardWorkspace& bw, const float* a_s, co
     if ((e = route_forward(*route, n, m, g, bw.gs, w.t0, w.t1, s)) != hipSuccess) return e;
     if ((e = route_forward(*route, n, 1, phi, w.phs, w.t0, w.t1, s)) != hipSuccess) return e;
   } else {
-    gather_rows(x, perm, phi, n, m, w.xs, w.phs, s);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    gather_rows(g, perm, nullptr, n, m, bw.gs, nullptr, s);
+    gather_rows2(x, g, perm, phi, n, m, w.xs, bw.gs, w.phs, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   LAPLEX_LAUNCH("k_pbwd_reduce", n, s,
@@ -1282,11 +1303,7 @@ static hipError_t run_pbwd_sym(const BackwardWorkspace& bw, const float* a_s, co
     if ((e = route_inverse(*route, n, 1, bw.das, da, w.t0, w.t1, s)) != hipSuccess) return e;
     return route_inverse(*route, n, 1, bw.dphs, dphi, w.t0, w.t1, s);
   }
-  scatter_rows(w.zs, perm, n, m, dx, s);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  scatter_rows(bw.das, perm, n, 1, da, s);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  scatter_rows(bw.dphs, perm, n, 1, dphi, s);
+  scatter_rows3(w.zs, perm, n, m, dx, bw.das, da, bw.dphs, dphi, s);
   return hipGetLastError();
 }
 
@@ -1811,9 +1828,7 @@ static hipError_t run_bwd_general(const BackwardWorkspace& bw, const float* a_s,
     if ((e = route_inverse(*route_b, k, m, w.zs, dx, w.t0, w.t1, s)) != hipSuccess) return e;
     if ((e = route_inverse(*route_b, k, 1, bw.dbs, db, w.t0, w.t1, s)) != hipSuccess) return e;
   } else {
-    scatter_rows(w.zs, perm_b, k, m, dx, s);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    scatter_rows(bw.dbs, perm_b, k, 1, db, s);
+    scatter_rows3(w.zs, perm_b, k, m, dx, bw.dbs, db, nullptr, nullptr, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (routed_a) return route_inverse(*route_a, n, 1, bw.das, da, w.t0, w.t1, s);
@@ -2295,20 +2310,14 @@ hipError_t backward_phased_general(const BackwardWorkspace& bw, const float* a_s
     if ((e = route_inverse(*route_b, k, 1, bw.dbs, db, w.t0, w.t1, s)) != hipSuccess) return e;
     if ((e = route_inverse(*route_b, k, 1, bw.dpsis, dpsi, w.t0, w.t1, s)) != hipSuccess) return e;
   } else {
-    const float* src[3] = {w.zs, bw.dbs, bw.dpsis};
-    float* dst[3] = {dx, db, dpsi};
-    for (int i = 0; i < 3; ++i) {
-      scatter_rows(src[i], perm_b, k, i == 0 ? m : 1, dst[i], s);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    scatter_rows3(w.zs, perm_b, k, m, dx, bw.dbs, db, bw.dpsis, dpsi, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (routed_a) {
     if ((e = route_inverse(*route_a, n, 1, bw.das, da, w.t0, w.t1, s)) != hipSuccess) return e;
     return route_inverse(*route_a, n, 1, bw.dphs, dphi, w.t0, w.t1, s);
   }
-  scatter_rows(bw.das, perm_a, n, 1, da, s);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  scatter_rows(bw.dphs, perm_a, n, 1, dphi, s);
+  scatter_rows3(bw.das, perm_a, n, 1, da, bw.dphs, dphi, nullptr, nullptr, s);
   return hipGetLastError();
 }
 

@@ -811,6 +811,52 @@ __global__ void k_scatter_rows(const float* __restrict__ src, const uint32_t* __
     *reinterpret_cast<T*>(dst + (uint64_t)d * m + (uint64_t)c * V) = *reinterpret_cast<const T*>(src + r * m + (uint64_t)c * V);
   }
 }
+// dst[perm[r]] = src[r] (rows of m floats) and, when given, d1[perm[r]] =
+// s1[r] and d2[perm[r]] = s2[r] (one float per row): arrays that follow the
+// same permutation move in one pass, which reads perm once
+template <int V>
+__global__ void k_scatter_rows3(const float* __restrict__ src, const uint32_t* __restrict__ perm, uint64_t rows, uint32_t m,
+                                float* __restrict__ dst, const float* __restrict__ s1, float* __restrict__ d1,
+                                const float* __restrict__ s2, float* __restrict__ d2) {
+  using T = typename RowPiece<V>::T;
+  const uint32_t P = m / V;
+  const uint64_t items = rows * P;
+  uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (; i < items; i += stride) {
+    const uint64_t r = piece_row(i, P, items);
+    const uint32_t c = (uint32_t)(i - r * P);
+    const uint32_t d = perm[r];
+    if ((uint64_t)d >= rows) continue;  // a handle from the sort is always in range
+    *reinterpret_cast<T*>(dst + (uint64_t)d * m + (uint64_t)c * V) = *reinterpret_cast<const T*>(src + r * m + (uint64_t)c * V);
+    if (c == 0) {
+      if (s1) d1[d] = s1[r];
+      if (s2) d2[d] = s2[r];
+    }
+  }
+}
+// xs[r] = x[perm[r]] (when x is given) and gs[r] = g[perm[r]], rows of m
+// floats, and phs[r] = ph[perm[r]] when ph is given: one pass, perm read once
+template <int V>
+__global__ void k_gather_rows2(const float* __restrict__ x, const float* __restrict__ g, const uint32_t* __restrict__ perm,
+                               const float* __restrict__ ph, uint64_t rows, uint32_t m, float* __restrict__ xs,
+                               float* __restrict__ gs, float* __restrict__ phs) {
+  using T = typename RowPiece<V>::T;
+  const uint32_t P = m / V;
+  const uint64_t items = rows * P;
+  uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (; i < items; i += stride) {
+    const uint64_t r = piece_row(i, P, items);
+    const uint32_t c = (uint32_t)(i - r * P);
+    uint32_t src = perm[r];
+    if ((uint64_t)src >= rows) src = 0;
+    const uint64_t o = (uint64_t)c * V;
+    if (x) *reinterpret_cast<T*>(xs + r * m + o) = *reinterpret_cast<const T*>(x + (uint64_t)src * m + o);
+    *reinterpret_cast<T*>(gs + r * m + o) = *reinterpret_cast<const T*>(g + (uint64_t)src * m + o);
+    if (ph && c == 0) phs[r] = ph[src];
+  }
+}
 template <int V>
 __global__ void k_gather_rows(const float* __restrict__ x, const uint32_t* __restrict__ perm, const float* __restrict__ ph,
                               uint64_t rows, uint32_t m, float* __restrict__ xs, float* __restrict__ phs) {
