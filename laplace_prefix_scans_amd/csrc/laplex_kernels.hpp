@@ -23,9 +23,13 @@ void prof_end(int slot, const char* name, uint64_t units, hipStream_t s);
   } while (0)
 
 // ------------------------------------------------------------------ sort
-constexpr int kSortBlock = 512;
-constexpr int kSortItems = 16;
-constexpr int kSortTile = kSortBlock * kSortItems;
+// Sort tiles of 8192 keys.  The first pass (offsets from the histogram's
+// tables, no look-back) runs 512 threads x 16 keys; the passes that look back
+// run 256 threads x 32 keys, so that four tiles share a CU and more of their
+// look-back waits overlap.  The route kernels move tiles with 512 threads.
+constexpr int kSortTile = 8192;
+constexpr int sort_block(int mode) { return mode == 0 ? 512 : 256; }
+constexpr int kRouteBlock = 512;
 
 // header words of the sort workspace
 constexpr int kHdrFlags = 0;    // sticky error bits (below)

@@ -116,14 +116,14 @@ __device__ __forceinline__ void load_tables(const uint16_t* __restrict__ dstart,
 // vec: `in` (fwd) or `out` (inv), the input-order side, is 16-byte aligned
 // (and in_b / out_b with PLANES).
 template <int W, bool PLANES>
-__global__ __launch_bounds__(kSortBlock) void k_route_fwd(const float* __restrict__ in, const float* __restrict__ in_b,
+__global__ __launch_bounds__(kRouteBlock) void k_route_fwd(const float* __restrict__ in, const float* __restrict__ in_b,
                                                           float* __restrict__ out,
                                                           const uint16_t* __restrict__ lpos, const uint16_t* __restrict__ dstart,
                                                           const uint32_t* __restrict__ gbase, uint64_t n, bool vec) {
   constexpr int TILE = kSortTile;
-  constexpr int NW = kSortBlock / kWave;
-  constexpr int STEPS = TILE / kSortBlock;
-  constexpr int GSTEPS = TILE / (kSortBlock * kGroup);
+  constexpr int NW = kRouteBlock / kWave;
+  constexpr int STEPS = TILE / kRouteBlock;
+  constexpr int GSTEPS = TILE / (kRouteBlock * kGroup);
   __shared__ float s_val[TILE * W];
   __shared__ uint8_t s_dig[TILE];
   __shared__ uint16_t s_start[257];
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kSortBlock) void k_route_fwd(const float* __restric
   float vv[GSTEPS][kGroup * W];
 #pragma unroll
   for (int r = 0; r < GSTEPS; ++r) {
-    const uint32_t i0 = (uint32_t)(r * kSortBlock + tid) * kGroup;
+    const uint32_t i0 = (uint32_t)(r * kRouteBlock + tid) * kGroup;
     if (i0 + kGroup <= count) {
       lp2[r] = *reinterpret_cast<const uint2*>(lpos + base + i0);
       ld_rows<W, PLANES>(in, in_b, base + i0, vv[r], vec);
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kSortBlock) void k_route_fwd(const float* __restric
   load_tables(dstart, gbase, tile, count, s_start, s_gb);
 #pragma unroll
   for (int r = 0; r < GSTEPS; ++r) {
-    const uint32_t i0 = (uint32_t)(r * kSortBlock + tid) * kGroup;
+    const uint32_t i0 = (uint32_t)(r * kRouteBlock + tid) * kGroup;
     if (i0 + kGroup <= count) {
       const uint32_t lp[kGroup] = {lp2[r].x & 0xFFFFu, lp2[r].x >> 16, lp2[r].y & 0xFFFFu, lp2[r].y >> 16};
       const float(&v)[kGroup * W] = vv[r];
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kSortBlock) void k_route_fwd(const float* __restric
   // digit-run side: each run written contiguously
 #pragma unroll
   for (int r = 0; r < STEPS; ++r) {
-    const uint32_t i = (uint32_t)(r * kSortBlock + tid);
+    const uint32_t i = (uint32_t)(r * kRouteBlock + tid);
     if (i < count) {
       const uint32_t o = s_gb[s_dig[i]] + i;
       if ((uint64_t)o < n) {
@@ -186,14 +186,14 @@ __global__ __launch_bounds__(kSortBlock) void k_route_fwd(const float* __restric
 }
 
 template <int W, bool PLANES>
-__global__ __launch_bounds__(kSortBlock) void k_route_inv(const float* __restrict__ in, float* __restrict__ out,
+__global__ __launch_bounds__(kRouteBlock) void k_route_inv(const float* __restrict__ in, float* __restrict__ out,
                                                           float* __restrict__ out_b,
                                                           const uint16_t* __restrict__ lpos, const uint16_t* __restrict__ dstart,
                                                           const uint32_t* __restrict__ gbase, uint64_t n, bool vec) {
   constexpr int TILE = kSortTile;
-  constexpr int NW = kSortBlock / kWave;
-  constexpr int STEPS = TILE / kSortBlock;
-  constexpr int GSTEPS = TILE / (kSortBlock * kGroup);
+  constexpr int NW = kRouteBlock / kWave;
+  constexpr int STEPS = TILE / kRouteBlock;
+  constexpr int GSTEPS = TILE / (kRouteBlock * kGroup);
   __shared__ float s_val[TILE * W];
   __shared__ uint8_t s_dig[TILE];
   __shared__ uint16_t s_start[257];
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kSortBlock) void k_route_inv(const float* __restric
   uint2 lp2[GSTEPS];
 #pragma unroll
   for (int r = 0; r < GSTEPS; ++r) {
-    const uint32_t i0 = (uint32_t)(r * kSortBlock + tid) * kGroup;
+    const uint32_t i0 = (uint32_t)(r * kRouteBlock + tid) * kGroup;
     lp2[r] = i0 + kGroup <= count ? *reinterpret_cast<const uint2*>(lpos + base + i0) : make_uint2(0u, 0u);
   }
   load_tables(dstart, gbase, tile, count, s_start, s_gb);
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kSortBlock) void k_route_inv(const float* __restric
   // digit-run side: each run read contiguously
 #pragma unroll
   for (int r = 0; r < STEPS; ++r) {
-    const uint32_t i = (uint32_t)(r * kSortBlock + tid);
+    const uint32_t i = (uint32_t)(r * kRouteBlock + tid);
     if (i < count) {
       const uint32_t src = s_gb[s_dig[i]] + i;
       const bool ok = (uint64_t)src < n;
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kSortBlock) void k_route_inv(const float* __restric
   // input order side
 #pragma unroll
   for (int r = 0; r < GSTEPS; ++r) {
-    const uint32_t i0 = (uint32_t)(r * kSortBlock + tid) * kGroup;
+    const uint32_t i0 = (uint32_t)(r * kRouteBlock + tid) * kGroup;
     if (i0 + kGroup <= count) {
       const uint32_t lp[kGroup] = {lp2[r].x & 0xFFFFu, lp2[r].x >> 16, lp2[r].y & 0xFFFFu, lp2[r].y >> 16};
       float v[kGroup * W];
@@ -315,17 +315,17 @@ __device__ __forceinline__ void build_chunks(RunChunks<W>& rc, const uint16_t* s
 // reaching past the end of the array is read float by float.  vec: `out` is
 // 16-byte aligned.
 template <int W, bool PLANES>
-__global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(W == 1 ? 8 : 1))) void k_route_inv_chunked(const float* __restrict__ in, float* __restrict__ out,
+__global__ __launch_bounds__(kRouteBlock) __attribute__((amdgpu_waves_per_eu(W == 1 ? 8 : 1))) void k_route_inv_chunked(const float* __restrict__ in, float* __restrict__ out,
                                                                   float* __restrict__ out_b,
                                                                   const uint16_t* __restrict__ lpos,
                                                                   const uint16_t* __restrict__ dstart,
                                                                   const uint32_t* __restrict__ gbase, uint64_t n, bool vec) {
   static_assert(W == 1 || W == 2 || W == 4, "rows must tile a 16-byte chunk");
   constexpr int TILE = kSortTile;
-  constexpr int NW = kSortBlock / kWave;
-  constexpr int GSTEPS = TILE / (kSortBlock * kGroup);
+  constexpr int NW = kRouteBlock / kWave;
+  constexpr int GSTEPS = TILE / (kRouteBlock * kGroup);
   constexpr int MAXCH = RunChunks<W>::kMax;
-  constexpr int CSTEPS = (MAXCH + kSortBlock - 1) / kSortBlock;
+  constexpr int CSTEPS = (MAXCH + kRouteBlock - 1) / kRouteBlock;
   constexpr int RPC = 4 / W;  // rows per chunk
   __shared__ float s_val[TILE * W];
   __shared__ uint16_t s_start[257];
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(W ==
   uint2 lp2[GSTEPS];
 #pragma unroll
   for (int r = 0; r < GSTEPS; ++r) {
-    const uint32_t i0 = (uint32_t)(r * kSortBlock + tid) * kGroup;
+    const uint32_t i0 = (uint32_t)(r * kRouteBlock + tid) * kGroup;
     lp2[r] = i0 + kGroup <= count ? *reinterpret_cast<const uint2*>(lpos + base + i0) : make_uint2(0u, 0u);
   }
   load_tables(dstart, gbase, tile, count, s_start, s_gb);
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(W ==
   uint32_t dr[CSTEPS];
 #pragma unroll
   for (int r = 0; r < CSTEPS; ++r) {
-    const uint32_t c = (uint32_t)(r * kSortBlock + tid);
+    const uint32_t c = (uint32_t)(r * kRouteBlock + tid);
     const uint32_t d = chunk_run(rc, c < total ? c : 0u);
     dr[r] = d;
     const uint32_t g = rc.c0[d] + (c - rc.cs[d]);  // global chunk index (< n W / 4 + 1 <= 2^32)
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(W ==
   }
 #pragma unroll
   for (int r = 0; r < CSTEPS; ++r) {
-    const uint32_t c = (uint32_t)(r * kSortBlock + tid);
+    const uint32_t c = (uint32_t)(r * kRouteBlock + tid);
     if (c < total) {
       const uint32_t d = dr[r];
       const uint64_t g = rc.c0[d] + (c - rc.cs[d]);
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(W ==
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < GSTEPS; ++r) {
-    const uint32_t i0 = (uint32_t)(r * kSortBlock + tid) * kGroup;
+    const uint32_t i0 = (uint32_t)(r * kRouteBlock + tid) * kGroup;
     if (i0 + kGroup <= count) {
       const uint32_t lp[kGroup] = {lp2[r].x & 0xFFFFu, lp2[r].x >> 16, lp2[r].y & 0xFFFFu, lp2[r].y >> 16};
       float v[kGroup * W];
@@ -448,15 +448,15 @@ static hipError_t route_pass(bool fwd, const SortRoute& r, int k, uint64_t n, co
   const uint64_t blocks = ((tiles + kXcds - 1) / kXcds) * kXcds;
   if (fwd)
     LAPLEX_LAUNCH(kFwd[W], n, s,
-                  k_route_fwd<W, PLANES><<<dim3((unsigned)blocks), dim3(kSortBlock), 0, s>>>(
+                  k_route_fwd<W, PLANES><<<dim3((unsigned)blocks), dim3(kRouteBlock), 0, s>>>(
                       in, in_b, out, r.lpos[k], r.dstart[k], r.gbase[k], n, vec));
   else if (W != 3 && al(in) && n * W >= 4)
     LAPLEX_LAUNCH(kInv[W], n, s,
-                  k_route_inv_chunked<W == 3 ? 1 : W, PLANES><<<dim3((unsigned)blocks), dim3(kSortBlock), 0, s>>>(
+                  k_route_inv_chunked<W == 3 ? 1 : W, PLANES><<<dim3((unsigned)blocks), dim3(kRouteBlock), 0, s>>>(
                       in, out, out_b, r.lpos[k], r.dstart[k], r.gbase[k], n, vec));
   else
     LAPLEX_LAUNCH(kInv[W], n, s,
-                  k_route_inv<W, PLANES><<<dim3((unsigned)blocks), dim3(kSortBlock), 0, s>>>(
+                  k_route_inv<W, PLANES><<<dim3((unsigned)blocks), dim3(kRouteBlock), 0, s>>>(
                       in, out, out_b, r.lpos[k], r.dstart[k], r.gbase[k], n, vec));
   return hipGetLastError();
 }

@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kScanThreads) void k_sort_offsets(const uint32_t* _
 constexpr int kLookback = 4;  // predecessor status words read per round trip (more costs more status traffic than it saves)
 
 template <int MODE, typename ST, bool PAY>
-__global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6))) void k_onesweep(const uint2* __restrict__ kvin, uint2* __restrict__ kvout,
+__global__ __launch_bounds__(sort_block(MODE)) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 6 : 4))) void k_onesweep(const uint2* __restrict__ kvin, uint2* __restrict__ kvout,
                                                          uint32_t* __restrict__ kout, uint32_t* __restrict__ vout,
                                                          const uint32_t* __restrict__ a_bits, ST* __restrict__ status,
                                                          uint32_t* __restrict__ header, int pass,
@@ -253,10 +253,11 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
                                                          uint64_t chunks_per_block, uint32_t spin_limit, bool publish) {
   static_assert(!PAY || MODE != 1, "the payload enters in pass 1 and leaves in pass 4");
   constexpr bool HOLDV = MODE != 0 || PAY;  // values held in registers (else recomputed input indices)
-  static_assert(kSortBlock % 256 == 0, "at least one thread per digit value");
-  constexpr int E = kSortItems;
+  constexpr int BLOCK = sort_block(MODE);
+  static_assert(BLOCK % 256 == 0, "at least one thread per digit value");
   constexpr int TILE = kSortTile;
-  constexpr int NW = kSortBlock / kWave;
+  constexpr int E = TILE / BLOCK;
+  constexpr int NW = BLOCK / kWave;
   __shared__ __align__(16) uint2 s_kv[TILE / 2];
   __shared__ uint32_t s_whist[NW][256];
   __shared__ uint32_t s_gbase[256];
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
   // workgroup together (its successors' bounded waits then give up too).  A
   // plain load: the word was written by an earlier kernel.
   if (tid == 0) s_stop = header[kHdrStop];
-  for (int i = tid; i < NW * 256; i += kSortBlock) s_match[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = tid; i < NW * 256; i += BLOCK) s_match[i] = make_uint4(0u, 0u, 0u, 0u);
   if (tid < 256) s_thist[tid] = 0u;
   __syncthreads();
   if (s_stop) return;
@@ -473,7 +474,7 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
     return HOLDV ? v[HOLDV ? e : 0] : (uint32_t)(base + first + (uint32_t)(e * kWave));
   };
   constexpr uint32_t HALF = TILE / 2;
-  constexpr int kOutSteps = HALF / kSortBlock;  // slots per thread and half
+  constexpr int kOutSteps = HALF / BLOCK;  // slots per thread and half
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint32_t lo = (uint32_t)h * HALF;
@@ -496,13 +497,13 @@ __global__ __launch_bounds__(kSortBlock) __attribute__((amdgpu_waves_per_eu(6)))
       uint2 kv[kOutBatch];
       uint32_t o[kOutBatch];
 #pragma unroll
-      for (int j = 0; j < kOutBatch; ++j) kv[j] = s_kv[(j0 + j) * kSortBlock + tid];  // slots past count: stale
+      for (int j = 0; j < kOutBatch; ++j) kv[j] = s_kv[(j0 + j) * BLOCK + tid];  // slots past count: stale
 #pragma unroll
       for (int j = 0; j < kOutBatch; ++j)
-        o[j] = s_gbase[(kv[j].x >> shift) & 255u] + lo + (uint32_t)((j0 + j) * kSortBlock + tid);
+        o[j] = s_gbase[(kv[j].x >> shift) & 255u] + lo + (uint32_t)((j0 + j) * BLOCK + tid);
 #pragma unroll
       for (int j = 0; j < kOutBatch; ++j) {
-        const uint32_t i = lo + (uint32_t)((j0 + j) * kSortBlock + tid);
+        const uint32_t i = lo + (uint32_t)((j0 + j) * BLOCK + tid);
         // o < n holds for consistent counts; it is checked so nothing is ever written out of range
         if (i < count && (uint64_t)o[j] < n) {
           if (MODE == 2) {
@@ -557,10 +558,10 @@ static hipError_t launch_sort_passes(const SortWorkspace& w, const float* a, uin
     uint16_t* rl = route ? route->lpos[p] : nullptr;
     uint16_t* rd = route ? route->dstart[p] : nullptr;
     uint32_t* rg = route ? route->gbase[p] : nullptr;
-    const dim3 grid((unsigned)tiles), grid0((unsigned)xcd_blocks(tiles)), block(kSortBlock);
+    const dim3 grid((unsigned)tiles), grid0((unsigned)xcd_blocks(tiles));
 #define LAPLEX_PASS(MODE, PAY, NAME)                                                                                  \
   LAPLEX_LAUNCH(NAME, n, s,                                                                                          \
-                (k_onesweep<MODE, ST, PAY><<<(MODE == 0 && table ? grid0 : grid), block, 0, s>>>(                     \
+                (k_onesweep<MODE, ST, PAY><<<(MODE == 0 && table ? grid0 : grid), dim3(sort_block(MODE)), 0, s>>>(     \
                     src, dst, fk, fv, a_bits, stp, w.header, p, w.offsets + p * 256, n, rl, rd, rg, pay,                \
                     MODE == 0 && table ? w.tcount : nullptr, w.gsum, cpb, spin_limit, publish)))
     if (p == 0 && pay)
