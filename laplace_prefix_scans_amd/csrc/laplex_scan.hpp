@@ -520,6 +520,19 @@ __device__ __forceinline__ void load_rows(const float* __restrict__ x, uint64_t 
       for (int j = 0; j < C; ++j) xv[e][j] = flat[e * C + j];
     return;
   }
+  if (C % 4 == 0 && vec && m % 4 == 0 && p0 + E <= n) {  // the chunk of each row as 16-byte pieces
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int q = 0; q < C / 4; ++q) {
+        const float4 t = *reinterpret_cast<const float4*>(x + (p0 + e) * m + cc * C + 4 * q);
+        xv[e][4 * q] = t.x;
+        xv[e][4 * q + 1 < C ? 4 * q + 1 : 0] = t.y;
+        xv[e][4 * q + 2 < C ? 4 * q + 2 : 0] = t.z;
+        xv[e][4 * q + 3 < C ? 4 * q + 3 : 0] = t.w;
+      }
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < E; ++e)
 #pragma unroll
@@ -580,9 +593,16 @@ __global__ __launch_bounds__(apply_block(PH ? 2 * C : C)) void k_sym_reduce(
 #pragma unroll
     for (int e = 0; e < E; ++e) sincosf(ph[e], &sn[e], &cs[e]);
   }
+  // the next column chunk's rows are requested before this chunk is reduced
+  float xv_n[E][C];
+  load_rows<E, C>(xs, p0, n, m, 0, true, xv_n);
   for (uint32_t cc = 0; cc < m / C; ++cc) {
     float xv[E][C];
-    load_rows<E, C>(xs, p0, n, m, cc, true, xv);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int j = 0; j < C; ++j) xv[e][j] = xv_n[e][j];
+    if (cc + 1 < m / C) load_rows<E, C>(xs, p0, n, m, cc + 1, true, xv_n);
     float sf[CC], sb[CC];
 #pragma unroll
     for (int j = 0; j < CC; ++j) sf[j] = sb[j] = 0.f;
