@@ -550,6 +550,16 @@ __device__ __forceinline__ void store_rows(float* __restrict__ y, uint64_t p0, u
     st_contig<E * C>(y + p0 * C, flat, vec);
     return;
   }
+  if (C % 4 == 0 && vec && m % 4 == 0 && p0 + E <= n) {  // the chunk of each row as 16-byte pieces
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int q = 0; q < C / 4; ++q)
+        *reinterpret_cast<float4*>(y + (p0 + e) * m + cc * C + 4 * q) =
+            make_float4(yv[e][4 * q], yv[e][4 * q + 1 < C ? 4 * q + 1 : 0], yv[e][4 * q + 2 < C ? 4 * q + 2 : 0],
+                        yv[e][4 * q + 3 < C ? 4 * q + 3 : 0]);
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < E; ++e)
     if (p0 + e < n)
