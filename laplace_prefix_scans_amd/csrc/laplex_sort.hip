@@ -238,7 +238,8 @@ __global__ __launch_bounds__(kScanThreads) void k_sort_offsets(const uint32_t* _
 // sorted anchors carry +0.0 for -0.0 (no index to look the sign up by).
 // Keys and values travel as interleaved pairs so that each digit run is one
 // contiguous stretch of 8-byte elements.
-// Threads 0..255 also own one digit value each for the per-digit steps.
+// Threads 0..255 also own one digit value each for the per-digit steps (all
+// of a 256-thread block, the first four waves of a 512-thread one).
 constexpr int kLookback = 4;  // predecessor status words read per round trip (more costs more status traffic than it saves)
 
 template <int MODE, typename ST, bool PAY>
@@ -451,7 +452,8 @@ __global__ __launch_bounds__(sort_block(MODE)) __attribute__((amdgpu_waves_per_e
 
   // place the keys in LDS in digit order (stable) and write them out, one
   // half of the tile's sorted order at a time (the staging buffer holds half a
-  // tile, which keeps three blocks resident per CU).  All table reads are
+  // tile, which keeps three 512-thread or four 256-thread blocks resident per
+  // CU).  All table reads are
   // issued before the LDS writes, and the route's global stores come after
   // them so that no LDS write waits on a store.
   const uint64_t rem = n - base;
