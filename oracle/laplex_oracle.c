@@ -116,7 +116,9 @@ int lo_sym_apply(const float* a, int64_t n, int64_t m, const float* x, double* y
       const float* xr = x + (size_t)perm[i] * m;
       for (int64_t c = 0; c < m; ++c) ls[i * m + c] = (double)xr[c] + d * ls[(i - 1) * m + c];
     }
-    /* upper-triangular (suffix) recurrence, combined on the fly */
+    /* upper-triangular (suffix) recurrence, combined on the fly; nothing
+     * follows the last element, so the carry into it is zero */
+    for (int64_t c = 0; c < m; ++c) u[c] = 0.0;
     for (int64_t i = n - 1; i >= 0; --i) {
       const float* xr = x + (size_t)perm[i] * m;
       double d = (i == n - 1) ? 0.0 : exp(as[i] - as[i + 1]);
