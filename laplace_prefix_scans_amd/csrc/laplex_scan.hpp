@@ -740,6 +740,15 @@ __device__ __forceinline__ void sym_apply_tile(const float* __restrict__ a_s, co
   const float2 ta = tanch[tile];
   const float sf = tile > 0 ? tanch[tile - 1].y : ta.x;
   const float sb = tile + 1 < T ? tanch[tile + 1].x : ta.y;
+  // Scattered rows of two chunks (m == 2C, the phased apply's usual case):
+  // the first chunk's outputs are held and each row is written whole with
+  // the second, so that both halves reach the row's cache line together.
+  const bool hold = SCATTER && PH && m == 2 * C;
+  float yprev[E][C];
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+#pragma unroll
+    for (int j = 0; j < C; ++j) yprev[e][j] = 0.f;
   for (uint32_t cc = 0; cc < m / C; ++cc) {
     float xv[E][C], cin_f[CC], cin_b[CC];
 #pragma unroll
@@ -779,7 +788,25 @@ __device__ __forceinline__ void sym_apply_tile(const float* __restrict__ a_s, co
     for (int e = 0; e < E; ++e)
 #pragma unroll
       for (int j = 0; j < C; ++j) yv[e][j] = PH ? fmaf(cs[e], v[e][j], sn[e] * v[e][C + j]) : v[e][j];
-    if (SCATTER) {
+    if (SCATTER && hold) {
+      if (cc == 0) {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+#pragma unroll
+          for (int j = 0; j < C; ++j) yprev[e][j] = yv[e][j];
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (FAST || p0 + e < n) {
+            float* yr = y + (uint64_t)dst[e] * m;
+#pragma unroll
+            for (int j = 0; j < C; ++j) yr[j] = yprev[e][j];
+#pragma unroll
+            for (int j = 0; j < C; ++j) yr[C + j] = yv[e][j];
+          }
+        }
+      }
+    } else if (SCATTER) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         if (FAST || p0 + e < n) {
