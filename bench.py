@@ -399,8 +399,9 @@ def micro(args):
     moving them along the sort's route, on arrays of 2^30 floats (4 GiB):
     a streaming copy, a random 4-byte gather y = x[p] and scatter y[p] = x
     for a uniformly random permutation p (the order a sort of iid anchors
-    produces), and random 64-byte rows (16 floats) gathered by index.  Each
-    is timed with HIP events over repeated launches (torch's kernels)."""
+    produces), and random 64-byte rows (16 floats) gathered by index, each by
+    torch's kernels; then the probe library's streaming patterns.  Each is
+    timed with HIP events over repeated launches."""
     import torch
     n = 1 << 30
     dev = torch.device("cuda:0")
@@ -436,6 +437,31 @@ def micro(args):
     ms = timed(lambda: torch.index_select(x2, 0, pr, out=y2))
     out["gather_64B_rows"] = {"ms": round(ms, 3), "useful_GBps": round(2 * 4 * n / (ms * 1e-3) / 1e9, 1),
                               "bytes": "64-byte rows read at random + written in order"}
+    # the streaming patterns of liblaplex_probe.so (include/laplex_probe.h),
+    # each over the same 4 GiB: two copy shapes, a read, a write, and one
+    # radix pass's data movement (8192-pair tiles into 256 regions) without
+    # its ranking
+    import ctypes
+    probe_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "laplace_prefix_scans_amd", "liblaplex_probe.so")
+    if not os.path.exists(probe_path):
+        raise RuntimeError("liblaplex_probe.so is not built (python -m laplace_prefix_scans_amd.build)")
+    probe = ctypes.CDLL(probe_path)
+    probe.laplex_probe.restype = ctypes.c_int
+    probe.laplex_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    nbytes = 4 * n
+
+    def run_probe(kind):
+        rc = probe.laplex_probe(kind, x.data_ptr(), y.data_ptr(), nbytes, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError("laplex_probe(%d) returned %d" % (kind, rc))
+
+    for kind, name, moved, what in ((0, "probe_copy_1", 2, "copy, one 16-byte piece per thread, 4 KiB per workgroup, per-XCD ranges"),
+                                    (1, "probe_copy_8", 2, "copy, eight 16-byte pieces per thread, 32 KiB per workgroup"),
+                                    (2, "probe_read", 1, "read, one 16-byte piece per thread"),
+                                    (3, "probe_write", 1, "write, one 16-byte piece per thread"),
+                                    (4, "probe_runs", 2, "8192-pair tiles read whole, written as 256 runs of 256 bytes")):
+        ms = timed(lambda: run_probe(kind))
+        out[name] = {"ms": round(ms, 3), "GBps": round(moved * nbytes / (ms * 1e-3) / 1e9, 1), "bytes": what}
     print(json.dumps({"micro": out, "n_floats": n, "peak_GBps": HBM_PEAK_GBPS}))
 
 

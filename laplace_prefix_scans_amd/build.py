@@ -1,4 +1,6 @@
-"""Build liblaplex.so (HIP, gfx950) in-tree with hipcc.
+"""Build liblaplex.so (HIP, gfx950) in-tree with hipcc, and beside it
+liblaplex_probe.so, the memory-system probes the benchmark measures the
+operator's kernels against.
 
     python -m laplace_prefix_scans_amd.build
 """
@@ -14,6 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblaplex.so")
 SOURCES = ["laplex_sort.hip", "laplex_route.hip", "laplex_apply.hip", "laplex_api.hip"]
+PROBE_LIB = os.path.join(HERE, "liblaplex_probe.so")
+PROBE_SOURCES = ["laplex_probe.hip"]
 ARCH = "gfx950"
 FLAGS = [
     "-O3",
@@ -42,19 +46,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every HIP source and link liblaplex.so (always rebuilds)."""
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every HIP source and link liblaplex.so and liblaplex_probe.so
+    (always rebuilds)."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 
