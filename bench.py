@@ -35,16 +35,22 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 CSRC = os.path.join(ROOT, "laplace_prefix_scans_amd", "csrc")
 
 
+# sources of the memory-system probes, which are not operator kernels
+PROBE_SOURCES = ("laplex_probe.hip",)
+
+
 def source_hash() -> str:
+    """Hash of the operator's kernel sources (the probes excluded), stamped on
+    each profile so that counters taken on other kernels are not used."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".hpp")):
+        if f.endswith((".hip", ".hpp")) and f not in PROBE_SOURCES:
             with open(os.path.join(CSRC, f), "rb") as fh:
                 h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
-SORT_TILE = 8192                       # keys per sort tile (512 threads x 16 keys)
+SORT_TILE = 8192                       # keys per sort tile
 ROUTE_BYTES = 2.0 + 1536.0 / SORT_TILE  # per element per routed pass: u16 tile-local position, plus
                                        # u16 run starts and u32 run positions (256 digits) per tile
 
