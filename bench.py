@@ -509,7 +509,7 @@ def main():
         print(ktxt + ctxt)
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (got --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
