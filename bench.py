@@ -50,9 +50,17 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-SORT_TILE = 8192                       # keys per sort tile
-ROUTE_BYTES = 2.0 + 1536.0 / SORT_TILE  # per element per routed pass: u16 tile-local position, plus
-                                       # u16 run starts and u32 run positions (256 digits) per tile
+SMALL_SORT_MAX = 1 << 17              # sorts of at most this many keys use 2048-key tiles, larger ones 8192
+
+
+def sort_tile(n: int) -> int:
+    return 2048 if n <= SMALL_SORT_MAX else 8192
+
+
+def route_bytes_per_elem(n: int) -> float:
+    """Per element per routed pass: a u16 tile-local position, plus u16 run
+    starts and u32 run positions (256 digits) per tile."""
+    return 2.0 + 1536.0 / sort_tile(n)
 
 
 def kernel_bytes(name: str, units: int, m: int, k: int = 0) -> float:
@@ -119,9 +127,9 @@ def kernel_bytes(name: str, units: int, m: int, k: int = 0) -> float:
 
 def overhead_bytes(name: str, units: int) -> float:
     """Route bookkeeping of one launch: the positions and run tables a routed
-    sort pass writes, or a route pass reads, ROUTE_BYTES per element."""
+    sort pass writes, or a route pass reads, per element of the sort."""
     if name.startswith(("k_route_fwd", "k_route_inv")) or (name.startswith("k_onesweep") and name.endswith("_routed")):
-        return ROUTE_BYTES * units
+        return route_bytes_per_elem(units) * units
     return 0.0
 
 

@@ -40,7 +40,7 @@ SortWorkspace carve_sort(void* ws, uint64_t n) {
   w.offsets = w.header + kSortOffsOffset / 4;
   w.status = c.take<void>(sort_status_bytes(n));  // directly after the header
   for (int i = 0; i < 2; ++i) w.kv[i] = c.take<uint2>(n * 8);
-  w.tcount = c.take<uint32_t>(sort_tiles(n) * 256 * 4);
+  w.tcount = c.take<uint32_t>(sort_tiles_alloc(n) * 256 * 4);
   w.gsum = c.take<uint32_t>((size_t)kHistMaxBlocks * 256 * 4);
   return w;
 }
@@ -49,7 +49,7 @@ size_t sort_bytes(uint64_t n) {
   c.take<uint32_t>(kSortHeaderBytes);
   c.take<void>(sort_status_bytes(n));
   for (int i = 0; i < 2; ++i) c.take<uint2>(n * 8);
-  c.take<uint32_t>(sort_tiles(n) * 256 * 4);
+  c.take<uint32_t>(sort_tiles_alloc(n) * 256 * 4);
   c.take<uint32_t>((size_t)kHistMaxBlocks * 256 * 4);
   return (c.off + 255) & ~size_t(255);
 }

@@ -26,10 +26,18 @@ void prof_end(int slot, const char* name, uint64_t units, hipStream_t s);
 // Sort tiles of 8192 keys.  The first pass (offsets from the histogram's
 // tables, no look-back) runs 512 threads x 16 keys; the passes that look back
 // run 256 threads x 32 keys, so that four tiles share a CU and more of their
-// look-back waits overlap.  The route kernels move tiles with 512 threads.
+// look-back waits overlap.  Sorts of at most kSmallSortMax keys use tiles of
+// 2048 keys (256 threads x 8 keys in every pass): with few tiles a pass lasts
+// about as long as one tile, and a quarter of the tile takes about 60 % of
+// the time.  The tile size is a function of n alone, so a sort and every
+// later use of its route agree on it.  The route kernels move tiles with 512
+// threads.
 constexpr int kSortTile = 8192;
-constexpr int sort_block(int mode) { return mode == 0 ? 512 : 256; }
+constexpr int kSortTileSmall = 2048;
+constexpr uint64_t kSmallSortMax = 1u << 17;
+constexpr int sort_block(int mode, int tile) { return mode == 0 && tile == kSortTile ? 512 : 256; }
 constexpr int kRouteBlock = 512;
+inline uint32_t sort_tile(uint64_t n) { return n <= kSmallSortMax ? (uint32_t)kSortTileSmall : (uint32_t)kSortTile; }
 
 // header words of the sort workspace
 constexpr int kHdrFlags = 0;    // sticky error bits (below)
@@ -54,7 +62,16 @@ struct SortWorkspace {
   uint32_t* tcount;   // [tiles][256] first-pass digit counts of the tiles before each tile in its histogram block's range
   uint32_t* gsum;     // [kHistMaxBlocks][256] per histogram block: its range's digit counts, then their exclusive prefix
 };
-inline uint64_t sort_tiles(uint64_t n) { return (n + kSortTile - 1) / kSortTile; }
+inline uint64_t sort_tiles(uint64_t n) { return (n + sort_tile(n) - 1) / sort_tile(n); }
+// Tiles the per-tile arrays (status words, first-pass counts, route tables)
+// are laid out for: the sort's own count, but past the switch to 8192-key
+// tiles never fewer than the 64 of a sort of kSmallSortMax keys, so that
+// every size grows with n and a workspace or route sized for n serves every
+// smaller n.
+inline uint64_t sort_tiles_alloc(uint64_t n) {
+  const uint64_t t = sort_tiles(n), at_switch = kSmallSortMax / kSortTileSmall;
+  return n <= kSmallSortMax || t >= at_switch ? t : at_switch;
+}
 constexpr int kHistMaxBlocks = 256;  // workgroups of the histogram read (rows of gsum)
 
 // Route of a sort: for every radix pass, the tile-local sorted position of

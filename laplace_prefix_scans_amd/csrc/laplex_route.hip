@@ -115,12 +115,12 @@ __device__ __forceinline__ void load_tables(const uint16_t* __restrict__ dstart,
 
 // vec: `in` (fwd) or `out` (inv), the input-order side, is 16-byte aligned
 // (and in_b / out_b with PLANES).
-template <int W, bool PLANES>
+template <int W, bool PLANES, int TILE>
 __global__ __launch_bounds__(kRouteBlock) void k_route_fwd(const float* __restrict__ in, const float* __restrict__ in_b,
                                                           float* __restrict__ out,
                                                           const uint16_t* __restrict__ lpos, const uint16_t* __restrict__ dstart,
                                                           const uint32_t* __restrict__ gbase, uint64_t n, bool vec) {
-  constexpr int TILE = kSortTile;
+  static_assert(TILE % (kRouteBlock * kGroup) == 0, "whole position groups per thread");
   constexpr int NW = kRouteBlock / kWave;
   constexpr int STEPS = TILE / kRouteBlock;
   constexpr int GSTEPS = TILE / (kRouteBlock * kGroup);
@@ -185,12 +185,12 @@ __global__ __launch_bounds__(kRouteBlock) void k_route_fwd(const float* __restri
   }
 }
 
-template <int W, bool PLANES>
+template <int W, bool PLANES, int TILE>
 __global__ __launch_bounds__(kRouteBlock) void k_route_inv(const float* __restrict__ in, float* __restrict__ out,
                                                           float* __restrict__ out_b,
                                                           const uint16_t* __restrict__ lpos, const uint16_t* __restrict__ dstart,
                                                           const uint32_t* __restrict__ gbase, uint64_t n, bool vec) {
-  constexpr int TILE = kSortTile;
+  static_assert(TILE % (kRouteBlock * kGroup) == 0, "whole position groups per thread");
   constexpr int NW = kRouteBlock / kWave;
   constexpr int STEPS = TILE / kRouteBlock;
   constexpr int GSTEPS = TILE / (kRouteBlock * kGroup);
@@ -256,9 +256,9 @@ __global__ __launch_bounds__(kRouteBlock) void k_route_inv(const float* __restri
 // it are numbered block-locally from cs[d], the first being global chunk
 // c0[d] (chunk_run finds the run of a block-local chunk).  L is clipped to
 // the array, so no chunk lies wholly past it.
-template <int W>
+template <int W, int TILE>
 struct RunChunks {
-  static constexpr int kMax = kSortTile * W / 4 + 512;  // sum over runs of (L W + 6) / 4
+  static constexpr int kMax = TILE * W / 4 + 512;  // sum over runs of (L W + 6) / 4
   uint32_t cs[257];
   uint32_t c0[256];
   uint32_t len[256];
@@ -268,8 +268,8 @@ struct RunChunks {
 // The run of block-local chunk c (cs[d] <= c < cs[d + 1]; empty runs have
 // cs[d] == cs[d + 1] and are passed over): a branch-free binary search over
 // the 257 prefix entries in LDS.
-template <int W>
-__device__ __forceinline__ uint32_t chunk_run(const RunChunks<W>& rc, uint32_t c) {
+template <int W, int TILE>
+__device__ __forceinline__ uint32_t chunk_run(const RunChunks<W, TILE>& rc, uint32_t c) {
   uint32_t d = 0;
 #pragma unroll
   for (uint32_t step = 128; step >= 1; step >>= 1) d = rc.cs[d + step] <= c ? d + step : d;
@@ -278,8 +278,8 @@ __device__ __forceinline__ uint32_t chunk_run(const RunChunks<W>& rc, uint32_t c
 
 // Called by every thread of the block after s_start / s_gb are written (and
 // not yet synchronised); ends with a barrier.
-template <int W, int NW>
-__device__ __forceinline__ void build_chunks(RunChunks<W>& rc, const uint16_t* s_start, const uint32_t* s_gb, uint64_t n) {
+template <int W, int NW, int TILE>
+__device__ __forceinline__ void build_chunks(RunChunks<W, TILE>& rc, const uint16_t* s_start, const uint32_t* s_gb, uint64_t n) {
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
   __syncthreads();
   uint32_t nch = 0, x = 0;
@@ -314,23 +314,23 @@ __device__ __forceinline__ void build_chunks(RunChunks<W>& rc, const uint16_t* s
 // lie outside the run belong to neighbouring runs and are discarded; a chunk
 // reaching past the end of the array is read float by float.  vec: `out` is
 // 16-byte aligned.
-template <int W, bool PLANES>
+template <int W, bool PLANES, int TILE>
 __global__ __launch_bounds__(kRouteBlock) __attribute__((amdgpu_waves_per_eu(W == 1 ? 8 : 1))) void k_route_inv_chunked(const float* __restrict__ in, float* __restrict__ out,
                                                                   float* __restrict__ out_b,
                                                                   const uint16_t* __restrict__ lpos,
                                                                   const uint16_t* __restrict__ dstart,
                                                                   const uint32_t* __restrict__ gbase, uint64_t n, bool vec) {
   static_assert(W == 1 || W == 2 || W == 4, "rows must tile a 16-byte chunk");
-  constexpr int TILE = kSortTile;
+  static_assert(TILE % (kRouteBlock * kGroup) == 0, "whole position groups per thread");
   constexpr int NW = kRouteBlock / kWave;
   constexpr int GSTEPS = TILE / (kRouteBlock * kGroup);
-  constexpr int MAXCH = RunChunks<W>::kMax;
+  constexpr int MAXCH = RunChunks<W, TILE>::kMax;
   constexpr int CSTEPS = (MAXCH + kRouteBlock - 1) / kRouteBlock;
   constexpr int RPC = 4 / W;  // rows per chunk
   __shared__ float s_val[TILE * W];
   __shared__ uint16_t s_start[257];
   __shared__ uint32_t s_gb[256];
-  __shared__ RunChunks<W> rc;
+  __shared__ RunChunks<W, TILE> rc;
   const int tid = threadIdx.x;
   uint64_t tile;
   if (!xcd_tile((n + TILE - 1) / TILE, tile)) return;
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kRouteBlock) __attribute__((amdgpu_waves_per_eu(W =
     lp2[r] = i0 + kGroup <= count ? *reinterpret_cast<const uint2*>(lpos + base + i0) : make_uint2(0u, 0u);
   }
   load_tables(dstart, gbase, tile, count, s_start, s_gb);
-  build_chunks<W, NW>(rc, s_start, s_gb, n);
+  build_chunks<W, NW, TILE>(rc, s_start, s_gb, n);
   const uint32_t total = rc.cs[256];
   const uint64_t nfl = n * W;  // >= 4 (the host launches this kernel only then)
   // all chunk loads are issued before any is consumed; a chunk that is not
@@ -413,13 +413,13 @@ __global__ __launch_bounds__(kRouteBlock) __attribute__((amdgpu_waves_per_eu(W =
 
 // ------------------------------------------------------------------ host side
 size_t route_bytes(uint64_t n) {
-  const uint64_t tiles = (n + kSortTile - 1) / kSortTile;
+  const uint64_t tiles = sort_tiles_alloc(n);
   auto up = [](uint64_t b) { return (b + 255) & ~uint64_t(255); };
   return (size_t)(4 * (up(2 * n) + up(tiles * 256 * 2) + up(tiles * 256 * 4)));
 }
 
 SortRoute carve_route(const void* base, uint64_t n) {
-  const uint64_t tiles = (n + kSortTile - 1) / kSortTile;
+  const uint64_t tiles = sort_tiles_alloc(n);
   auto up = [](uint64_t b) { return (b + 255) & ~uint64_t(255); };
   uintptr_t p = reinterpret_cast<uintptr_t>(base);
   SortRoute r;
@@ -436,29 +436,37 @@ SortRoute carve_route(const void* base, uint64_t n) {
 
 // One pass of a route.  in_b (forward) / out_b (inverse), when given, make the
 // input-order side two separate arrays forming rows of W = 2 floats.
-template <int W, bool PLANES>
-static hipError_t route_pass(bool fwd, const SortRoute& r, int k, uint64_t n, const float* in, const float* in_b, float* out,
-                             float* out_b, hipStream_t s) {
+template <int W, bool PLANES, int TILE>
+static hipError_t route_pass_tile(bool fwd, const SortRoute& r, int k, uint64_t n, const float* in, const float* in_b,
+                                  float* out, float* out_b, hipStream_t s) {
   // the input-order side: `in` going forward, `out` going back
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   const bool vec = fwd ? (al(in) && (!PLANES || al(in_b))) : (al(out) && (!PLANES || al(out_b)));
   static const char* const kFwd[5] = {"", "k_route_fwd_w1", "k_route_fwd_w2", "k_route_fwd_w3", "k_route_fwd_w4"};
   static const char* const kInv[5] = {"", "k_route_inv_w1", "k_route_inv_w2", "k_route_inv_w3", "k_route_inv_w4"};
-  const uint64_t tiles = (n + kSortTile - 1) / kSortTile;
+  const uint64_t tiles = (n + TILE - 1) / TILE;
   const uint64_t blocks = ((tiles + kXcds - 1) / kXcds) * kXcds;
   if (fwd)
     LAPLEX_LAUNCH(kFwd[W], n, s,
-                  k_route_fwd<W, PLANES><<<dim3((unsigned)blocks), dim3(kRouteBlock), 0, s>>>(
+                  k_route_fwd<W, PLANES, TILE><<<dim3((unsigned)blocks), dim3(kRouteBlock), 0, s>>>(
                       in, in_b, out, r.lpos[k], r.dstart[k], r.gbase[k], n, vec));
   else if (W != 3 && al(in) && n * W >= 4)
     LAPLEX_LAUNCH(kInv[W], n, s,
-                  k_route_inv_chunked<W == 3 ? 1 : W, PLANES><<<dim3((unsigned)blocks), dim3(kRouteBlock), 0, s>>>(
+                  k_route_inv_chunked<W == 3 ? 1 : W, PLANES, TILE><<<dim3((unsigned)blocks), dim3(kRouteBlock), 0, s>>>(
                       in, out, out_b, r.lpos[k], r.dstart[k], r.gbase[k], n, vec));
   else
     LAPLEX_LAUNCH(kInv[W], n, s,
-                  k_route_inv<W, PLANES><<<dim3((unsigned)blocks), dim3(kRouteBlock), 0, s>>>(
+                  k_route_inv<W, PLANES, TILE><<<dim3((unsigned)blocks), dim3(kRouteBlock), 0, s>>>(
                       in, out, out_b, r.lpos[k], r.dstart[k], r.gbase[k], n, vec));
   return hipGetLastError();
+}
+// the route's tiles are the sort's, whose size follows from n
+template <int W, bool PLANES>
+static hipError_t route_pass(bool fwd, const SortRoute& r, int k, uint64_t n, const float* in, const float* in_b, float* out,
+                             float* out_b, hipStream_t s) {
+  if (sort_tile(n) == (uint32_t)kSortTileSmall)
+    return route_pass_tile<W, PLANES, kSortTileSmall>(fwd, r, k, n, in, in_b, out, out_b, s);
+  return route_pass_tile<W, PLANES, kSortTile>(fwd, r, k, n, in, in_b, out, out_b, s);
 }
 
 static hipError_t route_pass_w(bool fwd, const SortRoute& r, int k, uint64_t n, uint32_t W, const float* in, float* out,

@@ -48,7 +48,8 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, uint64_t count, uint32_t va
 // One replica of every histogram per lane position (lane mod 32), so the 32
 // lanes an LDS cycle serves always hit 32 different banks; 1024 threads keep
 // enough loads in flight with one block per CU.
-// The same read also counts the first pass's digit in each sort tile: block
+// The same read also counts the first pass's digit in each 8192-key sort tile
+// (sorts with smaller tiles look back in every pass and ignore it): block
 // b reads a contiguous range of chunks (two tiles each), keeps a running
 // count per digit, and writes each tile's count of the tiles before it in
 // the block's range (tcount) and the range's total (bsum[b]); an exclusive
@@ -242,8 +243,8 @@ __global__ __launch_bounds__(kScanThreads) void k_sort_offsets(const uint32_t* _
 // of a 256-thread block, the first four waves of a 512-thread one).
 constexpr int kLookback = 4;  // predecessor status words read per round trip (more costs more status traffic than it saves)
 
-template <int MODE, typename ST, bool PAY>
-__global__ __launch_bounds__(sort_block(MODE)) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 6 : 4))) void k_onesweep(const uint2* __restrict__ kvin, uint2* __restrict__ kvout,
+template <int MODE, typename ST, bool PAY, int TILE>
+__global__ __launch_bounds__(sort_block(MODE, TILE)) __attribute__((amdgpu_waves_per_eu(MODE == 0 && TILE == kSortTile ? 6 : 4))) void k_onesweep(const uint2* __restrict__ kvin, uint2* __restrict__ kvout,
                                                          uint32_t* __restrict__ kout, uint32_t* __restrict__ vout,
                                                          const uint32_t* __restrict__ a_bits, ST* __restrict__ status,
                                                          uint32_t* __restrict__ header, int pass,
@@ -254,12 +255,14 @@ __global__ __launch_bounds__(sort_block(MODE)) __attribute__((amdgpu_waves_per_e
                                                          uint64_t chunks_per_block, uint32_t spin_limit, bool publish) {
   static_assert(!PAY || MODE != 1, "the payload enters in pass 1 and leaves in pass 4");
   constexpr bool HOLDV = MODE != 0 || PAY;  // values held in registers (else recomputed input indices)
-  constexpr int BLOCK = sort_block(MODE);
+  constexpr int BLOCK = sort_block(MODE, TILE);
   static_assert(BLOCK % 256 == 0, "at least one thread per digit value");
-  constexpr int TILE = kSortTile;
+  static_assert(TILE == kSortTile || TILE == kSortTileSmall, "a sort tile size");
   constexpr int E = TILE / BLOCK;
   constexpr int NW = BLOCK / kWave;
-  __shared__ __align__(16) uint2 s_kv[TILE / 2];
+  // staging for half a tile, large enough for the ranking scratch too
+  constexpr int kStage = TILE / 2 > NW * 256 * 2 ? TILE / 2 : NW * 256 * 2;
+  __shared__ __align__(16) uint2 s_kv[kStage];
   __shared__ uint32_t s_whist[NW][256];
   __shared__ uint32_t s_gbase[256];
   __shared__ uint32_t s_wsum[4];
@@ -278,7 +281,7 @@ __global__ __launch_bounds__(sort_block(MODE)) __attribute__((amdgpu_waves_per_e
   // by the histogram read, so tiles depend on no other tile and are placed
   // by block index; otherwise tiles are taken in ticket order for the
   // look-back.
-  const bool table = MODE == 0 && tcount != nullptr;
+  const bool table = MODE == 0 && TILE == kSortTile && tcount != nullptr;
   uint64_t xtile = 0;
   if (table && !xcd_tile((n + TILE - 1) / TILE, xtile)) return;
   if (!table && tid == 0) s_tile = atomicAdd(&header[kHdrTicket0 + pass], 1u);
@@ -541,7 +544,7 @@ static uint32_t debug_stall_spins() {
   return (uint32_t)std::min<unsigned long>(v, kSpinLimit);
 }
 
-template <typename ST>
+template <typename ST, int TILE>
 static hipError_t launch_sort_passes(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,
                                      const SortRoute* route, const uint32_t* pay, bool table, uint64_t cpb,
                                      hipStream_t s, bool debug) {
@@ -549,7 +552,7 @@ static hipError_t launch_sort_passes(const SortWorkspace& w, const float* a, uin
   const uint32_t spin_limit = dbg ? dbg : kSpinLimit;
   const bool publish = dbg == 0;
   const uint32_t* a_bits = reinterpret_cast<const uint32_t*>(a);
-  const uint64_t tiles = (n + kSortTile - 1) / kSortTile;
+  const uint64_t tiles = (n + TILE - 1) / TILE;
   ST* st = reinterpret_cast<ST*>(w.status);
   const uint2* src = nullptr;
   for (int p = 0; p < 4; ++p) {
@@ -563,7 +566,7 @@ static hipError_t launch_sort_passes(const SortWorkspace& w, const float* a, uin
     const dim3 grid((unsigned)tiles), grid0((unsigned)xcd_blocks(tiles));
 #define LAPLEX_PASS(MODE, PAY, NAME)                                                                                  \
   LAPLEX_LAUNCH(NAME, n, s,                                                                                          \
-                (k_onesweep<MODE, ST, PAY><<<(MODE == 0 && table ? grid0 : grid), dim3(sort_block(MODE)), 0, s>>>(     \
+                (k_onesweep<MODE, ST, PAY, TILE><<<(MODE == 0 && table ? grid0 : grid), dim3(sort_block(MODE, TILE)), 0, s>>>( \
                     src, dst, fk, fv, a_bits, stp, w.header, p, w.offsets + p * 256, n, rl, rd, rg, pay,                \
                     MODE == 0 && table ? w.tcount : nullptr, w.gsum, cpb, spin_limit, publish)))
     if (p == 0 && pay)
@@ -585,7 +588,7 @@ static hipError_t launch_sort_passes(const SortWorkspace& w, const float* a, uin
 }
 
 size_t sort_status_bytes(uint64_t n) {
-  const uint64_t tiles = (n + kSortTile - 1) / kSortTile;
+  const uint64_t tiles = sort_tiles_alloc(n);
   const size_t word = (n <= (1ull << 30)) ? 4 : 8;
   return (size_t)(4 * tiles * 256) * word;
 }
@@ -607,13 +610,16 @@ static hipError_t sort_impl(const SortWorkspace& w, const float* a, uint64_t n, 
                 k_sort_hist<<<(unsigned)hist_blocks, kHistBlock, 0, s>>>(reinterpret_cast<const uint32_t*>(a), n, w.hist,
                                                                          w.header, w.tcount, w.gsum, cpb));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // small sorts keep the first pass's look-back
-  const bool table = sort_tiles(n) >= kTableMinTiles;
+  // small sorts keep the first pass's look-back; the tables count keys per
+  // 8192-key tile, so small tiles always look back
+  const bool small = sort_tile(n) == (uint32_t)kSortTileSmall;
+  const bool table = !small && sort_tiles(n) >= kTableMinTiles;
   LAPLEX_LAUNCH("k_sort_offsets", 1024, s,
                 k_sort_offsets<<<1, kScanThreads, 0, s>>>(w.hist, w.offsets, w.header, w.gsum, table ? hist_blocks : 0));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (n <= (1ull << 30)) return launch_sort_passes<uint32_t>(w, a, n, a_sorted, perm, route, pay, table, cpb, s, debug);
-  return launch_sort_passes<uint64_t>(w, a, n, a_sorted, perm, route, pay, table, cpb, s, debug);
+  if (small) return launch_sort_passes<uint32_t, kSortTileSmall>(w, a, n, a_sorted, perm, route, pay, false, cpb, s, debug);
+  if (n <= (1ull << 30)) return launch_sort_passes<uint32_t, kSortTile>(w, a, n, a_sorted, perm, route, pay, table, cpb, s, debug);
+  return launch_sort_passes<uint64_t, kSortTile>(w, a, n, a_sorted, perm, route, pay, table, cpb, s, debug);
 }
 
 hipError_t sort_anchors(const SortWorkspace& w, const float* a, uint64_t n, float* a_sorted, uint32_t* perm,

@@ -52,6 +52,21 @@ def test_workspace_sizes(L):
         assert a % 256 == 0 and b % 256 == 0 and b >= a
 
 
+def test_sizes_grow_with_n(L):
+    """Sorts of up to 2^17 keys use 2048-key tiles and larger ones 8192-key
+    tiles; route and workspace sizes still never shrink as n grows (a buffer
+    sized for n serves every smaller n), across that switch and the size
+    (2^19) from which the large tiles outnumber the small ones at 2^17."""
+    import laplace_prefix_scans_amd as lp
+    ns = [1, 2047, 2048, 2049, 1 << 16, (1 << 17) - 1, 1 << 17, (1 << 17) + 1, (1 << 17) + 8193, 1 << 18,
+          (1 << 19) - 1, 1 << 19, (1 << 19) + 1, (1 << 19) + 8193, 1 << 20]
+    sizes = [L.laplex_route_bytes(n) for n in ns]
+    assert sizes == sorted(sizes), sizes
+    for op in range(12):
+        sizes = [lp.laplex_workspace_bytes(op, n, 1000, 2) for n in ns]
+        assert sizes == sorted(sizes), (op, sizes)
+
+
 def test_host_argument_errors(L):
     vp = ctypes.c_void_p
     A = vp(0x100000)      # never dereferenced: every call below fails a check first

@@ -60,7 +60,7 @@ def test_backward_sym_parity(n, m, ties):
         assert e_dx <= TOL and e_da <= TOL, "n=%d m=%d ties=%s route=%s: dx %.2e da %.2e" % (n, m, ties, route, e_dx, e_da)
 
 
-@pytest.mark.parametrize("n,m", [(5000, 1), (70001, 2), (9999, 4)])
+@pytest.mark.parametrize("n,m", [(5000, 1), (70001, 2), (9999, 4), (140001, 1), ((1 << 17) + 1, 3)])
 def test_backward_route_bitwise(n, m):
     """Moving rows along the route or by index gives the same bits."""
     a, x, g = _case(n, m, 7 + n, True)

@@ -68,7 +68,7 @@ def test_backward_general_parity(n, k, m, ties):
             n, k, m, ties, route, e_dx, e_da, e_db)
 
 
-@pytest.mark.parametrize("n,k,m", [(5000, 700, 1), (7001, 7001, 2), (999, 9999, 4)])
+@pytest.mark.parametrize("n,k,m", [(5000, 700, 1), (7001, 7001, 2), (999, 9999, 4), (140001, 131073, 1)])
 def test_backward_general_route_bitwise(n, k, m):
     """Moving rows along the routes or by index gives the same bits."""
     a, b, x, g = _case(n, k, m, 7 + n + k, True)

@@ -65,7 +65,7 @@ def test_backward_phased_parity(n, m, ties):
         assert max(errs) <= TOL, "n=%d m=%d ties=%s route=%s: dx %.2e da %.2e dphi %.2e" % ((n, m, ties, route) + errs)
 
 
-@pytest.mark.parametrize("n,m", [(5000, 1), (7001, 2), (999, 4)])
+@pytest.mark.parametrize("n,m", [(5000, 1), (7001, 2), (999, 4), ((1 << 17) + 1, 2)])
 def test_backward_phased_route_bitwise(n, m):
     """Moving rows along the route or by index gives the same bits."""
     a, phi, x, g = _case(n, m, 9 + n, True)

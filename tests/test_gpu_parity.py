@@ -41,6 +41,16 @@ def _anchor_cases():
         "signed_zero_600000": r.choice(np.array([0.0, -0.0, 2.0, -2.0], np.float32), 600000),
         # 257 histogram chunks: two chunks per histogram block, some blocks empty
         "chunks257_int_ties": r.integers(0, 1 << 12, 16384 * 257 + 3).astype(np.float32),
+        # sorts of up to 2^17 keys run on 2048-key tiles, larger ones on 8192:
+        # both sides of the switch, and the small cases' patterns on the
+        # large tiles
+        "switch_131072_ties": r.integers(-500, 500, 1 << 17).astype(np.float32),
+        "switch_131073_ties": r.integers(-500, 500, (1 << 17) + 1).astype(np.float32),
+        "all_equal_140000": np.full(140000, 2.5, np.float32),
+        "sorted_140001": np.sort(r.standard_normal(140001).astype(np.float32)),
+        "reversed_140001": np.sort(r.standard_normal(140001).astype(np.float32))[::-1].copy(),
+        "signed_zero_131075": r.choice(np.array([0.0, -0.0, 3.0, -3.0], np.float32), 131075),
+        "wide_range_140000": (r.standard_normal(140000) * 1e30).astype(np.float32),
     }
 
 

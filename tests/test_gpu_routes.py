@@ -24,6 +24,7 @@ def _sorted_with_route(a):
 
 
 @pytest.mark.parametrize("n,m", [(1, 1), (5, 2), (4095, 1), (4096, 3), (4097, 4), (70001, 1), (300000, 2), (123457, 4),
+                                 (1 << 17, 3), ((1 << 17) + 1, 2),
                                  (20000, 8)])
 def test_sym_route_bitwise(n, m):
     import laplace_prefix_scans_amd as lp
@@ -64,7 +65,7 @@ def test_sym_route_bitwise_large(n, m):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("n,m", [(4096, 1), (70001, 2), (9999, 4)])
+@pytest.mark.parametrize("n,m", [(4096, 1), (70001, 2), (9999, 4), (140001, 2)])
 def test_phased_route_bitwise(n, m):
     import laplace_prefix_scans_amd as lp
     r = _rng(7 + n + m)
@@ -79,7 +80,7 @@ def test_phased_route_bitwise(n, m):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("n,k,m", [(5000, 300, 1), (200000, 70000, 2), (3000, 90000, 3), (100000, 1, 1)])
+@pytest.mark.parametrize("n,k,m", [(5000, 300, 1), (200000, 70000, 2), (3000, 90000, 3), (100000, 1, 1), (9000, 140001, 1)])
 @pytest.mark.parametrize("which", ["a", "b", "both"])
 def test_general_route_bitwise(n, k, m, which):
     import laplace_prefix_scans_amd as lp
