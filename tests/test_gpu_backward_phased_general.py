@@ -69,8 +69,9 @@ def test_backward_phased_general_parity(n, k, m, ties):
         assert max(e) <= TOL, "n=%d k=%d m=%d ties=%s route=%s: %s" % (n, k, m, ties, route, ["%.2e" % v for v in e])
 
 
-def test_backward_phased_general_route_bitwise():
-    a, phi, b, psi, x, g = _case(5000, 900, 2, 11, True)
+@pytest.mark.parametrize("n,k,m", [(5000, 900, 2), (140001, 131073, 1)])
+def test_backward_phased_general_route_bitwise(n, k, m):
+    a, phi, b, psi, x, g = _case(n, k, m, 11, True)
     r0 = _run(a, phi, b, psi, x, g, False)
     r1 = _run(a, phi, b, psi, x, g, True)
     for u, v in zip(r0, r1):
